@@ -1,0 +1,127 @@
+/*
+ * retention.h - C ABI of the MI355X (gfx950) multi-scale retention library, libretention.so.
+ *
+ * Retention is the sequence mixer of RetNet: for each (batch b, head h) with a fixed decay gamma_h,
+ *     S_n = gamma S_{n-1} + k_n^T v_n,   o_n = q_n S_n            (state S: d_k x d_v, S before token 0 given)
+ * with q and k first rotated by their absolute position (xPos/rotary form). Sources: "Hybrid Architectures:
+ * RetNet and the Three Computation Paradigms" (sections 2, 4, 6 and 7) and the RetNet paper summary
+ * (Eq. 5 parallel, Eq. 6 recurrent, Eq. 7 chunkwise; the paper's ParallelRetention / RecurrentRetention /
+ * ChunkwiseRetention interfaces, whose precomputed decay tensors are replaced here by gamma itself).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layouts (row-major, contiguous, device memory):
+ *     q, k  [B, N, H, d_k]      v, o  [B, N, H, d_v]      state [B, H, d_k, d_v] (fp32, d_v fastest)
+ *     decode step: q, k [B, H, d_k], v, o [B, H, d_v]
+ * dtypes: q/k/v in `in_dt`, o in `out_dt`; supported pairs are (F32, F32), (BF16, BF16) and (BF16, F32).
+ *     Products accumulate in fp32 and the state is always fp32. On the BF16 path the rotated q and k, the
+ *     masked scores and the copy of the state used for q.S are rounded to bf16 (nearest-even) as MFMA
+ *     operands; the carried state is never rounded.
+ * gamma: HOST float[H], 0 < gamma <= 1 (per-head decay; multi-scale schedule 1 - 2^(-5-h) in the pages).
+ * theta: HOST double[d_k/2] rotation frequencies, or NULL for no rotation. Pair (2i, 2i+1) of q and of k at
+ *     absolute position p is turned by the angle +p*theta_i, so q'.k' depends on positions only through
+ *     n - m (the conjugate-transpose reading of the paper summary's rotation; blog section 6.8).
+ * pos0 / pos: absolute position of the first token (0 for a fresh sequence).
+ * stream: a hipStream_t (NULL = the null stream). Every call only enqueues work and never synchronises.
+ * Ownership: the caller owns every buffer. The library allocates no device memory; gamma/theta are read
+ *     during the call and copied into kernel arguments.
+ * Alignment: device pointers must be 16-byte aligned.
+ * Errors: a non-zero status is returned before anything is enqueued, and ret_last_error() gives a detail
+ *     string for the calling thread. RET_ERR_INVALID_ARG: null pointer, non-positive size, gamma outside
+ *     (0, 1] or NaN, odd d_k with theta, misalignment, o aliasing an input, bad dtype pair.
+ *     RET_ERR_UNSUPPORTED: a shape outside the kernels' tiling (listed per call). RET_ERR_HIP: a launch failed
+ *     (device faults surface at the caller's next synchronisation). There is no fallback path.
+ * NaN/Inf in inputs propagate into outputs; nothing traps.
+ */
+#ifndef RETENTION_H
+#define RETENTION_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RET_ABI_VERSION 1
+
+typedef enum { RET_F32 = 0, RET_BF16 = 1 } ret_dtype_t;
+
+typedef enum {
+    RET_OK = 0,
+    RET_ERR_INVALID_ARG = -1,
+    RET_ERR_UNSUPPORTED = -2,
+    RET_ERR_WORKSPACE = -3,
+    RET_ERR_HIP = -4
+} ret_status_t;
+
+/* ABI version of the loaded library (RET_ABI_VERSION at build time). */
+int ret_abi_version(void);
+
+/* Static text for a status code. */
+const char* ret_status_string(int status);
+
+/* Detail for the last non-OK status returned on the calling thread ("" if none). */
+const char* ret_last_error(void);
+
+/*
+ * Parallel form: O = (Q K^T (.) D) V, D[n][m] = gamma^(n-m) for n >= m and 0 otherwise, per (b, h), over the
+ * whole sequence (blog sections 4.2-4.3; paper summary Eq. 5). No state in or out. Cost O(N^2 d).
+ * Supported: F32 input: d_k in {16, 32, 64}, d_v a multiple of 16. BF16 input: d_k in {32, 64, 128, 256},
+ * d_v a multiple of 64. N >= 1 (any length).
+ */
+ret_status_t ret_parallel_fwd(const void* q, const void* k, const void* v, void* o, int B, int N, int H, int dk,
+                              int dv, ret_dtype_t in_dt, ret_dtype_t out_dt, const float* gamma,
+                              const double* theta, int64_t pos0, void* stream);
+
+/*
+ * Workspace (device bytes) that ret_chunkwise_fwd uses to split each sequence into segments that run in
+ * parallel (a two-level scan of the chunk state). 0 means the call runs one segment per (b, h) and needs
+ * none. Passing a smaller workspace than this is allowed: the call then uses fewer segments.
+ */
+size_t ret_chunkwise_workspace_bytes(int B, int N, int H, int dk, int dv, int chunk, ret_dtype_t in_dt);
+
+/*
+ * Chunkwise recurrent form with chunk size `chunk` (blog section 7.2; paper summary Eq. 7). For chunk i of
+ * length L (the last chunk may be shorter):
+ *     O_[i] = (Q_[i] K_[i]^T (.) D) V_[i] + (Q_[i] R_{i-1}) (.) xi,   xi_j = gamma^(j+1)
+ *     R_i   = gamma^L R_{i-1} + K_[i]^T (V_[i] (.) zeta),             zeta_j = gamma^(L-1-j)
+ * with R_{-1} = state_in (NULL = zeros). state_out (may be NULL, may equal state_in) receives the state after
+ * the last token, so a sequence can resume with pos0 = N and state_in = state_out, or hand over to
+ * ret_recurrent_step. Results equal the recurrent and parallel forms up to rounding.
+ * workspace: device memory of `workspace_bytes` (see ret_chunkwise_workspace_bytes), or NULL with 0.
+ * Supported: F32 input: d_k in {16, 32, 64}, d_v a multiple of 16, chunk in {16, 32, 64}. BF16 input:
+ * d_k in {32, 64, 128, 256}, d_v a multiple of 64, chunk in {32, 64, 128}. N >= 1.
+ */
+ret_status_t ret_chunkwise_fwd(const void* q, const void* k, const void* v, void* o, int B, int N, int H, int dk,
+                               int dv, ret_dtype_t in_dt, ret_dtype_t out_dt, const float* gamma,
+                               const double* theta, int64_t pos0, int chunk, const float* state_in,
+                               float* state_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One recurrent (decode) step at absolute position `pos` (blog section 2.1; paper summary Eq. 6):
+ *     S <- gamma S + k'^T v,   o = q' S      (update, then read; the token sees itself)
+ * `state` [B, H, d_k, d_v] fp32 is updated in place. q, k [B, H, d_k], v, o [B, H, d_v].
+ * Supported: d_k in {16, 32, 64, 128, 256}, d_v a multiple of 4 and <= 512.
+ */
+ret_status_t ret_recurrent_step(const void* q, const void* k, const void* v, void* o, float* state, int B, int H,
+                                int dk, int dv, ret_dtype_t in_dt, ret_dtype_t out_dt, const float* gamma,
+                                const double* theta, int64_t pos, void* stream);
+
+/*
+ * Kernel timing for measurement tools. While enabled, every kernel the library launches is bracketed by a
+ * pair of HIP events on the launch stream. ret_timing_query synchronises those events and returns the total
+ * milliseconds and launch count recorded for kernels whose name equals `kernel` ("" or NULL = all).
+ * ret_timing_reset drops the records. Kernel names: "ret_chunk_full", "ret_chunk_local",
+ * "ret_segment_scan", "ret_parallel", "ret_recurrent_step". Not for use while kernels are being captured
+ * into a graph.
+ */
+int ret_timing_enable(int on);
+int ret_timing_query(const char* kernel, double* total_ms, int64_t* launches);
+void ret_timing_reset(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RETENTION_H */

@@ -1,0 +1,345 @@
+// C ABI of libretention.so: argument validation, kernel selection, segment planning, launches and the
+// optional kernel-timing records. Sources for each operation are cited in retention.h.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "retention.h"
+
+// =====================================================================================================
+// Host side: validation, kernel selection, launches, timing records.
+// =====================================================================================================
+namespace {
+
+using namespace ret;
+
+thread_local std::string g_last_error;
+
+ret_status_t fail(ret_status_t st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+ret_status_t fail(ret_status_t st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+// ---- timing records ----
+struct TimingRec {
+    const char* name;
+    hipEvent_t start, stop;
+};
+std::mutex g_timing_mu;
+bool g_timing_on = false;
+std::vector<TimingRec> g_timing;
+
+struct LaunchTimer {
+    hipEvent_t start = nullptr, stop = nullptr;
+    hipStream_t stream;
+    const char* name;
+    bool on;
+    LaunchTimer(const char* n, hipStream_t s) : stream(s), name(n) {
+        {
+            std::lock_guard<std::mutex> lk(g_timing_mu);
+            on = g_timing_on;
+        }
+        if (on && hipEventCreate(&start) == hipSuccess && hipEventCreate(&stop) == hipSuccess)
+            hipEventRecord(start, stream);
+        else
+            on = false;
+    }
+    void done() {
+        if (!on) return;
+        hipEventRecord(stop, stream);
+        std::lock_guard<std::mutex> lk(g_timing_mu);
+        g_timing.push_back({name, start, stop});
+    }
+};
+
+ret_status_t launch_status(const char* what) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(RET_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+    return RET_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+ret_status_t check_common(const void* q, const void* k, const void* v, void* o, int B, int N, int H, int dk, int dv,
+                          ret_dtype_t in_dt, ret_dtype_t out_dt, const float* gamma, const double* theta) {
+    if (!q || !k || !v || !o) return fail(RET_ERR_INVALID_ARG, "null q/k/v/o pointer");
+    if (B <= 0 || N <= 0 || H <= 0 || dk <= 0 || dv <= 0)
+        return fail(RET_ERR_INVALID_ARG, "sizes must be positive (B=%d N=%d H=%d dk=%d dv=%d)", B, N, H, dk, dv);
+    if (!gamma) return fail(RET_ERR_INVALID_ARG, "null gamma");
+    if (in_dt != RET_F32 && in_dt != RET_BF16) return fail(RET_ERR_INVALID_ARG, "bad in_dt %d", (int)in_dt);
+    if (out_dt != RET_F32 && out_dt != RET_BF16) return fail(RET_ERR_INVALID_ARG, "bad out_dt %d", (int)out_dt);
+    if (in_dt == RET_F32 && out_dt != RET_F32)
+        return fail(RET_ERR_INVALID_ARG, "F32 input requires F32 output");
+    if (H > kMaxHeads) return fail(RET_ERR_UNSUPPORTED, "H=%d exceeds %d heads", H, kMaxHeads);
+    if ((long long)B * H > 65535) return fail(RET_ERR_UNSUPPORTED, "B*H=%lld exceeds 65535", (long long)B * H);
+    for (int h = 0; h < H; ++h)
+        if (!(gamma[h] > 0.f && gamma[h] <= 1.f))
+            return fail(RET_ERR_INVALID_ARG, "gamma[%d]=%g outside (0, 1]", h, (double)gamma[h]);
+    if (theta) {
+        if (dk % 2) return fail(RET_ERR_INVALID_ARG, "rotation needs an even d_k (got %d)", dk);
+        if (dk / 2 > kMaxPairs) return fail(RET_ERR_UNSUPPORTED, "rotation supports d_k <= %d", 2 * kMaxPairs);
+        for (int i = 0; i < dk / 2; ++i)
+            if (!isfinite(theta[i])) return fail(RET_ERR_INVALID_ARG, "theta[%d] is not finite", i);
+    }
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+        return fail(RET_ERR_INVALID_ARG, "q/k/v/o must be 16-byte aligned");
+    if (o == q || o == k || o == v) return fail(RET_ERR_INVALID_ARG, "o must not alias q, k or v");
+    return RET_OK;
+}
+
+void fill_fwd(FwdArgs& A, const void* q, const void* k, const void* v, void* o, int B, int N, int H, int dk, int dv,
+              ret_dtype_t out_dt, const float* gamma, const double* theta, int64_t pos0) {
+    memset(&A, 0, sizeof(A));
+    A.q = q;
+    A.k = k;
+    A.v = v;
+    A.o = o;
+    A.B = B;
+    A.N = N;
+    A.H = H;
+    A.dk = dk;
+    A.dv = dv;
+    A.out_bf16 = out_dt == RET_BF16;
+    A.rotate = theta != nullptr;
+    A.pos0 = pos0;
+    for (int h = 0; h < H; ++h) A.log2g[h] = (float)log2((double)gamma[h]);
+    if (theta)
+        for (int i = 0; i < dk / 2; ++i) A.theta[i] = theta[i];
+}
+
+// ---- kernel selection ----
+bool pick_chunk(ret_dtype_t in_dt, int dk, int dv, int C, ChunkKernels* out) {
+    if (in_dt == RET_F32) return chunk_kernels_f32(dk, dv, C, out);
+    if (dk == 32 || dk == 64) return chunk_kernels_bf16_small(dk, dv, C, out);
+    if (dk == 128) return chunk_kernels_bf16_128(dk, dv, C, out);
+    if (dk == 256) return chunk_kernels_bf16_256(dk, dv, C, out);
+    return false;
+}
+
+bool pick_parallel(ret_dtype_t in_dt, int dk, int dv, ParKernel* out) {
+    return parallel_kernel_get(in_dt == RET_BF16, dk, dv, out);
+}
+
+// ---- segment heuristic ----
+int env_int(const char* name, int dflt) {
+    const char* s = getenv(name);
+    if (!s || !*s) return dflt;
+    return atoi(s);
+}
+
+// Number of segments per sequence and tokens per segment. Enough workgroups to fill the chip, but segments of
+// at least ~256 tokens so the per-segment state traffic stays small against the segment's own data.
+void plan_segments(int B, int N, int H, int dv, int C, int dvt, int* nseg, int* seg_len) {
+    const long long units = (long long)B * H * ((dv + dvt - 1) / dvt);
+    const int nchunks = (N + C - 1) / C;
+    const int target = env_int("RET_TARGET_WGS", 1024);
+    int g = (int)((target + units - 1) / units);
+    const int forced = env_int("RET_SEGMENTS", 0);
+    if (forced > 0) g = forced;
+    if (g < 1) g = 1;
+    if (g > nchunks) g = nchunks;
+    int spc = (nchunks + g - 1) / g;  // chunks per segment
+    const int min_spc = forced > 0 ? 1 : (256 + C - 1) / C;
+    if (spc < min_spc) spc = min_spc;
+    if (spc > nchunks) spc = nchunks;
+    *seg_len = spc * C;
+    *nseg = (nchunks + spc - 1) / spc;
+}
+
+size_t segment_ws_bytes(int B, int H, int dk, int dv, int nseg) {
+    return nseg > 1 ? (size_t)B * H * nseg * dk * dv * sizeof(float) : 0;
+}
+
+}  // namespace
+
+// =====================================================================================================
+// Exported C ABI
+// =====================================================================================================
+extern "C" {
+
+int ret_abi_version(void) { return RET_ABI_VERSION; }
+
+const char* ret_status_string(int status) {
+    switch (status) {
+        case RET_OK: return "ok";
+        case RET_ERR_INVALID_ARG: return "invalid argument";
+        case RET_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+        case RET_ERR_WORKSPACE: return "workspace too small or missing";
+        case RET_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* ret_last_error(void) { return g_last_error.c_str(); }
+
+ret_status_t ret_parallel_fwd(const void* q, const void* k, const void* v, void* o, int B, int N, int H, int dk,
+                              int dv, ret_dtype_t in_dt, ret_dtype_t out_dt, const float* gamma,
+                              const double* theta, int64_t pos0, void* stream) {
+    ret_status_t st = check_common(q, k, v, o, B, N, H, dk, dv, in_dt, out_dt, gamma, theta);
+    if (st != RET_OK) return st;
+    ParKernel pk;
+    if (!pick_parallel(in_dt, dk, dv, &pk))
+        return fail(RET_ERR_UNSUPPORTED, "parallel form: unsupported d_k=%d d_v=%d for %s input", dk, dv,
+                    in_dt == RET_F32 ? "F32" : "BF16");
+    FwdArgs A;
+    fill_fwd(A, q, k, v, o, B, N, H, dk, dv, out_dt, gamma, theta, pos0);
+    hipStream_t s = (hipStream_t)stream;
+    dim3 grid((N + pk.bq - 1) / pk.bq, dv / pk.dvt, B * H);
+    LaunchTimer tm("ret_parallel", s);
+    hipLaunchKernelGGL(pk.fn, grid, dim3(kThreads), 0, s, A);
+    tm.done();
+    return launch_status("ret_parallel");
+}
+
+size_t ret_chunkwise_workspace_bytes(int B, int N, int H, int dk, int dv, int chunk, ret_dtype_t in_dt) {
+    ChunkKernels ck;
+    if (B <= 0 || N <= 0 || H <= 0 || dk <= 0 || dv <= 0 || chunk <= 0) return 0;
+    if (!pick_chunk(in_dt, dk, dv, chunk, &ck)) return 0;
+    int nseg, seg_len;
+    plan_segments(B, N, H, dv, chunk, ck.dvt, &nseg, &seg_len);
+    return segment_ws_bytes(B, H, dk, dv, nseg);
+}
+
+ret_status_t ret_chunkwise_fwd(const void* q, const void* k, const void* v, void* o, int B, int N, int H, int dk,
+                               int dv, ret_dtype_t in_dt, ret_dtype_t out_dt, const float* gamma,
+                               const double* theta, int64_t pos0, int chunk, const float* state_in,
+                               float* state_out, void* workspace, size_t workspace_bytes, void* stream) {
+    ret_status_t st = check_common(q, k, v, o, B, N, H, dk, dv, in_dt, out_dt, gamma, theta);
+    if (st != RET_OK) return st;
+    if (chunk <= 0) return fail(RET_ERR_INVALID_ARG, "chunk must be positive (got %d)", chunk);
+    if ((state_in && !aligned16(state_in)) || (state_out && !aligned16(state_out)))
+        return fail(RET_ERR_INVALID_ARG, "state buffers must be 16-byte aligned");
+    if (workspace_bytes > 0 && !workspace) return fail(RET_ERR_WORKSPACE, "workspace_bytes > 0 with a null workspace");
+    if (workspace && !aligned16(workspace)) return fail(RET_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    ChunkKernels ck;
+    if (!pick_chunk(in_dt, dk, dv, chunk, &ck))
+        return fail(RET_ERR_UNSUPPORTED, "chunkwise form: unsupported d_k=%d d_v=%d chunk=%d for %s input", dk, dv,
+                    chunk, in_dt == RET_F32 ? "F32" : "BF16");
+    int nseg, seg_len;
+    plan_segments(B, N, H, dv, chunk, ck.dvt, &nseg, &seg_len);
+    // Fewer segments when the workspace given is smaller than the plan's.
+    while (nseg > 1 && segment_ws_bytes(B, H, dk, dv, nseg) > workspace_bytes) {
+        const int nchunks = (N + chunk - 1) / chunk;
+        int spc = seg_len / chunk * 2;
+        if (spc > nchunks) spc = nchunks;
+        seg_len = spc * chunk;
+        nseg = (nchunks + spc - 1) / spc;
+    }
+    if (nseg == 1) seg_len = N;
+
+    FwdArgs A;
+    fill_fwd(A, q, k, v, o, B, N, H, dk, dv, out_dt, gamma, theta, pos0);
+    A.state_in = state_in;
+    A.state_out = state_out;
+    A.ws = (float*)workspace;
+    A.nseg = nseg;
+    A.seg_len = seg_len;
+    hipStream_t s = (hipStream_t)stream;
+    const int ntiles = dv / ck.dvt;
+    if (nseg > 1) {
+        {
+            LaunchTimer tm("ret_chunk_local", s);
+            hipLaunchKernelGGL(ck.local, dim3(nseg - 1, ntiles, B * H), dim3(kThreads), 0, s, A);
+            tm.done();
+            if ((st = launch_status("ret_chunk_local")) != RET_OK) return st;
+        }
+        {
+            const long long per4 = (long long)dk * dv / 4;
+            LaunchTimer tm("ret_segment_scan", s);
+            hipLaunchKernelGGL(segment_scan_get(), dim3((unsigned)((per4 + kThreads - 1) / kThreads), B * H),
+                               dim3(kThreads), 0, s, A);
+            tm.done();
+            if ((st = launch_status("ret_segment_scan")) != RET_OK) return st;
+        }
+    }
+    LaunchTimer tm("ret_chunk_full", s);
+    hipLaunchKernelGGL(ck.full, dim3(nseg, ntiles, B * H), dim3(kThreads), 0, s, A);
+    tm.done();
+    return launch_status("ret_chunk_full");
+}
+
+ret_status_t ret_recurrent_step(const void* q, const void* k, const void* v, void* o, float* state, int B, int H,
+                                int dk, int dv, ret_dtype_t in_dt, ret_dtype_t out_dt, const float* gamma,
+                                const double* theta, int64_t pos, void* stream) {
+    ret_status_t st = check_common(q, k, v, o, B, 1, H, dk, dv, in_dt, out_dt, gamma, theta);
+    if (st != RET_OK) return st;
+    if (!state) return fail(RET_ERR_INVALID_ARG, "null state");
+    if (!aligned16(state)) return fail(RET_ERR_INVALID_ARG, "state must be 16-byte aligned");
+    if (dv % 4 || dv > 512) return fail(RET_ERR_UNSUPPORTED, "decode step: d_v must be a multiple of 4, <= 512");
+    StepArgs A;
+    memset(&A, 0, sizeof(A));
+    A.q = q;
+    A.k = k;
+    A.v = v;
+    A.o = o;
+    A.state = state;
+    A.B = B;
+    A.H = H;
+    A.dk = dk;
+    A.dv = dv;
+    A.in_bf16 = in_dt == RET_BF16;
+    A.out_bf16 = out_dt == RET_BF16;
+    A.rotate = theta != nullptr;
+    A.pos = pos;
+    for (int h = 0; h < H; ++h) A.gamma[h] = gamma[h];
+    if (theta)
+        for (int i = 0; i < dk / 2; ++i) A.theta[i] = theta[i];
+    step_kernel_t fn = step_kernel_get(dk);
+    if (!fn) return fail(RET_ERR_UNSUPPORTED, "decode step: d_k=%d not in {16,32,64,128,256}", dk);
+    hipStream_t s = (hipStream_t)stream;
+    LaunchTimer tm("ret_recurrent_step", s);
+    hipLaunchKernelGGL(fn, dim3((dv + 63) / 64, B * H), dim3(kThreads), 0, s, A);
+    tm.done();
+    return launch_status("ret_recurrent_step");
+}
+
+int ret_timing_enable(int on) {
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    int prev = g_timing_on;
+    g_timing_on = on != 0;
+    return prev;
+}
+
+int ret_timing_query(const char* kernel, double* total_ms, int64_t* launches) {
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    double tot = 0.0;
+    int64_t n = 0;
+    for (auto& r : g_timing) {
+        if (kernel && *kernel && strcmp(kernel, r.name) != 0) continue;
+        if (hipEventSynchronize(r.stop) != hipSuccess) return RET_ERR_HIP;
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess) return RET_ERR_HIP;
+        tot += ms;
+        ++n;
+    }
+    if (total_ms) *total_ms = tot;
+    if (launches) *launches = n;
+    return RET_OK;
+}
+
+void ret_timing_reset(void) {
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    for (auto& r : g_timing) {
+        hipEventDestroy(r.start);
+        hipEventDestroy(r.stop);
+    }
+    g_timing.clear();
+}
+
+}  // extern "C"

@@ -1,0 +1,90 @@
+"""The C-ABI library loads, exports every entry point include/retention.h declares, and rejects invalid
+arguments on the host before touching a GPU (no GPU needed; no compute call is made)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "retention.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ret_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from linear_recurrent_sequence_amd import retention
+    return retention.load()
+
+
+def test_header_declares_the_three_operations():
+    names = _declared()
+    for fn in ("ret_chunkwise_fwd", "ret_recurrent_step", "ret_parallel_fwd", "ret_chunkwise_workspace_bytes"):
+        assert fn in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared():
+        assert hasattr(lib, name), "libretention.so does not export %s" % name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.ret_abi_version() == 1
+    assert lib.ret_status_string(0) == b"ok"
+    assert lib.ret_status_string(-2) == b"unsupported shape or dtype"
+
+
+def _call_chunk(lib, **kw):
+    a = dict(q=16, k=32, v=48, o=64, B=1, N=64, H=2, dk=64, dv=64, ind=1, outd=1, gamma=[0.9, 0.99], theta=None,
+             pos0=0, chunk=64, sin=None, sout=None, ws=None, wsb=0)
+    a.update(kw)
+    g = np.asarray(a["gamma"], np.float32)
+    th = None if a["theta"] is None else np.asarray(a["theta"], np.float64)
+    return lib.ret_chunkwise_fwd(a["q"], a["k"], a["v"], a["o"], a["B"], a["N"], a["H"], a["dk"], a["dv"],
+                                 a["ind"], a["outd"], g.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
+                                 None if th is None else th.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+                                 a["pos0"], a["chunk"], a["sin"], a["sout"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1),                 # null pointer
+    (dict(N=0), -1),                    # empty sequence
+    (dict(gamma=[0.9, 1.5]), -1),       # gamma outside (0, 1]
+    (dict(gamma=[0.9, 0.0]), -1),
+    (dict(gamma=[0.9, float("nan")]), -1),
+    (dict(q=8), -1),                    # misaligned
+    (dict(o=16), -1),                   # o aliases q
+    (dict(ind=0, outd=1), -1),          # F32 input with BF16 output
+    (dict(chunk=0), -1),
+    (dict(dk=63, theta=[0.1] * 31), -1),  # odd d_k with rotation
+    (dict(dk=48), -2),                  # no instance for d_k = 48
+    (dict(dv=96), -2),                  # bf16 d_v must be a multiple of 64
+    (dict(chunk=48), -2),
+    (dict(wsb=1024), -3),               # workspace bytes without a workspace
+])
+def test_chunkwise_rejects_invalid_arguments(lib, kw, status):
+    assert _call_chunk(lib, **kw) == status
+    assert lib.ret_last_error() != b""
+
+
+def test_workspace_query(lib):
+    # one (b, h) with a long sequence is split into segments; many short sequences are not
+    n_long = lib.ret_chunkwise_workspace_bytes(1, 65536, 8, 128, 128, 128, 1)
+    assert n_long > 0 and n_long % (8 * 128 * 128 * 4) == 0
+    assert lib.ret_chunkwise_workspace_bytes(128, 512, 8, 64, 64, 64, 1) == 0
+    assert lib.ret_chunkwise_workspace_bytes(1, 64, 8, 48, 64, 64, 1) == 0  # unsupported shape: 0
+
+
+def test_step_and_parallel_reject_invalid_arguments(lib):
+    g = np.asarray([0.9], np.float32).ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+    assert lib.ret_recurrent_step(16, 32, 48, 64, None, 1, 1, 64, 64, 1, 1, g, None, 0, None) == -1
+    assert lib.ret_recurrent_step(16, 32, 48, 64, 80, 1, 1, 64, 66, 1, 1, g, None, 0, None) == -2
+    assert lib.ret_recurrent_step(16, 32, 48, 64, 80, 1, 1, 48, 64, 1, 1, g, None, 0, None) == -2
+    assert lib.ret_parallel_fwd(16, 32, 48, 64, 1, 8, 1, 48, 64, 1, 1, g, None, 0, None) == -2
+    assert lib.ret_parallel_fwd(16, 32, 48, 64, 1, -1, 1, 64, 64, 1, 1, g, None, 0, None) == -1

@@ -1,0 +1,248 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the fp64 oracle on the same seeded inputs.
+
+Bar (max|gpu - oracle| / max|oracle| over the whole tensor): 1e-5 for fp32 inputs, 2e-2 for bf16 inputs
+with fp32 accumulation. Outputs and final states are both checked.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from linear_recurrent_sequence_amd import workloads as W
+from tests.conftest import print_case
+from tests.helpers import empty_out, rel_err, to_dev, to_host, tol
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def R():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from linear_recurrent_sequence_amd import retention
+    retention.load(build_if_missing=True)
+    return retention
+
+
+def _gpu_chunkwise(R, q, k, v, w_dtype, gamma, chunk, theta=None, pos0=0, s_in=None, dv=None, out_dtype=None):
+    import torch
+    qd, kd, vd = to_dev(q, w_dtype), to_dev(k, w_dtype), to_dev(v, w_dtype)
+    B, N, H, dk = q.shape
+    dv = v.shape[3]
+    o = empty_out((B, N, H, dv), out_dtype or w_dtype)
+    sin = None if s_in is None else torch.from_numpy(np.ascontiguousarray(s_in, np.float32)).cuda()
+    sout = torch.empty((B, H, dk, dv), dtype=torch.float32, device="cuda")
+    ws = R.chunkwise_workspace(qd, vd, chunk)
+    R.ret_chunkwise_fwd(qd, kd, vd, o, gamma, chunk, theta=theta, pos0=pos0, state_in=sin, state_out=sout,
+                        workspace=ws)
+    torch.cuda.synchronize()
+    return to_host(o), to_host(sout)
+
+
+# ---------------------------------------------------------------------------------------------------
+# Workload 1: fp32, B=1 N=64 H=8 d=16, no rotation; parallel, recurrent and chunkwise (chunk 16).
+# ---------------------------------------------------------------------------------------------------
+def test_workload1_all_three_forms(R):
+    import torch
+    w = W.WORKLOADS[1]
+    q, k, v, _ = W.make_qkv(w)
+    print_case("workload1", w)
+    o_ref, s_ref = oracle.recurrent(q, k, v, w.gamma)
+    # chunkwise
+    o, s = _gpu_chunkwise(R, q, k, v, "f32", w.gamma, w.chunk)
+    assert rel_err(o, o_ref) <= 1e-5 and rel_err(s, s_ref) <= 1e-5, (rel_err(o, o_ref), rel_err(s, s_ref))
+    # parallel
+    qd, kd, vd = to_dev(q, "f32"), to_dev(k, "f32"), to_dev(v, "f32")
+    op = empty_out(v.shape, "f32")
+    R.ret_parallel_fwd(qd, kd, vd, op, w.gamma)
+    torch.cuda.synchronize()
+    assert rel_err(to_host(op), o_ref) <= 1e-5
+    # recurrent: 64 single-token steps
+    state = torch.zeros((1, 8, 16, 16), dtype=torch.float32, device="cuda")
+    outs = []
+    for n in range(w.N):
+        on = empty_out((1, 8, 16), "f32")
+        R.ret_recurrent_step(qd[:, n].contiguous(), kd[:, n].contiguous(), vd[:, n].contiguous(), on, state,
+                             w.gamma, pos=n)
+        outs.append(on)
+    torch.cuda.synchronize()
+    orr = np.stack([to_host(x) for x in outs], axis=1)
+    assert rel_err(orr, o_ref) <= 1e-5 and rel_err(to_host(state), s_ref) <= 1e-5
+
+
+# ---------------------------------------------------------------------------------------------------
+# Multi-tile shapes with ragged tails, rotation, pos0 and an initial state.
+# ---------------------------------------------------------------------------------------------------
+SMALL = [
+    # dtype, B, N, H, dk, dv, chunk, rotate, pos0, state_in, segments (None = planner)
+    ("f32", 2, 200, 3, 32, 48, 32, True, 5, True, None),
+    ("f32", 1, 77, 2, 64, 16, 64, True, 0, False, None),
+    ("f32", 1, 150, 2, 16, 32, 16, False, 0, True, 3),
+    ("bf16", 2, 333, 3, 64, 128, 64, True, 11, True, None),
+    ("bf16", 1, 700, 2, 128, 64, 128, True, 0, True, 3),
+    ("bf16", 1, 300, 2, 32, 64, 32, True, 3, False, 4),
+    ("bf16", 1, 260, 1, 256, 128, 128, True, 0, True, 2),
+    ("bf16", 3, 1, 2, 64, 64, 64, True, 9, True, None),      # one token
+    ("bf16", 1, 45, 2, 64, 64, 64, False, 0, False, None),   # shorter than one chunk
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "%s-B%d-N%d-H%d-dk%d-dv%d-C%d" % c[:7])
+def test_chunkwise_small(R, case, monkeypatch):
+    dt, B, N, H, dk, dv, C, rot, pos0, with_state, segs = case
+    print_case("chunkwise_small", case)
+    if segs is not None:
+        monkeypatch.setenv("RET_SEGMENTS", str(segs))
+    rng = np.random.default_rng(100 + N)
+    scale = 1.0 if dt == "f32" else 8.0
+    q = W.normal(rng, (B, N, H, dk), scale, dt)
+    k = W.normal(rng, (B, N, H, dk), scale, dt)
+    v = W.normal(rng, (B, N, H, dv), scale, dt)
+    s0 = rng.standard_normal((B, H, dk, dv)).astype(np.float32) if with_state else None
+    gamma = W.gamma_schedule(H)
+    theta = W.theta_schedule(dk) if rot else None
+    o_ref, s_ref = oracle.chunkwise(q, k, v, gamma, C, theta=theta, pos0=pos0, state_in=s0)
+    o, s = _gpu_chunkwise(R, q, k, v, dt, gamma, C, theta=theta, pos0=pos0, s_in=s0)
+    eo, es = rel_err(o, o_ref), rel_err(s, s_ref)
+    print("  err o=%.3g state=%.3g" % (eo, es))
+    assert eo <= tol(dt) and es <= tol(dt), (eo, es)
+
+
+@pytest.mark.parametrize("dt,dk,dv", [("f32", 32, 32), ("bf16", 64, 64), ("bf16", 256, 128)])
+def test_parallel_small(R, dt, dk, dv):
+    import torch
+    print_case("parallel_small", dt, dk, dv)
+    rng = np.random.default_rng(7)
+    B, N, H = 2, 150, 2
+    scale = 1.0 if dt == "f32" else 8.0
+    q = W.normal(rng, (B, N, H, dk), scale, dt)
+    k = W.normal(rng, (B, N, H, dk), scale, dt)
+    v = W.normal(rng, (B, N, H, dv), scale, dt)
+    gamma = np.array([0.9, 0.999], np.float32)
+    theta = W.theta_schedule(dk)
+    ref = oracle.parallel(q, k, v, gamma, theta=theta, pos0=3)
+    o = empty_out((B, N, H, dv), dt)
+    R.ret_parallel_fwd(to_dev(q, dt), to_dev(k, dt), to_dev(v, dt), o, gamma, theta=theta, pos0=3)
+    torch.cuda.synchronize()
+    assert rel_err(to_host(o), ref) <= tol(dt)
+
+
+@pytest.mark.parametrize("dt,dk,dv", [("f32", 16, 16), ("f32", 64, 36), ("bf16", 64, 64), ("bf16", 128, 128),
+                                      ("bf16", 256, 200)])
+def test_recurrent_steps_small(R, dt, dk, dv):
+    import torch
+    print_case("recurrent_small", dt, dk, dv)
+    rng = np.random.default_rng(9)
+    B, H, n = 3, 2, 20
+    scale = 1.0 if dt == "f32" else 8.0
+    q = W.normal(rng, (B, n, H, dk), scale, dt)
+    k = W.normal(rng, (B, n, H, dk), scale, dt)
+    v = W.normal(rng, (B, n, H, dv), scale, dt)
+    s0 = rng.standard_normal((B, H, dk, dv)).astype(np.float32)
+    gamma = np.array([0.95, 1.0], np.float32)
+    theta = W.theta_schedule(dk)
+    o_ref, s_ref = oracle.recurrent(q, k, v, gamma, theta=theta, pos0=1000, state_in=s0)
+    qd, kd, vd = to_dev(q, dt), to_dev(k, dt), to_dev(v, dt)
+    state = torch.from_numpy(s0).cuda()
+    outs = []
+    for t in range(n):
+        o = empty_out((B, H, dv), dt)
+        R.ret_recurrent_step(qd[:, t].contiguous(), kd[:, t].contiguous(), vd[:, t].contiguous(), o, state, gamma,
+                             pos=1000 + t, theta=theta)
+        outs.append(o)
+    torch.cuda.synchronize()
+    got = np.stack([to_host(x) for x in outs], axis=1)
+    assert rel_err(got, o_ref) <= tol(dt) and rel_err(to_host(state), s_ref) <= tol(dt)
+
+
+# ---------------------------------------------------------------------------------------------------
+# Full-size workloads 2-5.
+# ---------------------------------------------------------------------------------------------------
+def test_workload2_chunkwise_full(R):
+    w = W.WORKLOADS[2]
+    print_case("workload2", w)
+    q, k, v, _ = W.make_qkv(w)
+    o_ref, s_ref = oracle.chunkwise(q, k, v, w.gamma, w.chunk, theta=w.theta)
+    o, s = _gpu_chunkwise(R, q, k, v, w.dtype, w.gamma, w.chunk, theta=w.theta)
+    eo, es = rel_err(o, o_ref), rel_err(s, s_ref)
+    print("  err o=%.3g state=%.3g" % (eo, es))
+    assert eo <= 2e-2 and es <= 2e-2
+
+
+def test_workload3_prefill_then_1024_decode_steps(R):
+    import torch
+    w = W.WORKLOADS[3]
+    print_case("workload3", w)
+    q, k, v, rng = W.make_qkv(w)
+    steps = [W.make_step(w, rng) for _ in range(w.steps)]
+    sq = np.stack([s[0] for s in steps], axis=1)
+    sk = np.stack([s[1] for s in steps], axis=1)
+    sv = np.stack([s[2] for s in steps], axis=1)
+    _, s_pre = oracle.chunkwise(q, k, v, w.gamma, w.chunk, theta=w.theta)
+    o_ref, s_ref = oracle.recurrent(sq, sk, sv, w.gamma, theta=w.theta, pos0=w.prefill, state_in=s_pre)
+    # GPU: chunkwise prefill, then the decode steps from the GPU's own state
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    o = empty_out(v.shape, "bf16")
+    state = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    R.ret_chunkwise_fwd(qd, kd, vd, o, w.gamma, w.chunk, theta=w.theta, state_out=state,
+                        workspace=R.chunkwise_workspace(qd, vd, w.chunk))
+    torch.cuda.synchronize()
+    assert rel_err(to_host(state), s_pre) <= 2e-2
+    sqd = to_dev(np.ascontiguousarray(sq.transpose(1, 0, 2, 3)), "bf16")
+    skd = to_dev(np.ascontiguousarray(sk.transpose(1, 0, 2, 3)), "bf16")
+    svd = to_dev(np.ascontiguousarray(sv.transpose(1, 0, 2, 3)), "bf16")
+    outs = torch.empty((w.steps, w.B, w.H, w.dv), dtype=torch.bfloat16, device="cuda")
+    for t in range(w.steps):
+        R.ret_recurrent_step(sqd[t], skd[t], svd[t], outs[t], state, w.gamma, pos=w.prefill + t, theta=w.theta)
+    torch.cuda.synchronize()
+    got = to_host(outs).transpose(1, 0, 2, 3)
+    eo, es = rel_err(got, o_ref), rel_err(to_host(state), s_ref)
+    print("  err o=%.3g state=%.3g" % (eo, es))
+    assert eo <= 2e-2 and es <= 2e-2
+
+
+def test_workload4_chunkwise_full(R):
+    w = W.WORKLOADS[4]
+    print_case("workload4", w)
+    q, k, v, _ = W.make_qkv(w)
+    o_ref, s_ref = oracle.chunkwise(q, k, v, w.gamma, w.chunk, theta=w.theta)
+    o, s = _gpu_chunkwise(R, q, k, v, w.dtype, w.gamma, w.chunk, theta=w.theta)
+    eo, es = rel_err(o, o_ref), rel_err(s, s_ref)
+    print("  err o=%.3g state=%.3g" % (eo, es))
+    assert eo <= 2e-2 and es <= 2e-2
+
+
+def test_workload5_long_sequence_then_256_decode_steps(R):
+    import torch
+    w = W.WORKLOADS[5]
+    print_case("workload5", w)
+    q, k, v, rng = W.make_qkv(w)
+    steps = [W.make_step(w, rng) for _ in range(w.steps)]
+    o_ref, s_ref = oracle.chunkwise(q, k, v, w.gamma, w.chunk, theta=w.theta)
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    del q, k, v
+    o = empty_out(o_ref.shape, "bf16")
+    state = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    R.ret_chunkwise_fwd(qd, kd, vd, o, w.gamma, w.chunk, theta=w.theta, state_out=state,
+                        workspace=R.chunkwise_workspace(qd, vd, w.chunk))
+    torch.cuda.synchronize()
+    eo, es = rel_err(to_host(o), o_ref), rel_err(to_host(state), s_ref)
+    print("  chunkwise err o=%.3g state=%.3g" % (eo, es))
+    assert eo <= 2e-2 and es <= 2e-2
+    del o_ref
+    sq = np.stack([s[0] for s in steps], axis=1)
+    sk = np.stack([s[1] for s in steps], axis=1)
+    sv = np.stack([s[2] for s in steps], axis=1)
+    od_ref, sd_ref = oracle.recurrent(sq, sk, sv, w.gamma, theta=w.theta, pos0=w.N, state_in=s_ref)
+    outs = []
+    for t in range(w.steps):
+        ot = empty_out((w.B, w.H, w.dv), "bf16")
+        R.ret_recurrent_step(to_dev(sq[:, t], "bf16"), to_dev(sk[:, t], "bf16"), to_dev(sv[:, t], "bf16"), ot, state,
+                             w.gamma, pos=w.N + t, theta=w.theta)
+        outs.append(ot)
+    torch.cuda.synchronize()
+    got = np.stack([to_host(x) for x in outs], axis=1)
+    ed, esd = rel_err(got, od_ref), rel_err(to_host(state), sd_ref)
+    print("  decode err o=%.3g state=%.3g" % (ed, esd))
+    assert ed <= 2e-2 and esd <= 2e-2
