@@ -1,0 +1,292 @@
+#!/usr/bin/env python3
+"""Benchmark of the retention hot path on one MI355X.
+
+A step is one ret_chunkwise_fwd call over the d_model=512 retention-layer workload (B=8, N=2048, H=8,
+d_k=d_v=64, chunk 64, bf16 inputs/outputs, xPos rotation, fp32 state out): tokens/s = B*N / step time,
+with inputs resident in HBM. The same JSON line carries the batched-decode workload (B=128, H=8, d=64,
+fp32 state, 1024 single-token ret_recurrent_step calls replayed from a HIP graph) in steps/s, the roofline
+of each path's dominant kernel (per-launch HIP-event durations recorded by the library over the timed
+region), and the fp64 CPU oracle timed on this host.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2|4|5] [--no-decode]
+                       [--no-cpu-baseline] [--copy-calibration]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+METRIC = "retention fwd tokens/sec (chunkwise) + decode steps/sec; % MFMA / HBM peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def source_digest() -> str:
+    """Digest of the HIP sources; counter-based traffic figures are only valid for the sources they came from."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "linear_recurrent_sequence_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def chunk_algorithmic(w, in_bytes=2, out_bytes=2):
+    """Bytes and FLOPs the chunkwise op must move / perform for one call over workload w.
+    Bytes: read q, k, v once, write o once, write the fp32 final state.
+    FLOPs per (token, head): causal minimum (C+1)(dk+dv) + 4 dk dv, and the pages' full-block
+    count 2C(dk+dv) + 4 dk dv (chunkwise cost analysis)."""
+    toks = w.B * w.N * w.H
+    nbytes = toks * ((2 * w.dk + w.dv) * in_bytes + w.dv * out_bytes) + w.B * w.H * w.dk * w.dv * 4
+    C = w.chunk
+    f_causal = toks * ((C + 1) * (w.dk + w.dv) + 4 * w.dk * w.dv)
+    f_pages = toks * (2 * C * (w.dk + w.dv) + 4 * w.dk * w.dv)
+    return nbytes, f_causal, f_pages
+
+
+def decode_algorithmic(B, H, dk, dv, in_bytes=2, out_bytes=2):
+    """Per decode step: read + write the fp32 state, read q, k, v, write o; 5 flops per state element."""
+    nbytes = B * H * (2 * dk * dv * 4 + (2 * dk + dv) * in_bytes + dv * out_bytes)
+    return nbytes, B * H * 5 * dk * dv
+
+
+def load_traffic(kernel: str, workload: str):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("workload") != workload or rec.get("source_digest") != source_digest():
+        return None
+    fetch = rec["fetch_kib_per_launch"] * 1024.0 / rec["copy_factor_fetch"]
+    write = rec["write_kib_per_launch"] * 1024.0 / rec["copy_factor_write"]
+    return fetch + write
+
+
+def bench_chunkwise(R, W, torch, wid, steps, warmup):
+    import numpy as np
+    w = W.WORKLOADS[wid]
+    q, k, v, _ = W.make_qkv(w)
+    dev = lambda x: torch.from_numpy(x).to(torch.bfloat16).cuda()
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    del q, k, v
+    o = torch.empty((w.B, w.N, w.H, w.dv), dtype=torch.bfloat16, device="cuda")
+    state = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    ws = R.chunkwise_workspace(qd, vd, w.chunk)
+
+    def step():
+        R.ret_chunkwise_fwd(qd, kd, vd, o, w.gamma, w.chunk, theta=w.theta, state_out=state, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    R.timing_reset()
+    R.timing_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    R.timing_enable(False)
+    ms_step = e0.elapsed_time(e1) / steps
+    kernels = {}
+    for name in ("ret_chunk_local", "ret_segment_scan", "ret_chunk_full"):
+        tot, n = R.timing_query(name)
+        if n:
+            kernels[name] = {"avg_us": 1e3 * tot / n, "launches": n}
+    R.timing_reset()
+    # second timed pass without the per-kernel events, for the step time itself
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_clean = e0.elapsed_time(e1) / steps
+    return w, ms_step, ms_clean, kernels, ws
+
+
+def bench_decode(R, W, torch, steps_graph=1024, reps=3):
+    import numpy as np
+    w = W.WORKLOADS[3]
+    rng = np.random.default_rng(w.seed)
+    q, k, v, rng = W.make_qkv(w, rng)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).cuda()
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    o = torch.empty((w.B, w.N, w.H, w.dv), dtype=torch.bfloat16, device="cuda")
+    state = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    R.ret_chunkwise_fwd(qd, kd, vd, o, w.gamma, w.chunk, theta=w.theta, state_out=state,
+                        workspace=R.chunkwise_workspace(qd, vd, w.chunk))
+    del qd, kd, vd, o
+    # per-step inputs drawn step by step (q, k, v), as the workload defines them
+    sq = np.empty((steps_graph, w.B, w.H, w.dk), np.float32)
+    sk = np.empty_like(sq)
+    sv = np.empty((steps_graph, w.B, w.H, w.dv), np.float32)
+    for t in range(steps_graph):
+        sq[t], sk[t], sv[t] = W.make_step(w, rng)
+    sqd, skd, svd = dev(sq), dev(sk), dev(sv)
+    outs = torch.empty((steps_graph, w.B, w.H, w.dv), dtype=torch.bfloat16, device="cuda")
+    theta = w.theta
+
+    def run_steps():
+        for t in range(steps_graph):
+            R.ret_recurrent_step(sqd[t], skd[t], svd[t], outs[t], state, w.gamma, pos=w.prefill + t, theta=theta)
+
+    # kernel durations from per-launch events (eager launches)
+    run_steps()
+    torch.cuda.synchronize()
+    R.timing_reset()
+    R.timing_enable(True)
+    run_steps()
+    torch.cuda.synchronize()
+    R.timing_enable(False)
+    tot, n = R.timing_query("ret_recurrent_step")
+    R.timing_reset()
+    kernel_us = 1e3 * tot / n
+    # steps/s from a captured graph of the whole decode loop
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            run_steps()
+    torch.cuda.current_stream().wait_stream(s)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = None
+    for _ in range(reps):
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    us_step = 1e3 * best / steps_graph
+    return w, us_step, kernel_us
+
+
+def cpu_baseline(W, wid):
+    """The fp64 oracle's chunkwise form on this host, over the whole workload (median of 3)."""
+    import oracle
+    w = W.WORKLOADS[wid]
+    q, k, v, _ = W.make_qkv(w)
+    threads = min(oracle.default_threads(), w.B * w.H)
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        oracle.chunkwise(q, k, v, w.gamma, w.chunk, theta=w.theta, threads=threads)
+        times.append(time.perf_counter() - t0)
+    t = sorted(times)[1]
+    return {"value": w.B * w.N / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "whole %s workload (B=%d N=%d H=%d), fp64 chunkwise form, median of 3 runs of %.2f s"
+                      % (w.name, w.B, w.N, w.H, t)}
+
+
+def copy_calibration(torch):
+    """A plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    n = 256 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=2, choices=[2, 4, 5])
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from linear_recurrent_sequence_amd import retention as R
+    from linear_recurrent_sequence_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    R.load(build_if_missing=True)
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
+
+    w, ms_step, ms_clean, kernels, ws = bench_chunkwise(R, W, torch, args.workload, args.steps, args.warmup)
+    nbytes, f_causal, f_pages = chunk_algorithmic(w)
+    tokens = w.B * w.N
+    dom = max(kernels, key=lambda n: kernels[n]["avg_us"] * kernels[n]["launches"])
+    dom_us = kernels[dom]["avg_us"]
+    achieved = nbytes / (dom_us * 1e-6) / 1e9
+    traffic = load_traffic(dom, w.name)
+    result = {
+        "metric": METRIC,
+        "value": tokens / (ms_clean * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_clean,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "%s: B=%d N=%d H=%d d_k=%d d_v=%d chunk=%d, bf16 in/out, fp32 state, xPos rotation"
+                               % (w.name, w.B, w.N, w.H, w.dk, w.dv, w.chunk),
+                   "global_batch": w.B, "seq_len": w.N},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": dom,
+                     "kernel_avg_us": dom_us, "alg_bytes_per_launch": nbytes},
+        "chunkwise": {
+            "ms_per_step_with_kernel_events": ms_step,
+            "kernels": kernels,
+            "step_hbm_frac": nbytes / (ms_clean * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "tflops_causal": f_causal / (ms_clean * 1e-3) / 1e12,
+            "tflops_pages_count": f_pages / (ms_clean * 1e-3) / 1e12,
+            "mfma_frac_causal": f_causal / (ms_clean * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "workspace_bytes": 0 if ws is None else ws.numel(),
+        },
+    }
+    if not args.no_decode:
+        dw, us_step, kernel_us = bench_decode(R, W, torch)
+        db, dflops = decode_algorithmic(dw.B, dw.H, dw.dk, dw.dv)
+        ach = db / (kernel_us * 1e-6) / 1e9
+        result["decode"] = {
+            "workload": "%s: B=%d H=%d d_k=%d d_v=%d, fp32 state, bf16 q/k/v/o, %d steps from a %d-token prefill, "
+                        "HIP graph" % (dw.name, dw.B, dw.H, dw.dk, dw.dv, dw.steps, dw.prefill),
+            "steps_per_s": 1e6 / us_step, "tokens_per_s": dw.B * 1e6 / us_step, "us_per_step": us_step,
+            "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": ach / HBM_PEAK_GBS, "traffic": load_traffic("ret_recurrent_step", dw.name),
+                         "kernel": "ret_recurrent_step", "kernel_avg_us": kernel_us, "alg_bytes_per_launch": db},
+            "step_hbm_frac": db / (us_step * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(W, args.workload)
+    result["context"] = ("pages' figures (whole 6.7B model, A100-80GB, vanilla PyTorch): 8.4x faster decoding and "
+                         "70% less memory than a KV-cached Transformer at 8k; not comparable to this kernel metric")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -35,7 +35,8 @@ struct Tri {
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // ---------------------------------------------------------------------------------------------------
-// chunk_full: one workgroup per (segment, d_v tile, b*H + h).
+// chunk_full: one workgroup per (segment, d_v tile, b*H + h). The segment's chunks are processed in stages
+// (chunk, d_k slice); the global loads of stage i+1 are issued before stage i is computed.
 // ---------------------------------------------------------------------------------------------------
 template <class E, int DK, int C, int DVT>
 struct FullCfg {
@@ -45,6 +46,7 @@ struct FullCfg {
     static constexpr int LDQ = KS + E::PAD;          // sQ, sK rows
     static constexpr int LDC = C + E::PAD;           // sKc, sVc, sP rows (token index contiguous)
     static constexpr int LDR = DK + E::PAD;          // sRt rows (d_k contiguous)
+    static constexpr int LDO = DVT + 8;              // output tile rows (elements of the output type)
     static constexpr int NB = C / 16;                // row/col blocks of a chunk
     static constexpr int NDV = DVT / 16;             // d_v blocks
     static constexpr int NKB = DK / 16;              // d_k blocks
@@ -54,8 +56,14 @@ struct FullCfg {
     static constexpr int NO_W = (NO + kWaves - 1) / kWaves;
     static constexpr int NR = NKB * NDV;             // R tiles
     static constexpr int NR_W = (NR + kWaves - 1) / kWaves;
+    static constexpr int UQ = (C / 8) * (KS / 8);    // staging units of Q (and of K) per slice
+    static constexpr int UV = (C / 8) * (DVT / 8);   // staging units of V (first slice only)
+    static constexpr int NU = (2 * UQ + UV + kThreads - 1) / kThreads;
     static constexpr int SQ = C * LDQ, SKC = KS * LDC, SVC = DVT * LDC, SP = C * LDC, SRT = DVT * LDR;
-    static constexpr int LDS_BYTES = (2 * SQ + SKC + SVC + SP + SRT) * (int)sizeof(st);
+    // Region A holds sQ, sK and sKc while a chunk's slices are computed, then the output tile (fp32 at most).
+    static constexpr int A_STAGE = (2 * SQ + SKC) * (int)sizeof(st), A_OUT = C * LDO * 4;
+    static constexpr int A_BYTES = ((A_STAGE > A_OUT ? A_STAGE : A_OUT) + 15) / 16 * 16;
+    static constexpr int LDS_BYTES = A_BYTES + (SVC + SP + SRT) * (int)sizeof(st);
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     static_assert(C % 16 == 0 && DVT % 16 == 0 && DK % KS == 0 && KS % E::KD == 0 && C % E::KD == 0, "tiling");
 };
@@ -68,9 +76,10 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_full_kernel(FwdArgs a) {
     st* sQ = smem;
     st* sK = sQ + F::SQ;
     st* sKc = sK + F::SQ;
-    st* sVc = sKc + F::SKC;
+    st* sVc = smem + F::A_BYTES / sizeof(st);
     st* sP = sVc + F::SVC;
     st* sRt = sP + F::SP;
+    char* sO = reinterpret_cast<char*>(smem);  // output tile, over region A once a chunk's slices are done
 
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
     const int seg = blockIdx.x, dvt = blockIdx.y, pair = blockIdx.z;
@@ -80,6 +89,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_full_kernel(FwdArgs a) {
     const st* q = (const st*)a.q;
     const st* k = (const st*)a.k;
     const st* v = (const st*)a.v;
+    const int osz = a.out_bf16 ? 2 : 4;
 
     // Scores above the diagonal are never written: keep them zero for the P.V product.
     for (int i = tid; i < F::SP; i += kThreads) sP[i] = (st)0;
@@ -102,7 +112,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_full_kernel(FwdArgs a) {
                 R[i][e] = init[(long long)(rb * 16 + 4 * (lane >> 4) + e) * a.dv + dv0 + cb * 16 + (lane & 15)];
         }
     }
-    // bf16 (or fp32) copy of R, transposed to [d_v][d_k], for the cross product.
+    // Copy of R (operand precision), transposed to [d_v][d_k], for the cross product.
 #pragma unroll
     for (int i = 0; i < F::NR_W; ++i) {
         const int t = w + kWaves * i;
@@ -114,52 +124,112 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_full_kernel(FwdArgs a) {
 
     const long long seg_t0 = (long long)seg * a.seg_len;
     const long long seg_t1 = min((long long)a.N, seg_t0 + a.seg_len);
-    for (long long t0 = seg_t0; t0 < seg_t1; t0 += C) {
-        const int L = (int)min((long long)C, seg_t1 - t0);
-        const float gL = gpow(lg, (float)L);
-        f32x4_t S[F::NS_W], O[F::NO_W];
-#pragma unroll
-        for (int i = 0; i < F::NS_W; ++i) S[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < F::NO_W; ++i) O[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int nst = (int)((seg_t1 - seg_t0 + C - 1) / C) * F::NSL;
+    const long long qk_row0 = ((long long)s.b * a.N) * a.H + s.h;  // token 0 of this (b, h), in rows of d
+    const int rsk = a.H * a.dk, rsv = a.H * a.dv;
 
+    Raw<E> buf[F::NU];
+    auto issue = [&](int i) {
+        const long long t0 = seg_t0 + (long long)(i / F::NSL) * C;
+        const int sl = i % F::NSL;
+        const int L = (int)min((long long)C, seg_t1 - t0);
+        const int total = 2 * F::UQ + (sl == 0 ? F::UV : 0);
 #pragma unroll
-        for (int sl = 0; sl < F::NSL; ++sl) {
-            __syncthreads();  // previous readers of the staging buffers are done; sRt writes are visible
-            stage_qk<E, C, F::KS>(q, k, s, a.dk, t0, L, sl * F::KS, a.theta, a.rotate, a.pos0, lg, sQ, F::LDQ, sK,
-                                  F::LDQ, sKc, F::LDC, tid);
-            if (sl == 0) stage_v<E, C, DVT>(v, s, a.dv, t0, L, dv0, sVc, F::LDC, tid);
-            __syncthreads();
-            // S += Q_s K_s^T over the lower-triangle tiles.
-#pragma unroll
-            for (int rb = 0, t = 0; rb < F::NB; ++rb)
-#pragma unroll
-                for (int cb = 0; cb <= rb; ++cb, ++t)
-                    if (t % kWaves == w)
-                        mma_nt(S[t / kWaves], sQ + rb * 16 * F::LDQ, F::LDQ, sK + cb * 16 * F::LDQ, F::LDQ, F::KS,
-                               lane);
-            // O += Q_s R_s (cross-chunk read of the state carried in from the previous chunk).
-#pragma unroll
-            for (int i = 0; i < F::NO_W; ++i) {
-                const int t = w + kWaves * i;
-                if (t < F::NO) {
-                    const int rb = t / F::NDV, cb = t % F::NDV;
-                    mma_nt(O[i], sQ + rb * 16 * F::LDQ, F::LDQ, sRt + cb * 16 * F::LDR + sl * F::KS, F::LDR, F::KS,
-                           lane);
+        for (int j = 0; j < F::NU; ++j) {
+            const int u = tid + kThreads * j;
+            if (u < total) {
+                const st* base;
+                int rs, tb;
+                if (u < 2 * F::UQ) {
+                    const int x = u < F::UQ ? u : u - F::UQ;
+                    tb = x / (F::KS / 8);
+                    base = (u < F::UQ ? q : k) + (qk_row0 + t0 * a.H) * a.dk + sl * F::KS + (x % (F::KS / 8)) * 8;
+                    rs = rsk;
+                } else {
+                    const int x = u - 2 * F::UQ;
+                    tb = x / (DVT / 8);
+                    base = v + (qk_row0 + t0 * a.H) * a.dv + dv0 + (x % (DVT / 8)) * 8;
+                    rs = rsv;
                 }
+                issue_unit(buf[j], base + (long long)tb * 8 * rs, rs, L - tb * 8);
             }
-            // R_s <- gamma^L R_s + K_s^T (V (.) zeta): zeta is folded into sKc.
+        }
+    };
+    auto commit = [&](int i) {
+        const long long t0 = seg_t0 + (long long)(i / F::NSL) * C;
+        const int sl = i % F::NSL;
+        const int L = (int)min((long long)C, seg_t1 - t0);
+        const int total = 2 * F::UQ + (sl == 0 ? F::UV : 0);
 #pragma unroll
-            for (int i = 0; i < F::NR_W; ++i) {
-                const int t = w + kWaves * i;
-                const int rb = t / F::NDV, cb = t % F::NDV;
-                if (t < F::NR && rb / (F::KS / 16) == sl) {
-                    R[i] *= gL;
-                    mma_nt(R[i], sKc + (rb - sl * (F::KS / 16)) * 16 * F::LDC, F::LDC, sVc + cb * 16 * F::LDC,
-                           F::LDC, C, lane);
+        for (int j = 0; j < F::NU; ++j) {
+            const int u = tid + kThreads * j;
+            if (u < total) {
+                if (u < 2 * F::UQ) {
+                    const int x = u < F::UQ ? u : u - F::UQ;
+                    const int tb = x / (F::KS / 8), db = x % (F::KS / 8);
+                    const int pair0 = (sl * F::KS + db * 8) / 2;
+                    const long long p0 = a.pos0 + t0 + tb * 8;
+                    if (u < F::UQ)
+                        commit_q<E>(buf[j], L - tb * 8, a.rotate, a.theta, pair0, p0, sQ + tb * 8 * F::LDQ + db * 8,
+                                    F::LDQ);
+                    else
+                        commit_k<E>(buf[j], L - tb * 8, a.rotate, a.theta, pair0, p0, lg, L - 1 - tb * 8,
+                                    sK + tb * 8 * F::LDQ + db * 8, F::LDQ, sKc + db * 8 * F::LDC + tb * 8, F::LDC);
+                } else {
+                    const int x = u - 2 * F::UQ;
+                    const int tb = x / (DVT / 8), db = x % (DVT / 8);
+                    commit_v(buf[j], L - tb * 8, sVc + db * 8 * F::LDC + tb * 8, F::LDC);
                 }
             }
         }
+    };
+
+    f32x4_t S[F::NS_W], O[F::NO_W];
+    if (nst > 0) issue(0);
+    for (int i = 0; i < nst; ++i) {
+        const int sl = i % F::NSL;
+        const long long t0 = seg_t0 + (long long)(i / F::NSL) * C;
+        const int L = (int)min((long long)C, seg_t1 - t0);
+        if (sl == 0) {
+#pragma unroll
+            for (int x = 0; x < F::NS_W; ++x) S[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int x = 0; x < F::NO_W; ++x) O[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        __syncthreads();  // staging buffers free; previous copies of R and of the output tile consumed
+        commit(i);
+        if (i + 1 < nst) issue(i + 1);
+        __syncthreads();
+        // S += Q_s K_s^T over the lower-triangle tiles.
+#pragma unroll
+        for (int rb = 0, t = 0; rb < F::NB; ++rb)
+#pragma unroll
+            for (int cb = 0; cb <= rb; ++cb, ++t)
+                if (t % kWaves == w)
+                    mma_nt(S[t / kWaves], sQ + rb * 16 * F::LDQ, F::LDQ, sK + cb * 16 * F::LDQ, F::LDQ, F::KS, lane);
+        // O += Q_s R_s (cross-chunk read of the state carried in from the previous chunk).
+#pragma unroll
+        for (int x = 0; x < F::NO_W; ++x) {
+            const int t = w + kWaves * x;
+            if (t < F::NO) {
+                const int rb = t / F::NDV, cb = t % F::NDV;
+                mma_nt(O[x], sQ + rb * 16 * F::LDQ, F::LDQ, sRt + cb * 16 * F::LDR + sl * F::KS, F::LDR, F::KS, lane);
+            }
+        }
+        // R_s <- gamma^L R_s + K_s^T (V (.) zeta): zeta is folded into sKc.
+        const float gL = gpow(lg, (float)L);
+#pragma unroll
+        for (int x = 0; x < F::NR_W; ++x) {
+            const int t = w + kWaves * x;
+            const int rb = t / F::NDV, cb = t % F::NDV;
+            if (t < F::NR && rb / (F::KS / 16) == sl) {
+                R[x] *= gL;
+                mma_nt(R[x], sKc + (rb - sl * (F::KS / 16)) * 16 * F::LDC, F::LDC, sVc + cb * 16 * F::LDC, F::LDC, C,
+                       lane);
+            }
+        }
+        if (sl != F::NSL - 1) continue;
+
         // Decay mask in registers: P[j][l] = S[j][l] * gamma^(j-l) for l <= j.
 #pragma unroll
         for (int rb = 0, t = 0; rb < F::NB; ++rb)
@@ -177,40 +247,46 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_full_kernel(FwdArgs a) {
                             sP[j * F::LDC + l] = val;
                     }
                 }
-        __syncthreads();
-        // O = (Q R) (.) xi + P V, then store rows j < L.
-        const long long obase = ((long long)s.b * a.N + t0) * a.H + s.h;
+        __syncthreads();  // P complete; all reads of sQ/sK/sRt for this chunk are done
+        // O = (Q R) (.) xi + P V, written to the output tile in LDS.
 #pragma unroll
-        for (int i = 0; i < F::NO_W; ++i) {
-            const int t = w + kWaves * i;
+        for (int x = 0; x < F::NO_W; ++x) {
+            const int t = w + kWaves * x;
             if (t < F::NO) {
                 const int rb = t / F::NDV, cb = t % F::NDV;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) O[i][e] *= gpow(lg, (float)(rb * 16 + 4 * (lane >> 4) + e + 1));
+                for (int e = 0; e < 4; ++e) O[x][e] *= gpow(lg, (float)(rb * 16 + 4 * (lane >> 4) + e + 1));
                 const int kmax = min(C, ((rb + 1) * 16 + E::KD - 1) / E::KD * E::KD);
-                mma_nt(O[i], sP + rb * 16 * F::LDC, F::LDC, sVc + cb * 16 * F::LDC, F::LDC, kmax, lane);
-                const int col = dv0 + cb * 16 + (lane & 15);
+                mma_nt(O[x], sP + rb * 16 * F::LDC, F::LDC, sVc + cb * 16 * F::LDC, F::LDC, kmax, lane);
+                const int col = cb * 16 + (lane & 15);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int j = rb * 16 + 4 * (lane >> 4) + e;
-                    if (j < L) {
-                        const long long off = (obase + (long long)j * a.H) * a.dv + col;
-                        if (a.out_bf16)
-                            store_out((uint16_t*)a.o + off, O[i][e]);
-                        else
-                            store_out((float*)a.o + off, O[i][e]);
-                    }
+                    if (a.out_bf16)
+                        reinterpret_cast<uint16_t*>(sO)[j * F::LDO + col] = f32_to_bf16(O[x][e]);
+                    else
+                        reinterpret_cast<float*>(sO)[j * F::LDO + col] = O[x][e];
                 }
             }
         }
-        // New bf16 copy of R for the next chunk. All reads of the old copy happened before the barrier above.
+        // New operand copy of R for the next chunk.
 #pragma unroll
-        for (int i = 0; i < F::NR_W; ++i) {
-            const int t = w + kWaves * i;
+        for (int x = 0; x < F::NR_W; ++x) {
+            const int t = w + kWaves * x;
             if (t < F::NR) {
                 const int rb = t / F::NDV, cb = t % F::NDV;
-                store4(sRt + (cb * 16 + (lane & 15)) * F::LDR + rb * 16 + 4 * (lane >> 4), R[i]);
+                store4(sRt + (cb * 16 + (lane & 15)) * F::LDR + rb * 16 + 4 * (lane >> 4), R[x]);
             }
+        }
+        __syncthreads();
+        // Coalesced 16-byte stores of the output rows j < L.
+        const int vec = 16 / osz;                  // elements per 16-byte store
+        const int per_row = DVT / vec;
+        char* obase = (char*)a.o + ((qk_row0 + t0 * a.H) * a.dv + dv0) * osz;
+        for (int x = tid; x < L * per_row; x += kThreads) {
+            const int j = x / per_row, c16 = x % per_row;
+            *reinterpret_cast<uint4*>(obase + ((long long)j * a.H * a.dv + c16 * vec) * osz) =
+                *reinterpret_cast<const uint4*>(sO + (j * F::LDO + c16 * vec) * osz);
         }
     }
     // The state after the last token of the sequence.
@@ -239,6 +315,8 @@ struct LocalCfg {
     static constexpr int NDV = DVT / 16, NKB = DK / 16;
     static constexpr int NR = NKB * NDV;
     static constexpr int NR_W = (NR + kWaves - 1) / kWaves;
+    static constexpr int UK = (C / 8) * (DK / 8), UV = (C / 8) * (DVT / 8);
+    static constexpr int NU = (UK + UV + kThreads - 1) / kThreads;
     static constexpr int SKC = DK * LDC, SVC = DVT * LDC;
     static constexpr int LDS_BYTES = (SKC + SVC) * (int)sizeof(st);
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -256,6 +334,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_local_kernel(FwdArgs a) {
     const Seq s{a.N, a.H, pair / a.H, pair % a.H};
     const int dv0 = dvt * DVT;
     const float lg = a.log2g[s.h];
+    const st* k = (const st*)a.k;
+    const st* v = (const st*)a.v;
 
     f32x4_t R[F::NR_W];
 #pragma unroll
@@ -263,21 +343,64 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_local_kernel(FwdArgs a) {
 
     const long long seg_t0 = (long long)seg * a.seg_len;
     const long long seg_t1 = min((long long)a.N, seg_t0 + a.seg_len);
-    for (long long t0 = seg_t0; t0 < seg_t1; t0 += C) {
+    const int nst = (int)((seg_t1 - seg_t0 + C - 1) / C);
+    const long long row0 = ((long long)s.b * a.N) * a.H + s.h;
+    const int rsk = a.H * a.dk, rsv = a.H * a.dv;
+
+    Raw<E> buf[F::NU];
+    auto issue = [&](int i) {
+        const long long t0 = seg_t0 + (long long)i * C;
         const int L = (int)min((long long)C, seg_t1 - t0);
-        const float gL = gpow(lg, (float)L);
-        __syncthreads();
-        stage_qk<E, C, DK>(nullptr, (const st*)a.k, s, a.dk, t0, L, 0, a.theta, a.rotate, a.pos0, lg, nullptr, 0,
-                           nullptr, 0, sKc, F::LDC, tid);
-        stage_v<E, C, DVT>((const st*)a.v, s, a.dv, t0, L, dv0, sVc, F::LDC, tid);
-        __syncthreads();
 #pragma unroll
-        for (int i = 0; i < F::NR_W; ++i) {
-            const int t = w + kWaves * i;
+        for (int j = 0; j < F::NU; ++j) {
+            const int u = tid + kThreads * j;
+            if (u < F::UK + F::UV) {
+                if (u < F::UK) {
+                    const int tb = u / (DK / 8);
+                    issue_unit(buf[j], k + (row0 + (t0 + tb * 8) * a.H) * a.dk + (u % (DK / 8)) * 8, rsk, L - tb * 8);
+                } else {
+                    const int x = u - F::UK, tb = x / (DVT / 8);
+                    issue_unit(buf[j], v + (row0 + (t0 + tb * 8) * a.H) * a.dv + dv0 + (x % (DVT / 8)) * 8, rsv,
+                               L - tb * 8);
+                }
+            }
+        }
+    };
+    auto commit = [&](int i) {
+        const long long t0 = seg_t0 + (long long)i * C;
+        const int L = (int)min((long long)C, seg_t1 - t0);
+#pragma unroll
+        for (int j = 0; j < F::NU; ++j) {
+            const int u = tid + kThreads * j;
+            if (u < F::UK + F::UV) {
+                if (u < F::UK) {
+                    const int tb = u / (DK / 8), db = u % (DK / 8);
+                    commit_k<E>(buf[j], L - tb * 8, a.rotate, a.theta, db * 4, a.pos0 + t0 + tb * 8, lg, L - 1 - tb * 8,
+                                nullptr, 0, sKc + db * 8 * F::LDC + tb * 8, F::LDC);
+                } else {
+                    const int x = u - F::UK, tb = x / (DVT / 8), db = x % (DVT / 8);
+                    commit_v(buf[j], L - tb * 8, sVc + db * 8 * F::LDC + tb * 8, F::LDC);
+                }
+            }
+        }
+    };
+
+    if (nst > 0) issue(0);
+    for (int i = 0; i < nst; ++i) {
+        const long long t0 = seg_t0 + (long long)i * C;
+        const int L = (int)min((long long)C, seg_t1 - t0);
+        __syncthreads();
+        commit(i);
+        if (i + 1 < nst) issue(i + 1);
+        __syncthreads();
+        const float gL = gpow(lg, (float)L);
+#pragma unroll
+        for (int x = 0; x < F::NR_W; ++x) {
+            const int t = w + kWaves * x;
             if (t < F::NR) {
                 const int rb = t / F::NDV, cb = t % F::NDV;
-                R[i] *= gL;
-                mma_nt(R[i], sKc + rb * 16 * F::LDC, F::LDC, sVc + cb * 16 * F::LDC, F::LDC, C, lane);
+                R[x] *= gL;
+                mma_nt(R[x], sKc + rb * 16 * F::LDC, F::LDC, sVc + cb * 16 * F::LDC, F::LDC, C, lane);
             }
         }
     }
@@ -326,7 +449,7 @@ __global__ __launch_bounds__(kThreads, 2) void parallel_kernel(FwdArgs a) {
     const long long q0 = (long long)qb * BQ;
     const int LQ = (int)min((long long)BQ, a.N - q0);
 
-    stage_qk<E, BQ, DK>((const st*)a.q, (const st*)a.q, s, a.dk, q0, LQ, 0, a.theta, a.rotate, a.pos0, lg, sQ, F::LDQ,
+    stage_qk<E, BQ, DK, true, false, false>((const st*)a.q, (const st*)a.q, s, a.dk, q0, LQ, 0, a.theta, a.rotate, a.pos0, lg, sQ, F::LDQ,
                         nullptr, 0, nullptr, 0, tid);
     f32x4_t O[F::NO_W];
 #pragma unroll
@@ -336,7 +459,7 @@ __global__ __launch_bounds__(kThreads, 2) void parallel_kernel(FwdArgs a) {
         const long long k0 = (long long)kb * BQ;
         const int LK = (int)min((long long)BQ, a.N - k0);
         __syncthreads();
-        stage_qk<E, BQ, DK>((const st*)a.k, (const st*)a.k, s, a.dk, k0, LK, 0, a.theta, a.rotate, a.pos0, lg,
+        stage_qk<E, BQ, DK, false, true, false>((const st*)a.k, (const st*)a.k, s, a.dk, k0, LK, 0, a.theta, a.rotate, a.pos0, lg,
                             nullptr, 0, sK, F::LDQ, nullptr, 0, tid);
         stage_v<E, BQ, DVT>((const st*)a.v, s, a.dv, k0, LK, dv0, sVc, F::LDC, tid);
         __syncthreads();

@@ -16,20 +16,19 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------------------------------
-// bf16 <-> fp32 (round to nearest, ties to even; NaN stays NaN)
+// bf16 <-> fp32. Rounding to bf16 is round-to-nearest-even by the gfx950 packed conversion
+// (v_cvt_pk_bf16_f32); NaN stays NaN.
 // ---------------------------------------------------------------------------------------------------
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
-__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
-    return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
-}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return (uint16_t)(pack2_bf16(f, 0.f) & 0xffffu); }
 
 // ---------------------------------------------------------------------------------------------------
 // Element traits. `st` is the storage type in global memory and LDS. KD is the MFMA reduction depth of one
@@ -148,9 +147,10 @@ __device__ __forceinline__ void mma_nt(f32x4_t& acc, const float* A, int lda, co
 // ---------------------------------------------------------------------------------------------------
 // Decay and rotation factors.
 // ---------------------------------------------------------------------------------------------------
-// gamma^e for e >= 0 from log2(gamma) (computed on the host in fp64). Never the global factorisation
-// gamma^n * gamma^-m, which overflows for long sequences.
-__device__ __forceinline__ float gpow(float log2g, float e) { return exp2f(e * log2g); }
+// gamma^e for e >= 0 from log2(gamma) (computed on the host in fp64), by the hardware base-2 exponential
+// (the exponent is <= 0, so results lie in (0, 1]; a result below the fp32 normal range becomes 0). Never the
+// global factorisation gamma^n * gamma^-m, which overflows for long sequences.
+__device__ __forceinline__ float gpow(float log2g, float e) { return __builtin_amdgcn_exp2f(e * log2g); }
 
 // cos/sin of the angle p*theta. The angle is formed in fp64 and reduced there by the nearest multiple of pi/2
 // (quadrant k), leaving r in [-pi/4, pi/4]; sin r and cos r then come from their Taylor series in fp32
@@ -222,11 +222,13 @@ struct RotUnit {
 };
 
 // Q and K slice [d0, d0+W) of tokens [t0, t0+CT): Q -> sQ (row), K -> sK (row) and sKc (column, each token
-// scaled by zeta_t before rounding). Rotation uses the global pair index (d0 + c) / 2. Within a unit the
-// rotation of token r+1 is that of token r turned by the one-token step (angle addition), so each unit
-// evaluates two accurate sin/cos per pair instead of eight; q and k share the factors. On the bf16 path the
-// eight K rows wait for the transpose packed (4 registers per row).
-template <class E, int CT, int W>
+// scaled by zeta_t before rounding); which destinations exist is fixed at compile time. Rotation uses the
+// global pair index (d0 + c) / 2. Within a unit the rotation of token r+1 is that of token r turned by the
+// one-token step (angle addition), so each unit evaluates two accurate sin/cos per pair instead of eight; q
+// and k share the factors. Loads are branch-free (rows past L re-read row L-1 and are zeroed by a select), so
+// all eight rows of a unit are in flight together. On the bf16 path the eight K rows wait for the transpose
+// packed (4 registers per row).
+template <class E, int CT, int W, bool HAS_Q, bool HAS_KROW, bool HAS_KCOL>
 __device__ __forceinline__ void stage_qk(const typename E::st* q, const typename E::st* k, const Seq& s, int dk,
                                          long long t0, int L, int d0, const double* theta, bool rotate,
                                          long long pos0, float log2g, typename E::st* sQ, int ldq,
@@ -235,40 +237,42 @@ __device__ __forceinline__ void stage_qk(const typename E::st* q, const typename
     constexpr bool kBF16 = sizeof(typename E::st) == 2;
     for (int u = tid; u < UT * UD; u += kThreads) {
         const int tb = u / UD, db = u % UD;
+        const int rs = s.H * dk;  // elements between consecutive tokens
+        const typename E::st* qb = HAS_Q ? row_ptr(q, s, dk, t0 + tb * 8, d0 + db * 8) : nullptr;
+        const typename E::st* kb = row_ptr(k, s, dk, t0 + tb * 8, d0 + db * 8);
+        float qv[HAS_Q ? 8 : 1][8], kv[8][8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int tr = min(tb * 8 + r, L - 1) - tb * 8;  // clamp: never read past the sequence
+            if constexpr (HAS_Q) load8(qb + tr * rs, qv[r]);
+            load8(kb + tr * rs, kv[r]);
+        }
         RotUnit rot;
         if (rotate) rot.init(theta, (d0 + db * 8) / 2, pos0 + t0 + tb * 8);
         uint4 kc16[8];
-        float kc32[kBF16 ? 1 : 8][8];
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            const int t = tb * 8 + r;
-            float qv[8], kv[8];
-            if (t < L) {
-                if (sQ) load8(row_ptr(q, s, dk, t0 + t, d0 + db * 8), qv);
-                load8(row_ptr(k, s, dk, t0 + t, d0 + db * 8), kv);
-            } else {
+            const bool live = tb * 8 + r < L;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) qv[e] = kv[e] = 0.f;
+            for (int e = 0; e < 8; ++e) {
+                if constexpr (HAS_Q) qv[r][e] = live ? qv[r][e] : 0.f;
+                kv[r][e] = live ? kv[r][e] : 0.f;
             }
             if (rotate) {
-                if (sQ) rot.apply(qv);
-                rot.apply(kv);
+                if constexpr (HAS_Q) rot.apply(qv[r]);
+                rot.apply(kv[r]);
                 rot.step();
             }
-            if (sQ) store8(sQ + t * ldq + db * 8, qv);
-            if (sK) store8(sK + t * ldk + db * 8, kv);
-            if (sKc) {
-                const float z = (t < L) ? gpow(log2g, (float)(L - 1 - t)) : 0.f;
+            if constexpr (HAS_Q) store8(sQ + (tb * 8 + r) * ldq + db * 8, qv[r]);
+            if constexpr (HAS_KROW) store8(sK + (tb * 8 + r) * ldk + db * 8, kv[r]);
+            if constexpr (HAS_KCOL) {
+                const float z = live ? gpow(log2g, (float)(L - 1 - (tb * 8 + r))) : 0.f;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) kv[e] *= z;
-                if constexpr (kBF16)
-                    kc16[r] = pack8_bf16(kv);
-                else
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) kc32[kBF16 ? 0 : r][e] = kv[e];
+                for (int e = 0; e < 8; ++e) kv[r][e] *= z;
+                if constexpr (kBF16) kc16[r] = pack8_bf16(kv[r]);
             }
         }
-        if (sKc) {
+        if constexpr (HAS_KCOL) {
             if constexpr (kBF16) {
                 uint4 cols[8];
                 transpose8_bf16(kc16, cols);
@@ -279,7 +283,7 @@ __device__ __forceinline__ void stage_qk(const typename E::st* q, const typename
                 for (int e = 0; e < 8; ++e) {
                     float col[8];
 #pragma unroll
-                    for (int r = 0; r < 8; ++r) col[r] = kc32[kBF16 ? 0 : r][e];
+                    for (int r = 0; r < 8; ++r) col[r] = kv[r][e];
                     store8(sKc + (db * 8 + e) * ldkc + tb * 8, col);
                 }
             }
@@ -287,21 +291,26 @@ __device__ __forceinline__ void stage_qk(const typename E::st* q, const typename
     }
 }
 
-// V columns [d0, d0+W) of tokens [t0, t0+CT) -> sVc (column layout). bf16 rows move as packed words.
+// V columns [d0, d0+W) of tokens [t0, t0+CT) -> sVc (column layout). bf16 rows move as packed words. Loads
+// are branch-free as in stage_qk.
 template <class E, int CT, int W>
 __device__ __forceinline__ void stage_v(const typename E::st* v, const Seq& s, int dv, long long t0, int L, int d0,
                                         typename E::st* sVc, int ldvc, int tid) {
     constexpr int UT = CT / 8, UD = W / 8;
     for (int u = tid; u < UT * UD; u += kThreads) {
         const int tb = u / UD, db = u % UD;
+        const typename E::st* vb = row_ptr(v, s, dv, t0 + tb * 8, d0 + db * 8);
+        const int rs = s.H * dv;
         if constexpr (sizeof(typename E::st) == 2) {
             uint4 rows[8], cols[8];
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
-                const int t = tb * 8 + r;
-                rows[r] = (t < L) ? *reinterpret_cast<const uint4*>(row_ptr(v, s, dv, t0 + t, d0 + db * 8))
-                                  : make_uint4(0u, 0u, 0u, 0u);
+                const int tr = min(tb * 8 + r, L - 1) - tb * 8;
+                rows[r] = *reinterpret_cast<const uint4*>(vb + tr * rs);
             }
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                if (tb * 8 + r >= L) rows[r] = make_uint4(0u, 0u, 0u, 0u);
             transpose8_bf16(rows, cols);
 #pragma unroll
             for (int e = 0; e < 8; ++e) *reinterpret_cast<uint4*>(sVc + (db * 8 + e) * ldvc + tb * 8) = cols[e];
@@ -309,21 +318,141 @@ __device__ __forceinline__ void stage_v(const typename E::st* v, const Seq& s, i
             float vv[8][8];
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
-                const int t = tb * 8 + r;
-                if (t < L)
-                    load8(row_ptr(v, s, dv, t0 + t, d0 + db * 8), vv[r]);
-                else
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) vv[r][e] = 0.f;
+                const int tr = min(tb * 8 + r, L - 1) - tb * 8;
+                load8(vb + tr * rs, vv[r]);
             }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 float col[8];
 #pragma unroll
-                for (int r = 0; r < 8; ++r) col[r] = vv[r][e];
+                for (int r = 0; r < 8; ++r) col[r] = (tb * 8 + r < L) ? vv[r][e] : 0.f;
                 store8(sVc + (db * 8 + e) * ldvc + tb * 8, col);
             }
         }
+    }
+}
+
+// ---------------------------------------------------------------------------------------------------
+// Pipelined staging. A unit is 8 consecutive tokens x 8 consecutive dims of one tensor. issue_unit() starts
+// the eight row loads into registers (rows past L re-read row L-1, never past the sequence);
+// commit_*() waits for them, zeroes rows past L, rotates / scales / transposes, and writes LDS. A kernel
+// issues the loads of stage i+1 before it computes stage i, so memory latency overlaps the MFMA work.
+// ---------------------------------------------------------------------------------------------------
+template <class E>
+struct Raw;
+template <>
+struct Raw<BF16> {
+    uint4 r[8];
+};
+template <>
+struct Raw<F32> {
+    float4 r[8][2];
+};
+
+__device__ __forceinline__ void issue_unit(Raw<BF16>& u, const uint16_t* base, int rs, int rows_live) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) u.r[r] = *reinterpret_cast<const uint4*>(base + min(r, rows_live - 1) * rs);
+}
+__device__ __forceinline__ void issue_unit(Raw<F32>& u, const float* base, int rs, int rows_live) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const float4* p = reinterpret_cast<const float4*>(base + min(r, rows_live - 1) * rs);
+        u.r[r][0] = p[0];
+        u.r[r][1] = p[1];
+    }
+}
+__device__ __forceinline__ void raw_row(const Raw<BF16>& u, int r, float* f) { unpack8_bf16(u.r[r], f); }
+__device__ __forceinline__ void raw_row(const Raw<F32>& u, int r, float* f) {
+    f[0] = u.r[r][0].x; f[1] = u.r[r][0].y; f[2] = u.r[r][0].z; f[3] = u.r[r][0].w;
+    f[4] = u.r[r][1].x; f[5] = u.r[r][1].y; f[6] = u.r[r][1].z; f[7] = u.r[r][1].w;
+}
+
+// Q unit -> row layout (rotated).
+template <class E>
+__device__ __forceinline__ void commit_q(const Raw<E>& u, int rows_live, bool rotate, const double* theta, int pair0,
+                                         long long p0, typename E::st* dst, int ld) {
+    RotUnit rot;
+    if (rotate) rot.init(theta, pair0, p0);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        float x[8];
+        raw_row(u, r, x);
+        const bool live = r < rows_live;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = live ? x[e] : 0.f;
+        if (rotate) {
+            rot.apply(x);
+            rot.step();
+        }
+        store8(dst + r * ld, x);
+    }
+}
+
+// K unit -> row layout (rotated) and column layout (rotated, token r scaled by zeta[r] = gamma^(L-1-t)).
+template <class E>
+__device__ __forceinline__ void commit_k(const Raw<E>& u, int rows_live, bool rotate, const double* theta, int pair0,
+                                         long long p0, float log2g, int zexp0, typename E::st* drow, int ldr,
+                                         typename E::st* dcol, int ldc) {
+    RotUnit rot;
+    if (rotate) rot.init(theta, pair0, p0);
+    uint4 kc16[8];
+    float kc32[sizeof(typename E::st) == 2 ? 1 : 8][8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        float x[8];
+        raw_row(u, r, x);
+        const bool live = r < rows_live;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = live ? x[e] : 0.f;
+        if (rotate) {
+            rot.apply(x);
+            rot.step();
+        }
+        if (drow) store8(drow + r * ldr, x);
+        const float z = live ? gpow(log2g, (float)(zexp0 - r)) : 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] *= z;
+        if constexpr (sizeof(typename E::st) == 2)
+            kc16[r] = pack8_bf16(x);
+        else
+#pragma unroll
+            for (int e = 0; e < 8; ++e) kc32[sizeof(typename E::st) == 2 ? 0 : r][e] = x[e];
+    }
+    if constexpr (sizeof(typename E::st) == 2) {
+        uint4 cols[8];
+        transpose8_bf16(kc16, cols);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) *reinterpret_cast<uint4*>(dcol + e * ldc) = cols[e];
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float col[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) col[r] = kc32[sizeof(typename E::st) == 2 ? 0 : r][e];
+            store8(dcol + e * ldc, col);
+        }
+    }
+}
+
+// V unit -> column layout.
+__device__ __forceinline__ void commit_v(const Raw<BF16>& u, int rows_live, uint16_t* dcol, int ldc) {
+    uint4 rows[8], cols[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) rows[r] = (r < rows_live) ? u.r[r] : make_uint4(0u, 0u, 0u, 0u);
+    transpose8_bf16(rows, cols);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) *reinterpret_cast<uint4*>(dcol + e * ldc) = cols[e];
+}
+__device__ __forceinline__ void commit_v(const Raw<F32>& u, int rows_live, float* dcol, int ldc) {
+    float x[8][8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) raw_row(u, r, x[r]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        float col[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) col[r] = (r < rows_live) ? x[r][e] : 0.f;
+        store8(dcol + e * ldc, col);
     }
 }
 
