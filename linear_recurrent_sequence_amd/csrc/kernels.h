@@ -2,6 +2,8 @@
 // getters; the C-ABI source launches them.
 #pragma once
 
+#include <type_traits>
+
 #include "retention_device.h"
 
 namespace ret {
@@ -34,9 +36,31 @@ struct Tri {
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
+// Compile-time loop: f(std::integral_constant<int, I>) for I = 0..N-1.
+template <int I, int N, class Fn>
+__device__ __forceinline__ void static_for(Fn&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
+// Tile t of the lower triangle (lb <= jb), enumerated row by row, as (jb, lb). t is wave-uniform, so this
+// runs on the scalar unit.
+template <int NB>
+__device__ __forceinline__ void tri_tile(int t, int& jb, int& lb) {
+    int r = 0;
+#pragma unroll
+    for (int i = 1; i < NB; ++i) r += (t >= i * (i + 1) / 2) ? 1 : 0;
+    jb = r;
+    lb = t - r * (r + 1) / 2;
+}
+
 // ---------------------------------------------------------------------------------------------------
 // chunk_full: one workgroup per (segment, d_v tile, b*H + h). The segment's chunks are processed in stages
 // (chunk, d_k slice); the global loads of stage i+1 are issued before stage i is computed.
+// Products are formed transposed where that helps the stores: S^T = K Q^T (each lane then holds 4 consecutive
+// keys of one query row of P) and O^T = R^T Q^T + V^T P^T (4 consecutive d_v of one output row).
 // ---------------------------------------------------------------------------------------------------
 template <class E, int DK, int C, int DVT>
 struct FullCfg {
@@ -56,9 +80,8 @@ struct FullCfg {
     static constexpr int NO_W = (NO + kWaves - 1) / kWaves;
     static constexpr int NR = NKB * NDV;             // R tiles
     static constexpr int NR_W = (NR + kWaves - 1) / kWaves;
-    static constexpr int UQ = (C / 8) * (KS / 8);    // staging units of Q (and of K) per slice
-    static constexpr int UV = (C / 8) * (DVT / 8);   // staging units of V (first slice only)
-    static constexpr int NU = (2 * UQ + UV + kThreads - 1) / kThreads;
+    typedef ItemWidth<C, KS> IQK;                    // Q+K staging items per slice
+    typedef ItemWidth<C, DVT> IV;                    // V staging items (first slice only)
     static constexpr int SQ = C * LDQ, SKC = KS * LDC, SVC = DVT * LDC, SP = C * LDC, SRT = DVT * LDR;
     // Region A holds sQ, sK and sKc while a chunk's slices are computed, then the output tile (fp32 at most).
     static constexpr int A_STAGE = (2 * SQ + SKC) * (int)sizeof(st), A_OUT = C * LDO * 4;
@@ -68,10 +91,21 @@ struct FullCfg {
     static_assert(C % 16 == 0 && DVT % 16 == 0 && DK % KS == 0 && KS % E::KD == 0 && C % E::KD == 0, "tiling");
 };
 
+// O^T tile x of wave w covers query block jb and d_v block db; with four d_v blocks, jb = x and db = w.
+template <class F>
+__device__ __forceinline__ int ojb(int w, int x) {
+    return F::NDV == kWaves ? x : (w + kWaves * x) / F::NDV;
+}
+template <class F>
+__device__ __forceinline__ int odb(int w, int x) {
+    return F::NDV == kWaves ? w : (w + kWaves * x) % F::NDV;
+}
+
 template <class E, int DK, int C, int DVT>
 __global__ __launch_bounds__(kThreads, 2) void chunk_full_kernel(FwdArgs a) {
     typedef FullCfg<E, DK, C, DVT> F;
     typedef typename E::st st;
+    constexpr int IQ = F::IQK::value, IVW = F::IV::value, NIQ = F::IQK::per_thread, NIV = F::IV::per_thread;
     __shared__ __attribute__((aligned(16))) st smem[F::LDS_BYTES / sizeof(st)];
     st* sQ = smem;
     st* sK = sQ + F::SQ;
@@ -81,18 +115,32 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_full_kernel(FwdArgs a) {
     st* sRt = sP + F::SP;
     char* sO = reinterpret_cast<char*>(smem);  // output tile, over region A once a chunk's slices are done
 
-    const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
+    const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g4 = 4 * (lane >> 4), n16 = lane & 15;
     const int seg = blockIdx.x, dvt = blockIdx.y, pair = blockIdx.z;
-    const Seq s{a.N, a.H, pair / a.H, pair % a.H};
+    const int b = pair / a.H, h = pair % a.H;
     const int dv0 = dvt * DVT;
-    const float lg = a.log2g[s.h];
-    const st* q = (const st*)a.q;
-    const st* k = (const st*)a.k;
-    const st* v = (const st*)a.v;
+    const float lg = a.log2g[h];
     const int osz = a.out_bf16 ? 2 : 4;
 
     // Scores above the diagonal are never written: keep them zero for the P.V product.
     for (int i = tid; i < F::SP; i += kThreads) sP[i] = (st)0;
+
+    // Decay factors that do not depend on the chunk: the mask gamma^(j-l) of each owned S^T tile (rows l,
+    // columns j) and xi_j = gamma^(j+1) of each owned O^T tile (columns j).
+    // S^T tiles of this wave: t = w + 4x in row-by-row lower-triangle order.
+    int Sjb[F::NS_W], Slb[F::NS_W];
+    float Dm[F::NS_W][4], Xi[F::NO_W];
+#pragma unroll
+    for (int x = 0; x < F::NS_W; ++x) {
+        tri_tile<F::NB>(min(w + kWaves * x, F::NS - 1), Sjb[x], Slb[x]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int d = 16 * (Sjb[x] - Slb[x]) + n16 - g4 - e;  // j - l
+            Dm[x][e] = d >= 0 ? gpow(lg, (float)d) : 0.f;
+        }
+    }
+#pragma unroll
+    for (int x = 0; x < F::NO_W; ++x) Xi[x] = gpow(lg, (float)(ojb<F>(w, x) * 16 + n16 + 1));
 
     // Initial state for this segment: the segment-scan result, state_in, or zeros.
     const float* init = nullptr;
@@ -108,8 +156,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_full_kernel(FwdArgs a) {
         if (t < F::NR && init) {
             const int rb = t / F::NDV, cb = t % F::NDV;
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                R[i][e] = init[(long long)(rb * 16 + 4 * (lane >> 4) + e) * a.dv + dv0 + cb * 16 + (lane & 15)];
+            for (int e = 0; e < 4; ++e) R[i][e] = init[(long long)(rb * 16 + g4 + e) * a.dv + dv0 + cb * 16 + n16];
         }
     }
     // Copy of R (operand precision), transposed to [d_v][d_k], for the cross product.
@@ -118,174 +165,179 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_full_kernel(FwdArgs a) {
         const int t = w + kWaves * i;
         if (t < F::NR) {
             const int rb = t / F::NDV, cb = t % F::NDV;
-            store4(sRt + (cb * 16 + (lane & 15)) * F::LDR + rb * 16 + 4 * (lane >> 4), R[i]);
+            store4(sRt + (cb * 16 + n16) * F::LDR + rb * 16 + g4, R[i]);
         }
     }
 
     const long long seg_t0 = (long long)seg * a.seg_len;
     const long long seg_t1 = min((long long)a.N, seg_t0 + a.seg_len);
     const int nst = (int)((seg_t1 - seg_t0 + C - 1) / C) * F::NSL;
-    const long long qk_row0 = ((long long)s.b * a.N) * a.H + s.h;  // token 0 of this (b, h), in rows of d
     const int rsk = a.H * a.dk, rsv = a.H * a.dv;
-
-    Raw<E> buf[F::NU];
-    auto issue = [&](int i) {
-        const long long t0 = seg_t0 + (long long)(i / F::NSL) * C;
-        const int sl = i % F::NSL;
-        const int L = (int)min((long long)C, seg_t1 - t0);
-        const int total = 2 * F::UQ + (sl == 0 ? F::UV : 0);
+    // This thread's staging items: token block and first dim; pointers at the segment's first chunk.
+    int qtb[NIQ], qdb[NIQ], vtb[NIV], vdb[NIV];
+    const st *qp[NIQ], *kp[NIQ], *vp[NIV];
+    RotStep<IQ / 2> rstep[NIQ][F::NSL];
+    float zfull[NIQ][8];
 #pragma unroll
-        for (int j = 0; j < F::NU; ++j) {
-            const int u = tid + kThreads * j;
-            if (u < total) {
-                const st* base;
-                int rs, tb;
-                if (u < 2 * F::UQ) {
-                    const int x = u < F::UQ ? u : u - F::UQ;
-                    tb = x / (F::KS / 8);
-                    base = (u < F::UQ ? q : k) + (qk_row0 + t0 * a.H) * a.dk + sl * F::KS + (x % (F::KS / 8)) * 8;
-                    rs = rsk;
-                } else {
-                    const int x = u - 2 * F::UQ;
-                    tb = x / (DVT / 8);
-                    base = v + (qk_row0 + t0 * a.H) * a.dv + dv0 + (x % (DVT / 8)) * 8;
-                    rs = rsv;
-                }
-                issue_unit(buf[j], base + (long long)tb * 8 * rs, rs, L - tb * 8);
+    for (int j = 0; j < NIQ; ++j) {
+        const int x = min(tid + kThreads * j, F::IQK::count - 1);
+        qtb[j] = x / (F::KS / IQ);
+        qdb[j] = x % (F::KS / IQ);
+        const long long off = (((long long)b * a.N + seg_t0 + qtb[j] * 8) * a.H + h) * a.dk + qdb[j] * IQ;
+        qp[j] = (const st*)a.q + off;
+        kp[j] = (const st*)a.k + off;
+#pragma unroll
+        for (int sl = 0; sl < F::NSL; ++sl)
+            if (a.rotate) rstep[j][sl].init(a.theta, (sl * F::KS + qdb[j] * IQ) / 2);
+        item_zeta(zfull[j], lg, C - 1 - qtb[j] * 8, 8);
+    }
+#pragma unroll
+    for (int j = 0; j < NIV; ++j) {
+        const int x = min(tid + kThreads * j, F::IV::count - 1);
+        vtb[j] = x / (DVT / IVW);
+        vdb[j] = x % (DVT / IVW);
+        vp[j] = (const st*)a.v + (((long long)b * a.N + seg_t0 + vtb[j] * 8) * a.H + h) * a.dv + dv0 + vdb[j] * IVW;
+    }
+    const float gC = gpow(lg, (float)C);
+
+    Item<E, IQ> bq[NIQ], bk[NIQ];
+    Item<E, IVW> bv[NIV];
+    auto issue = [&](int i) {
+        const int c = i / F::NSL, sl = i % F::NSL;
+        const int L = (int)min((long long)C, seg_t1 - seg_t0 - (long long)c * C);
+        const long long cq = (long long)c * C * rsk + sl * F::KS;
+#pragma unroll
+        for (int j = 0; j < NIQ; ++j)
+            if (tid + kThreads * j < F::IQK::count) {
+                issue_item<E, IQ>(bq[j], qp[j] + cq, rsk, L - qtb[j] * 8);
+                issue_item<E, IQ>(bk[j], kp[j] + cq, rsk, L - qtb[j] * 8);
             }
+        if (sl == 0) {
+            const long long cv = (long long)c * C * rsv;
+#pragma unroll
+            for (int j = 0; j < NIV; ++j)
+                if (tid + kThreads * j < F::IV::count) issue_item<E, IVW>(bv[j], vp[j] + cv, rsv, L - vtb[j] * 8);
         }
     };
     auto commit = [&](int i) {
-        const long long t0 = seg_t0 + (long long)(i / F::NSL) * C;
-        const int sl = i % F::NSL;
+        const int c = i / F::NSL, sl = i % F::NSL;
+        const long long t0 = seg_t0 + (long long)c * C;
         const int L = (int)min((long long)C, seg_t1 - t0);
-        const int total = 2 * F::UQ + (sl == 0 ? F::UV : 0);
 #pragma unroll
-        for (int j = 0; j < F::NU; ++j) {
-            const int u = tid + kThreads * j;
-            if (u < total) {
-                if (u < 2 * F::UQ) {
-                    const int x = u < F::UQ ? u : u - F::UQ;
-                    const int tb = x / (F::KS / 8), db = x % (F::KS / 8);
-                    const int pair0 = (sl * F::KS + db * 8) / 2;
-                    const long long p0 = a.pos0 + t0 + tb * 8;
-                    if (u < F::UQ)
-                        commit_q<E>(buf[j], L - tb * 8, a.rotate, a.theta, pair0, p0, sQ + tb * 8 * F::LDQ + db * 8,
-                                    F::LDQ);
-                    else
-                        commit_k<E>(buf[j], L - tb * 8, a.rotate, a.theta, pair0, p0, lg, L - 1 - tb * 8,
-                                    sK + tb * 8 * F::LDQ + db * 8, F::LDQ, sKc + db * 8 * F::LDC + tb * 8, F::LDC);
+        for (int j = 0; j < NIQ; ++j)
+            if (tid + kThreads * j < F::IQK::count) {
+                float zt[8];
+                if (L == C) {
+#pragma unroll
+                    for (int r = 0; r < 8; ++r) zt[r] = zfull[j][r];
                 } else {
-                    const int x = u - 2 * F::UQ;
-                    const int tb = x / (DVT / 8), db = x % (DVT / 8);
-                    commit_v(buf[j], L - tb * 8, sVc + db * 8 * F::LDC + tb * 8, F::LDC);
+                    item_zeta(zt, lg, L - 1 - qtb[j] * 8, L - qtb[j] * 8);
                 }
+                RotStep<IQ / 2> rs = rstep[j][0];
+#pragma unroll
+                for (int x = 1; x < F::NSL; ++x)
+                    if (sl == x) rs = rstep[j][x];
+                commit_qk<E, IQ, true, true>(&bq[j], bk[j], L - qtb[j] * 8, a.rotate, a.theta,
+                                             (sl * F::KS + qdb[j] * IQ) / 2, a.pos0 + t0 + qtb[j] * 8, rs, zt,
+                                             sQ + qtb[j] * 8 * F::LDQ + qdb[j] * IQ, F::LDQ,
+                                             sK + qtb[j] * 8 * F::LDQ + qdb[j] * IQ, F::LDQ,
+                                             sKc + qdb[j] * IQ * F::LDC + qtb[j] * 8, F::LDC);
             }
+        if (sl == 0) {
+#pragma unroll
+            for (int j = 0; j < NIV; ++j)
+                if (tid + kThreads * j < F::IV::count)
+                    commit_vcol<E, IVW>(bv[j], L - vtb[j] * 8, sVc + vdb[j] * IVW * F::LDC + vtb[j] * 8, F::LDC);
         }
     };
 
-    f32x4_t S[F::NS_W], O[F::NO_W];
+    const int nchunks = nst / F::NSL;
     if (nst > 0) issue(0);
-    for (int i = 0; i < nst; ++i) {
-        const int sl = i % F::NSL;
-        const long long t0 = seg_t0 + (long long)(i / F::NSL) * C;
+    for (int c = 0; c < nchunks; ++c) {
+        const long long t0 = seg_t0 + (long long)c * C;
         const int L = (int)min((long long)C, seg_t1 - t0);
-        if (sl == 0) {
+        const float gL = L == C ? gC : gpow(lg, (float)L);
+        f32x4_t S[F::NS_W], O[F::NO_W];
 #pragma unroll
-            for (int x = 0; x < F::NS_W; ++x) S[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int x = 0; x < F::NS_W; ++x) S[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int x = 0; x < F::NO_W; ++x) O[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
-        __syncthreads();  // staging buffers free; previous copies of R and of the output tile consumed
-        commit(i);
-        if (i + 1 < nst) issue(i + 1);
-        __syncthreads();
-        // S += Q_s K_s^T over the lower-triangle tiles.
+        for (int x = 0; x < F::NO_W; ++x) O[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        static_for<0, F::NSL>([&](auto slc) {
+            constexpr int sl = decltype(slc)::value;
+            const int i = c * F::NSL + sl;
+            __syncthreads();  // staging buffers free; previous copies of R and of the output tile consumed
+            commit(i);
+            if (i + 1 < nst) issue(i + 1);
+            __syncthreads();
+            // S^T += K_s Q_s^T over this wave's lower-triangle tiles (keys l <= queries j). Slots past the last
+            // tile repeat it; their results are never stored.
 #pragma unroll
-        for (int rb = 0, t = 0; rb < F::NB; ++rb)
+            for (int x = 0; x < F::NS_W; ++x)
+                mma_nt(S[x], sK + Slb[x] * 16 * F::LDQ, F::LDQ, sQ + Sjb[x] * 16 * F::LDQ, F::LDQ, F::KS, lane);
+            // O^T += R_s^T Q_s^T (cross-chunk read of the state carried in from the previous chunk).
 #pragma unroll
-            for (int cb = 0; cb <= rb; ++cb, ++t)
-                if (t % kWaves == w)
-                    mma_nt(S[t / kWaves], sQ + rb * 16 * F::LDQ, F::LDQ, sK + cb * 16 * F::LDQ, F::LDQ, F::KS, lane);
-        // O += Q_s R_s (cross-chunk read of the state carried in from the previous chunk).
+            for (int x = 0; x < F::NO_W; ++x)
+                if (F::NO % kWaves == 0 || w + kWaves * x < F::NO) {
+                    const int jb = ojb<F>(w, x), db = odb<F>(w, x);
+                    mma_nt(O[x], sRt + db * 16 * F::LDR + sl * F::KS, F::LDR, sQ + jb * 16 * F::LDQ, F::LDQ, F::KS,
+                           lane);
+                }
+            // R_s <- gamma^L R_s + K_s^T (V (.) zeta): zeta is folded into sKc. R tile x of wave w covers d_k
+            // block rb = (w + 4x) / NDV; with four d_v blocks rb = x, known at compile time.
 #pragma unroll
-        for (int x = 0; x < F::NO_W; ++x) {
-            const int t = w + kWaves * x;
-            if (t < F::NO) {
-                const int rb = t / F::NDV, cb = t % F::NDV;
-                mma_nt(O[x], sQ + rb * 16 * F::LDQ, F::LDQ, sRt + cb * 16 * F::LDR + sl * F::KS, F::LDR, F::KS, lane);
+            for (int x = 0; x < F::NR_W; ++x) {
+                const int t = w + kWaves * x;
+                const int rb = F::NDV == kWaves ? x : t / F::NDV, cb = F::NDV == kWaves ? w : t % F::NDV;
+                if ((F::NR % kWaves == 0 || t < F::NR) && rb / (F::KS / 16) == sl) {
+                    R[x] *= gL;
+                    mma_nt(R[x], sKc + (rb - sl * (F::KS / 16)) * 16 * F::LDC, F::LDC, sVc + cb * 16 * F::LDC,
+                           F::LDC, C, lane);
+                }
             }
-        }
-        // R_s <- gamma^L R_s + K_s^T (V (.) zeta): zeta is folded into sKc.
-        const float gL = gpow(lg, (float)L);
-#pragma unroll
-        for (int x = 0; x < F::NR_W; ++x) {
-            const int t = w + kWaves * x;
-            const int rb = t / F::NDV, cb = t % F::NDV;
-            if (t < F::NR && rb / (F::KS / 16) == sl) {
-                R[x] *= gL;
-                mma_nt(R[x], sKc + (rb - sl * (F::KS / 16)) * 16 * F::LDC, F::LDC, sVc + cb * 16 * F::LDC, F::LDC, C,
-                       lane);
-            }
-        }
-        if (sl != F::NSL - 1) continue;
+        });
 
-        // Decay mask in registers: P[j][l] = S[j][l] * gamma^(j-l) for l <= j.
+        // Decay mask: P[j][l..l+3] = S^T[l..l+3][j] * gamma^(j-l), four consecutive keys per store.
 #pragma unroll
-        for (int rb = 0, t = 0; rb < F::NB; ++rb)
+        for (int x = 0; x < F::NS_W; ++x)
+            if (w + kWaves * x < F::NS) {
+                f32x4_t pv;
 #pragma unroll
-            for (int cb = 0; cb <= rb; ++cb, ++t)
-                if (t % kWaves == w) {
-                    const int l = cb * 16 + (lane & 15);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int j = rb * 16 + 4 * (lane >> 4) + e;
-                        const float val = (l <= j) ? S[t / kWaves][e] * gpow(lg, (float)(j - l)) : 0.f;
-                        if constexpr (sizeof(st) == 2)
-                            sP[j * F::LDC + l] = f32_to_bf16(val);
-                        else
-                            sP[j * F::LDC + l] = val;
-                    }
-                }
-        __syncthreads();  // P complete; all reads of sQ/sK/sRt for this chunk are done
-        // O = (Q R) (.) xi + P V, written to the output tile in LDS.
+                for (int e = 0; e < 4; ++e) pv[e] = S[x][e] * Dm[x][e];
+                store4(sP + (Sjb[x] * 16 + n16) * F::LDC + Slb[x] * 16 + g4, pv);
+            }
+        __syncthreads();  // P complete; all reads of sQ/sK/sKc/sRt for this chunk are done
+        // O^T = xi (.) (R^T Q^T) + V^T P^T, then the output tile in LDS (4 consecutive d_v per store).
 #pragma unroll
         for (int x = 0; x < F::NO_W; ++x) {
-            const int t = w + kWaves * x;
-            if (t < F::NO) {
-                const int rb = t / F::NDV, cb = t % F::NDV;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) O[x][e] *= gpow(lg, (float)(rb * 16 + 4 * (lane >> 4) + e + 1));
-                const int kmax = min(C, ((rb + 1) * 16 + E::KD - 1) / E::KD * E::KD);
-                mma_nt(O[x], sP + rb * 16 * F::LDC, F::LDC, sVc + cb * 16 * F::LDC, F::LDC, kmax, lane);
-                const int col = cb * 16 + (lane & 15);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int j = rb * 16 + 4 * (lane >> 4) + e;
-                    if (a.out_bf16)
-                        reinterpret_cast<uint16_t*>(sO)[j * F::LDO + col] = f32_to_bf16(O[x][e]);
-                    else
-                        reinterpret_cast<float*>(sO)[j * F::LDO + col] = O[x][e];
-                }
+            if (F::NO % kWaves == 0 || w + kWaves * x < F::NO) {
+                const int jb = ojb<F>(w, x), db = odb<F>(w, x);
+                O[x] *= Xi[x];
+                const int kmax = min(C, ((jb + 1) * 16 + E::KD - 1) / E::KD * E::KD);
+                mma_nt(O[x], sVc + db * 16 * F::LDC, F::LDC, sP + jb * 16 * F::LDC, F::LDC, kmax, lane);
+                const int row = jb * 16 + n16, col = db * 16 + g4;
+                if (a.out_bf16)
+                    store4(reinterpret_cast<uint16_t*>(sO) + row * F::LDO + col, O[x]);
+                else
+                    store4(reinterpret_cast<float*>(sO) + row * F::LDO + col, O[x]);
             }
         }
         // New operand copy of R for the next chunk.
 #pragma unroll
         for (int x = 0; x < F::NR_W; ++x) {
             const int t = w + kWaves * x;
-            if (t < F::NR) {
-                const int rb = t / F::NDV, cb = t % F::NDV;
-                store4(sRt + (cb * 16 + (lane & 15)) * F::LDR + rb * 16 + 4 * (lane >> 4), R[x]);
+            if (F::NR % kWaves == 0 || t < F::NR) {
+                const int rb = F::NDV == kWaves ? x : t / F::NDV, cb = F::NDV == kWaves ? w : t % F::NDV;
+                store4(sRt + (cb * 16 + n16) * F::LDR + rb * 16 + g4, R[x]);
             }
         }
         __syncthreads();
         // Coalesced 16-byte stores of the output rows j < L.
-        const int vec = 16 / osz;                  // elements per 16-byte store
+        const int vec = 16 / osz;  // elements per 16-byte store
         const int per_row = DVT / vec;
-        char* obase = (char*)a.o + ((qk_row0 + t0 * a.H) * a.dv + dv0) * osz;
+        char* obase = (char*)a.o + ((((long long)b * a.N + t0) * a.H + h) * a.dv + dv0) * osz;
         for (int x = tid; x < L * per_row; x += kThreads) {
             const int j = x / per_row, c16 = x % per_row;
-            *reinterpret_cast<uint4*>(obase + ((long long)j * a.H * a.dv + c16 * vec) * osz) =
+            *reinterpret_cast<uint4*>(obase + ((long long)j * rsv + c16 * vec) * osz) =
                 *reinterpret_cast<const uint4*>(sO + (j * F::LDO + c16 * vec) * osz);
         }
     }
@@ -298,8 +350,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_full_kernel(FwdArgs a) {
             if (t < F::NR) {
                 const int rb = t / F::NDV, cb = t % F::NDV;
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    out[(long long)(rb * 16 + 4 * (lane >> 4) + e) * a.dv + dv0 + cb * 16 + (lane & 15)] = R[i][e];
+                for (int e = 0; e < 4; ++e) out[(long long)(rb * 16 + g4 + e) * a.dv + dv0 + cb * 16 + n16] = R[i][e];
             }
         }
     }
@@ -315,8 +366,8 @@ struct LocalCfg {
     static constexpr int NDV = DVT / 16, NKB = DK / 16;
     static constexpr int NR = NKB * NDV;
     static constexpr int NR_W = (NR + kWaves - 1) / kWaves;
-    static constexpr int UK = (C / 8) * (DK / 8), UV = (C / 8) * (DVT / 8);
-    static constexpr int NU = (UK + UV + kThreads - 1) / kThreads;
+    typedef ItemWidth<C, DK> IK;
+    typedef ItemWidth<C, DVT> IV;
     static constexpr int SKC = DK * LDC, SVC = DVT * LDC;
     static constexpr int LDS_BYTES = (SKC + SVC) * (int)sizeof(st);
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -347,22 +398,26 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_local_kernel(FwdArgs a) {
     const long long row0 = ((long long)s.b * a.N) * a.H + s.h;
     const int rsk = a.H * a.dk, rsv = a.H * a.dv;
 
-    Raw<E> buf[F::NU];
+    constexpr int IKW = F::IK::value, IVW = F::IV::value;
+    Item<E, IKW> bk[F::IK::per_thread];
+    Item<E, IVW> bv[F::IV::per_thread];
     auto issue = [&](int i) {
         const long long t0 = seg_t0 + (long long)i * C;
         const int L = (int)min((long long)C, seg_t1 - t0);
 #pragma unroll
-        for (int j = 0; j < F::NU; ++j) {
-            const int u = tid + kThreads * j;
-            if (u < F::UK + F::UV) {
-                if (u < F::UK) {
-                    const int tb = u / (DK / 8);
-                    issue_unit(buf[j], k + (row0 + (t0 + tb * 8) * a.H) * a.dk + (u % (DK / 8)) * 8, rsk, L - tb * 8);
-                } else {
-                    const int x = u - F::UK, tb = x / (DVT / 8);
-                    issue_unit(buf[j], v + (row0 + (t0 + tb * 8) * a.H) * a.dv + dv0 + (x % (DVT / 8)) * 8, rsv,
-                               L - tb * 8);
-                }
+        for (int j = 0; j < F::IK::per_thread; ++j) {
+            const int x = tid + kThreads * j;
+            if (x < F::IK::count) {
+                const int tb = x / (DK / IKW), db = x % (DK / IKW);
+                issue_item<E, IKW>(bk[j], k + (row0 + (t0 + tb * 8) * a.H) * a.dk + db * IKW, rsk, L - tb * 8);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < F::IV::per_thread; ++j) {
+            const int x = tid + kThreads * j;
+            if (x < F::IV::count) {
+                const int tb = x / (DVT / IVW), db = x % (DVT / IVW);
+                issue_item<E, IVW>(bv[j], v + (row0 + (t0 + tb * 8) * a.H) * a.dv + dv0 + db * IVW, rsv, L - tb * 8);
             }
         }
     };
@@ -370,17 +425,25 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_local_kernel(FwdArgs a) {
         const long long t0 = seg_t0 + (long long)i * C;
         const int L = (int)min((long long)C, seg_t1 - t0);
 #pragma unroll
-        for (int j = 0; j < F::NU; ++j) {
-            const int u = tid + kThreads * j;
-            if (u < F::UK + F::UV) {
-                if (u < F::UK) {
-                    const int tb = u / (DK / 8), db = u % (DK / 8);
-                    commit_k<E>(buf[j], L - tb * 8, a.rotate, a.theta, db * 4, a.pos0 + t0 + tb * 8, lg, L - 1 - tb * 8,
-                                nullptr, 0, sKc + db * 8 * F::LDC + tb * 8, F::LDC);
-                } else {
-                    const int x = u - F::UK, tb = x / (DVT / 8), db = x % (DVT / 8);
-                    commit_v(buf[j], L - tb * 8, sVc + db * 8 * F::LDC + tb * 8, F::LDC);
-                }
+        for (int j = 0; j < F::IK::per_thread; ++j) {
+            const int x = tid + kThreads * j;
+            if (x < F::IK::count) {
+                const int tb = x / (DK / IKW), db = x % (DK / IKW);
+                float zt[8];
+                item_zeta(zt, lg, L - 1 - tb * 8, L - tb * 8);
+                RotStep<IKW / 2> rs;
+                if (a.rotate) rs.init(a.theta, db * IKW / 2);
+                commit_qk<E, IKW, false, false>(nullptr, bk[j], L - tb * 8, a.rotate, a.theta, db * IKW / 2,
+                                                a.pos0 + t0 + tb * 8, rs, zt, nullptr, 0, nullptr, 0,
+                                                sKc + db * IKW * F::LDC + tb * 8, F::LDC);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < F::IV::per_thread; ++j) {
+            const int x = tid + kThreads * j;
+            if (x < F::IV::count) {
+                const int tb = x / (DVT / IVW), db = x % (DVT / IVW);
+                commit_vcol<E, IVW>(bv[j], L - tb * 8, sVc + db * IVW * F::LDC + tb * 8, F::LDC);
             }
         }
     };

@@ -5,25 +5,35 @@ namespace ret {
 
 // ---------------------------------------------------------------------------------------------------
 // segment_scan: per (b, h), W[0] = state_in (or 0); W[g] = gamma^seg_len W[g-1] + W[g] for g = 1..nseg-1,
-// where W[g] held the local end state of segment g - 1. Elementwise over d_k x d_v, sequential over g.
+// where W[g] held the local end state of segment g - 1. Elementwise over d_k x d_v, sequential over g. The
+// loads of a group of segments are issued together before the dependent chain runs, so the chain costs one
+// memory round trip per group rather than one per segment.
 // ---------------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void segment_scan_kernel(FwdArgs a) {
+    constexpr int G = 16;  // segments loaded per round trip
     const int pair = blockIdx.y;
     const long long per = (long long)a.dk * a.dv;
     const long long e = ((long long)blockIdx.x * kThreads + threadIdx.x) * 4;
     if (e >= per) return;
-    const float decay = gpow(a.log2g[pair % a.H], (float)a.seg_len);
-    float* W = a.ws + (long long)pair * a.nseg * per;
+    const float decay = __builtin_amdgcn_exp2f((float)a.seg_len * a.log2g[pair % a.H]);
+    float* W = a.ws + (long long)pair * a.nseg * per + e;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     if (a.state_in) acc = *reinterpret_cast<const float4*>(a.state_in + (long long)pair * per + e);
-    *reinterpret_cast<float4*>(W + e) = acc;
-    for (int g = 1; g < a.nseg; ++g) {
-        float4 u = *reinterpret_cast<const float4*>(W + (long long)g * per + e);
-        acc.x = decay * acc.x + u.x;
-        acc.y = decay * acc.y + u.y;
-        acc.z = decay * acc.z + u.z;
-        acc.w = decay * acc.w + u.w;
-        *reinterpret_cast<float4*>(W + (long long)g * per + e) = acc;
+    *reinterpret_cast<float4*>(W) = acc;
+    for (int g0 = 1; g0 < a.nseg; g0 += G) {
+        float4 u[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j)  // branch-free: past the last segment re-read the last one (unused)
+            u[j] = *reinterpret_cast<const float4*>(W + (long long)min(g0 + j, a.nseg - 1) * per);
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+            if (g0 + j < a.nseg) {
+                acc.x = decay * acc.x + u[j].x;
+                acc.y = decay * acc.y + u[j].y;
+                acc.z = decay * acc.z + u[j].z;
+                acc.w = decay * acc.w + u[j].w;
+                *reinterpret_cast<float4*>(W + (long long)(g0 + j) * per) = acc;
+            }
     }
 }
 

@@ -333,127 +333,190 @@ __device__ __forceinline__ void stage_v(const typename E::st* v, const Seq& s, i
 }
 
 // ---------------------------------------------------------------------------------------------------
-// Pipelined staging. A unit is 8 consecutive tokens x 8 consecutive dims of one tensor. issue_unit() starts
-// the eight row loads into registers (rows past L re-read row L-1, never past the sequence);
-// commit_*() waits for them, zeroes rows past L, rotates / scales / transposes, and writes LDS. A kernel
-// issues the loads of stage i+1 before it computes stage i, so memory latency overlaps the MFMA work.
+// Pipelined staging. An item is 8 consecutive tokens x IW consecutive dims of one tensor, kept in registers
+// as raw words between issue_item() (the eight row loads; rows past L re-read row L-1, never past the
+// sequence) and a commit (zero rows past L, rotate / scale, write LDS). Kernels issue the loads of stage i+1
+// before computing stage i, so memory latency overlaps the MFMA work. Items are sized so that every thread
+// of the workgroup holds one Q+K item and one V item per stage; q and k of an item share rotation factors.
 // ---------------------------------------------------------------------------------------------------
-template <class E>
-struct Raw;
-template <>
-struct Raw<BF16> {
-    uint4 r[8];
-};
-template <>
-struct Raw<F32> {
-    float4 r[8][2];
+template <class E, int IW>
+struct Item {
+    static constexpr int WPR = IW * (int)sizeof(typename E::st) / 4;  // 32-bit words per row
+    uint32_t w[8][WPR];
 };
 
-__device__ __forceinline__ void issue_unit(Raw<BF16>& u, const uint16_t* base, int rs, int rows_live) {
-#pragma unroll
-    for (int r = 0; r < 8; ++r) u.r[r] = *reinterpret_cast<const uint4*>(base + min(r, rows_live - 1) * rs);
-}
-__device__ __forceinline__ void issue_unit(Raw<F32>& u, const float* base, int rs, int rows_live) {
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        const float4* p = reinterpret_cast<const float4*>(base + min(r, rows_live - 1) * rs);
-        u.r[r][0] = p[0];
-        u.r[r][1] = p[1];
-    }
-}
-__device__ __forceinline__ void raw_row(const Raw<BF16>& u, int r, float* f) { unpack8_bf16(u.r[r], f); }
-__device__ __forceinline__ void raw_row(const Raw<F32>& u, int r, float* f) {
-    f[0] = u.r[r][0].x; f[1] = u.r[r][0].y; f[2] = u.r[r][0].z; f[3] = u.r[r][0].w;
-    f[4] = u.r[r][1].x; f[5] = u.r[r][1].y; f[6] = u.r[r][1].z; f[7] = u.r[r][1].w;
-}
-
-// Q unit -> row layout (rotated).
-template <class E>
-__device__ __forceinline__ void commit_q(const Raw<E>& u, int rows_live, bool rotate, const double* theta, int pair0,
-                                         long long p0, typename E::st* dst, int ld) {
-    RotUnit rot;
-    if (rotate) rot.init(theta, pair0, p0);
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        float x[8];
-        raw_row(u, r, x);
-        const bool live = r < rows_live;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = live ? x[e] : 0.f;
-        if (rotate) {
-            rot.apply(x);
-            rot.step();
-        }
-        store8(dst + r * ld, x);
-    }
-}
-
-// K unit -> row layout (rotated) and column layout (rotated, token r scaled by zeta[r] = gamma^(L-1-t)).
-template <class E>
-__device__ __forceinline__ void commit_k(const Raw<E>& u, int rows_live, bool rotate, const double* theta, int pair0,
-                                         long long p0, float log2g, int zexp0, typename E::st* drow, int ldr,
-                                         typename E::st* dcol, int ldc) {
-    RotUnit rot;
-    if (rotate) rot.init(theta, pair0, p0);
-    uint4 kc16[8];
-    float kc32[sizeof(typename E::st) == 2 ? 1 : 8][8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        float x[8];
-        raw_row(u, r, x);
-        const bool live = r < rows_live;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = live ? x[e] : 0.f;
-        if (rotate) {
-            rot.apply(x);
-            rot.step();
-        }
-        if (drow) store8(drow + r * ldr, x);
-        const float z = live ? gpow(log2g, (float)(zexp0 - r)) : 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] *= z;
-        if constexpr (sizeof(typename E::st) == 2)
-            kc16[r] = pack8_bf16(x);
-        else
-#pragma unroll
-            for (int e = 0; e < 8; ++e) kc32[sizeof(typename E::st) == 2 ? 0 : r][e] = x[e];
-    }
-    if constexpr (sizeof(typename E::st) == 2) {
-        uint4 cols[8];
-        transpose8_bf16(kc16, cols);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) *reinterpret_cast<uint4*>(dcol + e * ldc) = cols[e];
+template <int N>
+__device__ __forceinline__ void load_words(uint32_t* w, const void* p) {
+    if constexpr (N == 1) {
+        w[0] = *reinterpret_cast<const uint32_t*>(p);
+    } else if constexpr (N == 2) {
+        uint2 x = *reinterpret_cast<const uint2*>(p);
+        w[0] = x.x; w[1] = x.y;
     } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float col[8];
-#pragma unroll
-            for (int r = 0; r < 8; ++r) col[r] = kc32[sizeof(typename E::st) == 2 ? 0 : r][e];
-            store8(dcol + e * ldc, col);
+        for (int i = 0; i < N; i += 4) {
+            uint4 x = reinterpret_cast<const uint4*>(p)[i / 4];
+            w[i] = x.x; w[i + 1] = x.y; w[i + 2] = x.z; w[i + 3] = x.w;
         }
     }
 }
-
-// V unit -> column layout.
-__device__ __forceinline__ void commit_v(const Raw<BF16>& u, int rows_live, uint16_t* dcol, int ldc) {
-    uint4 rows[8], cols[8];
+template <int N>
+__device__ __forceinline__ void store_words(void* p, const uint32_t* w) {
+    if constexpr (N == 1) {
+        *reinterpret_cast<uint32_t*>(p) = w[0];
+    } else if constexpr (N == 2) {
+        *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
+    } else {
 #pragma unroll
-    for (int r = 0; r < 8; ++r) rows[r] = (r < rows_live) ? u.r[r] : make_uint4(0u, 0u, 0u, 0u);
-    transpose8_bf16(rows, cols);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) *reinterpret_cast<uint4*>(dcol + e * ldc) = cols[e];
-}
-__device__ __forceinline__ void commit_v(const Raw<F32>& u, int rows_live, float* dcol, int ldc) {
-    float x[8][8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) raw_row(u, r, x[r]);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        float col[8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) col[r] = (r < rows_live) ? x[r][e] : 0.f;
-        store8(dcol + e * ldc, col);
+        for (int i = 0; i < N; i += 4) reinterpret_cast<uint4*>(p)[i / 4] = make_uint4(w[i], w[i + 1], w[i + 2], w[i + 3]);
     }
 }
+
+template <class E, int IW>
+__device__ __forceinline__ void issue_item(Item<E, IW>& it, const typename E::st* base, int rs, int rows_live) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) load_words<Item<E, IW>::WPR>(it.w[r], base + min(r, rows_live - 1) * rs);
+}
+
+// Row r of an item widened to fp32 (zero past rows_live).
+template <class E, int IW>
+__device__ __forceinline__ void item_row(const Item<E, IW>& it, int r, int rows_live, float* f) {
+    const bool live = r < rows_live;
+    if constexpr (sizeof(typename E::st) == 2) {
+#pragma unroll
+        for (int i = 0; i < IW / 2; ++i) {
+            const uint32_t x = live ? it.w[r][i] : 0u;
+            f[2 * i] = __uint_as_float(x << 16);
+            f[2 * i + 1] = __uint_as_float(x & 0xffff0000u);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < IW; ++i) f[i] = live ? __uint_as_float(it.w[r][i]) : 0.f;
+    }
+}
+
+// IW fp32 values stored as one row segment (rounded to the storage type).
+template <class E, int IW>
+__device__ __forceinline__ void store_row(typename E::st* dst, const float* f) {
+    if constexpr (sizeof(typename E::st) == 2) {
+        uint32_t w[IW / 2];
+#pragma unroll
+        for (int i = 0; i < IW / 2; ++i) w[i] = pack2_bf16(f[2 * i], f[2 * i + 1]);
+        store_words<IW / 2>(dst, w);
+    } else {
+        uint32_t w[IW];
+#pragma unroll
+        for (int i = 0; i < IW; ++i) w[i] = __float_as_uint(f[i]);
+        store_words<IW>(dst, w);
+    }
+}
+
+// Column e of 8 rows x[r][e] stored as 8 consecutive tokens (16 bytes bf16, 32 bytes fp32).
+template <class E, int IW>
+__device__ __forceinline__ void store_col(typename E::st* dst, const float (&x)[8][IW], int e) {
+    if constexpr (sizeof(typename E::st) == 2) {
+        uint32_t w[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) w[m] = pack2_bf16(x[2 * m][e], x[2 * m + 1][e]);
+        store_words<4>(dst, w);
+    } else {
+        uint32_t w[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) w[r] = __float_as_uint(x[r][e]);
+        store_words<8>(dst, w);
+    }
+}
+
+// Rotation of NP pairs along 8 consecutive tokens: the factors of the first token are evaluated accurately;
+// each next token's factors are the previous ones turned by the one-token step (angle addition). The step
+// factors (cos theta_i, sin theta_i) are evaluated once per kernel by the caller.
+template <int NP>
+struct RotStep {
+    float dc[NP], ds[NP];
+    __device__ __forceinline__ void init(const double* theta, int pair0) {
+#pragma unroll
+        for (int j = 0; j < NP; ++j) rot_cs(1, theta[pair0 + j], &dc[j], &ds[j]);
+    }
+};
+template <int NP>
+struct Rot8 {
+    float c[NP], s[NP];
+    __device__ __forceinline__ void init(const double* theta, int pair0, long long p0) {
+#pragma unroll
+        for (int j = 0; j < NP; ++j) rot_cs(p0, theta[pair0 + j], &c[j], &s[j]);
+    }
+    __device__ __forceinline__ void apply(float* x) const {
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+            const float a0 = x[2 * j], a1 = x[2 * j + 1];
+            x[2 * j] = a0 * c[j] - a1 * s[j];
+            x[2 * j + 1] = a0 * s[j] + a1 * c[j];
+        }
+    }
+    __device__ __forceinline__ void step(const RotStep<NP>& st) {
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+            const float nc = c[j] * st.dc[j] - s[j] * st.ds[j];
+            s[j] = s[j] * st.dc[j] + c[j] * st.ds[j];
+            c[j] = nc;
+        }
+    }
+};
+
+// Q and K items of the same 8 tokens x IW dims: Q -> sQ rows, K -> sK rows and sKc columns (token r scaled
+// by zeta[r] before rounding). Destinations are chosen at compile time.
+template <class E, int IW, bool HAS_Q, bool HAS_KROW>
+__device__ __forceinline__ void commit_qk(const Item<E, IW>* qi, const Item<E, IW>& ki, int rows_live, bool rotate,
+                                          const double* theta, int pair0, long long p0, const RotStep<IW / 2>& rs,
+                                          const float* zeta, typename E::st* dq, int ldq, typename E::st* dkr,
+                                          int ldk, typename E::st* dkc, int ldc) {
+    Rot8<IW / 2> rot;
+    if (rotate) rot.init(theta, pair0, p0);
+    float kx[8][IW];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        float qx[IW];
+        if constexpr (HAS_Q) item_row<E, IW>(*qi, r, rows_live, qx);
+        item_row<E, IW>(ki, r, rows_live, kx[r]);
+        if (rotate) {
+            if constexpr (HAS_Q) rot.apply(qx);
+            rot.apply(kx[r]);
+            rot.step(rs);
+        }
+        if constexpr (HAS_Q) store_row<E, IW>(dq + r * ldq, qx);
+        if constexpr (HAS_KROW) store_row<E, IW>(dkr + r * ldk, kx[r]);
+#pragma unroll
+        for (int e = 0; e < IW; ++e) kx[r][e] *= zeta[r];
+    }
+#pragma unroll
+    for (int e = 0; e < IW; ++e) store_col<E, IW>(dkc + e * ldc, kx, e);
+}
+
+// zeta[r] = gamma^(zexp0 - r) for the 8 rows of an item (0 for rows at or past rows_live).
+__device__ __forceinline__ void item_zeta(float* zeta, float log2g, int zexp0, int rows_live) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) zeta[r] = r < rows_live ? gpow(log2g, (float)(zexp0 - r)) : 0.f;
+}
+
+// V item -> sVc columns.
+template <class E, int IW>
+__device__ __forceinline__ void commit_vcol(const Item<E, IW>& vi, int rows_live, typename E::st* dvc, int ldc) {
+    float x[8][IW];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) item_row<E, IW>(vi, r, rows_live, x[r]);
+#pragma unroll
+    for (int e = 0; e < IW; ++e) store_col<E, IW>(dvc + e * ldc, x, e);
+}
+
+// Item width for a CT x W tile: about one item per thread (at least one rotation pair, at most 8 dims), and
+// the number of items each thread handles.
+template <int CT, int W>
+struct ItemWidth {
+    static constexpr int raw = CT * W / (8 * kThreads);
+    static constexpr int value = raw <= 2 ? 2 : raw <= 4 ? 4 : 8;
+    static constexpr int count = (CT / 8) * (W / value);
+    static constexpr int per_thread = (count + kThreads - 1) / kThreads;
+    static_assert(W % value == 0, "item width");
+};
 
 }  // namespace ret
