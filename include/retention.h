@@ -77,7 +77,8 @@ ret_status_t ret_parallel_fwd(const void* q, const void* k, const void* v, void*
 /*
  * Workspace (device bytes) that ret_chunkwise_fwd uses to split each sequence into segments that run in
  * parallel (a two-level scan of the chunk state). 0 means the call runs one segment per (b, h) and needs
- * none. Passing a smaller workspace than this is allowed: the call then uses fewer segments.
+ * none. Passing a smaller workspace than this is allowed: the call then uses fewer segments. The workspace
+ * needs no initialisation; calls sharing a workspace must not overlap in time (on one stream they do not).
  */
 size_t ret_chunkwise_workspace_bytes(int B, int N, int H, int dk, int dv, int chunk, ret_dtype_t in_dt);
 

@@ -300,11 +300,11 @@ ret_status_t ret_recurrent_step(const void* q, const void* k, const void* v, voi
     for (int h = 0; h < H; ++h) A.gamma[h] = gamma[h];
     if (theta)
         for (int i = 0; i < dk / 2; ++i) A.theta[i] = theta[i];
-    step_kernel_t fn = step_kernel_get(dk);
+    step_kernel_t fn = step_kernel_get(in_dt == RET_BF16, dk);
     if (!fn) return fail(RET_ERR_UNSUPPORTED, "decode step: d_k=%d not in {16,32,64,128,256}", dk);
     hipStream_t s = (hipStream_t)stream;
     LaunchTimer tm("ret_recurrent_step", s);
-    hipLaunchKernelGGL(fn, dim3((dv + 63) / 64, B * H), dim3(kThreads), 0, s, A);
+    hipLaunchKernelGGL(fn, dim3((dv + 63) / 64, B * H), dim3(dk >= 64 ? dk : 64), 0, s, A);
     tm.done();
     return launch_status("ret_recurrent_step");
 }

@@ -121,26 +121,58 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_full_kernel(FwdArgs a) {
     const int dv0 = dvt * DVT;
     const float lg = a.log2g[h];
     const int osz = a.out_bf16 ? 2 : 4;
+    const long long seg_t0 = (long long)seg * a.seg_len;
+    const long long seg_t1 = min((long long)a.N, seg_t0 + a.seg_len);
+    const int nchunks = (int)((seg_t1 - seg_t0 + C - 1) / C);
+    const int nst = nchunks * F::NSL;
+    const int rsk = a.H * a.dk, rsv = a.H * a.dv;
 
-    // Scores above the diagonal are never written: keep them zero for the P.V product.
-    for (int i = tid; i < F::SP; i += kThreads) sP[i] = (st)0;
-
-    // Decay factors that do not depend on the chunk: the mask gamma^(j-l) of each owned S^T tile (rows l,
-    // columns j) and xi_j = gamma^(j+1) of each owned O^T tile (columns j).
-    // S^T tiles of this wave: t = w + 4x in row-by-row lower-triangle order.
-    int Sjb[F::NS_W], Slb[F::NS_W];
-    float Dm[F::NS_W][4], Xi[F::NO_W];
+    // This thread's staging items: token block and first dim; pointers at the segment's first chunk.
+    int qtb[NIQ], qdb[NIQ], vtb[NIV], vdb[NIV];
+    const st *qp[NIQ], *kp[NIQ], *vp[NIV];
 #pragma unroll
-    for (int x = 0; x < F::NS_W; ++x) {
-        tri_tile<F::NB>(min(w + kWaves * x, F::NS - 1), Sjb[x], Slb[x]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int d = 16 * (Sjb[x] - Slb[x]) + n16 - g4 - e;  // j - l
-            Dm[x][e] = d >= 0 ? gpow(lg, (float)d) : 0.f;
-        }
+    for (int j = 0; j < NIQ; ++j) {
+        const int x = min(tid + kThreads * j, F::IQK::count - 1);
+        qtb[j] = x / (F::KS / IQ);
+        qdb[j] = x % (F::KS / IQ);
+        const long long off = (((long long)b * a.N + seg_t0 + qtb[j] * 8) * a.H + h) * a.dk + qdb[j] * IQ;
+        qp[j] = (const st*)a.q + off;
+        kp[j] = (const st*)a.k + off;
     }
 #pragma unroll
-    for (int x = 0; x < F::NO_W; ++x) Xi[x] = gpow(lg, (float)(ojb<F>(w, x) * 16 + n16 + 1));
+    for (int j = 0; j < NIV; ++j) {
+        const int x = min(tid + kThreads * j, F::IV::count - 1);
+        vtb[j] = x / (DVT / IVW);
+        vdb[j] = x % (DVT / IVW);
+        vp[j] = (const st*)a.v + (((long long)b * a.N + seg_t0 + vtb[j] * 8) * a.H + h) * a.dv + dv0 + vdb[j] * IVW;
+    }
+
+    // NBUF register buffers: the loads of stage i + NBUF are issued as soon as stage i has been committed.
+    // Two buffers where the registers allow it (chunks up to 64 tokens), else one.
+    constexpr int NBUF = C <= 64 ? 2 : 1;
+    Item<E, IQ> bq[NBUF][NIQ], bk[NBUF][NIQ];
+    Item<E, IVW> bv[NBUF][NIV];
+    auto issue = [&](int i, auto parc) __attribute__((always_inline)) {
+        constexpr int par = decltype(parc)::value;
+        const int c = i / F::NSL, sl = i % F::NSL;
+        const int L = (int)min((long long)C, seg_t1 - seg_t0 - (long long)c * C);
+        const long long cq = (long long)c * C * rsk + sl * F::KS;
+#pragma unroll
+        for (int j = 0; j < NIQ; ++j)
+            if (tid + kThreads * j < F::IQK::count) {
+                issue_item<E, IQ>(bq[par][j], qp[j] + cq, rsk, L - qtb[j] * 8);
+                issue_item<E, IQ>(bk[par][j], kp[j] + cq, rsk, L - qtb[j] * 8);
+            }
+        if (sl == 0) {
+            const long long cv = (long long)c * C * rsv;
+#pragma unroll
+            for (int j = 0; j < NIV; ++j)
+                if (tid + kThreads * j < F::IV::count) issue_item<E, IVW>(bv[par][j], vp[j] + cv, rsv, L - vtb[j] * 8);
+        }
+    };
+    if (nst > 0) issue(0, std::integral_constant<int, 0>{});
+    if constexpr (NBUF == 2)
+        if (nst > 1) issue(1, std::integral_constant<int, NBUF - 1>{});
 
     // Initial state for this segment: the segment-scan result, state_in, or zeros.
     const float* init = nullptr;
@@ -159,6 +191,37 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_full_kernel(FwdArgs a) {
             for (int e = 0; e < 4; ++e) R[i][e] = init[(long long)(rb * 16 + g4 + e) * a.dv + dv0 + cb * 16 + n16];
         }
     }
+
+    // Scores above the diagonal are never written: keep them zero for the P.V product.
+    for (int i = tid; i < F::SP; i += kThreads) sP[i] = (st)0;
+
+    // Decay factors that do not depend on the chunk: the mask gamma^(j-l) of each owned S^T tile (rows l,
+    // columns j) and xi_j = gamma^(j+1) of each owned O^T tile (columns j). S^T tiles of this wave: t = w + 4x
+    // in row-by-row lower-triangle order.
+    int Sjb[F::NS_W], Slb[F::NS_W];
+    float Dm[F::NS_W][4], Xi[F::NO_W];
+#pragma unroll
+    for (int x = 0; x < F::NS_W; ++x) {
+        tri_tile<F::NB>(min(w + kWaves * x, F::NS - 1), Sjb[x], Slb[x]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int d = 16 * (Sjb[x] - Slb[x]) + n16 - g4 - e;  // j - l
+            Dm[x][e] = d >= 0 ? gpow(lg, (float)d) : 0.f;
+        }
+    }
+#pragma unroll
+    for (int x = 0; x < F::NO_W; ++x) Xi[x] = gpow(lg, (float)(ojb<F>(w, x) * 16 + n16 + 1));
+    RotStep<IQ / 2> rstep[NIQ][F::NSL];
+    float zfull[NIQ][8];
+#pragma unroll
+    for (int j = 0; j < NIQ; ++j) {
+#pragma unroll
+        for (int sl = 0; sl < F::NSL; ++sl)
+            if (a.rotate) rstep[j][sl].init(a.theta, (sl * F::KS + qdb[j] * IQ) / 2);
+        item_zeta(zfull[j], lg, C - 1 - qtb[j] * 8, 8);
+    }
+    const float gC = gpow(lg, (float)C);
+
     // Copy of R (operand precision), transposed to [d_v][d_k], for the cross product.
 #pragma unroll
     for (int i = 0; i < F::NR_W; ++i) {
@@ -169,58 +232,9 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_full_kernel(FwdArgs a) {
         }
     }
 
-    const long long seg_t0 = (long long)seg * a.seg_len;
-    const long long seg_t1 = min((long long)a.N, seg_t0 + a.seg_len);
-    const int nst = (int)((seg_t1 - seg_t0 + C - 1) / C) * F::NSL;
-    const int rsk = a.H * a.dk, rsv = a.H * a.dv;
-    // This thread's staging items: token block and first dim; pointers at the segment's first chunk.
-    int qtb[NIQ], qdb[NIQ], vtb[NIV], vdb[NIV];
-    const st *qp[NIQ], *kp[NIQ], *vp[NIV];
-    RotStep<IQ / 2> rstep[NIQ][F::NSL];
-    float zfull[NIQ][8];
-#pragma unroll
-    for (int j = 0; j < NIQ; ++j) {
-        const int x = min(tid + kThreads * j, F::IQK::count - 1);
-        qtb[j] = x / (F::KS / IQ);
-        qdb[j] = x % (F::KS / IQ);
-        const long long off = (((long long)b * a.N + seg_t0 + qtb[j] * 8) * a.H + h) * a.dk + qdb[j] * IQ;
-        qp[j] = (const st*)a.q + off;
-        kp[j] = (const st*)a.k + off;
-#pragma unroll
-        for (int sl = 0; sl < F::NSL; ++sl)
-            if (a.rotate) rstep[j][sl].init(a.theta, (sl * F::KS + qdb[j] * IQ) / 2);
-        item_zeta(zfull[j], lg, C - 1 - qtb[j] * 8, 8);
-    }
-#pragma unroll
-    for (int j = 0; j < NIV; ++j) {
-        const int x = min(tid + kThreads * j, F::IV::count - 1);
-        vtb[j] = x / (DVT / IVW);
-        vdb[j] = x % (DVT / IVW);
-        vp[j] = (const st*)a.v + (((long long)b * a.N + seg_t0 + vtb[j] * 8) * a.H + h) * a.dv + dv0 + vdb[j] * IVW;
-    }
-    const float gC = gpow(lg, (float)C);
-
-    Item<E, IQ> bq[NIQ], bk[NIQ];
-    Item<E, IVW> bv[NIV];
-    auto issue = [&](int i) {
-        const int c = i / F::NSL, sl = i % F::NSL;
-        const int L = (int)min((long long)C, seg_t1 - seg_t0 - (long long)c * C);
-        const long long cq = (long long)c * C * rsk + sl * F::KS;
-#pragma unroll
-        for (int j = 0; j < NIQ; ++j)
-            if (tid + kThreads * j < F::IQK::count) {
-                issue_item<E, IQ>(bq[j], qp[j] + cq, rsk, L - qtb[j] * 8);
-                issue_item<E, IQ>(bk[j], kp[j] + cq, rsk, L - qtb[j] * 8);
-            }
-        if (sl == 0) {
-            const long long cv = (long long)c * C * rsv;
-#pragma unroll
-            for (int j = 0; j < NIV; ++j)
-                if (tid + kThreads * j < F::IV::count) issue_item<E, IVW>(bv[j], vp[j] + cv, rsv, L - vtb[j] * 8);
-        }
-    };
-    auto commit = [&](int i) {
-        const int c = i / F::NSL, sl = i % F::NSL;
+    auto commit = [&](int i, auto parc, auto slc) __attribute__((always_inline)) {
+        constexpr int par = decltype(parc)::value, sl = decltype(slc)::value;
+        const int c = i / F::NSL;
         const long long t0 = seg_t0 + (long long)c * C;
         const int L = (int)min((long long)C, seg_t1 - t0);
 #pragma unroll
@@ -233,27 +247,23 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_full_kernel(FwdArgs a) {
                 } else {
                     item_zeta(zt, lg, L - 1 - qtb[j] * 8, L - qtb[j] * 8);
                 }
-                RotStep<IQ / 2> rs = rstep[j][0];
-#pragma unroll
-                for (int x = 1; x < F::NSL; ++x)
-                    if (sl == x) rs = rstep[j][x];
-                commit_qk<E, IQ, true, true>(&bq[j], bk[j], L - qtb[j] * 8, a.rotate, a.theta,
-                                             (sl * F::KS + qdb[j] * IQ) / 2, a.pos0 + t0 + qtb[j] * 8, rs, zt,
-                                             sQ + qtb[j] * 8 * F::LDQ + qdb[j] * IQ, F::LDQ,
+                commit_qk<E, IQ, true, true>(&bq[par][j], bk[par][j], L - qtb[j] * 8, a.rotate, a.theta,
+                                             (sl * F::KS + qdb[j] * IQ) / 2, a.pos0 + t0 + qtb[j] * 8, rstep[j][sl],
+                                             zt, sQ + qtb[j] * 8 * F::LDQ + qdb[j] * IQ, F::LDQ,
                                              sK + qtb[j] * 8 * F::LDQ + qdb[j] * IQ, F::LDQ,
                                              sKc + qdb[j] * IQ * F::LDC + qtb[j] * 8, F::LDC);
             }
-        if (sl == 0) {
+        if constexpr (sl == 0) {
 #pragma unroll
             for (int j = 0; j < NIV; ++j)
                 if (tid + kThreads * j < F::IV::count)
-                    commit_vcol<E, IVW>(bv[j], L - vtb[j] * 8, sVc + vdb[j] * IVW * F::LDC + vtb[j] * 8, F::LDC);
+                    commit_vcol<E, IVW>(bv[par][j], L - vtb[j] * 8, sVc + vdb[j] * IVW * F::LDC + vtb[j] * 8, F::LDC);
         }
     };
 
-    const int nchunks = nst / F::NSL;
-    if (nst > 0) issue(0);
-    for (int c = 0; c < nchunks; ++c) {
+    // One chunk; cpar is the chunk's parity, so every stage's buffer parity is known at compile time.
+    auto chunk = [&](int c, auto cparc) __attribute__((always_inline)) {
+        constexpr int cpar = decltype(cparc)::value;
         const long long t0 = seg_t0 + (long long)c * C;
         const int L = (int)min((long long)C, seg_t1 - t0);
         const float gL = L == C ? gC : gpow(lg, (float)L);
@@ -262,12 +272,13 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_full_kernel(FwdArgs a) {
         for (int x = 0; x < F::NS_W; ++x) S[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int x = 0; x < F::NO_W; ++x) O[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        static_for<0, F::NSL>([&](auto slc) {
+        static_for<0, F::NSL>([&](auto slc) __attribute__((always_inline)) {
             constexpr int sl = decltype(slc)::value;
+            constexpr int par = NBUF == 2 ? (cpar * F::NSL + sl) & 1 : 0;
             const int i = c * F::NSL + sl;
             __syncthreads();  // staging buffers free; previous copies of R and of the output tile consumed
-            commit(i);
-            if (i + 1 < nst) issue(i + 1);
+            commit(i, std::integral_constant<int, par>{}, slc);
+            if (i + NBUF < nst) issue(i + NBUF, std::integral_constant<int, par>{});
             __syncthreads();
             // S^T += K_s Q_s^T over this wave's lower-triangle tiles (keys l <= queries j). Slots past the last
             // tile repeat it; their results are never stored.
@@ -340,7 +351,13 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_full_kernel(FwdArgs a) {
             *reinterpret_cast<uint4*>(obase + ((long long)j * rsv + c16 * vec) * osz) =
                 *reinterpret_cast<const uint4*>(sO + (j * F::LDO + c16 * vec) * osz);
         }
+    };
+
+    for (int c = 0; c < nchunks; c += 2) {
+        chunk(c, std::integral_constant<int, 0>{});
+        if (c + 1 < nchunks) chunk(c + 1, std::integral_constant<int, 1>{});
     }
+
     // The state after the last token of the sequence.
     if (seg == a.nseg - 1 && a.state_out) {
         float* out = a.state_out + (long long)pair * DK * a.dv;
@@ -401,7 +418,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_local_kernel(FwdArgs a) {
     constexpr int IKW = F::IK::value, IVW = F::IV::value;
     Item<E, IKW> bk[F::IK::per_thread];
     Item<E, IVW> bv[F::IV::per_thread];
-    auto issue = [&](int i) {
+    auto issue = [&](int i) __attribute__((always_inline)) {
         const long long t0 = seg_t0 + (long long)i * C;
         const int L = (int)min((long long)C, seg_t1 - t0);
 #pragma unroll
@@ -421,7 +438,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_local_kernel(FwdArgs a) {
             }
         }
     };
-    auto commit = [&](int i) {
+    auto commit = [&](int i) __attribute__((always_inline)) {
         const long long t0 = seg_t0 + (long long)i * C;
         const int L = (int)min((long long)C, seg_t1 - t0);
 #pragma unroll
@@ -478,6 +495,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_local_kernel(FwdArgs a) {
                 out[(long long)(rb * 16 + 4 * (lane >> 4) + e) * a.dv + dv0 + cb * 16 + (lane & 15)] = R[i][e];
         }
     }
+
 }
 
 // ---------------------------------------------------------------------------------------------------
@@ -580,9 +598,12 @@ __global__ __launch_bounds__(kThreads, 2) void parallel_kernel(FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------------
-// recurrent_step: one workgroup per (64-column d_v tile, b*H + h). Thread (rg, cg): columns 4cg..4cg+3 of the
-// tile, rows rg, rg+16, ... Each row update S = gamma S + k_r v is a float4 read-modify-write; the partial
-// sums of o = q S are reduced over the 16 row groups in LDS.
+// recurrent_step: one workgroup per (64-column d_v tile, b*H + h) with one wave per 64 state rows. Lane
+// (rg, cg) of a wave owns columns 4cg..4cg+3 and 16 consecutive rows of the wave's 64 (rg = lane / 16): its
+// rows are read first (16 float4 loads in flight), updated S = gamma S + k_r v and written back in place,
+// while o = q S is summed over its rows, then over the four row groups with lane shuffles, then over the
+// waves through LDS. The rotation factors of the wave's 32 pairs are evaluated one pair per lane and shared
+// with shuffles.
 // ---------------------------------------------------------------------------------------------------
 struct StepArgs {
     const void* q;
@@ -601,81 +622,120 @@ __device__ __forceinline__ float ld_in(const void* p, long long i, int bf) {
     return bf ? bf16_to_f32(((const uint16_t*)p)[i]) : ((const float*)p)[i];
 }
 
-template <int DK>
-__global__ __launch_bounds__(kThreads) void recurrent_step_kernel(StepArgs a) {
-    __shared__ float sq[DK], sk[DK];
-    __shared__ float4 part[16][16];
-    const int tid = threadIdx.x, cg = tid & 15, rg = tid >> 4;
+// n consecutive input elements (fp32 or bf16) widened to fp32, loaded as 16/8-byte vectors.
+template <class E, int N>
+__device__ __forceinline__ void load_n(const typename E::st* p, float* f) {
+    if constexpr (sizeof(typename E::st) == 2) {
+        static_assert(N % 4 == 0, "bf16 vector loads");
+        if constexpr (N % 8 == 0) {
+#pragma unroll
+            for (int i = 0; i < N; i += 8) load8(p + i, f + i);
+        } else {
+#pragma unroll
+            for (int i = 0; i < N; i += 4) {
+                const uint2 u = *reinterpret_cast<const uint2*>(p + i);
+                f[i] = __uint_as_float(u.x << 16);
+                f[i + 1] = __uint_as_float(u.x & 0xffff0000u);
+                f[i + 2] = __uint_as_float(u.y << 16);
+                f[i + 3] = __uint_as_float(u.y & 0xffff0000u);
+            }
+        }
+    } else {
+        static_assert(N % 4 == 0, "fp32 vector loads");
+#pragma unroll
+        for (int i = 0; i < N; i += 4) {
+            const float4 x = *reinterpret_cast<const float4*>(p + i);
+            f[i] = x.x;
+            f[i + 1] = x.y;
+            f[i + 2] = x.z;
+            f[i + 3] = x.w;
+        }
+    }
+}
+
+template <class E, int DK>
+__global__ __launch_bounds__(DK >= 64 ? DK : 64) void recurrent_step_kernel(StepArgs a) {
+    typedef typename E::st st;
+    constexpr int NW = DK >= 64 ? DK / 64 : 1;  // waves: 64 rows each
+    constexpr int WR = DK / NW;                 // rows per wave
+    constexpr int RPT = WR / 4;                 // rows per lane
+    __shared__ float4 part[NW > 1 ? NW : 1][16];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int cg = lane & 15, rg = lane >> 4;
     const int pair = blockIdx.y, h = pair % a.H;
     const int c0 = blockIdx.x * 64 + 4 * cg;
-    const long long qk0 = (long long)pair * a.dk;
-    // Rotated q and k (fp32) for this head and position.
-    for (int i = tid; i < a.dk / 2; i += kThreads) {
-        float q0 = ld_in(a.q, qk0 + 2 * i, a.in_bf16), q1 = ld_in(a.q, qk0 + 2 * i + 1, a.in_bf16);
-        float k0 = ld_in(a.k, qk0 + 2 * i, a.in_bf16), k1 = ld_in(a.k, qk0 + 2 * i + 1, a.in_bf16);
-        if (a.rotate) {
-            float c, sn;
-            rot_cs(a.pos, a.theta[i], &c, &sn);
-            sq[2 * i] = q0 * c - q1 * sn;
-            sq[2 * i + 1] = q0 * sn + q1 * c;
-            sk[2 * i] = k0 * c - k1 * sn;
-            sk[2 * i + 1] = k0 * sn + k1 * c;
-        } else {
-            sq[2 * i] = q0;
-            sq[2 * i + 1] = q1;
-            sk[2 * i] = k0;
-            sk[2 * i + 1] = k1;
+    const bool active = c0 < a.dv;
+    const int r0 = wv * WR + rg * RPT;  // first row of this lane
+    // The state rows are read first so that their latency overlaps everything else.
+    float* S = a.state + (long long)pair * DK * a.dv + (active ? c0 : 0);
+    float4 x[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) x[i] = *reinterpret_cast<const float4*>(S + (long long)(r0 + i) * a.dv);
+    float vv[4], qv[RPT], kv[RPT];
+    load_n<E, 4>((const st*)a.v + (long long)pair * a.dv + (active ? c0 : 0), vv);
+    load_n<E, RPT>((const st*)a.q + (long long)pair * a.dk + r0, qv);
+    load_n<E, RPT>((const st*)a.k + (long long)pair * a.dk + r0, kv);
+    if (a.rotate) {
+        // Lane j evaluates pair wv*WR/2 + j (j < WR/2); the lane owning rows r0.. takes pairs r0/2 + p.
+        float cj = 1.f, sj = 0.f;
+        if (lane < WR / 2) rot_cs(a.pos, a.theta[wv * WR / 2 + lane], &cj, &sj);
+#pragma unroll
+        for (int p = 0; p < RPT / 2; ++p) {
+            const int src = rg * (RPT / 2) + p;
+            const float c = __shfl(cj, src), sn = __shfl(sj, src);
+            const float q0 = qv[2 * p], q1 = qv[2 * p + 1], k0 = kv[2 * p], k1 = kv[2 * p + 1];
+            qv[2 * p] = q0 * c - q1 * sn;
+            qv[2 * p + 1] = q0 * sn + q1 * c;
+            kv[2 * p] = k0 * c - k1 * sn;
+            kv[2 * p + 1] = k0 * sn + k1 * c;
         }
     }
-    const bool active = c0 < a.dv;
-    float4 vv = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (active) {
-        const long long vo = (long long)pair * a.dv + c0;
-        vv = make_float4(ld_in(a.v, vo, a.in_bf16), ld_in(a.v, vo + 1, a.in_bf16), ld_in(a.v, vo + 2, a.in_bf16),
-                         ld_in(a.v, vo + 3, a.in_bf16));
-    }
-    __syncthreads();
     const float g = a.gamma[h];
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (active) {
-        constexpr int RPT = DK / 16;  // rows per thread
-        float* S = a.state + (long long)pair * DK * a.dv + c0;
-        float4 x[RPT];
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) x[i] = *reinterpret_cast<const float4*>(S + (long long)(rg + 16 * i) * a.dv);
-#pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            const int r = rg + 16 * i;
-            const float kr = sk[r], qr = sq[r];
-            x[i].x = g * x[i].x + kr * vv.x;
-            x[i].y = g * x[i].y + kr * vv.y;
-            x[i].z = g * x[i].z + kr * vv.z;
-            x[i].w = g * x[i].w + kr * vv.w;
-            acc.x += qr * x[i].x;
-            acc.y += qr * x[i].y;
-            acc.z += qr * x[i].z;
-            acc.w += qr * x[i].w;
-        }
-#pragma unroll
-        for (int i = 0; i < RPT; ++i) *reinterpret_cast<float4*>(S + (long long)(rg + 16 * i) * a.dv) = x[i];
+    for (int i = 0; i < RPT; ++i) {
+        x[i].x = g * x[i].x + kv[i] * vv[0];
+        x[i].y = g * x[i].y + kv[i] * vv[1];
+        x[i].z = g * x[i].z + kv[i] * vv[2];
+        x[i].w = g * x[i].w + kv[i] * vv[3];
+        acc.x += qv[i] * x[i].x;
+        acc.y += qv[i] * x[i].y;
+        acc.z += qv[i] * x[i].z;
+        acc.w += qv[i] * x[i].w;
     }
-    part[rg][cg] = acc;
-    __syncthreads();
-    if (tid < 64) {
-        const int cgo = tid >> 2, comp = tid & 3;
-        float sum = 0.f;
+    if (active) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float4 p = part[r][cgo];
-            sum += comp == 0 ? p.x : comp == 1 ? p.y : comp == 2 ? p.z : p.w;
+        for (int i = 0; i < RPT; ++i) *reinterpret_cast<float4*>(S + (long long)(r0 + i) * a.dv) = x[i];
+    }
+    // Sum over the four row groups of the wave (lanes 16 and 32 apart).
+#pragma unroll
+    for (int m = 16; m <= 32; m *= 2) {
+        acc.x += __shfl_xor(acc.x, m);
+        acc.y += __shfl_xor(acc.y, m);
+        acc.z += __shfl_xor(acc.z, m);
+        acc.w += __shfl_xor(acc.w, m);
+    }
+    if constexpr (NW > 1) {
+        if (rg == 0) part[wv][cg] = acc;
+        __syncthreads();
+        if (wv != 0) return;
+        acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int w2 = 0; w2 < NW; ++w2) {
+            const float4 p = part[w2][cg];
+            acc.x += p.x;
+            acc.y += p.y;
+            acc.z += p.z;
+            acc.w += p.w;
         }
-        const int col = blockIdx.x * 64 + tid;
-        if (col < a.dv) {
-            const long long off = (long long)pair * a.dv + col;
-            if (a.out_bf16)
-                store_out((uint16_t*)a.o + off, sum);
-            else
-                store_out((float*)a.o + off, sum);
+    }
+    if (rg == 0 && active) {
+        const long long off = (long long)pair * a.dv + c0;
+        if (a.out_bf16) {
+            *reinterpret_cast<uint2*>((uint16_t*)a.o + off) =
+                make_uint2(pack2_bf16(acc.x, acc.y), pack2_bf16(acc.z, acc.w));
+        } else {
+            *reinterpret_cast<float4*>((float*)a.o + off) = acc;
         }
     }
 }
@@ -703,12 +763,12 @@ ChunkKernels chunk_entry() {
 }
 
 // Getters, one per kernel-group source. Return false when the shape has no instance.
+fwd_kernel_t segment_scan_get();
 bool chunk_kernels_f32(int dk, int dv, int C, ChunkKernels* out);
 bool chunk_kernels_bf16_small(int dk, int dv, int C, ChunkKernels* out);   // d_k in {32, 64}
 bool chunk_kernels_bf16_128(int dk, int dv, int C, ChunkKernels* out);     // d_k = 128
 bool chunk_kernels_bf16_256(int dk, int dv, int C, ChunkKernels* out);     // d_k = 256
 bool parallel_kernel_get(bool bf16_in, int dk, int dv, ParKernel* out);
-step_kernel_t step_kernel_get(int dk);
-fwd_kernel_t segment_scan_get();
+step_kernel_t step_kernel_get(bool bf16_in, int dk);
 
 }  // namespace ret

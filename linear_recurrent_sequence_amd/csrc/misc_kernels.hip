@@ -53,15 +53,19 @@ bool parallel_kernel_get(bool bf16_in, int dk, int dv, ParKernel* out) {
     return false;
 }
 
-step_kernel_t step_kernel_get(int dk) {
-    switch (dk) {
-        case 16: return recurrent_step_kernel<16>;
-        case 32: return recurrent_step_kernel<32>;
-        case 64: return recurrent_step_kernel<64>;
-        case 128: return recurrent_step_kernel<128>;
-        case 256: return recurrent_step_kernel<256>;
-        default: return nullptr;
+step_kernel_t step_kernel_get(bool bf16_in, int dk) {
+#define RET_STEP(E)                                 \
+    switch (dk) {                                   \
+        case 16: return recurrent_step_kernel<E, 16>;   \
+        case 32: return recurrent_step_kernel<E, 32>;   \
+        case 64: return recurrent_step_kernel<E, 64>;   \
+        case 128: return recurrent_step_kernel<E, 128>; \
+        case 256: return recurrent_step_kernel<E, 256>; \
+        default: return nullptr;                    \
     }
+    if (bf16_in) RET_STEP(BF16)
+    RET_STEP(F32)
+#undef RET_STEP
 }
 
 fwd_kernel_t segment_scan_get() { return segment_scan_kernel; }

@@ -128,7 +128,8 @@ def ret_chunkwise_workspace_bytes(B, N, H, dk, dv, chunk, in_dtype=torch.bfloat1
 
 
 def chunkwise_workspace(q, v, chunk):
-    """Allocate (with torch) the workspace ret_chunkwise_fwd plans for these shapes, or None."""
+    """Allocate (with torch) the workspace ret_chunkwise_fwd plans for these shapes, or None. Its contents need no
+    initialisation."""
     B, N, H, dk = q.shape
     nbytes = ret_chunkwise_workspace_bytes(B, N, H, dk, v.shape[3], chunk, q.dtype)
     if nbytes == 0:
