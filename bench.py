@@ -9,7 +9,7 @@ of each path's dominant kernel (per-launch HIP-event durations recorded by the l
 region), and the fp64 CPU oracle timed on this host.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2|4|5] [--no-decode]
-                       [--no-cpu-baseline] [--copy-calibration]
+                       [--no-cpu-baseline] [--copy-calibration] [--decode-steps S]
 """
 from __future__ import annotations
 
@@ -214,6 +214,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--decode-steps", type=int, default=1024, help="decode steps per graph (1024 in the workload)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
@@ -269,7 +270,7 @@ def main():
         },
     }
     if not args.no_decode:
-        dw, us_step, kernel_us = bench_decode(R, W, torch)
+        dw, us_step, kernel_us = bench_decode(R, W, torch, steps_graph=args.decode_steps)
         db, dflops = decode_algorithmic(dw.B, dw.H, dw.dk, dw.dv)
         ach = db / (kernel_us * 1e-6) / 1e9
         result["decode"] = {
