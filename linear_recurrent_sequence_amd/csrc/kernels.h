@@ -83,10 +83,17 @@ struct FullCfg {
     typedef ItemWidth<C, KS> IQK;                    // Q+K staging items per slice
     typedef ItemWidth<C, DVT> IV;                    // V staging items (first slice only)
     static constexpr int SQ = C * LDQ, SKC = KS * LDC, SVC = DVT * LDC, SP = C * LDC, SRT = DVT * LDR;
-    // Region A holds sQ, sK and sKc while a chunk's slices are computed, then the output tile (fp32 at most).
+    // Region A holds sQ, sK and sKc while a chunk's slices are computed. The output tile (fp32 at most) gets
+    // its own region when the LDS budget allows (SEP_O): its global stores then overlap the next chunk's
+    // staging. Otherwise it reuses region A once the chunk's slices are done.
     static constexpr int A_STAGE = (2 * SQ + SKC) * (int)sizeof(st), A_OUT = C * LDO * 4;
-    static constexpr int A_BYTES = ((A_STAGE > A_OUT ? A_STAGE : A_OUT) + 15) / 16 * 16;
-    static constexpr int LDS_BYTES = A_BYTES + (SVC + SP + SRT) * (int)sizeof(st);
+    static constexpr int REST = (SVC + SP + SRT) * (int)sizeof(st);
+    static constexpr int WITH_SEP = ((A_STAGE + 15) / 16 * 16) + REST + A_OUT;
+    static constexpr int WITHOUT_SEP = ((A_STAGE > A_OUT ? A_STAGE : A_OUT) + 15) / 16 * 16 + REST;
+    // (a separate tile must not cost a workgroup per CU: 80 KB is the two-workgroup limit)
+    static constexpr bool SEP_O = WITH_SEP <= 160 * 1024 && (WITH_SEP <= 80 * 1024 || WITHOUT_SEP > 80 * 1024);
+    static constexpr int A_BYTES = SEP_O ? (A_STAGE + 15) / 16 * 16 : ((A_STAGE > A_OUT ? A_STAGE : A_OUT) + 15) / 16 * 16;
+    static constexpr int LDS_BYTES = A_BYTES + REST + (SEP_O ? A_OUT : 0);
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     static_assert(C % 16 == 0 && DVT % 16 == 0 && DK % KS == 0 && KS % E::KD == 0 && C % E::KD == 0, "tiling");
 };
@@ -113,7 +120,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_full_kernel(FwdArgs a) {
     st* sVc = smem + F::A_BYTES / sizeof(st);
     st* sP = sVc + F::SVC;
     st* sRt = sP + F::SP;
-    char* sO = reinterpret_cast<char*>(smem);  // output tile, over region A once a chunk's slices are done
+    char* sO = F::SEP_O ? reinterpret_cast<char*>(sRt + F::SRT) : reinterpret_cast<char*>(smem);  // output tile
 
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g4 = 4 * (lane >> 4), n16 = lane & 15;
     const int seg = blockIdx.x, dvt = blockIdx.y, pair = blockIdx.z;
@@ -261,6 +268,21 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_full_kernel(FwdArgs a) {
         }
     };
 
+    // Coalesced 16-byte stores of output rows j < L of the chunk starting at t0 from the output tile.
+    auto store_out_tile = [&](long long t0, int L) __attribute__((always_inline)) {
+        const int vec = 16 / osz;  // elements per 16-byte store
+        const int per_row = DVT / vec;
+        char* obase = (char*)a.o + ((((long long)b * a.N + t0) * a.H + h) * a.dv + dv0) * osz;
+        for (int x = tid; x < L * per_row; x += kThreads) {
+            const int j = x / per_row, c16 = x % per_row;
+            *reinterpret_cast<uint4*>(obase + ((long long)j * rsv + c16 * vec) * osz) =
+                *reinterpret_cast<const uint4*>(sO + (j * F::LDO + c16 * vec) * osz);
+        }
+    };
+    // With four d_v blocks, each wave's O^T and R tiles share one d_v block, so the operand fragment of that
+    // block is read from LDS once per k-step and reused across the wave's tiles.
+    constexpr bool SHARED_DV = F::NDV == kWaves;
+
     // One chunk; cpar is the chunk's parity, so every stage's buffer parity is known at compile time.
     auto chunk = [&](int c, auto cparc) __attribute__((always_inline)) {
         constexpr int cpar = decltype(cparc)::value;
@@ -276,9 +298,13 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_full_kernel(FwdArgs a) {
             constexpr int sl = decltype(slc)::value;
             constexpr int par = NBUF == 2 ? (cpar * F::NSL + sl) & 1 : 0;
             const int i = c * F::NSL + sl;
-            __syncthreads();  // staging buffers free; previous copies of R and of the output tile consumed
+            // Staging buffers free: for a chunk's first slice with a separate output tile, the barrier that
+            // ended the previous chunk already guarantees it.
+            if (!(F::SEP_O && sl == 0 && c > 0)) __syncthreads();
             commit(i, std::integral_constant<int, par>{}, slc);
             if (i + NBUF < nst) issue(i + NBUF, std::integral_constant<int, par>{});
+            if constexpr (F::SEP_O && sl == 0)
+                if (c > 0) store_out_tile(t0 - C, C);  // the previous chunk's output, overlapping this staging
             __syncthreads();
             // S^T += K_s Q_s^T over this wave's lower-triangle tiles (keys l <= queries j). Slots past the last
             // tile repeat it; their results are never stored.
@@ -286,23 +312,45 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_full_kernel(FwdArgs a) {
             for (int x = 0; x < F::NS_W; ++x)
                 mma_nt(S[x], sK + Slb[x] * 16 * F::LDQ, F::LDQ, sQ + Sjb[x] * 16 * F::LDQ, F::LDQ, F::KS, lane);
             // O^T += R_s^T Q_s^T (cross-chunk read of the state carried in from the previous chunk).
+            if constexpr (SHARED_DV) {
 #pragma unroll
-            for (int x = 0; x < F::NO_W; ++x)
-                if (F::NO % kWaves == 0 || w + kWaves * x < F::NO) {
-                    const int jb = ojb<F>(w, x), db = odb<F>(w, x);
-                    mma_nt(O[x], sRt + db * 16 * F::LDR + sl * F::KS, F::LDR, sQ + jb * 16 * F::LDQ, F::LDQ, F::KS,
-                           lane);
+                for (int kk = 0; kk < F::KS; kk += E::KD) {
+                    const auto fa = frag(sRt + w * 16 * F::LDR + sl * F::KS, F::LDR, kk, lane);
+#pragma unroll
+                    for (int x = 0; x < F::NO_W; ++x) mfma(O[x], fa, frag(sQ + x * 16 * F::LDQ, F::LDQ, kk, lane));
                 }
-            // R_s <- gamma^L R_s + K_s^T (V (.) zeta): zeta is folded into sKc. R tile x of wave w covers d_k
-            // block rb = (w + 4x) / NDV; with four d_v blocks rb = x, known at compile time.
+            } else {
 #pragma unroll
-            for (int x = 0; x < F::NR_W; ++x) {
-                const int t = w + kWaves * x;
-                const int rb = F::NDV == kWaves ? x : t / F::NDV, cb = F::NDV == kWaves ? w : t % F::NDV;
-                if ((F::NR % kWaves == 0 || t < F::NR) && rb / (F::KS / 16) == sl) {
-                    R[x] *= gL;
-                    mma_nt(R[x], sKc + (rb - sl * (F::KS / 16)) * 16 * F::LDC, F::LDC, sVc + cb * 16 * F::LDC,
-                           F::LDC, C, lane);
+                for (int x = 0; x < F::NO_W; ++x)
+                    if (F::NO % kWaves == 0 || w + kWaves * x < F::NO) {
+                        const int jb = ojb<F>(w, x), db = odb<F>(w, x);
+                        mma_nt(O[x], sRt + db * 16 * F::LDR + sl * F::KS, F::LDR, sQ + jb * 16 * F::LDQ, F::LDQ,
+                               F::KS, lane);
+                    }
+            }
+            // R_s <- gamma^L R_s + K_s^T (V (.) zeta): zeta is folded into sKc. R tile x of wave w covers d_k
+            // block rb = (w + 4x) / NDV; with four d_v blocks rb = x and the d_v block is the wave's.
+            if constexpr (SHARED_DV) {
+                constexpr int XB = F::KS / 16;  // this slice's R tiles: x in [sl*XB, (sl+1)*XB)
+#pragma unroll
+                for (int x = sl * XB; x < (sl + 1) * XB; ++x) R[x] *= gL;
+#pragma unroll
+                for (int kk = 0; kk < C; kk += E::KD) {
+                    const auto fb = frag(sVc + w * 16 * F::LDC, F::LDC, kk, lane);
+#pragma unroll
+                    for (int x = sl * XB; x < (sl + 1) * XB; ++x)
+                        mfma(R[x], frag(sKc + (x - sl * XB) * 16 * F::LDC, F::LDC, kk, lane), fb);
+                }
+            } else {
+#pragma unroll
+                for (int x = 0; x < F::NR_W; ++x) {
+                    const int t = w + kWaves * x;
+                    const int rb = t / F::NDV, cb = t % F::NDV;
+                    if ((F::NR % kWaves == 0 || t < F::NR) && rb / (F::KS / 16) == sl) {
+                        R[x] *= gL;
+                        mma_nt(R[x], sKc + (rb - sl * (F::KS / 16)) * 16 * F::LDC, F::LDC, sVc + cb * 16 * F::LDC,
+                               F::LDC, C, lane);
+                    }
                 }
             }
         });
@@ -319,12 +367,24 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_full_kernel(FwdArgs a) {
         __syncthreads();  // P complete; all reads of sQ/sK/sKc/sRt for this chunk are done
         // O^T = xi (.) (R^T Q^T) + V^T P^T, then the output tile in LDS (4 consecutive d_v per store).
 #pragma unroll
+        for (int x = 0; x < F::NO_W; ++x) O[x] *= Xi[x];
+        if constexpr (SHARED_DV) {
+#pragma unroll
+            for (int kk = 0; kk < C; kk += E::KD) {
+                const auto fa = frag(sVc + w * 16 * F::LDC, F::LDC, kk, lane);
+#pragma unroll
+                for (int x = 0; x < F::NO_W; ++x)
+                    if (kk < (x + 1) * 16) mfma(O[x], fa, frag(sP + x * 16 * F::LDC, F::LDC, kk, lane));
+            }
+        }
+#pragma unroll
         for (int x = 0; x < F::NO_W; ++x) {
             if (F::NO % kWaves == 0 || w + kWaves * x < F::NO) {
                 const int jb = ojb<F>(w, x), db = odb<F>(w, x);
-                O[x] *= Xi[x];
-                const int kmax = min(C, ((jb + 1) * 16 + E::KD - 1) / E::KD * E::KD);
-                mma_nt(O[x], sVc + db * 16 * F::LDC, F::LDC, sP + jb * 16 * F::LDC, F::LDC, kmax, lane);
+                if constexpr (!SHARED_DV) {
+                    const int kmax = min(C, ((jb + 1) * 16 + E::KD - 1) / E::KD * E::KD);
+                    mma_nt(O[x], sVc + db * 16 * F::LDC, F::LDC, sP + jb * 16 * F::LDC, F::LDC, kmax, lane);
+                }
                 const int row = jb * 16 + n16, col = db * 16 + g4;
                 if (a.out_bf16)
                     store4(reinterpret_cast<uint16_t*>(sO) + row * F::LDO + col, O[x]);
@@ -342,21 +402,15 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_full_kernel(FwdArgs a) {
             }
         }
         __syncthreads();
-        // Coalesced 16-byte stores of the output rows j < L.
-        const int vec = 16 / osz;  // elements per 16-byte store
-        const int per_row = DVT / vec;
-        char* obase = (char*)a.o + ((((long long)b * a.N + t0) * a.H + h) * a.dv + dv0) * osz;
-        for (int x = tid; x < L * per_row; x += kThreads) {
-            const int j = x / per_row, c16 = x % per_row;
-            *reinterpret_cast<uint4*>(obase + ((long long)j * rsv + c16 * vec) * osz) =
-                *reinterpret_cast<const uint4*>(sO + (j * F::LDO + c16 * vec) * osz);
-        }
+        if constexpr (!F::SEP_O) store_out_tile(t0, L);
     };
 
     for (int c = 0; c < nchunks; c += 2) {
         chunk(c, std::integral_constant<int, 0>{});
         if (c + 1 < nchunks) chunk(c + 1, std::integral_constant<int, 1>{});
     }
+    if constexpr (F::SEP_O)
+        if (nchunks > 0) store_out_tile(seg_t0 + (long long)(nchunks - 1) * C, (int)(seg_t1 - seg_t0 - (long long)(nchunks - 1) * C));
 
     // The state after the last token of the sequence.
     if (seg == a.nseg - 1 && a.state_out) {

@@ -144,6 +144,21 @@ __device__ __forceinline__ void mma_nt(f32x4_t& acc, const float* A, int lda, co
     for (int k = 0; k < klen; k += 4) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[k], b[k], acc, 0, 0, 0);
 }
 
+// One MFMA operand fragment: rows 0..15 of a k-contiguous LDS matrix at k offset k0 (the same lane map as
+// mma_nt), so that a fragment shared by several tiles is read from LDS once.
+__device__ __forceinline__ bf16x8_t frag(const uint16_t* M, int ld, int k0, int lane) {
+    return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(M + (lane & 15) * ld + k0 + 8 * (lane >> 4)));
+}
+__device__ __forceinline__ float frag(const float* M, int ld, int k0, int lane) {
+    return M[(lane & 15) * ld + k0 + (lane >> 4)];
+}
+__device__ __forceinline__ void mfma(f32x4_t& acc, bf16x8_t a, bf16x8_t b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mfma(f32x4_t& acc, float a, float b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+}
+
 // ---------------------------------------------------------------------------------------------------
 // Decay and rotation factors.
 // ---------------------------------------------------------------------------------------------------
