@@ -101,7 +101,7 @@ def bench_chunkwise(R, W, torch, wid, steps, warmup):
     R.timing_enable(False)
     ms_step = e0.elapsed_time(e1) / steps
     kernels = {}
-    for name in ("ret_chunk_local", "ret_segment_scan", "ret_chunk_full"):
+    for name in ("ret_chunk_fused", "ret_chunk_local", "ret_segment_scan", "ret_chunk_full"):
         tot, n = R.timing_query(name)
         if n:
             kernels[name] = {"avg_us": 1e3 * tot / n, "launches": n}
@@ -114,6 +114,7 @@ def bench_chunkwise(R, W, torch, wid, steps, warmup):
     e1.record()
     torch.cuda.synchronize()
     ms_clean = e0.elapsed_time(e1) / steps
+    R.ret_chunkwise_check(ws)  # no call of the timed region abandoned a segment-chain wait
     return w, ms_step, ms_clean, kernels, ws
 
 

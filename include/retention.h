@@ -76,11 +76,20 @@ ret_status_t ret_parallel_fwd(const void* q, const void* k, const void* v, void*
 
 /*
  * Workspace (device bytes) that ret_chunkwise_fwd uses to split each sequence into segments that run in
- * parallel (a two-level scan of the chunk state). 0 means the call runs one segment per (b, h) and needs
- * none. Passing a smaller workspace than this is allowed: the call then uses fewer segments. The workspace
- * needs no initialisation; calls sharing a workspace must not overlap in time (on one stream they do not).
+ * parallel: the end state of each segment is passed to the next (a scan of the chunk state over segments).
+ * 0 means the call runs one segment per (b, h) and needs none. Passing a smaller workspace than this is
+ * allowed: the call then uses fewer segments. The workspace must be zero-filled before its first use; every
+ * call leaves it in a state the next call accepts (its first 256 bytes zero except a sticky error word).
+ * Calls sharing a workspace must not overlap in time (on one stream they do not).
  */
 size_t ret_chunkwise_workspace_bytes(int B, int N, int H, int dk, int dv, int chunk, ret_dtype_t in_dt);
+
+/*
+ * Synchronises `stream` and reports whether any call that used this workspace had to abandon a wait for
+ * the state of an earlier segment (a sticky flag in the workspace; the outputs of such a call are wrong).
+ * RET_OK if not (or workspace is NULL), RET_ERR_HIP with detail otherwise.
+ */
+ret_status_t ret_chunkwise_check(const void* workspace, void* stream);
 
 /*
  * Chunkwise recurrent form with chunk size `chunk` (blog section 7.2; paper summary Eq. 7). For chunk i of
@@ -113,8 +122,8 @@ ret_status_t ret_recurrent_step(const void* q, const void* k, const void* v, voi
  * Kernel timing for measurement tools. While enabled, every kernel the library launches is bracketed by a
  * pair of HIP events on the launch stream. ret_timing_query synchronises those events and returns the total
  * milliseconds and launch count recorded for kernels whose name equals `kernel` ("" or NULL = all).
- * ret_timing_reset drops the records. Kernel names: "ret_chunk_full", "ret_chunk_local",
- * "ret_segment_scan", "ret_parallel", "ret_recurrent_step". Not for use while kernels are being captured
+ * ret_timing_reset drops the records. Kernel names: "ret_chunk_fused" (bf16 input), "ret_chunk_full",
+ * "ret_chunk_local", "ret_segment_scan" (fp32 input), "ret_parallel", "ret_recurrent_step". Not for use while kernels are being captured
  * into a graph.
  */
 int ret_timing_enable(int on);

@@ -162,8 +162,12 @@ void plan_segments(int B, int N, int H, int dv, int C, int dvt, int* nseg, int* 
     *nseg = (nchunks + spc - 1) / spc;
 }
 
-size_t segment_ws_bytes(int B, int H, int dk, int dv, int nseg) {
-    return nseg > 1 ? (size_t)B * H * nseg * dk * dv * sizeof(float) : 0;
+// Workspace bytes for nseg segments: the chain layout for the single-pass kernels, else one end state per
+// (sequence, segment) for the split kernels.
+size_t segment_ws_bytes(const ChunkKernels& ck, int B, int H, int dk, int dv, int nseg) {
+    if (nseg <= 1) return 0;
+    if (ck.fused) return chain_layout(B * H * (dv / ck.dvt), nseg, dk * ck.dvt).bytes;
+    return sizeof(ChainHeader) + (size_t)B * H * nseg * dk * dv * sizeof(float);
 }
 
 }  // namespace
@@ -213,7 +217,7 @@ size_t ret_chunkwise_workspace_bytes(int B, int N, int H, int dk, int dv, int ch
     if (!pick_chunk(in_dt, dk, dv, chunk, &ck)) return 0;
     int nseg, seg_len;
     plan_segments(B, N, H, dv, chunk, ck.dvt, &nseg, &seg_len);
-    return segment_ws_bytes(B, H, dk, dv, nseg);
+    return segment_ws_bytes(ck, B, H, dk, dv, nseg);
 }
 
 ret_status_t ret_chunkwise_fwd(const void* q, const void* k, const void* v, void* o, int B, int N, int H, int dk,
@@ -231,10 +235,14 @@ ret_status_t ret_chunkwise_fwd(const void* q, const void* k, const void* v, void
     if (!pick_chunk(in_dt, dk, dv, chunk, &ck))
         return fail(RET_ERR_UNSUPPORTED, "chunkwise form: unsupported d_k=%d d_v=%d chunk=%d for %s input", dk, dv,
                     chunk, in_dt == RET_F32 ? "F32" : "BF16");
+    // The kernels address one chunk of one head with 32-bit byte offsets.
+    if ((long long)chunk * H * (dk > dv ? dk : dv) * 4 >= (1LL << 31))
+        return fail(RET_ERR_UNSUPPORTED, "chunkwise form: chunk*H*max(d_k,d_v) too large (%d*%d*%d)", chunk, H,
+                    dk > dv ? dk : dv);
     int nseg, seg_len;
     plan_segments(B, N, H, dv, chunk, ck.dvt, &nseg, &seg_len);
     // Fewer segments when the workspace given is smaller than the plan's.
-    while (nseg > 1 && segment_ws_bytes(B, H, dk, dv, nseg) > workspace_bytes) {
+    while (nseg > 1 && segment_ws_bytes(ck, B, H, dk, dv, nseg) > workspace_bytes) {
         const int nchunks = (N + chunk - 1) / chunk;
         int spc = seg_len / chunk * 2;
         if (spc > nchunks) spc = nchunks;
@@ -247,11 +255,19 @@ ret_status_t ret_chunkwise_fwd(const void* q, const void* k, const void* v, void
     fill_fwd(A, q, k, v, o, B, N, H, dk, dv, out_dt, gamma, theta, pos0);
     A.state_in = state_in;
     A.state_out = state_out;
-    A.ws = (float*)workspace;
+    // The split kernels keep their segment states after the (unused, zero) chain header.
+    A.ws = ck.fused || !workspace ? (float*)workspace : (float*)((char*)workspace + sizeof(ChainHeader));
     A.nseg = nseg;
     A.seg_len = seg_len;
     hipStream_t s = (hipStream_t)stream;
     const int ntiles = dv / ck.dvt;
+    if (ck.fused) {
+        const unsigned grid = (unsigned)((long long)nseg * B * H * ntiles);
+        LaunchTimer tm("ret_chunk_fused", s);
+        hipLaunchKernelGGL(ck.fused, dim3(grid), dim3(kThreads), 0, s, A);
+        tm.done();
+        return launch_status("ret_chunk_fused");
+    }
     if (nseg > 1) {
         {
             LaunchTimer tm("ret_chunk_local", s);
@@ -330,6 +346,16 @@ int ret_timing_query(const char* kernel, double* total_ms, int64_t* launches) {
     }
     if (total_ms) *total_ms = tot;
     if (launches) *launches = n;
+    return RET_OK;
+}
+
+ret_status_t ret_chunkwise_check(const void* workspace, void* stream) {
+    if (!workspace) return RET_OK;
+    ChainHeader h;
+    if (hipMemcpyAsync(&h, workspace, sizeof(h), hipMemcpyDeviceToHost, (hipStream_t)stream) != hipSuccess ||
+        hipStreamSynchronize((hipStream_t)stream) != hipSuccess)
+        return fail(RET_ERR_HIP, "reading the workspace header failed");
+    if (h.error) return fail(RET_ERR_HIP, "a segment-chain wait gave up: outputs of that call are invalid");
     return RET_OK;
 }
 

@@ -1,0 +1,643 @@
+// bf16-input chunkwise kernels (gfx950). Same computation as the generic chunk kernels in kernels.h, with a
+// staging scheme built on two gfx950 features:
+//  * buffer loads/stores whose resource covers exactly the live rows of the current chunk: rows past the end
+//    of the sequence read as zero and stores to them are dropped, so no clamps, selects or guards, and the
+//    row offsets are scalar (one per pass) on top of one per-thread offset fixed for the whole kernel;
+//  * LDS transpose reads (ds_read_b64_tr_b16), so K and V live in LDS row-major only and the products that
+//    contract over tokens (K^T V and V^T P^T) read them transposed.
+// Each thread moves 16-byte row segments (8 dims of one token). The rotation factors of a thread's segment
+// follow its tokens across passes and chunks by angle addition and are re-evaluated exactly every 8 chunks.
+#pragma once
+
+#include "kernels.h"
+
+namespace ret {
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Word 3 of a gfx9 buffer resource for raw (stride 0, 32-bit data format) access: every dword is range
+// checked against the record count, loads out of range return 0 and stores out of range are dropped.
+constexpr int kRawBufferWord3 = 0x00020000;
+
+__device__ __forceinline__ rsrc_t bytes_rsrc(const void* base, int nbytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nbytes, kRawBufferWord3);
+}
+__device__ __forceinline__ u32x4_t buf_load16(rsrc_t r, int voff, int soff) {
+    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ void buf_store16(rsrc_t r, int voff, int soff, u32x4_t x) {
+    __builtin_amdgcn_raw_buffer_store_b128(x, r, voff, soff, 0);
+}
+
+// Transposed MFMA operand from a row-major LDS matrix X[k][n] (pitch ld): lane l receives
+// X[k0 + 8*(l/16) + i][n0 + l%16], i = 0..7, i.e. the operand whose row index is n and reduction index is k.
+// `tro` is the lane's part of the address, tr_lane_offset(ld, lane). Within each group of 16 lanes one
+// transpose read turns 4 rows x 16 columns (lane 4r+c addresses row r, columns 4c..4c+3) into 16 lanes x 4
+// rows; two reads cover the 8 reduction indices of the lane's group.
+__device__ __forceinline__ int tr_lane_offset(int ld, int lane) {
+    return (8 * (lane >> 4) + ((lane >> 2) & 3)) * ld + 4 * (lane & 3);
+}
+__device__ __forceinline__ bf16x8_t frag_tr(const uint16_t* X, int ld, int k0, int n0, int tro) {
+    typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+    uint16_t* p = const_cast<uint16_t*>(X) + k0 * ld + n0 + tro;
+    const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)p);
+    const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p + 4 * ld));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Rows of a T x W bf16 tile moved as 16-byte segments: SPR segments per row, RP rows per pass of the
+// workgroup, NP passes. Thread t owns segment t % SPR of rows t / SPR + p * RP.
+template <int T, int W>
+struct RowTile {
+    static constexpr int SPR = W / 8;
+    static constexpr int RP = kThreads / SPR;
+    static constexpr int NP = (T + RP - 1) / RP;
+    static constexpr bool PARTIAL = T % RP != 0;
+    static_assert(W % 8 == 0 && kThreads % SPR == 0, "row tile");
+    __device__ static __forceinline__ bool live(int row0, int p) { return !PARTIAL || row0 + p * RP < T; }
+};
+
+// Rotation factors of the four pairs of one 16-byte segment.
+struct Rot4 {
+    float c[4], s[4];
+    __device__ __forceinline__ void eval(long long p, const double* theta, int pair0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) rot_cs(p, theta[pair0 + j], &c[j], &s[j]);
+    }
+    // this <- this turned by st (angle addition)
+    __device__ __forceinline__ void turn(const Rot4& st) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float nc = c[j] * st.c[j] - s[j] * st.s[j];
+            s[j] = s[j] * st.c[j] + c[j] * st.s[j];
+            c[j] = nc;
+        }
+    }
+    __device__ __forceinline__ void apply(float* x) const {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float a0 = x[2 * j], a1 = x[2 * j + 1];
+            x[2 * j] = a0 * c[j] - a1 * s[j];
+            x[2 * j + 1] = a0 * s[j] + a1 * c[j];
+        }
+    }
+};
+
+__device__ __forceinline__ void unpack8(u32x4_t u, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __uint_as_float(u[i] << 16);
+        f[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ u32x4_t pack8(const float* f) {
+    return u32x4_t{pack2_bf16(f[0], f[1]), pack2_bf16(f[2], f[3]), pack2_bf16(f[4], f[5]), pack2_bf16(f[6], f[7])};
+}
+__device__ __forceinline__ void lds_store16(uint16_t* p, u32x4_t x) { *reinterpret_cast<u32x4_t*>(p) = x; }
+
+// Per-thread rotation state of the Q/K segments of one d_k slice: the factors of the thread's row in the
+// current pass (cur), the step between passes (RP tokens) and the step from the last pass of a chunk to the
+// first of the next (C - (NP - 1) RP tokens; the same step unless the tile is partial).
+template <int C, int RP, int NP>
+struct SliceRot {
+    Rot4 cur, pass;
+    Rot4 wrap;  // used only for partial tiles
+    static constexpr bool SAME = C == NP * RP;
+    __device__ __forceinline__ void init_steps(const double* theta, int pair0) {
+        pass.eval(RP, theta, pair0);
+        if constexpr (!SAME) wrap.eval(C - (NP - 1) * RP, theta, pair0);
+    }
+    __device__ __forceinline__ void next_chunk() {
+        if constexpr (SAME) cur.turn(pass);
+        else cur.turn(wrap);
+    }
+};
+
+
+// ---------------------------------------------------------------------------------------------------
+// Segment chain. With nseg > 1 segments per sequence, the state entering segment s is
+//   R_in(s) = sum_{j<s} gamma^((s-1-j) T) A_j + gamma^(s T) state_in,   T = tokens per segment,
+// where A_j is segment j's end state from a zero start (its aggregate). The workgroups of a unit (one d_v
+// tile of one (b, h)) take their segments as tickets from the unit's counter, so every predecessor of a
+// segment has started before it waits. Segments form groups of 8: a
+// segment adds up the aggregates of the earlier segments of its group and the inclusive prefix I = R_in(g0)
+// that enters the group, which the last segment of the previous group publishes (it computes its own R_in
+// the same way). Every R_in is thus a sum in a fixed order, independent of timing, over at most 8 slots.
+// Published states are written and read at device scope (sc1) and a slot's flag is raised only after the
+// slot's stores completed; a wait that sees no progress for ~0.17 s gives up and sets the sticky error word
+// instead of hanging. The unit's last workgroup past the look-back returns its counters and flags to zero.
+// ---------------------------------------------------------------------------------------------------
+constexpr int kChainGroup = 8;                    // segments per look-back group
+constexpr int kChainAux = 16;                     // buffer cache policy: sc1 (device-scope coherent)
+constexpr unsigned long long kChainSpin = 1ull << 24;  // give-up time in s_memrealtime ticks (100 MHz)
+
+// Waits until flags[lo .. lo+n) are all nonzero (n <= 64; lane i watches flag lo + i). False if it gave up.
+__device__ __forceinline__ bool chain_wait(const int* flags, int lo, int n, int* error) {
+    const int lane = threadIdx.x & 63;
+    const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+    for (;;) {
+        const int f = lane < n ? __hip_atomic_load(flags + lo + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 1;
+        if (__builtin_amdgcn_ballot_w64(f == 0) == 0) return true;
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kChainSpin) {
+            __hip_atomic_store(error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return false;
+        }
+        __builtin_amdgcn_s_sleep(4);
+    }
+}
+
+// One state slot: DK x 64 floats in the thread order of the R tiles (tile x of thread t at (x*256 + t)*16 bytes).
+template <int NKB>
+__device__ __forceinline__ void slot_store(float* slot, const f32x4_t* R, int tid) {
+    const rsrc_t r = bytes_rsrc(slot, NKB * kThreads * 16);
+#pragma unroll
+    for (int x = 0; x < NKB; ++x)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, R[x]), r, tid * 16, x * kThreads * 16,
+                                               kChainAux);
+}
+template <int NKB>
+__device__ __forceinline__ void slot_load(const float* slot, f32x4_t* v, int tid) {
+    const rsrc_t r = bytes_rsrc(slot, NKB * kThreads * 16);
+#pragma unroll
+    for (int x = 0; x < NKB; ++x)
+        v[x] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, tid * 16, x * kThreads * 16,
+                                                                                  kChainAux));
+}
+
+// ---------------------------------------------------------------------------------------------------
+// chunk_fused (bf16): one workgroup per (segment, d_v tile of 64, b*H + h). Wave w owns d_v block w of every
+// output and state tile. With several segments the workgroup first runs the local pass over its segment
+// (R <- gamma^L R + (K (.) zeta)^T V from zero) and joins the segment chain; then the full pass from the
+// entering state: per chunk and d_k slice S^T = K Q^T over the lower-triangle tiles, the cross term
+// O^T += R^T Q^T and the state update; then P = mask (.) S and O^T = xi (.) O^T + V^T P^T.
+// ---------------------------------------------------------------------------------------------------
+template <int DK, int C, int DVT>
+struct FullB {
+    static constexpr int KS = DK < 64 ? DK : 64;
+    static constexpr int NSL = DK / KS;
+    static constexpr int LDQ = KS + 8, LDV = DVT + 8, LDP = C + 8, LDR = DK + 8, LDO = DVT + 8, LDK = DK + 8;
+    static constexpr int NB = C / 16, NDV = DVT / 16, NKB = DK / 16, XB = KS / 16;
+    static constexpr int NS = Tri<NB>::count, NS_W = (NS + kWaves - 1) / kWaves;
+    typedef RowTile<C, KS> TQ;
+    typedef RowTile<C, DVT> TV;
+    typedef RowTile<C, DK> TK;  // local pass: whole d_k
+    static constexpr int SQ = C * LDQ, SV = C * LDV, SP = C * LDP, SRT = DVT * LDR;
+    static constexpr int A_STAGE = 3 * SQ * 2, A_OUT = C * LDO * 4;
+    static constexpr int REST = (SV + SP + SRT) * 2;
+    static constexpr int WITH_SEP = (A_STAGE + 15) / 16 * 16 + REST + A_OUT;
+    static constexpr int WITHOUT_SEP = ((A_STAGE > A_OUT ? A_STAGE : A_OUT) + 15) / 16 * 16 + REST;
+    static constexpr bool SEP_O = WITH_SEP <= 160 * 1024 && (WITH_SEP <= 80 * 1024 || WITHOUT_SEP > 80 * 1024);
+    static constexpr int A_BYTES =
+        SEP_O ? (A_STAGE + 15) / 16 * 16 : ((A_STAGE > A_OUT ? A_STAGE : A_OUT) + 15) / 16 * 16;
+    static constexpr int FULL_BYTES = A_BYTES + REST + (SEP_O ? A_OUT : 0);
+    static constexpr int LOCAL_BYTES = (C * LDK + C * LDV) * 2;  // local pass: sKz [C][DK] and sV [C][DVT]
+    static constexpr int LDS_BYTES = FULL_BYTES > LOCAL_BYTES ? FULL_BYTES : LOCAL_BYTES;
+    // two workgroups per CU when the LDS allows and the registers of d_k = 256 are not needed
+    static constexpr int OCC = LDS_BYTES <= 80 * 1024 && DK <= 128 ? 2 : 1;
+    static_assert(NDV == kWaves, "one d_v block per wave");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    static_assert(C % 32 == 0 && KS % 32 == 0, "tiling");
+};
+
+template <int DK, int C, int DVT>
+__global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT>::OCC)) void chunk_fused_bf16(FwdArgs a) {
+    typedef FullB<DK, C, DVT> F;
+    typedef typename F::TQ TQ;
+    typedef typename F::TV TV;
+    typedef typename F::TK TK;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[F::LDS_BYTES / 2];
+    // Broadcast word (ticket, finish count): the first word of the staging region, which no thread writes
+    // before a barrier that follows every read of it.
+    int& s_word = *reinterpret_cast<int*>(smem);
+    uint16_t* sQ = smem;
+    uint16_t* sK = sQ + F::SQ;
+    uint16_t* sKz = sK + F::SQ;
+    uint16_t* sV = smem + F::A_BYTES / 2;
+    uint16_t* sP = sV + F::SV;
+    uint16_t* sRt = sP + F::SP;
+    char* sO = F::SEP_O ? reinterpret_cast<char*>(sRt + F::SRT) : reinterpret_cast<char*>(smem);
+
+    const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g4 = 4 * (lane >> 4), n16 = lane & 15;
+    const int ntiles = __builtin_amdgcn_readfirstlane(a.dv / DVT);
+    const int units = __builtin_amdgcn_readfirstlane(a.B * a.H * ntiles);
+    const bool chained = a.nseg > 1;
+    ChainHeader* hdr = reinterpret_cast<ChainHeader*>(a.ws);
+    // The unit comes from the launch index; with several segments the segment is the unit's next ticket, so
+    // the workgroups that own a unit's earlier segments have all started.
+    const int unit = __builtin_amdgcn_readfirstlane((int)(blockIdx.x % (unsigned)units));
+    int seg = __builtin_amdgcn_readfirstlane((int)(blockIdx.x / (unsigned)units));
+    int* ctr = nullptr;
+    if (chained) {
+        ctr = reinterpret_cast<int*>(reinterpret_cast<char*>(a.ws) + chain_layout(units, a.nseg, DK * DVT).ctr_off) +
+              2 * unit;
+        if (tid == 0) s_word = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        seg = __builtin_amdgcn_readfirstlane(s_word);
+        __syncthreads();
+    }
+    // Scalar arguments re-read as wave-uniform values: they are live across the divergent ticket branch.
+    const int aB = __builtin_amdgcn_readfirstlane(a.B), aN = __builtin_amdgcn_readfirstlane(a.N);
+    const int aH = __builtin_amdgcn_readfirstlane(a.H), adk = __builtin_amdgcn_readfirstlane(a.dk);
+    const int adv = __builtin_amdgcn_readfirstlane(a.dv), anseg = __builtin_amdgcn_readfirstlane(a.nseg);
+    const int aseg_len = __builtin_amdgcn_readfirstlane(a.seg_len);
+    const int pair = unit / ntiles;
+    const int b = pair / aH, h = pair % aH;
+    const int dv0 = (unit % ntiles) * DVT;
+    const float lg = a.log2g[h];
+    const long long seg_t0 = (long long)seg * aseg_len;
+    const int seg_n = (int)(min((long long)aN, seg_t0 + aseg_len) - seg_t0);  // tokens in this segment
+    const int nchunks = (seg_n + C - 1) / C;
+    const int rsk = aH * adk, rsv = aH * adv;  // elements between consecutive tokens
+    const long long head0 = ((long long)b * aN + seg_t0) * aH + h;
+    const uint16_t* qh = (const uint16_t*)a.q + head0 * adk;
+    const uint16_t* kh = (const uint16_t*)a.k + head0 * adk;
+    const uint16_t* vh = (const uint16_t*)a.v + head0 * adv + dv0;
+    const int osz = a.out_bf16 ? 2 : 4;
+    char* oh = (char*)a.o + (head0 * adv + dv0) * osz;
+    const int vrow = tid / TV::SPR, vseg = tid % TV::SPR;
+    const int voff = (vrow * rsv + vseg * 8) * 2;
+    const int tro_v = tr_lane_offset(F::LDV, lane);
+
+    f32x4_t R[F::NKB];
+#pragma unroll
+    for (int x = 0; x < F::NKB; ++x) R[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // Segment chain storage (chained runs).
+    const bool last = seg == anseg - 1;
+    const size_t slot = (size_t)DK * DVT;
+    const ChainLayout lay = chain_layout(units, anseg, (int)slot);
+    int* flags = reinterpret_cast<int*>(reinterpret_cast<char*>(a.ws) + lay.flags_off) + (size_t)unit * anseg;
+    float* agg = reinterpret_cast<float*>(reinterpret_cast<char*>(a.ws) + lay.agg_off) + (size_t)unit * anseg * slot;
+    float* inc = reinterpret_cast<float*>(reinterpret_cast<char*>(a.ws) + lay.inc_off) + (size_t)unit * anseg * slot;
+    const int g0 = seg / kChainGroup * kChainGroup;              // first segment of this segment's group
+    const bool boundary = seg % kChainGroup == kChainGroup - 1;  // publishes the prefix for the next group
+
+    // ---- local pass over the segment (chained runs, all segments but the last) ----
+    if (chained && !last) {
+        uint16_t* lK = smem;
+        uint16_t* lV = smem + C * F::LDK;
+        const int krow = tid / TK::SPR, kseg = tid % TK::SPR;
+        const int koff = (krow * rsk + kseg * 8) * 2;
+        const int tro_k = tr_lane_offset(F::LDK, lane);
+        u32x4_t lk[TK::NP], lv[TV::NP];
+        auto lissue = [&](int c) __attribute__((always_inline)) {
+            const long long tc = (long long)c * C;
+            const rsrc_t rk = bytes_rsrc(kh + tc * rsk, ((C - 1) * rsk + DK) * 2);
+            const rsrc_t rv = bytes_rsrc(vh + tc * rsv, ((C - 1) * rsv + DVT) * 2);
+#pragma unroll
+            for (int p = 0; p < TK::NP; ++p) lk[p] = buf_load16(rk, koff, p * TK::RP * rsk * 2);
+#pragma unroll
+            for (int p = 0; p < TV::NP; ++p) lv[p] = buf_load16(rv, voff, p * TV::RP * rsv * 2);
+        };
+        lissue(0);
+        float zl[TK::NP];
+#pragma unroll
+        for (int p = 0; p < TK::NP; ++p) zl[p] = gpow(lg, (float)(C - 1 - (krow + p * TK::RP)));
+        const float gC = gpow(lg, (float)C);
+        SliceRot<C, TK::RP, TK::NP> lrot;  // identity factors without rotation (theta all zero)
+        lrot.init_steps(a.theta, kseg * 4);
+        for (int c = 0; c < nchunks; ++c) {  // segments before the last hold whole chunks only
+            if (c > 0) __syncthreads();
+            if ((c & 7) == 0) lrot.cur.eval(a.pos0 + seg_t0 + (long long)c * C + krow, a.theta, kseg * 4);
+#pragma unroll
+            for (int p = 0; p < TK::NP; ++p)
+                if (TK::live(krow, p)) {
+                    float kf[8];
+                    unpack8(lk[p], kf);
+                    lrot.cur.apply(kf);
+                    if (p + 1 < TK::NP) lrot.cur.turn(lrot.pass);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) kf[e] *= zl[p];
+                    lds_store16(lK + (krow + p * TK::RP) * F::LDK + kseg * 8, pack8(kf));
+                }
+            lrot.next_chunk();
+#pragma unroll
+            for (int p = 0; p < TV::NP; ++p)
+                if (TV::live(vrow, p)) lds_store16(lV + (vrow + p * TV::RP) * F::LDV + vseg * 8, lv[p]);
+            if (c + 1 < nchunks) lissue(c + 1);
+            __syncthreads();
+#pragma unroll
+            for (int x = 0; x < F::NKB; ++x) R[x] *= gC;
+#pragma unroll
+            for (int f = 0; f < C / 32; ++f) {
+                const bf16x8_t fb = frag_tr(lV, F::LDV, 32 * f, w * 16, tro_v);
+#pragma unroll
+                for (int x = 0; x < F::NKB; ++x) mfma(R[x], frag_tr(lK, F::LDK, 32 * f, x * 16, tro_k), fb);
+            }
+        }
+        __syncthreads();  // the local tiles are dead before the full pass reuses the LDS
+        if (!boundary) {  // publish the aggregate for the later segments of the group (nothing else in flight)
+            slot_store<F::NKB>(agg + seg * slot, R, tid);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (tid == 0) {
+                __hip_atomic_store(flags + seg, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __builtin_amdgcn_s_waitcnt(0);
+            }
+        }
+    }
+
+    // ---- full-pass staging: the first stages' loads go out before the chain wait ----
+    const int qrow = tid / TQ::SPR, qseg = tid % TQ::SPR;
+    const int qoff = (qrow * rsk + qseg * 8) * 2;
+    const int tro_q = tr_lane_offset(F::LDQ, lane);
+    constexpr int NBUF = C <= 64 ? 2 : 1;
+    u32x4_t bq[NBUF][TQ::NP], bk[NBUF][TQ::NP], bv[NBUF][TV::NP];
+    auto issue = [&](int i, auto parc) __attribute__((always_inline)) {
+        constexpr int par = decltype(parc)::value;
+        const int c = i / F::NSL, sl = i % F::NSL;
+        const int L = min(C, seg_n - c * C);
+        const long long tc = (long long)c * C;
+        const rsrc_t rq = bytes_rsrc(qh + tc * rsk + sl * F::KS, ((L - 1) * rsk + F::KS) * 2);
+        const rsrc_t rk = bytes_rsrc(kh + tc * rsk + sl * F::KS, ((L - 1) * rsk + F::KS) * 2);
+#pragma unroll
+        for (int p = 0; p < TQ::NP; ++p) {
+            bq[par][p] = buf_load16(rq, qoff, p * TQ::RP * rsk * 2);
+            bk[par][p] = buf_load16(rk, qoff, p * TQ::RP * rsk * 2);
+        }
+        if (sl == 0) {
+            const rsrc_t rv = bytes_rsrc(vh + tc * rsv, ((L - 1) * rsv + DVT) * 2);
+#pragma unroll
+            for (int p = 0; p < TV::NP; ++p) bv[par][p] = buf_load16(rv, voff, p * TV::RP * rsv * 2);
+        }
+    };
+    const int nst = nchunks * F::NSL;
+    if (nst > 0) issue(0, std::integral_constant<int, 0>{});
+    if constexpr (NBUF == 2)
+        if (nst > 1) issue(1, std::integral_constant<int, 1>{});
+
+    // ---- entering state ----
+    if (chained) {
+        const float gT = gpow(lg, (float)aseg_len);
+        // R_in = sum over the group's earlier segments of gamma^((seg-1-j)T) A_j, plus the decayed prefix that
+        // enters the group (the previous group's published prefix, or state_in for the first group). The
+        // order of the terms is fixed, so results do not depend on timing.
+        f32x4_t Rin[F::NKB];
+#pragma unroll
+        for (int x = 0; x < F::NKB; ++x) Rin[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        // One poll covers every flag this segment needs; the slots are then read in batches of LB (loads of a
+        // batch in flight together) and added in the fixed order.
+        const int lo = g0 > 0 ? g0 - 1 : g0;
+        const bool ok = chain_wait(flags, lo, seg - lo, &hdr->error);  // on give-up the sum stays partial
+        constexpr int LB = F::NKB >= 16 ? 1 : F::NKB >= 8 ? 2 : 4;
+        float dec = 1.f;
+        for (int j0 = seg - 1; ok && j0 >= g0; j0 -= LB) {
+            f32x4_t v[LB][F::NKB];
+#pragma unroll
+            for (int i = 0; i < LB; ++i)
+                if (j0 - i >= g0) slot_load<F::NKB>(agg + (j0 - i) * slot, v[i], tid);
+#pragma unroll
+            for (int i = 0; i < LB; ++i)
+                if (j0 - i >= g0) {
+#pragma unroll
+                    for (int x = 0; x < F::NKB; ++x) Rin[x] += dec * v[i][x];
+                    dec *= gT;
+                }
+        }
+        if (g0 > 0) {
+            if (ok) {
+                f32x4_t v[F::NKB];
+                slot_load<F::NKB>(inc + (g0 - 1) * slot, v, tid);
+#pragma unroll
+                for (int x = 0; x < F::NKB; ++x) Rin[x] += dec * v[x];
+            }
+        } else if (a.state_in) {
+#pragma unroll
+            for (int x = 0; x < F::NKB; ++x)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    Rin[x][e] += dec * a.state_in[((long long)pair * DK + x * 16 + g4 + e) * adv + dv0 + w * 16 + n16];
+        }
+        if (!last && boundary) {  // publish the prefix I_s = gamma^T R_in + A_s leaving the group
+            f32x4_t I[F::NKB];
+#pragma unroll
+            for (int x = 0; x < F::NKB; ++x) I[x] = gT * Rin[x] + R[x];
+            slot_store<F::NKB>(inc + seg * slot, I, tid);
+            __builtin_amdgcn_s_waitcnt(0);
+        }
+        __syncthreads();
+        if (tid == 0) {
+            if (!last && boundary) {
+                __hip_atomic_store(flags + seg, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __builtin_amdgcn_s_waitcnt(0);  // the flag lands before this workgroup counts as finished
+            }
+            s_word = __hip_atomic_fetch_add(ctr + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        // The unit's last workgroup past its look-back finds the unit's others past it too: reset the unit.
+        if (__builtin_amdgcn_readfirstlane(s_word) == anseg - 1) {
+            for (int i = tid; i < anseg; i += kThreads)
+                __hip_atomic_store(flags + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (tid == 0) {
+                __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(ctr + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+#pragma unroll
+        for (int x = 0; x < F::NKB; ++x) R[x] = Rin[x];
+    } else if (a.state_in) {
+#pragma unroll
+        for (int x = 0; x < F::NKB; ++x)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                R[x][e] = a.state_in[((long long)pair * DK + x * 16 + g4 + e) * adv + dv0 + w * 16 + n16];
+    }
+
+    // Scores above the diagonal are never written: keep them zero for the P.V product.
+    for (int i = tid; i < F::SP; i += kThreads) sP[i] = 0;
+
+    // Chunk-independent decay factors: the mask gamma^(j-l) of each owned S^T tile (rows l, columns j), xi_j =
+    // gamma^(j+1) of each O^T tile (column j) and zeta of each staged row of a full chunk.
+    int Sjb[F::NS_W], Slb[F::NS_W];
+    float Dm[F::NS_W][4], Xi[F::NB], zfull[TQ::NP];
+#pragma unroll
+    for (int x = 0; x < F::NS_W; ++x) {
+        tri_tile<F::NB>(min(w + kWaves * x, F::NS - 1), Sjb[x], Slb[x]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int d = 16 * (Sjb[x] - Slb[x]) + n16 - g4 - e;  // j - l
+            Dm[x][e] = d >= 0 ? gpow(lg, (float)d) : 0.f;
+        }
+    }
+#pragma unroll
+    for (int x = 0; x < F::NB; ++x) Xi[x] = gpow(lg, (float)(x * 16 + n16 + 1));
+#pragma unroll
+    for (int p = 0; p < TQ::NP; ++p) zfull[p] = gpow(lg, (float)(C - 1 - (qrow + p * TQ::RP)));
+    const float gC = gpow(lg, (float)C);
+    // Without rotation theta is all zero and every factor is exactly (1, 0).
+    SliceRot<C, TQ::RP, TQ::NP> rot[F::NSL];
+#pragma unroll
+    for (int sl = 0; sl < F::NSL; ++sl) rot[sl].init_steps(a.theta, (sl * F::KS + qseg * 8) / 2);
+
+    // Copy of R (operand precision), transposed to [d_v][d_k], for the cross product.
+#pragma unroll
+    for (int x = 0; x < F::NKB; ++x) store4(sRt + (w * 16 + n16) * F::LDR + x * 16 + g4, R[x]);
+
+    auto commit = [&](int i, auto parc, auto slc) __attribute__((always_inline)) {
+        constexpr int par = decltype(parc)::value, sl = decltype(slc)::value;
+        const int c = i / F::NSL;
+        const int L = min(C, seg_n - c * C);
+        if ((c & 7) == 0)  // exact factors every 8 chunks; angle addition in between
+            rot[sl].cur.eval(a.pos0 + seg_t0 + (long long)c * C + qrow, a.theta, (sl * F::KS + qseg * 8) / 2);
+#pragma unroll
+        for (int p = 0; p < TQ::NP; ++p) {
+            const int r = qrow + p * TQ::RP;
+            if (TQ::live(qrow, p)) {
+                float qf[8], kf[8];
+                unpack8(bq[par][p], qf);
+                unpack8(bk[par][p], kf);
+                rot[sl].cur.apply(qf);
+                rot[sl].cur.apply(kf);
+                if (p + 1 < TQ::NP) rot[sl].cur.turn(rot[sl].pass);
+                lds_store16(sQ + r * F::LDQ + qseg * 8, pack8(qf));
+                lds_store16(sK + r * F::LDQ + qseg * 8, pack8(kf));
+                const float z = L == C ? zfull[p] : (r < L ? gpow(lg, (float)(L - 1 - r)) : 0.f);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) kf[e] *= z;
+                lds_store16(sKz + r * F::LDQ + qseg * 8, pack8(kf));
+            }
+        }
+        rot[sl].next_chunk();
+        if constexpr (sl == 0) {
+#pragma unroll
+            for (int p = 0; p < TV::NP; ++p)
+                if (TV::live(vrow, p)) lds_store16(sV + (vrow + p * TV::RP) * F::LDV + vseg * 8, bv[par][p]);
+        }
+    };
+
+    // 16-byte stores of the output tile rows of chunk c; rows past the sequence fall outside the buffer range
+    // and are dropped.
+    auto store_out_tile = [&](int c) __attribute__((always_inline)) {
+        const int L = min(C, seg_n - c * C);
+        const rsrc_t ro = bytes_rsrc(oh + (long long)c * C * rsv * osz, ((L - 1) * rsv + DVT) * osz);
+        if (a.out_bf16) {
+            constexpr int PR = DVT / 8, RPP = kThreads / PR;  // segments per row, rows per pass
+            const int j = tid / PR, c8 = tid % PR;
+#pragma unroll
+            for (int p = 0; p < C / RPP; ++p)
+                buf_store16(ro, (j * rsv + c8 * 8) * 2, p * RPP * rsv * 2,
+                            *reinterpret_cast<const u32x4_t*>(sO + ((j + p * RPP) * F::LDO + c8 * 8) * 2));
+        } else {
+            constexpr int PR = DVT / 4, RPP = kThreads / PR;
+            const int j = tid / PR, c4 = tid % PR;
+#pragma unroll
+            for (int p = 0; p < C / RPP; ++p)
+                buf_store16(ro, (j * rsv + c4 * 4) * 4, p * RPP * rsv * 4,
+                            *reinterpret_cast<const u32x4_t*>(sO + ((j + p * RPP) * F::LDO + c4 * 4) * 4));
+        }
+    };
+
+    constexpr int KF = C / 32;  // reduction steps over the tokens of a chunk
+    auto chunk = [&](int c, auto cparc) __attribute__((always_inline)) {
+        constexpr int cpar = decltype(cparc)::value;
+        const int L = min(C, seg_n - c * C);
+        const float gL = L == C ? gC : gpow(lg, (float)L);
+        f32x4_t S[F::NS_W], O[F::NB];
+#pragma unroll
+        for (int x = 0; x < F::NS_W; ++x) S[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int x = 0; x < F::NB; ++x) O[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        bf16x8_t fv[KF];  // V operand of d_v block w (B of the state update, A of the P.V product)
+        static_for<0, F::NSL>([&](auto slc) __attribute__((always_inline)) {
+            constexpr int sl = decltype(slc)::value;
+            constexpr int par = NBUF == 2 ? (cpar * F::NSL + sl) & 1 : 0;
+            const int i = c * F::NSL + sl;
+            // Staging buffers free: for a chunk's first slice with a separate output tile, the barrier that
+            // ended the previous chunk already guarantees it.
+            if (!(F::SEP_O && sl == 0 && c > 0)) __syncthreads();
+            commit(i, std::integral_constant<int, par>{}, slc);
+            if (i + NBUF < nst) issue(i + NBUF, std::integral_constant<int, par>{});
+            if constexpr (F::SEP_O && sl == 0)
+                if (c > 0) store_out_tile(c - 1);  // the previous chunk's output, overlapping this staging
+            __syncthreads();
+            // S^T += K_s Q_s^T over this wave's lower-triangle tiles (keys l <= queries j). Slots past the last
+            // tile repeat it; their results are never stored.
+#pragma unroll
+            for (int kk = 0; kk < F::KS; kk += 32) {
+#pragma unroll
+                for (int x = 0; x < F::NS_W; ++x)
+                    mfma(S[x], frag(sK + Slb[x] * 16 * F::LDQ, F::LDQ, kk, lane),
+                         frag(sQ + Sjb[x] * 16 * F::LDQ, F::LDQ, kk, lane));
+            }
+            // O^T += R_s^T Q_s^T: the cross-chunk read of the state carried in from the previous chunk.
+#pragma unroll
+            for (int kk = 0; kk < F::KS; kk += 32) {
+                const bf16x8_t fa = frag(sRt + w * 16 * F::LDR + sl * F::KS, F::LDR, kk, lane);
+#pragma unroll
+                for (int x = 0; x < F::NB; ++x) mfma(O[x], fa, frag(sQ + x * 16 * F::LDQ, F::LDQ, kk, lane));
+            }
+            // R_s <- gamma^L R_s + (K_s (.) zeta)^T V.
+            if constexpr (sl == 0) {
+#pragma unroll
+                for (int f = 0; f < KF; ++f) fv[f] = frag_tr(sV, F::LDV, 32 * f, w * 16, tro_v);
+            }
+#pragma unroll
+            for (int x = sl * F::XB; x < (sl + 1) * F::XB; ++x) R[x] *= gL;
+#pragma unroll
+            for (int f = 0; f < KF; ++f) {
+#pragma unroll
+                for (int x = sl * F::XB; x < (sl + 1) * F::XB; ++x)
+                    mfma(R[x], frag_tr(sKz, F::LDQ, 32 * f, (x - sl * F::XB) * 16, tro_q), fv[f]);
+            }
+        });
+
+        // Decay mask: P[j][l..l+3] = S^T[l..l+3][j] * gamma^(j-l), four consecutive keys per store.
+#pragma unroll
+        for (int x = 0; x < F::NS_W; ++x)
+            if (w + kWaves * x < F::NS) {
+                f32x4_t pv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) pv[e] = S[x][e] * Dm[x][e];
+                store4(sP + (Sjb[x] * 16 + n16) * F::LDP + Slb[x] * 16 + g4, pv);
+            }
+        __syncthreads();  // P complete; all reads of the staged slices and of sRt for this chunk are done
+        // O^T = xi (.) (R^T Q^T) + V^T P^T over keys up to each query block, then the output tile in LDS.
+#pragma unroll
+        for (int x = 0; x < F::NB; ++x) O[x] *= Xi[x];
+#pragma unroll
+        for (int f = 0; f < KF; ++f) {
+#pragma unroll
+            for (int x = 0; x < F::NB; ++x)
+                if (32 * f < (x + 1) * 16) mfma(O[x], fv[f], frag(sP + x * 16 * F::LDP, F::LDP, 32 * f, lane));
+        }
+#pragma unroll
+        for (int x = 0; x < F::NB; ++x) {
+            const int row = x * 16 + n16, col = w * 16 + g4;
+            if (a.out_bf16)
+                store4(reinterpret_cast<uint16_t*>(sO) + row * F::LDO + col, O[x]);
+            else
+                store4(reinterpret_cast<float*>(sO) + row * F::LDO + col, O[x]);
+        }
+        // New operand copy of R for the next chunk.
+#pragma unroll
+        for (int x = 0; x < F::NKB; ++x) store4(sRt + (w * 16 + n16) * F::LDR + x * 16 + g4, R[x]);
+        __syncthreads();
+        if constexpr (!F::SEP_O) store_out_tile(c);
+    };
+
+    for (int c = 0; c < nchunks; c += 2) {
+        chunk(c, std::integral_constant<int, 0>{});
+        if (c + 1 < nchunks) chunk(c + 1, std::integral_constant<int, 1>{});
+    }
+    if constexpr (F::SEP_O)
+        if (nchunks > 0) store_out_tile(nchunks - 1);
+
+    // The state after the last token of the sequence.
+    if (last && a.state_out) {
+        float* out = a.state_out + (long long)pair * DK * adv;
+#pragma unroll
+        for (int x = 0; x < F::NKB; ++x) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) out[(long long)(x * 16 + g4 + e) * adv + dv0 + w * 16 + n16] = R[x][e];
+        }
+    }
+}
+
+template <int DK, int C>
+ChunkKernels chunk_entry_bf16() {
+    return {nullptr, nullptr, chunk_fused_bf16<DK, C, 64>, 64};
+}
+
+}  // namespace ret

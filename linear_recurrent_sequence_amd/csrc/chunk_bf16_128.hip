@@ -1,12 +1,12 @@
 // bf16-input chunkwise kernels, d_k in {128}, chunk in {32, 64, 128}, d_v tiles of 64.
-#include "kernels.h"
+#include "chunk_bf16.h"
 
 namespace ret {
 
 bool chunk_kernels_bf16_128(int dk, int dv, int C, ChunkKernels* out) {
     if (dv % 64) return false;
 #define RET_CASE(DKv, Cv) \
-    if (dk == DKv && C == Cv) { *out = chunk_entry<BF16, DKv, Cv, 64>(); return true; }
+    if (dk == DKv && C == Cv) { *out = chunk_entry_bf16<DKv, Cv>(); return true; }
     RET_CASE(128, 32)
     RET_CASE(128, 64)
     RET_CASE(128, 128)

@@ -27,6 +27,30 @@ struct FwdArgs {
     double theta[kMaxPairs];
 };
 
+// Workspace of the single-pass chunkwise kernel when a sequence is split into nseg > 1 segments: a header,
+// two counters per unit (next segment ticket, workgroups past the look-back), one flag per (unit, segment)
+// and two state slots per (unit, segment), the aggregate and the inclusive prefix (slot_floats floats each;
+// unit = one d_v tile of one (b, h)). Header, counters and flags must be zero before a run and are zero
+// again after it, except the sticky `error` word.
+struct ChainHeader {
+    int reserved[2];
+    int error;  // nonzero: a wait gave up
+    int pad[61];
+};
+struct ChainLayout {
+    size_t ctr_off, flags_off, agg_off, inc_off, bytes;
+};
+__host__ __device__ inline ChainLayout chain_layout(int units, int nseg, int slot_floats) {
+    ChainLayout L;
+    const size_t nslots = (size_t)units * nseg;
+    L.ctr_off = sizeof(ChainHeader);
+    L.flags_off = L.ctr_off + ((size_t)units * 8 + 255) / 256 * 256;
+    L.agg_off = L.flags_off + (nslots * 4 + 255) / 256 * 256;
+    L.inc_off = L.agg_off + nslots * slot_floats * 4;
+    L.bytes = L.inc_off + nslots * slot_floats * 4;
+    return L;
+}
+
 // Tile lists. S tiles of a CxC chunk are the lower triangle (cb <= rb), enumerated row by row; tile i of any
 // list belongs to wave i % 4 and lives in that wave's accumulator slot i / 4.
 template <int NB>
@@ -802,8 +826,10 @@ namespace ret {
 typedef void (*fwd_kernel_t)(FwdArgs);
 typedef void (*step_kernel_t)(StepArgs);
 
+// Chunkwise kernels of one shape: either the three-kernel split (local states, segment scan, full pass) or
+// one single-pass kernel with the segment chain (fused, non-null).
 struct ChunkKernels {
-    fwd_kernel_t full, local;
+    fwd_kernel_t full, local, fused;
     int dvt;
 };
 struct ParKernel {
@@ -813,7 +839,7 @@ struct ParKernel {
 
 template <class E, int DK, int C, int DVT>
 ChunkKernels chunk_entry() {
-    return {chunk_full_kernel<E, DK, C, DVT>, chunk_local_kernel<E, DK, C, DVT>, DVT};
+    return {chunk_full_kernel<E, DK, C, DVT>, chunk_local_kernel<E, DK, C, DVT>, nullptr, DVT};
 }
 
 // Getters, one per kernel-group source. Return false when the shape has no instance.

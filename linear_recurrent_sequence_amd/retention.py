@@ -56,6 +56,8 @@ def load(build_if_missing: bool = True):
     lib.ret_chunkwise_fwd.restype = i32
     lib.ret_recurrent_step.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, fp, dp, i64, vp]
     lib.ret_recurrent_step.restype = i32
+    lib.ret_chunkwise_check.argtypes = [vp, vp]
+    lib.ret_chunkwise_check.restype = i32
     lib.ret_timing_enable.argtypes = [i32]
     lib.ret_timing_enable.restype = i32
     lib.ret_timing_query.argtypes = [ctypes.c_char_p, dp, ctypes.POINTER(i64)]
@@ -128,13 +130,20 @@ def ret_chunkwise_workspace_bytes(B, N, H, dk, dv, chunk, in_dtype=torch.bfloat1
 
 
 def chunkwise_workspace(q, v, chunk):
-    """Allocate (with torch) the workspace ret_chunkwise_fwd plans for these shapes, or None. Its contents need no
-    initialisation."""
+    """Allocate (with torch) the zero-filled workspace ret_chunkwise_fwd plans for these shapes, or None. Calls
+    leave it ready for the next call."""
     B, N, H, dk = q.shape
     nbytes = ret_chunkwise_workspace_bytes(B, N, H, dk, v.shape[3], chunk, q.dtype)
     if nbytes == 0:
         return None
-    return torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    return torch.zeros(nbytes, dtype=torch.uint8, device=q.device)
+
+
+def ret_chunkwise_check(workspace, stream=None):
+    """Raise if a call that used `workspace` abandoned a segment-chain wait (synchronises the stream)."""
+    if workspace is None:
+        return
+    _check("ret_chunkwise_check", load().ret_chunkwise_check(_dev(workspace, "workspace"), _stream(stream)))
 
 
 def ret_chunkwise_fwd(q, k, v, o, gamma, chunk, theta=None, pos0=0, state_in=None, state_out=None,

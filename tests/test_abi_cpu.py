@@ -76,7 +76,13 @@ def test_chunkwise_rejects_invalid_arguments(lib, kw, status):
 def test_workspace_query(lib):
     # one (b, h) with a long sequence is split into segments; many short sequences are not
     n_long = lib.ret_chunkwise_workspace_bytes(1, 65536, 8, 128, 128, 128, 1)
-    assert n_long > 0 and n_long % (8 * 128 * 128 * 4) == 0
+    # 16 units (8 heads x 2 d_v tiles of 64) x 64 segments of 1024 tokens: a 256-byte header, two int
+    # counters per unit (padded to 256 bytes), one int flag per (unit, segment) and two 128x64 fp32 state
+    # slots (aggregate, inclusive prefix) per (unit, segment)
+    assert n_long == 256 + 256 + 16 * 64 * 4 + 2 * 16 * 64 * 128 * 64 * 4
+    # fp32 input runs the split kernels: the header, then one d_k x d_v state per (b, h, segment)
+    n_f32 = lib.ret_chunkwise_workspace_bytes(1, 4096, 2, 64, 64, 64, 0)
+    assert n_f32 > 256 and (n_f32 - 256) % (2 * 64 * 64 * 4) == 0
     assert lib.ret_chunkwise_workspace_bytes(128, 512, 8, 64, 64, 64, 1) == 0
     assert lib.ret_chunkwise_workspace_bytes(1, 64, 8, 48, 64, 64, 1) == 0  # unsupported shape: 0
 

@@ -37,6 +37,7 @@ def _gpu_chunkwise(R, q, k, v, w_dtype, gamma, chunk, theta=None, pos0=0, s_in=N
     R.ret_chunkwise_fwd(qd, kd, vd, o, gamma, chunk, theta=theta, pos0=pos0, state_in=sin, state_out=sout,
                         workspace=ws)
     torch.cuda.synchronize()
+    R.ret_chunkwise_check(ws)
     return to_host(o), to_host(sout)
 
 
@@ -85,6 +86,7 @@ SMALL = [
     ("bf16", 1, 260, 1, 256, 128, 128, True, 0, True, 2),
     ("bf16", 3, 1, 2, 64, 64, 64, True, 9, True, None),      # one token
     ("bf16", 1, 45, 2, 64, 64, 64, False, 0, False, None),   # shorter than one chunk
+    ("bf16", 1, 1100, 1, 64, 64, 64, True, 7, False, 1),     # 18 chunks in one segment
 ]
 
 
@@ -107,6 +109,48 @@ def test_chunkwise_small(R, case, monkeypatch):
     eo, es = rel_err(o, o_ref), rel_err(s, s_ref)
     print("  err o=%.3g state=%.3g" % (eo, es))
     assert eo <= tol(dt) and es <= tol(dt), (eo, es)
+
+
+def test_chunkwise_workspace_reuse_and_repeatability(R, monkeypatch):
+    """One workspace serves repeated calls and a call of another shape: every call leaves it ready for the
+    next. 11 and 9 segments span two look-back groups, so the prefix handed across a group boundary is
+    used. The segment states are summed in a fixed order, so repeated calls give identical bits."""
+    import torch
+    cases = [(2, 1400, 2, 64, 128, 64, 11), (1, 1150, 2, 128, 64, 128, 9)]
+    ws_bytes = 0
+    for B, N, H, dk, dv, C, segs in cases:
+        monkeypatch.setenv("RET_SEGMENTS", str(segs))
+        ws_bytes = max(ws_bytes, R.ret_chunkwise_workspace_bytes(B, N, H, dk, dv, C))
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
+    for B, N, H, dk, dv, C, segs in cases:
+        print_case("workspace_reuse", (B, N, H, dk, dv, C, segs))
+        monkeypatch.setenv("RET_SEGMENTS", str(segs))
+        rng = np.random.default_rng(7 + N)
+        q = W.normal(rng, (B, N, H, dk), 8.0, "bf16")
+        k = W.normal(rng, (B, N, H, dk), 8.0, "bf16")
+        v = W.normal(rng, (B, N, H, dv), 8.0, "bf16")
+        s0 = rng.standard_normal((B, H, dk, dv)).astype(np.float32)
+        gamma, theta = W.gamma_schedule(H), W.theta_schedule(dk)
+        o_ref, s_ref = oracle.chunkwise(q, k, v, gamma, C, theta=theta, pos0=5, state_in=s0)
+        qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+        sin = torch.from_numpy(s0).cuda()
+        runs = []
+        for _ in range(3):
+            o = empty_out((B, N, H, dv), "bf16")
+            sout = torch.empty((B, H, dk, dv), dtype=torch.float32, device="cuda")
+            R.ret_chunkwise_fwd(qd, kd, vd, o, gamma, C, theta=theta, pos0=5, state_in=sin, state_out=sout,
+                                workspace=ws)
+            torch.cuda.synchronize()
+            R.ret_chunkwise_check(ws)
+            runs.append((to_host(o), to_host(sout)))
+        for o, sout in runs:
+            assert rel_err(o, o_ref) <= tol("bf16") and rel_err(sout, s_ref) <= tol("bf16")
+        for o, sout in runs[1:]:
+            assert np.array_equal(o, runs[0][0]) and np.array_equal(sout, runs[0][1])
+        units = B * H * (dv // 64)
+        up = lambda n: (n + 255) // 256 * 256
+        hdr = ws[:256 + up(units * 8) + up(units * segs * 4)].cpu().numpy().view(np.int32)
+        assert (hdr == 0).all(), hdr[:4]  # error word, per-unit tickets and counters, slot flags back at zero
 
 
 @pytest.mark.parametrize("dt,dk,dv", [("f32", 32, 32), ("bf16", 64, 64), ("bf16", 256, 128)])
