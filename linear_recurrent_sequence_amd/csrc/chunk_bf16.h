@@ -47,6 +47,35 @@ __device__ __forceinline__ bf16x8_t frag_tr(const uint16_t* X, int ld, int k0, i
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// Operand fragments in the permuted reduction order used by the fused kernel: within each 32-wide reduction
+// step, lane group g (= lane / 16) holds indices 4g..4g+3 and 16+4g..16+4g+3. An MFMA sums over the reduction
+// index, so any order shared by both operands gives the same product; this one matches the accumulator
+// layout of a 16x16 tile (lane group g holds rows 4g..4g+3), so accumulators of two vertically adjacent
+// tiles form an operand without leaving their lanes.
+// Row-major X[m][k] (pitch ld): lane l receives X[l%16][k0 + 4g + i] and X[l%16][k0 + 16 + 4g + i].
+__device__ __forceinline__ bf16x8_t frag_p(const uint16_t* X, int ld, int k0, int lane) {
+    const uint16_t* p = X + (lane & 15) * ld + k0 + 4 * (lane >> 4);
+    const uint2 lo = *reinterpret_cast<const uint2*>(p), hi = *reinterpret_cast<const uint2*>(p + 16);
+    return __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+// Transposed, from row-major X[k][n]: lane l receives X[k0 + 4g + i][n0 + l%16] and X[k0 + 16 + 4g + i][n0 + l%16].
+// `tro` is trp_lane_offset(ld, lane).
+__device__ __forceinline__ int trp_lane_offset(int ld, int lane) {
+    return (4 * (lane >> 4) + ((lane >> 2) & 3)) * ld + 4 * (lane & 3);
+}
+__device__ __forceinline__ bf16x8_t frag_trp(const uint16_t* X, int ld, int k0, int n0, int tro) {
+    typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+    uint16_t* p = const_cast<uint16_t*>(X) + k0 * ld + n0 + tro;
+    const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)p);
+    const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p + 16 * ld));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+// Two accumulator tiles (rows 0..15 and 16..31 of a 32-row block) as one operand in the permuted order.
+__device__ __forceinline__ bf16x8_t acc_pair(f32x4_t a, f32x4_t b) {
+    return __builtin_bit_cast(bf16x8_t, make_uint4(pack2_bf16(a[0], a[1]), pack2_bf16(a[2], a[3]),
+                                                   pack2_bf16(b[0], b[1]), pack2_bf16(b[2], b[3])));
+}
+
 // Rows of a T x W bf16 tile moved as 16-byte segments: SPR segments per row, RP rows per pass of the
 // workgroup, NP passes. Thread t owns segment t % SPR of rows t / SPR + p * RP.
 template <int T, int W>
@@ -119,7 +148,8 @@ struct SliceRot {
 // ---------------------------------------------------------------------------------------------------
 // Segment chain. With nseg > 1 segments per sequence, the state entering segment s is
 //   R_in(s) = sum_{j<s} gamma^((s-1-j) T) A_j + gamma^(s T) state_in,   T = tokens per segment,
-// where A_j is segment j's end state from a zero start (its aggregate). The workgroups of a unit (one d_v
+// where A_j is segment j's end state from a zero start (its aggregate; the first segment's includes the
+// decayed state_in, which then needs no term of its own). The workgroups of a unit (one d_v
 // tile of one (b, h)) take their segments as tickets from the unit's counter, so every predecessor of a
 // segment has started before it waits. Segments form groups of 8: a
 // segment adds up the aggregates of the earlier segments of its group and the inclusive prefix I = R_in(g0)
@@ -148,10 +178,19 @@ __device__ __forceinline__ bool chain_wait(const int* flags, int lo, int n, int*
     }
 }
 
+// A pointer the caller knows to be wave-uniform, moved to scalar registers (the compiler cannot always prove
+// it after divergent regions, and a buffer resource built from vector registers costs a loop per access).
+template <class T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+    const unsigned long long u = reinterpret_cast<unsigned long long>(p);
+    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)u), hi = __builtin_amdgcn_readfirstlane((unsigned)(u >> 32));
+    return reinterpret_cast<T*>(((unsigned long long)hi << 32) | lo);
+}
+
 // One state slot: DK x 64 floats in the thread order of the R tiles (tile x of thread t at (x*256 + t)*16 bytes).
 template <int NKB>
 __device__ __forceinline__ void slot_store(float* slot, const f32x4_t* R, int tid) {
-    const rsrc_t r = bytes_rsrc(slot, NKB * kThreads * 16);
+    const rsrc_t r = bytes_rsrc(uniform_ptr(slot), NKB * kThreads * 16);
 #pragma unroll
     for (int x = 0; x < NKB; ++x)
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, R[x]), r, tid * 16, x * kThreads * 16,
@@ -159,7 +198,7 @@ __device__ __forceinline__ void slot_store(float* slot, const f32x4_t* R, int ti
 }
 template <int NKB>
 __device__ __forceinline__ void slot_load(const float* slot, f32x4_t* v, int tid) {
-    const rsrc_t r = bytes_rsrc(slot, NKB * kThreads * 16);
+    const rsrc_t r = bytes_rsrc(uniform_ptr(slot), NKB * kThreads * 16);
 #pragma unroll
     for (int x = 0; x < NKB; ++x)
         v[x] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, tid * 16, x * kThreads * 16,
@@ -169,36 +208,32 @@ __device__ __forceinline__ void slot_load(const float* slot, f32x4_t* v, int tid
 // ---------------------------------------------------------------------------------------------------
 // chunk_fused (bf16): one workgroup per (segment, d_v tile of 64, b*H + h). Wave w owns d_v block w of every
 // output and state tile. With several segments the workgroup first runs the local pass over its segment
-// (R <- gamma^L R + (K (.) zeta)^T V from zero) and joins the segment chain; then the full pass from the
-// entering state: per chunk and d_k slice S^T = K Q^T over the lower-triangle tiles, the cross term
-// O^T += R^T Q^T and the state update; then P = mask (.) S and O^T = xi (.) O^T + V^T P^T.
+// (R <- gamma^L R + (K (.) zeta)^T V from zero, or from state_in for the first segment), publishes the end
+// state and joins the segment chain for its entering state. The full pass then runs from that state: per
+// chunk and d_k slice S^T = K Q^T (all lower-triangle tiles, kept in registers), the cross term
+// O^T += R^T Q^T with R^T taken from the state accumulators and the state update; then
+// O^T = xi (.) O^T + V^T P^T with P = mask (.) S straight from the S^T accumulators, stored to the output.
 // ---------------------------------------------------------------------------------------------------
 template <int DK, int C, int DVT>
 struct FullB {
     static constexpr int KS = DK < 64 ? DK : 64;
     static constexpr int NSL = DK / KS;
-    static constexpr int LDQ = KS + 8, LDV = DVT + 8, LDP = C + 8, LDR = DK + 8, LDO = DVT + 8, LDK = DK + 8;
+    static constexpr int LDQ = KS + 8, LDV = DVT + 8, LDK = DK + 8;
     static constexpr int NB = C / 16, NDV = DVT / 16, NKB = DK / 16, XB = KS / 16;
-    static constexpr int NS = Tri<NB>::count, NS_W = (NS + kWaves - 1) / kWaves;
+    static constexpr int NS = Tri<NB>::count;
     typedef RowTile<C, KS> TQ;
     typedef RowTile<C, DVT> TV;
     typedef RowTile<C, DK> TK;  // local pass: whole d_k
-    static constexpr int SQ = C * LDQ, SV = C * LDV, SP = C * LDP, SRT = DVT * LDR;
-    static constexpr int A_STAGE = 3 * SQ * 2, A_OUT = C * LDO * 4;
-    static constexpr int REST = (SV + SP + SRT) * 2;
-    static constexpr int WITH_SEP = (A_STAGE + 15) / 16 * 16 + REST + A_OUT;
-    static constexpr int WITHOUT_SEP = ((A_STAGE > A_OUT ? A_STAGE : A_OUT) + 15) / 16 * 16 + REST;
-    static constexpr bool SEP_O = WITH_SEP <= 160 * 1024 && (WITH_SEP <= 80 * 1024 || WITHOUT_SEP > 80 * 1024);
-    static constexpr int A_BYTES =
-        SEP_O ? (A_STAGE + 15) / 16 * 16 : ((A_STAGE > A_OUT ? A_STAGE : A_OUT) + 15) / 16 * 16;
-    static constexpr int FULL_BYTES = A_BYTES + REST + (SEP_O ? A_OUT : 0);
+    static constexpr int SQ = C * LDQ, SV = C * LDV;
+    static constexpr int FULL_BYTES = (3 * SQ + SV) * 2;         // sQ, sK, sKz, sV
     static constexpr int LOCAL_BYTES = (C * LDK + C * LDV) * 2;  // local pass: sKz [C][DK] and sV [C][DVT]
     static constexpr int LDS_BYTES = FULL_BYTES > LOCAL_BYTES ? FULL_BYTES : LOCAL_BYTES;
-    // two workgroups per CU when the LDS allows and the registers of d_k = 256 are not needed
-    static constexpr int OCC = LDS_BYTES <= 80 * 1024 && DK <= 128 ? 2 : 1;
+    // two workgroups per CU when the LDS allows and the registers of d_k >= 128 are not needed
+    static constexpr int OCC = LDS_BYTES <= 80 * 1024 && DK <= 64 ? 2 : 1;
     static_assert(NDV == kWaves, "one d_v block per wave");
+    static_assert(C == 32 || C == 64, "chunk tile of 32 or 64 tokens");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-    static_assert(C % 32 == 0 && KS % 32 == 0, "tiling");
+    static_assert(KS % 32 == 0, "tiling");
 };
 
 template <int DK, int C, int DVT>
@@ -214,10 +249,7 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT>::OCC)) void chunk_fuse
     uint16_t* sQ = smem;
     uint16_t* sK = sQ + F::SQ;
     uint16_t* sKz = sK + F::SQ;
-    uint16_t* sV = smem + F::A_BYTES / 2;
-    uint16_t* sP = sV + F::SV;
-    uint16_t* sRt = sP + F::SP;
-    char* sO = F::SEP_O ? reinterpret_cast<char*>(sRt + F::SRT) : reinterpret_cast<char*>(smem);
+    uint16_t* sV = sKz + F::SQ;
 
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g4 = 4 * (lane >> 4), n16 = lane & 15;
     const int ntiles = __builtin_amdgcn_readfirstlane(a.dv / DVT);
@@ -258,11 +290,21 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT>::OCC)) void chunk_fuse
     char* oh = (char*)a.o + (head0 * adv + dv0) * osz;
     const int vrow = tid / TV::SPR, vseg = tid % TV::SPR;
     const int voff = (vrow * rsv + vseg * 8) * 2;
-    const int tro_v = tr_lane_offset(F::LDV, lane);
+    const int tro_v = tr_lane_offset(F::LDV, lane), tro_vp = trp_lane_offset(F::LDV, lane);
+    // State_in enters through the first segment: its local pass starts from it, so its published end state
+    // carries state_in into every later R_in, and its full pass starts from it again.
+    auto load_state_in = [&](f32x4_t* R) __attribute__((always_inline)) {
+#pragma unroll
+        for (int x = 0; x < F::NKB; ++x)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                R[x][e] = a.state_in[((long long)pair * DK + x * 16 + g4 + e) * adv + dv0 + w * 16 + n16];
+    };
 
     f32x4_t R[F::NKB];
 #pragma unroll
     for (int x = 0; x < F::NKB; ++x) R[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (seg == 0 && a.state_in) load_state_in(R);
 
     // Segment chain storage (chained runs).
     const bool last = seg == anseg - 1;
@@ -339,11 +381,11 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT>::OCC)) void chunk_fuse
         }
     }
 
-    // ---- full-pass staging: the first stages' loads go out before the chain wait ----
+    // ---- full pass: staging ----
     const int qrow = tid / TQ::SPR, qseg = tid % TQ::SPR;
     const int qoff = (qrow * rsk + qseg * 8) * 2;
-    const int tro_q = tr_lane_offset(F::LDQ, lane);
-    constexpr int NBUF = C <= 64 ? 2 : 1;
+    const int tro_q = trp_lane_offset(F::LDQ, lane);
+    constexpr int NBUF = C <= 64 && DK <= 64 ? 2 : 1;  // register buffers of staged loads
     u32x4_t bq[NBUF][TQ::NP], bk[NBUF][TQ::NP], bv[NBUF][TV::NP];
     auto issue = [&](int i, auto parc) __attribute__((always_inline)) {
         constexpr int par = decltype(parc)::value;
@@ -368,49 +410,43 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT>::OCC)) void chunk_fuse
     if constexpr (NBUF == 2)
         if (nst > 1) issue(1, std::integral_constant<int, 1>{});
 
-    // ---- entering state ----
+    // ---- entering state: state_in for the first segment, else R_in from the segment chain ----
     if (chained) {
         const float gT = gpow(lg, (float)aseg_len);
-        // R_in = sum over the group's earlier segments of gamma^((seg-1-j)T) A_j, plus the decayed prefix that
-        // enters the group (the previous group's published prefix, or state_in for the first group). The
-        // order of the terms is fixed, so results do not depend on timing.
+        // R_in = sum over the group's earlier segments j of gamma^((seg-1-j)T) R_j, plus gamma^((seg-g0)T) times
+        // the prefix entering the group (published by the previous group's last segment). One poll covers
+        // every flag; slots are read in batches of LB and added in a fixed order, so results do not depend
+        // on timing.
         f32x4_t Rin[F::NKB];
 #pragma unroll
         for (int x = 0; x < F::NKB; ++x) Rin[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        // One poll covers every flag this segment needs; the slots are then read in batches of LB (loads of a
-        // batch in flight together) and added in the fixed order.
-        const int lo = g0 > 0 ? g0 - 1 : g0;
-        const bool ok = chain_wait(flags, lo, seg - lo, &hdr->error);  // on give-up the sum stays partial
-        constexpr int LB = F::NKB >= 16 ? 1 : F::NKB >= 8 ? 2 : 4;
-        float dec = 1.f;
-        for (int j0 = seg - 1; ok && j0 >= g0; j0 -= LB) {
-            f32x4_t v[LB][F::NKB];
+        if (seg > 0) {
+            const int lo = g0 > 0 ? g0 - 1 : g0;
+            // (wave-uniform: the wait's result is a ballot; on give-up the sum stays partial)
+            const bool ok = __builtin_amdgcn_readfirstlane((int)chain_wait(flags, lo, seg - lo, &hdr->error)) != 0;
+            constexpr int LB = F::NKB >= 16 ? 1 : F::NKB >= 8 ? 2 : 4;
+            float dec = 1.f;
+            for (int j0 = seg - 1; ok && j0 >= g0; j0 -= LB) {
+                f32x4_t v[LB][F::NKB];
 #pragma unroll
-            for (int i = 0; i < LB; ++i)
-                if (j0 - i >= g0) slot_load<F::NKB>(agg + (j0 - i) * slot, v[i], tid);
+                for (int i = 0; i < LB; ++i)
+                    if (j0 - i >= g0) slot_load<F::NKB>(agg + (j0 - i) * slot, v[i], tid);
 #pragma unroll
-            for (int i = 0; i < LB; ++i)
-                if (j0 - i >= g0) {
+                for (int i = 0; i < LB; ++i)
+                    if (j0 - i >= g0) {
 #pragma unroll
-                    for (int x = 0; x < F::NKB; ++x) Rin[x] += dec * v[i][x];
-                    dec *= gT;
-                }
-        }
-        if (g0 > 0) {
-            if (ok) {
+                        for (int x = 0; x < F::NKB; ++x) Rin[x] += dec * v[i][x];
+                        dec *= gT;
+                    }
+            }
+            if (g0 > 0 && ok) {
                 f32x4_t v[F::NKB];
                 slot_load<F::NKB>(inc + (g0 - 1) * slot, v, tid);
 #pragma unroll
                 for (int x = 0; x < F::NKB; ++x) Rin[x] += dec * v[x];
             }
-        } else if (a.state_in) {
-#pragma unroll
-            for (int x = 0; x < F::NKB; ++x)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    Rin[x][e] += dec * a.state_in[((long long)pair * DK + x * 16 + g4 + e) * adv + dv0 + w * 16 + n16];
         }
-        if (!last && boundary) {  // publish the prefix I_s = gamma^T R_in + A_s leaving the group
+        if (!last && boundary) {  // the prefix leaving the group: R_in of the next segment
             f32x4_t I[F::NKB];
 #pragma unroll
             for (int x = 0; x < F::NKB; ++x) I[x] = gT * Rin[x] + R[x];
@@ -437,30 +473,24 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT>::OCC)) void chunk_fuse
         }
 #pragma unroll
         for (int x = 0; x < F::NKB; ++x) R[x] = Rin[x];
-    } else if (a.state_in) {
+        if (seg == 0) {
 #pragma unroll
-        for (int x = 0; x < F::NKB; ++x)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                R[x][e] = a.state_in[((long long)pair * DK + x * 16 + g4 + e) * adv + dv0 + w * 16 + n16];
-    }
-
-    // Scores above the diagonal are never written: keep them zero for the P.V product.
-    for (int i = tid; i < F::SP; i += kThreads) sP[i] = 0;
-
-    // Chunk-independent decay factors: the mask gamma^(j-l) of each owned S^T tile (rows l, columns j), xi_j =
-    // gamma^(j+1) of each O^T tile (column j) and zeta of each staged row of a full chunk.
-    int Sjb[F::NS_W], Slb[F::NS_W];
-    float Dm[F::NS_W][4], Xi[F::NB], zfull[TQ::NP];
-#pragma unroll
-    for (int x = 0; x < F::NS_W; ++x) {
-        tri_tile<F::NB>(min(w + kWaves * x, F::NS - 1), Sjb[x], Slb[x]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int d = 16 * (Sjb[x] - Slb[x]) + n16 - g4 - e;  // j - l
-            Dm[x][e] = d >= 0 ? gpow(lg, (float)d) : 0.f;
+            for (int x = 0; x < F::NKB; ++x) R[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            if (a.state_in) load_state_in(R);
         }
     }
+
+    // Chunk-independent decay factors: the mask gamma^(j-l) for S^T tiles Delta = jb - lb blocks below the
+    // diagonal (rows l, columns j of the lane), xi_j = gamma^(j+1) of each O^T tile (column j) and zeta of
+    // each staged row of a full chunk.
+    float Dm[F::NB][4], Xi[F::NB], zfull[TQ::NP];
+#pragma unroll
+    for (int d = 0; d < F::NB; ++d)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int jl = 16 * d + n16 - g4 - e;  // j - l
+            Dm[d][e] = jl >= 0 ? gpow(lg, (float)jl) : 0.f;
+        }
 #pragma unroll
     for (int x = 0; x < F::NB; ++x) Xi[x] = gpow(lg, (float)(x * 16 + n16 + 1));
 #pragma unroll
@@ -470,10 +500,6 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT>::OCC)) void chunk_fuse
     SliceRot<C, TQ::RP, TQ::NP> rot[F::NSL];
 #pragma unroll
     for (int sl = 0; sl < F::NSL; ++sl) rot[sl].init_steps(a.theta, (sl * F::KS + qseg * 8) / 2);
-
-    // Copy of R (operand precision), transposed to [d_v][d_k], for the cross product.
-#pragma unroll
-    for (int x = 0; x < F::NKB; ++x) store4(sRt + (w * 16 + n16) * F::LDR + x * 16 + g4, R[x]);
 
     auto commit = [&](int i, auto parc, auto slc) __attribute__((always_inline)) {
         constexpr int par = decltype(parc)::value, sl = decltype(slc)::value;
@@ -507,71 +533,72 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT>::OCC)) void chunk_fuse
         }
     };
 
-    // 16-byte stores of the output tile rows of chunk c; rows past the sequence fall outside the buffer range
-    // and are dropped.
-    auto store_out_tile = [&](int c) __attribute__((always_inline)) {
+    // Output stores straight from the O^T accumulators: lane (g, n16) of tile x holds 4 consecutive d_v of
+    // query x*16 + n16. Rows past the sequence fall outside the buffer range and are dropped.
+    const int o_voff = (n16 * rsv + w * 16 + g4) * osz;
+    auto store_out = [&](int c, const f32x4_t* O) __attribute__((always_inline)) {
         const int L = min(C, seg_n - c * C);
         const rsrc_t ro = bytes_rsrc(oh + (long long)c * C * rsv * osz, ((L - 1) * rsv + DVT) * osz);
         if (a.out_bf16) {
-            constexpr int PR = DVT / 8, RPP = kThreads / PR;  // segments per row, rows per pass
-            const int j = tid / PR, c8 = tid % PR;
 #pragma unroll
-            for (int p = 0; p < C / RPP; ++p)
-                buf_store16(ro, (j * rsv + c8 * 8) * 2, p * RPP * rsv * 2,
-                            *reinterpret_cast<const u32x4_t*>(sO + ((j + p * RPP) * F::LDO + c8 * 8) * 2));
+            for (int x = 0; x < F::NB; ++x)
+                __builtin_amdgcn_raw_buffer_store_b64(
+                    __builtin_bit_cast(uint32_t __attribute__((ext_vector_type(2))),
+                                       make_uint2(pack2_bf16(O[x][0], O[x][1]), pack2_bf16(O[x][2], O[x][3]))),
+                    ro, o_voff, x * 16 * rsv * 2, 0);
         } else {
-            constexpr int PR = DVT / 4, RPP = kThreads / PR;
-            const int j = tid / PR, c4 = tid % PR;
 #pragma unroll
-            for (int p = 0; p < C / RPP; ++p)
-                buf_store16(ro, (j * rsv + c4 * 4) * 4, p * RPP * rsv * 4,
-                            *reinterpret_cast<const u32x4_t*>(sO + ((j + p * RPP) * F::LDO + c4 * 4) * 4));
+            for (int x = 0; x < F::NB; ++x)
+                buf_store16(ro, o_voff, x * 16 * rsv * 4, __builtin_bit_cast(u32x4_t, O[x]));
         }
     };
 
+    // S^T tile (jb, lb), lb <= jb, in row-by-row lower-triangle order.
+    auto tri = [](int jb, int lb) constexpr { return jb * (jb + 1) / 2 + lb; };
     constexpr int KF = C / 32;  // reduction steps over the tokens of a chunk
     auto chunk = [&](int c, auto cparc) __attribute__((always_inline)) {
         constexpr int cpar = decltype(cparc)::value;
         const int L = min(C, seg_n - c * C);
         const float gL = L == C ? gC : gpow(lg, (float)L);
-        f32x4_t S[F::NS_W], O[F::NB];
+        f32x4_t S[F::NS], O[F::NB];
 #pragma unroll
-        for (int x = 0; x < F::NS_W; ++x) S[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int x = 0; x < F::NS; ++x) S[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int x = 0; x < F::NB; ++x) O[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        bf16x8_t fv[KF];  // V operand of d_v block w (B of the state update, A of the P.V product)
+        bf16x8_t fv[KF];  // V^T operand of d_v block w (B of the state update, A of the P.V product)
         static_for<0, F::NSL>([&](auto slc) __attribute__((always_inline)) {
             constexpr int sl = decltype(slc)::value;
             constexpr int par = NBUF == 2 ? (cpar * F::NSL + sl) & 1 : 0;
             const int i = c * F::NSL + sl;
-            // Staging buffers free: for a chunk's first slice with a separate output tile, the barrier that
-            // ended the previous chunk already guarantees it.
-            if (!(F::SEP_O && sl == 0 && c > 0)) __syncthreads();
+            __syncthreads();  // every wave is done with the staged tiles of the previous stage
             commit(i, std::integral_constant<int, par>{}, slc);
             if (i + NBUF < nst) issue(i + NBUF, std::integral_constant<int, par>{});
-            if constexpr (F::SEP_O && sl == 0)
-                if (c > 0) store_out_tile(c - 1);  // the previous chunk's output, overlapping this staging
             __syncthreads();
-            // S^T += K_s Q_s^T over this wave's lower-triangle tiles (keys l <= queries j). Slots past the last
-            // tile repeat it; their results are never stored.
 #pragma unroll
             for (int kk = 0; kk < F::KS; kk += 32) {
+                // Q and K fragments of every block, shared by S^T = K Q^T (all lower-triangle tiles: every
+                // wave needs all of P) and the cross term O^T += R^T Q^T.
+                bf16x8_t qf[F::NB], kf[F::NB];
 #pragma unroll
-                for (int x = 0; x < F::NS_W; ++x)
-                    mfma(S[x], frag(sK + Slb[x] * 16 * F::LDQ, F::LDQ, kk, lane),
-                         frag(sQ + Sjb[x] * 16 * F::LDQ, F::LDQ, kk, lane));
-            }
-            // O^T += R_s^T Q_s^T: the cross-chunk read of the state carried in from the previous chunk.
+                for (int x = 0; x < F::NB; ++x) {
+                    qf[x] = frag_p(sQ + x * 16 * F::LDQ, F::LDQ, kk, lane);
+                    kf[x] = frag_p(sK + x * 16 * F::LDQ, F::LDQ, kk, lane);
+                }
 #pragma unroll
-            for (int kk = 0; kk < F::KS; kk += 32) {
-                const bf16x8_t fa = frag(sRt + w * 16 * F::LDR + sl * F::KS, F::LDR, kk, lane);
+                for (int jb = 0; jb < F::NB; ++jb)
 #pragma unroll
-                for (int x = 0; x < F::NB; ++x) mfma(O[x], fa, frag(sQ + x * 16 * F::LDQ, F::LDQ, kk, lane));
+                    for (int lb = 0; lb <= jb; ++lb) mfma(S[tri(jb, lb)], kf[lb], qf[jb]);
+                // R^T of d_v block w over d_k rows sl*KS + kk .. +31, straight from the state accumulators
+                // (previous chunk's state: this slice's update follows).
+                const int rb = (sl * F::KS + kk) / 16;
+                const bf16x8_t ra = acc_pair(R[rb], R[rb + 1]);
+#pragma unroll
+                for (int x = 0; x < F::NB; ++x) mfma(O[x], ra, qf[x]);
             }
             // R_s <- gamma^L R_s + (K_s (.) zeta)^T V.
             if constexpr (sl == 0) {
 #pragma unroll
-                for (int f = 0; f < KF; ++f) fv[f] = frag_tr(sV, F::LDV, 32 * f, w * 16, tro_v);
+                for (int f = 0; f < KF; ++f) fv[f] = frag_trp(sV, F::LDV, 32 * f, w * 16, tro_vp);
             }
 #pragma unroll
             for (int x = sl * F::XB; x < (sl + 1) * F::XB; ++x) R[x] *= gL;
@@ -579,50 +606,33 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT>::OCC)) void chunk_fuse
             for (int f = 0; f < KF; ++f) {
 #pragma unroll
                 for (int x = sl * F::XB; x < (sl + 1) * F::XB; ++x)
-                    mfma(R[x], frag_tr(sKz, F::LDQ, 32 * f, (x - sl * F::XB) * 16, tro_q), fv[f]);
+                    mfma(R[x], frag_trp(sKz, F::LDQ, 32 * f, (x - sl * F::XB) * 16, tro_q), fv[f]);
             }
         });
-
-        // Decay mask: P[j][l..l+3] = S^T[l..l+3][j] * gamma^(j-l), four consecutive keys per store.
-#pragma unroll
-        for (int x = 0; x < F::NS_W; ++x)
-            if (w + kWaves * x < F::NS) {
-                f32x4_t pv;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) pv[e] = S[x][e] * Dm[x][e];
-                store4(sP + (Sjb[x] * 16 + n16) * F::LDP + Slb[x] * 16 + g4, pv);
-            }
-        __syncthreads();  // P complete; all reads of the staged slices and of sRt for this chunk are done
-        // O^T = xi (.) (R^T Q^T) + V^T P^T over keys up to each query block, then the output tile in LDS.
+        // O^T = xi (.) (R^T Q^T) + V^T P^T, P = mask (.) S taken from the S^T accumulators as the B operand
+        // (keys 32f.. of query block x are tiles lb = 2f and 2f + 1).
 #pragma unroll
         for (int x = 0; x < F::NB; ++x) O[x] *= Xi[x];
 #pragma unroll
         for (int f = 0; f < KF; ++f) {
 #pragma unroll
-            for (int x = 0; x < F::NB; ++x)
-                if (32 * f < (x + 1) * 16) mfma(O[x], fv[f], frag(sP + x * 16 * F::LDP, F::LDP, 32 * f, lane));
+            for (int x = 2 * f; x < F::NB; ++x) {
+                const f32x4_t p0 = S[tri(x, 2 * f)] * f32x4_t{Dm[x - 2 * f][0], Dm[x - 2 * f][1], Dm[x - 2 * f][2],
+                                                              Dm[x - 2 * f][3]};
+                f32x4_t p1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                if (2 * f + 1 <= x)
+                    p1 = S[tri(x, 2 * f + 1)] * f32x4_t{Dm[x - 2 * f - 1][0], Dm[x - 2 * f - 1][1],
+                                                        Dm[x - 2 * f - 1][2], Dm[x - 2 * f - 1][3]};
+                mfma(O[x], fv[f], acc_pair(p0, p1));
+            }
         }
-#pragma unroll
-        for (int x = 0; x < F::NB; ++x) {
-            const int row = x * 16 + n16, col = w * 16 + g4;
-            if (a.out_bf16)
-                store4(reinterpret_cast<uint16_t*>(sO) + row * F::LDO + col, O[x]);
-            else
-                store4(reinterpret_cast<float*>(sO) + row * F::LDO + col, O[x]);
-        }
-        // New operand copy of R for the next chunk.
-#pragma unroll
-        for (int x = 0; x < F::NKB; ++x) store4(sRt + (w * 16 + n16) * F::LDR + x * 16 + g4, R[x]);
-        __syncthreads();
-        if constexpr (!F::SEP_O) store_out_tile(c);
+        store_out(c, O);
     };
 
     for (int c = 0; c < nchunks; c += 2) {
         chunk(c, std::integral_constant<int, 0>{});
         if (c + 1 < nchunks) chunk(c + 1, std::integral_constant<int, 1>{});
     }
-    if constexpr (F::SEP_O)
-        if (nchunks > 0) store_out_tile(nchunks - 1);
 
     // The state after the last token of the sequence.
     if (last && a.state_out) {
@@ -635,9 +645,11 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT>::OCC)) void chunk_fuse
     }
 }
 
+// Chunks of 128 tokens run as 64-token sub-chunks: the chunkwise recurrence gives the same result for any
+// chunk size (up to rounding), and 64-token tiles keep all of P in registers.
 template <int DK, int C>
 ChunkKernels chunk_entry_bf16() {
-    return {nullptr, nullptr, chunk_fused_bf16<DK, C, 64>, 64};
+    return {nullptr, nullptr, chunk_fused_bf16<DK, (C > 64 ? 64 : C), 64>, 64};
 }
 
 }  // namespace ret
