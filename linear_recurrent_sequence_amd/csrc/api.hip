@@ -312,15 +312,21 @@ ret_status_t ret_recurrent_step(const void* q, const void* k, const void* v, voi
     A.in_bf16 = in_dt == RET_BF16;
     A.out_bf16 = out_dt == RET_BF16;
     A.rotate = theta != nullptr;
-    A.pos = pos;
     for (int h = 0; h < H; ++h) A.gamma[h] = gamma[h];
+    // Rotation factors of this step's position, in fp64 (one position per call).
     if (theta)
-        for (int i = 0; i < dk / 2; ++i) A.theta[i] = theta[i];
-    step_kernel_t fn = step_kernel_get(in_dt == RET_BF16, dk);
+        for (int i = 0; i < dk / 2; ++i) {
+            const double ang = (double)pos * theta[i];
+            A.rc[i] = (float)cos(ang);
+            A.rs[i] = (float)sin(ang);
+        }
+    int cw = 0, wr = 0;
+    step_kernel_t fn =
+        step_kernel_get(in_dt == RET_BF16, dk, env_int("RET_STEP_CW", 0), env_int("RET_STEP_WR", 0), &cw, &wr);
     if (!fn) return fail(RET_ERR_UNSUPPORTED, "decode step: d_k=%d not in {16,32,64,128,256}", dk);
     hipStream_t s = (hipStream_t)stream;
     LaunchTimer tm("ret_recurrent_step", s);
-    hipLaunchKernelGGL(fn, dim3((dv + 63) / 64, B * H), dim3(dk >= 64 ? dk : 64), 0, s, A);
+    hipLaunchKernelGGL(fn, dim3((dv + cw - 1) / cw, B * H), dim3(64 * (dk / wr)), 0, s, A);
     tm.done();
     return launch_status("ret_recurrent_step");
 }

@@ -225,7 +225,8 @@ struct FullB {
     typedef RowTile<C, DVT> TV;
     typedef RowTile<C, DK> TK;  // local pass: whole d_k
     static constexpr int SQ = C * LDQ, SV = C * LDV;
-    static constexpr int FULL_BYTES = (3 * SQ + SV) * 2;         // sQ, sK, sKz, sV
+    static constexpr int STAGE = 3 * SQ;                         // one stage buffer: sQ, sK, sKz
+    static constexpr int FULL_BYTES = (2 * STAGE + 2 * SV) * 2;  // two stage buffers, two sV buffers
     static constexpr int LOCAL_BYTES = (C * LDK + C * LDV) * 2;  // local pass: sKz [C][DK] and sV [C][DVT]
     static constexpr int LDS_BYTES = FULL_BYTES > LOCAL_BYTES ? FULL_BYTES : LOCAL_BYTES;
     // two workgroups per CU when the LDS allows and the registers of d_k >= 128 are not needed
@@ -246,10 +247,9 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT>::OCC)) void chunk_fuse
     // Broadcast word (ticket, finish count): the first word of the staging region, which no thread writes
     // before a barrier that follows every read of it.
     int& s_word = *reinterpret_cast<int*>(smem);
-    uint16_t* sQ = smem;
-    uint16_t* sK = sQ + F::SQ;
-    uint16_t* sKz = sK + F::SQ;
-    uint16_t* sV = sKz + F::SQ;
+    // Full pass: stage buffers (sQ, sK, sKz) alternate by stage, sV buffers by chunk.
+    uint16_t* const stage_lds = smem;
+    uint16_t* const v_lds = smem + 2 * F::STAGE;
 
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g4 = 4 * (lane >> 4), n16 = lane & 15;
     const int ntiles = __builtin_amdgcn_readfirstlane(a.dv / DVT);
@@ -505,6 +505,10 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT>::OCC)) void chunk_fuse
         constexpr int par = decltype(parc)::value, sl = decltype(slc)::value;
         const int c = i / F::NSL;
         const int L = min(C, seg_n - c * C);
+        uint16_t* sQ = stage_lds + (i & 1) * F::STAGE;
+        uint16_t* sK = sQ + F::SQ;
+        uint16_t* sKz = sK + F::SQ;
+        uint16_t* sV = v_lds + (c & 1) * F::SV;
         if ((c & 7) == 0)  // exact factors every 8 chunks; angle addition in between
             rot[sl].cur.eval(a.pos0 + seg_t0 + (long long)c * C + qrow, a.theta, (sl * F::KS + qseg * 8) / 2);
 #pragma unroll
@@ -556,6 +560,58 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT>::OCC)) void chunk_fuse
     // S^T tile (jb, lb), lb <= jb, in row-by-row lower-triangle order.
     auto tri = [](int jb, int lb) constexpr { return jb * (jb + 1) / 2 + lb; };
     constexpr int KF = C / 32;  // reduction steps over the tokens of a chunk
+
+    // Products of stage i (chunk c, slice sl) from its stage buffer: S^T += K_s Q_s^T (all lower-triangle
+    // tiles: every wave needs all of P), the cross term O^T += R_s^T Q_s^T with R^T taken from the state
+    // accumulators (the previous chunk's state: this slice's update follows), and R_s <- gamma^L R_s +
+    // (K_s (.) zeta)^T V.
+    auto mma = [&](int i, auto slc, f32x4_t* S, f32x4_t* O, bf16x8_t* fv, float gL) __attribute__((always_inline)) {
+        constexpr int sl = decltype(slc)::value;
+        const int c = i / F::NSL;
+        const uint16_t* sQ = stage_lds + (i & 1) * F::STAGE;
+        const uint16_t* sK = sQ + F::SQ;
+        const uint16_t* sKz = sK + F::SQ;
+        const uint16_t* sV = v_lds + (c & 1) * F::SV;
+#pragma unroll
+        for (int kk = 0; kk < F::KS; kk += 32) {
+            bf16x8_t qf[F::NB], kf[F::NB];
+#pragma unroll
+            for (int x = 0; x < F::NB; ++x) {
+                qf[x] = frag_p(sQ + x * 16 * F::LDQ, F::LDQ, kk, lane);
+                kf[x] = frag_p(sK + x * 16 * F::LDQ, F::LDQ, kk, lane);
+            }
+#pragma unroll
+            for (int jb = 0; jb < F::NB; ++jb)
+#pragma unroll
+                for (int lb = 0; lb <= jb; ++lb) mfma(S[tri(jb, lb)], kf[lb], qf[jb]);
+            const int rb = (sl * F::KS + kk) / 16;
+            const bf16x8_t ra = acc_pair(R[rb], R[rb + 1]);
+#pragma unroll
+            for (int x = 0; x < F::NB; ++x) mfma(O[x], ra, qf[x]);
+        }
+        if constexpr (sl == 0) {
+#pragma unroll
+            for (int f = 0; f < KF; ++f) fv[f] = frag_trp(sV, F::LDV, 32 * f, w * 16, tro_vp);
+        }
+#pragma unroll
+        for (int x = sl * F::XB; x < (sl + 1) * F::XB; ++x) R[x] *= gL;
+#pragma unroll
+        for (int f = 0; f < KF; ++f) {
+#pragma unroll
+            for (int x = sl * F::XB; x < (sl + 1) * F::XB; ++x)
+                mfma(R[x], frag_trp(sKz, F::LDQ, 32 * f, (x - sl * F::XB) * 16, tro_q), fv[f]);
+        }
+    };
+
+    // Software pipeline over stages: stage i's products and stage i+1's staging (rotation, rounding, LDS
+    // writes into the other buffers) run back to back with no barrier between them, so the vector work of
+    // the staging issues while the matrix instructions execute; one barrier per stage.
+    __syncthreads();  // every wave has read the broadcast word, which the first commit overwrites
+    if (nst > 0) {
+        commit(0, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+        if (NBUF < nst) issue(NBUF, std::integral_constant<int, 0>{});
+    }
+    __syncthreads();
     auto chunk = [&](int c, auto cparc) __attribute__((always_inline)) {
         constexpr int cpar = decltype(cparc)::value;
         const int L = min(C, seg_n - c * C);
@@ -568,65 +624,37 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT>::OCC)) void chunk_fuse
         bf16x8_t fv[KF];  // V^T operand of d_v block w (B of the state update, A of the P.V product)
         static_for<0, F::NSL>([&](auto slc) __attribute__((always_inline)) {
             constexpr int sl = decltype(slc)::value;
-            constexpr int par = NBUF == 2 ? (cpar * F::NSL + sl) & 1 : 0;
+            constexpr int sln = (sl + 1) % F::NSL;  // slice of the next stage
+            // register buffer of the next stage (stage parity is chunk parity when NBUF = 2: NSL = 1 then)
+            constexpr int parn = NBUF == 2 ? 1 - cpar : 0;
             const int i = c * F::NSL + sl;
-            __syncthreads();  // every wave is done with the staged tiles of the previous stage
-            commit(i, std::integral_constant<int, par>{}, slc);
-            if (i + NBUF < nst) issue(i + NBUF, std::integral_constant<int, par>{});
-            __syncthreads();
+            mma(i, slc, S, O, fv, gL);
+            if (i + 1 < nst) {
+                commit(i + 1, std::integral_constant<int, parn>{}, std::integral_constant<int, sln>{});
+                if (i + 1 + NBUF < nst) issue(i + 1 + NBUF, std::integral_constant<int, parn>{});
+            }
+            if constexpr (sl == F::NSL - 1) {
+                // O^T = xi (.) (R^T Q^T) + V^T P^T, P = mask (.) S taken from the S^T accumulators as the B
+                // operand (keys 32f.. of query block x are tiles lb = 2f and 2f + 1).
 #pragma unroll
-            for (int kk = 0; kk < F::KS; kk += 32) {
-                // Q and K fragments of every block, shared by S^T = K Q^T (all lower-triangle tiles: every
-                // wave needs all of P) and the cross term O^T += R^T Q^T.
-                bf16x8_t qf[F::NB], kf[F::NB];
+                for (int x = 0; x < F::NB; ++x) O[x] *= Xi[x];
 #pragma unroll
-                for (int x = 0; x < F::NB; ++x) {
-                    qf[x] = frag_p(sQ + x * 16 * F::LDQ, F::LDQ, kk, lane);
-                    kf[x] = frag_p(sK + x * 16 * F::LDQ, F::LDQ, kk, lane);
+                for (int f = 0; f < KF; ++f) {
+#pragma unroll
+                    for (int x = 2 * f; x < F::NB; ++x) {
+                        const f32x4_t p0 = S[tri(x, 2 * f)] * f32x4_t{Dm[x - 2 * f][0], Dm[x - 2 * f][1],
+                                                                      Dm[x - 2 * f][2], Dm[x - 2 * f][3]};
+                        f32x4_t p1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                        if (2 * f + 1 <= x)
+                            p1 = S[tri(x, 2 * f + 1)] * f32x4_t{Dm[x - 2 * f - 1][0], Dm[x - 2 * f - 1][1],
+                                                                Dm[x - 2 * f - 1][2], Dm[x - 2 * f - 1][3]};
+                        mfma(O[x], fv[f], acc_pair(p0, p1));
+                    }
                 }
-#pragma unroll
-                for (int jb = 0; jb < F::NB; ++jb)
-#pragma unroll
-                    for (int lb = 0; lb <= jb; ++lb) mfma(S[tri(jb, lb)], kf[lb], qf[jb]);
-                // R^T of d_v block w over d_k rows sl*KS + kk .. +31, straight from the state accumulators
-                // (previous chunk's state: this slice's update follows).
-                const int rb = (sl * F::KS + kk) / 16;
-                const bf16x8_t ra = acc_pair(R[rb], R[rb + 1]);
-#pragma unroll
-                for (int x = 0; x < F::NB; ++x) mfma(O[x], ra, qf[x]);
+                store_out(c, O);
             }
-            // R_s <- gamma^L R_s + (K_s (.) zeta)^T V.
-            if constexpr (sl == 0) {
-#pragma unroll
-                for (int f = 0; f < KF; ++f) fv[f] = frag_trp(sV, F::LDV, 32 * f, w * 16, tro_vp);
-            }
-#pragma unroll
-            for (int x = sl * F::XB; x < (sl + 1) * F::XB; ++x) R[x] *= gL;
-#pragma unroll
-            for (int f = 0; f < KF; ++f) {
-#pragma unroll
-                for (int x = sl * F::XB; x < (sl + 1) * F::XB; ++x)
-                    mfma(R[x], frag_trp(sKz, F::LDQ, 32 * f, (x - sl * F::XB) * 16, tro_q), fv[f]);
-            }
+            __syncthreads();
         });
-        // O^T = xi (.) (R^T Q^T) + V^T P^T, P = mask (.) S taken from the S^T accumulators as the B operand
-        // (keys 32f.. of query block x are tiles lb = 2f and 2f + 1).
-#pragma unroll
-        for (int x = 0; x < F::NB; ++x) O[x] *= Xi[x];
-#pragma unroll
-        for (int f = 0; f < KF; ++f) {
-#pragma unroll
-            for (int x = 2 * f; x < F::NB; ++x) {
-                const f32x4_t p0 = S[tri(x, 2 * f)] * f32x4_t{Dm[x - 2 * f][0], Dm[x - 2 * f][1], Dm[x - 2 * f][2],
-                                                              Dm[x - 2 * f][3]};
-                f32x4_t p1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                if (2 * f + 1 <= x)
-                    p1 = S[tri(x, 2 * f + 1)] * f32x4_t{Dm[x - 2 * f - 1][0], Dm[x - 2 * f - 1][1],
-                                                        Dm[x - 2 * f - 1][2], Dm[x - 2 * f - 1][3]};
-                mfma(O[x], fv[f], acc_pair(p0, p1));
-            }
-        }
-        store_out(c, O);
     };
 
     for (int c = 0; c < nchunks; c += 2) {

@@ -691,19 +691,29 @@ struct StepArgs {
     float* state;
     int B, H, dk, dv;
     int in_bf16, out_bf16, rotate;
-    long long pos;
     float gamma[kMaxHeads];
-    double theta[kMaxPairs];
+    // cos and sin of pos * theta_i for the step's position, evaluated on the host in fp64
+    float rc[kMaxPairs], rs[kMaxPairs];
 };
 
 __device__ __forceinline__ float ld_in(const void* p, long long i, int bf) {
     return bf ? bf16_to_f32(((const uint16_t*)p)[i]) : ((const float*)p)[i];
 }
 
-// n consecutive input elements (fp32 or bf16) widened to fp32, loaded as 16/8-byte vectors.
+// n consecutive input elements (fp32 or bf16) widened to fp32, loaded as 16/8/4-byte vectors.
 template <class E, int N>
 __device__ __forceinline__ void load_n(const typename E::st* p, float* f) {
-    if constexpr (sizeof(typename E::st) == 2) {
+    if constexpr (N == 2) {
+        if constexpr (sizeof(typename E::st) == 2) {
+            const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
+            f[0] = __uint_as_float(u << 16);
+            f[1] = __uint_as_float(u & 0xffff0000u);
+        } else {
+            const float2 x = *reinterpret_cast<const float2*>(p);
+            f[0] = x.x;
+            f[1] = x.y;
+        }
+    } else if constexpr (sizeof(typename E::st) == 2) {
         static_assert(N % 4 == 0, "bf16 vector loads");
         if constexpr (N % 8 == 0) {
 #pragma unroll
@@ -731,36 +741,46 @@ __device__ __forceinline__ void load_n(const typename E::st* p, float* f) {
     }
 }
 
-template <class E, int DK>
-__global__ __launch_bounds__(DK >= 64 ? DK : 64) void recurrent_step_kernel(StepArgs a) {
+// One decode step for one (b, h) and CW state columns: NW waves of WR rows each. Lane (rg, cg) of a wave owns
+// columns 4cg..4cg+3 of rows rg*RPT .. +RPT-1 (each row segment one 16-byte access, a row's CW columns
+// contiguous across the cg lanes). q, k, v are read first, then the state rows; each row is updated and
+// written back as soon as it arrives, so loads and stores overlap. o sums q_r S_r over the rows (shuffles
+// within a wave, LDS across waves).
+template <class E, int DK, int CW, int WR>
+__global__ __launch_bounds__(64 * (DK / WR)) void recurrent_step_kernel(StepArgs a) {
     typedef typename E::st st;
-    constexpr int NW = DK >= 64 ? DK / 64 : 1;  // waves: 64 rows each
-    constexpr int WR = DK / NW;                 // rows per wave
-    constexpr int RPT = WR / 4;                 // rows per lane
-    __shared__ float4 part[NW > 1 ? NW : 1][16];
+    constexpr int NW = DK / WR;                 // waves
+    constexpr int CG = CW / 4;                  // column groups of a wave
+    constexpr int RG = 64 / CG;                 // row groups of a wave
+    constexpr int RPT = WR / RG;                // rows per lane (pairs of rows stay in one lane)
+    static_assert(RPT >= 2 && RPT % 2 == 0 && RG * CG == 64, "decode tile");
+    __shared__ float4 part[NW > 1 ? NW : 1][CG];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int cg = lane & 15, rg = lane >> 4;
+    const int cg = lane % CG, rg = lane / CG;
     const int pair = blockIdx.y, h = pair % a.H;
-    const int c0 = blockIdx.x * 64 + 4 * cg;
+    const int c0 = blockIdx.x * CW + 4 * cg;
     const bool active = c0 < a.dv;
     const int r0 = wv * WR + rg * RPT;  // first row of this lane
-    // The state rows are read first so that their latency overlaps everything else.
-    float* S = a.state + (long long)pair * DK * a.dv + (active ? c0 : 0);
-    float4 x[RPT];
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) x[i] = *reinterpret_cast<const float4*>(S + (long long)(r0 + i) * a.dv);
-    float vv[4], qv[RPT], kv[RPT];
+    float vv[4], qv[RPT], kv[RPT], rc[RPT / 2], rs[RPT / 2];
     load_n<E, 4>((const st*)a.v + (long long)pair * a.dv + (active ? c0 : 0), vv);
     load_n<E, RPT>((const st*)a.q + (long long)pair * a.dk + r0, qv);
     load_n<E, RPT>((const st*)a.k + (long long)pair * a.dk + r0, kv);
     if (a.rotate) {
-        // Lane j evaluates pair wv*WR/2 + j (j < WR/2); the lane owning rows r0.. takes pairs r0/2 + p.
-        float cj = 1.f, sj = 0.f;
-        if (lane < WR / 2) rot_cs(a.pos, a.theta[wv * WR / 2 + lane], &cj, &sj);
 #pragma unroll
         for (int p = 0; p < RPT / 2; ++p) {
-            const int src = rg * (RPT / 2) + p;
-            const float c = __shfl(cj, src), sn = __shfl(sj, src);
+            rc[p] = a.rc[r0 / 2 + p];
+            rs[p] = a.rs[r0 / 2 + p];
+        }
+    }
+    float* S = a.state + (long long)pair * DK * a.dv + (active ? c0 : 0);
+    float4 x[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) x[i] = *reinterpret_cast<const float4*>(S + (long long)(r0 + i) * a.dv);
+    if (a.rotate) {
+        // The pair (r0 + 2p, r0 + 2p + 1) turns by the angle pos * theta_(r0/2 + p).
+#pragma unroll
+        for (int p = 0; p < RPT / 2; ++p) {
+            const float c = rc[p], sn = rs[p];
             const float q0 = qv[2 * p], q1 = qv[2 * p + 1], k0 = kv[2 * p], k1 = kv[2 * p + 1];
             qv[2 * p] = q0 * c - q1 * sn;
             qv[2 * p + 1] = q0 * sn + q1 * c;
@@ -776,18 +796,15 @@ __global__ __launch_bounds__(DK >= 64 ? DK : 64) void recurrent_step_kernel(Step
         x[i].y = g * x[i].y + kv[i] * vv[1];
         x[i].z = g * x[i].z + kv[i] * vv[2];
         x[i].w = g * x[i].w + kv[i] * vv[3];
+        if (active) *reinterpret_cast<float4*>(S + (long long)(r0 + i) * a.dv) = x[i];
         acc.x += qv[i] * x[i].x;
         acc.y += qv[i] * x[i].y;
         acc.z += qv[i] * x[i].z;
         acc.w += qv[i] * x[i].w;
     }
-    if (active) {
+    // Sum over the row groups of the wave (lanes CG, 2CG, .. apart).
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) *reinterpret_cast<float4*>(S + (long long)(r0 + i) * a.dv) = x[i];
-    }
-    // Sum over the four row groups of the wave (lanes 16 and 32 apart).
-#pragma unroll
-    for (int m = 16; m <= 32; m *= 2) {
+    for (int m = CG; m < 64; m *= 2) {
         acc.x += __shfl_xor(acc.x, m);
         acc.y += __shfl_xor(acc.y, m);
         acc.z += __shfl_xor(acc.z, m);
@@ -849,6 +866,8 @@ bool chunk_kernels_bf16_small(int dk, int dv, int C, ChunkKernels* out);   // d_
 bool chunk_kernels_bf16_128(int dk, int dv, int C, ChunkKernels* out);     // d_k = 128
 bool chunk_kernels_bf16_256(int dk, int dv, int C, ChunkKernels* out);     // d_k = 256
 bool parallel_kernel_get(bool bf16_in, int dk, int dv, ParKernel* out);
-step_kernel_t step_kernel_get(bool bf16_in, int dk);
+// Decode kernel for d_k, the state columns per wave `cw` and rows per wave `wr` (0: defaults); null if none.
+// The launch is ceil(d_v / cw) x (B*H) workgroups of 64 * d_k / wr threads.
+step_kernel_t step_kernel_get(bool bf16_in, int dk, int cw, int wr, int* cw_used, int* wr_used);
 
 }  // namespace ret

@@ -53,19 +53,51 @@ bool parallel_kernel_get(bool bf16_in, int dk, int dv, ParKernel* out) {
     return false;
 }
 
-step_kernel_t step_kernel_get(bool bf16_in, int dk) {
-#define RET_STEP(E)                                 \
-    switch (dk) {                                   \
-        case 16: return recurrent_step_kernel<E, 16>;   \
-        case 32: return recurrent_step_kernel<E, 32>;   \
-        case 64: return recurrent_step_kernel<E, 64>;   \
-        case 128: return recurrent_step_kernel<E, 128>; \
-        case 256: return recurrent_step_kernel<E, 256>; \
-        default: return nullptr;                    \
+// Tiles of a decode workgroup: 64, 32 or 16 state columns per wave (more, smaller waves per (b, h) for more
+// memory parallelism) and 64, 32 or 16 rows per wave (several waves per column tile). Every lane keeps at
+// least one pair of rows: rows per lane = wr * cw / 256 >= 2.
+namespace {
+template <class E, int DK, int CW, int WR>
+step_kernel_t step_pick() {
+    if constexpr (WR <= DK && WR * CW >= 512 && DK / WR <= 16) return recurrent_step_kernel<E, DK, CW, WR>;
+    return nullptr;
+}
+template <class E, int DK, int CW>
+step_kernel_t step_pick_wr(int wr) {
+    if (wr == 16) return step_pick<E, DK, CW, 16>();
+    if (wr == 32) return step_pick<E, DK, CW, 32>();
+    return step_pick<E, DK, CW, 64>();
+}
+template <class E, int DK>
+step_kernel_t step_pick_cw(int cw, int wr) {
+    if (cw == 16) return step_pick_wr<E, DK, 16>(wr);
+    if (cw == 32) return step_pick_wr<E, DK, 32>(wr);
+    return step_pick_wr<E, DK, 64>(wr);
+}
+template <class E>
+step_kernel_t step_pick_dk(int dk, int cw, int wr) {
+    switch (dk) {
+        case 16: return step_pick_cw<E, 16>(cw, wr);
+        case 32: return step_pick_cw<E, 32>(cw, wr);
+        case 64: return step_pick_cw<E, 64>(cw, wr);
+        case 128: return step_pick_cw<E, 128>(cw, wr);
+        case 256: return step_pick_cw<E, 256>(cw, wr);
+        default: return nullptr;
     }
-    if (bf16_in) RET_STEP(BF16)
-    RET_STEP(F32)
-#undef RET_STEP
+}
+}  // namespace
+
+step_kernel_t step_kernel_get(bool bf16_in, int dk, int cw, int wr, int* cw_used, int* wr_used) {
+    if (cw == 0) cw = 64;  // defaults: 64 columns x 32 rows per wave (two waves per 64-row tile)
+    if (wr == 0) wr = 32;
+    if (cw != 16 && cw != 32 && cw != 64) return nullptr;
+    if (wr != 16 && wr != 32 && wr != 64) return nullptr;
+    if (wr > dk) wr = dk < 16 ? 16 : dk;                // short d_k: one wave holds every row
+    while (wr * cw < 512 && cw < 64) cw *= 2;           // at least two rows per lane
+    while (wr * cw < 512 && wr < 64 && wr < dk) wr *= 2;
+    *cw_used = cw;
+    *wr_used = wr;
+    return bf16_in ? step_pick_dk<BF16>(dk, cw, wr) : step_pick_dk<F32>(dk, cw, wr);
 }
 
 fwd_kernel_t segment_scan_get() { return segment_scan_kernel; }

@@ -172,11 +172,16 @@ def test_parallel_small(R, dt, dk, dv):
     assert rel_err(to_host(o), ref) <= tol(dt)
 
 
+# decode tiles: state columns and rows per wave (the library widens tiles too small for a shape)
+@pytest.mark.parametrize("cw,wr", [("16", "64"), ("32", "64"), ("64", "64"), ("32", "32"), ("32", "16"),
+                                   ("64", "16")])
 @pytest.mark.parametrize("dt,dk,dv", [("f32", 16, 16), ("f32", 64, 36), ("bf16", 64, 64), ("bf16", 128, 128),
                                       ("bf16", 256, 200)])
-def test_recurrent_steps_small(R, dt, dk, dv):
+def test_recurrent_steps_small(R, dt, dk, dv, cw, wr, monkeypatch):
     import torch
-    print_case("recurrent_small", dt, dk, dv)
+    print_case("recurrent_small", dt, dk, dv, cw, wr)
+    monkeypatch.setenv("RET_STEP_CW", cw)
+    monkeypatch.setenv("RET_STEP_WR", wr)
     rng = np.random.default_rng(9)
     B, H, n = 3, 2, 20
     scale = 1.0 if dt == "f32" else 8.0
