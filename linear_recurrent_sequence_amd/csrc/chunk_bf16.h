@@ -159,6 +159,7 @@ struct SliceRot {
 // slot's stores completed; a wait that sees no progress for ~0.17 s gives up and sets the sticky error word
 // instead of hanging. The unit's last workgroup past the look-back returns its counters and flags to zero.
 // ---------------------------------------------------------------------------------------------------
+constexpr int kOutAux = 0;                        // output stores: default cache policy (streaming measured slower)
 constexpr int kChainGroup = 8;                    // segments per look-back group
 constexpr int kChainAux = 16;                     // buffer cache policy: sc1 (device-scope coherent)
 constexpr unsigned long long kChainSpin = 1ull << 24;  // give-up time in s_memrealtime ticks (100 MHz)
@@ -225,12 +226,20 @@ struct FullB {
     typedef RowTile<C, DVT> TV;
     typedef RowTile<C, DK> TK;  // local pass: whole d_k
     static constexpr int SQ = C * LDQ, SV = C * LDV;
-    static constexpr int STAGE = 3 * SQ;                         // one stage buffer: sQ, sK, sKz
-    static constexpr int FULL_BYTES = (2 * STAGE + 2 * SV) * 2;  // two stage buffers, two sV buffers
+    static constexpr int STAGE = 3 * SQ;  // one stage buffer: sQ, sK, sKz
+    // With one d_k slice a chunk's V is read while the next chunk's is staged: two V buffers. With several,
+    // V is read only in the first slice's products, a barrier ahead of the next chunk's staging: one.
+    static constexpr int NVB = NSL == 1 ? 2 : 1;
+    // Large d_k: each wave computes only its share of the S^T tiles and P goes through LDS, instead of every
+    // wave computing all tiles (which costs NB(NB+1)/2 * d_k/32 MFMAs per wave per chunk).
+    static constexpr bool SHARED_P = DK >= 128;
+    static constexpr int NS_W = (NS + kWaves - 1) / kWaves;
+    static constexpr int LDP = C + 8, SP = SHARED_P ? C * LDP : 0;
+    static constexpr int FULL_BYTES = (2 * STAGE + NVB * SV + SP) * 2;
     static constexpr int LOCAL_BYTES = (C * LDK + C * LDV) * 2;  // local pass: sKz [C][DK] and sV [C][DVT]
     static constexpr int LDS_BYTES = FULL_BYTES > LOCAL_BYTES ? FULL_BYTES : LOCAL_BYTES;
-    // two workgroups per CU when the LDS allows and the registers of d_k >= 128 are not needed
-    static constexpr int OCC = LDS_BYTES <= 80 * 1024 && DK <= 64 ? 2 : 1;
+    // two workgroups per CU when the LDS allows and the registers of d_k = 256 are not needed
+    static constexpr int OCC = LDS_BYTES <= 80 * 1024 && DK <= 128 ? 2 : 1;
     static_assert(NDV == kWaves, "one d_v block per wave");
     static_assert(C == 32 || C == 64, "chunk tile of 32 or 64 tokens");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -250,6 +259,7 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT>::OCC)) void chunk_fuse
     // Full pass: stage buffers (sQ, sK, sKz) alternate by stage, sV buffers by chunk.
     uint16_t* const stage_lds = smem;
     uint16_t* const v_lds = smem + 2 * F::STAGE;
+    uint16_t* const sP = v_lds + F::NVB * F::SV;  // shared P (large d_k only)
 
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g4 = 4 * (lane >> 4), n16 = lane & 15;
     const int ntiles = __builtin_amdgcn_readfirstlane(a.dv / DVT);
@@ -493,6 +503,18 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT>::OCC)) void chunk_fuse
         }
 #pragma unroll
     for (int x = 0; x < F::NB; ++x) Xi[x] = gpow(lg, (float)(x * 16 + n16 + 1));
+    // Shared-P layout: S^T tile slot x of wave w is lower-triangle tile w + 4x (slots past the last tile repeat
+    // it; their results are never stored), with its mask factors.
+    int Sjb[F::NS_W], Slb[F::NS_W];
+    f32x4_t DmS[F::NS_W];
+    if constexpr (F::SHARED_P) {
+#pragma unroll
+        for (int x = 0; x < F::NS_W; ++x) {
+            tri_tile<F::NB>(min(w + kWaves * x, F::NS - 1), Sjb[x], Slb[x]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) DmS[x][e] = Dm[Sjb[x] - Slb[x]][e];
+        }
+    }
 #pragma unroll
     for (int p = 0; p < TQ::NP; ++p) zfull[p] = gpow(lg, (float)(C - 1 - (qrow + p * TQ::RP)));
     const float gC = gpow(lg, (float)C);
@@ -508,7 +530,7 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT>::OCC)) void chunk_fuse
         uint16_t* sQ = stage_lds + (i & 1) * F::STAGE;
         uint16_t* sK = sQ + F::SQ;
         uint16_t* sKz = sK + F::SQ;
-        uint16_t* sV = v_lds + (c & 1) * F::SV;
+        uint16_t* sV = v_lds + (F::NVB == 2 ? (c & 1) * F::SV : 0);
         if ((c & 7) == 0)  // exact factors every 8 chunks; angle addition in between
             rot[sl].cur.eval(a.pos0 + seg_t0 + (long long)c * C + qrow, a.theta, (sl * F::KS + qseg * 8) / 2);
 #pragma unroll
@@ -549,11 +571,12 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT>::OCC)) void chunk_fuse
                 __builtin_amdgcn_raw_buffer_store_b64(
                     __builtin_bit_cast(uint32_t __attribute__((ext_vector_type(2))),
                                        make_uint2(pack2_bf16(O[x][0], O[x][1]), pack2_bf16(O[x][2], O[x][3]))),
-                    ro, o_voff, x * 16 * rsv * 2, 0);
+                    ro, o_voff, x * 16 * rsv * 2, kOutAux);
         } else {
 #pragma unroll
             for (int x = 0; x < F::NB; ++x)
-                buf_store16(ro, o_voff, x * 16 * rsv * 4, __builtin_bit_cast(u32x4_t, O[x]));
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, O[x]), ro, o_voff, x * 16 * rsv * 4,
+                                                       kOutAux);
         }
     };
 
@@ -571,19 +594,26 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT>::OCC)) void chunk_fuse
         const uint16_t* sQ = stage_lds + (i & 1) * F::STAGE;
         const uint16_t* sK = sQ + F::SQ;
         const uint16_t* sKz = sK + F::SQ;
-        const uint16_t* sV = v_lds + (c & 1) * F::SV;
+        const uint16_t* sV = v_lds + (F::NVB == 2 ? (c & 1) * F::SV : 0);
 #pragma unroll
         for (int kk = 0; kk < F::KS; kk += 32) {
             bf16x8_t qf[F::NB], kf[F::NB];
 #pragma unroll
             for (int x = 0; x < F::NB; ++x) {
                 qf[x] = frag_p(sQ + x * 16 * F::LDQ, F::LDQ, kk, lane);
-                kf[x] = frag_p(sK + x * 16 * F::LDQ, F::LDQ, kk, lane);
+                if constexpr (!F::SHARED_P) kf[x] = frag_p(sK + x * 16 * F::LDQ, F::LDQ, kk, lane);
             }
+            if constexpr (F::SHARED_P) {
 #pragma unroll
-            for (int jb = 0; jb < F::NB; ++jb)
+                for (int x = 0; x < F::NS_W; ++x)
+                    mfma(S[x], frag_p(sK + Slb[x] * 16 * F::LDQ, F::LDQ, kk, lane),
+                         frag_p(sQ + Sjb[x] * 16 * F::LDQ, F::LDQ, kk, lane));
+            } else {
 #pragma unroll
-                for (int lb = 0; lb <= jb; ++lb) mfma(S[tri(jb, lb)], kf[lb], qf[jb]);
+                for (int jb = 0; jb < F::NB; ++jb)
+#pragma unroll
+                    for (int lb = 0; lb <= jb; ++lb) mfma(S[tri(jb, lb)], kf[lb], qf[jb]);
+            }
             const int rb = (sl * F::KS + kk) / 16;
             const bf16x8_t ra = acc_pair(R[rb], R[rb + 1]);
 #pragma unroll
@@ -606,6 +636,8 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT>::OCC)) void chunk_fuse
     // Software pipeline over stages: stage i's products and stage i+1's staging (rotation, rounding, LDS
     // writes into the other buffers) run back to back with no barrier between them, so the vector work of
     // the staging issues while the matrix instructions execute; one barrier per stage.
+    if constexpr (F::SHARED_P)  // scores above the diagonal are never written: zero for the P.V product
+        for (int i = tid; i < F::SP; i += kThreads) sP[i] = 0;
     __syncthreads();  // every wave has read the broadcast word, which the first commit overwrites
     if (nst > 0) {
         commit(0, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
@@ -616,9 +648,10 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT>::OCC)) void chunk_fuse
         constexpr int cpar = decltype(cparc)::value;
         const int L = min(C, seg_n - c * C);
         const float gL = L == C ? gC : gpow(lg, (float)L);
-        f32x4_t S[F::NS], O[F::NB];
+        constexpr int NSA = F::SHARED_P ? F::NS_W : F::NS;  // S^T accumulators of this wave
+        f32x4_t S[NSA], O[F::NB];
 #pragma unroll
-        for (int x = 0; x < F::NS; ++x) S[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int x = 0; x < NSA; ++x) S[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int x = 0; x < F::NB; ++x) O[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         bf16x8_t fv[KF];  // V^T operand of d_v block w (B of the state update, A of the P.V product)
@@ -633,7 +666,22 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT>::OCC)) void chunk_fuse
                 commit(i + 1, std::integral_constant<int, parn>{}, std::integral_constant<int, sln>{});
                 if (i + 1 + NBUF < nst) issue(i + 1 + NBUF, std::integral_constant<int, parn>{});
             }
-            if constexpr (sl == F::NSL - 1) {
+            if constexpr (sl == F::NSL - 1 && F::SHARED_P) {
+                // P = mask (.) S^T of this wave's tiles into LDS (4 consecutive keys of one query per lane),
+                // then O^T = xi (.) (R^T Q^T) + V^T P^T with P read back in the permuted key order.
+#pragma unroll
+                for (int x = 0; x < F::NS_W; ++x)
+                    if (w + kWaves * x < F::NS) store4(sP + (Sjb[x] * 16 + n16) * F::LDP + Slb[x] * 16 + g4, S[x] * DmS[x]);
+                __syncthreads();
+#pragma unroll
+                for (int x = 0; x < F::NB; ++x) O[x] *= Xi[x];
+#pragma unroll
+                for (int f = 0; f < KF; ++f) {
+#pragma unroll
+                    for (int x = 2 * f; x < F::NB; ++x) mfma(O[x], fv[f], frag_p(sP + x * 16 * F::LDP, F::LDP, 32 * f, lane));
+                }
+                store_out(c, O);
+            } else if constexpr (sl == F::NSL - 1) {
                 // O^T = xi (.) (R^T Q^T) + V^T P^T, P = mask (.) S taken from the S^T accumulators as the B
                 // operand (keys 32f.. of query block x are tiles lb = 2f and 2f + 1).
 #pragma unroll
