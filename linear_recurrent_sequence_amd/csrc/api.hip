@@ -170,6 +170,38 @@ size_t segment_ws_bytes(const ChunkKernels& ck, int B, int H, int dk, int dv, in
     return sizeof(ChainHeader) + (size_t)B * H * nseg * dk * dv * sizeof(float);
 }
 
+// The plan of one chunkwise call: segments, and whether q and k are rotated once up front into the workspace
+// (bf16 single-pass kernels with at least 4 d_v tiles, i.e. staging would rotate the same rows 4+ times).
+// Workspace layout: [segment chain or split-kernel states][q'][k'], each part 256-byte aligned. A smaller
+// workspace first drops the rotated copies, then halves the segment count until the states fit.
+struct ChunkPlan {
+    int nseg, seg_len;
+    size_t chain_bytes, rot_bytes;
+};
+ChunkPlan plan_chunk(const ChunkKernels& ck, int B, int N, int H, int dk, int dv, int chunk, bool rotate,
+                     size_t avail) {
+    ChunkPlan p;
+    plan_segments(B, N, H, dv, chunk, ck.dvt, &p.nseg, &p.seg_len);
+    p.chain_bytes = (segment_ws_bytes(ck, B, H, dk, dv, p.nseg) + 255) / 256 * 256;
+    p.rot_bytes = 0;
+    if (ck.fused_pre && rotate && dv / ck.dvt >= 4)
+        p.rot_bytes = 2 * (((size_t)B * N * H * dk * 2 + 255) / 256 * 256);
+    if (p.chain_bytes + p.rot_bytes > avail) p.rot_bytes = 0;
+    while (p.nseg > 1 && segment_ws_bytes(ck, B, H, dk, dv, p.nseg) > avail) {
+        const int nchunks = (N + chunk - 1) / chunk;
+        int spc = p.seg_len / chunk * 2;
+        if (spc > nchunks) spc = nchunks;
+        p.seg_len = spc * chunk;
+        p.nseg = (nchunks + spc - 1) / spc;
+        p.chain_bytes = (segment_ws_bytes(ck, B, H, dk, dv, p.nseg) + 255) / 256 * 256;
+    }
+    if (p.nseg == 1) {
+        p.seg_len = N;
+        p.chain_bytes = 0;
+    }
+    return p;
+}
+
 }  // namespace
 
 // =====================================================================================================
@@ -215,9 +247,8 @@ size_t ret_chunkwise_workspace_bytes(int B, int N, int H, int dk, int dv, int ch
     ChunkKernels ck;
     if (B <= 0 || N <= 0 || H <= 0 || dk <= 0 || dv <= 0 || chunk <= 0) return 0;
     if (!pick_chunk(in_dt, dk, dv, chunk, &ck)) return 0;
-    int nseg, seg_len;
-    plan_segments(B, N, H, dv, chunk, ck.dvt, &nseg, &seg_len);
-    return segment_ws_bytes(ck, B, H, dk, dv, nseg);
+    const ChunkPlan p = plan_chunk(ck, B, N, H, dk, dv, chunk, true, SIZE_MAX);
+    return p.chain_bytes + p.rot_bytes;
 }
 
 ret_status_t ret_chunkwise_fwd(const void* q, const void* k, const void* v, void* o, int B, int N, int H, int dk,
@@ -239,17 +270,8 @@ ret_status_t ret_chunkwise_fwd(const void* q, const void* k, const void* v, void
     if ((long long)chunk * H * (dk > dv ? dk : dv) * 4 >= (1LL << 31))
         return fail(RET_ERR_UNSUPPORTED, "chunkwise form: chunk*H*max(d_k,d_v) too large (%d*%d*%d)", chunk, H,
                     dk > dv ? dk : dv);
-    int nseg, seg_len;
-    plan_segments(B, N, H, dv, chunk, ck.dvt, &nseg, &seg_len);
-    // Fewer segments when the workspace given is smaller than the plan's.
-    while (nseg > 1 && segment_ws_bytes(ck, B, H, dk, dv, nseg) > workspace_bytes) {
-        const int nchunks = (N + chunk - 1) / chunk;
-        int spc = seg_len / chunk * 2;
-        if (spc > nchunks) spc = nchunks;
-        seg_len = spc * chunk;
-        nseg = (nchunks + spc - 1) / spc;
-    }
-    if (nseg == 1) seg_len = N;
+    const ChunkPlan plan = plan_chunk(ck, B, N, H, dk, dv, chunk, theta != nullptr, workspace_bytes);
+    const int nseg = plan.nseg, seg_len = plan.seg_len;
 
     FwdArgs A;
     fill_fwd(A, q, k, v, o, B, N, H, dk, dv, out_dt, gamma, theta, pos0);
@@ -262,9 +284,25 @@ ret_status_t ret_chunkwise_fwd(const void* q, const void* k, const void* v, void
     hipStream_t s = (hipStream_t)stream;
     const int ntiles = dv / ck.dvt;
     if (ck.fused) {
+        // Staging copies rows instead of rotating them when there is no rotation, or when q and k are rotated
+        // once up front (several d_v tiles stage the same rows).
+        fwd_kernel_t fn = ck.fused;
+        if (!theta) {
+            fn = ck.fused_pre;
+            A.qr = const_cast<void*>(q);
+            A.kr = const_cast<void*>(k);
+        } else if (plan.rot_bytes > 0) {
+            fn = ck.fused_pre;
+            A.qr = (char*)workspace + plan.chain_bytes;
+            A.kr = (char*)A.qr + plan.rot_bytes / 2;
+            LaunchTimer tr("ret_rotate_qk", s);
+            hipLaunchKernelGGL(rotate_qk_get(), dim3(rotate_qk_blocks(B, N, H, dk)), dim3(256), 0, s, A);
+            tr.done();
+            if ((st = launch_status("ret_rotate_qk")) != RET_OK) return st;
+        }
         const unsigned grid = (unsigned)((long long)nseg * B * H * ntiles);
         LaunchTimer tm("ret_chunk_fused", s);
-        hipLaunchKernelGGL(ck.fused, dim3(grid), dim3(kThreads), 0, s, A);
+        hipLaunchKernelGGL(fn, dim3(grid), dim3(kThreads), 0, s, A);
         tm.done();
         return launch_status("ret_chunk_fused");
     }

@@ -159,7 +159,7 @@ struct SliceRot {
 // slot's stores completed; a wait that sees no progress for ~0.17 s gives up and sets the sticky error word
 // instead of hanging. The unit's last workgroup past the look-back returns its counters and flags to zero.
 // ---------------------------------------------------------------------------------------------------
-constexpr int kOutAux = 0;                        // output stores: default cache policy (streaming measured slower)
+constexpr int kOutAux = 0;                        // output stores: default policy (nt and sc1 measured no faster)
 constexpr int kChainGroup = 8;                    // segments per look-back group
 constexpr int kChainAux = 16;                     // buffer cache policy: sc1 (device-scope coherent)
 constexpr unsigned long long kChainSpin = 1ull << 24;  // give-up time in s_memrealtime ticks (100 MHz)
@@ -215,18 +215,25 @@ __device__ __forceinline__ void slot_load(const float* slot, f32x4_t* v, int tid
 // O^T += R^T Q^T with R^T taken from the state accumulators and the state update; then
 // O^T = xi (.) O^T + V^T P^T with P = mask (.) S straight from the S^T accumulators, stored to the output.
 // ---------------------------------------------------------------------------------------------------
-template <int DK, int C, int DVT>
+template <int DK, int C, int DVT, bool PRE>
 struct FullB {
     static constexpr int KS = DK < 64 ? DK : 64;
     static constexpr int NSL = DK / KS;
-    static constexpr int LDQ = KS + 8, LDV = DVT + 8, LDK = DK + 8;
+    // Row pitches (elements) of 36 words mod 64 LDS banks, so the rows one fragment or transposed read
+    // touches fall in distinct banks: a width plus 8 gives that at 64 columns but 4 mod 64 at 128 and 256,
+    // and 20 at 32.
+    static constexpr int pitch(int w) { return w + ((72 - w) % 128 + 128) % 128; }
+    static constexpr int LDQ = pitch(KS), LDV = pitch(DVT), LDK = pitch(DK);
     static constexpr int NB = C / 16, NDV = DVT / 16, NKB = DK / 16, XB = KS / 16;
     static constexpr int NS = Tri<NB>::count;
     typedef RowTile<C, KS> TQ;
     typedef RowTile<C, DVT> TV;
     typedef RowTile<C, DK> TK;  // local pass: whole d_k
     static constexpr int SQ = C * LDQ, SV = C * LDV;
-    static constexpr int STAGE = 3 * SQ;  // one stage buffer: sQ, sK, sKz
+    // One stage buffer: sQ, sK and (rotating in staging) sKz = K (.) zeta; with pre-rotated operands zeta goes
+    // on the smaller V tile instead (sVz beside sV).
+    static constexpr int STAGE = (PRE ? 2 : 3) * SQ;
+    static constexpr int VBUF = (PRE ? 2 : 1) * SV;
     // With one d_k slice a chunk's V is read while the next chunk's is staged: two V buffers. With several,
     // V is read only in the first slice's products, a barrier ahead of the next chunk's staging: one.
     static constexpr int NVB = NSL == 1 ? 2 : 1;
@@ -235,7 +242,7 @@ struct FullB {
     static constexpr bool SHARED_P = DK >= 128;
     static constexpr int NS_W = (NS + kWaves - 1) / kWaves;
     static constexpr int LDP = C + 8, SP = SHARED_P ? C * LDP : 0;
-    static constexpr int FULL_BYTES = (2 * STAGE + NVB * SV + SP) * 2;
+    static constexpr int FULL_BYTES = (2 * STAGE + NVB * VBUF + SP) * 2;
     static constexpr int LOCAL_BYTES = (C * LDK + C * LDV) * 2;  // local pass: sKz [C][DK] and sV [C][DVT]
     static constexpr int LDS_BYTES = FULL_BYTES > LOCAL_BYTES ? FULL_BYTES : LOCAL_BYTES;
     // two workgroups per CU when the LDS allows and the registers of d_k = 256 are not needed
@@ -244,11 +251,12 @@ struct FullB {
     static_assert(C == 32 || C == 64, "chunk tile of 32 or 64 tokens");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     static_assert(KS % 32 == 0, "tiling");
+    static_assert((LDK / 2) % 64 == 36 && (LDQ / 2) % 64 == 36 && (LDV / 2) % 64 == 36, "LDS row pitch");
 };
 
-template <int DK, int C, int DVT>
-__global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT>::OCC)) void chunk_fused_bf16(FwdArgs a) {
-    typedef FullB<DK, C, DVT> F;
+template <int DK, int C, int DVT, bool PRE>
+__global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT, PRE>::OCC)) void chunk_fused_bf16(FwdArgs a) {
+    typedef FullB<DK, C, DVT, PRE> F;
     typedef typename F::TQ TQ;
     typedef typename F::TV TV;
     typedef typename F::TK TK;
@@ -259,7 +267,7 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT>::OCC)) void chunk_fuse
     // Full pass: stage buffers (sQ, sK, sKz) alternate by stage, sV buffers by chunk.
     uint16_t* const stage_lds = smem;
     uint16_t* const v_lds = smem + 2 * F::STAGE;
-    uint16_t* const sP = v_lds + F::NVB * F::SV;  // shared P (large d_k only)
+    uint16_t* const sP = v_lds + F::NVB * F::VBUF;  // shared P (large d_k only)
 
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g4 = 4 * (lane >> 4), n16 = lane & 15;
     const int ntiles = __builtin_amdgcn_readfirstlane(a.dv / DVT);
@@ -267,8 +275,18 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT>::OCC)) void chunk_fuse
     const bool chained = a.nseg > 1;
     ChainHeader* hdr = reinterpret_cast<ChainHeader*>(a.ws);
     // The unit comes from the launch index; with several segments the segment is the unit's next ticket, so
-    // the workgroups that own a unit's earlier segments have all started.
-    const int unit = __builtin_amdgcn_readfirstlane((int)(blockIdx.x % (unsigned)units));
+    // the workgroups that own a unit's earlier segments have all started. Workgroups are dispatched to the 8
+    // XCDs in turn (launch index mod 8); when the grid divides evenly, the d_v tiles of one (b, h) get launch
+    // indices of one residue, so they run on one XCD and its L2 serves the q and k rows they all stage.
+    const int pairs = units / ntiles;
+    int unit_i;
+    if (ntiles > 1 && gridDim.x % (8u * ntiles) == 0) {
+        const int xcd = blockIdx.x % 8, q8 = blockIdx.x / 8;
+        unit_i = ((q8 / ntiles * 8 + xcd) % pairs) * ntiles + q8 % ntiles;
+    } else {
+        unit_i = blockIdx.x % (unsigned)units;
+    }
+    const int unit = __builtin_amdgcn_readfirstlane(unit_i);
     int seg = __builtin_amdgcn_readfirstlane((int)(blockIdx.x / (unsigned)units));
     int* ctr = nullptr;
     if (chained) {
@@ -293,8 +311,9 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT>::OCC)) void chunk_fuse
     const int nchunks = (seg_n + C - 1) / C;
     const int rsk = aH * adk, rsv = aH * adv;  // elements between consecutive tokens
     const long long head0 = ((long long)b * aN + seg_t0) * aH + h;
-    const uint16_t* qh = (const uint16_t*)a.q + head0 * adk;
-    const uint16_t* kh = (const uint16_t*)a.k + head0 * adk;
+    // q and k, or their rotated copies (PRE: staging copies rows instead of rotating them)
+    const uint16_t* qh = (const uint16_t*)(PRE ? a.qr : a.q) + head0 * adk;
+    const uint16_t* kh = (const uint16_t*)(PRE ? a.kr : a.k) + head0 * adk;
     const uint16_t* vh = (const uint16_t*)a.v + head0 * adv + dv0;
     const int osz = a.out_bf16 ? 2 : 4;
     char* oh = (char*)a.o + (head0 * adv + dv0) * osz;
@@ -333,42 +352,64 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT>::OCC)) void chunk_fuse
         const int krow = tid / TK::SPR, kseg = tid % TK::SPR;
         const int koff = (krow * rsk + kseg * 8) * 2;
         const int tro_k = tr_lane_offset(F::LDK, lane);
-        u32x4_t lk[TK::NP], lv[TV::NP];
-        auto lissue = [&](int c) __attribute__((always_inline)) {
+        // Two register buffers: the loads of chunk c+2 go out as soon as chunk c is staged.
+        u32x4_t lk[2][TK::NP], lv[2][TV::NP];
+        auto lissue = [&](int c, auto parc) __attribute__((always_inline)) {
+            constexpr int par = decltype(parc)::value;
             const long long tc = (long long)c * C;
             const rsrc_t rk = bytes_rsrc(kh + tc * rsk, ((C - 1) * rsk + DK) * 2);
             const rsrc_t rv = bytes_rsrc(vh + tc * rsv, ((C - 1) * rsv + DVT) * 2);
 #pragma unroll
-            for (int p = 0; p < TK::NP; ++p) lk[p] = buf_load16(rk, koff, p * TK::RP * rsk * 2);
+            for (int p = 0; p < TK::NP; ++p) lk[par][p] = buf_load16(rk, koff, p * TK::RP * rsk * 2);
 #pragma unroll
-            for (int p = 0; p < TV::NP; ++p) lv[p] = buf_load16(rv, voff, p * TV::RP * rsv * 2);
+            for (int p = 0; p < TV::NP; ++p) lv[par][p] = buf_load16(rv, voff, p * TV::RP * rsv * 2);
         };
-        lissue(0);
-        float zl[TK::NP];
+        lissue(0, std::integral_constant<int, 0>{});
+        if (nchunks > 1) lissue(1, std::integral_constant<int, 1>{});
+        float zl[TK::NP], zlv[TV::NP];
 #pragma unroll
         for (int p = 0; p < TK::NP; ++p) zl[p] = gpow(lg, (float)(C - 1 - (krow + p * TK::RP)));
+#pragma unroll
+        for (int p = 0; p < TV::NP; ++p) zlv[p] = gpow(lg, (float)(C - 1 - (vrow + p * TV::RP)));
         const float gC = gpow(lg, (float)C);
         SliceRot<C, TK::RP, TK::NP> lrot;  // identity factors without rotation (theta all zero)
-        lrot.init_steps(a.theta, kseg * 4);
-        for (int c = 0; c < nchunks; ++c) {  // segments before the last hold whole chunks only
+        if constexpr (!PRE) lrot.init_steps(a.theta, kseg * 4);
+        // One chunk of the local pass (segments before the last hold whole chunks only).
+        auto lchunk = [&](int c, auto parc) __attribute__((always_inline)) {
+            constexpr int par = decltype(parc)::value;
             if (c > 0) __syncthreads();
-            if ((c & 7) == 0) lrot.cur.eval(a.pos0 + seg_t0 + (long long)c * C + krow, a.theta, kseg * 4);
+            if constexpr (PRE) {  // K' as staged; zeta on V
 #pragma unroll
-            for (int p = 0; p < TK::NP; ++p)
-                if (TK::live(krow, p)) {
-                    float kf[8];
-                    unpack8(lk[p], kf);
-                    lrot.cur.apply(kf);
-                    if (p + 1 < TK::NP) lrot.cur.turn(lrot.pass);
+                for (int p = 0; p < TK::NP; ++p)
+                    if (TK::live(krow, p)) lds_store16(lK + (krow + p * TK::RP) * F::LDK + kseg * 8, lk[par][p]);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) kf[e] *= zl[p];
-                    lds_store16(lK + (krow + p * TK::RP) * F::LDK + kseg * 8, pack8(kf));
-                }
-            lrot.next_chunk();
+                for (int p = 0; p < TV::NP; ++p)
+                    if (TV::live(vrow, p)) {
+                        float vf[8];
+                        unpack8(lv[par][p], vf);
 #pragma unroll
-            for (int p = 0; p < TV::NP; ++p)
-                if (TV::live(vrow, p)) lds_store16(lV + (vrow + p * TV::RP) * F::LDV + vseg * 8, lv[p]);
-            if (c + 1 < nchunks) lissue(c + 1);
+                        for (int e = 0; e < 8; ++e) vf[e] *= zlv[p];
+                        lds_store16(lV + (vrow + p * TV::RP) * F::LDV + vseg * 8, pack8(vf));
+                    }
+            } else {
+                if ((c & 7) == 0) lrot.cur.eval(a.pos0 + seg_t0 + (long long)c * C + krow, a.theta, kseg * 4);
+#pragma unroll
+                for (int p = 0; p < TK::NP; ++p)
+                    if (TK::live(krow, p)) {
+                        float kf[8];
+                        unpack8(lk[par][p], kf);
+                        lrot.cur.apply(kf);
+                        if (p + 1 < TK::NP) lrot.cur.turn(lrot.pass);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) kf[e] *= zl[p];
+                        lds_store16(lK + (krow + p * TK::RP) * F::LDK + kseg * 8, pack8(kf));
+                    }
+                lrot.next_chunk();
+#pragma unroll
+                for (int p = 0; p < TV::NP; ++p)
+                    if (TV::live(vrow, p)) lds_store16(lV + (vrow + p * TV::RP) * F::LDV + vseg * 8, lv[par][p]);
+            }
+            if (c + 2 < nchunks) lissue(c + 2, parc);
             __syncthreads();
 #pragma unroll
             for (int x = 0; x < F::NKB; ++x) R[x] *= gC;
@@ -378,6 +419,10 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT>::OCC)) void chunk_fuse
 #pragma unroll
                 for (int x = 0; x < F::NKB; ++x) mfma(R[x], frag_tr(lK, F::LDK, 32 * f, x * 16, tro_k), fb);
             }
+        };
+        for (int c = 0; c < nchunks; c += 2) {
+            lchunk(c, std::integral_constant<int, 0>{});
+            if (c + 1 < nchunks) lchunk(c + 1, std::integral_constant<int, 1>{});
         }
         __syncthreads();  // the local tiles are dead before the full pass reuses the LDS
         if (!boundary) {  // publish the aggregate for the later segments of the group (nothing else in flight)
@@ -395,7 +440,10 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT>::OCC)) void chunk_fuse
     const int qrow = tid / TQ::SPR, qseg = tid % TQ::SPR;
     const int qoff = (qrow * rsk + qseg * 8) * 2;
     const int tro_q = trp_lane_offset(F::LDQ, lane);
-    constexpr int NBUF = C <= 64 && DK <= 64 ? 2 : 1;  // register buffers of staged loads
+    // Two register buffers of staged loads: stage i+2's loads go out as soon as stage i is staged. Stage
+    // parity is the chunk's with one d_k slice, the slice's with an even number of slices.
+    constexpr int NBUF = 2;
+    static_assert(F::NSL == 1 || F::NSL % 2 == 0, "stage parity");
     u32x4_t bq[NBUF][TQ::NP], bk[NBUF][TQ::NP], bv[NBUF][TV::NP];
     auto issue = [&](int i, auto parc) __attribute__((always_inline)) {
         constexpr int par = decltype(parc)::value;
@@ -517,11 +565,16 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT>::OCC)) void chunk_fuse
     }
 #pragma unroll
     for (int p = 0; p < TQ::NP; ++p) zfull[p] = gpow(lg, (float)(C - 1 - (qrow + p * TQ::RP)));
+    float zvfull[TV::NP];  // zeta of the staged V rows of a full chunk (pre-rotated operands)
+#pragma unroll
+    for (int p = 0; p < TV::NP; ++p) zvfull[p] = gpow(lg, (float)(C - 1 - (vrow + p * TV::RP)));
     const float gC = gpow(lg, (float)C);
     // Without rotation theta is all zero and every factor is exactly (1, 0).
     SliceRot<C, TQ::RP, TQ::NP> rot[F::NSL];
+    if constexpr (!PRE) {
 #pragma unroll
-    for (int sl = 0; sl < F::NSL; ++sl) rot[sl].init_steps(a.theta, (sl * F::KS + qseg * 8) / 2);
+        for (int sl = 0; sl < F::NSL; ++sl) rot[sl].init_steps(a.theta, (sl * F::KS + qseg * 8) / 2);
+    }
 
     auto commit = [&](int i, auto parc, auto slc) __attribute__((always_inline)) {
         constexpr int par = decltype(parc)::value, sl = decltype(slc)::value;
@@ -529,33 +582,59 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT>::OCC)) void chunk_fuse
         const int L = min(C, seg_n - c * C);
         uint16_t* sQ = stage_lds + (i & 1) * F::STAGE;
         uint16_t* sK = sQ + F::SQ;
-        uint16_t* sKz = sK + F::SQ;
-        uint16_t* sV = v_lds + (F::NVB == 2 ? (c & 1) * F::SV : 0);
-        if ((c & 7) == 0)  // exact factors every 8 chunks; angle addition in between
-            rot[sl].cur.eval(a.pos0 + seg_t0 + (long long)c * C + qrow, a.theta, (sl * F::KS + qseg * 8) / 2);
+        uint16_t* sV = v_lds + (F::NVB == 2 ? (c & 1) * F::VBUF : 0);
+        if constexpr (PRE) {
+            // rows as staged; V also scaled by zeta into sVz
 #pragma unroll
-        for (int p = 0; p < TQ::NP; ++p) {
-            const int r = qrow + p * TQ::RP;
-            if (TQ::live(qrow, p)) {
-                float qf[8], kf[8];
-                unpack8(bq[par][p], qf);
-                unpack8(bk[par][p], kf);
-                rot[sl].cur.apply(qf);
-                rot[sl].cur.apply(kf);
-                if (p + 1 < TQ::NP) rot[sl].cur.turn(rot[sl].pass);
-                lds_store16(sQ + r * F::LDQ + qseg * 8, pack8(qf));
-                lds_store16(sK + r * F::LDQ + qseg * 8, pack8(kf));
-                const float z = L == C ? zfull[p] : (r < L ? gpow(lg, (float)(L - 1 - r)) : 0.f);
+            for (int p = 0; p < TQ::NP; ++p)
+                if (TQ::live(qrow, p)) {
+                    lds_store16(sQ + (qrow + p * TQ::RP) * F::LDQ + qseg * 8, bq[par][p]);
+                    lds_store16(sK + (qrow + p * TQ::RP) * F::LDQ + qseg * 8, bk[par][p]);
+                }
+            if constexpr (sl == 0) {
+                uint16_t* sVz = sV + F::SV;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) kf[e] *= z;
-                lds_store16(sKz + r * F::LDQ + qseg * 8, pack8(kf));
+                for (int p = 0; p < TV::NP; ++p) {
+                    const int r = vrow + p * TV::RP;
+                    if (TV::live(vrow, p)) {
+                        lds_store16(sV + r * F::LDV + vseg * 8, bv[par][p]);
+                        const float z = L == C ? zvfull[p] : (r < L ? gpow(lg, (float)(L - 1 - r)) : 0.f);
+                        float vf[8];
+                        unpack8(bv[par][p], vf);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) vf[e] *= z;
+                        lds_store16(sVz + r * F::LDV + vseg * 8, pack8(vf));
+                    }
+                }
             }
-        }
-        rot[sl].next_chunk();
-        if constexpr (sl == 0) {
+        } else {
+            uint16_t* sKz = sK + F::SQ;
+            if ((c & 7) == 0)  // exact factors every 8 chunks; angle addition in between
+                rot[sl].cur.eval(a.pos0 + seg_t0 + (long long)c * C + qrow, a.theta, (sl * F::KS + qseg * 8) / 2);
 #pragma unroll
-            for (int p = 0; p < TV::NP; ++p)
-                if (TV::live(vrow, p)) lds_store16(sV + (vrow + p * TV::RP) * F::LDV + vseg * 8, bv[par][p]);
+            for (int p = 0; p < TQ::NP; ++p) {
+                const int r = qrow + p * TQ::RP;
+                if (TQ::live(qrow, p)) {
+                    float qf[8], kf[8];
+                    unpack8(bq[par][p], qf);
+                    unpack8(bk[par][p], kf);
+                    rot[sl].cur.apply(qf);
+                    rot[sl].cur.apply(kf);
+                    if (p + 1 < TQ::NP) rot[sl].cur.turn(rot[sl].pass);
+                    lds_store16(sQ + r * F::LDQ + qseg * 8, pack8(qf));
+                    lds_store16(sK + r * F::LDQ + qseg * 8, pack8(kf));
+                    const float z = L == C ? zfull[p] : (r < L ? gpow(lg, (float)(L - 1 - r)) : 0.f);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) kf[e] *= z;
+                    lds_store16(sKz + r * F::LDQ + qseg * 8, pack8(kf));
+                }
+            }
+            rot[sl].next_chunk();
+            if constexpr (sl == 0) {
+#pragma unroll
+                for (int p = 0; p < TV::NP; ++p)
+                    if (TV::live(vrow, p)) lds_store16(sV + (vrow + p * TV::RP) * F::LDV + vseg * 8, bv[par][p]);
+            }
         }
     };
 
@@ -588,13 +667,15 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT>::OCC)) void chunk_fuse
     // tiles: every wave needs all of P), the cross term O^T += R_s^T Q_s^T with R^T taken from the state
     // accumulators (the previous chunk's state: this slice's update follows), and R_s <- gamma^L R_s +
     // (K_s (.) zeta)^T V.
-    auto mma = [&](int i, auto slc, f32x4_t* S, f32x4_t* O, bf16x8_t* fv, float gL) __attribute__((always_inline)) {
+    auto mma = [&](int i, auto slc, f32x4_t* S, f32x4_t* O, bf16x8_t* fv, bf16x8_t* fvz, float gL)
+                   __attribute__((always_inline)) {
         constexpr int sl = decltype(slc)::value;
         const int c = i / F::NSL;
         const uint16_t* sQ = stage_lds + (i & 1) * F::STAGE;
         const uint16_t* sK = sQ + F::SQ;
-        const uint16_t* sKz = sK + F::SQ;
-        const uint16_t* sV = v_lds + (F::NVB == 2 ? (c & 1) * F::SV : 0);
+        // state update operands: (K (.) zeta)^T V, or with pre-rotated operands K^T (V (.) zeta)
+        const uint16_t* sKA = PRE ? sK : sK + F::SQ;
+        const uint16_t* sV = v_lds + (F::NVB == 2 ? (c & 1) * F::VBUF : 0);
 #pragma unroll
         for (int kk = 0; kk < F::KS; kk += 32) {
             bf16x8_t qf[F::NB], kf[F::NB];
@@ -621,7 +702,10 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT>::OCC)) void chunk_fuse
         }
         if constexpr (sl == 0) {
 #pragma unroll
-            for (int f = 0; f < KF; ++f) fv[f] = frag_trp(sV, F::LDV, 32 * f, w * 16, tro_vp);
+            for (int f = 0; f < KF; ++f) {
+                fv[f] = frag_trp(sV, F::LDV, 32 * f, w * 16, tro_vp);
+                if constexpr (PRE) fvz[f] = frag_trp(sV + F::SV, F::LDV, 32 * f, w * 16, tro_vp);
+            }
         }
 #pragma unroll
         for (int x = sl * F::XB; x < (sl + 1) * F::XB; ++x) R[x] *= gL;
@@ -629,7 +713,7 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT>::OCC)) void chunk_fuse
         for (int f = 0; f < KF; ++f) {
 #pragma unroll
             for (int x = sl * F::XB; x < (sl + 1) * F::XB; ++x)
-                mfma(R[x], frag_trp(sKz, F::LDQ, 32 * f, (x - sl * F::XB) * 16, tro_q), fv[f]);
+                mfma(R[x], frag_trp(sKA, F::LDQ, 32 * f, (x - sl * F::XB) * 16, tro_q), PRE ? fvz[f] : fv[f]);
         }
     };
 
@@ -654,14 +738,15 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT>::OCC)) void chunk_fuse
         for (int x = 0; x < NSA; ++x) S[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int x = 0; x < F::NB; ++x) O[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        bf16x8_t fv[KF];  // V^T operand of d_v block w (B of the state update, A of the P.V product)
+        bf16x8_t fv[KF];   // V^T operand of d_v block w (A of the P.V product; B of the state update unless PRE)
+        bf16x8_t fvz[KF];  // (V (.) zeta)^T operand: B of the state update with pre-rotated operands
         static_for<0, F::NSL>([&](auto slc) __attribute__((always_inline)) {
             constexpr int sl = decltype(slc)::value;
             constexpr int sln = (sl + 1) % F::NSL;  // slice of the next stage
             // register buffer of the next stage (stage parity is chunk parity when NBUF = 2: NSL = 1 then)
-            constexpr int parn = NBUF == 2 ? 1 - cpar : 0;
+            constexpr int parn = F::NSL == 1 ? 1 - cpar : (sl + 1) & 1;
             const int i = c * F::NSL + sl;
-            mma(i, slc, S, O, fv, gL);
+            mma(i, slc, S, O, fv, fvz, gL);
             if (i + 1 < nst) {
                 commit(i + 1, std::integral_constant<int, parn>{}, std::integral_constant<int, sln>{});
                 if (i + 1 + NBUF < nst) issue(i + 1 + NBUF, std::integral_constant<int, parn>{});
@@ -725,7 +810,8 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT>::OCC)) void chunk_fuse
 // chunk size (up to rounding), and 64-token tiles keep all of P in registers.
 template <int DK, int C>
 ChunkKernels chunk_entry_bf16() {
-    return {nullptr, nullptr, chunk_fused_bf16<DK, (C > 64 ? 64 : C), 64>, 64};
+    constexpr int CI = C > 64 ? 64 : C;
+    return {nullptr, nullptr, chunk_fused_bf16<DK, CI, 64, false>, chunk_fused_bf16<DK, CI, 64, true>, 64};
 }
 
 }  // namespace ret

@@ -17,6 +17,8 @@ struct FwdArgs {
     const float* state_in;   // [B,H,dk,dv] or null
     float* state_out;        // [B,H,dk,dv] or null
     float* ws;               // [B*H][nseg][dk][dv] segment states (split runs)
+    void* qr;                // rotated copies of q and k (bf16 single-pass kernel with pre-rotated operands)
+    void* kr;
     int B, N, H, dk, dv;
     int nseg;                // segments per sequence
     int seg_len;             // tokens per segment (multiple of the chunk), last segment may be shorter
@@ -847,6 +849,7 @@ typedef void (*step_kernel_t)(StepArgs);
 // one single-pass kernel with the segment chain (fused, non-null).
 struct ChunkKernels {
     fwd_kernel_t full, local, fused;
+    fwd_kernel_t fused_pre;  // single-pass kernel staging pre-rotated q', k' (or unrotated q, k)
     int dvt;
 };
 struct ParKernel {
@@ -856,11 +859,19 @@ struct ParKernel {
 
 template <class E, int DK, int C, int DVT>
 ChunkKernels chunk_entry() {
-    return {chunk_full_kernel<E, DK, C, DVT>, chunk_local_kernel<E, DK, C, DVT>, nullptr, DVT};
+    return {chunk_full_kernel<E, DK, C, DVT>, chunk_local_kernel<E, DK, C, DVT>, nullptr, nullptr, DVT};
 }
 
 // Getters, one per kernel-group source. Return false when the shape has no instance.
 fwd_kernel_t segment_scan_get();
+// q' and k' (bf16): q and k rotated by their absolute positions, into a.qr / a.kr; rotate_qk_blocks() 256-thread
+// workgroups.
+fwd_kernel_t rotate_qk_get();
+constexpr int kRotTokens = 16;  // consecutive tokens per thread of the rotation kernel
+inline unsigned rotate_qk_blocks(int B, int N, int H, int dk) {
+    const long long threads = (long long)B * ((N + kRotTokens - 1) / kRotTokens) * (H * dk / 8);
+    return (unsigned)((threads + 255) / 256);
+}
 bool chunk_kernels_f32(int dk, int dv, int C, ChunkKernels* out);
 bool chunk_kernels_bf16_small(int dk, int dv, int C, ChunkKernels* out);   // d_k in {32, 64}
 bool chunk_kernels_bf16_128(int dk, int dv, int C, ChunkKernels* out);     // d_k = 128

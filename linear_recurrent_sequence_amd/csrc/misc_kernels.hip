@@ -37,6 +37,54 @@ __global__ __launch_bounds__(kThreads) void segment_scan_kernel(FwdArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------------------------------
+// rotate_qk: q' = rotated q, k' = rotated k (bf16 in, bf16 out), the rotation the chunk kernels otherwise
+// apply while staging. Written once when a call stages the same rows for several d_v tiles. Thread: one
+// 16-byte segment (8 dims, 4 pairs) of one (b, h) row over kRotTokens consecutive tokens; the factors of the
+// first token are evaluated exactly, later ones by angle addition with the one-token step.
+// ---------------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void rotate_qk_kernel(FwdArgs a) {
+    const int segs = a.H * a.dk / 8;  // segments of one token's row over all heads
+    const int nblk = (a.N + kRotTokens - 1) / kRotTokens;
+    const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (gid >= (long long)a.B * nblk * segs) return;
+    const int r = (int)(gid % segs);
+    const long long bt = gid / segs;
+    const int b = (int)(bt / nblk), n0 = (int)(bt % nblk) * kRotTokens;
+    const int h = r / (a.dk / 8), pair0 = (r % (a.dk / 8)) * 4;
+    float c[4], s[4], dc[4], ds[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        rot_cs(a.pos0 + n0, a.theta[pair0 + j], &c[j], &s[j]);
+        rot_cs(1, a.theta[pair0 + j], &dc[j], &ds[j]);
+    }
+    const long long row = (long long)a.H * a.dk;  // elements between tokens
+    const long long base = (((long long)b * a.N + n0) * a.H + h) * a.dk + pair0 * 2;
+    const int nt = min(kRotTokens, a.N - n0);
+    for (int i = 0; i < nt; ++i) {
+        const uint4 uq = *reinterpret_cast<const uint4*>((const uint16_t*)a.q + base + i * row);
+        const uint4 uk = *reinterpret_cast<const uint4*>((const uint16_t*)a.k + base + i * row);
+        float fq[8], fk[8];
+        unpack8_bf16(uq, fq);
+        unpack8_bf16(uk, fk);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float q0 = fq[2 * j], q1 = fq[2 * j + 1], k0 = fk[2 * j], k1 = fk[2 * j + 1];
+            fq[2 * j] = q0 * c[j] - q1 * s[j];
+            fq[2 * j + 1] = q0 * s[j] + q1 * c[j];
+            fk[2 * j] = k0 * c[j] - k1 * s[j];
+            fk[2 * j + 1] = k0 * s[j] + k1 * c[j];
+            const float nc = c[j] * dc[j] - s[j] * ds[j];
+            s[j] = s[j] * dc[j] + c[j] * ds[j];
+            c[j] = nc;
+        }
+        *reinterpret_cast<uint4*>((uint16_t*)a.qr + base + i * row) = pack8_bf16(fq);
+        *reinterpret_cast<uint4*>((uint16_t*)a.kr + base + i * row) = pack8_bf16(fk);
+    }
+}
+
+fwd_kernel_t rotate_qk_get() { return rotate_qk_kernel; }
+
 bool parallel_kernel_get(bool bf16_in, int dk, int dv, ParKernel* out) {
     if (!bf16_in) {
         if (dv % 16) return false;

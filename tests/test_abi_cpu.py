@@ -83,6 +83,11 @@ def test_workspace_query(lib):
     # fp32 input runs the split kernels: the header, then one d_k x d_v state per (b, h, segment)
     n_f32 = lib.ret_chunkwise_workspace_bytes(1, 4096, 2, 64, 64, 64, 0)
     assert n_f32 > 256 and (n_f32 - 256) % (2 * 64 * 64 * 4) == 0
+    # 8 d_v tiles of 64 per head: q and k are rotated once into the workspace (two bf16 copies) beside the
+    # segment chain
+    n_wide = lib.ret_chunkwise_workspace_bytes(1, 8192, 16, 256, 512, 128, 1)
+    rot = 2 * 1 * 8192 * 16 * 256 * 2
+    assert n_wide > rot and (n_wide - rot) % 256 == 0
     assert lib.ret_chunkwise_workspace_bytes(128, 512, 8, 64, 64, 64, 1) == 0
     assert lib.ret_chunkwise_workspace_bytes(1, 64, 8, 48, 64, 64, 1) == 0  # unsupported shape: 0
 

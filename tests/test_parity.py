@@ -87,6 +87,8 @@ SMALL = [
     ("bf16", 3, 1, 2, 64, 64, 64, True, 9, True, None),      # one token
     ("bf16", 1, 45, 2, 64, 64, 64, False, 0, False, None),   # shorter than one chunk
     ("bf16", 1, 1100, 1, 64, 64, 64, True, 7, False, 1),     # 18 chunks in one segment
+    ("bf16", 2, 300, 2, 64, 256, 64, True, 3, True, 3),      # 4 d_v tiles: q, k rotated once up front
+    ("bf16", 1, 333, 1, 256, 512, 128, True, 0, True, 2),    # 8 d_v tiles, d_k 256
 ]
 
 
@@ -109,6 +111,26 @@ def test_chunkwise_small(R, case, monkeypatch):
     eo, es = rel_err(o, o_ref), rel_err(s, s_ref)
     print("  err o=%.3g state=%.3g" % (eo, es))
     assert eo <= tol(dt) and es <= tol(dt), (eo, es)
+
+
+def test_chunkwise_wide_dv_without_workspace(R):
+    """Without a workspace a call runs one segment per (b, h) and rotates q and k while staging, also where a
+    full workspace would hold rotated copies (8 d_v tiles)."""
+    B, N, H, dk, dv, C = 1, 200, 2, 128, 512, 64
+    print_case("wide_dv_no_workspace", (B, N, H, dk, dv, C))
+    rng = np.random.default_rng(31)
+    q = W.normal(rng, (B, N, H, dk), 8.0, "bf16")
+    k = W.normal(rng, (B, N, H, dk), 8.0, "bf16")
+    v = W.normal(rng, (B, N, H, dv), 8.0, "bf16")
+    gamma, theta = W.gamma_schedule(H), W.theta_schedule(dk)
+    o_ref, s_ref = oracle.chunkwise(q, k, v, gamma, C, theta=theta, pos0=17)
+    import torch
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    o = empty_out((B, N, H, dv), "bf16")
+    sout = torch.empty((B, H, dk, dv), dtype=torch.float32, device="cuda")
+    R.ret_chunkwise_fwd(qd, kd, vd, o, gamma, C, theta=theta, pos0=17, state_out=sout, workspace=None)
+    torch.cuda.synchronize()
+    assert rel_err(to_host(o), o_ref) <= tol("bf16") and rel_err(to_host(sout), s_ref) <= tol("bf16")
 
 
 def test_chunkwise_workspace_reuse_and_repeatability(R, monkeypatch):
