@@ -75,12 +75,17 @@ ret_status_t ret_parallel_fwd(const void* q, const void* k, const void* v, void*
                               const double* theta, int64_t pos0, void* stream);
 
 /*
- * Workspace (device bytes) that ret_chunkwise_fwd uses to split each sequence into segments that run in
- * parallel: the end state of each segment is passed to the next (a scan of the chunk state over segments).
- * 0 means the call runs one segment per (b, h) and needs none. Passing a smaller workspace than this is
- * allowed: the call then uses fewer segments. The workspace must be zero-filled before its first use; every
- * call leaves it in a state the next call accepts (its first 256 bytes zero except a sticky error word).
- * Calls sharing a workspace must not overlap in time (on one stream they do not).
+ * Workspace (device bytes) that ret_chunkwise_fwd can use, for the given shape and input dtype:
+ *  - segment states: each sequence is split into segments that run in parallel, and the state entering a
+ *    segment is built from the end states of the segments before it (a scan of the chunk state over
+ *    segments; BF16 input: counters, flags and two d_k x 64 fp32 slots per segment and d_v tile of 64);
+ *  - BF16 input with rotation and d_v >= 256: bf16 copies of q and k rotated once (2 * B*N*H*d_k*2 bytes),
+ *    so the d_v tiles of a head do not each rotate the same rows.
+ * 0 means the call runs one segment per (b, h) and needs none. A smaller workspace is allowed: the call then
+ * first drops the rotated copies, then uses fewer segments; the results are the same up to rounding order.
+ * The workspace must be zero-filled before its first use. Every call leaves it in a state the next call
+ * accepts: the header (first 256 bytes) zero except a sticky error word, counters and flags zero. Calls
+ * sharing a workspace must not overlap in time (on one stream they do not). The library never frees it.
  */
 size_t ret_chunkwise_workspace_bytes(int B, int N, int H, int dk, int dv, int chunk, ret_dtype_t in_dt);
 
@@ -101,7 +106,10 @@ ret_status_t ret_chunkwise_check(const void* workspace, void* stream);
  * ret_recurrent_step. Results equal the recurrent and parallel forms up to rounding.
  * workspace: device memory of `workspace_bytes` (see ret_chunkwise_workspace_bytes), or NULL with 0.
  * Supported: F32 input: d_k in {16, 32, 64}, d_v a multiple of 16, chunk in {16, 32, 64}. BF16 input:
- * d_k in {32, 64, 128, 256}, d_v a multiple of 64, chunk in {32, 64, 128}. N >= 1.
+ * d_k in {32, 64, 128, 256}, d_v a multiple of 64, chunk in {32, 64, 128}. N >= 1. BF16 chunks of 128
+ * are computed as pairs of 64-token chunks, which the chunkwise form allows (any chunk size gives the same
+ * result up to rounding). Kernels that read a chunk address it with 32-bit offsets: chunk * H * max(d_k, d_v)
+ * * 4 must stay below 2^31 (RET_ERR_UNSUPPORTED otherwise).
  */
 ret_status_t ret_chunkwise_fwd(const void* q, const void* k, const void* v, void* o, int B, int N, int H, int dk,
                                int dv, ret_dtype_t in_dt, ret_dtype_t out_dt, const float* gamma,
@@ -122,9 +130,9 @@ ret_status_t ret_recurrent_step(const void* q, const void* k, const void* v, voi
  * Kernel timing for measurement tools. While enabled, every kernel the library launches is bracketed by a
  * pair of HIP events on the launch stream. ret_timing_query synchronises those events and returns the total
  * milliseconds and launch count recorded for kernels whose name equals `kernel` ("" or NULL = all).
- * ret_timing_reset drops the records. Kernel names: "ret_chunk_fused" (bf16 input), "ret_chunk_full",
- * "ret_chunk_local", "ret_segment_scan" (fp32 input), "ret_parallel", "ret_recurrent_step". Not for use while kernels are being captured
- * into a graph.
+ * ret_timing_reset drops the records. Kernel names: "ret_chunk_fused" and "ret_rotate_qk" (bf16 input),
+ * "ret_chunk_full", "ret_chunk_local", "ret_segment_scan" (fp32 input), "ret_parallel", "ret_recurrent_step".
+ * Not for use while kernels are being captured into a graph.
  */
 int ret_timing_enable(int on);
 int ret_timing_query(const char* kernel, double* total_ms, int64_t* launches);
