@@ -103,7 +103,8 @@ def bench_chunkwise(R, W, torch, wid, steps, warmup):
     R.timing_enable(False)
     ms_step = e0.elapsed_time(e1) / steps
     kernels = {}
-    for name in ("ret_rotate_qk", "ret_chunk_fused", "ret_chunk_local", "ret_segment_scan", "ret_chunk_full"):
+    for name in ("ret_rotate_qk", "ret_chunk_seg", "ret_chunk_fused", "ret_chunk_local", "ret_segment_scan",
+                 "ret_chunk_full"):
         tot, n = R.timing_query(name)
         if n:
             kernels[name] = {"avg_us": 1e3 * tot / n, "launches": n}

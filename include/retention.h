@@ -130,9 +130,9 @@ ret_status_t ret_recurrent_step(const void* q, const void* k, const void* v, voi
  * Kernel timing for measurement tools. While enabled, every kernel the library launches is bracketed by a
  * pair of HIP events on the launch stream. ret_timing_query synchronises those events and returns the total
  * milliseconds and launch count recorded for kernels whose name equals `kernel` ("" or NULL = all).
- * ret_timing_reset drops the records. Kernel names: "ret_chunk_fused" and "ret_rotate_qk" (bf16 input),
- * "ret_chunk_full", "ret_chunk_local", "ret_segment_scan" (fp32 input), "ret_parallel", "ret_recurrent_step".
- * Not for use while kernels are being captured into a graph.
+ * ret_timing_reset drops the records. Kernel names: "ret_chunk_seg", "ret_chunk_fused" and "ret_rotate_qk"
+ * (bf16 input), "ret_chunk_full", "ret_chunk_local", "ret_segment_scan" (fp32 input), "ret_parallel",
+ * "ret_recurrent_step". Not for use while kernels are being captured into a graph.
  */
 int ret_timing_enable(int on);
 int ret_timing_query(const char* kernel, double* total_ms, int64_t* launches);

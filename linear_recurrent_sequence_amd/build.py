@@ -19,6 +19,9 @@ COMMON = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
     # packed fp32 ops stay off: hipcc -O3 would otherwise form them from plain float code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the kernels' atomics are issued by one lane on purpose; the atomic optimizer would turn each into a
+    # wave-level scan whose result is needed at once, which puts a wait for every earlier load right behind it
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall", "-Wno-unused-function", "-Wno-unused-result",
 ]
 NOISE = "'-packed-fp32-ops' is not a recognized feature"

@@ -56,13 +56,13 @@ struct LaunchTimer {
             on = g_timing_on;
         }
         if (on && hipEventCreate(&start) == hipSuccess && hipEventCreate(&stop) == hipSuccess)
-            hipEventRecord(start, stream);
+            (void)hipEventRecord(start, stream);
         else
             on = false;
     }
     void done() {
         if (!on) return;
-        hipEventRecord(stop, stream);
+        (void)hipEventRecord(stop, stream);
         std::lock_guard<std::mutex> lk(g_timing_mu);
         g_timing.push_back({name, start, stop});
     }
@@ -284,15 +284,19 @@ ret_status_t ret_chunkwise_fwd(const void* q, const void* k, const void* v, void
     hipStream_t s = (hipStream_t)stream;
     const int ntiles = dv / ck.dvt;
     if (ck.fused) {
+        // Segments short enough to stay on chip take the on-chip variant (RET_SEG_ONCHIP=0 turns it off).
+        const bool onchip = nseg > 1 && ck.seg && seg_len <= ck.seg_tokens && env_int("RET_SEG_ONCHIP", 1) != 0;
         // Staging copies rows instead of rotating them when there is no rotation, or when q and k are rotated
         // once up front (several d_v tiles stage the same rows).
-        fwd_kernel_t fn = ck.fused;
+        fwd_kernel_t fn = onchip ? ck.seg : ck.fused;
+        const fwd_kernel_t fn_pre = onchip ? ck.seg_pre : ck.fused_pre;
+        const char* name = onchip ? "ret_chunk_seg" : "ret_chunk_fused";
         if (!theta) {
-            fn = ck.fused_pre;
+            fn = fn_pre;
             A.qr = const_cast<void*>(q);
             A.kr = const_cast<void*>(k);
         } else if (plan.rot_bytes > 0) {
-            fn = ck.fused_pre;
+            fn = fn_pre;
             A.qr = (char*)workspace + plan.chain_bytes;
             A.kr = (char*)A.qr + plan.rot_bytes / 2;
             LaunchTimer tr("ret_rotate_qk", s);
@@ -301,10 +305,10 @@ ret_status_t ret_chunkwise_fwd(const void* q, const void* k, const void* v, void
             if ((st = launch_status("ret_rotate_qk")) != RET_OK) return st;
         }
         const unsigned grid = (unsigned)((long long)nseg * B * H * ntiles);
-        LaunchTimer tm("ret_chunk_fused", s);
+        LaunchTimer tm(name, s);
         hipLaunchKernelGGL(fn, dim3(grid), dim3(kThreads), 0, s, A);
         tm.done();
-        return launch_status("ret_chunk_fused");
+        return launch_status(name);
     }
     if (nseg > 1) {
         {
@@ -406,8 +410,8 @@ ret_status_t ret_chunkwise_check(const void* workspace, void* stream) {
 void ret_timing_reset(void) {
     std::lock_guard<std::mutex> lk(g_timing_mu);
     for (auto& r : g_timing) {
-        hipEventDestroy(r.start);
-        hipEventDestroy(r.stop);
+        (void)hipEventDestroy(r.start);
+        (void)hipEventDestroy(r.stop);
     }
     g_timing.clear();
 }

@@ -206,6 +206,172 @@ __device__ __forceinline__ void slot_load(const float* slot, f32x4_t* v, int tid
                                                                                   kChainAux));
 }
 
+// The unit (one d_v tile of one (b, h)) of this workgroup, from the launch index. Workgroups are dispatched to
+// the 8 XCDs in turn (launch index mod 8); when the grid divides evenly, the d_v tiles of one (b, h) get launch
+// indices of one residue, so they run on one XCD and its L2 serves the q and k rows they all stage.
+__device__ __forceinline__ int unit_of_block(int ntiles, int units) {
+    const int pairs = units / ntiles;
+    int unit_i;
+    if (ntiles > 1 && gridDim.x % (8u * ntiles) == 0) {
+        const int xcd = blockIdx.x % 8, q8 = blockIdx.x / 8;
+        unit_i = ((q8 / ntiles * 8 + xcd) % pairs) * ntiles + q8 % ntiles;
+    } else {
+        unit_i = blockIdx.x % (unsigned)units;
+    }
+    return __builtin_amdgcn_readfirstlane(unit_i);
+}
+
+// Chain storage of one unit (chained runs).
+struct Chain {
+    int* ctr;      // [2]: next segment ticket, workgroups past the look-back
+    int* flags;    // [nseg]: nonzero once the segment's aggregate (or, for a group's last segment, the prefix
+                   // leaving the group) is published
+    float* agg;    // [nseg][slot]: aggregates
+    float* inc;    // [nseg][slot]: prefixes leaving a group (published by its last segment)
+    int* error;    // sticky error word of the header
+    int slot;      // floats per state slot
+};
+__device__ __forceinline__ Chain chain_of(void* ws, int units, int nseg, int unit, int slot_floats) {
+    const ChainLayout lay = chain_layout(units, nseg, slot_floats);
+    char* base = reinterpret_cast<char*>(ws);
+    Chain ch;
+    ch.ctr = reinterpret_cast<int*>(base + lay.ctr_off) + 2 * unit;
+    ch.flags = reinterpret_cast<int*>(base + lay.flags_off) + (size_t)unit * nseg;
+    ch.agg = reinterpret_cast<float*>(base + lay.agg_off) + (size_t)unit * nseg * slot_floats;
+    ch.inc = reinterpret_cast<float*>(base + lay.inc_off) + (size_t)unit * nseg * slot_floats;
+    ch.error = &reinterpret_cast<ChainHeader*>(ws)->error;
+    ch.slot = slot_floats;
+    return ch;
+}
+
+// The unit's next segment: a ticket from the unit's counter, broadcast through the shared word `bc`, so the
+// workgroups that own a unit's earlier segments have all started.
+__device__ __forceinline__ int chain_ticket(const Chain& ch, int& bc) {
+    if (threadIdx.x == 0) bc = __hip_atomic_fetch_add(ch.ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int seg = __builtin_amdgcn_readfirstlane(bc);
+    __syncthreads();
+    return seg;
+}
+
+// s_waitcnt immediate that waits until at most n vector memory operations of the wave are outstanding (and
+// for nothing else). Those complete in the order they were issued, so this waits for all but the n latest.
+__host__ __device__ constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) & 3) << 14 | 7 << 4 | 15 << 8; }
+
+// Publishes segment seg's aggregate R (not for a group's last segment, whose flag announces the prefix).
+// `then` may issue NTHEN vector memory operations per thread (loads the caller wants in flight early): they go
+// out after the slot stores, and the wait before the flag covers the stores only. The flag store itself is
+// not waited for here; the workgroup's count (chain_enter or chain_finish) waits for it first.
+template <int NKB, int NTHEN, class Then>
+__device__ __forceinline__ void chain_publish(const Chain& ch, int seg, const f32x4_t* R, Then&& then) {
+    slot_store<NKB>(ch.agg + (size_t)seg * ch.slot, R, threadIdx.x);
+    __asm__ volatile("" ::: "memory");  // `then` stays behind the stores
+    then();
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(NTHEN));
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_store(ch.flags + seg, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <int NKB>
+__device__ __forceinline__ void chain_publish(const Chain& ch, int seg, const f32x4_t* R) {
+    chain_publish<NKB, 0>(ch, seg, R, [] {});
+}
+
+// R_in of segment seg: the sum over the group's earlier segments j of gamma^((seg-1-j)T) A_j, plus
+// gamma^((seg-g0)T) times the prefix entering the group (published by the previous group's last segment).
+// One poll covers every flag; slots are read in batches and added in a fixed order, so results do not depend
+// on timing. A group's last segment (not the sequence's) then publishes gamma^T R_in + A_seg, A_seg = Rown.
+// With COUNT, the workgroup then counts itself past the look-back and the unit's last one resets the unit's
+// counters and flags (its other workgroups have read them all by then); without, chain_finish does that at
+// the end of the kernel. `bc` is a shared broadcast word.
+template <int NKB, bool COUNT>
+__device__ __forceinline__ void chain_enter(const Chain& ch, int seg, int nseg, float gT, const f32x4_t* Rown,
+                                            f32x4_t* Rin, int& bc) {
+    const int tid = threadIdx.x;
+    const int g0 = seg / kChainGroup * kChainGroup;              // first segment of this segment's group
+    const bool boundary = seg % kChainGroup == kChainGroup - 1;  // publishes the prefix for the next group
+    const bool last = seg == nseg - 1;
+#pragma unroll
+    for (int x = 0; x < NKB; ++x) Rin[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (seg > 0) {
+        const int lo = g0 > 0 ? g0 - 1 : g0;
+        // (wave-uniform: the wait's result is a ballot; on give-up the sum stays partial)
+        const bool ok = __builtin_amdgcn_readfirstlane((int)chain_wait(ch.flags, lo, seg - lo, ch.error)) != 0;
+        constexpr int LB = NKB >= 16 ? 1 : NKB >= 8 ? 2 : 4;
+        float dec = 1.f;
+        for (int j0 = seg - 1; ok && j0 >= g0; j0 -= LB) {
+            f32x4_t v[LB][NKB];
+#pragma unroll
+            for (int i = 0; i < LB; ++i)
+                if (j0 - i >= g0) slot_load<NKB>(ch.agg + (size_t)(j0 - i) * ch.slot, v[i], tid);
+#pragma unroll
+            for (int i = 0; i < LB; ++i)
+                if (j0 - i >= g0) {
+#pragma unroll
+                    for (int x = 0; x < NKB; ++x) Rin[x] += dec * v[i][x];
+                    dec *= gT;
+                }
+        }
+        if (g0 > 0 && ok) {
+            f32x4_t v[NKB];
+            slot_load<NKB>(ch.inc + (size_t)(g0 - 1) * ch.slot, v, tid);
+#pragma unroll
+            for (int x = 0; x < NKB; ++x) Rin[x] += dec * v[x];
+        }
+    }
+    if (!last && boundary) {  // the prefix leaving the group: R_in of the next segment
+        f32x4_t I[NKB];
+#pragma unroll
+        for (int x = 0; x < NKB; ++x) I[x] = gT * Rin[x] + Rown[x];
+        slot_store<NKB>(ch.inc + (size_t)seg * ch.slot, I, tid);
+        __builtin_amdgcn_s_waitcnt(0);
+    }
+    __syncthreads();
+    if (tid == 0 && !last && boundary) __hip_atomic_store(ch.flags + seg, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if constexpr (COUNT) {
+        if (tid == 0) {
+            __builtin_amdgcn_s_waitcnt(0);  // this workgroup's flag stores land before it counts
+            bc = __hip_atomic_fetch_add(ch.ctr + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        if (__builtin_amdgcn_readfirstlane(bc) == nseg - 1) {
+            for (int i = tid; i < nseg; i += kThreads)
+                __hip_atomic_store(ch.flags + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (tid == 0) {
+                __hip_atomic_store(ch.ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(ch.ctr + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
+}
+
+// At the end of the kernel: the workgroup counts itself finished, and the unit's last one resets the unit's
+// counters and flags (the others are finished, so past every read of them). Counting only here keeps the
+// counter's round trip off the path to the outputs where loads are in flight at the look-back: a vector
+// atomic's result also waits for every load the wave issued before it. The unit's storage is located afresh from the workspace, so nothing stays live across
+// the kernel for it. `bc` is a shared broadcast word.
+__device__ __forceinline__ void chain_finish(const FwdArgs& a, int dvt, int slot_floats, int& bc) {
+    const int ntiles = __builtin_amdgcn_readfirstlane(a.dv / dvt);
+    const int units = __builtin_amdgcn_readfirstlane(a.B * a.H * ntiles);
+    const int nseg = __builtin_amdgcn_readfirstlane(a.nseg);
+    const Chain ch = chain_of(a.ws, units, nseg, unit_of_block(ntiles, units), slot_floats);
+    const int tid = threadIdx.x;
+    __syncthreads();
+    if (tid == 0) {
+        __builtin_amdgcn_s_waitcnt(0);  // this workgroup's flag stores land before it counts
+        bc = __hip_atomic_fetch_add(ch.ctr + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (__builtin_amdgcn_readfirstlane(bc) == nseg - 1) {
+        for (int i = tid; i < nseg; i += kThreads)
+            __hip_atomic_store(ch.flags + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tid == 0) {
+            __hip_atomic_store(ch.ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(ch.ctr + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------------------------------
 // chunk_fused (bf16): one workgroup per (segment, d_v tile of 64, b*H + h). Wave w owns d_v block w of every
 // output and state tile. With several segments the workgroup first runs the local pass over its segment
@@ -273,32 +439,16 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT, PRE>::OCC)) void chunk
     const int ntiles = __builtin_amdgcn_readfirstlane(a.dv / DVT);
     const int units = __builtin_amdgcn_readfirstlane(a.B * a.H * ntiles);
     const bool chained = a.nseg > 1;
-    ChainHeader* hdr = reinterpret_cast<ChainHeader*>(a.ws);
-    // The unit comes from the launch index; with several segments the segment is the unit's next ticket, so
-    // the workgroups that own a unit's earlier segments have all started. Workgroups are dispatched to the 8
-    // XCDs in turn (launch index mod 8); when the grid divides evenly, the d_v tiles of one (b, h) get launch
-    // indices of one residue, so they run on one XCD and its L2 serves the q and k rows they all stage.
-    const int pairs = units / ntiles;
-    int unit_i;
-    if (ntiles > 1 && gridDim.x % (8u * ntiles) == 0) {
-        const int xcd = blockIdx.x % 8, q8 = blockIdx.x / 8;
-        unit_i = ((q8 / ntiles * 8 + xcd) % pairs) * ntiles + q8 % ntiles;
-    } else {
-        unit_i = blockIdx.x % (unsigned)units;
-    }
-    const int unit = __builtin_amdgcn_readfirstlane(unit_i);
+    // The unit comes from the launch index; with several segments the segment is the unit's next ticket.
+    const int unit = unit_of_block(ntiles, units);
     int seg = __builtin_amdgcn_readfirstlane((int)(blockIdx.x / (unsigned)units));
-    int* ctr = nullptr;
+    Chain ch{};
     if (chained) {
-        ctr = reinterpret_cast<int*>(reinterpret_cast<char*>(a.ws) + chain_layout(units, a.nseg, DK * DVT).ctr_off) +
-              2 * unit;
-        if (tid == 0) s_word = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __syncthreads();
-        seg = __builtin_amdgcn_readfirstlane(s_word);
-        __syncthreads();
+        ch = chain_of(a.ws, units, a.nseg, unit, DK * DVT);
+        seg = chain_ticket(ch, s_word);
     }
     // Scalar arguments re-read as wave-uniform values: they are live across the divergent ticket branch.
-    const int aB = __builtin_amdgcn_readfirstlane(a.B), aN = __builtin_amdgcn_readfirstlane(a.N);
+    const int aN = __builtin_amdgcn_readfirstlane(a.N);
     const int aH = __builtin_amdgcn_readfirstlane(a.H), adk = __builtin_amdgcn_readfirstlane(a.dk);
     const int adv = __builtin_amdgcn_readfirstlane(a.dv), anseg = __builtin_amdgcn_readfirstlane(a.nseg);
     const int aseg_len = __builtin_amdgcn_readfirstlane(a.seg_len);
@@ -335,15 +485,8 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT, PRE>::OCC)) void chunk
     for (int x = 0; x < F::NKB; ++x) R[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     if (seg == 0 && a.state_in) load_state_in(R);
 
-    // Segment chain storage (chained runs).
     const bool last = seg == anseg - 1;
-    const size_t slot = (size_t)DK * DVT;
-    const ChainLayout lay = chain_layout(units, anseg, (int)slot);
-    int* flags = reinterpret_cast<int*>(reinterpret_cast<char*>(a.ws) + lay.flags_off) + (size_t)unit * anseg;
-    float* agg = reinterpret_cast<float*>(reinterpret_cast<char*>(a.ws) + lay.agg_off) + (size_t)unit * anseg * slot;
-    float* inc = reinterpret_cast<float*>(reinterpret_cast<char*>(a.ws) + lay.inc_off) + (size_t)unit * anseg * slot;
-    const int g0 = seg / kChainGroup * kChainGroup;              // first segment of this segment's group
-    const bool boundary = seg % kChainGroup == kChainGroup - 1;  // publishes the prefix for the next group
+    const bool boundary = seg % kChainGroup == kChainGroup - 1;  // a group's last segment publishes a prefix
 
     // ---- local pass over the segment (chained runs, all segments but the last) ----
     if (chained && !last) {
@@ -425,15 +568,8 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT, PRE>::OCC)) void chunk
             if (c + 1 < nchunks) lchunk(c + 1, std::integral_constant<int, 1>{});
         }
         __syncthreads();  // the local tiles are dead before the full pass reuses the LDS
-        if (!boundary) {  // publish the aggregate for the later segments of the group (nothing else in flight)
-            slot_store<F::NKB>(agg + seg * slot, R, tid);
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-            if (tid == 0) {
-                __hip_atomic_store(flags + seg, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __builtin_amdgcn_s_waitcnt(0);
-            }
-        }
+        // publish the aggregate for the later segments of the group (nothing else in flight)
+        if (!boundary) chain_publish<F::NKB>(ch, seg, R);
     }
 
     // ---- full pass: staging ----
@@ -470,65 +606,8 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT, PRE>::OCC)) void chunk
 
     // ---- entering state: state_in for the first segment, else R_in from the segment chain ----
     if (chained) {
-        const float gT = gpow(lg, (float)aseg_len);
-        // R_in = sum over the group's earlier segments j of gamma^((seg-1-j)T) R_j, plus gamma^((seg-g0)T) times
-        // the prefix entering the group (published by the previous group's last segment). One poll covers
-        // every flag; slots are read in batches of LB and added in a fixed order, so results do not depend
-        // on timing.
         f32x4_t Rin[F::NKB];
-#pragma unroll
-        for (int x = 0; x < F::NKB; ++x) Rin[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        if (seg > 0) {
-            const int lo = g0 > 0 ? g0 - 1 : g0;
-            // (wave-uniform: the wait's result is a ballot; on give-up the sum stays partial)
-            const bool ok = __builtin_amdgcn_readfirstlane((int)chain_wait(flags, lo, seg - lo, &hdr->error)) != 0;
-            constexpr int LB = F::NKB >= 16 ? 1 : F::NKB >= 8 ? 2 : 4;
-            float dec = 1.f;
-            for (int j0 = seg - 1; ok && j0 >= g0; j0 -= LB) {
-                f32x4_t v[LB][F::NKB];
-#pragma unroll
-                for (int i = 0; i < LB; ++i)
-                    if (j0 - i >= g0) slot_load<F::NKB>(agg + (j0 - i) * slot, v[i], tid);
-#pragma unroll
-                for (int i = 0; i < LB; ++i)
-                    if (j0 - i >= g0) {
-#pragma unroll
-                        for (int x = 0; x < F::NKB; ++x) Rin[x] += dec * v[i][x];
-                        dec *= gT;
-                    }
-            }
-            if (g0 > 0 && ok) {
-                f32x4_t v[F::NKB];
-                slot_load<F::NKB>(inc + (g0 - 1) * slot, v, tid);
-#pragma unroll
-                for (int x = 0; x < F::NKB; ++x) Rin[x] += dec * v[x];
-            }
-        }
-        if (!last && boundary) {  // the prefix leaving the group: R_in of the next segment
-            f32x4_t I[F::NKB];
-#pragma unroll
-            for (int x = 0; x < F::NKB; ++x) I[x] = gT * Rin[x] + R[x];
-            slot_store<F::NKB>(inc + seg * slot, I, tid);
-            __builtin_amdgcn_s_waitcnt(0);
-        }
-        __syncthreads();
-        if (tid == 0) {
-            if (!last && boundary) {
-                __hip_atomic_store(flags + seg, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __builtin_amdgcn_s_waitcnt(0);  // the flag lands before this workgroup counts as finished
-            }
-            s_word = __hip_atomic_fetch_add(ctr + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        __syncthreads();
-        // The unit's last workgroup past its look-back finds the unit's others past it too: reset the unit.
-        if (__builtin_amdgcn_readfirstlane(s_word) == anseg - 1) {
-            for (int i = tid; i < anseg; i += kThreads)
-                __hip_atomic_store(flags + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (tid == 0) {
-                __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(ctr + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
+        chain_enter<F::NKB, true>(ch, seg, anseg, gpow(lg, (float)aseg_len), R, Rin, s_word);
 #pragma unroll
         for (int x = 0; x < F::NKB; ++x) R[x] = Rin[x];
         if (seg == 0) {
@@ -811,7 +890,8 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT, PRE>::OCC)) void chunk
 template <int DK, int C>
 ChunkKernels chunk_entry_bf16() {
     constexpr int CI = C > 64 ? 64 : C;
-    return {nullptr, nullptr, chunk_fused_bf16<DK, CI, 64, false>, chunk_fused_bf16<DK, CI, 64, true>, 64};
+    return {nullptr, nullptr, chunk_fused_bf16<DK, CI, 64, false>, chunk_fused_bf16<DK, CI, 64, true>, 64,
+            nullptr, nullptr, 0};
 }
 
 }  // namespace ret

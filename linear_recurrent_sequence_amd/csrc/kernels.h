@@ -851,6 +851,9 @@ struct ChunkKernels {
     fwd_kernel_t full, local, fused;
     fwd_kernel_t fused_pre;  // single-pass kernel staging pre-rotated q', k' (or unrotated q, k)
     int dvt;
+    // single-pass kernels for chained runs whose segments hold at most seg_tokens tokens (0: none)
+    fwd_kernel_t seg, seg_pre;
+    int seg_tokens;
 };
 struct ParKernel {
     fwd_kernel_t fn;
@@ -859,7 +862,7 @@ struct ParKernel {
 
 template <class E, int DK, int C, int DVT>
 ChunkKernels chunk_entry() {
-    return {chunk_full_kernel<E, DK, C, DVT>, chunk_local_kernel<E, DK, C, DVT>, nullptr, nullptr, DVT};
+    return {chunk_full_kernel<E, DK, C, DVT>, chunk_local_kernel<E, DK, C, DVT>, nullptr, nullptr, DVT, nullptr, nullptr, 0};
 }
 
 // Getters, one per kernel-group source. Return false when the shape has no instance.

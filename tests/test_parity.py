@@ -89,6 +89,10 @@ SMALL = [
     ("bf16", 1, 1100, 1, 64, 64, 64, True, 7, False, 1),     # 18 chunks in one segment
     ("bf16", 2, 300, 2, 64, 256, 64, True, 3, True, 3),      # 4 d_v tiles: q, k rotated once up front
     ("bf16", 1, 333, 1, 256, 512, 128, True, 0, True, 2),    # 8 d_v tiles, d_k 256
+    # segments of at most 256 tokens with d_k <= 64 run on chip (the whole segment held in LDS and registers)
+    ("bf16", 2, 1000, 2, 64, 64, 128, False, 0, True, None),  # chunk 128 as two 64s, ragged last segment
+    ("bf16", 1, 2500, 2, 32, 64, 64, True, 0, True, 10),     # 10 segments: two look-back groups
+    ("bf16", 1, 530, 3, 64, 192, 32, True, 2, True, 3),      # chunk 32, 3 d_v tiles, 6 chunks per segment
 ]
 
 
@@ -111,6 +115,26 @@ def test_chunkwise_small(R, case, monkeypatch):
     eo, es = rel_err(o, o_ref), rel_err(s, s_ref)
     print("  err o=%.3g state=%.3g" % (eo, es))
     assert eo <= tol(dt) and es <= tol(dt), (eo, es)
+
+
+@pytest.mark.parametrize("onchip", ["1", "0"])
+def test_chunkwise_short_segments_either_kernel(R, onchip, monkeypatch):
+    """Segments of at most 256 tokens: the on-chip kernel (default) and the streaming single-pass kernel
+    (RET_SEG_ONCHIP=0) give the oracle's result on the same inputs, with a state handed in and out."""
+    monkeypatch.setenv("RET_SEG_ONCHIP", onchip)
+    B, N, H, dk, dv, C = 2, 1234, 2, 64, 128, 64
+    print_case("short_segments onchip=%s" % onchip, (B, N, H, dk, dv, C))
+    rng = np.random.default_rng(57)
+    q = W.normal(rng, (B, N, H, dk), 8.0, "bf16")
+    k = W.normal(rng, (B, N, H, dk), 8.0, "bf16")
+    v = W.normal(rng, (B, N, H, dv), 8.0, "bf16")
+    s0 = rng.standard_normal((B, H, dk, dv)).astype(np.float32)
+    gamma, theta = W.gamma_schedule(H), W.theta_schedule(dk)
+    o_ref, s_ref = oracle.chunkwise(q, k, v, gamma, C, theta=theta, pos0=40, state_in=s0)
+    o, s = _gpu_chunkwise(R, q, k, v, "bf16", gamma, C, theta=theta, pos0=40, s_in=s0)
+    eo, es = rel_err(o, o_ref), rel_err(s, s_ref)
+    print("  err o=%.3g state=%.3g" % (eo, es))
+    assert eo <= tol("bf16") and es <= tol("bf16"), (eo, es)
 
 
 def test_chunkwise_wide_dv_without_workspace(R):
