@@ -145,10 +145,10 @@ int env_int(const char* name, int dflt) {
 
 // Number of segments per sequence and tokens per segment. Enough workgroups to fill the chip, but segments of
 // at least ~256 tokens so the per-segment state traffic stays small against the segment's own data.
-void plan_segments(int B, int N, int H, int dv, int C, int dvt, int* nseg, int* seg_len) {
+void plan_segments(int B, int N, int H, int dv, int C, int dvt, int target_wgs, int* nseg, int* seg_len) {
     const long long units = (long long)B * H * ((dv + dvt - 1) / dvt);
     const int nchunks = (N + C - 1) / C;
-    const int target = env_int("RET_TARGET_WGS", 1024);
+    const int target = env_int("RET_TARGET_WGS", target_wgs > 0 ? target_wgs : 1024);
     int g = (int)((target + units - 1) / units);
     const int forced = env_int("RET_SEGMENTS", 0);
     if (forced > 0) g = forced;
@@ -181,7 +181,7 @@ struct ChunkPlan {
 ChunkPlan plan_chunk(const ChunkKernels& ck, int B, int N, int H, int dk, int dv, int chunk, bool rotate,
                      size_t avail) {
     ChunkPlan p;
-    plan_segments(B, N, H, dv, chunk, ck.dvt, &p.nseg, &p.seg_len);
+    plan_segments(B, N, H, dv, chunk, ck.dvt, ck.target_wgs, &p.nseg, &p.seg_len);
     p.chain_bytes = (segment_ws_bytes(ck, B, H, dk, dv, p.nseg) + 255) / 256 * 256;
     p.rot_bytes = 0;
     if (ck.fused_pre && rotate && dv / ck.dvt >= 4)
@@ -305,8 +305,9 @@ ret_status_t ret_chunkwise_fwd(const void* q, const void* k, const void* v, void
             if ((st = launch_status("ret_rotate_qk")) != RET_OK) return st;
         }
         const unsigned grid = (unsigned)((long long)nseg * B * H * ntiles);
+        const int threads = onchip || !ck.threads ? kThreads : ck.threads;
         LaunchTimer tm(name, s);
-        hipLaunchKernelGGL(fn, dim3(grid), dim3(kThreads), 0, s, A);
+        hipLaunchKernelGGL(fn, dim3(grid), dim3(threads), 0, s, A);
         tm.done();
         return launch_status(name);
     }

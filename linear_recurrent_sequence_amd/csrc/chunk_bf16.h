@@ -76,15 +76,15 @@ __device__ __forceinline__ bf16x8_t acc_pair(f32x4_t a, f32x4_t b) {
                                                    pack2_bf16(b[0], b[1]), pack2_bf16(b[2], b[3])));
 }
 
-// Rows of a T x W bf16 tile moved as 16-byte segments: SPR segments per row, RP rows per pass of the
-// workgroup, NP passes. Thread t owns segment t % SPR of rows t / SPR + p * RP.
-template <int T, int W>
+// Rows of a T x W bf16 tile moved as 16-byte segments by NT threads: SPR segments per row, RP rows per pass of
+// the workgroup, NP passes. Thread t owns segment t % SPR of rows t / SPR + p * RP.
+template <int T, int W, int NT = kThreads>
 struct RowTile {
     static constexpr int SPR = W / 8;
-    static constexpr int RP = kThreads / SPR;
+    static constexpr int RP = NT / SPR;
     static constexpr int NP = (T + RP - 1) / RP;
     static constexpr bool PARTIAL = T % RP != 0;
-    static_assert(W % 8 == 0 && kThreads % SPR == 0, "row tile");
+    static_assert(W % 8 == 0 && NT % SPR == 0, "row tile");
     __device__ static __forceinline__ bool live(int row0, int p) { return !PARTIAL || row0 + p * RP < T; }
 };
 
@@ -188,22 +188,22 @@ __device__ __forceinline__ T* uniform_ptr(T* p) {
     return reinterpret_cast<T*>(((unsigned long long)hi << 32) | lo);
 }
 
-// One state slot: DK x 64 floats in the thread order of the R tiles (tile x of thread t at (x*256 + t)*16 bytes).
-template <int NKB>
+// One state slot: DK x (16 * NT / 64) floats in the thread order of the R tiles (tile x of thread t at
+// (x*NT + t)*16 bytes).
+template <int NKB, int NT>
 __device__ __forceinline__ void slot_store(float* slot, const f32x4_t* R, int tid) {
-    const rsrc_t r = bytes_rsrc(uniform_ptr(slot), NKB * kThreads * 16);
+    const rsrc_t r = bytes_rsrc(uniform_ptr(slot), NKB * NT * 16);
 #pragma unroll
     for (int x = 0; x < NKB; ++x)
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, R[x]), r, tid * 16, x * kThreads * 16,
-                                               kChainAux);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, R[x]), r, tid * 16, x * NT * 16, kChainAux);
 }
-template <int NKB>
+template <int NKB, int NT>
 __device__ __forceinline__ void slot_load(const float* slot, f32x4_t* v, int tid) {
-    const rsrc_t r = bytes_rsrc(uniform_ptr(slot), NKB * kThreads * 16);
+    const rsrc_t r = bytes_rsrc(uniform_ptr(slot), NKB * NT * 16);
 #pragma unroll
     for (int x = 0; x < NKB; ++x)
-        v[x] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, tid * 16, x * kThreads * 16,
-                                                                                  kChainAux));
+        v[x] = __builtin_bit_cast(f32x4_t,
+                                  __builtin_amdgcn_raw_buffer_load_b128(r, tid * 16, x * NT * 16, kChainAux));
 }
 
 // The unit (one d_v tile of one (b, h)) of this workgroup, from the launch index. Workgroups are dispatched to
@@ -262,9 +262,9 @@ __host__ __device__ constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4
 // `then` may issue NTHEN vector memory operations per thread (loads the caller wants in flight early): they go
 // out after the slot stores, and the wait before the flag covers the stores only. The flag store itself is
 // not waited for here; the workgroup's count (chain_enter or chain_finish) waits for it first.
-template <int NKB, int NTHEN, class Then>
+template <int NKB, int NT, int NTHEN, class Then>
 __device__ __forceinline__ void chain_publish(const Chain& ch, int seg, const f32x4_t* R, Then&& then) {
-    slot_store<NKB>(ch.agg + (size_t)seg * ch.slot, R, threadIdx.x);
+    slot_store<NKB, NT>(ch.agg + (size_t)seg * ch.slot, R, threadIdx.x);
     __asm__ volatile("" ::: "memory");  // `then` stays behind the stores
     then();
     __asm__ volatile("" ::: "memory");
@@ -272,9 +272,9 @@ __device__ __forceinline__ void chain_publish(const Chain& ch, int seg, const f3
     __syncthreads();
     if (threadIdx.x == 0) __hip_atomic_store(ch.flags + seg, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-template <int NKB>
+template <int NKB, int NT>
 __device__ __forceinline__ void chain_publish(const Chain& ch, int seg, const f32x4_t* R) {
-    chain_publish<NKB, 0>(ch, seg, R, [] {});
+    chain_publish<NKB, NT, 0>(ch, seg, R, [] {});
 }
 
 // R_in of segment seg: the sum over the group's earlier segments j of gamma^((seg-1-j)T) A_j, plus
@@ -284,7 +284,7 @@ __device__ __forceinline__ void chain_publish(const Chain& ch, int seg, const f3
 // With COUNT, the workgroup then counts itself past the look-back and the unit's last one resets the unit's
 // counters and flags (its other workgroups have read them all by then); without, chain_finish does that at
 // the end of the kernel. `bc` is a shared broadcast word.
-template <int NKB, bool COUNT>
+template <int NKB, int NT, bool COUNT>
 __device__ __forceinline__ void chain_enter(const Chain& ch, int seg, int nseg, float gT, const f32x4_t* Rown,
                                             f32x4_t* Rin, int& bc) {
     const int tid = threadIdx.x;
@@ -303,7 +303,7 @@ __device__ __forceinline__ void chain_enter(const Chain& ch, int seg, int nseg, 
             f32x4_t v[LB][NKB];
 #pragma unroll
             for (int i = 0; i < LB; ++i)
-                if (j0 - i >= g0) slot_load<NKB>(ch.agg + (size_t)(j0 - i) * ch.slot, v[i], tid);
+                if (j0 - i >= g0) slot_load<NKB, NT>(ch.agg + (size_t)(j0 - i) * ch.slot, v[i], tid);
 #pragma unroll
             for (int i = 0; i < LB; ++i)
                 if (j0 - i >= g0) {
@@ -314,7 +314,7 @@ __device__ __forceinline__ void chain_enter(const Chain& ch, int seg, int nseg, 
         }
         if (g0 > 0 && ok) {
             f32x4_t v[NKB];
-            slot_load<NKB>(ch.inc + (size_t)(g0 - 1) * ch.slot, v, tid);
+            slot_load<NKB, NT>(ch.inc + (size_t)(g0 - 1) * ch.slot, v, tid);
 #pragma unroll
             for (int x = 0; x < NKB; ++x) Rin[x] += dec * v[x];
         }
@@ -323,7 +323,7 @@ __device__ __forceinline__ void chain_enter(const Chain& ch, int seg, int nseg, 
         f32x4_t I[NKB];
 #pragma unroll
         for (int x = 0; x < NKB; ++x) I[x] = gT * Rin[x] + Rown[x];
-        slot_store<NKB>(ch.inc + (size_t)seg * ch.slot, I, tid);
+        slot_store<NKB, NT>(ch.inc + (size_t)seg * ch.slot, I, tid);
         __builtin_amdgcn_s_waitcnt(0);
     }
     __syncthreads();
@@ -335,7 +335,7 @@ __device__ __forceinline__ void chain_enter(const Chain& ch, int seg, int nseg, 
         }
         __syncthreads();
         if (__builtin_amdgcn_readfirstlane(bc) == nseg - 1) {
-            for (int i = tid; i < nseg; i += kThreads)
+            for (int i = tid; i < nseg; i += (int)blockDim.x)
                 __hip_atomic_store(ch.flags + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (tid == 0) {
                 __hip_atomic_store(ch.ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -363,7 +363,7 @@ __device__ __forceinline__ void chain_finish(const FwdArgs& a, int dvt, int slot
     }
     __syncthreads();
     if (__builtin_amdgcn_readfirstlane(bc) == nseg - 1) {
-        for (int i = tid; i < nseg; i += kThreads)
+        for (int i = tid; i < nseg; i += (int)blockDim.x)
             __hip_atomic_store(ch.flags + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (tid == 0) {
             __hip_atomic_store(ch.ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -381,8 +381,9 @@ __device__ __forceinline__ void chain_finish(const FwdArgs& a, int dvt, int slot
 // O^T += R^T Q^T with R^T taken from the state accumulators and the state update; then
 // O^T = xi (.) O^T + V^T P^T with P = mask (.) S straight from the S^T accumulators, stored to the output.
 // ---------------------------------------------------------------------------------------------------
-template <int DK, int C, int DVT, bool PRE>
+template <int DK, int C, int DVT, bool PRE, int NT>
 struct FullB {
+    static constexpr int NW = NT / 64;  // waves; wave w owns d_v columns 16w..16w+15 of the tile
     static constexpr int KS = DK < 64 ? DK : 64;
     static constexpr int NSL = DK / KS;
     // Row pitches (elements) of 36 words mod 64 LDS banks, so the rows one fragment or transposed read
@@ -392,9 +393,9 @@ struct FullB {
     static constexpr int LDQ = pitch(KS), LDV = pitch(DVT), LDK = pitch(DK);
     static constexpr int NB = C / 16, NDV = DVT / 16, NKB = DK / 16, XB = KS / 16;
     static constexpr int NS = Tri<NB>::count;
-    typedef RowTile<C, KS> TQ;
-    typedef RowTile<C, DVT> TV;
-    typedef RowTile<C, DK> TK;  // local pass: whole d_k
+    typedef RowTile<C, KS, NT> TQ;
+    typedef RowTile<C, DVT, NT> TV;
+    typedef RowTile<C, DK, NT> TK;  // local pass: whole d_k
     static constexpr int SQ = C * LDQ, SV = C * LDV;
     // One stage buffer: sQ, sK and (rotating in staging) sKz = K (.) zeta; with pre-rotated operands zeta goes
     // on the smaller V tile instead (sVz beside sV).
@@ -406,23 +407,23 @@ struct FullB {
     // Large d_k: each wave computes only its share of the S^T tiles and P goes through LDS, instead of every
     // wave computing all tiles (which costs NB(NB+1)/2 * d_k/32 MFMAs per wave per chunk).
     static constexpr bool SHARED_P = DK >= 128;
-    static constexpr int NS_W = (NS + kWaves - 1) / kWaves;
+    static constexpr int NS_W = (NS + NW - 1) / NW;
     static constexpr int LDP = C + 8, SP = SHARED_P ? C * LDP : 0;
     static constexpr int FULL_BYTES = (2 * STAGE + NVB * VBUF + SP) * 2;
     static constexpr int LOCAL_BYTES = (C * LDK + C * LDV) * 2;  // local pass: sKz [C][DK] and sV [C][DVT]
     static constexpr int LDS_BYTES = FULL_BYTES > LOCAL_BYTES ? FULL_BYTES : LOCAL_BYTES;
     // two workgroups per CU when the LDS allows and the registers of d_k = 256 are not needed
     static constexpr int OCC = LDS_BYTES <= 80 * 1024 && DK <= 128 ? 2 : 1;
-    static_assert(NDV == kWaves, "one d_v block per wave");
+    static_assert(NDV == NW, "one d_v block per wave");
     static_assert(C == 32 || C == 64, "chunk tile of 32 or 64 tokens");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     static_assert(KS % 32 == 0, "tiling");
     static_assert((LDK / 2) % 64 == 36 && (LDQ / 2) % 64 == 36 && (LDV / 2) % 64 == 36, "LDS row pitch");
 };
 
-template <int DK, int C, int DVT, bool PRE>
-__global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT, PRE>::OCC)) void chunk_fused_bf16(FwdArgs a) {
-    typedef FullB<DK, C, DVT, PRE> F;
+template <int DK, int C, int DVT, bool PRE, int NT>
+__global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT>::OCC)) void chunk_fused_bf16(FwdArgs a) {
+    typedef FullB<DK, C, DVT, PRE, NT> F;
     typedef typename F::TQ TQ;
     typedef typename F::TV TV;
     typedef typename F::TK TK;
@@ -569,7 +570,7 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT, PRE>::OCC)) void chunk
         }
         __syncthreads();  // the local tiles are dead before the full pass reuses the LDS
         // publish the aggregate for the later segments of the group (nothing else in flight)
-        if (!boundary) chain_publish<F::NKB>(ch, seg, R);
+        if (!boundary) chain_publish<F::NKB, NT>(ch, seg, R);
     }
 
     // ---- full pass: staging ----
@@ -607,7 +608,7 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT, PRE>::OCC)) void chunk
     // ---- entering state: state_in for the first segment, else R_in from the segment chain ----
     if (chained) {
         f32x4_t Rin[F::NKB];
-        chain_enter<F::NKB, true>(ch, seg, anseg, gpow(lg, (float)aseg_len), R, Rin, s_word);
+        chain_enter<F::NKB, NT, true>(ch, seg, anseg, gpow(lg, (float)aseg_len), R, Rin, s_word);
 #pragma unroll
         for (int x = 0; x < F::NKB; ++x) R[x] = Rin[x];
         if (seg == 0) {
@@ -637,7 +638,7 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT, PRE>::OCC)) void chunk
     if constexpr (F::SHARED_P) {
 #pragma unroll
         for (int x = 0; x < F::NS_W; ++x) {
-            tri_tile<F::NB>(min(w + kWaves * x, F::NS - 1), Sjb[x], Slb[x]);
+            tri_tile<F::NB>(min(w + F::NW * x, F::NS - 1), Sjb[x], Slb[x]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) DmS[x][e] = Dm[Sjb[x] - Slb[x]][e];
         }
@@ -800,7 +801,7 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT, PRE>::OCC)) void chunk
     // writes into the other buffers) run back to back with no barrier between them, so the vector work of
     // the staging issues while the matrix instructions execute; one barrier per stage.
     if constexpr (F::SHARED_P)  // scores above the diagonal are never written: zero for the P.V product
-        for (int i = tid; i < F::SP; i += kThreads) sP[i] = 0;
+        for (int i = tid; i < F::SP; i += NT) sP[i] = 0;
     __syncthreads();  // every wave has read the broadcast word, which the first commit overwrites
     if (nst > 0) {
         commit(0, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
@@ -835,7 +836,7 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT, PRE>::OCC)) void chunk
                 // then O^T = xi (.) (R^T Q^T) + V^T P^T with P read back in the permuted key order.
 #pragma unroll
                 for (int x = 0; x < F::NS_W; ++x)
-                    if (w + kWaves * x < F::NS) store4(sP + (Sjb[x] * 16 + n16) * F::LDP + Slb[x] * 16 + g4, S[x] * DmS[x]);
+                    if (w + F::NW * x < F::NS) store4(sP + (Sjb[x] * 16 + n16) * F::LDP + Slb[x] * 16 + g4, S[x] * DmS[x]);
                 __syncthreads();
 #pragma unroll
                 for (int x = 0; x < F::NB; ++x) O[x] *= Xi[x];
@@ -887,11 +888,21 @@ __global__ __launch_bounds__(kThreads, (FullB<DK, C, DVT, PRE>::OCC)) void chunk
 
 // Chunks of 128 tokens run as 64-token sub-chunks: the chunkwise recurrence gives the same result for any
 // chunk size (up to rounding), and 64-token tiles keep all of P in registers.
-template <int DK, int C>
+// Workgroups of 256 threads (4 waves, d_v tiles of 64), or of 512 (8 waves, d_v tiles of 128) where d_k is 256:
+// one d_v tile's products are d_k-deep, so a wider tile shares the scores and the q/k staging among twice the
+// columns, and two waves per SIMD hide each other's latencies.
+template <int DK, int C, int NT = (DK >= 256 ? 512 : 256)>
 ChunkKernels chunk_entry_bf16() {
-    constexpr int CI = C > 64 ? 64 : C;
-    return {nullptr, nullptr, chunk_fused_bf16<DK, CI, 64, false>, chunk_fused_bf16<DK, CI, 64, true>, 64,
-            nullptr, nullptr, 0};
+    constexpr int CI = C > 64 ? 64 : C, DVT = 16 * NT / 64;
+    ChunkKernels k{};
+    k.fused = chunk_fused_bf16<DK, CI, DVT, false, NT>;
+    k.fused_pre = chunk_fused_bf16<DK, CI, DVT, true, NT>;
+    k.dvt = DVT;
+    k.threads = NT;
+    // 512-thread workgroups run one per CU: one workgroup per CU in total measured fastest (fewer, longer
+    // segments); 256-thread ones two per CU, with two rounds of them.
+    k.target_wgs = NT >= 512 ? 256 : 1024;
+    return k;
 }
 
 }  // namespace ret

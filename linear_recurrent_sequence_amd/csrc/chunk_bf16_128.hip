@@ -1,4 +1,4 @@
-// bf16-input chunkwise kernels, d_k in {128}, chunk in {32, 64, 128}, d_v tiles of 64.
+// bf16-input chunkwise kernels, d_k in {128}, chunk in {32, 64, 128}, d_v tiles of 64 (256 threads).
 #include "chunk_bf16.h"
 
 namespace ret {

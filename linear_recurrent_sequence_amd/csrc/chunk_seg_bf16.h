@@ -260,9 +260,9 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_seg_bf16(FwdArgs a) {
     });
 
     // ---- segment chain: publish the local end state (the aggregate), then the entering state R_in ----
-    if (!last && !boundary) chain_publish<F::NKB>(ch, seg, R);
+    if (!last && !boundary) chain_publish<F::NKB, kThreads>(ch, seg, R);
     f32x4_t Rin[F::NKB];
-    chain_enter<F::NKB, false>(ch, seg, anseg, gpow(lg, (float)aseg_len), R, Rin, s_word);
+    chain_enter<F::NKB, kThreads, false>(ch, seg, anseg, gpow(lg, (float)aseg_len), R, Rin, s_word);
 
     // ---- the chain's term, then the outputs: O_c += xi (.) gamma^(cC) (Q'_c R_in) ----
     bf16x8_t rin[KK];

@@ -854,6 +854,8 @@ struct ChunkKernels {
     // single-pass kernels for chained runs whose segments hold at most seg_tokens tokens (0: none)
     fwd_kernel_t seg, seg_pre;
     int seg_tokens;
+    int threads;      // workgroup size of the fused kernels (0: kThreads)
+    int target_wgs;   // workgroups the segment planner aims for (0: the default)
 };
 struct ParKernel {
     fwd_kernel_t fn;
@@ -862,7 +864,8 @@ struct ParKernel {
 
 template <class E, int DK, int C, int DVT>
 ChunkKernels chunk_entry() {
-    return {chunk_full_kernel<E, DK, C, DVT>, chunk_local_kernel<E, DK, C, DVT>, nullptr, nullptr, DVT, nullptr, nullptr, 0};
+    return {chunk_full_kernel<E, DK, C, DVT>, chunk_local_kernel<E, DK, C, DVT>, nullptr, nullptr, DVT, nullptr, nullptr, 0,
+            kThreads, 0};
 }
 
 // Getters, one per kernel-group source. Return false when the shape has no instance.
