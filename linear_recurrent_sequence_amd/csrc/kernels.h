@@ -678,12 +678,13 @@ __global__ __launch_bounds__(kThreads, 2) void parallel_kernel(FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------------
-// recurrent_step: one workgroup per (64-column d_v tile, b*H + h) with one wave per 64 state rows. Lane
-// (rg, cg) of a wave owns columns 4cg..4cg+3 and 16 consecutive rows of the wave's 64 (rg = lane / 16): its
-// rows are read first (16 float4 loads in flight), updated S = gamma S + k_r v and written back in place,
-// while o = q S is summed over its rows, then over the four row groups with lane shuffles, then over the
-// waves through LDS. The rotation factors of the wave's 32 pairs are evaluated one pair per lane and shared
-// with shuffles.
+// recurrent_step: one workgroup per (CW-column d_v tile, b*H + h) with one wave per WR state rows (defaults
+// CW = 64, WR = 32: two waves per 64-row tile). Lane (rg, cg) of a wave owns columns 4cg..4cg+3 and WR/RG
+// consecutive rows (RG = 64 / (CW/4) row groups): it loads q, k, v and the rotation factors of its rows first,
+// then its state rows (all in flight at once), rotates q and k, updates each row S = gamma S + k_r v and writes
+// it back in place as it goes, while o = q S is summed over its rows, then over the wave's row groups with lane
+// shuffles, then over the waves through LDS. The rotation factors cos/sin(pos theta_i) come from the host,
+// evaluated there in fp64 once per step.
 // ---------------------------------------------------------------------------------------------------
 struct StepArgs {
     const void* q;

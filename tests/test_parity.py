@@ -117,6 +117,27 @@ def test_chunkwise_small(R, case, monkeypatch):
     assert eo <= tol(dt) and es <= tol(dt), (eo, es)
 
 
+@pytest.mark.parametrize("threads", ["512", "256"])
+def test_chunkwise_dk256_workgroup_sizes(R, threads, monkeypatch):
+    """d_k 256 runs 512-thread workgroups (d_v tiles of 128) where d_v allows; RET_DK256_THREADS=256 selects the
+    256-thread kernels (d_v tiles of 64). Both match the oracle, with two segments and 3 d_v tiles of 128."""
+    monkeypatch.setenv("RET_DK256_THREADS", threads)
+    monkeypatch.setenv("RET_SEGMENTS", "2")
+    B, N, H, dk, dv, C = 1, 300, 2, 256, 384, 64
+    print_case("dk256 threads=%s" % threads, (B, N, H, dk, dv, C))
+    rng = np.random.default_rng(71)
+    q = W.normal(rng, (B, N, H, dk), 16.0, "bf16")
+    k = W.normal(rng, (B, N, H, dk), 16.0, "bf16")
+    v = W.normal(rng, (B, N, H, dv), 16.0, "bf16")
+    s0 = rng.standard_normal((B, H, dk, dv)).astype(np.float32)
+    gamma, theta = W.gamma_schedule(H), W.theta_schedule(dk)
+    o_ref, s_ref = oracle.chunkwise(q, k, v, gamma, C, theta=theta, pos0=9, state_in=s0)
+    o, s = _gpu_chunkwise(R, q, k, v, "bf16", gamma, C, theta=theta, pos0=9, s_in=s0)
+    eo, es = rel_err(o, o_ref), rel_err(s, s_ref)
+    print("  err o=%.3g state=%.3g" % (eo, es))
+    assert eo <= tol("bf16") and es <= tol("bf16"), (eo, es)
+
+
 @pytest.mark.parametrize("onchip", ["1", "0"])
 def test_chunkwise_short_segments_either_kernel(R, onchip, monkeypatch):
     """Segments of at most 256 tokens: the on-chip kernel (default) and the streaming single-pass kernel
