@@ -265,6 +265,23 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_seg_bf16(FwdArgs a) {
     chain_enter<F::NKB, kThreads, false>(ch, seg, anseg, gpow(lg, (float)aseg_len), R, Rin, s_word);
 
     // ---- the chain's term, then the outputs: O_c += xi (.) gamma^(cC) (Q'_c R_in) ----
+    // bf16 outputs leave through the K' staging tiles (free by now; chunk c uses tile c % 2, last read before the
+    // barrier of chunk c - 1) as whole rows: each wave writes its O^T tiles as rows of O, then 8 lanes store one
+    // row's 64 d_v (128 bytes) with one 16-byte store each, instead of four waves writing 32-byte pieces of it.
+    auto store_rows = [&](int c, const f32x4_t* O, uint16_t* buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int x = 0; x < NB; ++x)
+            *reinterpret_cast<uint2*>(buf + (x * 16 + n16) * LD + w * 16 + g4) =
+                make_uint2(pack2_bf16(O[x][0], O[x][1]), pack2_bf16(O[x][2], O[x][3]));
+        __syncthreads();
+        const int L = min(C, seg_n - c * C);
+        const rsrc_t ro = bytes_rsrc(oh + (long long)c * C * rsv * 2, ((L - 1) * rsv + 64) * 2);
+        const int row = tid / 8, sg = tid % 8;
+#pragma unroll
+        for (int p = 0; p < C / 32; ++p)
+            buf_store16(ro, ((row + 32 * p) * rsv + sg * 8) * 2, 0,
+                        *reinterpret_cast<const u32x4_t*>(buf + (row + 32 * p) * LD + sg * 8));
+    };
     bf16x8_t rin[KK];
 #pragma unroll
     for (int k = 0; k < KK; ++k) rin[k] = acc_pair(Rin[2 * k], Rin[2 * k + 1]);
@@ -282,7 +299,10 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_seg_bf16(FwdArgs a) {
                     Op[c][x] += (gc * Xi[x]) * X;
                 }
             }
-            store_out(c, Op[c]);
+            if (a.out_bf16)
+                store_rows(c, Op[c], sKst + (c & 1) * F::TILE);
+            else
+                store_out(c, Op[c]);
         }
     });
 
