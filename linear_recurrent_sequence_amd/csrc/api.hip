@@ -184,7 +184,9 @@ ChunkPlan plan_chunk(const ChunkKernels& ck, int B, int N, int H, int dk, int dv
     plan_segments(B, N, H, dv, chunk, ck.dvt, ck.target_wgs, &p.nseg, &p.seg_len);
     p.chain_bytes = (segment_ws_bytes(ck, B, H, dk, dv, p.nseg) + 255) / 256 * 256;
     p.rot_bytes = 0;
-    if (ck.fused_pre && rotate && dv / ck.dvt >= 4)
+    // RET_PREROTATE=0 / 1 turns the up-front rotation off / on wherever a kernel supports it.
+    const int pre = env_int("RET_PREROTATE", -1);
+    if (ck.fused_pre && rotate && (pre < 0 ? dv / ck.dvt >= 4 : pre != 0))
         p.rot_bytes = 2 * (((size_t)B * N * H * dk * 2 + 255) / 256 * 256);
     if (p.chain_bytes + p.rot_bytes > avail) p.rot_bytes = 0;
     while (p.nseg > 1 && segment_ws_bytes(ck, B, H, dk, dv, p.nseg) > avail) {

@@ -31,22 +31,6 @@ __device__ __forceinline__ void buf_store16(rsrc_t r, int voff, int soff, u32x4_
     __builtin_amdgcn_raw_buffer_store_b128(x, r, voff, soff, 0);
 }
 
-// Transposed MFMA operand from a row-major LDS matrix X[k][n] (pitch ld): lane l receives
-// X[k0 + 8*(l/16) + i][n0 + l%16], i = 0..7, i.e. the operand whose row index is n and reduction index is k.
-// `tro` is the lane's part of the address, tr_lane_offset(ld, lane). Within each group of 16 lanes one
-// transpose read turns 4 rows x 16 columns (lane 4r+c addresses row r, columns 4c..4c+3) into 16 lanes x 4
-// rows; two reads cover the 8 reduction indices of the lane's group.
-__device__ __forceinline__ int tr_lane_offset(int ld, int lane) {
-    return (8 * (lane >> 4) + ((lane >> 2) & 3)) * ld + 4 * (lane & 3);
-}
-__device__ __forceinline__ bf16x8_t frag_tr(const uint16_t* X, int ld, int k0, int n0, int tro) {
-    typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
-    uint16_t* p = const_cast<uint16_t*>(X) + k0 * ld + n0 + tro;
-    const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)p);
-    const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p + 4 * ld));
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
 // Operand fragments in the permuted reduction order used by the fused kernel: within each 32-wide reduction
 // step, lane group g (= lane / 16) holds indices 4g..4g+3 and 16+4g..16+4g+3. An MFMA sums over the reduction
 // index, so any order shared by both operands gives the same product; this one matches the accumulator
@@ -68,6 +52,43 @@ __device__ __forceinline__ bf16x8_t frag_trp(const uint16_t* X, int ld, int k0, 
     uint16_t* p = const_cast<uint16_t*>(X) + k0 * ld + n0 + tro;
     const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)p);
     const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p + 16 * ld));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+// LDS tile of W bf16 columns laid out for both read patterns of the products. With 64 banks of 4 bytes the
+// LDS serves a 64-lane 8-byte read as two halves of 32 lanes, and each half should touch all 64 banks once:
+//  * row fragments (frag_ps): 16 consecutive rows x 2 adjacent 8-byte units;
+//  * transposed fragments (frag_trps): 8 consecutive rows x 4 adjacent units.
+// A row pitch of W + 16 columns (8 mod 16 words past a multiple of 64 banks) serves the second; swapping the two
+// 8-column halves of every 16 columns in rows 8..15 of each 16 (c ^ 8) then also serves the first. The swap
+// keeps 16-byte staging stores whole and does not interact with column offsets that are multiples of 16, so a
+// lane's part of a fragment address is one value per tile and the rest are constants.
+template <int W>
+struct Swz {
+    static constexpr int LD = W + 16;
+    // element offset of column c (a multiple of 4) of row r
+    __device__ static __forceinline__ int off(int r, int c) { return r * LD + (c ^ (((r >> 3) & 1) << 3)); }
+    // lane part of frag_ps / frag_trps addresses
+    __device__ static __forceinline__ int lane_p(int lane) { return off(lane & 15, 4 * (lane >> 4)); }
+    __device__ static __forceinline__ int lane_trp(int lane) {
+        return off(4 * (lane >> 4) + ((lane >> 2) & 3), 4 * (lane & 3));
+    }
+};
+// frag_p on a Swz tile: rows r0 + l%16 (r0 a multiple of 16), reduction columns k0 + 4g.. and k0 + 16 + 4g..
+// (k0 a multiple of 32). `lo_` is Swz<W>::lane_p(lane).
+template <int W>
+__device__ __forceinline__ bf16x8_t frag_ps(const uint16_t* X, int r0, int k0, int lo_) {
+    const uint16_t* p = X + r0 * Swz<W>::LD + k0 + lo_;
+    const uint2 lo = *reinterpret_cast<const uint2*>(p), hi = *reinterpret_cast<const uint2*>(p + 16);
+    return __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+// frag_trp on a Swz tile X[k][n]: lane l receives X[k0 + 4g + i][n0 + l%16] and X[k0 + 16 + 4g + i][n0 + l%16]
+// (k0 a multiple of 32, n0 of 16). `lo_` is Swz<W>::lane_trp(lane).
+template <int W>
+__device__ __forceinline__ bf16x8_t frag_trps(const uint16_t* X, int k0, int n0, int lo_) {
+    typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+    uint16_t* p = const_cast<uint16_t*>(X) + k0 * Swz<W>::LD + n0 + lo_;
+    const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)p);
+    const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p + 16 * Swz<W>::LD));
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 // Two accumulator tiles (rows 0..15 and 16..31 of a 32-row block) as one operand in the permuted order.
@@ -381,22 +402,18 @@ __device__ __forceinline__ void chain_finish(const FwdArgs& a, int dvt, int slot
 // O^T += R^T Q^T with R^T taken from the state accumulators and the state update; then
 // O^T = xi (.) O^T + V^T P^T with P = mask (.) S straight from the S^T accumulators, stored to the output.
 // ---------------------------------------------------------------------------------------------------
-template <int DK, int C, int DVT, bool PRE, int NT>
+template <int DK, int C, int DVT, bool PRE, int NT, int NDW>
 struct FullB {
-    static constexpr int NW = NT / 64;  // waves; wave w owns d_v columns 16w..16w+15 of the tile
+    static constexpr int NW = NT / 64;  // waves; wave w owns d_v blocks w*NDW .. w*NDW + NDW - 1 of 16 columns
     static constexpr int KS = DK < 64 ? DK : 64;
     static constexpr int NSL = DK / KS;
-    // Row pitches (elements) of 36 words mod 64 LDS banks, so the rows one fragment or transposed read
-    // touches fall in distinct banks: a width plus 8 gives that at 64 columns but 4 mod 64 at 128 and 256,
-    // and 20 at 32.
-    static constexpr int pitch(int w) { return w + ((72 - w) % 128 + 128) % 128; }
-    static constexpr int LDQ = pitch(KS), LDV = pitch(DVT), LDK = pitch(DK);
+    // q/k slices, V and the local pass's K are Swz tiles of KS, DVT and DK columns.
     static constexpr int NB = C / 16, NDV = DVT / 16, NKB = DK / 16, XB = KS / 16;
     static constexpr int NS = Tri<NB>::count;
     typedef RowTile<C, KS, NT> TQ;
     typedef RowTile<C, DVT, NT> TV;
     typedef RowTile<C, DK, NT> TK;  // local pass: whole d_k
-    static constexpr int SQ = C * LDQ, SV = C * LDV;
+    static constexpr int SQ = C * Swz<KS>::LD, SV = C * Swz<DVT>::LD;
     // One stage buffer: sQ, sK and (rotating in staging) sKz = K (.) zeta; with pre-rotated operands zeta goes
     // on the smaller V tile instead (sVz beside sV).
     static constexpr int STAGE = (PRE ? 2 : 3) * SQ;
@@ -410,20 +427,20 @@ struct FullB {
     static constexpr int NS_W = (NS + NW - 1) / NW;
     static constexpr int LDP = C + 8, SP = SHARED_P ? C * LDP : 0;
     static constexpr int FULL_BYTES = (2 * STAGE + NVB * VBUF + SP) * 2;
-    static constexpr int LOCAL_BYTES = (C * LDK + C * LDV) * 2;  // local pass: sKz [C][DK] and sV [C][DVT]
+    static constexpr int LOCAL_BYTES = (C * Swz<DK>::LD + C * Swz<DVT>::LD) * 2;  // local pass: sKz [C][DK] and sV [C][DVT]
     static constexpr int LDS_BYTES = FULL_BYTES > LOCAL_BYTES ? FULL_BYTES : LOCAL_BYTES;
     // two workgroups per CU when the LDS allows and the registers of d_k = 256 are not needed
-    static constexpr int OCC = LDS_BYTES <= 80 * 1024 && DK <= 128 ? 2 : 1;
-    static_assert(NDV == NW, "one d_v block per wave");
+    static constexpr int OCC = LDS_BYTES <= 80 * 1024 && DK * NDW <= 128 ? 2 : 1;
+    static_assert(NDV == NW * NDW, "NDW d_v blocks per wave");
     static_assert(C == 32 || C == 64, "chunk tile of 32 or 64 tokens");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     static_assert(KS % 32 == 0, "tiling");
-    static_assert((LDK / 2) % 64 == 36 && (LDQ / 2) % 64 == 36 && (LDV / 2) % 64 == 36, "LDS row pitch");
 };
 
-template <int DK, int C, int DVT, bool PRE, int NT>
-__global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT>::OCC)) void chunk_fused_bf16(FwdArgs a) {
-    typedef FullB<DK, C, DVT, PRE, NT> F;
+template <int DK, int C, int DVT, bool PRE, int NT, int NDW>
+__global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT, NDW>::OCC)) void chunk_fused_bf16(FwdArgs a) {
+    typedef FullB<DK, C, DVT, PRE, NT, NDW> F;
+    constexpr int NR = F::NKB * NDW;  // state tiles of a wave: R[x * NDW + j] = rows 16x.., d_v block w * NDW + j
     typedef typename F::TQ TQ;
     typedef typename F::TV TV;
     typedef typename F::TK TK;
@@ -470,20 +487,26 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT>::OCC)) void chunk_f
     char* oh = (char*)a.o + (head0 * adv + dv0) * osz;
     const int vrow = tid / TV::SPR, vseg = tid % TV::SPR;
     const int voff = (vrow * rsv + vseg * 8) * 2;
-    const int tro_v = tr_lane_offset(F::LDV, lane), tro_vp = trp_lane_offset(F::LDV, lane);
+    typedef Swz<F::KS> ZQ;
+    typedef Swz<DVT> ZV;
+    typedef Swz<DK> ZK;
+    const int lq_p = ZQ::lane_p(lane), lq_t = ZQ::lane_trp(lane), lv_t = ZV::lane_trp(lane);
     // State_in enters through the first segment: its local pass starts from it, so its published end state
     // carries state_in into every later R_in, and its full pass starts from it again.
     auto load_state_in = [&](f32x4_t* R) __attribute__((always_inline)) {
 #pragma unroll
         for (int x = 0; x < F::NKB; ++x)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                R[x][e] = a.state_in[((long long)pair * DK + x * 16 + g4 + e) * adv + dv0 + w * 16 + n16];
+            for (int j = 0; j < NDW; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    R[x * NDW + j][e] = a.state_in[((long long)pair * DK + x * 16 + g4 + e) * adv + dv0 +
+                                                   (w * NDW + j) * 16 + n16];
     };
 
-    f32x4_t R[F::NKB];
+    f32x4_t R[NR];
 #pragma unroll
-    for (int x = 0; x < F::NKB; ++x) R[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int x = 0; x < NR; ++x) R[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     if (seg == 0 && a.state_in) load_state_in(R);
 
     const bool last = seg == anseg - 1;
@@ -492,10 +515,10 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT>::OCC)) void chunk_f
     // ---- local pass over the segment (chained runs, all segments but the last) ----
     if (chained && !last) {
         uint16_t* lK = smem;
-        uint16_t* lV = smem + C * F::LDK;
+        uint16_t* lV = smem + C * ZK::LD;
+        const int lk_t = ZK::lane_trp(lane);
         const int krow = tid / TK::SPR, kseg = tid % TK::SPR;
         const int koff = (krow * rsk + kseg * 8) * 2;
-        const int tro_k = tr_lane_offset(F::LDK, lane);
         // Two register buffers: the loads of chunk c+2 go out as soon as chunk c is staged.
         u32x4_t lk[2][TK::NP], lv[2][TV::NP];
         auto lissue = [&](int c, auto parc) __attribute__((always_inline)) {
@@ -525,7 +548,7 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT>::OCC)) void chunk_f
             if constexpr (PRE) {  // K' as staged; zeta on V
 #pragma unroll
                 for (int p = 0; p < TK::NP; ++p)
-                    if (TK::live(krow, p)) lds_store16(lK + (krow + p * TK::RP) * F::LDK + kseg * 8, lk[par][p]);
+                    if (TK::live(krow, p)) lds_store16(lK + ZK::off(krow + p * TK::RP, kseg * 8), lk[par][p]);
 #pragma unroll
                 for (int p = 0; p < TV::NP; ++p)
                     if (TV::live(vrow, p)) {
@@ -533,7 +556,7 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT>::OCC)) void chunk_f
                         unpack8(lv[par][p], vf);
 #pragma unroll
                         for (int e = 0; e < 8; ++e) vf[e] *= zlv[p];
-                        lds_store16(lV + (vrow + p * TV::RP) * F::LDV + vseg * 8, pack8(vf));
+                        lds_store16(lV + ZV::off(vrow + p * TV::RP, vseg * 8), pack8(vf));
                     }
             } else {
                 if ((c & 7) == 0) lrot.cur.eval(a.pos0 + seg_t0 + (long long)c * C + krow, a.theta, kseg * 4);
@@ -546,22 +569,28 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT>::OCC)) void chunk_f
                         if (p + 1 < TK::NP) lrot.cur.turn(lrot.pass);
 #pragma unroll
                         for (int e = 0; e < 8; ++e) kf[e] *= zl[p];
-                        lds_store16(lK + (krow + p * TK::RP) * F::LDK + kseg * 8, pack8(kf));
+                        lds_store16(lK + ZK::off(krow + p * TK::RP, kseg * 8), pack8(kf));
                     }
                 lrot.next_chunk();
 #pragma unroll
                 for (int p = 0; p < TV::NP; ++p)
-                    if (TV::live(vrow, p)) lds_store16(lV + (vrow + p * TV::RP) * F::LDV + vseg * 8, lv[par][p]);
+                    if (TV::live(vrow, p)) lds_store16(lV + ZV::off(vrow + p * TV::RP, vseg * 8), lv[par][p]);
             }
             if (c + 2 < nchunks) lissue(c + 2, parc);
             __syncthreads();
 #pragma unroll
-            for (int x = 0; x < F::NKB; ++x) R[x] *= gC;
+            for (int x = 0; x < NR; ++x) R[x] *= gC;
 #pragma unroll
             for (int f = 0; f < C / 32; ++f) {
-                const bf16x8_t fb = frag_tr(lV, F::LDV, 32 * f, w * 16, tro_v);
+                bf16x8_t fb[NDW];
 #pragma unroll
-                for (int x = 0; x < F::NKB; ++x) mfma(R[x], frag_tr(lK, F::LDK, 32 * f, x * 16, tro_k), fb);
+                for (int j = 0; j < NDW; ++j) fb[j] = frag_trps<DVT>(lV, 32 * f, (w * NDW + j) * 16, lv_t);
+#pragma unroll
+                for (int x = 0; x < F::NKB; ++x) {
+                    const bf16x8_t ka = frag_trps<DK>(lK, 32 * f, x * 16, lk_t);
+#pragma unroll
+                    for (int j = 0; j < NDW; ++j) mfma(R[x * NDW + j], ka, fb[j]);
+                }
             }
         };
         for (int c = 0; c < nchunks; c += 2) {
@@ -570,13 +599,12 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT>::OCC)) void chunk_f
         }
         __syncthreads();  // the local tiles are dead before the full pass reuses the LDS
         // publish the aggregate for the later segments of the group (nothing else in flight)
-        if (!boundary) chain_publish<F::NKB, NT>(ch, seg, R);
+        if (!boundary) chain_publish<NR, NT>(ch, seg, R);
     }
 
     // ---- full pass: staging ----
     const int qrow = tid / TQ::SPR, qseg = tid % TQ::SPR;
     const int qoff = (qrow * rsk + qseg * 8) * 2;
-    const int tro_q = trp_lane_offset(F::LDQ, lane);
     // Two register buffers of staged loads: stage i+2's loads go out as soon as stage i is staged. Stage
     // parity is the chunk's with one d_k slice, the slice's with an even number of slices.
     constexpr int NBUF = 2;
@@ -607,13 +635,13 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT>::OCC)) void chunk_f
 
     // ---- entering state: state_in for the first segment, else R_in from the segment chain ----
     if (chained) {
-        f32x4_t Rin[F::NKB];
-        chain_enter<F::NKB, NT, true>(ch, seg, anseg, gpow(lg, (float)aseg_len), R, Rin, s_word);
+        f32x4_t Rin[NR];
+        chain_enter<NR, NT, true>(ch, seg, anseg, gpow(lg, (float)aseg_len), R, Rin, s_word);
 #pragma unroll
-        for (int x = 0; x < F::NKB; ++x) R[x] = Rin[x];
+        for (int x = 0; x < NR; ++x) R[x] = Rin[x];
         if (seg == 0) {
 #pragma unroll
-            for (int x = 0; x < F::NKB; ++x) R[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int x = 0; x < NR; ++x) R[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             if (a.state_in) load_state_in(R);
         }
     }
@@ -668,8 +696,8 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT>::OCC)) void chunk_f
 #pragma unroll
             for (int p = 0; p < TQ::NP; ++p)
                 if (TQ::live(qrow, p)) {
-                    lds_store16(sQ + (qrow + p * TQ::RP) * F::LDQ + qseg * 8, bq[par][p]);
-                    lds_store16(sK + (qrow + p * TQ::RP) * F::LDQ + qseg * 8, bk[par][p]);
+                    lds_store16(sQ + ZQ::off(qrow + p * TQ::RP, qseg * 8), bq[par][p]);
+                    lds_store16(sK + ZQ::off(qrow + p * TQ::RP, qseg * 8), bk[par][p]);
                 }
             if constexpr (sl == 0) {
                 uint16_t* sVz = sV + F::SV;
@@ -677,13 +705,13 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT>::OCC)) void chunk_f
                 for (int p = 0; p < TV::NP; ++p) {
                     const int r = vrow + p * TV::RP;
                     if (TV::live(vrow, p)) {
-                        lds_store16(sV + r * F::LDV + vseg * 8, bv[par][p]);
+                        lds_store16(sV + ZV::off(r, vseg * 8), bv[par][p]);
                         const float z = L == C ? zvfull[p] : (r < L ? gpow(lg, (float)(L - 1 - r)) : 0.f);
                         float vf[8];
                         unpack8(bv[par][p], vf);
 #pragma unroll
                         for (int e = 0; e < 8; ++e) vf[e] *= z;
-                        lds_store16(sVz + r * F::LDV + vseg * 8, pack8(vf));
+                        lds_store16(sVz + ZV::off(r, vseg * 8), pack8(vf));
                     }
                 }
             }
@@ -701,41 +729,47 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT>::OCC)) void chunk_f
                     rot[sl].cur.apply(qf);
                     rot[sl].cur.apply(kf);
                     if (p + 1 < TQ::NP) rot[sl].cur.turn(rot[sl].pass);
-                    lds_store16(sQ + r * F::LDQ + qseg * 8, pack8(qf));
-                    lds_store16(sK + r * F::LDQ + qseg * 8, pack8(kf));
+                    lds_store16(sQ + ZQ::off(r, qseg * 8), pack8(qf));
+                    lds_store16(sK + ZQ::off(r, qseg * 8), pack8(kf));
                     const float z = L == C ? zfull[p] : (r < L ? gpow(lg, (float)(L - 1 - r)) : 0.f);
 #pragma unroll
                     for (int e = 0; e < 8; ++e) kf[e] *= z;
-                    lds_store16(sKz + r * F::LDQ + qseg * 8, pack8(kf));
+                    lds_store16(sKz + ZQ::off(r, qseg * 8), pack8(kf));
                 }
             }
             rot[sl].next_chunk();
             if constexpr (sl == 0) {
 #pragma unroll
                 for (int p = 0; p < TV::NP; ++p)
-                    if (TV::live(vrow, p)) lds_store16(sV + (vrow + p * TV::RP) * F::LDV + vseg * 8, bv[par][p]);
+                    if (TV::live(vrow, p)) lds_store16(sV + ZV::off(vrow + p * TV::RP, vseg * 8), bv[par][p]);
             }
         }
     };
 
-    // Output stores straight from the O^T accumulators: lane (g, n16) of tile x holds 4 consecutive d_v of
-    // query x*16 + n16. Rows past the sequence fall outside the buffer range and are dropped.
-    const int o_voff = (n16 * rsv + w * 16 + g4) * osz;
+    // Output stores straight from the O^T accumulators: lane (g, n16) of tile (x, j) holds 4 consecutive d_v of
+    // query x*16 + n16 in d_v block w * NDW + j. Rows past the sequence fall outside the buffer range and are
+    // dropped.
+    const int o_voff = (n16 * rsv + w * NDW * 16 + g4) * osz;
     auto store_out = [&](int c, const f32x4_t* O) __attribute__((always_inline)) {
         const int L = min(C, seg_n - c * C);
         const rsrc_t ro = bytes_rsrc(oh + (long long)c * C * rsv * osz, ((L - 1) * rsv + DVT) * osz);
         if (a.out_bf16) {
 #pragma unroll
             for (int x = 0; x < F::NB; ++x)
-                __builtin_amdgcn_raw_buffer_store_b64(
-                    __builtin_bit_cast(uint32_t __attribute__((ext_vector_type(2))),
-                                       make_uint2(pack2_bf16(O[x][0], O[x][1]), pack2_bf16(O[x][2], O[x][3]))),
-                    ro, o_voff, x * 16 * rsv * 2, kOutAux);
+#pragma unroll
+                for (int j = 0; j < NDW; ++j)
+                    __builtin_amdgcn_raw_buffer_store_b64(
+                        __builtin_bit_cast(uint32_t __attribute__((ext_vector_type(2))),
+                                           make_uint2(pack2_bf16(O[x * NDW + j][0], O[x * NDW + j][1]),
+                                                      pack2_bf16(O[x * NDW + j][2], O[x * NDW + j][3]))),
+                        ro, o_voff, (x * 16 * rsv + j * 16) * 2, kOutAux);
         } else {
 #pragma unroll
             for (int x = 0; x < F::NB; ++x)
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, O[x]), ro, o_voff, x * 16 * rsv * 4,
-                                                       kOutAux);
+#pragma unroll
+                for (int j = 0; j < NDW; ++j)
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, O[x * NDW + j]), ro, o_voff,
+                                                           (x * 16 * rsv + j * 16) * 4, kOutAux);
         }
     };
 
@@ -761,14 +795,13 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT>::OCC)) void chunk_f
             bf16x8_t qf[F::NB], kf[F::NB];
 #pragma unroll
             for (int x = 0; x < F::NB; ++x) {
-                qf[x] = frag_p(sQ + x * 16 * F::LDQ, F::LDQ, kk, lane);
-                if constexpr (!F::SHARED_P) kf[x] = frag_p(sK + x * 16 * F::LDQ, F::LDQ, kk, lane);
+                qf[x] = frag_ps<F::KS>(sQ, x * 16, kk, lq_p);
+                if constexpr (!F::SHARED_P) kf[x] = frag_ps<F::KS>(sK, x * 16, kk, lq_p);
             }
             if constexpr (F::SHARED_P) {
 #pragma unroll
                 for (int x = 0; x < F::NS_W; ++x)
-                    mfma(S[x], frag_p(sK + Slb[x] * 16 * F::LDQ, F::LDQ, kk, lane),
-                         frag_p(sQ + Sjb[x] * 16 * F::LDQ, F::LDQ, kk, lane));
+                    mfma(S[x], frag_ps<F::KS>(sK, Slb[x] * 16, kk, lq_p), frag_ps<F::KS>(sQ, Sjb[x] * 16, kk, lq_p));
             } else {
 #pragma unroll
                 for (int jb = 0; jb < F::NB; ++jb)
@@ -776,24 +809,32 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT>::OCC)) void chunk_f
                     for (int lb = 0; lb <= jb; ++lb) mfma(S[tri(jb, lb)], kf[lb], qf[jb]);
             }
             const int rb = (sl * F::KS + kk) / 16;
-            const bf16x8_t ra = acc_pair(R[rb], R[rb + 1]);
 #pragma unroll
-            for (int x = 0; x < F::NB; ++x) mfma(O[x], ra, qf[x]);
+            for (int j = 0; j < NDW; ++j) {
+                const bf16x8_t ra = acc_pair(R[rb * NDW + j], R[(rb + 1) * NDW + j]);
+#pragma unroll
+                for (int x = 0; x < F::NB; ++x) mfma(O[x * NDW + j], ra, qf[x]);
+            }
         }
         if constexpr (sl == 0) {
 #pragma unroll
-            for (int f = 0; f < KF; ++f) {
-                fv[f] = frag_trp(sV, F::LDV, 32 * f, w * 16, tro_vp);
-                if constexpr (PRE) fvz[f] = frag_trp(sV + F::SV, F::LDV, 32 * f, w * 16, tro_vp);
-            }
+            for (int f = 0; f < KF; ++f)
+#pragma unroll
+                for (int j = 0; j < NDW; ++j) {
+                    fv[f * NDW + j] = frag_trps<DVT>(sV, 32 * f, (w * NDW + j) * 16, lv_t);
+                    if constexpr (PRE) fvz[f * NDW + j] = frag_trps<DVT>(sV + F::SV, 32 * f, (w * NDW + j) * 16, lv_t);
+                }
         }
 #pragma unroll
-        for (int x = sl * F::XB; x < (sl + 1) * F::XB; ++x) R[x] *= gL;
+        for (int x = sl * F::XB * NDW; x < (sl + 1) * F::XB * NDW; ++x) R[x] *= gL;
 #pragma unroll
         for (int f = 0; f < KF; ++f) {
 #pragma unroll
-            for (int x = sl * F::XB; x < (sl + 1) * F::XB; ++x)
-                mfma(R[x], frag_trp(sKA, F::LDQ, 32 * f, (x - sl * F::XB) * 16, tro_q), PRE ? fvz[f] : fv[f]);
+            for (int x = sl * F::XB; x < (sl + 1) * F::XB; ++x) {
+                const bf16x8_t ka = frag_trps<F::KS>(sKA, 32 * f, (x - sl * F::XB) * 16, lq_t);
+#pragma unroll
+                for (int j = 0; j < NDW; ++j) mfma(R[x * NDW + j], ka, PRE ? fvz[f * NDW + j] : fv[f * NDW + j]);
+            }
         }
     };
 
@@ -813,13 +854,14 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT>::OCC)) void chunk_f
         const int L = min(C, seg_n - c * C);
         const float gL = L == C ? gC : gpow(lg, (float)L);
         constexpr int NSA = F::SHARED_P ? F::NS_W : F::NS;  // S^T accumulators of this wave
-        f32x4_t S[NSA], O[F::NB];
+        f32x4_t S[NSA], O[F::NB * NDW];
 #pragma unroll
         for (int x = 0; x < NSA; ++x) S[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int x = 0; x < F::NB; ++x) O[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        bf16x8_t fv[KF];   // V^T operand of d_v block w (A of the P.V product; B of the state update unless PRE)
-        bf16x8_t fvz[KF];  // (V (.) zeta)^T operand: B of the state update with pre-rotated operands
+        for (int x = 0; x < F::NB * NDW; ++x) O[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        // V^T operands of the wave's d_v blocks (A of the P.V product; B of the state update unless PRE), and
+        // (V (.) zeta)^T: B of the state update with pre-rotated operands
+        bf16x8_t fv[KF * NDW], fvz[KF * NDW];
         static_for<0, F::NSL>([&](auto slc) __attribute__((always_inline)) {
             constexpr int sl = decltype(slc)::value;
             constexpr int sln = (sl + 1) % F::NSL;  // slice of the next stage
@@ -839,18 +881,22 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT>::OCC)) void chunk_f
                     if (w + F::NW * x < F::NS) store4(sP + (Sjb[x] * 16 + n16) * F::LDP + Slb[x] * 16 + g4, S[x] * DmS[x]);
                 __syncthreads();
 #pragma unroll
-                for (int x = 0; x < F::NB; ++x) O[x] *= Xi[x];
+                for (int x = 0; x < F::NB * NDW; ++x) O[x] *= Xi[x / NDW];
 #pragma unroll
                 for (int f = 0; f < KF; ++f) {
 #pragma unroll
-                    for (int x = 2 * f; x < F::NB; ++x) mfma(O[x], fv[f], frag_p(sP + x * 16 * F::LDP, F::LDP, 32 * f, lane));
+                    for (int x = 2 * f; x < F::NB; ++x) {
+                        const bf16x8_t pf = frag_p(sP + x * 16 * F::LDP, F::LDP, 32 * f, lane);
+#pragma unroll
+                        for (int j = 0; j < NDW; ++j) mfma(O[x * NDW + j], fv[f * NDW + j], pf);
+                    }
                 }
                 store_out(c, O);
             } else if constexpr (sl == F::NSL - 1) {
                 // O^T = xi (.) (R^T Q^T) + V^T P^T, P = mask (.) S taken from the S^T accumulators as the B
                 // operand (keys 32f.. of query block x are tiles lb = 2f and 2f + 1).
 #pragma unroll
-                for (int x = 0; x < F::NB; ++x) O[x] *= Xi[x];
+                for (int x = 0; x < F::NB * NDW; ++x) O[x] *= Xi[x / NDW];
 #pragma unroll
                 for (int f = 0; f < KF; ++f) {
 #pragma unroll
@@ -861,7 +907,9 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT>::OCC)) void chunk_f
                         if (2 * f + 1 <= x)
                             p1 = S[tri(x, 2 * f + 1)] * f32x4_t{Dm[x - 2 * f - 1][0], Dm[x - 2 * f - 1][1],
                                                                 Dm[x - 2 * f - 1][2], Dm[x - 2 * f - 1][3]};
-                        mfma(O[x], fv[f], acc_pair(p0, p1));
+                        const bf16x8_t pb = acc_pair(p0, p1);
+#pragma unroll
+                        for (int j = 0; j < NDW; ++j) mfma(O[x * NDW + j], fv[f * NDW + j], pb);
                     }
                 }
                 store_out(c, O);
@@ -879,29 +927,32 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT>::OCC)) void chunk_f
     if (last && a.state_out) {
         float* out = a.state_out + (long long)pair * DK * adv;
 #pragma unroll
-        for (int x = 0; x < F::NKB; ++x) {
+        for (int x = 0; x < F::NKB; ++x)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) out[(long long)(x * 16 + g4 + e) * adv + dv0 + w * 16 + n16] = R[x][e];
-        }
+            for (int j = 0; j < NDW; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    out[(long long)(x * 16 + g4 + e) * adv + dv0 + (w * NDW + j) * 16 + n16] = R[x * NDW + j][e];
     }
 }
 
 // Chunks of 128 tokens run as 64-token sub-chunks: the chunkwise recurrence gives the same result for any
 // chunk size (up to rounding), and 64-token tiles keep all of P in registers.
-// Workgroups of 256 threads (4 waves, d_v tiles of 64), or of 512 (8 waves, d_v tiles of 128) where d_k is 256:
-// one d_v tile's products are d_k-deep, so a wider tile shares the scores and the q/k staging among twice the
-// columns, and two waves per SIMD hide each other's latencies.
-template <int DK, int C, int NT = (DK >= 256 ? 512 : 256)>
+// Workgroups of 256 threads (4 waves, d_v tiles of 64), or d_v tiles of 128 where d_k is 256: one d_v tile's
+// products are d_k-deep, so a wider tile shares the scores and the q/k staging among twice the columns. The
+// wider tile is either 8 waves of 16 columns (two waves per SIMD hide each other's latencies) or 4 waves of
+// NDW = 2 blocks of 16 columns (each Q', K' or P fragment read from LDS feeds two MFMAs).
+template <int DK, int C, int NT = (DK >= 256 ? 512 : 256), int NDW = 1>
 ChunkKernels chunk_entry_bf16() {
-    constexpr int CI = C > 64 ? 64 : C, DVT = 16 * NT / 64;
+    constexpr int CI = C > 64 ? 64 : C, DVT = 16 * (NT / 64) * NDW;
     ChunkKernels k{};
-    k.fused = chunk_fused_bf16<DK, CI, DVT, false, NT>;
-    k.fused_pre = chunk_fused_bf16<DK, CI, DVT, true, NT>;
+    k.fused = chunk_fused_bf16<DK, CI, DVT, false, NT, NDW>;
+    k.fused_pre = chunk_fused_bf16<DK, CI, DVT, true, NT, NDW>;
     k.dvt = DVT;
     k.threads = NT;
-    // 512-thread workgroups run one per CU: one workgroup per CU in total measured fastest (fewer, longer
-    // segments); 256-thread ones two per CU, with two rounds of them.
-    k.target_wgs = NT >= 512 ? 256 : 1024;
+    // d_v tiles of 128 run one workgroup per CU: one workgroup per CU in total measured fastest (fewer, longer
+    // segments); 256-thread ones with 16-column waves two per CU, with two rounds of them.
+    k.target_wgs = NT * NDW >= 512 ? 256 : 1024;
     return k;
 }
 

@@ -1,7 +1,10 @@
-// bf16-input chunkwise kernels, d_k in {256}, chunk in {32, 64, 128}: workgroups of 512 threads with d_v tiles
-// of 128 where d_v allows it (RET_DK256_THREADS=256 asks for the 256-thread kernels), else 256 threads with
-// d_v tiles of 64.
+// bf16-input chunkwise kernels, d_k in {256}, chunk in {32, 64, 128}. Where d_v is a multiple of 128 the d_v
+// tile is 128 columns: 512 threads whose waves own 16 columns each (the default: two waves per SIMD), or 256
+// threads whose waves own 32 columns each (twice the operand reuse per LDS read, one wave per SIMD).
+// RET_DK256_THREADS picks 512, 256x2, or 256 (the 256-thread kernel with 16-column waves and d_v tiles of 64).
+// Other d_v: 256 threads with d_v tiles of 64.
 #include <stdlib.h>
+#include <string.h>
 
 #include "chunk_bf16.h"
 
@@ -10,11 +13,16 @@ namespace ret {
 bool chunk_kernels_bf16_256(int dk, int dv, int C, ChunkKernels* out) {
     if (dv % 64) return false;
     const char* env = getenv("RET_DK256_THREADS");
-    const bool wide = dv % 128 == 0 && !(env && atoi(env) == 256);
-#define RET_CASE(DKv, Cv)                                                                   \
-    if (dk == DKv && C == Cv) {                                                             \
-        *out = wide ? chunk_entry_bf16<DKv, Cv, 512>() : chunk_entry_bf16<DKv, Cv, 256>(); \
-        return true;                                                                        \
+    int mode = 1;  // 0: 256 threads x 16 columns, 1: 512 x 16, 2: 256 x 32
+    if (env && !strcmp(env, "256")) mode = 0;
+    else if (env && !strcmp(env, "256x2")) mode = 2;
+    if (dv % 128) mode = 0;
+#define RET_CASE(DKv, Cv)                                                                             \
+    if (dk == DKv && C == Cv) {                                                                       \
+        *out = mode == 1   ? chunk_entry_bf16<DKv, Cv, 512>()                                         \
+               : mode == 2 ? chunk_entry_bf16<DKv, Cv, 256, 2>()                                      \
+                           : chunk_entry_bf16<DKv, Cv, 256>();                                        \
+        return true;                                                                                  \
     }
     RET_CASE(256, 32)
     RET_CASE(256, 64)

@@ -117,10 +117,11 @@ def test_chunkwise_small(R, case, monkeypatch):
     assert eo <= tol(dt) and es <= tol(dt), (eo, es)
 
 
-@pytest.mark.parametrize("threads", ["512", "256"])
+@pytest.mark.parametrize("threads", ["256x2", "512", "256"])
 def test_chunkwise_dk256_workgroup_sizes(R, threads, monkeypatch):
-    """d_k 256 runs 512-thread workgroups (d_v tiles of 128) where d_v allows; RET_DK256_THREADS=256 selects the
-    256-thread kernels (d_v tiles of 64). Both match the oracle, with two segments and 3 d_v tiles of 128."""
+    """d_k 256 with d_v tiles of 128 (512 threads whose waves own 16 columns: the default; or 256 threads of 32
+    columns), and the 256-thread kernels with d_v tiles of 64. All match the oracle, with two segments and 3 d_v
+    tiles of 128."""
     monkeypatch.setenv("RET_DK256_THREADS", threads)
     monkeypatch.setenv("RET_SEGMENTS", "2")
     B, N, H, dk, dv, C = 1, 300, 2, 256, 384, 64
@@ -158,10 +159,11 @@ def test_chunkwise_short_segments_either_kernel(R, onchip, monkeypatch):
     assert eo <= tol("bf16") and es <= tol("bf16"), (eo, es)
 
 
-def test_chunkwise_wide_dv_without_workspace(R):
+@pytest.mark.parametrize("dk", [128, 256])
+def test_chunkwise_wide_dv_without_workspace(R, dk):
     """Without a workspace a call runs one segment per (b, h) and rotates q and k while staging, also where a
-    full workspace would hold rotated copies (8 d_v tiles)."""
-    B, N, H, dk, dv, C = 1, 200, 2, 128, 512, 64
+    full workspace would hold rotated copies (8 or 4 d_v tiles)."""
+    B, N, H, dv, C = 1, 200, 2, 512, 64
     print_case("wide_dv_no_workspace", (B, N, H, dk, dv, C))
     rng = np.random.default_rng(31)
     q = W.normal(rng, (B, N, H, dk), 8.0, "bf16")
