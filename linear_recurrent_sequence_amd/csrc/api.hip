@@ -365,13 +365,13 @@ ret_status_t ret_recurrent_step(const void* q, const void* k, const void* v, voi
             A.rc[i] = (float)cos(ang);
             A.rs[i] = (float)sin(ang);
         }
-    int cw = 0, wr = 0;
-    step_kernel_t fn =
-        step_kernel_get(in_dt == RET_BF16, dk, env_int("RET_STEP_CW", 0), env_int("RET_STEP_WR", 0), &cw, &wr);
+    int cw = 0, wr = 0, ppw = 1;
+    step_kernel_t fn = step_kernel_get(in_dt == RET_BF16, dk, dv, B * H, env_int("RET_STEP_CW", 0),
+                                       env_int("RET_STEP_WR", 0), env_int("RET_STEP_PAIRS", 0), &cw, &wr, &ppw);
     if (!fn) return fail(RET_ERR_UNSUPPORTED, "decode step: d_k=%d not in {16,32,64,128,256}", dk);
     hipStream_t s = (hipStream_t)stream;
     LaunchTimer tm("ret_recurrent_step", s);
-    hipLaunchKernelGGL(fn, dim3((dv + cw - 1) / cw, B * H), dim3(64 * (dk / wr)), 0, s, A);
+    hipLaunchKernelGGL(fn, dim3((dv + cw - 1) / cw, (B * H + ppw - 1) / ppw), dim3(64 * (dk / wr) * ppw), 0, s, A);
     tm.done();
     return launch_status("ret_recurrent_step");
 }

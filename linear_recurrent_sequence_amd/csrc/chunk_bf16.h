@@ -13,7 +13,6 @@
 
 namespace ret {
 
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
@@ -275,9 +274,6 @@ __device__ __forceinline__ int chain_ticket(const Chain& ch, int& bc) {
     return seg;
 }
 
-// s_waitcnt immediate that waits until at most n vector memory operations of the wave are outstanding (and
-// for nothing else). Those complete in the order they were issued, so this waits for all but the n latest.
-__host__ __device__ constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) & 3) << 14 | 7 << 4 | 15 << 8; }
 
 // Publishes segment seg's aggregate R (not for a group's last segment, whose flag announces the prefix).
 // `then` may issue NTHEN vector memory operations per thread (loads the caller wants in flight early): they go

@@ -744,54 +744,79 @@ __device__ __forceinline__ void load_n(const typename E::st* p, float* f) {
     }
 }
 
-// One decode step for one (b, h) and CW state columns: NW waves of WR rows each. Lane (rg, cg) of a wave owns
-// columns 4cg..4cg+3 of rows rg*RPT .. +RPT-1 (each row segment one 16-byte access, a row's CW columns
-// contiguous across the cg lanes). q, k, v are read first, then the state rows; each row is updated and
-// written back as soon as it arrives, so loads and stores overlap. o sums q_r S_r over the rows (shuffles
-// within a wave, LDS across waves).
-template <class E, int DK, int CW, int WR>
-__global__ __launch_bounds__(64 * (DK / WR)) void recurrent_step_kernel(StepArgs a) {
+// (b, h) pairs per grouped decode workgroup: as many as fill 8 waves of d_k / wr waves each.
+__host__ __device__ constexpr int step_group_pairs(int dk, int wr) { return dk / wr >= 8 ? 1 : 8 / (dk / wr); }
+
+// One decode step for PPW (b, h) pairs and CW state columns: NW waves of WR rows per pair. Lane (rg, cg) of a wave
+// owns columns 4cg..4cg+3 of rows rg*RPT .. +RPT-1 (each row segment one 16-byte access, a row's CW columns
+// contiguous across the cg lanes). Every address is formed first and every load (q, k, v, the rotation factors,
+// then the state rows) issued before any is waited for; each row is updated and written back as soon as it
+// arrives, so loads and stores overlap. o sums q_r S_r over the rows (shuffles within a wave, LDS across waves).
+// Several pairs share a workgroup of up to 8 waves: fewer, larger workgroups reach the state sooner than many
+// small ones. Pairs past B*H (a partial last workgroup) load the last pair and store nothing.
+template <class E, int DK, int CW, int WR, int PPW>
+__global__ __launch_bounds__(64 * (DK / WR) * PPW) void recurrent_step_kernel(StepArgs a) {
     typedef typename E::st st;
-    constexpr int NW = DK / WR;                 // waves
+    constexpr int NW = DK / WR;                 // waves per pair
     constexpr int CG = CW / 4;                  // column groups of a wave
     constexpr int RG = 64 / CG;                 // row groups of a wave
     constexpr int RPT = WR / RG;                // rows per lane (pairs of rows stay in one lane)
     static_assert(RPT >= 2 && RPT % 2 == 0 && RG * CG == 64, "decode tile");
-    __shared__ float4 part[NW > 1 ? NW : 1][CG];
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    __shared__ float4 part[PPW][NW][CG];
+    const int tid = threadIdx.x, lane = tid & 63, wv = (tid >> 6) % NW, sub = tid / (64 * NW);
     const int cg = lane % CG, rg = lane / CG;
-    const int pair = blockIdx.y, h = pair % a.H;
+    const int npairs = a.B * a.H, dv = a.dv;
+    const int pair_id = blockIdx.y * PPW + sub;
+    const bool live = pair_id < npairs;
+    // wave-uniform: gamma is a scalar read, issued with the kernel arguments
+    const int pair = __builtin_amdgcn_readfirstlane(live ? pair_id : npairs - 1);
+    const float g = a.gamma[pair % a.H];
     const int c0 = blockIdx.x * CW + 4 * cg;
-    const bool active = c0 < a.dv;
+    const bool active = live && c0 < dv;
+    const int cc = c0 < dv ? c0 : 0;    // column of the loads (in range also for idle lanes)
     const int r0 = wv * WR + rg * RPT;  // first row of this lane
+    const st* vp = (const st*)a.v + (long long)pair * dv + cc;
+    const st* qp = (const st*)a.q + (long long)pair * DK + r0;
+    const st* kp = (const st*)a.k + (long long)pair * DK + r0;
+    // The pair's state through one buffer resource: row i of the lane at the lane's offset plus a scalar i*dv*4,
+    // so the RPT loads go out back to back from one address register. Idle lanes point past the resource:
+    // their loads read zeros and their stores are dropped.
+    const int sbytes = DK * dv * 4;
+    const __amdgpu_buffer_rsrc_t srs =
+        __builtin_amdgcn_make_buffer_rsrc(a.state + (long long)pair * DK * dv, (short)0, sbytes, 0x00020000);
+    const int svoff = active ? (r0 * dv + c0) * 4 : sbytes;
     float vv[4], qv[RPT], kv[RPT], rc[RPT / 2], rs[RPT / 2];
-    load_n<E, 4>((const st*)a.v + (long long)pair * a.dv + (active ? c0 : 0), vv);
-    load_n<E, RPT>((const st*)a.q + (long long)pair * a.dk + r0, qv);
-    load_n<E, RPT>((const st*)a.k + (long long)pair * a.dk + r0, kv);
-    if (a.rotate) {
+    load_n<E, 4>(vp, vv);
+    load_n<E, RPT>(qp, qv);
+    load_n<E, RPT>(kp, kv);
 #pragma unroll
-        for (int p = 0; p < RPT / 2; ++p) {
-            rc[p] = a.rc[r0 / 2 + p];
-            rs[p] = a.rs[r0 / 2 + p];
-        }
+    for (int p = 0; p < RPT / 2; ++p) {  // read also without rotation, so that no branch holds them back
+        rc[p] = a.rc[r0 / 2 + p];
+        rs[p] = a.rs[r0 / 2 + p];
     }
-    float* S = a.state + (long long)pair * DK * a.dv + (active ? c0 : 0);
     float4 x[RPT];
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) x[i] = *reinterpret_cast<const float4*>(S + (long long)(r0 + i) * a.dv);
-    if (a.rotate) {
-        // The pair (r0 + 2p, r0 + 2p + 1) turns by the angle pos * theta_(r0/2 + p).
-#pragma unroll
-        for (int p = 0; p < RPT / 2; ++p) {
-            const float c = rc[p], sn = rs[p];
-            const float q0 = qv[2 * p], q1 = qv[2 * p + 1], k0 = kv[2 * p], k1 = kv[2 * p + 1];
-            qv[2 * p] = q0 * c - q1 * sn;
-            qv[2 * p + 1] = q0 * sn + q1 * c;
-            kv[2 * p] = k0 * c - k1 * sn;
-            kv[2 * p + 1] = k0 * sn + k1 * c;
-        }
+    for (int i = 0; i < RPT; ++i) {
+        const f32x4_t t = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(srs, svoff, i * dv * 4, 0));
+        x[i] = make_float4(t[0], t[1], t[2], t[3]);
     }
-    const float g = a.gamma[h];
+    // Every row has arrived before the first state store goes out. The compiler's own waits would otherwise let
+    // later rows' loads be outstanding behind stores, and count on loads and stores completing in issue order,
+    // which holds for loads among themselves only.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __builtin_amdgcn_sched_barrier(0);  // every load above is issued before any of the work below
+    // The pair (r0 + 2p, r0 + 2p + 1) turns by the angle pos * theta_(r0/2 + p); without rotation the inputs
+    // pass unchanged (a select, not a branch: the factor loads stay ahead of the state loads).
+    const bool rot = a.rotate != 0;
+#pragma unroll
+    for (int p = 0; p < RPT / 2; ++p) {
+        const float c = rc[p], sn = rs[p];
+        const float q0 = qv[2 * p], q1 = qv[2 * p + 1], k0 = kv[2 * p], k1 = kv[2 * p + 1];
+        qv[2 * p] = rot ? q0 * c - q1 * sn : q0;
+        qv[2 * p + 1] = rot ? q0 * sn + q1 * c : q1;
+        kv[2 * p] = rot ? k0 * c - k1 * sn : k0;
+        kv[2 * p + 1] = rot ? k0 * sn + k1 * c : k1;
+    }
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
@@ -799,7 +824,8 @@ __global__ __launch_bounds__(64 * (DK / WR)) void recurrent_step_kernel(StepArgs
         x[i].y = g * x[i].y + kv[i] * vv[1];
         x[i].z = g * x[i].z + kv[i] * vv[2];
         x[i].w = g * x[i].w + kv[i] * vv[3];
-        if (active) *reinterpret_cast<float4*>(S + (long long)(r0 + i) * a.dv) = x[i];
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, f32x4_t{x[i].x, x[i].y, x[i].z, x[i].w}), srs,
+                                               svoff, i * dv * 4, 0);
         acc.x += qv[i] * x[i].x;
         acc.y += qv[i] * x[i].y;
         acc.z += qv[i] * x[i].z;
@@ -814,13 +840,13 @@ __global__ __launch_bounds__(64 * (DK / WR)) void recurrent_step_kernel(StepArgs
         acc.w += __shfl_xor(acc.w, m);
     }
     if constexpr (NW > 1) {
-        if (rg == 0) part[wv][cg] = acc;
+        if (rg == 0) part[sub][wv][cg] = acc;
         __syncthreads();
         if (wv != 0) return;
         acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int w2 = 0; w2 < NW; ++w2) {
-            const float4 p = part[w2][cg];
+            const float4 p = part[sub][w2][cg];
             acc.x += p.x;
             acc.y += p.y;
             acc.z += p.z;
@@ -828,7 +854,7 @@ __global__ __launch_bounds__(64 * (DK / WR)) void recurrent_step_kernel(StepArgs
         }
     }
     if (rg == 0 && active) {
-        const long long off = (long long)pair * a.dv + c0;
+        const long long off = (long long)pair * dv + c0;
         if (a.out_bf16) {
             *reinterpret_cast<uint2*>((uint16_t*)a.o + off) =
                 make_uint2(pack2_bf16(acc.x, acc.y), pack2_bf16(acc.z, acc.w));
@@ -886,6 +912,9 @@ bool chunk_kernels_bf16_256(int dk, int dv, int C, ChunkKernels* out);     // d_
 bool parallel_kernel_get(bool bf16_in, int dk, int dv, ParKernel* out);
 // Decode kernel for d_k, the state columns per wave `cw` and rows per wave `wr` (0: defaults); null if none.
 // The launch is ceil(d_v / cw) x (B*H) workgroups of 64 * d_k / wr threads.
-step_kernel_t step_kernel_get(bool bf16_in, int dk, int cw, int wr, int* cw_used, int* wr_used);
+// Decode kernel for a (d_k, column tile cw, rows per wave wr) tile, 0 = default; with pairs_mode 0 it groups
+// (b, h) pairs into workgroups of up to 8 waves where B*H leaves a workgroup per CU; 1 / 2 force one / grouped.
+step_kernel_t step_kernel_get(bool bf16_in, int dk, int dv, int npairs, int cw, int wr, int pairs_mode, int* cw_used,
+                              int* wr_used, int* ppw_used);
 
 }  // namespace ret

@@ -103,39 +103,45 @@ bool parallel_kernel_get(bool bf16_in, int dk, int dv, ParKernel* out) {
 
 // Tiles of a decode workgroup: 64, 32 or 16 state columns per wave (more, smaller waves per (b, h) for more
 // memory parallelism) and 64, 32 or 16 rows per wave (several waves per column tile). Every lane keeps at
-// least one pair of rows: rows per lane = wr * cw / 256 >= 2.
+// least one pair of rows: rows per lane = wr * cw / 256 >= 2. Workgroups hold one (b, h) pair, or as many as
+// fill 8 waves (step_group_pairs).
 namespace {
 template <class E, int DK, int CW, int WR>
-step_kernel_t step_pick() {
-    if constexpr (WR <= DK && WR * CW >= 512 && DK / WR <= 16) return recurrent_step_kernel<E, DK, CW, WR>;
+step_kernel_t step_pick(bool grouped) {
+    if constexpr (WR <= DK && WR * CW >= 512 && DK / WR <= 16) {
+        constexpr int G = step_group_pairs(DK, WR);
+        if (grouped && G > 1) return recurrent_step_kernel<E, DK, CW, WR, G>;
+        return recurrent_step_kernel<E, DK, CW, WR, 1>;
+    }
     return nullptr;
 }
 template <class E, int DK, int CW>
-step_kernel_t step_pick_wr(int wr) {
-    if (wr == 16) return step_pick<E, DK, CW, 16>();
-    if (wr == 32) return step_pick<E, DK, CW, 32>();
-    return step_pick<E, DK, CW, 64>();
+step_kernel_t step_pick_wr(int wr, bool grouped) {
+    if (wr == 16) return step_pick<E, DK, CW, 16>(grouped);
+    if (wr == 32) return step_pick<E, DK, CW, 32>(grouped);
+    return step_pick<E, DK, CW, 64>(grouped);
 }
 template <class E, int DK>
-step_kernel_t step_pick_cw(int cw, int wr) {
-    if (cw == 16) return step_pick_wr<E, DK, 16>(wr);
-    if (cw == 32) return step_pick_wr<E, DK, 32>(wr);
-    return step_pick_wr<E, DK, 64>(wr);
+step_kernel_t step_pick_cw(int cw, int wr, bool grouped) {
+    if (cw == 16) return step_pick_wr<E, DK, 16>(wr, grouped);
+    if (cw == 32) return step_pick_wr<E, DK, 32>(wr, grouped);
+    return step_pick_wr<E, DK, 64>(wr, grouped);
 }
 template <class E>
-step_kernel_t step_pick_dk(int dk, int cw, int wr) {
+step_kernel_t step_pick_dk(int dk, int cw, int wr, bool grouped) {
     switch (dk) {
-        case 16: return step_pick_cw<E, 16>(cw, wr);
-        case 32: return step_pick_cw<E, 32>(cw, wr);
-        case 64: return step_pick_cw<E, 64>(cw, wr);
-        case 128: return step_pick_cw<E, 128>(cw, wr);
-        case 256: return step_pick_cw<E, 256>(cw, wr);
+        case 16: return step_pick_cw<E, 16>(cw, wr, grouped);
+        case 32: return step_pick_cw<E, 32>(cw, wr, grouped);
+        case 64: return step_pick_cw<E, 64>(cw, wr, grouped);
+        case 128: return step_pick_cw<E, 128>(cw, wr, grouped);
+        case 256: return step_pick_cw<E, 256>(cw, wr, grouped);
         default: return nullptr;
     }
 }
 }  // namespace
 
-step_kernel_t step_kernel_get(bool bf16_in, int dk, int cw, int wr, int* cw_used, int* wr_used) {
+step_kernel_t step_kernel_get(bool bf16_in, int dk, int dv, int npairs, int cw, int wr, int pairs_mode, int* cw_used,
+                              int* wr_used, int* ppw_used) {
     if (cw == 0) cw = 64;  // defaults: 64 columns x 32 rows per wave (two waves per 64-row tile)
     if (wr == 0) wr = 32;
     if (cw != 16 && cw != 32 && cw != 64) return nullptr;
@@ -145,7 +151,12 @@ step_kernel_t step_kernel_get(bool bf16_in, int dk, int cw, int wr, int* cw_used
     while (wr * cw < 512 && wr < 64 && wr < dk) wr *= 2;
     *cw_used = cw;
     *wr_used = wr;
-    return bf16_in ? step_pick_dk<BF16>(dk, cw, wr) : step_pick_dk<F32>(dk, cw, wr);
+    // Grouped workgroups where they still give every CU one: mode 0 decides, 1 forces one pair, 2 grouping.
+    const int g = step_group_pairs(dk, wr);
+    const long long wgs = (long long)(npairs + g - 1) / g * ((dv + cw - 1) / cw);
+    const bool grouped = g > 1 && (pairs_mode == 2 || (pairs_mode == 0 && wgs >= 256));
+    *ppw_used = grouped ? g : 1;
+    return bf16_in ? step_pick_dk<BF16>(dk, cw, wr, grouped) : step_pick_dk<F32>(dk, cw, wr, grouped);
 }
 
 fwd_kernel_t segment_scan_get() { return segment_scan_kernel; }

@@ -14,6 +14,11 @@ constexpr int kMaxPairs = 128;  // rotation frequencies per head: d_k <= 256
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// s_waitcnt immediate that waits until at most n vector memory operations of the wave are outstanding (and
+// for nothing else). Those complete in the order they were issued, so this waits for all but the n latest.
+__host__ __device__ constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) & 3) << 14 | 7 << 4 | 15 << 8; }
 
 // ---------------------------------------------------------------------------------------------------
 // bf16 <-> fp32. Rounding to bf16 is round-to-nearest-even by the gfx950 packed conversion

@@ -241,16 +241,19 @@ def test_parallel_small(R, dt, dk, dv):
     assert rel_err(to_host(o), ref) <= tol(dt)
 
 
-# decode tiles: state columns and rows per wave (the library widens tiles too small for a shape)
+# decode tiles: state columns and rows per wave (the library widens tiles too small for a shape); pairs "2"
+# forces workgroups of several (b, h) pairs, here with a partial last workgroup (6 pairs)
+@pytest.mark.parametrize("pairs", ["0", "2"])
 @pytest.mark.parametrize("cw,wr", [("16", "64"), ("32", "64"), ("64", "64"), ("32", "32"), ("32", "16"),
                                    ("64", "16")])
 @pytest.mark.parametrize("dt,dk,dv", [("f32", 16, 16), ("f32", 64, 36), ("bf16", 64, 64), ("bf16", 128, 128),
                                       ("bf16", 256, 200)])
-def test_recurrent_steps_small(R, dt, dk, dv, cw, wr, monkeypatch):
+def test_recurrent_steps_small(R, dt, dk, dv, cw, wr, pairs, monkeypatch):
     import torch
-    print_case("recurrent_small", dt, dk, dv, cw, wr)
+    print_case("recurrent_small", dt, dk, dv, cw, wr, pairs)
     monkeypatch.setenv("RET_STEP_CW", cw)
     monkeypatch.setenv("RET_STEP_WR", wr)
+    monkeypatch.setenv("RET_STEP_PAIRS", pairs)
     rng = np.random.default_rng(9)
     B, H, n = 3, 2, 20
     scale = 1.0 if dt == "f32" else 8.0
