@@ -140,6 +140,28 @@ def test_chunkwise_dk256_workgroup_sizes(R, threads, monkeypatch):
 
 
 @pytest.mark.parametrize("onchip", ["1", "0"])
+@pytest.mark.parametrize("pre", ["1", "0"])
+def test_chunkwise_prerotation_either_way(R, pre, onchip, monkeypatch):
+    """q and k rotated once into the workspace (RET_PREROTATE=1) or while staging (0), on a shape with 4 d_v tiles
+    and two segments, in the on-chip and the streaming kernel: all match the oracle."""
+    monkeypatch.setenv("RET_PREROTATE", pre)
+    monkeypatch.setenv("RET_SEG_ONCHIP", onchip)
+    monkeypatch.setenv("RET_SEGMENTS", "2")
+    B, N, H, dk, dv, C = 1, 333, 2, 64, 256, 64
+    print_case("prerotation=%s onchip=%s" % (pre, onchip), (B, N, H, dk, dv, C))
+    rng = np.random.default_rng(83)
+    q = W.normal(rng, (B, N, H, dk), 8.0, "bf16")
+    k = W.normal(rng, (B, N, H, dk), 8.0, "bf16")
+    v = W.normal(rng, (B, N, H, dv), 8.0, "bf16")
+    gamma, theta = W.gamma_schedule(H), W.theta_schedule(dk)
+    o_ref, s_ref = oracle.chunkwise(q, k, v, gamma, C, theta=theta, pos0=21)
+    o, s = _gpu_chunkwise(R, q, k, v, "bf16", gamma, C, theta=theta, pos0=21)
+    eo, es = rel_err(o, o_ref), rel_err(s, s_ref)
+    print("  err o=%.3g state=%.3g" % (eo, es))
+    assert eo <= tol("bf16") and es <= tol("bf16"), (eo, es)
+
+
+@pytest.mark.parametrize("onchip", ["1", "0"])
 def test_chunkwise_short_segments_either_kernel(R, onchip, monkeypatch):
     """Segments of at most 256 tokens: the on-chip kernel (default) and the streaming single-pass kernel
     (RET_SEG_ONCHIP=0) give the oracle's result on the same inputs, with a state handed in and out."""
