@@ -19,18 +19,21 @@ template <int DK, int C, bool PRE>
 struct SegB {
     static constexpr int RT = 256;       // tokens of a segment held on chip
     static constexpr int MAXC = RT / C;  // chunks of a segment
-    static constexpr int LD = 72;        // row pitch of the Q', K' and V tiles: 36 words mod 64 LDS banks
+    // Q' tiles are read as row fragments only: a row pitch of 36 words mod 64 LDS banks serves them. The K'
+    // and V staging tiles, read transposed as well, are Swz tiles.
+    static constexpr int LD = 72;
     static constexpr int NB = C / 16, NKB = DK / 16, KF = C / 32, KK = DK / 32;
     static constexpr int NBUF = 2;       // chunks of loads in flight ahead of the one being staged
     typedef RowTile<C, DK> TQ;           // q and k rows of a chunk
     typedef RowTile<C, 64> TV;           // v rows of the d_v tile
-    static constexpr int TILE = C * LD;
+    static constexpr int TILE = C * LD, KTILE = C * Swz<DK>::LD, VTILE = C * Swz<64>::LD;
     // Q' tiles of the segment, then two K' and two V staging tiles
-    static constexpr int LDS_BYTES = (MAXC + 4) * TILE * 2;
+    static constexpr int LDS_BYTES = (MAXC * TILE + 2 * KTILE + 2 * VTILE) * 2;
     static_assert(DK == 32 || DK == 64, "one d_k slice of at most 64");
     static_assert(C == 32 || C == 64, "chunk tile of 32 or 64 tokens");
     static_assert(LDS_BYTES <= 80 * 1024, "two workgroups per CU");
     static_assert((LD / 2) % 64 == 36, "LDS row pitch");
+    static_assert(VTILE >= TILE, "a V staging tile holds a chunk of bf16 output rows at pitch LD");
 };
 
 template <int DK, int C, bool PRE>
@@ -46,7 +49,9 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_seg_bf16(FwdArgs a) {
     __shared__ double s_theta[DK / 2];
     uint16_t* const sQres = smem;                     // Q' of chunk c at sQres + c * TILE
     uint16_t* const sKst = smem + F::MAXC * F::TILE;  // K' staging tiles 0, 1
-    uint16_t* const sVst = sKst + 2 * F::TILE;        // V staging tiles 0, 1
+    uint16_t* const sVst = sKst + 2 * F::KTILE;       // V staging tiles 0, 1
+    typedef Swz<DK> ZK;
+    typedef Swz<64> ZV;
 
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g4 = 4 * (lane >> 4), n16 = lane & 15;
     const int ntiles = __builtin_amdgcn_readfirstlane(a.dv / 64);
@@ -66,7 +71,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_seg_bf16(FwdArgs a) {
     const int qoff = (qrow * rsk + qseg * 8) * 2;
     const int vrow = tid / TV::SPR, vseg = tid % TV::SPR;
     const int voff = (vrow * rsv + vseg * 8) * 2;
-    const int tro = trp_lane_offset(LD, lane);
+    const int lk_p = ZK::lane_p(lane), lk_t = ZK::lane_trp(lane), lv_t = ZV::lane_trp(lane);
 
     // ---- the segment: the unit's next ticket, so every earlier segment of the unit has started ----
     if constexpr (!PRE)
@@ -165,17 +170,18 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_seg_bf16(FwdArgs a) {
             // Stage chunk c: Q' into its own tile, K' and V into staging tile c % 2 (last read by chunk c - 2,
             // whose products every wave finished before the barrier of chunk c - 1).
             uint16_t* sQ = sQres + c * F::TILE;
-            uint16_t* sK = sKst + (c & 1) * F::TILE;
-            uint16_t* sV = sVst + (c & 1) * F::TILE;
+            uint16_t* sK = sKst + (c & 1) * F::KTILE;
+            uint16_t* sV = sVst + (c & 1) * F::VTILE;
             if constexpr (!PRE)
                 if (c % 8 == 0) rot.cur.eval(a.pos0 + seg_t0 + (long long)c * C + qrow, s_theta, qseg * 4);
 #pragma unroll
             for (int p = 0; p < TQ::NP; ++p)
                 if (TQ::live(qrow, p)) {
                     const int r = (qrow + p * TQ::RP) * LD + qseg * 8;
+                    const int rk = ZK::off(qrow + p * TQ::RP, qseg * 8);
                     if constexpr (PRE) {
                         lds_store16(sQ + r, bq[par][p]);
-                        lds_store16(sK + r, bk[par][p]);
+                        lds_store16(sK + rk, bk[par][p]);
                     } else {
                         float qf[8], kf[8];
                         unpack8(bq[par][p], qf);
@@ -184,13 +190,13 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_seg_bf16(FwdArgs a) {
                         rot.cur.apply(kf);
                         if (p + 1 < TQ::NP) rot.cur.turn(rot.pass);
                         lds_store16(sQ + r, pack8(qf));
-                        lds_store16(sK + r, pack8(kf));
+                        lds_store16(sK + rk, pack8(kf));
                     }
                 }
             if constexpr (!PRE) rot.next_chunk();
 #pragma unroll
             for (int p = 0; p < TV::NP; ++p)
-                if (TV::live(vrow, p)) lds_store16(sV + (vrow + p * TV::RP) * LD + vseg * 8, bv[par][p]);
+                if (TV::live(vrow, p)) lds_store16(sV + ZV::off(vrow + p * TV::RP, vseg * 8), bv[par][p]);
             if constexpr (c + NBUF < F::MAXC) issue(std::integral_constant<int, c + NBUF>{});
             __syncthreads();
 
@@ -200,7 +206,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_seg_bf16(FwdArgs a) {
             bf16x8_t fv[KF], fvz[KF];
 #pragma unroll
             for (int f = 0; f < KF; ++f) {
-                fv[f] = frag_trp(sV, LD, 32 * f, w * 16, tro);
+                fv[f] = frag_trps<64>(sV, 32 * f, w * 16, lv_t);
                 float vf[8];
                 unpack8(__builtin_bit_cast(u32x4_t, fv[f]), vf);
 #pragma unroll
@@ -217,7 +223,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_seg_bf16(FwdArgs a) {
             for (int k = 0; k < KK; ++k) {
                 ra[k] = acc_pair(R[2 * k], R[2 * k + 1]);
 #pragma unroll
-                for (int lb = 0; lb < NB; ++lb) kf[k][lb] = frag_p(sK + lb * 16 * LD, LD, 32 * k, lane);
+                for (int lb = 0; lb < NB; ++lb) kf[k][lb] = frag_ps<DK>(sK, lb * 16, 32 * k, lk_p);
             }
             // Per query block x: S^T tiles (x, lb <= x) = K' Q'^T, the cross term O^T = R^T Q'^T, then
             // O^T = xi (.) O^T + V^T P^T with P = mask (.) S from the S^T accumulators as the B operand (keys
@@ -255,7 +261,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_seg_bf16(FwdArgs a) {
 #pragma unroll
             for (int f = 0; f < KF; ++f)
 #pragma unroll
-                for (int x = 0; x < F::NKB; ++x) mfma(R[x], frag_trp(sK, LD, 32 * f, x * 16, tro), fvz[f]);
+                for (int x = 0; x < F::NKB; ++x) mfma(R[x], frag_trps<DK>(sK, 32 * f, x * 16, lk_t), fvz[f]);
         }
     });
 
@@ -265,7 +271,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_seg_bf16(FwdArgs a) {
     chain_enter<F::NKB, kThreads, false>(ch, seg, anseg, gpow(lg, (float)aseg_len), R, Rin, s_word);
 
     // ---- the chain's term, then the outputs: O_c += xi (.) gamma^(cC) (Q'_c R_in) ----
-    // bf16 outputs leave through the K' staging tiles (free by now; chunk c uses tile c % 2, last read before the
+    // bf16 outputs leave through the V staging tiles (free by now; chunk c uses tile c % 2, last read before the
     // barrier of chunk c - 1) as whole rows: each wave writes its O^T tiles as rows of O, then 8 lanes store one
     // row's 64 d_v (128 bytes) with one 16-byte store each, instead of four waves writing 32-byte pieces of it.
     auto store_rows = [&](int c, const f32x4_t* O, uint16_t* buf) __attribute__((always_inline)) {
@@ -300,7 +306,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_seg_bf16(FwdArgs a) {
                 }
             }
             if (a.out_bf16)
-                store_rows(c, Op[c], sKst + (c & 1) * F::TILE);
+                store_rows(c, Op[c], sVst + (c & 1) * F::VTILE);
             else
                 store_out(c, Op[c]);
         }
