@@ -10,8 +10,9 @@ values), and returns float64 results:
     q, k   [B, N, H, dk]      v, o   [B, N, H, dv]      state  [B, H, dk, dv]
     gamma  [H]                theta  [dk // 2] or None (no rotation)
 
-Sources: "Hybrid Architectures: RetNet and the Three Computation Paradigms" (sections 2-7) and the RetNet
-paper summary (Eq. 5, 6 and 7). Which function follows which equation is stated in the C file.
+Sources: "Hybrid Architectures: RetNet and the Three Computation Paradigms" (sections 2-9) and the RetNet
+paper summary (Eq. 5, 6 and 7; "Gating mechanism"; "Retention Score Normalization"). Which function follows
+which passage is stated in the C file.
 """
 from __future__ import annotations
 
@@ -50,7 +51,10 @@ def _load():
     lib.orc_parallel_rows.argtypes = [P, P, P, I, I, I, I, I, P, P, LL, ctypes.POINTER(LL), I, P, I]
     lib.orc_recurrent.argtypes = [P, P, P, P, I, I, I, I, I, P, P, LL, P, P, I]
     lib.orc_chunkwise.argtypes = [P, P, P, P, I, I, I, I, I, P, P, LL, I, P, P, I]
-    for f in (lib.orc_parallel, lib.orc_parallel_rows, lib.orc_recurrent, lib.orc_chunkwise):
+    lib.orc_parallel_normalized.argtypes = [P, P, P, P, I, I, I, I, I, P, P, LL, I, I]
+    lib.orc_msr_epilogue.argtypes = [P, P, P, P, P, LL, I, I, ctypes.c_double]
+    for f in (lib.orc_parallel, lib.orc_parallel_rows, lib.orc_recurrent, lib.orc_chunkwise,
+              lib.orc_parallel_normalized, lib.orc_msr_epilogue):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -103,6 +107,35 @@ def parallel(q, k, v, gamma, theta=None, pos0=0, threads=None):
                               int(pos0), threads or default_threads())
     _check(rc, "parallel")
     return o
+
+
+def parallel_normalized(q, k, v, gamma, theta=None, pos0=0, scale=False, decay=False, scores=False, threads=None):
+    """Parallel form with the score normalizations (blog section 8.5; paper summary, "Retention Score
+    Normalization"): QK^T / sqrt(d_k) (scale), D~ rows (decay), R~ rows (scores)."""
+    q, k, v, g, th, (B, N, H, dk, dv) = _common(q, k, v, gamma, theta)
+    o = np.zeros((B, N, H, dv), np.float64)
+    norm = (1 if scale else 0) | (2 if decay else 0) | (4 if scores else 0)
+    rc = _load().orc_parallel_normalized(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, N, H, dk, dv, _ptr(g), _ptr(th),
+                                         int(pos0), norm, threads or default_threads())
+    _check(rc, "parallel_normalized")
+    return o
+
+
+def msr_epilogue(o, gate=None, weight=None, bias=None, eps=1e-5):
+    """y = swish(gate) (.) GroupNorm_h(o) (blog sections 8.4 and 9.1; paper summary, "Gating mechanism").
+    o, gate: [..., H, dv] (any leading shape: tokens); weight, bias: [H*dv] or None; one group per head."""
+    o = _f64(o)
+    H, dv = o.shape[-2], o.shape[-1]
+    rows = int(np.prod(o.shape[:-2], dtype=np.int64))
+    g = None if gate is None else _f64(gate)
+    if g is not None and g.shape != o.shape:
+        raise ValueError("gate must have the shape of o")
+    w = None if weight is None else _f64(np.reshape(weight, (H * dv,)))
+    b = None if bias is None else _f64(np.reshape(bias, (H * dv,)))
+    y = np.zeros(o.shape, np.float64)
+    rc = _load().orc_msr_epilogue(_ptr(o), _ptr(g), _ptr(w), _ptr(b), _ptr(y), rows, H, dv, float(eps))
+    _check(rc, "msr_epilogue")
+    return y
 
 
 def parallel_rows(q, k, v, gamma, rows, theta=None, pos0=0, threads=None):

@@ -10,7 +10,11 @@
  *   - the parallel form   O = (Q K^T (.) D) V,  D[n][m] = gamma^(n-m) for n >= m, else 0;
  *   - the recurrent form  S_n = gamma S_{n-1} + k_n^T v_n,  o_n = q_n S_n  (update, then read);
  *   - the chunkwise form  O_[i] = (Q_[i] K_[i]^T (.) D) V_[i] + (Q_[i] R_{i-1}) (.) xi,
- *                         R_i = gamma^L R_{i-1} + K_[i]^T (V_[i] (.) zeta).
+ *                         R_i = gamma^L R_{i-1} + K_[i]^T (V_[i] (.) zeta);
+ *   - the parallel form with the retention score normalizations (blog section 8.5; paper summary,
+ *     "Retention Score Normalization"): QK^T / sqrt(d_k), D~ and R~;
+ *   - the multi-scale retention epilogue (blog sections 8.4 and 9.1; paper summary, "Gating mechanism"):
+ *     y = swish(g) (.) GroupNorm_h(o), with g = X W_G given.
  *
  * Readings where the pages leave a step open (each is also listed in the design notes):
  *   - the rotation turns pair (x_{2i}, x_{2i+1}) of BOTH q and k by +p*theta_i, then a real dot product
@@ -100,7 +104,8 @@ typedef struct {
     int nrows;
     int B, N, H, dk, dv, chunk;
     long long pos0;
-    int form; /* 0 parallel, 1 recurrent, 2 chunkwise, 3 parallel rows */
+    int form; /* 0 parallel, 1 recurrent, 2 chunkwise, 3 parallel rows, 4 normalized parallel */
+    int norm; /* normalized parallel form: ORC_NORM_* flags */
     int nthreads, tid;
     int status;
 } job;
@@ -109,6 +114,7 @@ static int form_parallel(job* J, int b, int h);
 static int form_recurrent(job* J, int b, int h);
 static int form_chunkwise(job* J, int b, int h);
 static int form_parallel_rows(job* J, int b, int h);
+static int form_parallel_norm(job* J, int b, int h);
 
 static void* worker(void* arg) {
     job* J = (job*)arg;
@@ -119,6 +125,7 @@ static void* worker(void* arg) {
             case 0: rc = form_parallel(J, b, h); break;
             case 1: rc = form_recurrent(J, b, h); break;
             case 2: rc = form_chunkwise(J, b, h); break;
+            case 4: rc = form_parallel_norm(J, b, h); break;
             default: rc = form_parallel_rows(J, b, h); break;
         }
         if (rc) J->status = rc;
@@ -193,6 +200,56 @@ static int form_parallel_rows(job* J, int b, int h) {
         double* o = J->o + (((size_t)b * J->nrows + r) * J->H + h) * (size_t)J->dv;
         parallel_row(&hs, J->dk, J->dv, J->gamma[h], (int)n, o);
     }
+    free_head(&hs);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------------------ */
+/* Parallel form with the score normalizations (blog section 8.5; paper summary, "Retention Score     */
+/* Normalization"), each switched on by a flag, applied in the pages' order:                         */
+/*   1. QK^T is divided by sqrt(d_k) (the pages' d is the q/k head dimension: the attention scaling); */
+/*   2. row n of the decay matrix is divided by the square root of its sum over the sequence so far:   */
+/*      D~[n][m] = D[n][m] / sqrt(sum_{i<=n} D[n][i]), 0-indexed;                                      */
+/*   3. R = (scaled QK^T) (.) D (or D~); row n is divided by max(|sum_m R[n][m]|, 1).                   */
+/* Output o_n = sum_m R~[n][m] v_m. Every factor is a scalar per (token, head).                      */
+/* ------------------------------------------------------------------------------------------------ */
+
+#define ORC_NORM_SCALE 1
+#define ORC_NORM_DECAY 2
+#define ORC_NORM_SCORES 4
+
+static int form_parallel_norm(job* J, int b, int h) {
+    head_seq hs;
+    const int N = J->N, dk = J->dk, dv = J->dv;
+    const double gamma = J->gamma[h];
+    double* w = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+    if (!w || load_head(&hs, J->q, J->k, J->v, N, J->H, dk, dv, b, h, J->theta, J->pos0)) {
+        free(w);
+        free_head(&hs);
+        return -3;
+    }
+    for (int n = 0; n < N; ++n) {
+        double dsum = 0.0; /* sum_{i<=n} D[n][i] */
+        for (int i = 0; i <= n; ++i) dsum += pow(gamma, (double)(n - i));
+        double rsum = 0.0;
+        for (int m = 0; m <= n; ++m) {
+            double qk = dot(hs.Qr + (size_t)n * dk, hs.Kr + (size_t)m * dk, dk);
+            if (J->norm & ORC_NORM_SCALE) qk /= sqrt((double)dk);
+            double D = pow(gamma, (double)(n - m));
+            if (J->norm & ORC_NORM_DECAY) D /= sqrt(dsum);
+            w[m] = qk * D;
+            rsum += w[m];
+        }
+        double den = 1.0;
+        if (J->norm & ORC_NORM_SCORES) den = fabs(rsum) > 1.0 ? fabs(rsum) : 1.0;
+        double* o = out_row(J->o, N, J->H, dv, b, n, h);
+        for (int j = 0; j < dv; ++j) o[j] = 0.0;
+        for (int m = 0; m <= n; ++m) {
+            const double* vm = hs.Vh + (size_t)m * dv;
+            for (int j = 0; j < dv; ++j) o[j] += (w[m] / den) * vm[j];
+        }
+    }
+    free(w);
     free_head(&hs);
     return 0;
 }
@@ -319,6 +376,61 @@ int orc_parallel(const double* q, const double* k, const double* v, double* o, i
     J.q = q; J.k = k; J.v = v; J.o = o; J.gamma = gamma; J.theta = theta;
     J.B = B; J.N = N; J.H = H; J.dk = dk; J.dv = dv; J.pos0 = pos0; J.form = 0; J.nthreads = nthreads;
     return run(J);
+}
+
+/* The parallel form with the score normalizations selected by norm (ORC_NORM_* flags). */
+int orc_parallel_normalized(const double* q, const double* k, const double* v, double* o, int B, int N, int H,
+                            int dk, int dv, const double* gamma, const double* theta, long long pos0, int norm,
+                            int threads) {
+    if (check_args(B, N, H, dk, dv, gamma, theta) || !q || !k || !v || !o || norm < 0 || norm > 7) return -1;
+    job J;
+    memset(&J, 0, sizeof(J));
+    J.q = q;
+    J.k = k;
+    J.v = v;
+    J.o = o;
+    J.gamma = gamma;
+    J.theta = theta;
+    J.B = B;
+    J.N = N;
+    J.H = H;
+    J.dk = dk;
+    J.dv = dv;
+    J.pos0 = pos0;
+    J.form = 4;
+    J.norm = norm;
+    J.nthreads = threads;
+    return run(J);
+}
+
+/* Multi-scale retention epilogue (blog sections 8.4 and 9.1; paper summary, "Gating mechanism"):
+ *   y = swish(g) (.) GroupNorm_h(o).
+ * o, g, y: [rows][H][dv] (rows = B*N tokens, or B for one decode step). GroupNorm has one group per head:
+ * each (row, head) vector of dv values is standardized by its own mean and biased variance,
+ * (x - mean) / sqrt(var + eps), then multiplied by weight[h*dv + c] and shifted by bias[h*dv + c] (either
+ * NULL: 1 and 0). swish(x) = x sigmoid(x). g NULL: no gate. y may equal o. */
+int orc_msr_epilogue(const double* o, const double* g, const double* weight, const double* bias, double* y,
+                     long long rows, int H, int dv, double eps) {
+    if (!o || !y || rows < 0 || H <= 0 || dv <= 0 || !(eps >= 0.0)) return -1;
+    for (long long r = 0; r < rows; ++r)
+        for (int h = 0; h < H; ++h) {
+            const size_t base = ((size_t)r * H + h) * (size_t)dv;
+            double mean = 0.0, var = 0.0;
+            for (int c = 0; c < dv; ++c) mean += o[base + c];
+            mean /= dv;
+            for (int c = 0; c < dv; ++c) var += (o[base + c] - mean) * (o[base + c] - mean);
+            var /= dv;
+            const double inv = 1.0 / sqrt(var + eps);
+            for (int c = 0; c < dv; ++c) {
+                double z = (o[base + c] - mean) * inv;
+                const size_t ch = (size_t)h * dv + c;
+                if (weight) z *= weight[ch];
+                if (bias) z += bias[ch];
+                if (g) z *= g[base + c] / (1.0 + exp(-g[base + c]));
+                y[base + c] = z;
+            }
+        }
+    return 0;
 }
 
 int orc_parallel_rows(const double* q, const double* k, const double* v, int B, int N, int H, int dk, int dv,

@@ -38,9 +38,16 @@ MUTANTS = {
     "parallel_decay_exponent": ("pow(gamma, (double)(n - m))", "pow(gamma, (double)(n - m + 1))"),
     "transposed_state_read": ("const double* Ri = R + (size_t)i * dv;", "const double* Ri = R + (size_t)i;"),
     "position_origin": ("theta, pos0 + n);\n        gather_plain", "theta, n);\n        gather_plain"),
+    "groupnorm_unbiased_variance": ("var /= dv;", "var /= (dv - 1);"),
+    "groupnorm_eps_dropped": ("const double inv = 1.0 / sqrt(var + eps);", "const double inv = 1.0 / sqrt(var);"),
+    "groupnorm_mean_kept": ("double z = (o[base + c] - mean) * inv;", "double z = o[base + c] * inv;"),
+    "swish_sign": ("(1.0 + exp(-g[base + c]))", "(1.0 + exp(g[base + c]))"),
+    "decay_norm_without_root": ("D /= sqrt(dsum);", "D /= dsum;"),
+    "score_norm_without_abs": ("den = fabs(rsum) > 1.0 ? fabs(rsum) : 1.0;", "den = rsum > 1.0 ? rsum : 1.0;"),
+    "score_scale_by_dv": ("qk /= sqrt((double)dk);", "qk /= sqrt((double)dv);"),
 }
 
-PIN_TESTS = ["test_oracle_pins.py", "test_oracle_forms.py"]
+PIN_TESTS = ["test_oracle_pins.py", "test_oracle_forms.py", "test_oracle_epilogue.py"]
 
 
 def _run_pins_against(src_text, tmp_path):
