@@ -4,11 +4,12 @@
 A step is one ret_chunkwise_fwd call over the d_model=512 retention-layer workload (B=8, N=2048, H=8,
 d_k=d_v=64, chunk 64, bf16 inputs/outputs, xPos rotation, fp32 state out): tokens/s = B*N / step time,
 with inputs resident in HBM. The same JSON line carries the batched-decode workload (B=128, H=8, d=64,
-fp32 state, 1024 single-token ret_recurrent_step calls replayed from a HIP graph) in steps/s, the roofline
-of each path's dominant kernel (per-launch HIP-event durations recorded by the library over the timed
-region), and the fp64 CPU oracle timed on this host.
+fp32 state, 1024 single-token ret_recurrent_step calls replayed from a HIP graph) in steps/s, the
+multi-scale retention epilogue (GroupNorm per head and swish gate) on the chunkwise output, alone and after
+the chunkwise call, the roofline of each path's dominant kernel (per-launch HIP-event durations recorded by
+the library over the timed region), and the fp64 CPU oracle timed on this host.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2|4|5] [--no-decode]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-decode] [--no-epilogue]
                        [--no-cpu-baseline] [--copy-calibration] [--decode-steps S]
 """
 from __future__ import annotations
@@ -137,6 +138,69 @@ def bench_chunkwise(R, W, torch, wid, steps, warmup):
     return w, ms_step, ms_clean, ms_graph, kernels, ws
 
 
+def graph_ms(torch, fn, steps):
+    """Milliseconds per call of `steps` calls of fn captured into one HIP graph and replayed (HIP events on the
+    replay stream)."""
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(steps):
+                fn()
+    torch.cuda.current_stream().wait_stream(s)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def bench_epilogue(R, W, torch, wid, steps):
+    """The multi-scale retention epilogue y = swish(gate) (.) GroupNorm_h(o) (per-channel affine; bf16 o, gate
+    and y) on the chunkwise workload's output: alone, and as the layer without its projections, both as
+    ret_chunkwise_msr_fwd (fused into the output stores where the kernel allows) and as two calls."""
+    import numpy as np
+    w = W.WORKLOADS[wid]
+    q, k, v, rng = W.make_qkv(w)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).cuda()
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    gate = dev(W.normal(rng, (w.B, w.N, w.H, w.dv), 1.0, "bf16"))
+    del q, k, v
+    gw = torch.from_numpy(rng.uniform(0.5, 1.5, w.H * w.dv).astype(np.float32)).cuda()
+    gb = torch.from_numpy((0.1 * rng.standard_normal(w.H * w.dv)).astype(np.float32)).cuda()
+    o = torch.empty((w.B, w.N, w.H, w.dv), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty_like(o)
+    ws = R.chunkwise_workspace(qd, vd, w.chunk)
+    chunk = lambda: R.ret_chunkwise_fwd(qd, kd, vd, o, w.gamma, w.chunk, theta=w.theta, workspace=ws)
+    epi = lambda: R.ret_msr_epilogue(o, y, gate=gate, gn_weight=gw, gn_bias=gb, eps=1e-5)
+    layer = lambda: R.ret_chunkwise_msr_fwd(qd, kd, vd, y, w.gamma, w.chunk, gate=gate, gn_weight=gw, gn_bias=gb,
+                                            eps=1e-5, theta=w.theta, workspace=ws)
+    chunk()
+    ms_epi = graph_ms(torch, epi, steps)
+    ms_layer2 = graph_ms(torch, lambda: (chunk(), epi()), steps)
+    ms_layer = graph_ms(torch, layer, steps)
+    R.ret_chunkwise_check(ws)
+    nbytes = 3 * o.numel() * 2 + 2 * w.H * w.dv * 4  # o and gate read, y written (bf16); weight and bias
+    ach = nbytes / (ms_epi * 1e-3) / 1e9
+    return {
+        "workload": "%s output: [%d, %d, %d, %d] bf16 o, gate and y, fp32 per-channel affine"
+                    % (w.name, w.B, w.N, w.H, w.dv),
+        "us_per_call": 1e3 * ms_epi,
+        "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                     "traffic": load_traffic("ret_msr_epilogue", w.name), "kernel": "ret_msr_epilogue",
+                     "kernel_avg_us": 1e3 * ms_epi, "alg_bytes_per_launch": nbytes},
+        "layer_us_per_call": 1e3 * ms_layer,
+        "layer_tokens_per_s": w.B * w.N / (ms_layer * 1e-3),
+        "layer_two_calls_us_per_call": 1e3 * ms_layer2,
+    }
+
+
 def bench_decode(R, W, torch, steps_graph=1024, reps=3):
     import numpy as np
     w = W.WORKLOADS[3]
@@ -233,6 +297,7 @@ def main():
     ap.add_argument("--workload", default="retention-layer-d512", choices=sorted(CHUNK_WORKLOADS),
                     help="chunkwise workload timed for `value`")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-epilogue", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=1024, help="decode steps per graph (1024 in the workload)")
@@ -309,6 +374,8 @@ def main():
                          "kernel": "ret_recurrent_step", "kernel_avg_us": kernel_us, "alg_bytes_per_launch": db},
             "step_hbm_frac": db / (us_step * 1e-6) / 1e9 / HBM_PEAK_GBS,
         }
+    if not args.no_epilogue:
+        result["epilogue"] = bench_epilogue(R, W, torch, wid, args.steps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(W, wid)
     result["context"] = ("pages' figures (whole 6.7B model, A100-80GB, vanilla PyTorch): 8.4x faster decoding and "

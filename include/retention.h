@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define RET_ABI_VERSION 1
+#define RET_ABI_VERSION 2
 
 typedef enum { RET_F32 = 0, RET_BF16 = 1 } ret_dtype_t;
 
@@ -127,12 +127,47 @@ ret_status_t ret_recurrent_step(const void* q, const void* k, const void* v, voi
                                 const double* theta, int64_t pos, void* stream);
 
 /*
+ * Multi-scale retention epilogue ("Hybrid Architectures: RetNet and the Three Computation Paradigms",
+ * sections 8.4 and 9.1; paper summary, "Gating mechanism"):
+ *     y = swish(gate) (.) GroupNorm_h(o),   swish(x) = x * sigmoid(x)
+ * o, gate, y: [rows, H, d_v] device arrays, row-major (rows = B*N tokens of a chunkwise or parallel call, or B
+ * for one decode step). GroupNorm has one group per head: each (row, head) vector of d_v values is
+ * standardized by its own mean and biased variance, (x - mean) / sqrt(var + eps), then multiplied by
+ * gn_weight[h * d_v + c] and shifted by gn_bias[h * d_v + c] (device float[H * d_v] each; NULL means 1 and 0).
+ * gate: the gate projection X W_G, or NULL for no gate; the projections themselves are the caller's.
+ * o_dt, gate_dt, y_dt: F32 or BF16 each. y may equal o or gate (in place); other overlaps are not allowed.
+ * Every pointer 16-byte aligned. rows = 0 does nothing. Supported: d_v in {16, 32, 64, 128, 256, 512} and
+ * rows * H < 2^31.
+ * eps >= 0 and finite (RET_ERR_INVALID_ARG otherwise). Asynchronous on `stream`.
+ */
+ret_status_t ret_msr_epilogue(const void* o, const void* gate, const float* gn_weight, const float* gn_bias,
+                              void* y, int64_t rows, int H, int dv, ret_dtype_t o_dt, ret_dtype_t gate_dt,
+                              ret_dtype_t y_dt, float eps, void* stream);
+
+/*
+ * Chunkwise retention followed by the multi-scale retention epilogue, into y [B, N, H, d_v]:
+ *     y = swish(gate) (.) GroupNorm_h(O),   O = ret_chunkwise_fwd's output, rounded to out_dt
+ * Arguments as ret_chunkwise_fwd (with y in the place of o) and ret_msr_epilogue (gate [B, N, H, d_v] or
+ * NULL, gate_dt, gn_weight, gn_bias, eps). Where the kernel holds whole head rows (bf16 input and output,
+ * d_v = 64, the on-chip kernel: segments of at most 256 tokens) the epilogue is applied before the outputs are
+ * stored, which saves writing and reading O; otherwise ret_msr_epilogue runs over y in place. Either way the
+ * result equals the two calls in sequence up to rounding. gate must not alias q, k, v or y. Every check of
+ * either call is made before anything is launched, except those of the chunkwise plan itself.
+ */
+ret_status_t ret_chunkwise_msr_fwd(const void* q, const void* k, const void* v, const void* gate, void* y, int B,
+                                   int N, int H, int dk, int dv, ret_dtype_t in_dt, ret_dtype_t out_dt,
+                                   ret_dtype_t gate_dt, const float* gamma, const double* theta, int64_t pos0,
+                                   int chunk, const float* state_in, float* state_out, const float* gn_weight,
+                                   const float* gn_bias, float eps, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+/*
  * Kernel timing for measurement tools. While enabled, every kernel the library launches is bracketed by a
  * pair of HIP events on the launch stream. ret_timing_query synchronises those events and returns the total
  * milliseconds and launch count recorded for kernels whose name equals `kernel` ("" or NULL = all).
  * ret_timing_reset drops the records. Kernel names: "ret_chunk_seg", "ret_chunk_fused" and "ret_rotate_qk"
  * (bf16 input), "ret_chunk_full", "ret_chunk_local", "ret_segment_scan" (fp32 input), "ret_parallel",
- * "ret_recurrent_step". Not for use while kernels are being captured into a graph.
+ * "ret_recurrent_step", "ret_msr_epilogue". Not for use while kernels are being captured into a graph.
  */
 int ret_timing_enable(int on);
 int ret_timing_query(const char* kernel, double* total_ms, int64_t* launches);

@@ -253,10 +253,25 @@ size_t ret_chunkwise_workspace_bytes(int B, int N, int H, int dk, int dv, int ch
     return p.chain_bytes + p.rot_bytes;
 }
 
-ret_status_t ret_chunkwise_fwd(const void* q, const void* k, const void* v, void* o, int B, int N, int H, int dk,
-                               int dv, ret_dtype_t in_dt, ret_dtype_t out_dt, const float* gamma,
-                               const double* theta, int64_t pos0, int chunk, const float* state_in,
-                               float* state_out, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The epilogue a chunkwise call may fuse into its output stores.
+struct EpiRequest {
+    const void* gate;
+    ret_dtype_t gate_dt;
+    const float *weight, *bias;
+    float eps;
+};
+
+// ret_chunkwise_fwd's work. With `epi`, the kernel applies the epilogue to the outputs before storing them where
+// it holds whole head rows (the on-chip kernel with bf16 output and d_v = 64), and *fused says whether it did.
+ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o, int B, int N, int H, int dk,
+                           int dv, ret_dtype_t in_dt, ret_dtype_t out_dt, const float* gamma, const double* theta,
+                           int64_t pos0, int chunk, const float* state_in, float* state_out, void* workspace,
+                           size_t workspace_bytes, void* stream, const EpiRequest* epi, bool* fused) {
+    if (fused) *fused = false;
     ret_status_t st = check_common(q, k, v, o, B, N, H, dk, dv, in_dt, out_dt, gamma, theta);
     if (st != RET_OK) return st;
     if (chunk <= 0) return fail(RET_ERR_INVALID_ARG, "chunk must be positive (got %d)", chunk);
@@ -308,6 +323,15 @@ ret_status_t ret_chunkwise_fwd(const void* q, const void* k, const void* v, void
         }
         const unsigned grid = (unsigned)((long long)nseg * B * H * ntiles);
         const int threads = onchip || !ck.threads ? kThreads : ck.threads;
+        if (epi && onchip && out_dt == RET_BF16 && dv == 64) {
+            A.epi = 1;
+            A.gate = epi->gate;
+            A.gate_bf16 = epi->gate_dt == RET_BF16;
+            A.gn_weight = epi->weight;
+            A.gn_bias = epi->bias;
+            A.eps = epi->eps;
+            if (fused) *fused = true;
+        }
         LaunchTimer tm(name, s);
         hipLaunchKernelGGL(fn, dim3(grid), dim3(threads), 0, s, A);
         tm.done();
@@ -333,6 +357,46 @@ ret_status_t ret_chunkwise_fwd(const void* q, const void* k, const void* v, void
     hipLaunchKernelGGL(ck.full, dim3(nseg, ntiles, B * H), dim3(kThreads), 0, s, A);
     tm.done();
     return launch_status("ret_chunk_full");
+}
+
+}  // namespace
+
+extern "C" {
+
+ret_status_t ret_chunkwise_fwd(const void* q, const void* k, const void* v, void* o, int B, int N, int H, int dk,
+                               int dv, ret_dtype_t in_dt, ret_dtype_t out_dt, const float* gamma,
+                               const double* theta, int64_t pos0, int chunk, const float* state_in,
+                               float* state_out, void* workspace, size_t workspace_bytes, void* stream) {
+    return chunkwise_run(q, k, v, o, B, N, H, dk, dv, in_dt, out_dt, gamma, theta, pos0, chunk, state_in, state_out,
+                         workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+ret_status_t ret_chunkwise_msr_fwd(const void* q, const void* k, const void* v, const void* gate, void* y, int B,
+                                   int N, int H, int dk, int dv, ret_dtype_t in_dt, ret_dtype_t out_dt,
+                                   ret_dtype_t gate_dt, const float* gamma, const double* theta, int64_t pos0,
+                                   int chunk, const float* state_in, float* state_out, const float* gn_weight,
+                                   const float* gn_bias, float eps, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+    // The epilogue's own checks first, so that nothing is launched for a call that would fail half way.
+    if (gate_dt != RET_F32 && gate_dt != RET_BF16) return fail(RET_ERR_INVALID_ARG, "bad gate dtype %d", (int)gate_dt);
+    if (!(eps >= 0.f) || !isfinite(eps)) return fail(RET_ERR_INVALID_ARG, "eps=%g must be finite and >= 0", eps);
+    if ((gate && !aligned16(gate)) || (gn_weight && !aligned16(gn_weight)) || (gn_bias && !aligned16(gn_bias)))
+        return fail(RET_ERR_INVALID_ARG, "gate/gn_weight/gn_bias must be 16-byte aligned");
+    int gpw = 0;
+    if (!epilogue_kernel_get(dv, &gpw))
+        return fail(RET_ERR_UNSUPPORTED, "epilogue: d_v=%d not in {16,32,64,128,256,512}", dv);
+    if (gate && (gate == q || gate == k || gate == v || gate == y))
+        return fail(RET_ERR_INVALID_ARG, "gate must not alias q, k, v or y");
+    if ((long long)B * N * H > 0x7fffffffLL)
+        return fail(RET_ERR_UNSUPPORTED, "epilogue: B*N*H=%lld exceeds 2^31 groups", (long long)B * N * H);
+    const EpiRequest epi{gate, gate_dt, gn_weight, gn_bias, eps};
+    bool fused = false;
+    ret_status_t st = chunkwise_run(q, k, v, y, B, N, H, dk, dv, in_dt, out_dt, gamma, theta, pos0, chunk, state_in,
+                                    state_out, workspace, workspace_bytes, stream, &epi, &fused);
+    if (st != RET_OK || fused) return st;
+    // not fused: the retention outputs are in y; the epilogue runs over them in place
+    return ret_msr_epilogue(y, gate, gn_weight, gn_bias, y, (int64_t)B * N, H, dv, out_dt, gate_dt, out_dt, eps,
+                            stream);
 }
 
 ret_status_t ret_recurrent_step(const void* q, const void* k, const void* v, void* o, float* state, int B, int H,
@@ -374,6 +438,46 @@ ret_status_t ret_recurrent_step(const void* q, const void* k, const void* v, voi
     hipLaunchKernelGGL(fn, dim3((dv + cw - 1) / cw, (B * H + ppw - 1) / ppw), dim3(64 * (dk / wr) * ppw), 0, s, A);
     tm.done();
     return launch_status("ret_recurrent_step");
+}
+
+ret_status_t ret_msr_epilogue(const void* o, const void* gate, const float* gn_weight, const float* gn_bias,
+                              void* y, int64_t rows, int H, int dv, ret_dtype_t o_dt, ret_dtype_t gate_dt,
+                              ret_dtype_t y_dt, float eps, void* stream) {
+    if (!o || !y) return fail(RET_ERR_INVALID_ARG, "null o/y pointer");
+    if (rows < 0 || H <= 0 || dv <= 0)
+        return fail(RET_ERR_INVALID_ARG, "sizes must be positive (rows=%lld H=%d dv=%d)", (long long)rows, H, dv);
+    for (ret_dtype_t t : {o_dt, gate_dt, y_dt})
+        if (t != RET_F32 && t != RET_BF16) return fail(RET_ERR_INVALID_ARG, "bad dtype %d", (int)t);
+    if (!(eps >= 0.f) || !isfinite(eps)) return fail(RET_ERR_INVALID_ARG, "eps=%g must be finite and >= 0", eps);
+    if (!aligned16(o) || !aligned16(y) || (gate && !aligned16(gate)) || (gn_weight && !aligned16(gn_weight)) ||
+        (gn_bias && !aligned16(gn_bias)))
+        return fail(RET_ERR_INVALID_ARG, "o/gate/y/gn_weight/gn_bias must be 16-byte aligned");
+    int gpw = 0;
+    const epi_kernel_t fn = epilogue_kernel_get(dv, &gpw);
+    if (!fn) return fail(RET_ERR_UNSUPPORTED, "epilogue: d_v=%d not in {16,32,64,128,256,512}", dv);
+    const long long groups = (long long)rows * H;
+    if (groups == 0) return RET_OK;
+    if (groups > 0x7fffffffLL)
+        return fail(RET_ERR_UNSUPPORTED, "epilogue: %lld rows x %d heads exceed 2^31 groups", (long long)rows, H);
+    const long long wgs = (groups + gpw - 1) / gpw;
+    EpiArgs A;
+    A.o = o;
+    A.gate = gate;
+    A.weight = gn_weight;
+    A.bias = gn_bias;
+    A.y = y;
+    A.groups = groups;
+    A.H = H;
+    A.dv = dv;
+    A.o_bf16 = o_dt == RET_BF16;
+    A.gate_bf16 = gate_dt == RET_BF16;
+    A.y_bf16 = y_dt == RET_BF16;
+    A.eps = eps;
+    hipStream_t s = (hipStream_t)stream;
+    LaunchTimer tm("ret_msr_epilogue", s);
+    hipLaunchKernelGGL(fn, dim3((unsigned)wgs), dim3(256), 0, s, A);
+    tm.done();
+    return launch_status("ret_msr_epilogue");
 }
 
 int ret_timing_enable(int on) {

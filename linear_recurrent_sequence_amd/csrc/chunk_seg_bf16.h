@@ -274,26 +274,79 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_seg_bf16(FwdArgs a) {
     // bf16 outputs leave through the V staging tiles (free by now; chunk c uses tile c % 2, last read before the
     // barrier of chunk c - 1) as whole rows: each wave writes its O^T tiles as rows of O, then 8 lanes store one
     // row's 64 d_v (128 bytes) with one 16-byte store each, instead of four waves writing 32-byte pieces of it.
-    auto store_rows = [&](int c, const f32x4_t* O, uint16_t* buf) __attribute__((always_inline)) {
+    //
+    // With the multi-scale retention epilogue (a.epi; d_v = 64, so a row is a whole head) the 8 lanes of a row
+    // hold one GroupNorm group: they standardize it by shuffles, apply the per-channel affine and the swish
+    // gate, and store y in place of o. The gate rows are read with the same range as the output rows, one chunk
+    // ahead of their use (gq[c % 2]), so only the first chunk's read is waited for in full.
+    const int gsz = a.gate_bf16 ? 2 : 4;
+    const char* gh = (const char*)a.gate + (head0 * adv + dv0) * gsz;
+    const int row = tid / 8, sg = tid % 8;
+    u32x4_t gq[2][C / 32][2];
+    auto gate_issue = [&](int c, u32x4_t (&gu)[C / 32][2]) __attribute__((always_inline)) {
+        if (a.epi && a.gate && c < nchunks) {
+            const int L = min(C, seg_n - c * C);
+            const rsrc_t rg = bytes_rsrc(gh + (long long)c * C * rsv * gsz, ((L - 1) * rsv + 64) * gsz);
+#pragma unroll
+            for (int p = 0; p < C / 32; ++p) {
+                const int off = ((row + 32 * p) * rsv + sg * 8) * gsz;
+                gu[p][0] = buf_load16(rg, off, 0);
+                gu[p][1] = a.gate_bf16 ? u32x4_t{0u, 0u, 0u, 0u} : buf_load16(rg, off + 16, 0);
+            }
+        }
+    };
+    auto store_rows = [&](int c, const f32x4_t* O, uint16_t* buf, const u32x4_t (&gu)[C / 32][2])
+                          __attribute__((always_inline)) {
 #pragma unroll
         for (int x = 0; x < NB; ++x)
             *reinterpret_cast<uint2*>(buf + (x * 16 + n16) * LD + w * 16 + g4) =
                 make_uint2(pack2_bf16(O[x][0], O[x][1]), pack2_bf16(O[x][2], O[x][3]));
-        __syncthreads();
         const int L = min(C, seg_n - c * C);
+        __syncthreads();
         const rsrc_t ro = bytes_rsrc(oh + (long long)c * C * rsv * 2, ((L - 1) * rsv + 64) * 2);
-        const int row = tid / 8, sg = tid % 8;
 #pragma unroll
-        for (int p = 0; p < C / 32; ++p)
-            buf_store16(ro, ((row + 32 * p) * rsv + sg * 8) * 2, 0,
-                        *reinterpret_cast<const u32x4_t*>(buf + (row + 32 * p) * LD + sg * 8));
+        for (int p = 0; p < C / 32; ++p) {
+            u32x4_t u = *reinterpret_cast<const u32x4_t*>(buf + (row + 32 * p) * LD + sg * 8);
+            if (a.epi) {
+                float x[8];
+                unpack8(u, x);
+                group_standardize<8, 8>(x, 64.f, a.eps);
+                const int ch = h * 64 + sg * 8;
+                if (a.gn_weight) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x[e] *= a.gn_weight[ch + e];
+                }
+                if (a.gn_bias) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x[e] += a.gn_bias[ch + e];
+                }
+                if (a.gate) {
+                    float gv[8];
+                    if (a.gate_bf16) {
+                        unpack8(gu[p][0], gv);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            gv[e] = __uint_as_float(gu[p][0][e]);
+                            gv[4 + e] = __uint_as_float(gu[p][1][e]);
+                        }
+                    }
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x[e] *= swish_hw(gv[e]);
+                }
+                u = pack8(x);
+            }
+            buf_store16(ro, ((row + 32 * p) * rsv + sg * 8) * 2, 0, u);
+        }
     };
     bf16x8_t rin[KK];
 #pragma unroll
     for (int k = 0; k < KK; ++k) rin[k] = acc_pair(Rin[2 * k], Rin[2 * k + 1]);
+    if (a.out_bf16) gate_issue(0, gq[0]);
     static_for<0, F::MAXC>([&](auto cc) __attribute__((always_inline)) {
         constexpr int c = decltype(cc)::value;
         if (c < nchunks) {
+            if (a.out_bf16 && c + 1 < F::MAXC) gate_issue(c + 1, gq[(c + 1) % 2]);
             if (seg > 0) {
                 const uint16_t* sQ = sQres + c * F::TILE;
                 const float gc = gpow(lg, (float)(c * C));
@@ -306,7 +359,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_seg_bf16(FwdArgs a) {
                 }
             }
             if (a.out_bf16)
-                store_rows(c, Op[c], sVst + (c & 1) * F::VTILE);
+                store_rows(c, Op[c], sVst + (c & 1) * F::VTILE, gq[c % 2]);
             else
                 store_out(c, Op[c]);
         }

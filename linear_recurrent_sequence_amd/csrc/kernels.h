@@ -25,9 +25,61 @@ struct FwdArgs {
     int out_bf16;
     int rotate;
     long long pos0;
+    // Multi-scale retention epilogue applied to the outputs before they are stored (epi != 0; only kernels
+    // that hold whole head rows take it): y = swish(gate) (.) GroupNorm_h(o).
+    const void* gate;        // [B,N,H,dv] like o, or null
+    const float* gn_weight;  // [H * dv] or null
+    const float* gn_bias;    // [H * dv] or null
+    float eps;
+    int epi, gate_bf16;
     float log2g[kMaxHeads];
     double theta[kMaxPairs];
 };
+
+// swish(g) = g sigmoid(g), the sigmoid as 1 / (1 + 2^(-g log2 e)) on the hardware 2^x and reciprocal (about
+// 1 ulp each).
+__device__ __forceinline__ float swish_hw(float g) {
+    return g * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g));
+}
+
+// Sum over LPG consecutive lanes (a power of 2, aligned), left in every one of them. Within a row of 16 lanes
+// the partner values move by DPP (quad permutations, then the half-row and row mirrors: after the steps
+// before, the mirrored lane holds the other half's sum), with no LDS round trip; across rows by shuffles.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+template <int LPG>
+__device__ __forceinline__ float lanes_sum(float s) {
+    if constexpr (LPG >= 2) s += dpp_mov<0xb1>(s);   // quad_perm [1,0,3,2]
+    if constexpr (LPG >= 4) s += dpp_mov<0x4e>(s);   // quad_perm [2,3,0,1]
+    if constexpr (LPG >= 8) s += dpp_mov<0x141>(s);  // row_half_mirror
+    if constexpr (LPG >= 16) s += dpp_mov<0x140>(s); // row_mirror
+#pragma unroll
+    for (int m = 16; m < LPG; m *= 2) s += __shfl_xor(s, m);
+    return s;
+}
+
+// GroupNorm of one group of values spread over LPG consecutive lanes (EPL values each, in x): standardized in
+// place by the group's mean and biased variance over n values, (x - mean) / sqrt(var + eps).
+template <int LPG, int EPL>
+__device__ __forceinline__ void group_standardize(float* x, float n, float eps) {
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) s += x[e];
+    s = lanes_sum<LPG>(s);
+    const float mean = s / n;
+    float s2 = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+        x[e] -= mean;
+        s2 += x[e] * x[e];
+    }
+    s2 = lanes_sum<LPG>(s2);
+    const float inv = __builtin_amdgcn_rsqf(s2 / n + eps);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) x[e] *= inv;
+}
 
 // Workspace of the single-pass chunkwise kernel when a sequence is split into nseg > 1 segments: a header,
 // two counters per unit (next segment ticket, workgroups past the look-back), one flag per (unit, segment)
@@ -910,11 +962,26 @@ bool chunk_kernels_bf16_small(int dk, int dv, int C, ChunkKernels* out);   // d_
 bool chunk_kernels_bf16_128(int dk, int dv, int C, ChunkKernels* out);     // d_k = 128
 bool chunk_kernels_bf16_256(int dk, int dv, int C, ChunkKernels* out);     // d_k = 256
 bool parallel_kernel_get(bool bf16_in, int dk, int dv, ParKernel* out);
-// Decode kernel for d_k, the state columns per wave `cw` and rows per wave `wr` (0: defaults); null if none.
-// The launch is ceil(d_v / cw) x (B*H) workgroups of 64 * d_k / wr threads.
-// Decode kernel for a (d_k, column tile cw, rows per wave wr) tile, 0 = default; with pairs_mode 0 it groups
-// (b, h) pairs into workgroups of up to 8 waves where B*H leaves a workgroup per CU; 1 / 2 force one / grouped.
+// Decode kernel for a (d_k, column tile cw, rows per wave wr) tile, 0 = default, null if none; with pairs_mode 0
+// it groups (b, h) pairs into workgroups of up to 8 waves where B*H leaves a workgroup per CU; 1 / 2 force one
+// / grouped. The launch is ceil(d_v / cw) x ceil(B*H / ppw) workgroups of 64 * (d_k / wr) * ppw threads.
 step_kernel_t step_kernel_get(bool bf16_in, int dk, int dv, int npairs, int cw, int wr, int pairs_mode, int* cw_used,
                               int* wr_used, int* ppw_used);
+
+// Multi-scale retention epilogue y = swish(gate) (.) GroupNorm_h(o) over groups of d_v values.
+struct EpiArgs {
+    const void* o;
+    const void* gate;     // null: no gate
+    const float* weight;  // [H * dv] or null
+    const float* bias;    // [H * dv] or null
+    void* y;
+    long long groups;  // rows * H
+    int H, dv;
+    int o_bf16, gate_bf16, y_bf16;
+    float eps;
+};
+typedef void (*epi_kernel_t)(EpiArgs);
+// Kernel for d_v in {16, 32, 64, 128, 256, 512} (null otherwise) and its groups per 256-thread workgroup.
+epi_kernel_t epilogue_kernel_get(int dv, int* groups_per_wg);
 
 }  // namespace ret

@@ -56,6 +56,11 @@ def load(build_if_missing: bool = True):
     lib.ret_chunkwise_fwd.restype = i32
     lib.ret_recurrent_step.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, fp, dp, i64, vp]
     lib.ret_recurrent_step.restype = i32
+    lib.ret_msr_epilogue.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, ctypes.c_float, vp]
+    lib.ret_msr_epilogue.restype = i32
+    lib.ret_chunkwise_msr_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, fp, dp, i64,
+                                          i32, vp, vp, vp, vp, ctypes.c_float, vp, sz, vp]
+    lib.ret_chunkwise_msr_fwd.restype = i32
     lib.ret_chunkwise_check.argtypes = [vp, vp]
     lib.ret_chunkwise_check.restype = i32
     lib.ret_timing_enable.argtypes = [i32]
@@ -179,6 +184,51 @@ def ret_recurrent_step(q, k, v, o, state, gamma, pos, theta=None, stream=None):
                                 dk, dv, _dt(q), _dt(o), gp, tp, int(pos), _stream(stream))
     _check("ret_recurrent_step", st)
     return o
+
+
+def ret_msr_epilogue(o, y, gate=None, gn_weight=None, gn_bias=None, eps=1e-5, stream=None):
+    """y = swish(gate) (.) GroupNorm_h(o), one GroupNorm group per head: o, gate, y [..., H, d_v] (the leading
+    dims are the rows); gn_weight, gn_bias float32 [H * d_v] or None. y may be o or gate (in place)."""
+    lib = load()
+    if o.dim() < 2 or tuple(y.shape) != tuple(o.shape) or (gate is not None and tuple(gate.shape) != tuple(o.shape)):
+        raise ValueError("o, y (and gate) must share one shape [..., H, d_v]")
+    H, dv = o.shape[-2], o.shape[-1]
+    rows = o.numel() // (H * dv) if H * dv else 0
+    for name, t in (("gn_weight", gn_weight), ("gn_bias", gn_bias)):
+        if t is not None and (t.dtype != torch.float32 or t.numel() != H * dv):
+            raise ValueError("%s must be float32 with H*d_v entries" % name)
+    st = lib.ret_msr_epilogue(_dev(o, "o"), _dev(gate, "gate"), _dev(gn_weight, "gn_weight"),
+                              _dev(gn_bias, "gn_bias"), _dev(y, "y"), rows, H, dv, _dt(o),
+                              _dt(gate) if gate is not None else RET_BF16, _dt(y), float(eps), _stream(stream))
+    _check("ret_msr_epilogue", st)
+    return y
+
+
+def ret_chunkwise_msr_fwd(q, k, v, y, gamma, chunk, gate=None, gn_weight=None, gn_bias=None, eps=1e-5, theta=None,
+                          pos0=0, state_in=None, state_out=None, workspace=None, stream=None):
+    """Chunkwise retention, then y = swish(gate) (.) GroupNorm_h(O), fused into the output stores where the
+    kernel holds whole head rows. Arguments as ret_chunkwise_fwd (y in the place of o) and ret_msr_epilogue."""
+    lib = load()
+    B, N, H, dk = q.shape
+    dv = v.shape[3]
+    if tuple(y.shape) != (B, N, H, dv) or (gate is not None and tuple(gate.shape) != (B, N, H, dv)):
+        raise ValueError("y (and gate) must be [B,N,H,d_v]")
+    for name, t in (("gn_weight", gn_weight), ("gn_bias", gn_bias)):
+        if t is not None and (t.dtype != torch.float32 or t.numel() != H * dv):
+            raise ValueError("%s must be float32 with H*d_v entries" % name)
+    for name, t in (("state_in", state_in), ("state_out", state_out)):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != (B, H, dk, dv)):
+            raise ValueError("%s must be float32 [B,H,dk,dv]" % name)
+    g, gp = _gamma(gamma, H)
+    th, tp = _theta(theta, dk)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.ret_chunkwise_msr_fwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(gate, "gate"), _dev(y, "y"), B, N,
+                                   H, dk, dv, _dt(q), _dt(y), _dt(gate) if gate is not None else RET_BF16, gp, tp,
+                                   int(pos0), int(chunk), _dev(state_in, "state_in"), _dev(state_out, "state_out"),
+                                   _dev(gn_weight, "gn_weight"), _dev(gn_bias, "gn_bias"), float(eps),
+                                   _dev(workspace, "workspace"), wsb, _stream(stream))
+    _check("ret_chunkwise_msr_fwd", st)
+    return y
 
 
 def timing_enable(on: bool) -> bool:

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ret_abi_version() == 1
+    assert lib.ret_abi_version() == 2
     assert lib.ret_status_string(0) == b"ok"
     assert lib.ret_status_string(-2) == b"unsupported shape or dtype"
 
@@ -99,3 +99,32 @@ def test_step_and_parallel_reject_invalid_arguments(lib):
     assert lib.ret_recurrent_step(16, 32, 48, 64, 80, 1, 1, 48, 64, 1, 1, g, None, 0, None) == -2
     assert lib.ret_parallel_fwd(16, 32, 48, 64, 1, 8, 1, 48, 64, 1, 1, g, None, 0, None) == -2
     assert lib.ret_parallel_fwd(16, 32, 48, 64, 1, -1, 1, 64, 64, 1, 1, g, None, 0, None) == -1
+
+
+def test_epilogue_rejects_invalid_arguments(lib):
+    """ret_msr_epilogue validates on the host; rows = 0 returns OK without a launch."""
+    e = lambda *a: lib.ret_msr_epilogue(*a)
+    assert e(None, None, None, None, 32, 4, 2, 64, 1, 1, 1, 1e-5, None) == -1           # null o
+    assert e(16, None, None, None, None, 4, 2, 64, 1, 1, 1, 1e-5, None) == -1           # null y
+    assert e(16, None, None, None, 32, -1, 2, 64, 1, 1, 1, 1e-5, None) == -1            # negative rows
+    assert e(16, None, None, None, 32, 4, 0, 64, 1, 1, 1, 1e-5, None) == -1             # no heads
+    assert e(16, None, None, None, 32, 4, 2, 64, 1, 1, 1, -1.0, None) == -1             # eps < 0
+    assert e(16, None, None, None, 32, 4, 2, 64, 1, 1, 1, float("nan"), None) == -1     # eps NaN
+    assert e(16, None, None, None, 32, 4, 2, 64, 1, 1, 7, 1e-5, None) == -1             # bad dtype
+    assert e(8, None, None, None, 32, 4, 2, 64, 1, 1, 1, 1e-5, None) == -1              # misaligned o
+    assert e(16, 40, None, None, 32, 4, 2, 64, 1, 1, 1, 1e-5, None) == -1               # misaligned gate
+    assert e(16, None, None, None, 32, 4, 2, 48, 1, 1, 1, 1e-5, None) == -2             # d_v not supported
+    assert e(16, None, None, None, 32, 0, 2, 64, 1, 1, 1, 1e-5, None) == 0              # empty: no launch
+
+
+def test_chunkwise_msr_rejects_invalid_arguments(lib):
+    """ret_chunkwise_msr_fwd checks the epilogue's arguments before anything is launched."""
+    g = np.asarray([0.9, 0.99], np.float32).ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+    call = lambda gate=None, y=64, dv=64, gdt=1, eps=1e-5, gw=None: lib.ret_chunkwise_msr_fwd(
+        16, 32, 48, gate, y, 1, 64, 2, 64, dv, 1, 1, gdt, g, None, 0, 64, None, None, gw, None, eps, None, 0, None)
+    assert call(gdt=5) == -1            # bad gate dtype
+    assert call(eps=-1.0) == -1         # eps < 0
+    assert call(gate=72) == -1          # misaligned gate
+    assert call(gw=8) == -1             # misaligned weight
+    assert call(gate=64) == -1          # gate aliases y
+    assert call(dv=96) == -2            # no epilogue for d_v = 96

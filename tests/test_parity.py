@@ -300,6 +300,149 @@ def test_recurrent_steps_small(R, dt, dk, dv, cw, wr, pairs, monkeypatch):
 
 
 # ---------------------------------------------------------------------------------------------------
+# Multi-scale retention epilogue: y = swish(gate) (.) GroupNorm_h(o).
+# ---------------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("affine,gated", [(True, True), (False, True), (True, False), (False, False)])
+@pytest.mark.parametrize("dts", [("bf16", "bf16", "bf16"), ("f32", "f32", "f32"), ("f32", "bf16", "bf16"),
+                                 ("bf16", "f32", "f32")])
+@pytest.mark.parametrize("dv", [16, 64, 128, 512])
+def test_msr_epilogue(R, dv, dts, affine, gated):
+    """Rows of 3 heads, 37 tokens (a partial last workgroup), every dtype mix, with and without the
+    per-channel affine and the gate."""
+    import torch
+    o_dt, g_dt, y_dt = dts
+    print_case("msr_epilogue", dv, dts, affine, gated)
+    rng = np.random.default_rng(300 + dv)
+    rows, H = 37, 3
+    # rows of very different scales and offsets, held exactly in the input dtype
+    o = W.round_to(rng.standard_normal((rows, H, dv)) * rng.uniform(0.05, 20.0, size=(rows, H, 1))
+                   + rng.uniform(-3.0, 3.0, size=(rows, H, 1)), o_dt)
+    g = W.normal(rng, (rows, H, dv), 0.5, g_dt) if gated else None
+    w = rng.standard_normal(H * dv).astype(np.float32) if affine else None
+    b = rng.standard_normal(H * dv).astype(np.float32) if affine else None
+    ref = oracle.msr_epilogue(o, g, w, b, eps=1e-5)
+    y = empty_out((rows, H, dv), y_dt)
+    td = lambda a: None if a is None else torch.from_numpy(a).cuda()
+    R.ret_msr_epilogue(to_dev(o, o_dt), y, gate=None if g is None else to_dev(g, g_dt), gn_weight=td(w),
+                       gn_bias=td(b), eps=1e-5)
+    torch.cuda.synchronize()
+    err = rel_err(to_host(y), ref)
+    print("  err %.3g" % err)
+    assert err <= tol(y_dt), err
+
+
+def test_msr_epilogue_in_place_and_decode_rows(R):
+    """y = o in place, on the rows of one decode step ([B, H, d_v]), eps 0.1."""
+    import torch
+    rng = np.random.default_rng(41)
+    B, H, dv = 5, 4, 64
+    o = W.normal(rng, (B, H, dv), 1.0, "f32")
+    g = W.normal(rng, (B, H, dv), 1.0, "f32")
+    ref = oracle.msr_epilogue(o, g, eps=0.1)
+    od = to_dev(o, "f32")
+    R.ret_msr_epilogue(od, od, gate=to_dev(g, "f32"), eps=0.1)
+    torch.cuda.synchronize()
+    assert rel_err(to_host(od), ref) <= 1e-5
+
+
+def test_msr_layer_chunkwise_then_epilogue(R):
+    """retention-layer-d512 in full: the chunkwise forward, then the epilogue with a gate and per-channel
+    affine, against the oracle's chunkwise form and epilogue."""
+    import torch
+    w = W.WORKLOADS[2]
+    print_case("msr_layer", w)
+    q, k, v, rng = W.make_qkv(w)
+    gate = W.normal(rng, (w.B, w.N, w.H, w.dv), 1.0, "bf16")
+    gw = rng.uniform(0.5, 1.5, w.H * w.dv).astype(np.float32)
+    gb = (0.1 * rng.standard_normal(w.H * w.dv)).astype(np.float32)
+    o_ref, _ = oracle.chunkwise(q, k, v, w.gamma, w.chunk, theta=w.theta)
+    y_ref = oracle.msr_epilogue(o_ref, gate, gw, gb, eps=1e-5)
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    o = empty_out((w.B, w.N, w.H, w.dv), "bf16")
+    R.ret_chunkwise_fwd(qd, kd, vd, o, w.gamma, w.chunk, theta=w.theta, workspace=R.chunkwise_workspace(qd, vd, w.chunk))
+    y = empty_out((w.B, w.N, w.H, w.dv), "bf16")
+    R.ret_msr_epilogue(o, y, gate=to_dev(gate, "bf16"), gn_weight=torch.from_numpy(gw).cuda(),
+                       gn_bias=torch.from_numpy(gb).cuda(), eps=1e-5)
+    torch.cuda.synchronize()
+    err = rel_err(to_host(y), y_ref)
+    print("  err %.3g" % err)
+    assert err <= 2e-2, err
+
+
+@pytest.mark.parametrize("gate_dt,affine", [("bf16", True), ("f32", True), (None, True), ("bf16", False)])
+def test_chunkwise_msr_fused(R, gate_dt, affine):
+    """retention-layer-d512 through ret_chunkwise_msr_fwd: the on-chip kernel applies the epilogue before its
+    stores. Against the oracle, and bit for bit against the chunkwise call followed by ret_msr_epilogue (the
+    same bf16 outputs, the same reduction order over 8 lanes of 8 values)."""
+    import torch
+    w = W.WORKLOADS[2]
+    print_case("chunkwise_msr_fused", gate_dt, affine)
+    q, k, v, rng = W.make_qkv(w)
+    gate = None if gate_dt is None else W.normal(rng, (w.B, w.N, w.H, w.dv), 1.0, gate_dt)
+    gw = rng.uniform(0.5, 1.5, w.H * w.dv).astype(np.float32) if affine else None
+    gb = (0.1 * rng.standard_normal(w.H * w.dv)).astype(np.float32) if affine else None
+    o_ref, _ = oracle.chunkwise(q, k, v, w.gamma, w.chunk, theta=w.theta)
+    y_ref = oracle.msr_epilogue(o_ref, gate, gw, gb, eps=1e-5)
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    gd = None if gate is None else to_dev(gate, gate_dt)
+    td = lambda a: None if a is None else torch.from_numpy(a).cuda()
+    ws = R.chunkwise_workspace(qd, vd, w.chunk)
+    y = empty_out((w.B, w.N, w.H, w.dv), "bf16")
+    R.ret_chunkwise_msr_fwd(qd, kd, vd, y, w.gamma, w.chunk, gate=gd, gn_weight=td(gw), gn_bias=td(gb), eps=1e-5,
+                            theta=w.theta, workspace=ws)
+    o = empty_out((w.B, w.N, w.H, w.dv), "bf16")
+    R.ret_chunkwise_fwd(qd, kd, vd, o, w.gamma, w.chunk, theta=w.theta, workspace=ws)
+    y2 = empty_out((w.B, w.N, w.H, w.dv), "bf16")
+    R.ret_msr_epilogue(o, y2, gate=gd, gn_weight=td(gw), gn_bias=td(gb), eps=1e-5)
+    torch.cuda.synchronize()
+    R.ret_chunkwise_check(ws)
+    err = rel_err(to_host(y), y_ref)
+    print("  err %.3g" % err)
+    assert err <= 2e-2, err
+    assert torch.equal(y, y2)
+
+
+@pytest.mark.parametrize("case", ["dv128", "f32_out", "streaming_kernel", "f32_in"])
+def test_chunkwise_msr_unfused(R, case, monkeypatch):
+    """Shapes the kernels cannot fuse (two d_v tiles per head, fp32 output, the streaming kernel, fp32 input):
+    the chunkwise call, then the epilogue over y in place, against the oracle."""
+    import torch
+    B, N, H, dk, dv, C, dt, odt = 2, 300, 2, 64, 64, 64, "bf16", "bf16"
+    if case == "dv128":
+        dv = 128
+    elif case == "f32_out":
+        odt = "f32"
+    elif case == "streaming_kernel":
+        monkeypatch.setenv("RET_SEG_ONCHIP", "0")
+        monkeypatch.setenv("RET_SEGMENTS", "2")
+    else:
+        dt, odt, dk, C = "f32", "f32", 32, 32
+    print_case("chunkwise_msr_unfused", case)
+    rng = np.random.default_rng(61)
+    q = W.normal(rng, (B, N, H, dk), 8.0, dt)
+    k = W.normal(rng, (B, N, H, dk), 8.0, dt)
+    v = W.normal(rng, (B, N, H, dv), 8.0, dt)
+    gate = W.normal(rng, (B, N, H, dv), 1.0, "bf16")
+    gw = rng.uniform(0.5, 1.5, H * dv).astype(np.float32)
+    gamma, theta = W.gamma_schedule(H), W.theta_schedule(dk)
+    s0 = rng.standard_normal((B, H, dk, dv)).astype(np.float32)
+    o_ref, s_ref = oracle.chunkwise(q, k, v, gamma, C, theta=theta, pos0=4, state_in=s0)
+    # the epilogue reads O as rounded to the output dtype
+    y_ref = oracle.msr_epilogue(W.round_to(o_ref, odt) if odt == "bf16" else o_ref, gate, gw, None, eps=1e-5)
+    qd, kd, vd = to_dev(q, dt), to_dev(k, dt), to_dev(v, dt)
+    y = empty_out((B, N, H, dv), odt)
+    sout = torch.empty((B, H, dk, dv), dtype=torch.float32, device="cuda")
+    ws = R.chunkwise_workspace(qd, vd, C)
+    R.ret_chunkwise_msr_fwd(qd, kd, vd, y, gamma, C, gate=to_dev(gate, "bf16"), gn_weight=torch.from_numpy(gw).cuda(),
+                            eps=1e-5, theta=theta, pos0=4, state_in=torch.from_numpy(s0).cuda(), state_out=sout,
+                            workspace=ws)
+    torch.cuda.synchronize()
+    err, es = rel_err(to_host(y), y_ref), rel_err(to_host(sout), s_ref)
+    print("  err %.3g state %.3g" % (err, es))
+    assert err <= tol(dt) and es <= tol(dt), (err, es)  # the bar of the input dtype, as for the chunkwise form
+
+
+# ---------------------------------------------------------------------------------------------------
 # Full-size workloads 2-5.
 # ---------------------------------------------------------------------------------------------------
 def test_workload2_chunkwise_full(R):
