@@ -53,8 +53,9 @@ def _load():
     lib.orc_chunkwise.argtypes = [P, P, P, P, I, I, I, I, I, P, P, LL, I, P, P, I]
     lib.orc_parallel_normalized.argtypes = [P, P, P, P, I, I, I, I, I, P, P, LL, I, I]
     lib.orc_msr_epilogue.argtypes = [P, P, P, P, P, LL, I, I, ctypes.c_double]
+    lib.orc_grad.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P, P, LL, I]
     for f in (lib.orc_parallel, lib.orc_parallel_rows, lib.orc_recurrent, lib.orc_chunkwise,
-              lib.orc_parallel_normalized, lib.orc_msr_epilogue):
+              lib.orc_parallel_normalized, lib.orc_msr_epilogue, lib.orc_grad):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -119,6 +120,20 @@ def parallel_normalized(q, k, v, gamma, theta=None, pos0=0, scale=False, decay=F
                                          int(pos0), norm, threads or default_threads())
     _check(rc, "parallel_normalized")
     return o
+
+
+def grad(q, k, v, dout, gamma, theta=None, pos0=0, threads=None):
+    """Gradients (dq, dk, dv) of sum(dout (.) O) for O the retention output from a zero state, by the adjoint of
+    the recurrent scan (see the C file)."""
+    q, k, v, g, th, (B, N, H, dk, dv) = _common(q, k, v, gamma, theta)
+    do = _f64(dout)
+    if do.shape != (B, N, H, dv):
+        raise ValueError("dout must be [B,N,H,dv]")
+    dq, dk_, dv_ = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)
+    rc = _load().orc_grad(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq), _ptr(dk_), _ptr(dv_), B, N, H, dk, dv,
+                          _ptr(g), _ptr(th), int(pos0), threads or default_threads())
+    _check(rc, "grad")
+    return dq, dk_, dv_
 
 
 def msr_epilogue(o, gate=None, weight=None, bias=None, eps=1e-5):

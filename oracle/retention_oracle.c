@@ -14,7 +14,11 @@
  *   - the parallel form with the retention score normalizations (blog section 8.5; paper summary,
  *     "Retention Score Normalization"): QK^T / sqrt(d_k), D~ and R~;
  *   - the multi-scale retention epilogue (blog sections 8.4 and 9.1; paper summary, "Gating mechanism"):
- *     y = swish(g) (.) GroupNorm_h(o), with g = X W_G given.
+ *     y = swish(g) (.) GroupNorm_h(o), with g = X W_G given;
+ *   - the gradients of the recurrent form from a zero state (the pages train with the chunkwise form, paper
+ *     summary "Overall RetNet Architecture and Training/Inference Protocol"), by the adjoint of the scan:
+ *     dq'_n = S_n dO_n, G_n = gamma G_{n+1} + q'_n^T dO_n, dk'_n = G_n v_n, dv_n = G_n^T k'_n, then dq, dk
+ *     rotated back by the transpose rotation.
  *
  * Readings where the pages leave a step open (each is also listed in the design notes):
  *   - the rotation turns pair (x_{2i}, x_{2i+1}) of BOTH q and k by +p*theta_i, then a real dot product
@@ -106,6 +110,8 @@ typedef struct {
     long long pos0;
     int form; /* 0 parallel, 1 recurrent, 2 chunkwise, 3 parallel rows, 4 normalized parallel */
     int norm; /* normalized parallel form: ORC_NORM_* flags */
+    const double* dout; /* gradients (form 5): dO [B][N][H][dv] in, dq, dk, dv out */
+    double *dq, *dk_, *dv_;
     int nthreads, tid;
     int status;
 } job;
@@ -115,6 +121,7 @@ static int form_recurrent(job* J, int b, int h);
 static int form_chunkwise(job* J, int b, int h);
 static int form_parallel_rows(job* J, int b, int h);
 static int form_parallel_norm(job* J, int b, int h);
+static int form_grad(job* J, int b, int h);
 
 static void* worker(void* arg) {
     job* J = (job*)arg;
@@ -126,6 +133,7 @@ static void* worker(void* arg) {
             case 1: rc = form_recurrent(J, b, h); break;
             case 2: rc = form_chunkwise(J, b, h); break;
             case 4: rc = form_parallel_norm(J, b, h); break;
+            case 5: rc = form_grad(J, b, h); break;
             default: rc = form_parallel_rows(J, b, h); break;
         }
         if (rc) J->status = rc;
@@ -250,6 +258,81 @@ static int form_parallel_norm(job* J, int b, int h) {
         }
     }
     free(w);
+    free_head(&hs);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------------------ */
+/* Gradients of the recurrent form, from a zero state, given dO = dL/dO (the adjoint of the scan):      */
+/*   forward:  S_n = gamma S_{n-1} + k'_n^T v_n,   dq'_n[i] = sum_j S_n[i][j] dO_n[j];                  */
+/*   backward: G_n = gamma G_{n+1} + q'_n^T dO_n,  dk'_n[i] = sum_j G_n[i][j] v_n[j],                    */
+/*             dv_n[j] = sum_i k'_n[i] G_n[i][j];                                                       */
+/* then the rotation's transpose: (dx_{2i}, dx_{2i+1}) = (c dx'_{2i} + s dx'_{2i+1}, -s dx'_{2i} + c dx'_{2i+1}) */
+/* with c, s of the angle (pos0 + n) theta_i, for dq and dk.                                           */
+/* ------------------------------------------------------------------------------------------------ */
+
+static void unrotate_row(double* d, int dk, const double* theta, long long p) {
+    if (!theta) return;
+    for (int i = 0; i < dk / 2; ++i) {
+        double phi = (double)p * theta[i];
+        double c = cos(phi), s = sin(phi);
+        double a = d[2 * i], b = d[2 * i + 1];
+        d[2 * i] = c * a + s * b;
+        d[2 * i + 1] = -s * a + c * b;
+    }
+}
+
+static int form_grad(job* J, int b, int h) {
+    const int N = J->N, H = J->H, dk = J->dk, dv = J->dv;
+    const double g = J->gamma[h];
+    head_seq hs;
+    double* S = (double*)calloc((size_t)dk * dv, sizeof(double));
+    double* dO = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1) * dv);
+    if (!S || !dO || load_head(&hs, J->q, J->k, J->v, N, H, dk, dv, b, h, J->theta, J->pos0)) {
+        free(S);
+        free(dO);
+        free_head(&hs);
+        return -3;
+    }
+    for (int n = 0; n < N; ++n) gather_plain(J->dout, dO + (size_t)n * dv, N, H, dv, b, n, h);
+    for (int n = 0; n < N; ++n) {
+        const double* kn = hs.Kr + (size_t)n * dk;
+        const double* vn = hs.Vh + (size_t)n * dv;
+        const double* don = dO + (size_t)n * dv;
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] = g * S[(size_t)i * dv + j] + kn[i] * vn[j];
+        double* dq = out_row(J->dq, N, H, dk, b, n, h);
+        for (int i = 0; i < dk; ++i) {
+            double acc = 0.0;
+            for (int j = 0; j < dv; ++j) acc += S[(size_t)i * dv + j] * don[j];
+            dq[i] = acc;
+        }
+        unrotate_row(dq, dk, J->theta, J->pos0 + n);
+    }
+    memset(S, 0, sizeof(double) * (size_t)dk * dv); /* S now holds G */
+    for (int n = N - 1; n >= 0; --n) {
+        const double* qn = hs.Qr + (size_t)n * dk;
+        const double* kn = hs.Kr + (size_t)n * dk;
+        const double* vn = hs.Vh + (size_t)n * dv;
+        const double* don = dO + (size_t)n * dv;
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] = g * S[(size_t)i * dv + j] + qn[i] * don[j];
+        double* dkr = out_row(J->dk_, N, H, dk, b, n, h);
+        for (int i = 0; i < dk; ++i) {
+            double acc = 0.0;
+            for (int j = 0; j < dv; ++j) acc += S[(size_t)i * dv + j] * vn[j];
+            dkr[i] = acc;
+        }
+        unrotate_row(dkr, dk, J->theta, J->pos0 + n);
+        double* dvr = out_row(J->dv_, N, H, dv, b, n, h);
+        for (int j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < dk; ++i) acc += kn[i] * S[(size_t)i * dv + j];
+            dvr[j] = acc;
+        }
+    }
+    free(S);
+    free(dO);
     free_head(&hs);
     return 0;
 }
@@ -431,6 +514,33 @@ int orc_msr_epilogue(const double* o, const double* g, const double* weight, con
             }
         }
     return 0;
+}
+
+/* Gradients of sum(dout (.) O) with respect to q, k and v, O the retention output from a zero state. */
+int orc_grad(const double* q, const double* k, const double* v, const double* dout, double* dq, double* dk_,
+             double* dv_, int B, int N, int H, int dk, int dv, const double* gamma, const double* theta,
+             long long pos0, int threads) {
+    if (check_args(B, N, H, dk, dv, gamma, theta) || !q || !k || !v || !dout || !dq || !dk_ || !dv_) return -1;
+    job J;
+    memset(&J, 0, sizeof(J));
+    J.q = q;
+    J.k = k;
+    J.v = v;
+    J.dout = dout;
+    J.dq = dq;
+    J.dk_ = dk_;
+    J.dv_ = dv_;
+    J.gamma = gamma;
+    J.theta = theta;
+    J.B = B;
+    J.N = N;
+    J.H = H;
+    J.dk = dk;
+    J.dv = dv;
+    J.pos0 = pos0;
+    J.form = 5;
+    J.nthreads = threads;
+    return run(J);
 }
 
 int orc_parallel_rows(const double* q, const double* k, const double* v, int B, int N, int H, int dk, int dv,

@@ -45,9 +45,16 @@ MUTANTS = {
     "decay_norm_without_root": ("D /= sqrt(dsum);", "D /= dsum;"),
     "score_norm_without_abs": ("den = fabs(rsum) > 1.0 ? fabs(rsum) : 1.0;", "den = rsum > 1.0 ? rsum : 1.0;"),
     "score_scale_by_dv": ("qk /= sqrt((double)dk);", "qk /= sqrt((double)dv);"),
+    "grad_adjoint_no_decay": ("S[(size_t)i * dv + j] = g * S[(size_t)i * dv + j] + qn[i] * don[j];",
+                              "S[(size_t)i * dv + j] = S[(size_t)i * dv + j] + qn[i] * don[j];"),
+    "grad_unrotate_sign": ("d[2 * i] = c * a + s * b;", "d[2 * i] = c * a - s * b;"),
+    "grad_dv_from_q": ("for (int i = 0; i < dk; ++i) acc += kn[i] * S[(size_t)i * dv + j];",
+                       "for (int i = 0; i < dk; ++i) acc += qn[i] * S[(size_t)i * dv + j];"),
+    "grad_dq_reads_state_transposed": ("for (int j = 0; j < dv; ++j) acc += S[(size_t)i * dv + j] * don[j];",
+                                       "for (int j = 0; j < dv; ++j) acc += S[(size_t)j * dk + i] * don[j];"),
 }
 
-PIN_TESTS = ["test_oracle_pins.py", "test_oracle_forms.py", "test_oracle_epilogue.py"]
+PIN_TESTS = ["test_oracle_pins.py", "test_oracle_forms.py", "test_oracle_epilogue.py", "test_oracle_grad.py"]
 
 
 def _run_pins_against(src_text, tmp_path):
