@@ -6,11 +6,12 @@ d_k=d_v=64, chunk 64, bf16 inputs/outputs, xPos rotation, fp32 state out): token
 with inputs resident in HBM. The same JSON line carries the batched-decode workload (B=128, H=8, d=64,
 fp32 state, 1024 single-token ret_recurrent_step calls replayed from a HIP graph) in steps/s, the
 multi-scale retention epilogue (GroupNorm per head and swish gate) on the chunkwise output, alone and after
-the chunkwise call, the roofline of each path's dominant kernel (per-launch HIP-event durations recorded by
-the library over the timed region), and the fp64 CPU oracle timed on this host.
+the chunkwise call, the gradients dq, dk, dv of the chunkwise call, the roofline of each path's dominant
+kernel (per-launch HIP-event durations recorded by the library over the timed region), and the fp64 CPU
+oracle timed on this host.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-decode] [--no-epilogue]
-                       [--no-cpu-baseline] [--copy-calibration] [--decode-steps S]
+                       [--no-backward] [--no-cpu-baseline] [--copy-calibration] [--decode-steps S]
 """
 from __future__ import annotations
 
@@ -201,6 +202,53 @@ def bench_epilogue(R, W, torch, wid, steps):
     }
 
 
+def bench_backward(R, W, torch, wid, steps):
+    """Gradients dq, dk, dv of the chunkwise workload (bf16 q, k, v, dO in; bf16 gradients out), replayed from a
+    HIP graph, with the per-kernel split from the library's launch events of one eager call."""
+    import numpy as np
+    w = W.WORKLOADS[wid]
+    q, k, v, rng = W.make_qkv(w)
+    do = W.make_dout(w, rng)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).cuda()
+    qd, kd, vd, dod = dev(q), dev(k), dev(v), dev(do)
+    del q, k, v, do
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    ws = R.chunkwise_bwd_workspace(qd, vd, w.chunk)
+    call = lambda: R.ret_chunkwise_bwd(qd, kd, vd, dod, dq, dk, dv, w.gamma, w.chunk, theta=w.theta, workspace=ws)
+    ms = graph_ms(torch, call, steps)
+    torch.cuda.synchronize()
+    R.timing_reset()
+    R.timing_enable(True)
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    R.timing_enable(False)
+    kernels = {}
+    for name in ("ret_permute_rotate", "ret_chunk_seg", "ret_chunk_fused", "ret_chunk_local", "ret_segment_scan"):
+        tot, n = R.timing_query(name)
+        if n:
+            kernels[name] = {"avg_us": 1e3 * tot / n, "launches_per_call": n // 3}
+    R.timing_reset()
+    R.ret_chunkwise_check(ws)
+    toks = w.B * w.N * w.H
+    nbytes = toks * (2 * w.dk + 2 * w.dv) * 2 + toks * (2 * w.dk + w.dv) * 2  # q, k, v, dO in; dq, dk, dv out
+    C = w.chunk
+    # three retentions, each the forward's causal count (C+1)(d_k+d_v) + 4 d_k d_v per (token, head)
+    flops = 3 * toks * ((C + 1) * (w.dk + w.dv) + 4 * w.dk * w.dv)
+    ach = nbytes / (ms * 1e-3) / 1e9
+    return {
+        "workload": "%s: B=%d N=%d H=%d d_k=%d d_v=%d chunk=%d, bf16 q/k/v/dO in, bf16 dq/dk/dv out, xPos rotation"
+                    % (w.name, w.B, w.N, w.H, w.dk, w.dv, w.chunk),
+        "us_per_call": 1e3 * ms,
+        "tokens_per_s": w.B * w.N / (ms * 1e-3),
+        "hbm_frac_whole_call": ach / HBM_PEAK_GBS,
+        "alg_bytes_per_call": nbytes,
+        "tflops_causal": flops / (ms * 1e-3) / 1e12,
+        "kernels": kernels,
+        "workspace_bytes": ws.numel(),
+    }
+
+
 def bench_decode(R, W, torch, steps_graph=1024, reps=3):
     import numpy as np
     w = W.WORKLOADS[3]
@@ -298,6 +346,7 @@ def main():
                     help="chunkwise workload timed for `value`")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-epilogue", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=1024, help="decode steps per graph (1024 in the workload)")
@@ -376,6 +425,8 @@ def main():
         }
     if not args.no_epilogue:
         result["epilogue"] = bench_epilogue(R, W, torch, wid, args.steps)
+    if not args.no_backward:
+        result["backward"] = bench_backward(R, W, torch, wid, args.steps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(W, wid)
     result["context"] = ("pages' figures (whole 6.7B model, A100-80GB, vanilla PyTorch): 8.4x faster decoding and "

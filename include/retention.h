@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define RET_ABI_VERSION 2
+#define RET_ABI_VERSION 3
 
 typedef enum { RET_F32 = 0, RET_BF16 = 1 } ret_dtype_t;
 
@@ -162,12 +162,34 @@ ret_status_t ret_chunkwise_msr_fwd(const void* q, const void* k, const void* v, 
                                    void* stream);
 
 /*
+ * Gradients of chunkwise retention, for training with the chunkwise form (paper summary, "Overall RetNet
+ * Architecture and Training/Inference Protocol"). With O the output of ret_chunkwise_fwd from a zero state
+ * (state_in NULL) and dout = dL/dO [B, N, H, d_v], writes dq, dk [B, N, H, d_k] and dv [B, N, H, d_v]; the
+ * gradients with respect to q and k are taken through their rotation. They follow from the parallel form
+ * ("Hybrid Architectures: RetNet and the Three Computation Paradigms", section 4.3; paper summary Eq. 5):
+ *     dq'_n = sum_{m<=n} gamma^(n-m) (dO_n . v_m) k'_m,    dk'_m = sum_{n>=m} gamma^(n-m) (dO_n . v_m) q'_n,
+ *     dv_m  = sum_{n>=m} gamma^(n-m) (q'_n . k'_m) dO_n,   dq, dk = dq', dk' turned back by the rotation's
+ *     transpose,
+ * each a retention (the last two over the reversed sequence) that the chunkwise kernels compute.
+ * in_dt: BF16 (q, k, v, dout); out_dt: F32 or BF16 (dq, dk, dv). No gradient for a state in or out.
+ * workspace: device memory of ret_chunkwise_bwd_workspace_bytes (zero-filled once by the caller, like the
+ * chunkwise workspace; every call leaves its chain part zeroed again; ret_chunkwise_check accepts it and
+ * reports a segment-chain wait that gave up). dq, dk, dv must not alias the inputs
+ * or each other. Supported: d_k, d_v in {64, 128, 256}, chunk in {32, 64, 128}. Asynchronous on `stream`.
+ */
+size_t ret_chunkwise_bwd_workspace_bytes(int B, int N, int H, int dk, int dv, int chunk);
+ret_status_t ret_chunkwise_bwd(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk_out,
+                               void* dv_out, int B, int N, int H, int dk, int dv, ret_dtype_t in_dt,
+                               ret_dtype_t out_dt, const float* gamma, const double* theta, int64_t pos0, int chunk,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Kernel timing for measurement tools. While enabled, every kernel the library launches is bracketed by a
  * pair of HIP events on the launch stream. ret_timing_query synchronises those events and returns the total
  * milliseconds and launch count recorded for kernels whose name equals `kernel` ("" or NULL = all).
  * ret_timing_reset drops the records. Kernel names: "ret_chunk_seg", "ret_chunk_fused" and "ret_rotate_qk"
  * (bf16 input), "ret_chunk_full", "ret_chunk_local", "ret_segment_scan" (fp32 input), "ret_parallel",
- * "ret_recurrent_step", "ret_msr_epilogue". Not for use while kernels are being captured into a graph.
+ * "ret_recurrent_step", "ret_msr_epilogue", "ret_permute_rotate" (gradients). Not for use while kernels are being captured into a graph.
  */
 int ret_timing_enable(int on);
 int ret_timing_query(const char* kernel, double* total_ms, int64_t* launches);

@@ -359,6 +359,58 @@ ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o,
     return launch_status("ret_chunk_full");
 }
 
+// Workspace of the gradients: the segment chain the three retentions share (one call after another; at offset
+// 0, at least 256 bytes, so ret_chunkwise_check reads its header), then their rotated and reversed inputs
+// (bf16) and their fp32 outputs.
+struct BwdLayout {
+    size_t kp, kr, qr, vr, dor, g1, g2, g3, chain, chain_bytes, total;
+};
+bool bwd_layout(int B, int N, int H, int dk, int dv, int chunk, BwdLayout* L) {
+    ChunkKernels ca, cb;
+    if (!pick_chunk(RET_BF16, dv, dk, chunk, &ca) || !pick_chunk(RET_BF16, dk, dv, chunk, &cb)) return false;
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    const size_t nk = (size_t)B * N * H * dk, nv = (size_t)B * N * H * dv;
+    const size_t ka = plan_chunk(ca, B, N, H, dv, dk, chunk, false, SIZE_MAX).chain_bytes;
+    const size_t kb = plan_chunk(cb, B, N, H, dk, dv, chunk, false, SIZE_MAX).chain_bytes;
+    L->chain = 0;
+    L->chain_bytes = ka > kb ? ka : kb;
+    L->kp = up(L->chain_bytes > 256 ? L->chain_bytes : 256);
+    L->kr = L->kp + up(nk * 2);
+    L->qr = L->kr + up(nk * 2);
+    L->vr = L->qr + up(nk * 2);
+    L->dor = L->vr + up(nv * 2);
+    L->g1 = L->dor + up(nv * 2);
+    L->g2 = L->g1 + up(nk * 4);
+    L->g3 = L->g2 + up(nv * 4);
+    L->total = L->g3 + up(nk * 4);
+    return true;
+}
+
+ret_status_t permute(const void* in, void* out, int B, int N, int H, int d, bool in_rev, bool out_rev, int rot_sign,
+                     bool in_bf16, bool out_bf16, const double* theta, int64_t pos0, hipStream_t s) {
+    PermArgs P;
+    memset(&P, 0, sizeof(P));
+    P.in = in;
+    P.out = out;
+    P.B = B;
+    P.N = N;
+    P.H = H;
+    P.d = d;
+    P.in_rev = in_rev;
+    P.out_rev = out_rev;
+    P.rot_sign = theta ? rot_sign : 0;
+    P.in_bf16 = in_bf16;
+    P.out_bf16 = out_bf16;
+    P.pos0 = pos0;
+    if (theta)
+        for (int i = 0; i < d / 2; ++i) P.theta[i] = theta[i];
+    const long long threads = (long long)B * N * H * (d / 8);
+    LaunchTimer tm("ret_permute_rotate", s);
+    hipLaunchKernelGGL(permute_rotate_get(), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, P);
+    tm.done();
+    return launch_status("ret_permute_rotate");
+}
+
 }  // namespace
 
 extern "C" {
@@ -478,6 +530,61 @@ ret_status_t ret_msr_epilogue(const void* o, const void* gate, const float* gn_w
     hipLaunchKernelGGL(fn, dim3((unsigned)wgs), dim3(256), 0, s, A);
     tm.done();
     return launch_status("ret_msr_epilogue");
+}
+
+size_t ret_chunkwise_bwd_workspace_bytes(int B, int N, int H, int dk, int dv, int chunk) {
+    BwdLayout L;
+    if (B <= 0 || N <= 0 || H <= 0 || dk <= 0 || dv <= 0 || chunk <= 0) return 0;
+    if (!bwd_layout(B, N, H, dk, dv, chunk, &L)) return 0;
+    return L.total;
+}
+
+ret_status_t ret_chunkwise_bwd(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk_out,
+                               void* dv_out, int B, int N, int H, int dk, int dv, ret_dtype_t in_dt,
+                               ret_dtype_t out_dt, const float* gamma, const double* theta, int64_t pos0, int chunk,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+    ret_status_t st = check_common(q, k, v, dq, B, N, H, dk, dv, in_dt, out_dt, gamma, theta);
+    if (st != RET_OK) return st;
+    if (in_dt != RET_BF16) return fail(RET_ERR_UNSUPPORTED, "gradients: BF16 inputs only");
+    if (!dout || !dk_out || !dv_out) return fail(RET_ERR_INVALID_ARG, "null dout/dk/dv pointer");
+    if (!aligned16(dout) || !aligned16(dk_out) || !aligned16(dv_out))
+        return fail(RET_ERR_INVALID_ARG, "dout/dq/dk/dv must be 16-byte aligned");
+    for (const void* g : {(const void*)dq, (const void*)dk_out, (const void*)dv_out})
+        if (g == q || g == k || g == v || g == dout) return fail(RET_ERR_INVALID_ARG, "gradients must not alias inputs");
+    if (dq == dk_out || dq == dv_out || dk_out == dv_out) return fail(RET_ERR_INVALID_ARG, "dq, dk, dv must differ");
+    if (chunk <= 0) return fail(RET_ERR_INVALID_ARG, "chunk must be positive (got %d)", chunk);
+    BwdLayout L;
+    if (!bwd_layout(B, N, H, dk, dv, chunk, &L))
+        return fail(RET_ERR_UNSUPPORTED, "gradients: d_k=%d d_v=%d chunk=%d (needs d_k, d_v in {64,128,256})", dk, dv,
+                    chunk);
+    if (!workspace || workspace_bytes < L.total)
+        return fail(RET_ERR_WORKSPACE, "gradients need a workspace of %zu bytes (got %zu)", L.total, workspace_bytes);
+    if (!aligned16(workspace)) return fail(RET_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
+    char* ws = (char*)workspace;
+    void *Kp = ws + L.kp, *Kr = ws + L.kr, *Qr = ws + L.qr, *Vr = ws + L.vr, *dOr = ws + L.dor;
+    void *G1 = ws + L.g1, *G2 = ws + L.g2, *G3 = ws + L.g3, *chain = ws + L.chain;
+    // inputs of the three retentions: K' in order; K', Q', V and dO reversed
+    if ((st = permute(k, Kp, B, N, H, dk, false, false, 1, true, true, theta, pos0, s)) != RET_OK) return st;
+    if ((st = permute(k, Kr, B, N, H, dk, false, true, 1, true, true, theta, pos0, s)) != RET_OK) return st;
+    if ((st = permute(q, Qr, B, N, H, dk, false, true, 1, true, true, theta, pos0, s)) != RET_OK) return st;
+    if ((st = permute(v, Vr, B, N, H, dv, false, true, 0, true, true, nullptr, 0, s)) != RET_OK) return st;
+    if ((st = permute(dout, dOr, B, N, H, dv, false, true, 0, true, true, nullptr, 0, s)) != RET_OK) return st;
+    // dq' = retention(dO, V, K'); dv^rev = retention(K'^rev, Q'^rev, dO^rev); dk'^rev = retention(V^rev, dO^rev, Q'^rev)
+    if ((st = chunkwise_run(dout, v, Kp, G1, B, N, H, dv, dk, RET_BF16, RET_F32, gamma, nullptr, 0, chunk, nullptr,
+                            nullptr, chain, L.chain_bytes, stream, nullptr, nullptr)) != RET_OK)
+        return st;
+    if ((st = chunkwise_run(Kr, Qr, dOr, G2, B, N, H, dk, dv, RET_BF16, RET_F32, gamma, nullptr, 0, chunk, nullptr,
+                            nullptr, chain, L.chain_bytes, stream, nullptr, nullptr)) != RET_OK)
+        return st;
+    if ((st = chunkwise_run(Vr, dOr, Qr, G3, B, N, H, dv, dk, RET_BF16, RET_F32, gamma, nullptr, 0, chunk, nullptr,
+                            nullptr, chain, L.chain_bytes, stream, nullptr, nullptr)) != RET_OK)
+        return st;
+    // back to the caller's order, dq and dk turned back by the transpose rotation
+    const bool ob = out_dt == RET_BF16;
+    if ((st = permute(G1, dq, B, N, H, dk, false, false, -1, false, ob, theta, pos0, s)) != RET_OK) return st;
+    if ((st = permute(G3, dk_out, B, N, H, dk, true, false, -1, false, ob, theta, pos0, s)) != RET_OK) return st;
+    return permute(G2, dv_out, B, N, H, dv, true, false, 0, false, ob, nullptr, 0, s);
 }
 
 int ret_timing_enable(int on) {

@@ -981,6 +981,21 @@ struct EpiArgs {
     float eps;
 };
 typedef void (*epi_kernel_t)(EpiArgs);
+
+// Reordering / rotation of one [B, N, H, d] tensor (d a multiple of 8): output row (b, n, h) is token
+// t = out_rev ? N-1-n : n, read from input row in_rev ? N-1-t : t and turned by rot_sign (pos0 + t) theta_i on
+// pairs (2i, 2i+1) (rot_sign 0: copied; -1: the transpose rotation). One 256-thread workgroup per 2048 values.
+struct PermArgs {
+    const void* in;
+    void* out;
+    int B, N, H, d;
+    int in_rev, out_rev, rot_sign;
+    int in_bf16, out_bf16;
+    long long pos0;
+    double theta[kMaxPairs];
+};
+typedef void (*perm_kernel_t)(PermArgs);
+perm_kernel_t permute_rotate_get();
 // Kernel for d_v in {16, 32, 64, 128, 256, 512} (null otherwise) and its groups per 256-thread workgroup.
 epi_kernel_t epilogue_kernel_get(int dv, int* groups_per_wg);
 

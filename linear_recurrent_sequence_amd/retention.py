@@ -61,6 +61,11 @@ def load(build_if_missing: bool = True):
     lib.ret_chunkwise_msr_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, fp, dp, i64,
                                           i32, vp, vp, vp, vp, ctypes.c_float, vp, sz, vp]
     lib.ret_chunkwise_msr_fwd.restype = i32
+    lib.ret_chunkwise_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.ret_chunkwise_bwd_workspace_bytes.restype = sz
+    lib.ret_chunkwise_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, fp, dp, i64, i32,
+                                      vp, sz, vp]
+    lib.ret_chunkwise_bwd.restype = i32
     lib.ret_chunkwise_check.argtypes = [vp, vp]
     lib.ret_chunkwise_check.restype = i32
     lib.ret_timing_enable.argtypes = [i32]
@@ -229,6 +234,37 @@ def ret_chunkwise_msr_fwd(q, k, v, y, gamma, chunk, gate=None, gn_weight=None, g
                                    _dev(workspace, "workspace"), wsb, _stream(stream))
     _check("ret_chunkwise_msr_fwd", st)
     return y
+
+
+def chunkwise_bwd_workspace(q, v, chunk):
+    """A zero-filled workspace of ret_chunkwise_bwd_workspace_bytes for these shapes."""
+    B, N, H, dk = q.shape
+    nbytes = load().ret_chunkwise_bwd_workspace_bytes(B, N, H, dk, v.shape[3], int(chunk))
+    if nbytes == 0:
+        raise ValueError("gradients: unsupported shape")
+    return torch.zeros((nbytes,), dtype=torch.uint8, device=q.device)
+
+
+def ret_chunkwise_bwd(q, k, v, dout, dq, dk, dv, gamma, chunk, theta=None, pos0=0, workspace=None, stream=None):
+    """dq, dk, dv <- gradients of sum(dout (.) O), O = chunkwise retention of (q, k, v) from a zero state."""
+    lib = load()
+    B, N, H, d_k = q.shape
+    d_v = v.shape[3]
+    if tuple(dout.shape) != (B, N, H, d_v) or tuple(dq.shape) != tuple(q.shape) or tuple(dk.shape) != tuple(k.shape) \
+            or tuple(dv.shape) != tuple(v.shape):
+        raise ValueError("dout/dv must be [B,N,H,d_v] and dq/dk [B,N,H,d_k]")
+    if dout.dtype != q.dtype or dq.dtype != dk.dtype or dq.dtype != dv.dtype:
+        raise ValueError("dout must have the inputs' dtype and dq, dk, dv one dtype")
+    g, gp = _gamma(gamma, H)
+    th, tp = _theta(theta, d_k)
+    if workspace is None:
+        workspace = chunkwise_bwd_workspace(q, v, chunk)
+    wsb = workspace.numel() * workspace.element_size()
+    st = lib.ret_chunkwise_bwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(dout, "dout"), _dev(dq, "dq"),
+                               _dev(dk, "dk"), _dev(dv, "dv"), B, N, H, d_k, d_v, _dt(q), _dt(dq), gp, tp, int(pos0),
+                               int(chunk), _dev(workspace, "workspace"), wsb, _stream(stream))
+    _check("ret_chunkwise_bwd", st)
+    return dq, dk, dv
 
 
 def timing_enable(on: bool) -> bool:

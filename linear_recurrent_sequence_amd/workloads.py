@@ -115,3 +115,8 @@ def make_step(w: Workload, rng: np.random.Generator):
     k = normal(rng, (w.B, w.H, w.dk), w.scale, w.dtype)
     v = normal(rng, (w.B, w.H, w.dv), w.scale, w.dtype)
     return q, k, v
+
+
+def make_dout(w: Workload, rng: np.random.Generator):
+    """Draw an output gradient dL/dO ([B, N, H, dv]) for the gradient checks, drawn like V."""
+    return normal(rng, (w.B, w.N, w.H, w.dv), w.scale, w.dtype)

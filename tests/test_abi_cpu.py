@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ret_abi_version() == 2
+    assert lib.ret_abi_version() == 3
     assert lib.ret_status_string(0) == b"ok"
     assert lib.ret_status_string(-2) == b"unsupported shape or dtype"
 
@@ -128,3 +128,30 @@ def test_chunkwise_msr_rejects_invalid_arguments(lib):
     assert call(gw=8) == -1             # misaligned weight
     assert call(gate=64) == -1          # gate aliases y
     assert call(dv=96) == -2            # no epilogue for d_v = 96
+
+
+def test_gradients_workspace_and_rejections(lib):
+    """ret_chunkwise_bwd: workspace size from the shapes, host-side rejections before any launch."""
+    wsq = lib.ret_chunkwise_bwd_workspace_bytes
+    # five bf16 copies (K' twice, Q', V, dO) and three fp32 outputs of [8, 2048, 8, 64], then a segment chain
+    n = 8 * 2048 * 8 * 64
+    assert wsq(8, 2048, 8, 64, 64, 64) >= 5 * n * 2 + 3 * n * 4
+    assert wsq(8, 2048, 8, 64, 64, 64) % 256 == 0
+    assert wsq(1, 100, 2, 32, 64, 64) == 0      # d_k = 32: no bf16 kernel
+    assert wsq(1, 8192, 16, 256, 512, 128) == 0  # d_v = 512 would be the d_k of dq's retention
+    assert wsq(1, 0, 2, 64, 64, 64) == 0
+    g = np.asarray([0.9, 0.99], np.float32).ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+    need = wsq(1, 64, 2, 64, 64, 64)
+
+    def call(q=16, k=32, v=48, do=64, dq=80, dk=96, dv=112, ind=1, outd=0, ws=4096, wsb=None, chunk=64, dkk=64):
+        return lib.ret_chunkwise_bwd(q, k, v, do, dq, dk, dv, 1, 64, 2, dkk, 64, ind, outd, g, None, 0, chunk, ws,
+                                     need if wsb is None else wsb, None)
+    assert call(ind=0) == -2            # fp32 inputs: not supported
+    assert call(do=None) == -1          # null dout
+    assert call(dk=16) == -1            # dk aliases q
+    assert call(dv=80) == -1            # dv aliases dq
+    assert call(do=72) == -1            # misaligned dout
+    assert call(chunk=0) == -1
+    assert call(dkk=48) == -2           # no kernel for d_k = 48
+    assert call(wsb=need - 256) == -3   # workspace too small
+    assert call(ws=None) == -3
