@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define RET_ABI_VERSION 3
+#define RET_ABI_VERSION 4
 
 typedef enum { RET_F32 = 0, RET_BF16 = 1 } ret_dtype_t;
 
@@ -106,10 +106,10 @@ ret_status_t ret_chunkwise_check(const void* workspace, void* stream);
  * ret_recurrent_step. Results equal the recurrent and parallel forms up to rounding.
  * workspace: device memory of `workspace_bytes` (see ret_chunkwise_workspace_bytes), or NULL with 0.
  * Supported: F32 input: d_k in {16, 32, 64}, d_v a multiple of 16, chunk in {16, 32, 64}. BF16 input:
- * d_k in {32, 64, 128, 256}, d_v a multiple of 64, chunk in {32, 64, 128}. N >= 1. BF16 chunks of 128
- * are computed as pairs of 64-token chunks, which the chunkwise form allows (any chunk size gives the same
- * result up to rounding). Kernels that read a chunk address it with 32-bit offsets: chunk * H * max(d_k, d_v)
- * * 4 must stay below 2^31 (RET_ERR_UNSUPPORTED otherwise).
+ * d_k in {32, 64, 128, 256}, d_v a multiple of 64, chunk in {32, 64, 128, 256, 512}. N >= 1. BF16 chunks
+ * longer than 64 tokens are computed as runs of 64-token chunks, which the chunkwise form allows (any chunk
+ * size gives the same result up to rounding). Kernels that read a chunk address it with 32-bit offsets:
+ * chunk * H * max(d_k, d_v) * 4 must stay below 2^31 (RET_ERR_UNSUPPORTED otherwise).
  */
 ret_status_t ret_chunkwise_fwd(const void* q, const void* k, const void* v, void* o, int B, int N, int H, int dk,
                                int dv, ret_dtype_t in_dt, ret_dtype_t out_dt, const float* gamma,
@@ -125,6 +125,20 @@ ret_status_t ret_chunkwise_fwd(const void* q, const void* k, const void* v, void
 ret_status_t ret_recurrent_step(const void* q, const void* k, const void* v, void* o, float* state, int B, int H,
                                 int dk, int dv, ret_dtype_t in_dt, ret_dtype_t out_dt, const float* gamma,
                                 const double* theta, int64_t pos, void* stream);
+
+/*
+ * The decode step of ret_recurrent_step with one position per sequence: sequence b is at absolute position
+ * pos[b] (a batch of sequences at different lengths; the pages decode one token per step at its own position,
+ * paper summary Eq. 6 and "Overall RetNet Architecture and Training/Inference Protocol"). pos: device int64[B],
+ * 8-byte aligned, read by the kernel when it runs (a captured graph can advance it on the device); unused
+ * without theta. The rotation factors are evaluated on the device (fp64 angle reduced by pi/2, fp32 sine and
+ * cosine; angle error about pos * 2^-52 rad) rather than on the host, so results may differ from
+ * ret_recurrent_step in the last bits. Otherwise as ret_recurrent_step.
+ */
+ret_status_t ret_recurrent_step_positions(const void* q, const void* k, const void* v, void* o, float* state, int B,
+                                          int H, int dk, int dv, ret_dtype_t in_dt, ret_dtype_t out_dt,
+                                          const float* gamma, const double* theta, const int64_t* pos,
+                                          void* stream);
 
 /*
  * Multi-scale retention epilogue ("Hybrid Architectures: RetNet and the Three Computation Paradigms",
@@ -175,7 +189,8 @@ ret_status_t ret_chunkwise_msr_fwd(const void* q, const void* k, const void* v, 
  * workspace: device memory of ret_chunkwise_bwd_workspace_bytes (zero-filled once by the caller, like the
  * chunkwise workspace; every call leaves its chain part zeroed again; ret_chunkwise_check accepts it and
  * reports a segment-chain wait that gave up). dq, dk, dv must not alias the inputs
- * or each other. Supported: d_k, d_v in {64, 128, 256}, chunk in {32, 64, 128}. Asynchronous on `stream`.
+ * or each other. Supported: d_k, d_v in {64, 128, 256}, chunk in {32, 64, 128, 256, 512}. Asynchronous on
+ * `stream`.
  */
 size_t ret_chunkwise_bwd_workspace_bytes(int B, int N, int H, int dk, int dv, int chunk);
 ret_status_t ret_chunkwise_bwd(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk_out,

@@ -451,9 +451,14 @@ ret_status_t ret_chunkwise_msr_fwd(const void* q, const void* k, const void* v, 
                             stream);
 }
 
-ret_status_t ret_recurrent_step(const void* q, const void* k, const void* v, void* o, float* state, int B, int H,
-                                int dk, int dv, ret_dtype_t in_dt, ret_dtype_t out_dt, const float* gamma,
-                                const double* theta, int64_t pos, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// One decode step; positions either one for the call (`pos`) or one per sequence (`pos_dev`, device [B]).
+ret_status_t step_run(const void* q, const void* k, const void* v, void* o, float* state, int B, int H, int dk,
+                      int dv, ret_dtype_t in_dt, ret_dtype_t out_dt, const float* gamma, const double* theta,
+                      int64_t pos, const int64_t* pos_dev, void* stream) {
     ret_status_t st = check_common(q, k, v, o, B, 1, H, dk, dv, in_dt, out_dt, gamma, theta);
     if (st != RET_OK) return st;
     if (!state) return fail(RET_ERR_INVALID_ARG, "null state");
@@ -474,8 +479,12 @@ ret_status_t ret_recurrent_step(const void* q, const void* k, const void* v, voi
     A.out_bf16 = out_dt == RET_BF16;
     A.rotate = theta != nullptr;
     for (int h = 0; h < H; ++h) A.gamma[h] = gamma[h];
-    // Rotation factors of this step's position, in fp64 (one position per call).
-    if (theta)
+    // Rotation factors of this step's position, in fp64 (one position per call); with per-sequence positions
+    // the kernel makes them from theta.
+    A.pos = theta ? (const long long*)pos_dev : nullptr;
+    if (theta && pos_dev)
+        for (int i = 0; i < dk / 2; ++i) A.theta[i] = theta[i];
+    else if (theta)
         for (int i = 0; i < dk / 2; ++i) {
             const double ang = (double)pos * theta[i];
             A.rc[i] = (float)cos(ang);
@@ -483,13 +492,33 @@ ret_status_t ret_recurrent_step(const void* q, const void* k, const void* v, voi
         }
     int cw = 0, wr = 0, ppw = 1;
     step_kernel_t fn = step_kernel_get(in_dt == RET_BF16, dk, dv, B * H, env_int("RET_STEP_CW", 0),
-                                       env_int("RET_STEP_WR", 0), env_int("RET_STEP_PAIRS", 0), &cw, &wr, &ppw);
+                                       env_int("RET_STEP_WR", 0), env_int("RET_STEP_PAIRS", 0), A.pos != nullptr,
+                                       &cw, &wr, &ppw);
     if (!fn) return fail(RET_ERR_UNSUPPORTED, "decode step: d_k=%d not in {16,32,64,128,256}", dk);
     hipStream_t s = (hipStream_t)stream;
     LaunchTimer tm("ret_recurrent_step", s);
     hipLaunchKernelGGL(fn, dim3((dv + cw - 1) / cw, (B * H + ppw - 1) / ppw), dim3(64 * (dk / wr) * ppw), 0, s, A);
     tm.done();
     return launch_status("ret_recurrent_step");
+}
+
+}  // namespace
+
+extern "C" {
+
+ret_status_t ret_recurrent_step(const void* q, const void* k, const void* v, void* o, float* state, int B, int H,
+                                int dk, int dv, ret_dtype_t in_dt, ret_dtype_t out_dt, const float* gamma,
+                                const double* theta, int64_t pos, void* stream) {
+    return step_run(q, k, v, o, state, B, H, dk, dv, in_dt, out_dt, gamma, theta, pos, nullptr, stream);
+}
+
+ret_status_t ret_recurrent_step_positions(const void* q, const void* k, const void* v, void* o, float* state, int B,
+                                          int H, int dk, int dv, ret_dtype_t in_dt, ret_dtype_t out_dt,
+                                          const float* gamma, const double* theta, const int64_t* pos,
+                                          void* stream) {
+    if (!pos) return fail(RET_ERR_INVALID_ARG, "null pos");
+    if ((uintptr_t)pos % 8) return fail(RET_ERR_INVALID_ARG, "pos must be 8-byte aligned");
+    return step_run(q, k, v, o, state, B, H, dk, dv, in_dt, out_dt, gamma, theta, 0, pos, stream);
 }
 
 ret_status_t ret_msr_epilogue(const void* o, const void* gate, const float* gn_weight, const float* gn_bias,

@@ -1,4 +1,5 @@
-// bf16-input chunkwise kernels, d_k in {256}, chunk in {32, 64, 128}. Where d_v is a multiple of 128 the d_v
+// bf16-input chunkwise kernels, d_k in {256}, chunk in {32, 64, 128, 256, 512} (chunks longer than 64 tokens
+// run as 64-token sub-chunks: the instances differ only in the segment plan). Where d_v is a multiple of 128 the d_v
 // tile is 128 columns: 512 threads whose waves own 16 columns each (the default: two waves per SIMD), or 256
 // threads whose waves own 32 columns each (twice the operand reuse per LDS read, one wave per SIMD).
 // RET_DK256_THREADS picks 512, 256x2, or 256 (the 256-thread kernel with 16-column waves and d_v tiles of 64).
@@ -26,6 +27,7 @@ bool chunk_kernels_bf16_256(int dk, int dv, int C, ChunkKernels* out) {
     }
     RET_CASE(256, 32)
     RET_CASE(256, 64)
+    if (C == 256 || C == 512) C = 128;
     RET_CASE(256, 128)
 #undef RET_CASE
     return false;

@@ -1,4 +1,5 @@
-// bf16-input chunkwise kernels, d_k in {32, 64}, chunk in {32, 64, 128}, d_v tiles of 64.
+// bf16-input chunkwise kernels, d_k in {32, 64}, chunk in {32, 64, 128, 256, 512}, d_v tiles of 64. Chunks
+// longer than 64 tokens run as 64-token sub-chunks: the instances differ only in the segment plan.
 #include "chunk_seg_bf16.h"
 
 namespace ret {
@@ -20,10 +21,12 @@ bool chunk_kernels_bf16_small(int dk, int dv, int C, ChunkKernels* out) {
     if (dk == DKv && C == Cv) { *out = chunk_entry_small<DKv, Cv>(); return true; }
     RET_CASE(32, 32)
     RET_CASE(32, 64)
-    RET_CASE(32, 128)
     RET_CASE(64, 32)
     RET_CASE(64, 64)
-    RET_CASE(64, 128)
+    if ((dk == 32 || dk == 64) && (C == 128 || C == 256 || C == 512)) {
+        *out = dk == 32 ? chunk_entry_small<32, 128>() : chunk_entry_small<64, 128>();
+        return true;
+    }
 #undef RET_CASE
     return false;
 }

@@ -749,6 +749,9 @@ struct StepArgs {
     float gamma[kMaxHeads];
     // cos and sin of pos * theta_i for the step's position, evaluated on the host in fp64
     float rc[kMaxPairs], rs[kMaxPairs];
+    // Per-sequence positions (device [B], or null): the factors then come from pos[b] and theta in the kernel.
+    const long long* pos;
+    double theta[kMaxPairs];
 };
 
 __device__ __forceinline__ float ld_in(const void* p, long long i, int bf) {
@@ -806,7 +809,7 @@ __host__ __device__ constexpr int step_group_pairs(int dk, int wr) { return dk /
 // arrives, so loads and stores overlap. o sums q_r S_r over the rows (shuffles within a wave, LDS across waves).
 // Several pairs share a workgroup of up to 8 waves: fewer, larger workgroups reach the state sooner than many
 // small ones. Pairs past B*H (a partial last workgroup) load the last pair and store nothing.
-template <class E, int DK, int CW, int WR, int PPW>
+template <class E, int DK, int CW, int WR, int PPW, bool POS>
 __global__ __launch_bounds__(64 * (DK / WR) * PPW) void recurrent_step_kernel(StepArgs a) {
     typedef typename E::st st;
     constexpr int NW = DK / WR;                 // waves per pair
@@ -838,13 +841,19 @@ __global__ __launch_bounds__(64 * (DK / WR) * PPW) void recurrent_step_kernel(St
         __builtin_amdgcn_make_buffer_rsrc(a.state + (long long)pair * DK * dv, (short)0, sbytes, 0x00020000);
     const int svoff = active ? (r0 * dv + c0) * 4 : sbytes;
     float vv[4], qv[RPT], kv[RPT], rc[RPT / 2], rs[RPT / 2];
+    // POS: each sequence at its own position pos[b] (a scalar load, issued with the others and used after the
+    // state loads); otherwise the call's factors from the kernel arguments
+    long long ppos = 0;
+    if constexpr (POS) ppos = a.pos[pair / a.H];
     load_n<E, 4>(vp, vv);
     load_n<E, RPT>(qp, qv);
     load_n<E, RPT>(kp, kv);
 #pragma unroll
     for (int p = 0; p < RPT / 2; ++p) {  // read also without rotation, so that no branch holds them back
-        rc[p] = a.rc[r0 / 2 + p];
-        rs[p] = a.rs[r0 / 2 + p];
+        if constexpr (!POS) {
+            rc[p] = a.rc[r0 / 2 + p];
+            rs[p] = a.rs[r0 / 2 + p];
+        }
     }
     float4 x[RPT];
 #pragma unroll
@@ -857,6 +866,10 @@ __global__ __launch_bounds__(64 * (DK / WR) * PPW) void recurrent_step_kernel(St
     // which holds for loads among themselves only.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __builtin_amdgcn_sched_barrier(0);  // every load above is issued before any of the work below
+    if constexpr (POS) {  // this sequence's own position: factors by rot_cs, as in the chunkwise kernels
+#pragma unroll
+        for (int p = 0; p < RPT / 2; ++p) rot_cs(ppos, a.theta[r0 / 2 + p], &rc[p], &rs[p]);
+    }
     // The pair (r0 + 2p, r0 + 2p + 1) turns by the angle pos * theta_(r0/2 + p); without rotation the inputs
     // pass unchanged (a select, not a branch: the factor loads stay ahead of the state loads).
     const bool rot = a.rotate != 0;
@@ -965,8 +978,9 @@ bool parallel_kernel_get(bool bf16_in, int dk, int dv, ParKernel* out);
 // Decode kernel for a (d_k, column tile cw, rows per wave wr) tile, 0 = default, null if none; with pairs_mode 0
 // it groups (b, h) pairs into workgroups of up to 8 waves where B*H leaves a workgroup per CU; 1 / 2 force one
 // / grouped. The launch is ceil(d_v / cw) x ceil(B*H / ppw) workgroups of 64 * (d_k / wr) * ppw threads.
-step_kernel_t step_kernel_get(bool bf16_in, int dk, int dv, int npairs, int cw, int wr, int pairs_mode, int* cw_used,
-                              int* wr_used, int* ppw_used);
+// positions: the per-sequence-position kernel (default tile only: cw and wr are ignored).
+step_kernel_t step_kernel_get(bool bf16_in, int dk, int dv, int npairs, int cw, int wr, int pairs_mode,
+                              bool positions, int* cw_used, int* wr_used, int* ppw_used);
 
 // Multi-scale retention epilogue y = swish(gate) (.) GroupNorm_h(o) over groups of d_v values.
 struct EpiArgs {

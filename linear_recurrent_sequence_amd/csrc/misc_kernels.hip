@@ -106,14 +106,26 @@ bool parallel_kernel_get(bool bf16_in, int dk, int dv, ParKernel* out) {
 // least one pair of rows: rows per lane = wr * cw / 256 >= 2. Workgroups hold one (b, h) pair, or as many as
 // fill 8 waves (step_group_pairs).
 namespace {
-template <class E, int DK, int CW, int WR>
+template <class E, int DK, int CW, int WR, bool POS = false>
 step_kernel_t step_pick(bool grouped) {
     if constexpr (WR <= DK && WR * CW >= 512 && DK / WR <= 16) {
         constexpr int G = step_group_pairs(DK, WR);
-        if (grouped && G > 1) return recurrent_step_kernel<E, DK, CW, WR, G>;
-        return recurrent_step_kernel<E, DK, CW, WR, 1>;
+        if (grouped && G > 1) return recurrent_step_kernel<E, DK, CW, WR, G, POS>;
+        return recurrent_step_kernel<E, DK, CW, WR, 1, POS>;
     }
     return nullptr;
+}
+// Per-sequence positions: the default tile of each d_k (64 columns; 32 rows per wave, d_k rows below 32).
+template <class E>
+step_kernel_t step_pick_positions(int dk, bool grouped) {
+    switch (dk) {
+        case 16: return step_pick<E, 16, 64, 16, true>(grouped);
+        case 32: return step_pick<E, 32, 64, 32, true>(grouped);
+        case 64: return step_pick<E, 64, 64, 32, true>(grouped);
+        case 128: return step_pick<E, 128, 64, 32, true>(grouped);
+        case 256: return step_pick<E, 256, 64, 32, true>(grouped);
+        default: return nullptr;
+    }
 }
 template <class E, int DK, int CW>
 step_kernel_t step_pick_wr(int wr, bool grouped) {
@@ -140,10 +152,10 @@ step_kernel_t step_pick_dk(int dk, int cw, int wr, bool grouped) {
 }
 }  // namespace
 
-step_kernel_t step_kernel_get(bool bf16_in, int dk, int dv, int npairs, int cw, int wr, int pairs_mode, int* cw_used,
-                              int* wr_used, int* ppw_used) {
-    if (cw == 0) cw = 64;  // defaults: 64 columns x 32 rows per wave (two waves per 64-row tile)
-    if (wr == 0) wr = 32;
+step_kernel_t step_kernel_get(bool bf16_in, int dk, int dv, int npairs, int cw, int wr, int pairs_mode,
+                              bool positions, int* cw_used, int* wr_used, int* ppw_used) {
+    if (cw == 0 || positions) cw = 64;  // defaults: 64 columns x 32 rows per wave (two waves per 64-row tile)
+    if (wr == 0 || positions) wr = 32;
     if (cw != 16 && cw != 32 && cw != 64) return nullptr;
     if (wr != 16 && wr != 32 && wr != 64) return nullptr;
     if (wr > dk) wr = dk < 16 ? 16 : dk;                // short d_k: one wave holds every row
@@ -156,6 +168,7 @@ step_kernel_t step_kernel_get(bool bf16_in, int dk, int dv, int npairs, int cw, 
     const long long wgs = (long long)(npairs + g - 1) / g * ((dv + cw - 1) / cw);
     const bool grouped = g > 1 && (pairs_mode == 2 || (pairs_mode == 0 && wgs >= 256));
     *ppw_used = grouped ? g : 1;
+    if (positions) return bf16_in ? step_pick_positions<BF16>(dk, grouped) : step_pick_positions<F32>(dk, grouped);
     return bf16_in ? step_pick_dk<BF16>(dk, cw, wr, grouped) : step_pick_dk<F32>(dk, cw, wr, grouped);
 }
 

@@ -56,6 +56,8 @@ def load(build_if_missing: bool = True):
     lib.ret_chunkwise_fwd.restype = i32
     lib.ret_recurrent_step.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, fp, dp, i64, vp]
     lib.ret_recurrent_step.restype = i32
+    lib.ret_recurrent_step_positions.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, fp, dp, vp, vp]
+    lib.ret_recurrent_step_positions.restype = i32
     lib.ret_msr_epilogue.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, ctypes.c_float, vp]
     lib.ret_msr_epilogue.restype = i32
     lib.ret_chunkwise_msr_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, fp, dp, i64,
@@ -188,6 +190,25 @@ def ret_recurrent_step(q, k, v, o, state, gamma, pos, theta=None, stream=None):
     st = lib.ret_recurrent_step(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"), _dev(state, "state"), B, H,
                                 dk, dv, _dt(q), _dt(o), gp, tp, int(pos), _stream(stream))
     _check("ret_recurrent_step", st)
+    return o
+
+
+def ret_recurrent_step_positions(q, k, v, o, state, gamma, pos, theta=None, stream=None):
+    """One decode step with sequence b at position pos[b] (pos: int64 [B] on the device, read when the kernel
+    runs)."""
+    lib = load()
+    B, H, dk = q.shape
+    dv = v.shape[2]
+    if state.dtype != torch.float32 or tuple(state.shape) != (B, H, dk, dv):
+        raise ValueError("state must be float32 [B,H,dk,dv]")
+    if pos.dtype != torch.int64 or tuple(pos.shape) != (B,) or not pos.is_contiguous():
+        raise ValueError("pos must be a contiguous int64 tensor [B]")
+    g, gp = _gamma(gamma, H)
+    th, tp = _theta(theta, dk)
+    st = lib.ret_recurrent_step_positions(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"),
+                                          _dev(state, "state"), B, H, dk, dv, _dt(q), _dt(o), gp, tp,
+                                          _dev(pos, "pos"), _stream(stream))
+    _check("ret_recurrent_step_positions", st)
     return o
 
 

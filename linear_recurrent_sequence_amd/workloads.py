@@ -24,6 +24,12 @@ def gamma_schedule(h: int) -> np.ndarray:
     return (1.0 - np.exp2(-5.0 - np.arange(h, dtype=np.float64))).astype(np.float32)
 
 
+def gamma_schedule_loglinear(h: int) -> np.ndarray:
+    """The larger models' schedule gamma = 1 - exp(linspace(log 1/32, log 1/512, h)) ([Paper] summary, multi-scale
+    retention): 1 - gamma runs geometrically from 1/32 to 1/512; fp32 (h >= 2)."""
+    return (1.0 - np.exp(np.linspace(np.log(1.0 / 32), np.log(1.0 / 512), h))).astype(np.float32)
+
+
 def theta_schedule(dk: int) -> np.ndarray:
     """theta_i = 10000^(-2i/dk) for i = 0..dk/2-1, fp64."""
     i = np.arange(dk // 2, dtype=np.float64)

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ret_abi_version() == 3
+    assert lib.ret_abi_version() == 4
     assert lib.ret_status_string(0) == b"ok"
     assert lib.ret_status_string(-2) == b"unsupported shape or dtype"
 
@@ -99,6 +99,15 @@ def test_step_and_parallel_reject_invalid_arguments(lib):
     assert lib.ret_recurrent_step(16, 32, 48, 64, 80, 1, 1, 48, 64, 1, 1, g, None, 0, None) == -2
     assert lib.ret_parallel_fwd(16, 32, 48, 64, 1, 8, 1, 48, 64, 1, 1, g, None, 0, None) == -2
     assert lib.ret_parallel_fwd(16, 32, 48, 64, 1, -1, 1, 64, 64, 1, 1, g, None, 0, None) == -1
+
+
+def test_step_positions_rejects_invalid_arguments(lib):
+    g = np.asarray([0.9], np.float32).ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+    call = lambda pos=96, dk=64: lib.ret_recurrent_step_positions(16, 32, 48, 64, 80, 1, 1, dk, 64, 1, 1, g, None,
+                                                                  pos, None)
+    assert call(pos=None) == -1         # positions are required
+    assert call(pos=100) == -1          # misaligned positions
+    assert call(dk=48) == -2            # no decode tile for d_k = 48
 
 
 def test_epilogue_rejects_invalid_arguments(lib):

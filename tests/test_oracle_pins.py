@@ -126,6 +126,16 @@ def test_gamma_schedule_table(golden):
     np.testing.assert_array_equal(np.round(win).astype(int), gt["effective_window_printed"][:4])
 
 
+def test_gamma_schedule_loglinear():
+    """The larger models' schedule: endpoints 1 - 1/32 and 1 - 1/512 (exact in fp32), 1 - gamma in geometric
+    progression between them, decays strictly slower head by head."""
+    g = workloads.gamma_schedule_loglinear(16).astype(np.float64)
+    assert g[0] == 1 - 1 / 32 and g[-1] == 1 - 1 / 512
+    ratios = (1 - g[1:]) / (1 - g[:-1])
+    np.testing.assert_allclose(ratios, (1 / 16) ** (1 / 15), rtol=1e-5)
+    assert np.all(np.diff(g) > 0)
+
+
 def _complex_unrolled(q, k, v, g, theta, pos0):
     """Paper summary's unrolled form in complex numbers, pure Python, for tiny inputs:
     o_n = sum_{m<=n} gamma^(n-m) Re[(Qc_n e^{i p_n theta}) (Kc_m e^{i p_m theta})^dagger] v_m."""

@@ -1,0 +1,206 @@
+"""GPU parity of the parameter variants against the fp64 oracle: chunk sizes of 256 and 512 (the paper's
+training chunk, with its d_k = 256, d_v = 512 heads), the larger models' decay schedule and the single-rate and
+no-decay ablations, and decode steps with one position per sequence.
+
+Bar (max|gpu - oracle| / max|oracle|): 1e-5 for fp32 inputs, 2e-2 for bf16 inputs.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from linear_recurrent_sequence_amd import workloads as W
+from tests.conftest import print_case
+from tests.helpers import empty_out, rel_err, to_dev, to_host, tol
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def R():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from linear_recurrent_sequence_amd import retention
+    retention.load(build_if_missing=True)
+    return retention
+
+
+def _chunkwise(R, q, k, v, dt, gamma, chunk, theta, pos0, s0):
+    import torch
+    qd, kd, vd = to_dev(q, dt), to_dev(k, dt), to_dev(v, dt)
+    B, N, H, dk = q.shape
+    dv = v.shape[3]
+    o = empty_out((B, N, H, dv), dt)
+    sin = None if s0 is None else torch.from_numpy(np.ascontiguousarray(s0, np.float32)).cuda()
+    sout = torch.empty((B, H, dk, dv), dtype=torch.float32, device="cuda")
+    ws = R.chunkwise_workspace(qd, vd, chunk)
+    R.ret_chunkwise_fwd(qd, kd, vd, o, gamma, chunk, theta=theta, pos0=pos0, state_in=sin, state_out=sout,
+                        workspace=ws)
+    torch.cuda.synchronize()
+    R.ret_chunkwise_check(ws)
+    return to_host(o), to_host(sout)
+
+
+LONG_CHUNKS = [
+    # B, N, H, dk, dv, chunk, pos0, state_in
+    (1, 1500, 2, 64, 64, 256, 3, False),
+    (2, 700, 2, 64, 128, 512, 0, True),
+    (1, 1100, 2, 128, 128, 512, 9, True),
+    (1, 1300, 2, 256, 512, 512, 0, True),   # the paper's training shape: d_k 256, d_v 512, chunk 512
+    (1, 2600, 1, 256, 128, 256, 1, False),
+]
+
+
+@pytest.mark.parametrize("case", LONG_CHUNKS, ids=lambda c: "B%d-N%d-H%d-dk%d-dv%d-C%d" % c[:6])
+def test_chunkwise_long_chunks(R, case):
+    B, N, H, dk, dv, C, pos0, with_state = case
+    print_case("long_chunks", case)
+    rng = np.random.default_rng(500 + N)
+    q = W.normal(rng, (B, N, H, dk), np.sqrt(dk), "bf16")
+    k = W.normal(rng, (B, N, H, dk), np.sqrt(dk), "bf16")
+    v = W.normal(rng, (B, N, H, dv), 1.0, "bf16")
+    s0 = rng.standard_normal((B, H, dk, dv)).astype(np.float32) if with_state else None
+    gamma, theta = W.gamma_schedule(H), W.theta_schedule(dk)
+    o_ref, s_ref = oracle.chunkwise(q, k, v, gamma, C, theta=theta, pos0=pos0, state_in=s0)
+    o, s = _chunkwise(R, q, k, v, "bf16", gamma, C, theta, pos0, s0)
+    eo, es = rel_err(o, o_ref), rel_err(s, s_ref)
+    print("  err o=%.3g state=%.3g" % (eo, es))
+    assert eo <= tol("bf16") and es <= tol("bf16"), (eo, es)
+
+
+def test_7b_class_layer_at_chunk_512(R):
+    """The 7b-class-layer workload (B=1, N=8192, H=16, d_k=256, d_v=512) at the paper's chunk of 512."""
+    w = W.WORKLOADS[4]
+    print_case("workload4-chunk512", w)
+    q, k, v, _ = W.make_qkv(w)
+    o_ref, s_ref = oracle.chunkwise(q, k, v, w.gamma, 512, theta=w.theta)
+    o, s = _chunkwise(R, q, k, v, "bf16", w.gamma, 512, w.theta, 0, None)
+    eo, es = rel_err(o, o_ref), rel_err(s, s_ref)
+    print("  err o=%.3g state=%.3g" % (eo, es))
+    assert eo <= tol("bf16") and es <= tol("bf16"), (eo, es)
+
+
+SCHEDULES = {
+    "loglinear": lambda H: W.gamma_schedule_loglinear(H),
+    "single_rate": lambda H: np.full(H, 127 / 128, np.float32),
+    "no_decay": lambda H: np.ones(H, np.float32),
+}
+
+
+@pytest.mark.parametrize("dt,dk,dv,C", [("f32", 32, 48, 32), ("bf16", 64, 64, 64), ("bf16", 128, 128, 128)])
+@pytest.mark.parametrize("sched", sorted(SCHEDULES))
+def test_decay_schedules_chunkwise_then_steps(R, sched, dt, dk, dv, C):
+    """Chunkwise prefill, then decode steps from the GPU's own state, under each decay schedule."""
+    import torch
+    print_case("schedule", sched, dt, dk, dv, C)
+    B, N, H, steps = 2, 333, 4, 6
+    rng = np.random.default_rng(77)
+    scale = 1.0 if dt == "f32" else float(np.sqrt(dk))
+    q = W.normal(rng, (B, N + steps, H, dk), scale, dt)
+    k = W.normal(rng, (B, N + steps, H, dk), scale, dt)
+    v = W.normal(rng, (B, N + steps, H, dv), 1.0, dt)
+    gamma, theta = SCHEDULES[sched](H), W.theta_schedule(dk)
+    o_ref, s_ref = oracle.recurrent(q, k, v, gamma, theta=theta)
+    qd, kd, vd = to_dev(q, dt), to_dev(k, dt), to_dev(v, dt)
+    o = empty_out((B, N, H, dv), dt)
+    state = torch.empty((B, H, dk, dv), dtype=torch.float32, device="cuda")
+    ws = R.chunkwise_workspace(qd[:, :N].contiguous(), vd[:, :N].contiguous(), C)
+    R.ret_chunkwise_fwd(qd[:, :N].contiguous(), kd[:, :N].contiguous(), vd[:, :N].contiguous(), o, gamma, C,
+                        theta=theta, state_out=state, workspace=ws)
+    outs = []
+    for t in range(N, N + steps):
+        ot = empty_out((B, H, dv), dt)
+        R.ret_recurrent_step(qd[:, t].contiguous(), kd[:, t].contiguous(), vd[:, t].contiguous(), ot, state, gamma,
+                             pos=t, theta=theta)
+        outs.append(ot)
+    torch.cuda.synchronize()
+    R.ret_chunkwise_check(ws)
+    got = np.concatenate([to_host(o), np.stack([to_host(x) for x in outs], axis=1)], axis=1)
+    eo, es = rel_err(got, o_ref), rel_err(to_host(state), s_ref)
+    print("  err o=%.3g state=%.3g" % (eo, es))
+    assert eo <= tol(dt) and es <= tol(dt), (eo, es)
+
+
+def _steps_per_position(q, k, v, gamma, theta, s0, pos):
+    """Oracle: each sequence b stepped on its own at its own position."""
+    B = q.shape[0]
+    o = np.zeros((B,) + v.shape[1:])
+    s = np.zeros(s0.shape)
+    for b in range(B):
+        ob, sb = oracle.recurrent_step(q[b:b + 1], k[b:b + 1], v[b:b + 1], gamma, s0[b:b + 1], int(pos[b]),
+                                       theta=theta)
+        o[b], s[b] = ob[0], sb[0]
+    return o, s
+
+
+@pytest.mark.parametrize("pairs", ["0", "2"])
+@pytest.mark.parametrize("dt,dk,dv", [("f32", 16, 16), ("f32", 64, 36), ("bf16", 64, 64), ("bf16", 128, 128),
+                                      ("bf16", 256, 200)])
+def test_step_per_sequence_positions(R, dt, dk, dv, pairs, monkeypatch):
+    import torch
+    print_case("step_positions", dt, dk, dv, pairs)
+    monkeypatch.setenv("RET_STEP_PAIRS", pairs)
+    rng = np.random.default_rng(21)
+    B, H = 6, 3
+    pos = np.array([0, 5, 100, 65536, 3, 1 << 30], np.int64)
+    scale = 1.0 if dt == "f32" else 8.0
+    q = W.normal(rng, (B, H, dk), scale, dt)
+    k = W.normal(rng, (B, H, dk), scale, dt)
+    v = W.normal(rng, (B, H, dv), scale, dt)
+    s0 = rng.standard_normal((B, H, dk, dv)).astype(np.float32)
+    gamma, theta = W.gamma_schedule(H), W.theta_schedule(dk)
+    o_ref, s_ref = _steps_per_position(q, k, v, gamma, theta, s0, pos)
+    state = torch.from_numpy(s0).cuda()
+    o = empty_out((B, H, dv), dt)
+    R.ret_recurrent_step_positions(to_dev(q, dt), to_dev(k, dt), to_dev(v, dt), o, state, gamma,
+                                   torch.from_numpy(pos).cuda(), theta=theta)
+    torch.cuda.synchronize()
+    eo, es = rel_err(to_host(o), o_ref), rel_err(to_host(state), s_ref)
+    print("  err o=%.3g state=%.3g" % (eo, es))
+    assert eo <= tol(dt) and es <= tol(dt), (eo, es)
+
+
+def test_step_positions_advanced_on_device_in_a_graph(R):
+    """Eight steps captured in a HIP graph, the positions advanced by a device add between steps; replayed
+    three times (the state carries on) and checked against the oracle after every replay."""
+    import torch
+    print_case("step_positions_graph")
+    rng = np.random.default_rng(22)
+    B, H, dk, dv, n = 4, 2, 64, 64, 8
+    q = W.normal(rng, (3 * n, B, H, dk), 8.0, "bf16")
+    k = W.normal(rng, (3 * n, B, H, dk), 8.0, "bf16")
+    v = W.normal(rng, (3 * n, B, H, dv), 8.0, "bf16")
+    gamma, theta = W.gamma_schedule(H), W.theta_schedule(dk)
+    start = np.array([7, 0, 300, 12], np.int64)
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    qs, ks, vs = (torch.empty_like(x[:n]) for x in (qd, kd, vd))
+    state = torch.zeros((B, H, dk, dv), dtype=torch.float32, device="cuda")
+    pos = torch.from_numpy(start.copy()).cuda()
+    outs = torch.empty((n, B, H, dv), dtype=torch.bfloat16, device="cuda")
+
+    def steps():
+        for t in range(n):
+            R.ret_recurrent_step_positions(qs[t], ks[t], vs[t], outs[t], state, gamma, pos, theta=theta)
+            pos.add_(1)
+
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            steps()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    ref_state = np.zeros((B, H, dk, dv))
+    for rep in range(3):
+        qs.copy_(qd[rep * n:(rep + 1) * n]), ks.copy_(kd[rep * n:(rep + 1) * n]), vs.copy_(vd[rep * n:(rep + 1) * n])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for t in range(n):
+            o_ref, ref_state = _steps_per_position(q[rep * n + t], k[rep * n + t], v[rep * n + t], gamma, theta,
+                                                   ref_state, start + rep * n + t)
+            e = rel_err(to_host(outs[t]), o_ref)
+            assert e <= tol("bf16"), (rep, t, e)
+        assert rel_err(to_host(state), ref_state) <= tol("bf16")
+        assert np.array_equal(pos.cpu().numpy(), start + (rep + 1) * n)
