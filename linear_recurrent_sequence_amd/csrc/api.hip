@@ -386,27 +386,29 @@ bool bwd_layout(int B, int N, int H, int dk, int dv, int chunk, BwdLayout* L) {
     return true;
 }
 
-ret_status_t permute(const void* in, void* out, int B, int N, int H, int d, bool in_rev, bool out_rev, int rot_sign,
-                     bool in_bf16, bool out_bf16, const double* theta, int64_t pos0, hipStream_t s) {
+// One launch of permute_rotate_kernel over the given jobs (at most kMaxPermJobs), one grid row per job.
+ret_status_t permute(const PermJob* jobs, int njobs, int B, int N, int H, const double* theta, int64_t pos0,
+                     hipStream_t s) {
     PermArgs P;
     memset(&P, 0, sizeof(P));
-    P.in = in;
-    P.out = out;
     P.B = B;
     P.N = N;
     P.H = H;
-    P.d = d;
-    P.in_rev = in_rev;
-    P.out_rev = out_rev;
-    P.rot_sign = theta ? rot_sign : 0;
-    P.in_bf16 = in_bf16;
-    P.out_bf16 = out_bf16;
     P.pos0 = pos0;
+    unsigned long long segs = 0;
+    for (int j = 0; j < njobs; ++j) {
+        P.job[j] = jobs[j];
+        if (!theta) P.job[j].rot = 0;
+        const unsigned long long sj = (unsigned long long)H * jobs[j].d / 8;
+        if (sj > segs) segs = sj;
+    }
     if (theta)
-        for (int i = 0; i < d / 2; ++i) P.theta[i] = theta[i];
-    const long long threads = (long long)B * N * H * (d / 8);
+        for (int i = 0; i < kMaxPairs; ++i) P.theta[i] = i < jobs[0].d / 2 ? theta[i] : 0.0;
+    const unsigned long long threads = (unsigned long long)B * ((N + kPermTokens - 1) / kPermTokens) * segs;
+    if ((long long)B * N >= (1LL << 31) || threads > 0xFFFFFF00ull)
+        return fail(RET_ERR_UNSUPPORTED, "gradients: B*N*H*max(d_k,d_v) too large for one reordering launch");
     LaunchTimer tm("ret_permute_rotate", s);
-    hipLaunchKernelGGL(permute_rotate_get(), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, P);
+    hipLaunchKernelGGL(permute_rotate_get(), dim3((unsigned)((threads + 255) / 256), njobs), dim3(256), 0, s, P);
     tm.done();
     return launch_status("ret_permute_rotate");
 }
@@ -593,12 +595,14 @@ ret_status_t ret_chunkwise_bwd(const void* q, const void* k, const void* v, cons
     char* ws = (char*)workspace;
     void *Kp = ws + L.kp, *Kr = ws + L.kr, *Qr = ws + L.qr, *Vr = ws + L.vr, *dOr = ws + L.dor;
     void *G1 = ws + L.g1, *G2 = ws + L.g2, *G3 = ws + L.g3, *chain = ws + L.chain;
-    // inputs of the three retentions: K' in order; K', Q', V and dO reversed
-    if ((st = permute(k, Kp, B, N, H, dk, false, false, 1, true, true, theta, pos0, s)) != RET_OK) return st;
-    if ((st = permute(k, Kr, B, N, H, dk, false, true, 1, true, true, theta, pos0, s)) != RET_OK) return st;
-    if ((st = permute(q, Qr, B, N, H, dk, false, true, 1, true, true, theta, pos0, s)) != RET_OK) return st;
-    if ((st = permute(v, Vr, B, N, H, dv, false, true, 0, true, true, nullptr, 0, s)) != RET_OK) return st;
-    if ((st = permute(dout, dOr, B, N, H, dv, false, true, 0, true, true, nullptr, 0, s)) != RET_OK) return st;
+    // inputs of the three retentions: K' in order; K', Q', V and dO reversed (one launch)
+    const PermJob pre[4] = {
+        {k, {Kp, Kr}, dk, 1, 0, {0, 1}, 1, 1},
+        {q, {Qr, nullptr}, dk, 1, 0, {1, 0}, 1, 1},
+        {v, {Vr, nullptr}, dv, 0, 0, {1, 0}, 1, 1},
+        {dout, {dOr, nullptr}, dv, 0, 0, {1, 0}, 1, 1},
+    };
+    if ((st = permute(pre, 4, B, N, H, theta, pos0, s)) != RET_OK) return st;
     // dq' = retention(dO, V, K'); dv^rev = retention(K'^rev, Q'^rev, dO^rev); dk'^rev = retention(V^rev, dO^rev, Q'^rev)
     if ((st = chunkwise_run(dout, v, Kp, G1, B, N, H, dv, dk, RET_BF16, RET_F32, gamma, nullptr, 0, chunk, nullptr,
                             nullptr, chain, L.chain_bytes, stream, nullptr, nullptr)) != RET_OK)
@@ -610,10 +614,13 @@ ret_status_t ret_chunkwise_bwd(const void* q, const void* k, const void* v, cons
                             nullptr, chain, L.chain_bytes, stream, nullptr, nullptr)) != RET_OK)
         return st;
     // back to the caller's order, dq and dk turned back by the transpose rotation
-    const bool ob = out_dt == RET_BF16;
-    if ((st = permute(G1, dq, B, N, H, dk, false, false, -1, false, ob, theta, pos0, s)) != RET_OK) return st;
-    if ((st = permute(G3, dk_out, B, N, H, dk, true, false, -1, false, ob, theta, pos0, s)) != RET_OK) return st;
-    return permute(G2, dv_out, B, N, H, dv, true, false, 0, false, ob, nullptr, 0, s);
+    const int ob = out_dt == RET_BF16;
+    const PermJob post[3] = {
+        {G1, {dq, nullptr}, dk, -1, 0, {0, 0}, 0, ob},
+        {G3, {dk_out, nullptr}, dk, -1, 1, {0, 0}, 0, ob},
+        {G2, {dv_out, nullptr}, dv, 0, 1, {0, 0}, 0, ob},
+    };
+    return permute(post, 3, B, N, H, theta, pos0, s);
 }
 
 int ret_timing_enable(int on) {

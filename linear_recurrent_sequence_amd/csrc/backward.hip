@@ -7,55 +7,81 @@
 //   dv_m  = sum_{n>=m} gamma^(n-m) (q'_n . k'_m) dO_n     retention of (K', Q', dO) over the reversed sequence
 //   dk'_m = sum_{n>=m} gamma^(n-m) (dO_n . v_m) q'_n      retention of (V, dO, Q') over the reversed sequence
 // and dq, dk are dq', dk' turned back by the transpose rotation. The forward chunkwise kernels compute the three
-// retentions; this kernel prepares their inputs (rotated, reversed) and finishes their outputs (reversed back,
-// rotated back).
+// retentions; this kernel prepares their inputs (rotated, reversed) in one launch and finishes their outputs
+// (reversed back, rotated back) in another.
 #include "kernels.h"
 
 namespace ret {
 
 namespace {
 
-// One thread: 8 consecutive dims (4 rotation pairs) of one output row. Output row (b, n, h) is token
-// t = out_rev ? N-1-n : n; it is read from input row in_rev ? N-1-t : t and turned by rot_sign (pos0 + t) theta_i.
-__global__ __launch_bounds__(256) void permute_rotate_kernel(PermArgs a) {
-    const int segs = a.d / 8;
-    const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
-    const long long rows = (long long)a.B * a.N * a.H;
-    if (gid >= rows * segs) return;
-    const int sg = (int)(gid % segs);
-    const long long row = gid / segs;  // ((b * N) + n) * H + h
-    const int h = (int)(row % a.H);
-    const long long bn = row / a.H;
-    const int n = (int)(bn % a.N);
-    const long long b = bn / a.N;
-    const int t = a.out_rev ? a.N - 1 - n : n;
-    const int src = a.in_rev ? a.N - 1 - t : t;
-    const long long ii = ((b * a.N + src) * a.H + h) * a.d + sg * 8;
-    const long long oi = row * a.d + sg * 8;
-    float x[8];
-    if (a.in_bf16) {
-        unpack8_bf16(*reinterpret_cast<const uint4*>((const uint16_t*)a.in + ii), x);
+// One thread: one 16-byte segment (8 values, 4 rotation pairs) of kPermTokens consecutive tokens' rows of one
+// job (blockIdx.y: the job's fields are scalar loads). Its loads are issued together; the rotation factors of
+// the first token are evaluated exactly and carried to the next by angle addition with the one-token step.
+// Consecutive threads take consecutive segments of a row, and a job with two outputs writes both from one read.
+__device__ __forceinline__ void perm_load(const PermJob& J, long long i, float* x) {
+    if (J.in_bf16) {
+        unpack8_bf16(*reinterpret_cast<const uint4*>((const uint16_t*)J.in + i), x);
     } else {
-        const float4 u = *reinterpret_cast<const float4*>((const float*)a.in + ii);
-        const float4 w = *reinterpret_cast<const float4*>((const float*)a.in + ii + 4);
+        const float4 u = *reinterpret_cast<const float4*>((const float*)J.in + i);
+        const float4 w = *reinterpret_cast<const float4*>((const float*)J.in + i + 4);
         x[0] = u.x, x[1] = u.y, x[2] = u.z, x[3] = u.w, x[4] = w.x, x[5] = w.y, x[6] = w.z, x[7] = w.w;
     }
-    if (a.rot_sign) {
+}
+
+__device__ __forceinline__ void perm_store(const PermJob& J, void* out, long long i, const float* x) {
+    if (J.out_bf16) {
+        *reinterpret_cast<uint4*>((uint16_t*)out + i) = pack8_bf16(x);
+    } else {
+        *reinterpret_cast<float4*>((float*)out + i) = make_float4(x[0], x[1], x[2], x[3]);
+        *reinterpret_cast<float4*>((float*)out + i + 4) = make_float4(x[4], x[5], x[6], x[7]);
+    }
+}
+
+__global__ __launch_bounds__(256) void permute_rotate_kernel(PermArgs a) {
+    const PermJob J = a.job[blockIdx.y];
+    const unsigned segs = (unsigned)(a.H * J.d / 8);  // segments of one token's row: h * d / 8 + s
+    const unsigned gid = blockIdx.x * 256u + threadIdx.x;
+    const unsigned nblk = (unsigned)((a.N + kPermTokens - 1) / kPermTokens);
+    const unsigned blk = gid / segs, sj = gid - blk * segs;
+    if (blk >= (unsigned)a.B * nblk) return;
+    const int b = (int)(blk / nblk), t0 = (int)(blk - (unsigned)b * nblk) * kPermTokens;
+    const int nt = min(kPermTokens, a.N - t0);
+    const long long rowlen = (long long)a.H * J.d;
+    const unsigned col = sj * 8u;
+    const long long base = (long long)b * a.N * rowlen + col;
+    float x[kPermTokens][8];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            float c, s;
-            rot_cs(a.pos0 + t, a.theta[sg * 4 + j], &c, &s);
-            if (a.rot_sign < 0) s = -s;  // the transpose rotation
-            const float x0 = x[2 * j], x1 = x[2 * j + 1];
-            x[2 * j] = x0 * c - x1 * s;
-            x[2 * j + 1] = x0 * s + x1 * c;
+    for (int i = 0; i < kPermTokens; ++i)
+        if (i < nt) perm_load(J, base + (J.in_rev ? a.N - 1 - (t0 + i) : t0 + i) * rowlen, x[i]);
+    if (J.rot) {
+        const int pair0 = (int)(col % (unsigned)J.d) / 2;
+        float c[4], s[4], dc[4], ds[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            rot_cs(a.pos0 + t0, a.theta[pair0 + e], &c[e], &s[e]);
+            rot_cs(1, a.theta[pair0 + e], &dc[e], &ds[e]);
+            if (J.rot < 0) s[e] = -s[e], ds[e] = -ds[e];  // the transpose rotation
+        }
+#pragma unroll
+        for (int i = 0; i < kPermTokens; ++i) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float x0 = x[i][2 * e], x1 = x[i][2 * e + 1];
+                x[i][2 * e] = x0 * c[e] - x1 * s[e];
+                x[i][2 * e + 1] = x0 * s[e] + x1 * c[e];
+                const float nc = c[e] * dc[e] - s[e] * ds[e];
+                s[e] = s[e] * dc[e] + c[e] * ds[e];
+                c[e] = nc;
+            }
         }
     }
-    if (a.out_bf16) {
-        *reinterpret_cast<uint4*>((uint16_t*)a.out + oi) = pack8_bf16(x);
-    } else {
-        *reinterpret_cast<float4*>((float*)a.out + oi) = make_float4(x[0], x[1], x[2], x[3]);
-        *reinterpret_cast<float4*>((float*)a.out + oi + 4) = make_float4(x[4], x[5], x[6], x[7]);
+#pragma unroll
+    for (int o = 0; o < 2; ++o) {
+        if (!J.out[o]) continue;
+#pragma unroll
+        for (int i = 0; i < kPermTokens; ++i)
+            if (i < nt) perm_store(J, J.out[o], base + (J.out_rev[o] ? a.N - 1 - (t0 + i) : t0 + i) * rowlen, x[i]);
     }
 }
 

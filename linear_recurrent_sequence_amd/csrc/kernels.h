@@ -999,12 +999,19 @@ typedef void (*epi_kernel_t)(EpiArgs);
 // Reordering / rotation of one [B, N, H, d] tensor (d a multiple of 8): output row (b, n, h) is token
 // t = out_rev ? N-1-n : n, read from input row in_rev ? N-1-t : t and turned by rot_sign (pos0 + t) theta_i on
 // pairs (2i, 2i+1) (rot_sign 0: copied; -1: the transpose rotation). One 256-thread workgroup per 2048 values.
-struct PermArgs {
+// Reordering and rotation of [B, N, H, d] tensors (the gradients' inputs and outputs). Per token t (rotation
+// angle (pos0 + t) theta_i), job j reads row (in_rev ? N-1-t : t) of `in` and writes row (rev ? N-1-t : t) of
+// out[0] and, if not null, of out[1]; rot: +1 turns by the rotation, -1 by its transpose, 0 copies.
+struct PermJob {
     const void* in;
-    void* out;
-    int B, N, H, d;
-    int in_rev, out_rev, rot_sign;
-    int in_bf16, out_bf16;
+    void* out[2];
+    int d, rot, in_rev, out_rev[2], in_bf16, out_bf16;
+};
+constexpr int kMaxPermJobs = 4;
+constexpr int kPermTokens = 4;  // consecutive tokens per thread
+struct PermArgs {
+    PermJob job[kMaxPermJobs];  // one per blockIdx.y
+    int B, N, H;
     long long pos0;
     double theta[kMaxPairs];
 };
