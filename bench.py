@@ -224,7 +224,8 @@ def bench_backward(R, W, torch, wid, steps):
     torch.cuda.synchronize()
     R.timing_enable(False)
     kernels = {}
-    for name in ("ret_permute_rotate", "ret_chunk_seg", "ret_chunk_fused", "ret_chunk_local", "ret_segment_scan"):
+    for name in ("ret_rotate_qk", "ret_permute_rotate", "ret_chunk_seg", "ret_chunk_fused", "ret_chunk_local",
+                 "ret_segment_scan"):
         tot, n = R.timing_query(name)
         if n:
             kernels[name] = {"avg_us": 1e3 * tot / n, "launches_per_call": n // 3}

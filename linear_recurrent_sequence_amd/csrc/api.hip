@@ -204,6 +204,12 @@ ChunkPlan plan_chunk(const ChunkKernels& ck, int B, int N, int H, int dk, int dv
     return p;
 }
 
+// Whether a plan runs the on-chip segment kernel: chained segments short enough to stay on chip
+// (RET_SEG_ONCHIP=0 turns it off).
+bool plan_onchip(const ChunkKernels& ck, const ChunkPlan& p) {
+    return ck.fused && p.nseg > 1 && ck.seg && p.seg_len <= ck.seg_tokens && env_int("RET_SEG_ONCHIP", 1) != 0;
+}
+
 }  // namespace
 
 // =====================================================================================================
@@ -270,7 +276,8 @@ struct EpiRequest {
 ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o, int B, int N, int H, int dk,
                            int dv, ret_dtype_t in_dt, ret_dtype_t out_dt, const float* gamma, const double* theta,
                            int64_t pos0, int chunk, const float* state_in, float* state_out, void* workspace,
-                           size_t workspace_bytes, void* stream, const EpiRequest* epi, bool* fused) {
+                           size_t workspace_bytes, void* stream, const EpiRequest* epi, bool* fused,
+                           bool rev = false) {
     if (fused) *fused = false;
     ret_status_t st = check_common(q, k, v, o, B, N, H, dk, dv, in_dt, out_dt, gamma, theta);
     if (st != RET_OK) return st;
@@ -283,6 +290,7 @@ ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o,
     if (!pick_chunk(in_dt, dk, dv, chunk, &ck))
         return fail(RET_ERR_UNSUPPORTED, "chunkwise form: unsupported d_k=%d d_v=%d chunk=%d for %s input", dk, dv,
                     chunk, in_dt == RET_F32 ? "F32" : "BF16");
+    if (rev && !ck.fused) return fail(RET_ERR_UNSUPPORTED, "reversed chunkwise run: not available for this shape");
     // The kernels address one chunk of one head with 32-bit byte offsets.
     if ((long long)chunk * H * (dk > dv ? dk : dv) * 4 >= (1LL << 31))
         return fail(RET_ERR_UNSUPPORTED, "chunkwise form: chunk*H*max(d_k,d_v) too large (%d*%d*%d)", chunk, H,
@@ -301,12 +309,15 @@ ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o,
     hipStream_t s = (hipStream_t)stream;
     const int ntiles = dv / ck.dvt;
     if (ck.fused) {
-        // Segments short enough to stay on chip take the on-chip variant (RET_SEG_ONCHIP=0 turns it off).
-        const bool onchip = nseg > 1 && ck.seg && seg_len <= ck.seg_tokens && env_int("RET_SEG_ONCHIP", 1) != 0;
+        // Segments short enough to stay on chip take the on-chip variant.
+        const bool onchip = plan_onchip(ck, plan);
         // Staging copies rows instead of rotating them when there is no rotation, or when q and k are rotated
         // once up front (several d_v tiles stage the same rows).
         fwd_kernel_t fn = onchip ? ck.seg : ck.fused;
-        const fwd_kernel_t fn_pre = onchip ? ck.seg_pre : ck.fused_pre;
+        const fwd_kernel_t fn_pre = onchip ? (rev ? ck.seg_rev : ck.seg_pre) : ck.fused_pre;
+        // the reversed run exists for the on-chip kernel without rotation, state or epilogue only
+        if (rev && (!onchip || !ck.seg_rev || theta || state_in || state_out || epi))
+            return fail(RET_ERR_UNSUPPORTED, "reversed chunkwise run: not available for this shape");
         const char* name = onchip ? "ret_chunk_seg" : "ret_chunk_fused";
         if (!theta) {
             fn = fn_pre;
@@ -359,22 +370,40 @@ ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o,
     return launch_status("ret_chunk_full");
 }
 
-// Workspace of the gradients: the segment chain the three retentions share (one call after another; at offset
-// 0, at least 256 bytes, so ret_chunkwise_check reads its header), then their rotated and reversed inputs
-// (bf16) and their fp32 outputs.
+// Workspace of the gradients. At offset 0 the segment chain the three retentions share (one call after
+// another; at least 256 bytes, so ret_chunkwise_check reads its header). Then, when both reversed retentions run
+// on the on-chip kernel's reversed traversal (direct): Q' and K' (bf16, only with rotation) and the fp32
+// outputs dq', dk'. Otherwise the reordered inputs K', K' reversed, Q' reversed, V reversed, dO reversed (bf16)
+// and the three fp32 outputs.
 struct BwdLayout {
-    size_t kp, kr, qr, vr, dor, g1, g2, g3, chain, chain_bytes, total;
+    bool direct;
+    size_t qp, kp, kr, qr, vr, dor, g1, g2, g3, chain, chain_bytes, total;
 };
-bool bwd_layout(int B, int N, int H, int dk, int dv, int chunk, BwdLayout* L) {
+bool bwd_layout(int B, int N, int H, int dk, int dv, int chunk, bool rotate, BwdLayout* L) {
     ChunkKernels ca, cb;
     if (!pick_chunk(RET_BF16, dv, dk, chunk, &ca) || !pick_chunk(RET_BF16, dk, dv, chunk, &cb)) return false;
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     const size_t nk = (size_t)B * N * H * dk, nv = (size_t)B * N * H * dv;
-    const size_t ka = plan_chunk(ca, B, N, H, dv, dk, chunk, false, SIZE_MAX).chain_bytes;
-    const size_t kb = plan_chunk(cb, B, N, H, dk, dv, chunk, false, SIZE_MAX).chain_bytes;
+    const ChunkPlan pa = plan_chunk(ca, B, N, H, dv, dk, chunk, false, SIZE_MAX);
+    const ChunkPlan pb = plan_chunk(cb, B, N, H, dk, dv, chunk, false, SIZE_MAX);
+    memset(L, 0, sizeof(*L));
+    L->direct = plan_onchip(ca, pa) && ca.seg_rev && plan_onchip(cb, pb) && cb.seg_rev &&
+                env_int("RET_BWD_DIRECT", 1) != 0;
     L->chain = 0;
-    L->chain_bytes = ka > kb ? ka : kb;
-    L->kp = up(L->chain_bytes > 256 ? L->chain_bytes : 256);
+    L->chain_bytes = pa.chain_bytes > pb.chain_bytes ? pa.chain_bytes : pb.chain_bytes;
+    size_t off = up(L->chain_bytes > 256 ? L->chain_bytes : 256);
+    if (L->direct) {
+        if (rotate) {
+            L->qp = off;
+            L->kp = L->qp + up(nk * 2);
+            off = L->kp + up(nk * 2);
+        }
+        L->g1 = off;
+        L->g3 = L->g1 + up(nk * 4);
+        L->total = L->g3 + up(nk * 4);
+        return true;
+    }
+    L->kp = off;
     L->kr = L->kp + up(nk * 2);
     L->qr = L->kr + up(nk * 2);
     L->vr = L->qr + up(nk * 2);
@@ -386,7 +415,6 @@ bool bwd_layout(int B, int N, int H, int dk, int dv, int chunk, BwdLayout* L) {
     return true;
 }
 
-// One launch of permute_rotate_kernel over the given jobs (at most kMaxPermJobs), one grid row per job.
 ret_status_t permute(const PermJob* jobs, int njobs, int B, int N, int H, const double* theta, int64_t pos0,
                      hipStream_t s) {
     PermArgs P;
@@ -566,7 +594,7 @@ ret_status_t ret_msr_epilogue(const void* o, const void* gate, const float* gn_w
 size_t ret_chunkwise_bwd_workspace_bytes(int B, int N, int H, int dk, int dv, int chunk) {
     BwdLayout L;
     if (B <= 0 || N <= 0 || H <= 0 || dk <= 0 || dv <= 0 || chunk <= 0) return 0;
-    if (!bwd_layout(B, N, H, dk, dv, chunk, &L)) return 0;
+    if (!bwd_layout(B, N, H, dk, dv, chunk, true, &L)) return 0;
     return L.total;
 }
 
@@ -585,7 +613,7 @@ ret_status_t ret_chunkwise_bwd(const void* q, const void* k, const void* v, cons
     if (dq == dk_out || dq == dv_out || dk_out == dv_out) return fail(RET_ERR_INVALID_ARG, "dq, dk, dv must differ");
     if (chunk <= 0) return fail(RET_ERR_INVALID_ARG, "chunk must be positive (got %d)", chunk);
     BwdLayout L;
-    if (!bwd_layout(B, N, H, dk, dv, chunk, &L))
+    if (!bwd_layout(B, N, H, dk, dv, chunk, theta != nullptr, &L))
         return fail(RET_ERR_UNSUPPORTED, "gradients: d_k=%d d_v=%d chunk=%d (needs d_k, d_v in {64,128,256})", dk, dv,
                     chunk);
     if (!workspace || workspace_bytes < L.total)
@@ -593,6 +621,45 @@ ret_status_t ret_chunkwise_bwd(const void* q, const void* k, const void* v, cons
     if (!aligned16(workspace)) return fail(RET_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
     hipStream_t s = (hipStream_t)stream;
     char* ws = (char*)workspace;
+    const int ob = out_dt == RET_BF16;
+    if (L.direct) {
+        // Q', K' (rotated once; q and k themselves without rotation), then dq' = retention(dO, V, K') and, over
+        // the reversed sequence on the reversed traversal, dv = retention(K', Q', dO) and dk' = retention(V, dO,
+        // Q'), written in token order.
+        const void *Qp = q, *Kp = k;
+        if (theta) {
+            FwdArgs A;
+            fill_fwd(A, q, k, v, nullptr, B, N, H, dk, dv, out_dt, gamma, theta, pos0);
+            A.qr = ws + L.qp;
+            A.kr = ws + L.kp;
+            Qp = A.qr;
+            Kp = A.kr;
+            LaunchTimer tr("ret_rotate_qk", s);
+            hipLaunchKernelGGL(rotate_qk_get(), dim3(rotate_qk_blocks(B, N, H, dk)), dim3(256), 0, s, A);
+            tr.done();
+            if ((st = launch_status("ret_rotate_qk")) != RET_OK) return st;
+        }
+        // without rotation dq' and dk' are the gradients: straight into dq, dk in the caller's dtype
+        void* G1 = theta ? (void*)(ws + L.g1) : dq;
+        void* G3 = theta ? (void*)(ws + L.g3) : dk_out;
+        const ret_dtype_t gdt = theta ? RET_F32 : out_dt;
+        void* chain = ws + L.chain;
+        if ((st = chunkwise_run(dout, v, Kp, G1, B, N, H, dv, dk, RET_BF16, gdt, gamma, nullptr, 0, chunk, nullptr,
+                                nullptr, chain, L.chain_bytes, stream, nullptr, nullptr)) != RET_OK)
+            return st;
+        if ((st = chunkwise_run(Kp, Qp, dout, dv_out, B, N, H, dk, dv, RET_BF16, out_dt, gamma, nullptr, 0, chunk,
+                                nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, true)) != RET_OK)
+            return st;
+        if ((st = chunkwise_run(v, dout, Qp, G3, B, N, H, dv, dk, RET_BF16, gdt, gamma, nullptr, 0, chunk, nullptr,
+                                nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, true)) != RET_OK)
+            return st;
+        if (!theta) return RET_OK;
+        const PermJob post[2] = {
+            {G1, {dq, nullptr}, dk, -1, 0, {0, 0}, 0, ob},
+            {G3, {dk_out, nullptr}, dk, -1, 0, {0, 0}, 0, ob},
+        };
+        return permute(post, 2, B, N, H, theta, pos0, s);
+    }
     void *Kp = ws + L.kp, *Kr = ws + L.kr, *Qr = ws + L.qr, *Vr = ws + L.vr, *dOr = ws + L.dor;
     void *G1 = ws + L.g1, *G2 = ws + L.g2, *G3 = ws + L.g3, *chain = ws + L.chain;
     // inputs of the three retentions: K' in order; K', Q', V and dO reversed (one launch)
@@ -614,7 +681,6 @@ ret_status_t ret_chunkwise_bwd(const void* q, const void* k, const void* v, cons
                             nullptr, chain, L.chain_bytes, stream, nullptr, nullptr)) != RET_OK)
         return st;
     // back to the caller's order, dq and dk turned back by the transpose rotation
-    const int ob = out_dt == RET_BF16;
     const PermJob post[3] = {
         {G1, {dq, nullptr}, dk, -1, 0, {0, 0}, 0, ob},
         {G3, {dk_out, nullptr}, dk, -1, 1, {0, 0}, 0, ob},

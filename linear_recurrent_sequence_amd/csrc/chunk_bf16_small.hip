@@ -11,6 +11,7 @@ ChunkKernels chunk_entry_small() {
     ChunkKernels k = chunk_entry_bf16<DK, C>();
     k.seg = chunk_seg_bf16<DK, CI, false>;
     k.seg_pre = chunk_seg_bf16<DK, CI, true>;
+    k.seg_rev = chunk_seg_bf16<DK, CI, true, true>;
     k.seg_tokens = SegB<DK, CI, false>::RT;
     return k;
 }

@@ -9,6 +9,11 @@
 // (rotated q) stays in its own LDS tile; the local end state is the segment's aggregate, published for the
 // later segments as soon as the last chunk is done. The chain's latency thus overlaps the segment's streaming
 // and main products instead of preceding them, and q, k and v are read from HBM once.
+//
+// REV runs the same recurrence over the reversed sequence (token n of the run is row N-1-n of q, k, v and o):
+// the gradients' retentions that sum over later tokens. Only with q and k as given (PRE, no rotation), and
+// without state in, state out or the epilogue. Every row of a reversed chunk gets its own buffer offset, which
+// is negative, hence out of range and read as zero or dropped, for rows past the chunk.
 #pragma once
 
 #include "chunk_bf16.h"
@@ -36,8 +41,9 @@ struct SegB {
     static_assert(VTILE >= TILE, "a V staging tile holds a chunk of bf16 output rows at pitch LD");
 };
 
-template <int DK, int C, bool PRE>
+template <int DK, int C, bool PRE, bool REV = false>
 __global__ __launch_bounds__(kThreads, 2) void chunk_seg_bf16(FwdArgs a) {
+    static_assert(!REV || PRE, "reversed runs take q and k as given");
     typedef SegB<DK, C, PRE> F;
     typedef typename F::TQ TQ;
     typedef typename F::TV TV;
@@ -80,7 +86,9 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_seg_bf16(FwdArgs a) {
     const long long seg_t0 = (long long)seg * aseg_len;
     const int seg_n = (int)(min((long long)aN, seg_t0 + aseg_len) - seg_t0);  // tokens in this segment
     const int nchunks = (seg_n + C - 1) / C;  // at most MAXC: the host plans segments of at most RT tokens
-    const long long head0 = ((long long)b * aN + seg_t0) * aH + h;
+    // REV: the rows of the run's chunk c start (in memory order) at token N - seg_t0 - c*C - L, so the head
+    // pointers address token 0 and rows_tok0 adds the chunk's first row.
+    const long long head0 = ((long long)b * aN + (REV ? 0 : seg_t0)) * aH + h;
     const uint16_t* qh = (const uint16_t*)(PRE ? a.qr : a.q) + head0 * adk;
     const uint16_t* kh = (const uint16_t*)(PRE ? a.kr : a.k) + head0 * adk;
     const uint16_t* vh = (const uint16_t*)a.v + head0 * adv + dv0;
@@ -92,21 +100,41 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_seg_bf16(FwdArgs a) {
     // ---- loads: q, k and v rows of chunk c into register buffer c % NBUF. A chunk's buffer resources cover
     // its live rows only: rows past the sequence, and every row of a chunk past the segment (an empty
     // resource), read as zero, so loads and tile stores need no branch and the waits on them stay exact. ----
+    // first row of chunk c in memory (in rows after the head pointer), and the byte offset of its row r: rows
+    // past the chunk's L live rows get a negative offset under REV, out of every range
+    auto rows_tok0 = [&](int c, int L) __attribute__((always_inline)) {
+        return REV ? (long long)aN - seg_t0 - (long long)c * C - L : (long long)c * C;
+    };
+    auto row_off = [&](int L, int r, int rs, int col, int esz) __attribute__((always_inline)) {
+        return ((REV ? L - 1 - r : r) * rs + col) * esz;
+    };
     auto rows_rsrc = [&](const uint16_t* base, int c, int rs, int width) __attribute__((always_inline)) {
         const int L = min(C, seg_n - c * C);
-        return bytes_rsrc(base + (long long)c * C * rs, L > 0 ? ((L - 1) * rs + width) * 2 : 0);
+        return bytes_rsrc(base + rows_tok0(c, L) * rs, L > 0 ? ((L - 1) * rs + width) * 2 : 0);
     };
     u32x4_t bq[NBUF][TQ::NP], bk[NBUF][TQ::NP], bv[NBUF][TV::NP];
     auto issue = [&](auto cc) __attribute__((always_inline)) {
         constexpr int c = decltype(cc)::value, par = c % NBUF;
         const rsrc_t rq = rows_rsrc(qh, c, rsk, DK), rk = rows_rsrc(kh, c, rsk, DK), rv = rows_rsrc(vh, c, rsv, 64);
+        if constexpr (REV) {
+            const int L = min(C, seg_n - c * C);
 #pragma unroll
-        for (int p = 0; p < TQ::NP; ++p) {
-            bk[par][p] = buf_load16(rk, qoff, p * TQ::RP * rsk * 2);
-            bq[par][p] = buf_load16(rq, qoff, p * TQ::RP * rsk * 2);
+            for (int p = 0; p < TQ::NP; ++p) {
+                const int off = row_off(L, qrow + p * TQ::RP, rsk, qseg * 8, 2);
+                bk[par][p] = buf_load16(rk, off, 0);
+                bq[par][p] = buf_load16(rq, off, 0);
+            }
+#pragma unroll
+            for (int p = 0; p < TV::NP; ++p) bv[par][p] = buf_load16(rv, row_off(L, vrow + p * TV::RP, rsv, vseg * 8, 2), 0);
+        } else {
+#pragma unroll
+            for (int p = 0; p < TQ::NP; ++p) {
+                bk[par][p] = buf_load16(rk, qoff, p * TQ::RP * rsk * 2);
+                bq[par][p] = buf_load16(rq, qoff, p * TQ::RP * rsk * 2);
+            }
+#pragma unroll
+            for (int p = 0; p < TV::NP; ++p) bv[par][p] = buf_load16(rv, voff, p * TV::RP * rsv * 2);
         }
-#pragma unroll
-        for (int p = 0; p < TV::NP; ++p) bv[par][p] = buf_load16(rv, voff, p * TV::RP * rsv * 2);
     };
     static_for<0, (NBUF < F::MAXC ? NBUF : F::MAXC)>([&](auto cc) __attribute__((always_inline)) { issue(cc); });
 
@@ -146,18 +174,21 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_seg_bf16(FwdArgs a) {
     const int o_voff = (n16 * rsv + w * 16 + g4) * osz;
     auto store_out = [&](int c, const f32x4_t* O) __attribute__((always_inline)) {
         const int L = min(C, seg_n - c * C);
-        const rsrc_t ro = bytes_rsrc(oh + (long long)c * C * rsv * osz, ((L - 1) * rsv + 64) * osz);
+        const rsrc_t ro = bytes_rsrc(oh + rows_tok0(c, L) * rsv * osz, ((L - 1) * rsv + 64) * osz);
+        // REV: row x*16 + n16 at its own (possibly negative) offset; else one offset plus a scalar per tile
+        const int vo = REV ? row_off(L, n16, rsv, w * 16 + g4, osz) : o_voff;
         if (a.out_bf16) {
 #pragma unroll
             for (int x = 0; x < NB; ++x)
                 __builtin_amdgcn_raw_buffer_store_b64(
                     __builtin_bit_cast(uint32_t __attribute__((ext_vector_type(2))),
                                        make_uint2(pack2_bf16(O[x][0], O[x][1]), pack2_bf16(O[x][2], O[x][3]))),
-                    ro, o_voff, x * 16 * rsv * 2, kOutAux);
+                    ro, REV ? vo - x * 16 * rsv * 2 : vo, REV ? 0 : x * 16 * rsv * 2, kOutAux);
         } else {
 #pragma unroll
             for (int x = 0; x < NB; ++x)
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, O[x]), ro, o_voff, x * 16 * rsv * 4,
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, O[x]), ro,
+                                                       REV ? vo - x * 16 * rsv * 4 : vo, REV ? 0 : x * 16 * rsv * 4,
                                                        kOutAux);
         }
     };
@@ -284,7 +315,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_seg_bf16(FwdArgs a) {
     const int row = tid / 8, sg = tid % 8;
     u32x4_t gq[2][C / 32][2];
     auto gate_issue = [&](int c, u32x4_t (&gu)[C / 32][2]) __attribute__((always_inline)) {
-        if (a.epi && a.gate && c < nchunks) {
+        if (!REV && a.epi && a.gate && c < nchunks) {
             const int L = min(C, seg_n - c * C);
             const rsrc_t rg = bytes_rsrc(gh + (long long)c * C * rsv * gsz, ((L - 1) * rsv + 64) * gsz);
 #pragma unroll
@@ -303,11 +334,11 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_seg_bf16(FwdArgs a) {
                 make_uint2(pack2_bf16(O[x][0], O[x][1]), pack2_bf16(O[x][2], O[x][3]));
         const int L = min(C, seg_n - c * C);
         __syncthreads();
-        const rsrc_t ro = bytes_rsrc(oh + (long long)c * C * rsv * 2, ((L - 1) * rsv + 64) * 2);
+        const rsrc_t ro = bytes_rsrc(oh + rows_tok0(c, L) * rsv * 2, ((L - 1) * rsv + 64) * 2);
 #pragma unroll
         for (int p = 0; p < C / 32; ++p) {
             u32x4_t u = *reinterpret_cast<const u32x4_t*>(buf + (row + 32 * p) * LD + sg * 8);
-            if (a.epi) {
+            if (!REV && a.epi) {
                 float x[8];
                 unpack8(u, x);
                 group_standardize<8, 8>(x, 64.f, a.eps);
@@ -336,7 +367,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_seg_bf16(FwdArgs a) {
                 }
                 u = pack8(x);
             }
-            buf_store16(ro, ((row + 32 * p) * rsv + sg * 8) * 2, 0, u);
+            buf_store16(ro, row_off(L, row + 32 * p, rsv, sg * 8, 2), 0, u);
         }
     };
     bf16x8_t rin[KK];

@@ -945,6 +945,7 @@ struct ChunkKernels {
     int dvt;
     // single-pass kernels for chained runs whose segments hold at most seg_tokens tokens (0: none)
     fwd_kernel_t seg, seg_pre;
+    fwd_kernel_t seg_rev;  // seg_pre over the reversed sequence (null: none)
     int seg_tokens;
     int threads;      // workgroup size of the fused kernels (0: kThreads)
     int target_wgs;   // workgroups the segment planner aims for (0: the default)

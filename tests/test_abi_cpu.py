@@ -142,10 +142,13 @@ def test_chunkwise_msr_rejects_invalid_arguments(lib):
 def test_gradients_workspace_and_rejections(lib):
     """ret_chunkwise_bwd: workspace size from the shapes, host-side rejections before any launch."""
     wsq = lib.ret_chunkwise_bwd_workspace_bytes
-    # five bf16 copies (K' twice, Q', V, dO) and three fp32 outputs of [8, 2048, 8, 64], then a segment chain
+    # d = 64 in short segments (the reversed traversal): the segment chain, then Q', K' (bf16) and dq', dk' (fp32)
     n = 8 * 2048 * 8 * 64
-    assert wsq(8, 2048, 8, 64, 64, 64) >= 5 * n * 2 + 3 * n * 4
+    assert 2 * n * 2 + 2 * n * 4 <= wsq(8, 2048, 8, 64, 64, 64) < 3 * n * 2 + 3 * n * 4
     assert wsq(8, 2048, 8, 64, 64, 64) % 256 == 0
+    # d_k = 128: five reordered bf16 copies (K' twice, Q', V, dO) and three fp32 outputs
+    n2 = 1 * 4096 * 4 * 128
+    assert wsq(1, 4096, 4, 128, 128, 64) >= 5 * n2 * 2 + 3 * n2 * 4
     assert wsq(1, 100, 2, 32, 64, 64) == 0      # d_k = 32: no bf16 kernel
     assert wsq(1, 8192, 16, 256, 512, 128) == 0  # d_v = 512 would be the d_k of dq's retention
     assert wsq(1, 0, 2, 64, 64, 64) == 0

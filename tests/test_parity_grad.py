@@ -47,6 +47,11 @@ GRAD_SMALL = [
     (2, 150, 2, 64, 64, 64, True, 11, "bf16"),  # bf16 gradients
     (1, 1, 2, 64, 64, 64, True, 5, "f32"),      # one token
     (3, 64, 2, 64, 64, 64, True, 0, "f32"),     # exactly one chunk
+    # d = 64 in several short segments: the reversed traversal (no reordered copies)
+    (2, 700, 4, 64, 64, 64, True, 9, "f32"),
+    (1, 1000, 3, 64, 64, 32, True, 0, "bf16"),  # chunk 32
+    (2, 600, 2, 64, 64, 64, False, 0, "bf16"),  # no rotation: dq and dk written by the retentions themselves
+    (1, 777, 2, 64, 64, 128, True, 4, "f32"),   # chunk 128 as 64-token sub-chunks
 ]
 
 
@@ -60,6 +65,19 @@ def test_gradients_small(R, case):
     do = W.make_dout(w, rng)
     ref = oracle.grad(q, k, v, do, w.gamma, theta=w.theta, pos0=pos0)
     got = _gpu_grad(R, q, k, v, do, w.gamma, chunk, w.theta, pos0, out_dt)
+    _check(got, ref, tol("bf16"))
+
+
+@pytest.mark.parametrize("direct", ["1", "0"])
+def test_gradients_both_paths(R, direct, monkeypatch):
+    """The reversed-traversal path and the reordered-copies path (RET_BWD_DIRECT=0) on one shape."""
+    monkeypatch.setenv("RET_BWD_DIRECT", direct)
+    w = W.Workload("grad", B=3, N=900, H=2, dk=64, dv=64, dtype="bf16", scale=8.0, seed=43, chunk=64, rotate=True)
+    print_case("gradients-path", direct, w)
+    q, k, v, rng = W.make_qkv(w)
+    do = W.make_dout(w, rng)
+    ref = oracle.grad(q, k, v, do, w.gamma, theta=w.theta, pos0=2)
+    got = _gpu_grad(R, q, k, v, do, w.gamma, w.chunk, w.theta, 2, "bf16")
     _check(got, ref, tol("bf16"))
 
 
