@@ -443,8 +443,11 @@ def main():
         }
     if not args.no_epilogue:
         result["epilogue"] = bench_epilogue(R, W, torch, wid, args.steps)
-    if not args.no_backward:
+    bw = W.WORKLOADS[wid]
+    if not args.no_backward and R.load().ret_chunkwise_bwd_workspace_bytes(bw.B, bw.N, bw.H, bw.dk, bw.dv, bw.chunk):
         result["backward"] = bench_backward(R, W, torch, wid, args.steps)
+    elif not args.no_backward:
+        result["backward"] = {"workload": bw.name, "skipped": "gradients need d_k, d_v in {64, 128, 256}"}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(W, wid)
     result["context"] = ("pages' figures (whole 6.7B model, A100-80GB, vanilla PyTorch): 8.4x faster decoding and "
