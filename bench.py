@@ -444,7 +444,8 @@ def main():
     if not args.no_epilogue:
         result["epilogue"] = bench_epilogue(R, W, torch, wid, args.steps)
     bw = W.WORKLOADS[wid]
-    if not args.no_backward and R.load().ret_chunkwise_bwd_workspace_bytes(bw.B, bw.N, bw.H, bw.dk, bw.dv, bw.chunk):
+    if not args.no_backward and R.load().ret_chunkwise_bwd_workspace_bytes(bw.B, bw.N, bw.H, bw.dk, bw.dv, bw.chunk,
+                                                                            R.RET_BF16):
         result["backward"] = bench_backward(R, W, torch, wid, args.steps)
     elif not args.no_backward:
         result["backward"] = {"workload": bw.name, "skipped": "gradients need d_k, d_v in {64, 128, 256}"}

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define RET_ABI_VERSION 4
+#define RET_ABI_VERSION 5
 
 typedef enum { RET_F32 = 0, RET_BF16 = 1 } ret_dtype_t;
 
@@ -185,14 +185,16 @@ ret_status_t ret_chunkwise_msr_fwd(const void* q, const void* k, const void* v, 
  *     dv_m  = sum_{n>=m} gamma^(n-m) (q'_n . k'_m) dO_n,   dq, dk = dq', dk' turned back by the rotation's
  *     transpose,
  * each a retention (the last two over the reversed sequence) that the chunkwise kernels compute.
- * in_dt: BF16 (q, k, v, dout); out_dt: F32 or BF16 (dq, dk, dv). No gradient for a state in or out.
+ * in_dt: BF16 or F32 (q, k, v, dout); out_dt: F32 or BF16 (dq, dk, dv; F32 for F32 input). No gradient for a
+ * state in or out.
  * workspace: device memory of ret_chunkwise_bwd_workspace_bytes (zero-filled once by the caller, like the
  * chunkwise workspace; every call leaves its chain part zeroed again; ret_chunkwise_check accepts it and
  * reports a segment-chain wait that gave up). dq, dk, dv must not alias the inputs
- * or each other. Supported: d_k, d_v in {64, 128, 256}, chunk in {32, 64, 128, 256, 512}. Asynchronous on
- * `stream`.
+ * or each other. Supported wherever the forward supports both (d_k, d_v) and (d_v, d_k) for the input dtype:
+ * BF16 d_k, d_v in {64, 128, 256}, chunk in {32, 64, 128, 256, 512}; F32 d_k, d_v in {16, 32, 64}, chunk in
+ * {16, 32, 64}. The workspace query returns 0 for other shapes. Asynchronous on `stream`.
  */
-size_t ret_chunkwise_bwd_workspace_bytes(int B, int N, int H, int dk, int dv, int chunk);
+size_t ret_chunkwise_bwd_workspace_bytes(int B, int N, int H, int dk, int dv, int chunk, ret_dtype_t in_dt);
 ret_status_t ret_chunkwise_bwd(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk_out,
                                void* dv_out, int B, int N, int H, int dk, int dv, ret_dtype_t in_dt,
                                ret_dtype_t out_dt, const float* gamma, const double* theta, int64_t pos0, int chunk,

@@ -372,22 +372,22 @@ ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o,
 
 // Workspace of the gradients. At offset 0 the segment chain the three retentions share (one call after
 // another; at least 256 bytes, so ret_chunkwise_check reads its header). Then, when both reversed retentions run
-// on the on-chip kernel's reversed traversal (direct): Q' and K' (bf16, only with rotation) and the fp32
-// outputs dq', dk'. Otherwise the reordered inputs K', K' reversed, Q' reversed, V reversed, dO reversed (bf16)
-// and the three fp32 outputs.
+// on the on-chip kernel's reversed traversal (direct, bf16 only): Q' and K' (bf16, only with rotation) and the
+// fp32 outputs dq', dk'. Otherwise the reordered inputs K', K' reversed, Q' reversed, V reversed, dO reversed (in
+// the input dtype) and the three fp32 outputs.
 struct BwdLayout {
     bool direct;
     size_t qp, kp, kr, qr, vr, dor, g1, g2, g3, chain, chain_bytes, total;
 };
-bool bwd_layout(int B, int N, int H, int dk, int dv, int chunk, bool rotate, BwdLayout* L) {
+bool bwd_layout(int B, int N, int H, int dk, int dv, int chunk, ret_dtype_t in_dt, bool rotate, BwdLayout* L) {
     ChunkKernels ca, cb;
-    if (!pick_chunk(RET_BF16, dv, dk, chunk, &ca) || !pick_chunk(RET_BF16, dk, dv, chunk, &cb)) return false;
+    if (!pick_chunk(in_dt, dv, dk, chunk, &ca) || !pick_chunk(in_dt, dk, dv, chunk, &cb)) return false;
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-    const size_t nk = (size_t)B * N * H * dk, nv = (size_t)B * N * H * dv;
+    const size_t nk = (size_t)B * N * H * dk, nv = (size_t)B * N * H * dv, es = in_dt == RET_BF16 ? 2 : 4;
     const ChunkPlan pa = plan_chunk(ca, B, N, H, dv, dk, chunk, false, SIZE_MAX);
     const ChunkPlan pb = plan_chunk(cb, B, N, H, dk, dv, chunk, false, SIZE_MAX);
     memset(L, 0, sizeof(*L));
-    L->direct = plan_onchip(ca, pa) && ca.seg_rev && plan_onchip(cb, pb) && cb.seg_rev &&
+    L->direct = in_dt == RET_BF16 && plan_onchip(ca, pa) && ca.seg_rev && plan_onchip(cb, pb) && cb.seg_rev &&
                 env_int("RET_BWD_DIRECT", 1) != 0;
     L->chain = 0;
     L->chain_bytes = pa.chain_bytes > pb.chain_bytes ? pa.chain_bytes : pb.chain_bytes;
@@ -404,11 +404,11 @@ bool bwd_layout(int B, int N, int H, int dk, int dv, int chunk, bool rotate, Bwd
         return true;
     }
     L->kp = off;
-    L->kr = L->kp + up(nk * 2);
-    L->qr = L->kr + up(nk * 2);
-    L->vr = L->qr + up(nk * 2);
-    L->dor = L->vr + up(nv * 2);
-    L->g1 = L->dor + up(nv * 2);
+    L->kr = L->kp + up(nk * es);
+    L->qr = L->kr + up(nk * es);
+    L->vr = L->qr + up(nk * es);
+    L->dor = L->vr + up(nv * es);
+    L->g1 = L->dor + up(nv * es);
     L->g2 = L->g1 + up(nk * 4);
     L->g3 = L->g2 + up(nv * 4);
     L->total = L->g3 + up(nk * 4);
@@ -591,10 +591,11 @@ ret_status_t ret_msr_epilogue(const void* o, const void* gate, const float* gn_w
     return launch_status("ret_msr_epilogue");
 }
 
-size_t ret_chunkwise_bwd_workspace_bytes(int B, int N, int H, int dk, int dv, int chunk) {
+size_t ret_chunkwise_bwd_workspace_bytes(int B, int N, int H, int dk, int dv, int chunk, ret_dtype_t in_dt) {
     BwdLayout L;
     if (B <= 0 || N <= 0 || H <= 0 || dk <= 0 || dv <= 0 || chunk <= 0) return 0;
-    if (!bwd_layout(B, N, H, dk, dv, chunk, true, &L)) return 0;
+    if (in_dt != RET_F32 && in_dt != RET_BF16) return 0;
+    if (!bwd_layout(B, N, H, dk, dv, chunk, in_dt, true, &L)) return 0;
     return L.total;
 }
 
@@ -604,7 +605,6 @@ ret_status_t ret_chunkwise_bwd(const void* q, const void* k, const void* v, cons
                                void* workspace, size_t workspace_bytes, void* stream) {
     ret_status_t st = check_common(q, k, v, dq, B, N, H, dk, dv, in_dt, out_dt, gamma, theta);
     if (st != RET_OK) return st;
-    if (in_dt != RET_BF16) return fail(RET_ERR_UNSUPPORTED, "gradients: BF16 inputs only");
     if (!dout || !dk_out || !dv_out) return fail(RET_ERR_INVALID_ARG, "null dout/dk/dv pointer");
     if (!aligned16(dout) || !aligned16(dk_out) || !aligned16(dv_out))
         return fail(RET_ERR_INVALID_ARG, "dout/dq/dk/dv must be 16-byte aligned");
@@ -613,9 +613,10 @@ ret_status_t ret_chunkwise_bwd(const void* q, const void* k, const void* v, cons
     if (dq == dk_out || dq == dv_out || dk_out == dv_out) return fail(RET_ERR_INVALID_ARG, "dq, dk, dv must differ");
     if (chunk <= 0) return fail(RET_ERR_INVALID_ARG, "chunk must be positive (got %d)", chunk);
     BwdLayout L;
-    if (!bwd_layout(B, N, H, dk, dv, chunk, theta != nullptr, &L))
-        return fail(RET_ERR_UNSUPPORTED, "gradients: d_k=%d d_v=%d chunk=%d (needs d_k, d_v in {64,128,256})", dk, dv,
-                    chunk);
+    if (!bwd_layout(B, N, H, dk, dv, chunk, in_dt, theta != nullptr, &L))
+        return fail(RET_ERR_UNSUPPORTED,
+                    "gradients: d_k=%d d_v=%d chunk=%d for %s input (both (d_k, d_v) and (d_v, d_k) need kernels)", dk,
+                    dv, chunk, in_dt == RET_F32 ? "F32" : "BF16");
     if (!workspace || workspace_bytes < L.total)
         return fail(RET_ERR_WORKSPACE, "gradients need a workspace of %zu bytes (got %zu)", L.total, workspace_bytes);
     if (!aligned16(workspace)) return fail(RET_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
@@ -662,22 +663,23 @@ ret_status_t ret_chunkwise_bwd(const void* q, const void* k, const void* v, cons
     }
     void *Kp = ws + L.kp, *Kr = ws + L.kr, *Qr = ws + L.qr, *Vr = ws + L.vr, *dOr = ws + L.dor;
     void *G1 = ws + L.g1, *G2 = ws + L.g2, *G3 = ws + L.g3, *chain = ws + L.chain;
-    // inputs of the three retentions: K' in order; K', Q', V and dO reversed (one launch)
+    // inputs of the three retentions: K' in order; K', Q', V and dO reversed (one launch, in the input dtype)
+    const int ib = in_dt == RET_BF16;
     const PermJob pre[4] = {
-        {k, {Kp, Kr}, dk, 1, 0, {0, 1}, 1, 1},
-        {q, {Qr, nullptr}, dk, 1, 0, {1, 0}, 1, 1},
-        {v, {Vr, nullptr}, dv, 0, 0, {1, 0}, 1, 1},
-        {dout, {dOr, nullptr}, dv, 0, 0, {1, 0}, 1, 1},
+        {k, {Kp, Kr}, dk, 1, 0, {0, 1}, ib, ib},
+        {q, {Qr, nullptr}, dk, 1, 0, {1, 0}, ib, ib},
+        {v, {Vr, nullptr}, dv, 0, 0, {1, 0}, ib, ib},
+        {dout, {dOr, nullptr}, dv, 0, 0, {1, 0}, ib, ib},
     };
     if ((st = permute(pre, 4, B, N, H, theta, pos0, s)) != RET_OK) return st;
     // dq' = retention(dO, V, K'); dv^rev = retention(K'^rev, Q'^rev, dO^rev); dk'^rev = retention(V^rev, dO^rev, Q'^rev)
-    if ((st = chunkwise_run(dout, v, Kp, G1, B, N, H, dv, dk, RET_BF16, RET_F32, gamma, nullptr, 0, chunk, nullptr,
+    if ((st = chunkwise_run(dout, v, Kp, G1, B, N, H, dv, dk, in_dt, RET_F32, gamma, nullptr, 0, chunk, nullptr,
                             nullptr, chain, L.chain_bytes, stream, nullptr, nullptr)) != RET_OK)
         return st;
-    if ((st = chunkwise_run(Kr, Qr, dOr, G2, B, N, H, dk, dv, RET_BF16, RET_F32, gamma, nullptr, 0, chunk, nullptr,
+    if ((st = chunkwise_run(Kr, Qr, dOr, G2, B, N, H, dk, dv, in_dt, RET_F32, gamma, nullptr, 0, chunk, nullptr,
                             nullptr, chain, L.chain_bytes, stream, nullptr, nullptr)) != RET_OK)
         return st;
-    if ((st = chunkwise_run(Vr, dOr, Qr, G3, B, N, H, dv, dk, RET_BF16, RET_F32, gamma, nullptr, 0, chunk, nullptr,
+    if ((st = chunkwise_run(Vr, dOr, Qr, G3, B, N, H, dv, dk, in_dt, RET_F32, gamma, nullptr, 0, chunk, nullptr,
                             nullptr, chain, L.chain_bytes, stream, nullptr, nullptr)) != RET_OK)
         return st;
     // back to the caller's order, dq and dk turned back by the transpose rotation

@@ -63,7 +63,7 @@ def load(build_if_missing: bool = True):
     lib.ret_chunkwise_msr_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, fp, dp, i64,
                                           i32, vp, vp, vp, vp, ctypes.c_float, vp, sz, vp]
     lib.ret_chunkwise_msr_fwd.restype = i32
-    lib.ret_chunkwise_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.ret_chunkwise_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     lib.ret_chunkwise_bwd_workspace_bytes.restype = sz
     lib.ret_chunkwise_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, fp, dp, i64, i32,
                                       vp, sz, vp]
@@ -260,7 +260,7 @@ def ret_chunkwise_msr_fwd(q, k, v, y, gamma, chunk, gate=None, gn_weight=None, g
 def chunkwise_bwd_workspace(q, v, chunk):
     """A zero-filled workspace of ret_chunkwise_bwd_workspace_bytes for these shapes."""
     B, N, H, dk = q.shape
-    nbytes = load().ret_chunkwise_bwd_workspace_bytes(B, N, H, dk, v.shape[3], int(chunk))
+    nbytes = load().ret_chunkwise_bwd_workspace_bytes(B, N, H, dk, v.shape[3], int(chunk), _dt(q))
     if nbytes == 0:
         raise ValueError("gradients: unsupported shape")
     return torch.zeros((nbytes,), dtype=torch.uint8, device=q.device)

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ret_abi_version() == 4
+    assert lib.ret_abi_version() == 5
     assert lib.ret_status_string(0) == b"ok"
     assert lib.ret_status_string(-2) == b"unsupported shape or dtype"
 
@@ -141,7 +141,7 @@ def test_chunkwise_msr_rejects_invalid_arguments(lib):
 
 def test_gradients_workspace_and_rejections(lib):
     """ret_chunkwise_bwd: workspace size from the shapes, host-side rejections before any launch."""
-    wsq = lib.ret_chunkwise_bwd_workspace_bytes
+    wsq = lambda *a, dt=1: lib.ret_chunkwise_bwd_workspace_bytes(*a, dt)
     # d = 64 in short segments (the reversed traversal): the segment chain, then Q', K' (bf16) and dq', dk' (fp32)
     n = 8 * 2048 * 8 * 64
     assert 2 * n * 2 + 2 * n * 4 <= wsq(8, 2048, 8, 64, 64, 64) < 3 * n * 2 + 3 * n * 4
@@ -158,7 +158,11 @@ def test_gradients_workspace_and_rejections(lib):
     def call(q=16, k=32, v=48, do=64, dq=80, dk=96, dv=112, ind=1, outd=0, ws=4096, wsb=None, chunk=64, dkk=64):
         return lib.ret_chunkwise_bwd(q, k, v, do, dq, dk, dv, 1, 64, 2, dkk, 64, ind, outd, g, None, 0, chunk, ws,
                                      need if wsb is None else wsb, None)
-    assert call(ind=0) == -2            # fp32 inputs: not supported
+    assert call(ind=0, dkk=128) == -2   # fp32 inputs: no fp32 kernel for d_k = 128
+    # fp32: five fp32 copies and three fp32 outputs; no fp32 kernel for d_k = 128
+    n3 = 2 * 300 * 2 * 32
+    assert wsq(2, 300, 2, 32, 32, 32, dt=0) >= 8 * n3 * 4
+    assert wsq(2, 300, 2, 128, 64, 64, dt=0) == 0
     assert call(do=None) == -1          # null dout
     assert call(dk=16) == -1            # dk aliases q
     assert call(dv=80) == -1            # dv aliases dq

@@ -23,9 +23,9 @@ def R():
     return retention
 
 
-def _gpu_grad(R, q, k, v, do, gamma, chunk, theta, pos0, out_dt, workspace=None):
+def _gpu_grad(R, q, k, v, do, gamma, chunk, theta, pos0, out_dt, workspace=None, in_dt="bf16"):
     import torch
-    qd, kd, vd, dod = (to_dev(x, "bf16") for x in (q, k, v, do))
+    qd, kd, vd, dod = (to_dev(x, in_dt) for x in (q, k, v, do))
     dq, dk, dv = empty_out(q.shape, out_dt), empty_out(k.shape, out_dt), empty_out(v.shape, out_dt)
     R.ret_chunkwise_bwd(qd, kd, vd, dod, dq, dk, dv, gamma, chunk, theta=theta, pos0=pos0, workspace=workspace)
     torch.cuda.synchronize()
@@ -79,6 +79,28 @@ def test_gradients_both_paths(R, direct, monkeypatch):
     ref = oracle.grad(q, k, v, do, w.gamma, theta=w.theta, pos0=2)
     got = _gpu_grad(R, q, k, v, do, w.gamma, w.chunk, w.theta, 2, "bf16")
     _check(got, ref, tol("bf16"))
+
+
+F32_CASES = [
+    # B, N, H, dk, dv, chunk, rotate, pos0
+    (2, 150, 2, 32, 32, 32, True, 3),
+    (1, 300, 3, 64, 16, 64, True, 0),
+    (2, 77, 2, 16, 64, 16, False, 0),
+]
+
+
+@pytest.mark.parametrize("case", F32_CASES, ids=lambda c: "B%d-N%d-H%d-dk%d-dv%d-C%d" % c[:6])
+def test_gradients_f32(R, case):
+    """fp32 inputs and gradients (the reordered-copies path on the fp32 kernels) at the fp32 bar of 1e-5."""
+    B, N, H, dk, dv, chunk, rot, pos0 = case
+    w = W.Workload("grad32", B=B, N=N, H=H, dk=dk, dv=dv, dtype="f32", scale=1.0, seed=51 + N, chunk=chunk,
+                   rotate=rot)
+    print_case("gradients-f32", w)
+    q, k, v, rng = W.make_qkv(w)
+    do = W.make_dout(w, rng)
+    ref = oracle.grad(q, k, v, do, w.gamma, theta=w.theta, pos0=pos0)
+    got = _gpu_grad(R, q, k, v, do, w.gamma, chunk, w.theta, pos0, "f32", in_dt="f32")
+    _check(got, ref, tol("f32"))
 
 
 def test_gradients_workspace_reused(R):
