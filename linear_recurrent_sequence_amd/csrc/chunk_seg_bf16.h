@@ -82,20 +82,27 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_seg_bf16(FwdArgs a) {
     // ---- the segment: the unit's next ticket, so every earlier segment of the unit has started ----
     if constexpr (!PRE)
         if (tid < DK / 2) s_theta[tid] = a.theta[tid];  // visible after the ticket's barriers
-    const int seg = chain_ticket(ch, s_word);
-    const long long seg_t0 = (long long)seg * aseg_len;
-    const int seg_n = (int)(min((long long)aN, seg_t0 + aseg_len) - seg_t0);  // tokens in this segment
-    const int nchunks = (seg_n + C - 1) / C;  // at most MAXC: the host plans segments of at most RT tokens
-    // REV: the rows of the run's chunk c start (in memory order) at token N - seg_t0 - c*C - L, so the head
-    // pointers address token 0 and rows_tok0 adds the chunk's first row.
-    const long long head0 = ((long long)b * aN + (REV ? 0 : seg_t0)) * aH + h;
-    const uint16_t* qh = (const uint16_t*)(PRE ? a.qr : a.q) + head0 * adk;
-    const uint16_t* kh = (const uint16_t*)(PRE ? a.kr : a.k) + head0 * adk;
-    const uint16_t* vh = (const uint16_t*)a.v + head0 * adv + dv0;
+    // The segment is the unit's next ticket, known only after a device-scope atomic. The first chunks' loads go
+    // out before it for the segment of the launch order (the usual ticket), and again if the ticket differs.
+    int seg = __builtin_amdgcn_readfirstlane((int)(blockIdx.x / (unsigned)units));
+    long long seg_t0, head0;
+    int seg_n, nchunks;
+    const uint16_t *qh, *kh, *vh;
+    char* oh;
     const int osz = a.out_bf16 ? 2 : 4;
-    char* oh = (char*)a.o + (head0 * adv + dv0) * osz;
-    const bool last = seg == anseg - 1;
-    const bool boundary = seg % kChainGroup == kChainGroup - 1;
+    auto place = [&](int sg) __attribute__((always_inline)) {
+        seg_t0 = (long long)sg * aseg_len;
+        seg_n = (int)(min((long long)aN, seg_t0 + aseg_len) - seg_t0);  // tokens in this segment
+        nchunks = (seg_n + C - 1) / C;  // at most MAXC: the host plans segments of at most RT tokens
+        // REV: the rows of the run's chunk c start (in memory order) at token N - seg_t0 - c*C - L, so the head
+        // pointers address token 0 and rows_tok0 adds the chunk's first row.
+        head0 = ((long long)b * aN + (REV ? 0 : seg_t0)) * aH + h;
+        qh = (const uint16_t*)(PRE ? a.qr : a.q) + head0 * adk;
+        kh = (const uint16_t*)(PRE ? a.kr : a.k) + head0 * adk;
+        vh = (const uint16_t*)a.v + head0 * adv + dv0;
+        oh = (char*)a.o + (head0 * adv + dv0) * osz;
+    };
+    place(seg);
 
     // ---- loads: q, k and v rows of chunk c into register buffer c % NBUF. A chunk's buffer resources cover
     // its live rows only: rows past the sequence, and every row of a chunk past the segment (an empty
@@ -137,6 +144,16 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_seg_bf16(FwdArgs a) {
         }
     };
     static_for<0, (NBUF < F::MAXC ? NBUF : F::MAXC)>([&](auto cc) __attribute__((always_inline)) { issue(cc); });
+    {
+        const int tk = chain_ticket(ch, s_word);
+        if (tk != seg) {
+            seg = tk;
+            place(seg);
+            static_for<0, (NBUF < F::MAXC ? NBUF : F::MAXC)>([&](auto cc) __attribute__((always_inline)) { issue(cc); });
+        }
+    }
+    const bool last = seg == anseg - 1;
+    const bool boundary = seg % kChainGroup == kChainGroup - 1;
 
     // The local state: zero, or state_in for the first segment (which then needs no chain term).
     f32x4_t R[F::NKB];
