@@ -277,7 +277,7 @@ ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o,
                            int dv, ret_dtype_t in_dt, ret_dtype_t out_dt, const float* gamma, const double* theta,
                            int64_t pos0, int chunk, const float* state_in, float* state_out, void* workspace,
                            size_t workspace_bytes, void* stream, const EpiRequest* epi, bool* fused,
-                           bool rev = false) {
+                           bool rev = false, const double* out_theta = nullptr) {
     if (fused) *fused = false;
     ret_status_t st = check_common(q, k, v, o, B, N, H, dk, dv, in_dt, out_dt, gamma, theta);
     if (st != RET_OK) return st;
@@ -315,9 +315,14 @@ ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o,
         // once up front (several d_v tiles stage the same rows).
         fwd_kernel_t fn = onchip ? ck.seg : ck.fused;
         const fwd_kernel_t fn_pre = onchip ? (rev ? ck.seg_rev : ck.seg_pre) : ck.fused_pre;
-        // the reversed run exists for the on-chip kernel without rotation, state or epilogue only
-        if (rev && (!onchip || !ck.seg_rev || theta || state_in || state_out || epi))
-            return fail(RET_ERR_UNSUPPORTED, "reversed chunkwise run: not available for this shape");
+        // the reversed run and the rotation of the outputs exist for the on-chip kernel without input rotation,
+        // state or epilogue only
+        if ((rev || out_theta) && (!onchip || (rev && !ck.seg_rev) || theta || state_in || state_out || epi))
+            return fail(RET_ERR_UNSUPPORTED, "reversed or output-rotated chunkwise run: not available for this shape");
+        if (out_theta) {
+            A.orot = 1;
+            for (int i = 0; i < dv / 2; ++i) A.theta[i] = out_theta[i];
+        }
         const char* name = onchip ? "ret_chunk_seg" : "ret_chunk_fused";
         if (!theta) {
             fn = fn_pre;
@@ -372,8 +377,7 @@ ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o,
 
 // Workspace of the gradients. At offset 0 the segment chain the three retentions share (one call after
 // another; at least 256 bytes, so ret_chunkwise_check reads its header). Then, when both reversed retentions run
-// on the on-chip kernel's reversed traversal (direct, bf16 only): Q' and K' (bf16, only with rotation) and the
-// fp32 outputs dq', dk'. Otherwise the reordered inputs K', K' reversed, Q' reversed, V reversed, dO reversed (in
+// on the on-chip kernel's reversed traversal (direct, bf16 only): Q' and K' (bf16, only with rotation). Otherwise the reordered inputs K', K' reversed, Q' reversed, V reversed, dO reversed (in
 // the input dtype) and the three fp32 outputs.
 struct BwdLayout {
     bool direct;
@@ -398,9 +402,7 @@ bool bwd_layout(int B, int N, int H, int dk, int dv, int chunk, ret_dtype_t in_d
             L->kp = L->qp + up(nk * 2);
             off = L->kp + up(nk * 2);
         }
-        L->g1 = off;
-        L->g3 = L->g1 + up(nk * 4);
-        L->total = L->g3 + up(nk * 4);
+        L->total = off;
         return true;
     }
     L->kp = off;
@@ -626,7 +628,7 @@ ret_status_t ret_chunkwise_bwd(const void* q, const void* k, const void* v, cons
     if (L.direct) {
         // Q', K' (rotated once; q and k themselves without rotation), then dq' = retention(dO, V, K') and, over
         // the reversed sequence on the reversed traversal, dv = retention(K', Q', dO) and dk' = retention(V, dO,
-        // Q'), written in token order.
+        // Q'), written in token order; dq' and dk' leave their kernels turned back by the transpose rotation.
         const void *Qp = q, *Kp = k;
         if (theta) {
             FwdArgs A;
@@ -640,26 +642,17 @@ ret_status_t ret_chunkwise_bwd(const void* q, const void* k, const void* v, cons
             tr.done();
             if ((st = launch_status("ret_rotate_qk")) != RET_OK) return st;
         }
-        // without rotation dq' and dk' are the gradients: straight into dq, dk in the caller's dtype
-        void* G1 = theta ? (void*)(ws + L.g1) : dq;
-        void* G3 = theta ? (void*)(ws + L.g3) : dk_out;
-        const ret_dtype_t gdt = theta ? RET_F32 : out_dt;
+        // dq and dk straight from the retentions, their output rows turned back by the transpose rotation
         void* chain = ws + L.chain;
-        if ((st = chunkwise_run(dout, v, Kp, G1, B, N, H, dv, dk, RET_BF16, gdt, gamma, nullptr, 0, chunk, nullptr,
-                                nullptr, chain, L.chain_bytes, stream, nullptr, nullptr)) != RET_OK)
+        if ((st = chunkwise_run(dout, v, Kp, dq, B, N, H, dv, dk, RET_BF16, out_dt, gamma, nullptr, pos0, chunk,
+                                nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, false, theta)) !=
+            RET_OK)
             return st;
         if ((st = chunkwise_run(Kp, Qp, dout, dv_out, B, N, H, dk, dv, RET_BF16, out_dt, gamma, nullptr, 0, chunk,
                                 nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, true)) != RET_OK)
             return st;
-        if ((st = chunkwise_run(v, dout, Qp, G3, B, N, H, dv, dk, RET_BF16, gdt, gamma, nullptr, 0, chunk, nullptr,
-                                nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, true)) != RET_OK)
-            return st;
-        if (!theta) return RET_OK;
-        const PermJob post[2] = {
-            {G1, {dq, nullptr}, dk, -1, 0, {0, 0}, 0, ob},
-            {G3, {dk_out, nullptr}, dk, -1, 0, {0, 0}, 0, ob},
-        };
-        return permute(post, 2, B, N, H, theta, pos0, s);
+        return chunkwise_run(v, dout, Qp, dk_out, B, N, H, dv, dk, RET_BF16, out_dt, gamma, nullptr, pos0, chunk,
+                             nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, true, theta);
     }
     void *Kp = ws + L.kp, *Kr = ws + L.kr, *Qr = ws + L.qr, *Vr = ws + L.vr, *dOr = ws + L.dor;
     void *G1 = ws + L.g1, *G2 = ws + L.g2, *G3 = ws + L.g3, *chain = ws + L.chain;

@@ -390,6 +390,22 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_seg_bf16(FwdArgs a) {
     bf16x8_t rin[KK];
 #pragma unroll
     for (int k = 0; k < KK; ++k) rin[k] = acc_pair(Rin[2 * k], Rin[2 * k + 1]);
+    // a.orot (PRE only, for the gradients): every output row turned back by the transpose of the rotation at its
+    // position. The lane's tile values are columns dv0 + 16w + g4 .. + 3 (two pairs) of run row x*16 + n16; the
+    // factors start exactly at the lane's first row and step 16 rows at a time by angle addition.
+    float oc[2] = {1.f, 1.f}, os[2] = {0.f, 0.f}, sc[2] = {1.f, 1.f}, ss[2] = {0.f, 0.f};
+    if constexpr (PRE) {
+        if (a.orot) {
+            const int p0 = (dv0 + w * 16 + g4) / 2;
+            const long long t0 = seg_t0 + n16;  // run index of the lane's row in tile 0 of chunk 0
+            const long long pos = a.pos0 + (REV ? (long long)aN - 1 - t0 : t0);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                rot_cs(pos, a.theta[p0 + j], &oc[j], &os[j]);
+                rot_cs(REV ? -16 : 16, a.theta[p0 + j], &sc[j], &ss[j]);
+            }
+        }
+    }
     if (a.out_bf16) gate_issue(0, gq[0]);
     static_for<0, F::MAXC>([&](auto cc) __attribute__((always_inline)) {
         constexpr int c = decltype(cc)::value;
@@ -404,6 +420,21 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_seg_bf16(FwdArgs a) {
 #pragma unroll
                     for (int k = 0; k < KK; ++k) mfma(X, rin[k], frag_p(sQ + x * 16 * LD, LD, 32 * k, lane));
                     Op[c][x] += (gc * Xi[x]) * X;
+                }
+            }
+            if constexpr (PRE) {
+                if (a.orot) {
+#pragma unroll
+                    for (int x = 0; x < NB; ++x)
+#pragma unroll
+                        for (int j = 0; j < 2; ++j) {
+                            const float x0 = Op[c][x][2 * j], x1 = Op[c][x][2 * j + 1];
+                            Op[c][x][2 * j] = x0 * oc[j] + x1 * os[j];
+                            Op[c][x][2 * j + 1] = x1 * oc[j] - x0 * os[j];
+                            const float nc = oc[j] * sc[j] - os[j] * ss[j];
+                            os[j] = os[j] * sc[j] + oc[j] * ss[j];
+                            oc[j] = nc;
+                        }
                 }
             }
             if (a.out_bf16)

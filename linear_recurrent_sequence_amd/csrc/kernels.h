@@ -32,6 +32,9 @@ struct FwdArgs {
     const float* gn_bias;    // [H * dv] or null
     float eps;
     int epi, gate_bf16;
+    // Output rows turned back by the transpose rotation at their positions (theta, pos0), for kernels that stage
+    // q and k as given (the gradients' dq' and dk' retentions).
+    int orot;
     float log2g[kMaxHeads];
     double theta[kMaxPairs];
 };
