@@ -187,10 +187,11 @@ ret_status_t ret_chunkwise_msr_fwd(const void* q, const void* k, const void* v, 
  * each a retention (the last two over the reversed sequence) that the chunkwise kernels compute.
  * in_dt: BF16 or F32 (q, k, v, dout); out_dt: F32 or BF16 (dq, dk, dv; F32 for F32 input). No gradient for a
  * state in or out.
- * workspace: device memory of ret_chunkwise_bwd_workspace_bytes (zero-filled once by the caller, like the
- * chunkwise workspace; every call leaves its chain part zeroed again; ret_chunkwise_check accepts it and
- * reports a segment-chain wait that gave up). dq, dk, dv must not alias the inputs
- * or each other. Supported wherever the forward supports both (d_k, d_v) and (d_v, d_k) for the input dtype:
+ * workspace: device memory of ret_chunkwise_bwd_workspace_bytes for the input dtype (zero-filled once by the
+ * caller, like the chunkwise workspace; every call leaves its chain part zeroed again; ret_chunkwise_check
+ * accepts it and reports a segment-chain wait that gave up). dq, dk, dv must not alias the inputs or each
+ * other. Errors: RET_ERR_INVALID_ARG (as ret_chunkwise_fwd, a null or aliased gradient), RET_ERR_UNSUPPORTED
+ * (shape), RET_ERR_WORKSPACE (missing or smaller than the query). Supported wherever the forward supports both (d_k, d_v) and (d_v, d_k) for the input dtype:
  * BF16 d_k, d_v in {64, 128, 256}, chunk in {32, 64, 128, 256, 512}; F32 d_k, d_v in {16, 32, 64}, chunk in
  * {16, 32, 64}. The workspace query returns 0 for other shapes. Asynchronous on `stream`.
  */
@@ -206,7 +207,8 @@ ret_status_t ret_chunkwise_bwd(const void* q, const void* k, const void* v, cons
  * milliseconds and launch count recorded for kernels whose name equals `kernel` ("" or NULL = all).
  * ret_timing_reset drops the records. Kernel names: "ret_chunk_seg", "ret_chunk_fused" and "ret_rotate_qk"
  * (bf16 input), "ret_chunk_full", "ret_chunk_local", "ret_segment_scan" (fp32 input), "ret_parallel",
- * "ret_recurrent_step", "ret_msr_epilogue", "ret_permute_rotate" (gradients). Not for use while kernels are being captured into a graph.
+ * "ret_recurrent_step", "ret_msr_epilogue", "ret_permute_rotate" (gradients). Not for use while kernels are
+ * being captured into a graph.
  */
 int ret_timing_enable(int on);
 int ret_timing_query(const char* kernel, double* total_ms, int64_t* launches);
