@@ -83,6 +83,8 @@ SCHEDULES = {
     "loglinear": lambda H: W.gamma_schedule_loglinear(H),
     "single_rate": lambda H: np.full(H, 127 / 128, np.float32),
     "no_decay": lambda H: np.ones(H, np.float32),
+    # fast decays next to none: gamma^k underflows to zero within a chunk for the first heads
+    "mixed_extremes": lambda H: np.array([1e-3, 0.25, 0.999, 1.0][:H] + [0.9] * max(0, H - 4), np.float32),
 }
 
 
