@@ -367,7 +367,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1024, help="decode steps per graph (1024 in the workload)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+        print("bench.py measures one GPU only: the library has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
 
