@@ -4,15 +4,18 @@
 
 namespace ret {
 
-// The single-pass kernels, plus the on-chip variant for short segments.
+// The single-pass kernels, plus the on-chip variant for short segments. The on-chip kernel runs 32-token
+// sub-chunks whatever the chunk: its segment is on chip anyway, and shorter steps bring each chunk's first
+// products and the segment's aggregate earlier (retention-layer-d512: 26.0 against 27.3 us per call; 38 against
+// 42 us MALL-cold).
 template <int DK, int C>
 ChunkKernels chunk_entry_small() {
-    constexpr int CI = C > 64 ? 64 : C;
+    constexpr int CS = 32;
     ChunkKernels k = chunk_entry_bf16<DK, C>();
-    k.seg = chunk_seg_bf16<DK, CI, false>;
-    k.seg_pre = chunk_seg_bf16<DK, CI, true>;
-    k.seg_rev = chunk_seg_bf16<DK, CI, true, true>;
-    k.seg_tokens = SegB<DK, CI, false>::RT;
+    k.seg = chunk_seg_bf16<DK, CS, false>;
+    k.seg_pre = chunk_seg_bf16<DK, CS, true>;
+    k.seg_rev = chunk_seg_bf16<DK, CS, true, true>;
+    k.seg_tokens = SegB<DK, CS, false>::RT;
     return k;
 }
 
