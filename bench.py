@@ -324,21 +324,45 @@ def bench_decode(R, W, torch, steps_graph=1024, reps=3):
     return w, us_step, kernel_us
 
 
-def cpu_baseline(W, wid, seconds=10.0):
-    """The fp64 oracle's chunkwise form on this host: whole-workload runs repeated for about `seconds`."""
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(W, wid, seconds=10.0, single_seconds=4.0):
+    """The fp64 oracle's chunkwise form on this host: whole-workload runs repeated for about `seconds` with one
+    thread per (b, h) up to the oracle's default thread count, then a bounded single-thread sample (the first
+    B/8 sequences, at least one) for about `single_seconds`."""
     import oracle
     w = W.WORKLOADS[wid]
     q, k, v, _ = W.make_qkv(w)
     threads = min(oracle.default_threads(), w.B * w.H)
-    runs, total = 0, 0.0
-    while runs == 0 or total < seconds:
-        t0 = time.perf_counter()
-        oracle.chunkwise(q, k, v, w.gamma, w.chunk, theta=w.theta, threads=threads)
-        total += time.perf_counter() - t0
-        runs += 1
+
+    def timed(qq, kk, vv, nthreads, budget):
+        runs, total = 0, 0.0
+        while runs == 0 or total < budget:
+            t0 = time.perf_counter()
+            oracle.chunkwise(qq, kk, vv, w.gamma, w.chunk, theta=w.theta, threads=nthreads)
+            total += time.perf_counter() - t0
+            runs += 1
+        return runs, total
+
+    runs, total = timed(q, k, v, threads, seconds)
+    b1 = max(1, w.B // 8)
+    runs1, total1 = timed(q[:b1], k[:b1], v[:b1], 1, single_seconds)
     return {"value": runs * w.B * w.N / total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": "%d runs of the whole %s workload (B=%d N=%d H=%d), fp64 chunkwise form, %.1f s in total"
-                      % (runs, w.name, w.B, w.N, w.H, total)}
+                      % (runs, w.name, w.B, w.N, w.H, total),
+            "single_thread_value": runs1 * b1 * w.N / total1,
+            "single_thread_sample": "%d runs of %d of the %d sequences on one thread, %.1f s in total"
+                                    % (runs1, b1, w.B, total1),
+            "cpu_model": _cpu_model(), "host_cpus": len(os.sched_getaffinity(0))}
 
 
 def copy_calibration(torch):
