@@ -31,3 +31,13 @@ def to_host(t) -> np.ndarray:
 def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
     scale = float(np.abs(ref).max())
     return float(np.abs(got - ref).max()) / (scale if scale > 0 else 1.0)
+
+
+def rel_err_per_head(got: np.ndarray, ref: np.ndarray, head_axis: int = 2) -> list:
+    """The same metric per head ([B, N, H, d] tensors: axis 2), for the logs of the full-size checks."""
+    out = []
+    for h in range(ref.shape[head_axis]):
+        r = np.take(ref, h, axis=head_axis)
+        g = np.take(got, h, axis=head_axis)
+        out.append(rel_err(g, r))
+    return out

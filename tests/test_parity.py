@@ -11,7 +11,7 @@ import pytest
 import oracle
 from linear_recurrent_sequence_amd import workloads as W
 from tests.conftest import print_case
-from tests.helpers import empty_out, rel_err, to_dev, to_host, tol
+from tests.helpers import empty_out, rel_err, rel_err_per_head, to_dev, to_host, tol
 
 pytestmark = pytest.mark.gpu
 
@@ -453,6 +453,7 @@ def test_workload2_chunkwise_full(R):
     o, s = _gpu_chunkwise(R, q, k, v, w.dtype, w.gamma, w.chunk, theta=w.theta)
     eo, es = rel_err(o, o_ref), rel_err(s, s_ref)
     print("  err o=%.3g state=%.3g" % (eo, es))
+    print("  per head:", " ".join("%.2e" % e for e in rel_err_per_head(o, o_ref)))
     assert eo <= 2e-2 and es <= 2e-2
 
 
@@ -496,6 +497,7 @@ def test_workload4_chunkwise_full(R):
     o, s = _gpu_chunkwise(R, q, k, v, w.dtype, w.gamma, w.chunk, theta=w.theta)
     eo, es = rel_err(o, o_ref), rel_err(s, s_ref)
     print("  err o=%.3g state=%.3g" % (eo, es))
+    print("  per head:", " ".join("%.2e" % e for e in rel_err_per_head(o, o_ref)))
     assert eo <= 2e-2 and es <= 2e-2
 
 
