@@ -129,3 +129,15 @@ def test_gradients_workload2_full(R):
     ref = oracle.grad(q, k, v, do, w.gamma, theta=w.theta)
     got = _gpu_grad(R, q, k, v, do, w.gamma, w.chunk, w.theta, 0, "f32")
     _check(got, ref, tol("bf16"))
+
+
+def test_gradients_long_sequence_full(R):
+    """The long-sequence workload (B=1, N=65536, H=8, d=128, chunk 128) at full size: the streaming kernels on
+    reordered copies, 64 segments per head."""
+    w = W.WORKLOADS[5]
+    print_case("gradients-workload5", w)
+    q, k, v, rng = W.make_qkv(w)
+    do = W.make_dout(w, rng)
+    ref = oracle.grad(q, k, v, do, w.gamma, theta=w.theta)
+    got = _gpu_grad(R, q, k, v, do, w.gamma, w.chunk, w.theta, 0, "bf16")
+    _check(got, ref, tol("bf16"))
