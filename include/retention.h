@@ -84,8 +84,10 @@ ret_status_t ret_parallel_fwd(const void* q, const void* k, const void* v, void*
  * 0 means the call runs one segment per (b, h) and needs none. A smaller workspace is allowed: the call then
  * first drops the rotated copies, then uses fewer segments; the results are the same up to rounding order.
  * The workspace must be zero-filled before its first use. Every call leaves it in a state the next call
- * accepts: the header (first 256 bytes) zero except a sticky error word, counters and flags zero. Calls
- * sharing a workspace must not overlap in time (on one stream they do not). The library never frees it.
+ * accepts: the header (first 256 bytes) zero except a sticky error word, counters and flags zero (they occupy
+ * the first 64 KB, ahead of every shape's state slots, while units x segments stays below about 16,000; beyond
+ * that, zero-fill the workspace again before a call of another shape). Calls sharing a workspace must not
+ * overlap in time (on one stream they do not). The library never frees it.
  */
 size_t ret_chunkwise_workspace_bytes(int B, int N, int H, int dk, int dv, int chunk, ret_dtype_t in_dt);
 
@@ -191,9 +193,12 @@ ret_status_t ret_chunkwise_msr_fwd(const void* q, const void* k, const void* v, 
  * caller, like the chunkwise workspace; every call leaves its chain part zeroed again; ret_chunkwise_check
  * accepts it and reports a segment-chain wait that gave up). dq, dk, dv must not alias the inputs or each
  * other. Errors: RET_ERR_INVALID_ARG (as ret_chunkwise_fwd, a null or aliased gradient), RET_ERR_UNSUPPORTED
- * (shape), RET_ERR_WORKSPACE (missing or smaller than the query). Supported wherever the forward supports both (d_k, d_v) and (d_v, d_k) for the input dtype:
- * BF16 d_k, d_v in {64, 128, 256}, chunk in {32, 64, 128, 256, 512}; F32 d_k, d_v in {16, 32, 64}, chunk in
- * {16, 32, 64}. The workspace query returns 0 for other shapes. Asynchronous on `stream`.
+ * (shape), RET_ERR_WORKSPACE (missing or smaller than the query). Supported wherever the forward supports
+ * (d_k, d_v) and (w, d_k) for the input dtype, with w = d_v or, when d_v is too wide for a retention's d_k,
+ * w = d_v / 2 (dq' and dk' are then sums of two retentions over the halves of d_v): BF16 d_k in {64, 128, 256}
+ * and d_v in {64, 128, 256, 512} (the paper's d_k = 256, d_v = 512 included), every BF16 chunk size; F32 d_k in
+ * {16, 32, 64}, d_v in {16, 32, 64, 128}, chunk in {16, 32, 64}. The workspace query returns 0 for other
+ * shapes. Asynchronous on `stream`.
  */
 size_t ret_chunkwise_bwd_workspace_bytes(int B, int N, int H, int dk, int dv, int chunk, ret_dtype_t in_dt);
 ret_status_t ret_chunkwise_bwd(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk_out,

@@ -381,18 +381,30 @@ ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o,
 // the input dtype) and the three fp32 outputs.
 struct BwdLayout {
     bool direct;
+    int nb, wb;  // d_v blocks of width wb for the retentions that contract over d_v (nb = 2 when d_v is wider
+                 // than their kernels' d_k; dq' and dk' are then sums of two retentions)
     size_t qp, kp, kr, qr, vr, dor, g1, g2, g3, chain, chain_bytes, total;
+    size_t vbn[2], dobn[2], vbr[2], dobr[2], g1b[2], g3b[2];  // per block (nb = 2)
 };
 bool bwd_layout(int B, int N, int H, int dk, int dv, int chunk, ret_dtype_t in_dt, bool rotate, BwdLayout* L) {
     ChunkKernels ca, cb;
-    if (!pick_chunk(in_dt, dv, dk, chunk, &ca) || !pick_chunk(in_dt, dk, dv, chunk, &cb)) return false;
+    memset(L, 0, sizeof(*L));
+    L->nb = 1;
+    L->wb = dv;
+    if (!pick_chunk(in_dt, dv, dk, chunk, &ca)) {
+        // d_v too wide to be the contraction width of a retention: two halves, each a retention of its own
+        if (dv % 2 || (dv / 2) % 16 || !pick_chunk(in_dt, dv / 2, dk, chunk, &ca)) return false;
+        L->nb = 2;
+        L->wb = dv / 2;
+    }
+    if (!pick_chunk(in_dt, dk, dv, chunk, &cb)) return false;
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     const size_t nk = (size_t)B * N * H * dk, nv = (size_t)B * N * H * dv, es = in_dt == RET_BF16 ? 2 : 4;
-    const ChunkPlan pa = plan_chunk(ca, B, N, H, dv, dk, chunk, false, SIZE_MAX);
+    const size_t nw = (size_t)B * N * H * L->wb;
+    const ChunkPlan pa = plan_chunk(ca, B, N, H, L->wb, dk, chunk, false, SIZE_MAX);
     const ChunkPlan pb = plan_chunk(cb, B, N, H, dk, dv, chunk, false, SIZE_MAX);
-    memset(L, 0, sizeof(*L));
-    L->direct = in_dt == RET_BF16 && plan_onchip(ca, pa) && ca.seg_rev && plan_onchip(cb, pb) && cb.seg_rev &&
-                env_int("RET_BWD_DIRECT", 1) != 0;
+    L->direct = in_dt == RET_BF16 && L->nb == 1 && plan_onchip(ca, pa) && ca.seg_rev && plan_onchip(cb, pb) &&
+                cb.seg_rev && env_int("RET_BWD_DIRECT", 1) != 0;
     L->chain = 0;
     L->chain_bytes = pa.chain_bytes > pb.chain_bytes ? pa.chain_bytes : pb.chain_bytes;
     size_t off = up(L->chain_bytes > 256 ? L->chain_bytes : 256);
@@ -403,6 +415,28 @@ bool bwd_layout(int B, int N, int H, int dk, int dv, int chunk, ret_dtype_t in_d
             off = L->kp + up(nk * 2);
         }
         L->total = off;
+        return true;
+    }
+    if (L->nb == 2) {
+        L->kp = off;
+        L->kr = L->kp + up(nk * es);
+        L->qr = L->kr + up(nk * es);
+        L->dor = L->qr + up(nk * es);
+        off = L->dor + up(nv * es);
+        for (int i = 0; i < 2; ++i) {
+            L->vbn[i] = off;
+            L->dobn[i] = L->vbn[i] + up(nw * es);
+            L->vbr[i] = L->dobn[i] + up(nw * es);
+            L->dobr[i] = L->vbr[i] + up(nw * es);
+            off = L->dobr[i] + up(nw * es);
+        }
+        for (int i = 0; i < 2; ++i) {
+            L->g1b[i] = off;
+            L->g3b[i] = L->g1b[i] + up(nk * 4);
+            off = L->g3b[i] + up(nk * 4);
+        }
+        L->g2 = off;
+        L->total = L->g2 + up(nv * 4);
         return true;
     }
     L->kp = off;
@@ -417,6 +451,24 @@ bool bwd_layout(int B, int N, int H, int dk, int dv, int chunk, ret_dtype_t in_d
     return true;
 }
 
+// The gradients' retentions share one segment chain, but calls of different shapes lay it out differently:
+// one call's published slots can lie where the next call expects zero counters and flags. Before a call whose
+// layout differs from the previous call's, its counters and flags (not the header, which keeps a sticky error)
+// are zeroed by a small kernel (graph-safe, unlike a memset node).
+ret_status_t chain_meta_zero(ret_dtype_t in_dt, int B, int N, int H, int dk, int dv, int chunk, void* chain,
+                             size_t chain_bytes, hipStream_t s) {
+    ChunkKernels ck;
+    if (!pick_chunk(in_dt, dk, dv, chunk, &ck) || !ck.fused) return RET_OK;  // the split kernels keep no flags
+    const ChunkPlan p = plan_chunk(ck, B, N, H, dk, dv, chunk, false, chain_bytes);
+    if (p.nseg <= 1) return RET_OK;
+    const ChainLayout lay = chain_layout(B * H * (dv / ck.dvt), p.nseg, dk * ck.dvt);
+    const long long n = (long long)(lay.agg_off - lay.ctr_off) / 4;
+    hipLaunchKernelGGL(zero_words_get(), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       (int*)((char*)chain + lay.ctr_off), n);
+    return launch_status("chain_meta_zero");
+}
+
+// One launch of permute_rotate_kernel over the given jobs (at most kMaxPermJobs), one grid row per job.
 ret_status_t permute(const PermJob* jobs, int njobs, int B, int N, int H, const double* theta, int64_t pos0,
                      hipStream_t s) {
     PermArgs P;
@@ -654,10 +706,50 @@ ret_status_t ret_chunkwise_bwd(const void* q, const void* k, const void* v, cons
         return chunkwise_run(v, dout, Qp, dk_out, B, N, H, dv, dk, RET_BF16, out_dt, gamma, nullptr, pos0, chunk,
                              nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, true, theta);
     }
+    const int ib = in_dt == RET_BF16;
+    if (L.nb == 2) {
+        // dq' = sum over the two d_v halves b of retention(dO_b, V_b, K'); dk'^rev likewise of
+        // retention(V_b^rev, dO_b^rev, Q'^rev); dv^rev = retention(K'^rev, Q'^rev, dO^rev) over the whole d_v
+        void *Kp = ws + L.kp, *Kr = ws + L.kr, *Qr = ws + L.qr, *dOr = ws + L.dor, *chain = ws + L.chain;
+        const int wb = L.wb;
+        const PermJob pre[3] = {
+            {k, {Kp, Kr}, dk, 1, 0, {0, 1}, ib, ib},
+            {q, {Qr, nullptr}, dk, 1, 0, {1, 0}, ib, ib},
+            {dout, {dOr, nullptr}, dv, 0, 0, {1, 0}, ib, ib},
+        };
+        if ((st = permute(pre, 3, B, N, H, theta, pos0, s)) != RET_OK) return st;
+        const PermJob halves[4] = {
+            {v, {ws + L.vbn[0], ws + L.vbr[0]}, wb, 0, 0, {0, 1}, ib, ib, nullptr, dv, 0},
+            {v, {ws + L.vbn[1], ws + L.vbr[1]}, wb, 0, 0, {0, 1}, ib, ib, nullptr, dv, wb},
+            {dout, {ws + L.dobn[0], ws + L.dobr[0]}, wb, 0, 0, {0, 1}, ib, ib, nullptr, dv, 0},
+            {dout, {ws + L.dobn[1], ws + L.dobr[1]}, wb, 0, 0, {0, 1}, ib, ib, nullptr, dv, wb},
+        };
+        if ((st = permute(halves, 4, B, N, H, nullptr, 0, s)) != RET_OK) return st;
+        for (int i = 0; i < 2; ++i)
+            if ((st = chunkwise_run(ws + L.dobn[i], ws + L.vbn[i], Kp, ws + L.g1b[i], B, N, H, wb, dk, in_dt, RET_F32,
+                                    gamma, nullptr, 0, chunk, nullptr, nullptr, chain, L.chain_bytes, stream, nullptr,
+                                    nullptr)) != RET_OK)
+                return st;
+        if ((st = chain_meta_zero(in_dt, B, N, H, dk, dv, chunk, chain, L.chain_bytes, s)) != RET_OK) return st;
+        if ((st = chunkwise_run(Kr, Qr, dOr, ws + L.g2, B, N, H, dk, dv, in_dt, RET_F32, gamma, nullptr, 0, chunk,
+                                nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr)) != RET_OK)
+            return st;
+        if ((st = chain_meta_zero(in_dt, B, N, H, wb, dk, chunk, chain, L.chain_bytes, s)) != RET_OK) return st;
+        for (int i = 0; i < 2; ++i)
+            if ((st = chunkwise_run(ws + L.vbr[i], ws + L.dobr[i], Qr, ws + L.g3b[i], B, N, H, wb, dk, in_dt, RET_F32,
+                                    gamma, nullptr, 0, chunk, nullptr, nullptr, chain, L.chain_bytes, stream, nullptr,
+                                    nullptr)) != RET_OK)
+                return st;
+        const PermJob post[3] = {
+            {ws + L.g1b[0], {dq, nullptr}, dk, -1, 0, {0, 0}, 0, ob, ws + L.g1b[1]},
+            {ws + L.g3b[0], {dk_out, nullptr}, dk, -1, 1, {0, 0}, 0, ob, ws + L.g3b[1]},
+            {ws + L.g2, {dv_out, nullptr}, dv, 0, 1, {0, 0}, 0, ob},
+        };
+        return permute(post, 3, B, N, H, theta, pos0, s);
+    }
     void *Kp = ws + L.kp, *Kr = ws + L.kr, *Qr = ws + L.qr, *Vr = ws + L.vr, *dOr = ws + L.dor;
     void *G1 = ws + L.g1, *G2 = ws + L.g2, *G3 = ws + L.g3, *chain = ws + L.chain;
     // inputs of the three retentions: K' in order; K', Q', V and dO reversed (one launch, in the input dtype)
-    const int ib = in_dt == RET_BF16;
     const PermJob pre[4] = {
         {k, {Kp, Kr}, dk, 1, 0, {0, 1}, ib, ib},
         {q, {Qr, nullptr}, dk, 1, 0, {1, 0}, ib, ib},
@@ -669,8 +761,12 @@ ret_status_t ret_chunkwise_bwd(const void* q, const void* k, const void* v, cons
     if ((st = chunkwise_run(dout, v, Kp, G1, B, N, H, dv, dk, in_dt, RET_F32, gamma, nullptr, 0, chunk, nullptr,
                             nullptr, chain, L.chain_bytes, stream, nullptr, nullptr)) != RET_OK)
         return st;
+    if (dk != dv && (st = chain_meta_zero(in_dt, B, N, H, dk, dv, chunk, chain, L.chain_bytes, s)) != RET_OK)
+        return st;
     if ((st = chunkwise_run(Kr, Qr, dOr, G2, B, N, H, dk, dv, in_dt, RET_F32, gamma, nullptr, 0, chunk, nullptr,
                             nullptr, chain, L.chain_bytes, stream, nullptr, nullptr)) != RET_OK)
+        return st;
+    if (dk != dv && (st = chain_meta_zero(in_dt, B, N, H, dv, dk, chunk, chain, L.chain_bytes, s)) != RET_OK)
         return st;
     if ((st = chunkwise_run(Vr, dOr, Qr, G3, B, N, H, dv, dk, in_dt, RET_F32, gamma, nullptr, 0, chunk, nullptr,
                             nullptr, chain, L.chain_bytes, stream, nullptr, nullptr)) != RET_OK)

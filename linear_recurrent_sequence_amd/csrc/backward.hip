@@ -19,12 +19,12 @@ namespace {
 // job (blockIdx.y: the job's fields are scalar loads). Its loads are issued together; the rotation factors of
 // the first token are evaluated exactly and carried to the next by angle addition with the one-token step.
 // Consecutive threads take consecutive segments of a row, and a job with two outputs writes both from one read.
-__device__ __forceinline__ void perm_load(const PermJob& J, long long i, float* x) {
-    if (J.in_bf16) {
-        unpack8_bf16(*reinterpret_cast<const uint4*>((const uint16_t*)J.in + i), x);
+__device__ __forceinline__ void perm_load(const void* p, bool bf16, long long i, float* x) {
+    if (bf16) {
+        unpack8_bf16(*reinterpret_cast<const uint4*>((const uint16_t*)p + i), x);
     } else {
-        const float4 u = *reinterpret_cast<const float4*>((const float*)J.in + i);
-        const float4 w = *reinterpret_cast<const float4*>((const float*)J.in + i + 4);
+        const float4 u = *reinterpret_cast<const float4*>((const float*)p + i);
+        const float4 w = *reinterpret_cast<const float4*>((const float*)p + i + 4);
         x[0] = u.x, x[1] = u.y, x[2] = u.z, x[3] = u.w, x[4] = w.x, x[5] = w.y, x[6] = w.z, x[7] = w.w;
     }
 }
@@ -50,10 +50,25 @@ __global__ __launch_bounds__(256) void permute_rotate_kernel(PermArgs a) {
     const long long rowlen = (long long)a.H * J.d;
     const unsigned col = sj * 8u;
     const long long base = (long long)b * a.N * rowlen + col;
+    // input: columns col0 .. col0 + d - 1 of each head of width d_in
+    const int din = J.d_in ? J.d_in : J.d;
+    const unsigned hh = col / (unsigned)J.d, cc = col - hh * (unsigned)J.d;
+    const long long rowlen_in = (long long)a.H * din;
+    const long long ibase = (long long)b * a.N * rowlen_in + (long long)hh * din + J.col0 + cc;
     float x[kPermTokens][8];
 #pragma unroll
     for (int i = 0; i < kPermTokens; ++i)
-        if (i < nt) perm_load(J, base + (J.in_rev ? a.N - 1 - (t0 + i) : t0 + i) * rowlen, x[i]);
+        if (i < nt) perm_load(J.in, J.in_bf16, ibase + (J.in_rev ? a.N - 1 - (t0 + i) : t0 + i) * rowlen_in, x[i]);
+    if (J.in2) {
+#pragma unroll
+        for (int i = 0; i < kPermTokens; ++i)
+            if (i < nt) {
+                float y[8];
+                perm_load(J.in2, J.in_bf16, ibase + (J.in_rev ? a.N - 1 - (t0 + i) : t0 + i) * rowlen_in, y);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[i][e] += y[e];
+            }
+    }
     if (J.rot) {
         const int pair0 = (int)(col % (unsigned)J.d) / 2;
         float c[4], s[4], dc[4], ds[4];
@@ -85,8 +100,14 @@ __global__ __launch_bounds__(256) void permute_rotate_kernel(PermArgs a) {
     }
 }
 
+__global__ __launch_bounds__(256) void zero_words_kernel(int* p, long long n) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0;
+}
+
 }  // namespace
 
 perm_kernel_t permute_rotate_get() { return permute_rotate_kernel; }
+zero_kernel_t zero_words_get() { return zero_words_kernel; }
 
 }  // namespace ret

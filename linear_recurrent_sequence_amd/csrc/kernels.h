@@ -97,12 +97,17 @@ struct ChainHeader {
 struct ChainLayout {
     size_t ctr_off, flags_off, agg_off, inc_off, bytes;
 };
+// Counters and flags take the first kChainMeta bytes whenever they fit: a call leaves them zero, and the slots of
+// any layout start past them, so a workspace can pass between calls of different shapes (units x segments up to
+// about 16,000) without being cleared again.
+constexpr size_t kChainMeta = 64 * 1024;
 __host__ __device__ inline ChainLayout chain_layout(int units, int nseg, int slot_floats) {
     ChainLayout L;
     const size_t nslots = (size_t)units * nseg;
     L.ctr_off = sizeof(ChainHeader);
     L.flags_off = L.ctr_off + ((size_t)units * 8 + 255) / 256 * 256;
     L.agg_off = L.flags_off + (nslots * 4 + 255) / 256 * 256;
+    if (L.agg_off < kChainMeta) L.agg_off = kChainMeta;
     L.inc_off = L.agg_off + nslots * slot_floats * 4;
     L.bytes = L.inc_off + nslots * slot_floats * 4;
     return L;
@@ -1004,12 +1009,15 @@ typedef void (*epi_kernel_t)(EpiArgs);
 // t = out_rev ? N-1-n : n, read from input row in_rev ? N-1-t : t and turned by rot_sign (pos0 + t) theta_i on
 // pairs (2i, 2i+1) (rot_sign 0: copied; -1: the transpose rotation). One 256-thread workgroup per 2048 values.
 // Reordering and rotation of [B, N, H, d] tensors (the gradients' inputs and outputs). Per token t (rotation
-// angle (pos0 + t) theta_i), job j reads row (in_rev ? N-1-t : t) of `in` and writes row (rev ? N-1-t : t) of
-// out[0] and, if not null, of out[1]; rot: +1 turns by the rotation, -1 by its transpose, 0 copies.
+// angle (pos0 + t) theta_i), job j reads row (in_rev ? N-1-t : t) of `in` (columns col0 .. col0 + d - 1 of each
+// head of width d_in), adds the same of `in2` if given, and writes row (rev ? N-1-t : t) of out[0] and, if not
+// null, of out[1]; rot: +1 turns by the rotation, -1 by its transpose, 0 copies.
 struct PermJob {
     const void* in;
     void* out[2];
     int d, rot, in_rev, out_rev[2], in_bf16, out_bf16;
+    const void* in2;  // added to `in` before the rotation (same layout and dtype), or null
+    int d_in, col0;   // input head width (0: d) and the first input column of each head taken
 };
 constexpr int kMaxPermJobs = 4;
 constexpr int kPermTokens = 4;  // consecutive tokens per thread
@@ -1021,6 +1029,9 @@ struct PermArgs {
 };
 typedef void (*perm_kernel_t)(PermArgs);
 perm_kernel_t permute_rotate_get();
+// Zeroes n 32-bit words (a segment chain's counters and flags between calls whose chain layouts differ).
+typedef void (*zero_kernel_t)(int*, long long);
+zero_kernel_t zero_words_get();
 // Kernel for d_v in {16, 32, 64, 128, 256, 512} (null otherwise) and its groups per 256-thread workgroup.
 epi_kernel_t epilogue_kernel_get(int dv, int* groups_per_wg);
 

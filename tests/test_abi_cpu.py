@@ -77,9 +77,9 @@ def test_workspace_query(lib):
     # one (b, h) with a long sequence is split into segments; many short sequences are not
     n_long = lib.ret_chunkwise_workspace_bytes(1, 65536, 8, 128, 128, 128, 1)
     # 16 units (8 heads x 2 d_v tiles of 64) x 64 segments of 1024 tokens: a 256-byte header, two int
-    # counters per unit (padded to 256 bytes), one int flag per (unit, segment) and two 128x64 fp32 state
+    # counters per unit and one int flag per (unit, segment) in the first 64 KB, then two 128x64 fp32 state
     # slots (aggregate, inclusive prefix) per (unit, segment)
-    assert n_long == 256 + 256 + 16 * 64 * 4 + 2 * 16 * 64 * 128 * 64 * 4
+    assert n_long == 64 * 1024 + 2 * 16 * 64 * 128 * 64 * 4
     # fp32 input runs the split kernels: the header, then one d_k x d_v state per (b, h, segment)
     n_f32 = lib.ret_chunkwise_workspace_bytes(1, 4096, 2, 64, 64, 64, 0)
     assert n_f32 > 256 and (n_f32 - 256) % (2 * 64 * 64 * 4) == 0
@@ -150,7 +150,11 @@ def test_gradients_workspace_and_rejections(lib):
     n2 = 1 * 4096 * 4 * 128
     assert wsq(1, 4096, 4, 128, 128, 64) >= 5 * n2 * 2 + 3 * n2 * 4
     assert wsq(1, 100, 2, 32, 64, 64) == 0      # d_k = 32: no bf16 kernel
-    assert wsq(1, 8192, 16, 256, 512, 128) == 0  # d_v = 512 would be the d_k of dq's retention
+    # d_v = 512 is wider than any retention's d_k: dq' and dk' are sums over two halves of 256 (copies of each
+    # half of V and dO, natural and reversed, and two fp32 outputs per half)
+    n4k, n4v = 8192 * 16 * 256, 8192 * 16 * 512
+    assert wsq(1, 8192, 16, 256, 512, 128) >= 3 * n4k * 2 + n4v * 2 + 8 * n4k * 2 + 4 * n4k * 4 + n4v * 4
+    assert wsq(1, 100, 2, 64, 1024, 64) == 0     # halves of 512 are still too wide
     assert wsq(1, 0, 2, 64, 64, 64) == 0
     g = np.asarray([0.9, 0.99], np.float32).ctypes.data_as(ctypes.POINTER(ctypes.c_float))
     need = wsq(1, 64, 2, 64, 64, 64)

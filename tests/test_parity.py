@@ -534,3 +534,29 @@ def test_workload5_long_sequence_then_256_decode_steps(R):
     ed, esd = rel_err(got, od_ref), rel_err(to_host(state), sd_ref)
     print("  decode err o=%.3g state=%.3g" % (ed, esd))
     assert ed <= 2e-2 and esd <= 2e-2
+
+
+def test_workspace_shared_by_calls_of_different_shapes(R):
+    """One workspace for calls of different shapes in turn: a small chain layout (2 units), a large one (64
+    units, whose counters and flags would lie over the small layout's state slots if these were not kept
+    apart), then the small one again; each against the oracle."""
+    import torch
+    print_case("workspace_shared")
+    rng = np.random.default_rng(71)
+    shapes = [(1, 2048, 2, 64, 64), (8, 2048, 8, 64, 64), (1, 2048, 2, 64, 64)]
+    need = max(R.load().ret_chunkwise_workspace_bytes(b, n, h, dk, dv, 64, R.RET_BF16) for b, n, h, dk, dv in shapes)
+    ws = torch.zeros((need,), dtype=torch.uint8, device="cuda")
+    for i, (B, N, H, dk, dv) in enumerate(shapes):
+        q = W.normal(rng, (B, N, H, dk), 8.0, "bf16")
+        k = W.normal(rng, (B, N, H, dk), 8.0, "bf16")
+        v = W.normal(rng, (B, N, H, dv), 8.0, "bf16")
+        gamma, theta = W.gamma_schedule(H), W.theta_schedule(dk)
+        qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+        o = empty_out((B, N, H, dv), "bf16")
+        R.ret_chunkwise_fwd(qd, kd, vd, o, gamma, 64, theta=theta, workspace=ws)
+        torch.cuda.synchronize()
+        R.ret_chunkwise_check(ws)
+        o_ref, _ = oracle.chunkwise(q, k, v, gamma, 64, theta=theta)
+        e = rel_err(to_host(o), o_ref)
+        print("  call %d %s: err %.3g" % (i, (B, N, H, dk, dv), e))
+        assert e <= tol("bf16"), (i, e)

@@ -52,6 +52,9 @@ GRAD_SMALL = [
     (1, 1000, 3, 64, 64, 32, True, 0, "bf16"),  # chunk 32
     (2, 600, 2, 64, 64, 64, False, 0, "bf16"),  # no rotation: dq and dk written by the retentions themselves
     (1, 777, 2, 64, 64, 128, True, 4, "f32"),   # chunk 128 as 64-token sub-chunks
+    # d_v = 512 (the paper's head: d_k 256, d_v 512): dq' and dk' as sums over two halves of d_v
+    (1, 700, 2, 256, 512, 128, True, 5, "bf16"),
+    (2, 300, 1, 128, 512, 64, False, 0, "f32"),
 ]
 
 
@@ -84,6 +87,7 @@ def test_gradients_both_paths(R, direct, monkeypatch):
 F32_CASES = [
     # B, N, H, dk, dv, chunk, rotate, pos0
     (2, 150, 2, 32, 32, 32, True, 3),
+    (1, 200, 2, 64, 128, 32, True, 7),   # d_v = 128: two halves of 64 (the fp32 kernels' widest d_k)
     (1, 300, 3, 64, 16, 64, True, 0),
     (2, 77, 2, 16, 64, 16, False, 0),
 ]
@@ -136,6 +140,18 @@ def test_gradients_long_sequence_full(R):
     reordered copies, 64 segments per head."""
     w = W.WORKLOADS[5]
     print_case("gradients-workload5", w)
+    q, k, v, rng = W.make_qkv(w)
+    do = W.make_dout(w, rng)
+    ref = oracle.grad(q, k, v, do, w.gamma, theta=w.theta)
+    got = _gpu_grad(R, q, k, v, do, w.gamma, w.chunk, w.theta, 0, "bf16")
+    _check(got, ref, tol("bf16"))
+
+
+def test_gradients_7b_class_layer_full(R):
+    """The 7b-class-layer workload (B=1, N=8192, H=16, d_k=256, d_v=512, chunk 128) at full size: the paper's
+    head shape, dq' and dk' as sums over the two halves of d_v."""
+    w = W.WORKLOADS[4]
+    print_case("gradients-workload4", w)
     q, k, v, rng = W.make_qkv(w)
     do = W.make_dout(w, rng)
     ref = oracle.grad(q, k, v, do, w.gamma, theta=w.theta)
