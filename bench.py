@@ -1,23 +1,30 @@
 #!/usr/bin/env python3
 """Benchmark of the retention hot path on one MI355X.
 
-A step is one ret_chunkwise_fwd call over the d_model=512 retention-layer workload (B=8, N=2048, H=8,
-d_k=d_v=64, chunk 64, bf16 inputs/outputs, xPos rotation, fp32 state out): tokens/s = B*N / step time,
-with inputs resident in HBM (a MALL-cold median, each call after a 512 MiB scratch write, is reported beside
-it). The same JSON line carries the batched-decode workload (B=128, H=8, d=64,
-fp32 state, 1024 single-token ret_recurrent_step calls replayed from a HIP graph) in steps/s, the
-multi-scale retention epilogue (GroupNorm per head and swish gate) on the chunkwise output, alone and after
-the chunkwise call, the gradients dq, dk, dv of the chunkwise call, the roofline of each path's dominant
-kernel (per-launch HIP-event durations recorded by the library over the timed region), and the fp64 CPU
-oracle timed on this host.
+A step is one ret_chunkwise_fwd call over the 7b-class retention layer (B=1, N=8192, H=16, d_k=256, d_v=512,
+chunk 128, bf16 inputs/outputs, xPos rotation, fp32 state out): tokens/s = B*N / step time, with inputs
+resident in HBM, from a replayed HIP graph of `steps` calls. Its roofline is the MFMA one: causal-count FLOPs
+per call over the dominant kernel's average launch duration (HIP events the library records on the launch
+stream, through a caller-owned timer, over the timed region), against the dense bf16 peak; the HBM fraction
+of the same kernel is reported beside it.
+
+The same JSON line carries, each with its own roofline:
+  * long-sequence (B=1, N=65536, H=8, d=128, chunk 128) and retention-layer-d512 (B=8, N=2048, H=8, d=64,
+    chunk 64) chunkwise calls, warm and MALL-cold (each call after a 512 MiB scratch write);
+  * batched decode (B=128, H=8, d=64, fp32 state, 1024 single-token ret_recurrent_step calls replayed from a
+    HIP graph), warm (one 16 MiB state, which the 256 MB Infinity Cache holds between steps) and MALL-cold
+    (the graph's steps cycle through 32 distinct states, 512 MiB, so every state read comes from HBM);
+  * the multi-scale retention epilogue on the d512 layer's output, and the gradients of each chunkwise
+    workload;
+  * the fp64 CPU oracle timed on this host on a bounded sample of the 7b-class workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-decode] [--no-epilogue]
-                       [--no-backward] [--no-cpu-baseline] [--copy-calibration] [--decode-steps S]
+                       [--no-backward] [--no-cpu-baseline] [--no-extra] [--copy-calibration]
+                       [--decode-steps S]
 """
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -32,17 +39,15 @@ METRIC = "retention fwd tokens/sec (chunkwise) + decode steps/sec; % MFMA / HBM 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # Chunkwise workloads by name -> key (and seed) in workloads.WORKLOADS
 CHUNK_WORKLOADS = {"retention-layer-d512": 2, "7b-class-layer": 4, "long-sequence": 5}
+CHUNK_KERNELS = ("ret_rotate_qk", "ret_chunk_seg", "ret_chunk_fused", "ret_chunk_local", "ret_segment_scan",
+                 "ret_chunk_full")
 
 
 def source_digest() -> str:
-    """Digest of the HIP sources; counter-based traffic figures are only valid for the sources they came from."""
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "linear_recurrent_sequence_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
-    return h.hexdigest()[:16]
+    """Digest of the library's sources; counter-based traffic figures are only valid for the sources they came
+    from."""
+    from linear_recurrent_sequence_amd import build
+    return build.source_digest()
 
 
 def chunk_algorithmic(w, in_bytes=2, out_bytes=2):
@@ -65,11 +70,14 @@ def decode_algorithmic(B, H, dk, dv, in_bytes=2, out_bytes=2):
 
 
 def load_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload` from the recorded FETCH_SIZE / WRITE_SIZE counters, scaled
+    by a plain copy's counters; None unless recorded for the current sources."""
     try:
         with open(TRAFFIC_FILE) as f:
-            rec = json.load(f).get(kernel)
+            recs = json.load(f)
     except (OSError, ValueError):
         return None
+    rec = recs.get("%s@%s" % (kernel, workload)) or recs.get(kernel)
     if not rec or rec.get("workload") != workload or rec.get("source_digest") != source_digest():
         return None
     fetch = rec["fetch_kib_per_launch"] * 1024.0 / rec["copy_factor_fetch"]
@@ -77,85 +85,9 @@ def load_traffic(kernel: str, workload: str):
     return fetch + write
 
 
-def bench_chunkwise(R, W, torch, wid, steps, warmup):
-    import numpy as np
-    w = W.WORKLOADS[wid]
-    q, k, v, _ = W.make_qkv(w)
-    dev = lambda x: torch.from_numpy(x).to(torch.bfloat16).cuda()
-    qd, kd, vd = dev(q), dev(k), dev(v)
-    del q, k, v
-    o = torch.empty((w.B, w.N, w.H, w.dv), dtype=torch.bfloat16, device="cuda")
-    state = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
-    ws = R.chunkwise_workspace(qd, vd, w.chunk)
-
-    def step():
-        R.ret_chunkwise_fwd(qd, kd, vd, o, w.gamma, w.chunk, theta=w.theta, state_out=state, workspace=ws)
-
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    R.timing_reset()
-    R.timing_enable(True)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    R.timing_enable(False)
-    ms_step = e0.elapsed_time(e1) / steps
-    kernels = {}
-    for name in ("ret_rotate_qk", "ret_chunk_seg", "ret_chunk_fused", "ret_chunk_local", "ret_segment_scan",
-                 "ret_chunk_full"):
-        tot, n = R.timing_query(name)
-        if n:
-            kernels[name] = {"avg_us": 1e3 * tot / n, "launches": n}
-    R.timing_reset()
-    # second timed pass without the per-kernel events, for the step time itself
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms_clean = e0.elapsed_time(e1) / steps
-    # third timed pass: the same calls replayed from a captured HIP graph (no host launch cost between them)
-    g = torch.cuda.CUDAGraph()
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        with torch.cuda.graph(g, stream=s):
-            for _ in range(steps):
-                step()
-    torch.cuda.current_stream().wait_stream(s)
-    g.replay()
-    torch.cuda.synchronize()
-    e0.record()
-    g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    ms_graph = e0.elapsed_time(e1) / steps
-    # fourth: each call after a 512 MiB scratch write, which evicts q, k, v from the 256 MB Infinity Cache (the
-    # other passes replay the same inputs, which then largely come from it); events around the call alone
-    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-    cold = []
-    for _ in range(min(steps, 20)):
-        scratch.fill_(1)
-        e0.record()
-        step()
-        e1.record()
-        torch.cuda.synchronize()
-        cold.append(e0.elapsed_time(e1))
-    del scratch
-    R.ret_chunkwise_check(ws)  # no call of the timed regions abandoned a segment-chain wait
-    cold.sort()
-    return w, ms_step, ms_clean, ms_graph, kernels, ws, cold[len(cold) // 2]
-
-
-def graph_ms(torch, fn, steps):
+def graph_ms(torch, fn, steps, reps=1):
     """Milliseconds per call of `steps` calls of fn captured into one HIP graph and replayed (HIP events on the
-    replay stream)."""
+    replay stream; the fastest of `reps` replays)."""
     fn()
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
@@ -169,11 +101,117 @@ def graph_ms(torch, fn, steps):
     g.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = None
+    for _ in range(reps):
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        best = ms if best is None else min(best, ms)
+    return best
+
+
+def kernel_times(timer, names, calls):
+    out = {}
+    for name in names:
+        tot, n = timer.query(name)
+        if n:
+            out[name] = {"avg_us": 1e3 * tot / n, "launches_per_call": n / calls}
+    return out
+
+
+def bench_chunkwise(R, W, torch, wid, steps, warmup, cold_reps=20):
+    """One chunkwise workload: warm graph replay, eager calls with per-kernel events, MALL-cold calls."""
+    w = W.WORKLOADS[wid]
+    q, k, v, _ = W.make_qkv(w)
+    dev = lambda x: torch.from_numpy(x).to(torch.bfloat16).cuda()
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    del q, k, v
+    o = torch.empty((w.B, w.N, w.H, w.dv), dtype=torch.bfloat16, device="cuda")
+    state = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    ws = R.chunkwise_workspace(qd, vd, w.chunk)
+
+    def step(options=None):
+        R.ret_chunkwise_fwd(qd, kd, vd, o, w.gamma, w.chunk, theta=w.theta, state_out=state, workspace=ws,
+                            options=options)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    # the timed region: `steps` calls replayed from a captured HIP graph (no host launch cost between them)
+    ms_graph = graph_ms(torch, step, steps, reps=3)
+    # per-kernel durations: the same calls eager, each launch bracketed by HIP events on its stream
+    timer = R.Timer()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     e0.record()
-    g.replay()
+    for _ in range(steps):
+        step({"timer": timer})
     e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+    ms_eager = e0.elapsed_time(e1) / steps
+    kernels = kernel_times(timer, CHUNK_KERNELS, steps)
+    timer.close()
+    # each call after a 512 MiB scratch write, which evicts q, k, v from the 256 MB Infinity Cache (the warm
+    # replays reuse the same inputs, which then partly come from it); events around the call alone
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    cold = []
+    for _ in range(cold_reps):
+        scratch.fill_(1)
+        e0.record()
+        step()
+        e1.record()
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    del scratch
+    R.ret_chunkwise_check(ws)  # no call of the timed regions abandoned a segment-chain wait
+    cold.sort()
+    nbytes, f_causal, f_pages = chunk_algorithmic(w)
+    tokens = w.B * w.N
+    dom = max(kernels, key=lambda n: kernels[n]["avg_us"] * kernels[n]["launches_per_call"])
+    # When a call is one kernel its duration is also the replayed graph's per-call time; otherwise its share
+    # from the per-launch events.
+    dom_us = kernels[dom]["avg_us"]
+    ms_cold = cold[len(cold) // 2]
+    res = {
+        "workload": "%s: B=%d N=%d H=%d d_k=%d d_v=%d chunk=%d, bf16 in/out, fp32 state, xPos rotation"
+                    % (w.name, w.B, w.N, w.H, w.dk, w.dv, w.chunk),
+        "ms_per_call": ms_graph,
+        "tokens_per_s": tokens / (ms_graph * 1e-3),
+        "ms_per_call_eager": ms_eager,
+        "ms_per_call_mall_cold_median": ms_cold,
+        "tokens_per_s_mall_cold": tokens / (ms_cold * 1e-3),
+        "kernels": kernels,
+        "dominant_kernel": dom,
+        "dominant_kernel_avg_us": dom_us,
+        "alg_bytes_per_call": nbytes,
+        "alg_flops_causal_per_call": f_causal,
+        "alg_flops_pages_count_per_call": f_pages,
+        "hbm_frac_whole_call": nbytes / (ms_graph * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "hbm_frac_dominant_kernel": nbytes / (dom_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        "mfma_frac_causal_whole_call": f_causal / (ms_graph * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        "mfma_frac_causal_dominant_kernel": f_causal / (dom_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS,
+        "mfma_frac_pages_count_whole_call": f_pages / (ms_graph * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        "traffic_bytes_dominant_kernel": load_traffic(dom, w.name),
+        "workspace_bytes": 0 if ws is None else ws.numel(),
+    }
+    return w, res
+
+
+def roofline_of(res, bound):
+    """The contract's roofline object for a chunkwise result: MFMA (causal-count TFLOP/s) or HBM (GB/s)."""
+    dom_us = res["dominant_kernel_avg_us"]
+    if bound == "mfma":
+        ach = res["alg_flops_causal_per_call"] / (dom_us * 1e-6) / 1e12
+        peak, unit = BF16_PEAK_TFLOPS, "TFLOP/s"
+    else:
+        ach = res["alg_bytes_per_call"] / (dom_us * 1e-6) / 1e9
+        peak, unit = HBM_PEAK_GBS, "GB/s"
+    return {"bound": bound, "achieved": ach, "peak": peak, "unit": unit, "frac": ach / peak,
+            "traffic": res["traffic_bytes_dominant_kernel"], "kernel": res["dominant_kernel"],
+            "kernel_avg_us": dom_us, "alg_bytes_per_launch": res["alg_bytes_per_call"],
+            "alg_flops_causal_per_launch": res["alg_flops_causal_per_call"]}
 
 
 def bench_epilogue(R, W, torch, wid, steps):
@@ -218,7 +256,7 @@ def bench_epilogue(R, W, torch, wid, steps):
 
 def bench_backward(R, W, torch, wid, steps):
     """Gradients dq, dk, dv of the chunkwise workload (bf16 q, k, v, dO in; bf16 gradients out), replayed from a
-    HIP graph, with the per-kernel split from the library's launch events of one eager call."""
+    HIP graph, with the per-kernel split from the launch events of eager calls."""
     import numpy as np
     w = W.WORKLOADS[wid]
     q, k, v, rng = W.make_qkv(w)
@@ -228,22 +266,16 @@ def bench_backward(R, W, torch, wid, steps):
     del q, k, v, do
     dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
     ws = R.chunkwise_bwd_workspace(qd, vd, w.chunk)
-    call = lambda: R.ret_chunkwise_bwd(qd, kd, vd, dod, dq, dk, dv, w.gamma, w.chunk, theta=w.theta, workspace=ws)
+    call = lambda options=None: R.ret_chunkwise_bwd(qd, kd, vd, dod, dq, dk, dv, w.gamma, w.chunk, theta=w.theta,
+                                                    workspace=ws, options=options)
     ms = graph_ms(torch, call, steps)
     torch.cuda.synchronize()
-    R.timing_reset()
-    R.timing_enable(True)
+    timer = R.Timer()
     for _ in range(3):
-        call()
+        call({"timer": timer})
     torch.cuda.synchronize()
-    R.timing_enable(False)
-    kernels = {}
-    for name in ("ret_rotate_qk", "ret_permute_rotate", "ret_chunk_seg", "ret_chunk_fused", "ret_chunk_local",
-                 "ret_segment_scan"):
-        tot, n = R.timing_query(name)
-        if n:
-            kernels[name] = {"avg_us": 1e3 * tot / n, "launches_per_call": n // 3}
-    R.timing_reset()
+    kernels = kernel_times(timer, ("ret_rotate_qk", "ret_permute_rotate") + CHUNK_KERNELS[1:], 3)
+    timer.close()
     R.ret_chunkwise_check(ws)
     toks = w.B * w.N * w.H
     nbytes = toks * (2 * w.dk + 2 * w.dv) * 2 + toks * (2 * w.dk + w.dv) * 2  # q, k, v, dO in; dq, dk, dv out
@@ -259,12 +291,16 @@ def bench_backward(R, W, torch, wid, steps):
         "hbm_frac_whole_call": ach / HBM_PEAK_GBS,
         "alg_bytes_per_call": nbytes,
         "tflops_causal": flops / (ms * 1e-3) / 1e12,
+        "mfma_frac_causal": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
         "kernels": kernels,
         "workspace_bytes": ws.numel(),
     }
 
 
-def bench_decode(R, W, torch, steps_graph=1024, reps=3):
+def bench_decode(R, W, torch, steps_graph=1024, reps=3, cold_states=32):
+    """Batched decode: 1024 steps of the workload's q, k, v (drawn step by step) from its prefilled state,
+    replayed from a HIP graph. Warm: one state. MALL-cold: step t updates state t % cold_states, a working set
+    of cold_states x 16 MiB, so no state is still cached when its turn comes again."""
     import numpy as np
     w = W.WORKLOADS[3]
     rng = np.random.default_rng(w.seed)
@@ -285,43 +321,27 @@ def bench_decode(R, W, torch, steps_graph=1024, reps=3):
     sqd, skd, svd = dev(sq), dev(sk), dev(sv)
     outs = torch.empty((steps_graph, w.B, w.H, w.dv), dtype=torch.bfloat16, device="cuda")
     theta = w.theta
+    states = state.unsqueeze(0).repeat(cold_states, 1, 1, 1, 1).contiguous()
 
-    def run_steps():
+    def run_steps(cold=False, options=None):
         for t in range(steps_graph):
-            R.ret_recurrent_step(sqd[t], skd[t], svd[t], outs[t], state, w.gamma, pos=w.prefill + t, theta=theta)
+            st = states[t % cold_states] if cold else state
+            R.ret_recurrent_step(sqd[t], skd[t], svd[t], outs[t], st, w.gamma, pos=w.prefill + t, theta=theta,
+                                 options=options)
 
-    # kernel durations from per-launch events (eager launches)
-    run_steps()
+    us_warm = 1e3 * graph_ms(torch, run_steps, 1, reps) / steps_graph
+    us_cold = 1e3 * graph_ms(torch, lambda: run_steps(True), 1, reps) / steps_graph
+    # kernel durations from per-launch events (eager launches), both ways
+    timer = R.Timer()
+    run_steps(False, {"timer": timer})
     torch.cuda.synchronize()
-    R.timing_reset()
-    R.timing_enable(True)
-    run_steps()
+    tot, n = timer.query("ret_recurrent_step")
+    timer.reset()
+    run_steps(True, {"timer": timer})
     torch.cuda.synchronize()
-    R.timing_enable(False)
-    tot, n = R.timing_query("ret_recurrent_step")
-    R.timing_reset()
-    kernel_us = 1e3 * tot / n
-    # steps/s from a captured graph of the whole decode loop
-    g = torch.cuda.CUDAGraph()
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        with torch.cuda.graph(g, stream=s):
-            run_steps()
-    torch.cuda.current_stream().wait_stream(s)
-    g.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    best = None
-    for _ in range(reps):
-        e0.record()
-        g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1)
-        best = ms if best is None else min(best, ms)
-    us_step = 1e3 * best / steps_graph
-    return w, us_step, kernel_us
+    tot_c, n_c = timer.query("ret_recurrent_step")
+    timer.close()
+    return w, us_warm, us_cold, 1e3 * tot / n, 1e3 * tot_c / n_c
 
 
 def _cpu_model() -> str:
@@ -335,33 +355,36 @@ def _cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(W, wid, seconds=10.0, single_seconds=4.0):
-    """The fp64 oracle's chunkwise form on this host: whole-workload runs repeated for about `seconds` with one
-    thread per (b, h) up to the oracle's default thread count, then a bounded single-thread sample (the first
-    B/8 sequences, at least one) for about `single_seconds`."""
+def cpu_baseline(W, wid, seconds=8.0, single_seconds=3.0, sample_tokens=1024):
+    """The fp64 oracle's chunkwise form on this host over a bounded sample of the workload: the first
+    `sample_tokens` tokens of every sequence and head, one thread per (b, h) up to the oracle's default thread
+    count, repeated for about `seconds`; then one (b, h) of the same sample on one thread for about
+    `single_seconds`. Scaled to tokens/s of the whole layer (all heads)."""
     import oracle
     w = W.WORKLOADS[wid]
     q, k, v, _ = W.make_qkv(w)
+    n = min(w.N, sample_tokens)
+    q, k, v = q[:, :n], k[:, :n], v[:, :n]
     threads = min(oracle.default_threads(), w.B * w.H)
 
-    def timed(qq, kk, vv, nthreads, budget):
+    def timed(qq, kk, vv, gamma, nthreads, budget):
         runs, total = 0, 0.0
         while runs == 0 or total < budget:
             t0 = time.perf_counter()
-            oracle.chunkwise(qq, kk, vv, w.gamma, w.chunk, theta=w.theta, threads=nthreads)
+            oracle.chunkwise(qq, kk, vv, gamma, w.chunk, theta=w.theta, threads=nthreads)
             total += time.perf_counter() - t0
             runs += 1
         return runs, total
 
-    runs, total = timed(q, k, v, threads, seconds)
-    b1 = max(1, w.B // 8)
-    runs1, total1 = timed(q[:b1], k[:b1], v[:b1], 1, single_seconds)
-    return {"value": runs * w.B * w.N / total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "%d runs of the whole %s workload (B=%d N=%d H=%d), fp64 chunkwise form, %.1f s in total"
-                      % (runs, w.name, w.B, w.N, w.H, total),
-            "single_thread_value": runs1 * b1 * w.N / total1,
-            "single_thread_sample": "%d runs of %d of the %d sequences on one thread, %.1f s in total"
-                                    % (runs1, b1, w.B, total1),
+    runs, total = timed(q, k, v, w.gamma, threads, seconds)
+    runs1, total1 = timed(q[:1, :, :1], k[:1, :, :1], v[:1, :, :1], w.gamma[:1], 1, single_seconds)
+    return {"value": runs * w.B * n / total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d runs of the first %d tokens of the %s workload (B=%d H=%d d_k=%d d_v=%d chunk=%d), fp64 "
+                      "chunkwise form, one thread per (b, h), %.1f s in total"
+                      % (runs, n, w.name, w.B, w.H, w.dk, w.dv, w.chunk, total),
+            "single_thread_value": runs1 * n / total1 / (w.B * w.H),
+            "single_thread_sample": "%d runs of one head over the same %d tokens on one thread, %.1f s in total; "
+                                    "scaled to tokens/s of all %d heads" % (runs1, n, total1, w.B * w.H),
             "cpu_model": _cpu_model(), "host_cpus": len(os.sched_getaffinity(0))}
 
 
@@ -379,20 +402,21 @@ def copy_calibration(torch):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="retention-layer-d512", choices=sorted(CHUNK_WORKLOADS),
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="7b-class-layer", choices=sorted(CHUNK_WORKLOADS),
                     help="chunkwise workload timed for `value`")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-epilogue", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="only the `value` workload's chunkwise call")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=1024, help="decode steps per graph (1024 in the workload)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: the library has no multi-GPU path (run with --gpus 1)",
-              file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path, and nothing here launches work "
+              "on a second GPU (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -407,73 +431,82 @@ def main():
         copy_calibration(torch)
         return
 
+    def progress(msg):
+        print("[bench] %s" % msg, file=sys.stderr, flush=True)
+
     wid = CHUNK_WORKLOADS[args.workload]
-    w, ms_step, ms_clean, ms_graph, kernels, ws, ms_cold = bench_chunkwise(R, W, torch, wid, args.steps,
-                                                                         args.warmup)
-    nbytes, f_causal, f_pages = chunk_algorithmic(w)
+    progress("chunkwise %s" % args.workload)
+    w, main_res = bench_chunkwise(R, W, torch, wid, args.steps, args.warmup)
+    bound = "mfma" if w.dk >= 256 else "hbm"  # the d_k 256 layer sits at the ridge; the others are HBM-bound
     tokens = w.B * w.N
-    dom = max(kernels, key=lambda n: kernels[n]["avg_us"] * kernels[n]["launches"])
-    # The dominant kernel's duration: when a call is that one kernel, the per-call time of the replayed graph
-    # (HIP events on the replay stream; it includes the gap between back-to-back kernels, so it errs slow).
-    # Otherwise its share from the per-launch events of the eager pass.
-    dom_us = 1e3 * ms_graph if len(kernels) == 1 else kernels[dom]["avg_us"]
-    achieved = nbytes / (dom_us * 1e-6) / 1e9
-    traffic = load_traffic(dom, w.name)
     result = {
         "metric": METRIC,
-        "value": tokens / (ms_graph * 1e-3),
+        "value": main_res["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_graph,
+        "ms_per_step": main_res["ms_per_call"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "%s: B=%d N=%d H=%d d_k=%d d_v=%d chunk=%d, bf16 in/out, fp32 state, xPos rotation"
-                               % (w.name, w.B, w.N, w.H, w.dk, w.dv, w.chunk),
-                   "global_batch": w.B, "seq_len": w.N},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": dom,
-                     "kernel_avg_us": dom_us, "alg_bytes_per_launch": nbytes},
-        "chunkwise": {
-            "ms_per_step_eager": ms_clean,
-            "ms_per_call_mall_cold_median": ms_cold,
-            "tokens_per_s_mall_cold": tokens / (ms_cold * 1e-3),
-            "ms_per_step_with_kernel_events": ms_step,
-            "kernels": kernels,
-            "step_hbm_frac": nbytes / (ms_graph * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "tflops_causal": f_causal / (ms_graph * 1e-3) / 1e12,
-            "tflops_pages_count": f_pages / (ms_graph * 1e-3) / 1e12,
-            "mfma_frac_causal": f_causal / (ms_graph * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-            "workspace_bytes": 0 if ws is None else ws.numel(),
-        },
+        "config": {"workload": main_res["workload"], "global_batch": w.B, "seq_len": w.N},
+        "roofline": roofline_of(main_res, bound),
+        "chunkwise": main_res,
     }
+    result["roofline"]["hbm_frac"] = main_res["hbm_frac_dominant_kernel"]
+    if not args.no_extra:
+        for name, key in sorted(CHUNK_WORKLOADS.items(), key=lambda kv: kv[1]):
+            if key == wid:
+                continue
+            progress("chunkwise %s" % name)
+            wx, res = bench_chunkwise(R, W, torch, key, args.steps, args.warmup)
+            res["roofline"] = roofline_of(res, "mfma" if wx.dk >= 256 else "hbm")
+            result[name] = res
     if not args.no_decode:
-        dw, us_step, kernel_us_eager = bench_decode(R, W, torch, steps_graph=args.decode_steps)
+        progress("decode")
+        dw, us_warm, us_cold, k_warm, k_cold = bench_decode(R, W, torch, steps_graph=args.decode_steps)
         db, dflops = decode_algorithmic(dw.B, dw.H, dw.dk, dw.dv)
-        kernel_us = us_step  # one kernel per step: the graph's per-step time (events on the replay stream)
-        ach = db / (kernel_us * 1e-6) / 1e9
+        ach_c, ach_w = db / (us_cold * 1e-6) / 1e9, db / (us_warm * 1e-6) / 1e9
         result["decode"] = {
             "workload": "%s: B=%d H=%d d_k=%d d_v=%d, fp32 state, bf16 q/k/v/o, %d steps from a %d-token prefill, "
-                        "HIP graph" % (dw.name, dw.B, dw.H, dw.dk, dw.dv, dw.steps, dw.prefill),
-            "steps_per_s": 1e6 / us_step, "tokens_per_s": dw.B * 1e6 / us_step, "us_per_step": us_step,
-            "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": ach / HBM_PEAK_GBS, "traffic": load_traffic("ret_recurrent_step", dw.name),
-                         "kernel": "ret_recurrent_step", "kernel_avg_us": kernel_us, "alg_bytes_per_launch": db},
-            "step_hbm_frac": db / (us_step * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                        "HIP graph" % (dw.name, dw.B, dw.H, dw.dk, dw.dv, args.decode_steps, dw.prefill),
+            "steps_per_s": 1e6 / us_cold, "tokens_per_s": dw.B * 1e6 / us_cold, "us_per_step": us_cold,
+            # one kernel per step: the graph's per-step time (events on the replay stream)
+            "roofline": {"bound": "hbm", "achieved": ach_c, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": ach_c / HBM_PEAK_GBS,
+                         "traffic": load_traffic("ret_recurrent_step", dw.name + " mall-cold"),
+                         "kernel": "ret_recurrent_step", "kernel_avg_us": us_cold, "alg_bytes_per_launch": db,
+                         "state": "MALL-cold: the steps cycle through 32 distinct 16 MiB states (512 MiB)"},
+            "warm": {"us_per_step": us_warm, "steps_per_s": 1e6 / us_warm,
+                     "roofline": {"bound": "hbm", "achieved": ach_w, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": ach_w / HBM_PEAK_GBS,
+                                  "traffic": load_traffic("ret_recurrent_step", dw.name),
+                                  "kernel": "ret_recurrent_step", "kernel_avg_us": us_warm,
+                                  "alg_bytes_per_launch": db,
+                                  "state": "warm: one 16 MiB state, held by the Infinity Cache between steps"}},
+            "kernel_avg_us_eager": {"warm": k_warm, "mall_cold": k_cold},
         }
     if not args.no_epilogue:
-        result["epilogue"] = bench_epilogue(R, W, torch, wid, args.steps)
-    bw = W.WORKLOADS[wid]
-    if not args.no_backward and R.load().ret_chunkwise_bwd_workspace_bytes(bw.B, bw.N, bw.H, bw.dk, bw.dv, bw.chunk,
-                                                                            R.RET_BF16):
-        result["backward"] = bench_backward(R, W, torch, wid, args.steps)
-    elif not args.no_backward:
-        result["backward"] = {"workload": bw.name, "skipped": "gradients need d_k, d_v in {64, 128, 256}"}
+        progress("epilogue")
+        result["epilogue"] = bench_epilogue(R, W, torch, CHUNK_WORKLOADS["retention-layer-d512"], args.steps)
+    if not args.no_backward:
+        result["backward"] = {}
+        for name, key in sorted(CHUNK_WORKLOADS.items(), key=lambda kv: kv[1]):
+            if args.no_extra and key != wid:
+                continue
+            bw = W.WORKLOADS[key]
+            if R.load().ret_chunkwise_bwd_workspace_bytes(bw.B, bw.N, bw.H, bw.dk, bw.dv, bw.chunk, R.RET_BF16):
+                progress("backward %s" % name)
+                bres = bench_backward(R, W, torch, key, max(3, args.steps // 4))
+                fwd = result["chunkwise"] if key == wid else result.get(name)
+                if fwd:
+                    bres["x_forward"] = bres["us_per_call"] / (1e3 * fwd["ms_per_call"])
+                result["backward"][name] = bres
     if not args.no_cpu_baseline:
+        progress("cpu baseline")
         result["cpu_baseline"] = cpu_baseline(W, wid)
     result["context"] = ("pages' figures (whole 6.7B model, A100-80GB, vanilla PyTorch): 8.4x faster decoding and "
                          "70% less memory than a KV-cached Transformer at 8k; not comparable to this kernel metric")

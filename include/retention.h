@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define RET_ABI_VERSION 5
+#define RET_ABI_VERSION 6
 
 typedef enum { RET_F32 = 0, RET_BF16 = 1 } ret_dtype_t;
 
@@ -57,6 +57,9 @@ typedef enum {
 
 /* ABI version of the loaded library (RET_ABI_VERSION at build time). */
 int ret_abi_version(void);
+
+/* Digest of the sources the library was built from (for detecting a stale build). */
+const char* ret_source_digest(void);
 
 /* Static text for a status code. */
 const char* ret_status_string(int status);
@@ -93,8 +96,11 @@ size_t ret_chunkwise_workspace_bytes(int B, int N, int H, int dk, int dv, int ch
 
 /*
  * Synchronises `stream` and reports whether any call that used this workspace had to abandon a wait for
- * the state of an earlier segment (a sticky flag in the workspace; the outputs of such a call are wrong).
- * RET_OK if not (or workspace is NULL), RET_ERR_HIP with detail otherwise.
+ * the state of an earlier segment (a sticky flag in the workspace). A wait gives up after about 0.17 s without
+ * any progress of the segments it waits for (a flag rising resets the limit); the segment that gave up then
+ * takes NaN for its entering state, so its outputs, and whatever is computed from its state (the final state,
+ * later segments' entering states where its state enters them), come out NaN rather than silently wrong. RET_OK if no wait gave up (or workspace is NULL), RET_ERR_HIP with detail
+ * otherwise.
  */
 ret_status_t ret_chunkwise_check(const void* workspace, void* stream);
 
@@ -207,17 +213,82 @@ ret_status_t ret_chunkwise_bwd(const void* q, const void* k, const void* v, cons
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Kernel timing for measurement tools. While enabled, every kernel the library launches is bracketed by a
- * pair of HIP events on the launch stream. ret_timing_query synchronises those events and returns the total
- * milliseconds and launch count recorded for kernels whose name equals `kernel` ("" or NULL = all).
- * ret_timing_reset drops the records. Kernel names: "ret_chunk_seg", "ret_chunk_fused" and "ret_rotate_qk"
- * (bf16 input), "ret_chunk_full", "ret_chunk_local", "ret_segment_scan" (fp32 input), "ret_parallel",
- * "ret_recurrent_step", "ret_msr_epilogue", "ret_permute_rotate" (gradients). Not for use while kernels are
- * being captured into a graph.
+ * Kernel launch records for measurement tools: a caller-owned object, passed in ret_options_t.timer. While a
+ * call holds one, every kernel it launches is bracketed by a pair of HIP events on the launch stream and
+ * recorded in it (the library keeps no timing state of its own). ret_timer_query synchronises those events and
+ * returns the total milliseconds and launch count recorded for kernels whose name equals `kernel` ("" or NULL =
+ * all). Kernel names: "ret_chunk_seg", "ret_chunk_fused" and "ret_rotate_qk" (bf16 input), "ret_chunk_full",
+ * "ret_chunk_local", "ret_segment_scan" (fp32 input), "ret_parallel", "ret_recurrent_step", "ret_msr_epilogue",
+ * "ret_permute_rotate" (gradients), "ret_norm_rows" (score normalization). A timer must not be attached to
+ * calls that are being captured into a graph. One timer may be shared by calls on several threads.
  */
-int ret_timing_enable(int on);
-int ret_timing_query(const char* kernel, double* total_ms, int64_t* launches);
-void ret_timing_reset(void);
+typedef struct ret_timer ret_timer_t;
+ret_timer_t* ret_timer_create(void);   /* NULL if out of host memory */
+void ret_timer_destroy(ret_timer_t* t);
+int ret_timer_query(ret_timer_t* t, const char* kernel, double* total_ms, int64_t* launches);
+void ret_timer_reset(ret_timer_t* t);
+
+/*
+ * Options of the *_ex entry points: the plan the library would otherwise choose, for measurements and for
+ * tests that compare kernels and plans (every choice gives the result of the default plan up to rounding
+ * order), and an optional timer. NULL options, or ret_options_default(), mean the library's own plan.
+ *   segments     > 0: segments per sequence of the chained chunkwise kernels (capped at one per chunk); 0: planner
+ *   target_wgs   > 0: workgroups the segment planner aims for; 0: the kernel's default
+ *   prerotate    -1: planner; 0: q and k rotated while staging; 1: rotated once up front into the workspace
+ *   onchip       -1 or 1: the on-chip segment kernel where segments fit (d_k <= 64, <= 256 tokens); 0: never
+ *   variant      0: default kernel of the shape; d_k = 256 with d_v a multiple of 128: 1 = 256 threads whose
+ *                waves own 32 columns, 2 = 256 threads with d_v tiles of 64
+ *   step_cw, step_wr, step_pairs   decode tile: columns per workgroup (16, 32, 64), rows per wave (16, 32, 64),
+ *                pairs (0 planner, 1 one (b, h) per workgroup, 2 grouped); 0 = default
+ *   bwd_direct   -1 or 1: gradients by the reversed traversal where available; 0: through reordered copies
+ *   chain_spin   segment-chain wait limit in device clock ticks (100 MHz) without progress before a wait gives
+ *                up; 0 = default (2^24 ticks, ~0.17 s); negative: every wait gives up at once (for testing the
+ *                give-up path: the affected outputs become NaN and ret_chunkwise_check reports it)
+ *   timer        launch records, or NULL
+ */
+typedef struct {
+    int segments;
+    int target_wgs;
+    int prerotate;
+    int onchip;
+    int variant;
+    int step_cw, step_wr, step_pairs;
+    int bwd_direct;
+    long long chain_spin;
+    ret_timer_t* timer;
+} ret_options_t;
+void ret_options_default(ret_options_t* o);
+
+/* ret_chunkwise_workspace_bytes, ret_chunkwise_bwd_workspace_bytes, ret_chunkwise_fwd, ret_chunkwise_msr_fwd,
+ * ret_chunkwise_bwd, ret_recurrent_step and ret_recurrent_step_positions with options (NULL = defaults);
+ * otherwise identical. A call planned with options wants the workspace its _ex query returns for them. */
+size_t ret_chunkwise_workspace_bytes_ex(int B, int N, int H, int dk, int dv, int chunk, ret_dtype_t in_dt,
+                                        const ret_options_t* opts);
+size_t ret_chunkwise_bwd_workspace_bytes_ex(int B, int N, int H, int dk, int dv, int chunk, ret_dtype_t in_dt,
+                                            const ret_options_t* opts);
+ret_status_t ret_chunkwise_fwd_ex(const void* q, const void* k, const void* v, void* o, int B, int N, int H, int dk,
+                                  int dv, ret_dtype_t in_dt, ret_dtype_t out_dt, const float* gamma,
+                                  const double* theta, int64_t pos0, int chunk, const float* state_in,
+                                  float* state_out, void* workspace, size_t workspace_bytes, void* stream,
+                                  const ret_options_t* opts);
+ret_status_t ret_chunkwise_msr_fwd_ex(const void* q, const void* k, const void* v, const void* gate, void* y, int B,
+                                      int N, int H, int dk, int dv, ret_dtype_t in_dt, ret_dtype_t out_dt,
+                                      ret_dtype_t gate_dt, const float* gamma, const double* theta, int64_t pos0,
+                                      int chunk, const float* state_in, float* state_out, const float* gn_weight,
+                                      const float* gn_bias, float eps, void* workspace, size_t workspace_bytes,
+                                      void* stream, const ret_options_t* opts);
+ret_status_t ret_chunkwise_bwd_ex(const void* q, const void* k, const void* v, const void* dout, void* dq,
+                                  void* dk_out, void* dv_out, int B, int N, int H, int dk, int dv, ret_dtype_t in_dt,
+                                  ret_dtype_t out_dt, const float* gamma, const double* theta, int64_t pos0,
+                                  int chunk, void* workspace, size_t workspace_bytes, void* stream,
+                                  const ret_options_t* opts);
+ret_status_t ret_recurrent_step_ex(const void* q, const void* k, const void* v, void* o, float* state, int B, int H,
+                                   int dk, int dv, ret_dtype_t in_dt, ret_dtype_t out_dt, const float* gamma,
+                                   const double* theta, int64_t pos, void* stream, const ret_options_t* opts);
+ret_status_t ret_recurrent_step_positions_ex(const void* q, const void* k, const void* v, void* o, float* state,
+                                             int B, int H, int dk, int dv, ret_dtype_t in_dt, ret_dtype_t out_dt,
+                                             const float* gamma, const double* theta, const int64_t* pos,
+                                             void* stream, const ret_options_t* opts);
 
 #ifdef __cplusplus
 }

@@ -3,6 +3,7 @@ parallel, then linked into a shared library next to this file."""
 from __future__ import annotations
 
 import glob
+import hashlib
 import os
 import subprocess
 import sys
@@ -37,9 +38,21 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
+def source_digest() -> str:
+    """Digest of every source the library is built from (kernels, host code, the public header). The library
+    carries the digest of the sources it was built from (ret_source_digest), so a stale build is detected."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.h")) +
+                   glob.glob(os.path.join(ROOT, "include", "*.h")))
+    for f in files:
+        with open(f, "rb") as fh:
+            h.update(os.path.relpath(f, ROOT).encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
 def build(verbose: bool = False, jobs: int | None = None) -> str:
     os.makedirs(OBJ_DIR, exist_ok=True)
-    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC, '-DRET_SOURCE_DIGEST="%s"' % source_digest()]
     objs, cmds = [], []
     for src in sources():
         obj = os.path.join(OBJ_DIR, os.path.basename(src)[:-4] + ".o")

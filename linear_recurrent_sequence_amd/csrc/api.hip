@@ -10,6 +10,7 @@
 #include <string.h>
 
 #include <mutex>
+#include <new>
 #include <string>
 #include <vector>
 
@@ -36,35 +37,67 @@ ret_status_t fail(ret_status_t st, const char* fmt, ...) {
     return st;
 }
 
-// ---- timing records ----
-struct TimingRec {
-    const char* name;
-    hipEvent_t start, stop;
+}  // namespace
+
+// ---- launch records: a caller-owned object (ret_options_t.timer); the library keeps none of its own ----
+struct ret_timer {
+    struct Rec {
+        const char* name;
+        hipEvent_t start, stop;
+    };
+    std::mutex mu;
+    std::vector<Rec> recs;
 };
-std::mutex g_timing_mu;
-bool g_timing_on = false;
-std::vector<TimingRec> g_timing;
+
+namespace {
+
+// The plan options with the library's defaults filled in (ret_options_t documents each field).
+struct Opts {
+    int segments = 0, target_wgs = 0, prerotate = -1, onchip = 1, variant = 0;
+    int step_cw = 0, step_wr = 0, step_pairs = 0, bwd_direct = 1;
+    long long chain_spin = 0;
+    ret_timer_t* timer = nullptr;
+};
+Opts resolve(const ret_options_t* o) {
+    Opts r;
+    if (!o) return r;
+    r.segments = o->segments > 0 ? o->segments : 0;
+    r.target_wgs = o->target_wgs > 0 ? o->target_wgs : 0;
+    r.prerotate = o->prerotate < 0 ? -1 : (o->prerotate != 0);
+    r.onchip = o->onchip != 0;
+    r.variant = o->variant;
+    r.step_cw = o->step_cw;
+    r.step_wr = o->step_wr;
+    r.step_pairs = o->step_pairs;
+    r.bwd_direct = o->bwd_direct != 0;
+    r.chain_spin = o->chain_spin;
+    r.timer = o->timer;
+    return r;
+}
+const Opts kDefaultOpts;
+
+// Kernel-argument form of the chain's wait limit: ticks, or -1 (every wait gives up at once).
+long long chain_spin_arg(const Opts& op) {
+    if (op.chain_spin < 0) return -1;
+    return op.chain_spin > 0 ? op.chain_spin : (1ll << 24);
+}
 
 struct LaunchTimer {
     hipEvent_t start = nullptr, stop = nullptr;
     hipStream_t stream;
     const char* name;
-    bool on;
-    LaunchTimer(const char* n, hipStream_t s) : stream(s), name(n) {
-        {
-            std::lock_guard<std::mutex> lk(g_timing_mu);
-            on = g_timing_on;
-        }
-        if (on && hipEventCreate(&start) == hipSuccess && hipEventCreate(&stop) == hipSuccess)
+    ret_timer_t* t;
+    LaunchTimer(const char* n, hipStream_t s, const Opts& op) : stream(s), name(n), t(op.timer) {
+        if (t && hipEventCreate(&start) == hipSuccess && hipEventCreate(&stop) == hipSuccess)
             (void)hipEventRecord(start, stream);
         else
-            on = false;
+            t = nullptr;
     }
     void done() {
-        if (!on) return;
+        if (!t) return;
         (void)hipEventRecord(stop, stream);
-        std::lock_guard<std::mutex> lk(g_timing_mu);
-        g_timing.push_back({name, start, stop});
+        std::lock_guard<std::mutex> lk(t->mu);
+        t->recs.push_back({name, start, stop});
     }
 };
 
@@ -124,11 +157,11 @@ void fill_fwd(FwdArgs& A, const void* q, const void* k, const void* v, void* o, 
 }
 
 // ---- kernel selection ----
-bool pick_chunk(ret_dtype_t in_dt, int dk, int dv, int C, ChunkKernels* out) {
+bool pick_chunk(ret_dtype_t in_dt, int dk, int dv, int C, ChunkKernels* out, const Opts& op = kDefaultOpts) {
     if (in_dt == RET_F32) return chunk_kernels_f32(dk, dv, C, out);
     if (dk == 32 || dk == 64) return chunk_kernels_bf16_small(dk, dv, C, out);
     if (dk == 128) return chunk_kernels_bf16_128(dk, dv, C, out);
-    if (dk == 256) return chunk_kernels_bf16_256(dk, dv, C, out);
+    if (dk == 256) return chunk_kernels_bf16_256(dk, dv, C, op.variant, out);
     return false;
 }
 
@@ -137,20 +170,15 @@ bool pick_parallel(ret_dtype_t in_dt, int dk, int dv, ParKernel* out) {
 }
 
 // ---- segment heuristic ----
-int env_int(const char* name, int dflt) {
-    const char* s = getenv(name);
-    if (!s || !*s) return dflt;
-    return atoi(s);
-}
-
 // Number of segments per sequence and tokens per segment. Enough workgroups to fill the chip, but segments of
 // at least ~256 tokens so the per-segment state traffic stays small against the segment's own data.
-void plan_segments(int B, int N, int H, int dv, int C, int dvt, int target_wgs, int* nseg, int* seg_len) {
+void plan_segments(int B, int N, int H, int dv, int C, int dvt, int target_wgs, const Opts& op, int* nseg,
+                   int* seg_len) {
     const long long units = (long long)B * H * ((dv + dvt - 1) / dvt);
     const int nchunks = (N + C - 1) / C;
-    const int target = env_int("RET_TARGET_WGS", target_wgs > 0 ? target_wgs : 1024);
+    const int target = op.target_wgs > 0 ? op.target_wgs : target_wgs > 0 ? target_wgs : 1024;
     int g = (int)((target + units - 1) / units);
-    const int forced = env_int("RET_SEGMENTS", 0);
+    const int forced = op.segments;
     if (forced > 0) g = forced;
     if (g < 1) g = 1;
     if (g > nchunks) g = nchunks;
@@ -179,13 +207,13 @@ struct ChunkPlan {
     size_t chain_bytes, rot_bytes;
 };
 ChunkPlan plan_chunk(const ChunkKernels& ck, int B, int N, int H, int dk, int dv, int chunk, bool rotate,
-                     size_t avail) {
+                     size_t avail, const Opts& op = kDefaultOpts) {
     ChunkPlan p;
-    plan_segments(B, N, H, dv, chunk, ck.dvt, ck.target_wgs, &p.nseg, &p.seg_len);
+    plan_segments(B, N, H, dv, chunk, ck.dvt, ck.target_wgs, op, &p.nseg, &p.seg_len);
     p.chain_bytes = (segment_ws_bytes(ck, B, H, dk, dv, p.nseg) + 255) / 256 * 256;
     p.rot_bytes = 0;
-    // RET_PREROTATE=0 / 1 turns the up-front rotation off / on wherever a kernel supports it.
-    const int pre = env_int("RET_PREROTATE", -1);
+    // prerotate 0 / 1 turns the up-front rotation off / on wherever a kernel supports it.
+    const int pre = op.prerotate;
     if (ck.fused_pre && rotate && (pre < 0 ? dv / ck.dvt >= 4 : pre != 0))
         p.rot_bytes = 2 * (((size_t)B * N * H * dk * 2 + 255) / 256 * 256);
     if (p.chain_bytes + p.rot_bytes > avail) p.rot_bytes = 0;
@@ -204,10 +232,10 @@ ChunkPlan plan_chunk(const ChunkKernels& ck, int B, int N, int H, int dk, int dv
     return p;
 }
 
-// Whether a plan runs the on-chip segment kernel: chained segments short enough to stay on chip
-// (RET_SEG_ONCHIP=0 turns it off).
-bool plan_onchip(const ChunkKernels& ck, const ChunkPlan& p) {
-    return ck.fused && p.nseg > 1 && ck.seg && p.seg_len <= ck.seg_tokens && env_int("RET_SEG_ONCHIP", 1) != 0;
+// Whether a plan runs the on-chip segment kernel: chained segments short enough to stay on chip (onchip = 0
+// turns it off).
+bool plan_onchip(const ChunkKernels& ck, const ChunkPlan& p, const Opts& op = kDefaultOpts) {
+    return ck.fused && p.nseg > 1 && ck.seg && p.seg_len <= ck.seg_tokens && op.onchip != 0;
 }
 
 }  // namespace
@@ -218,6 +246,11 @@ bool plan_onchip(const ChunkKernels& ck, const ChunkPlan& p) {
 extern "C" {
 
 int ret_abi_version(void) { return RET_ABI_VERSION; }
+
+#ifndef RET_SOURCE_DIGEST
+#define RET_SOURCE_DIGEST "unknown"
+#endif
+const char* ret_source_digest(void) { return RET_SOURCE_DIGEST; }
 
 const char* ret_status_string(int status) {
     switch (status) {
@@ -245,23 +278,70 @@ ret_status_t ret_parallel_fwd(const void* q, const void* k, const void* v, void*
     fill_fwd(A, q, k, v, o, B, N, H, dk, dv, out_dt, gamma, theta, pos0);
     hipStream_t s = (hipStream_t)stream;
     dim3 grid((N + pk.bq - 1) / pk.bq, dv / pk.dvt, B * H);
-    LaunchTimer tm("ret_parallel", s);
+    LaunchTimer tm("ret_parallel", s, kDefaultOpts);
     hipLaunchKernelGGL(pk.fn, grid, dim3(kThreads), 0, s, A);
     tm.done();
     return launch_status("ret_parallel");
 }
 
-size_t ret_chunkwise_workspace_bytes(int B, int N, int H, int dk, int dv, int chunk, ret_dtype_t in_dt) {
+size_t ret_chunkwise_workspace_bytes_ex(int B, int N, int H, int dk, int dv, int chunk, ret_dtype_t in_dt,
+                                        const ret_options_t* opts) {
+    const Opts op = resolve(opts);
     ChunkKernels ck;
     if (B <= 0 || N <= 0 || H <= 0 || dk <= 0 || dv <= 0 || chunk <= 0) return 0;
-    if (!pick_chunk(in_dt, dk, dv, chunk, &ck)) return 0;
-    const ChunkPlan p = plan_chunk(ck, B, N, H, dk, dv, chunk, true, SIZE_MAX);
+    if (!pick_chunk(in_dt, dk, dv, chunk, &ck, op)) return 0;
+    const ChunkPlan p = plan_chunk(ck, B, N, H, dk, dv, chunk, true, SIZE_MAX, op);
     return p.chain_bytes + p.rot_bytes;
+}
+
+size_t ret_chunkwise_workspace_bytes(int B, int N, int H, int dk, int dv, int chunk, ret_dtype_t in_dt) {
+    return ret_chunkwise_workspace_bytes_ex(B, N, H, dk, dv, chunk, in_dt, nullptr);
 }
 
 }  // extern "C"
 
 namespace {
+
+// ret_msr_epilogue's work.
+ret_status_t epilogue_run(const void* o, const void* gate, const float* gn_weight, const float* gn_bias, void* y,
+                          int64_t rows, int H, int dv, ret_dtype_t o_dt, ret_dtype_t gate_dt, ret_dtype_t y_dt,
+                          float eps, void* stream, const Opts& op) {
+    if (!o || !y) return fail(RET_ERR_INVALID_ARG, "null o/y pointer");
+    if (rows < 0 || H <= 0 || dv <= 0)
+        return fail(RET_ERR_INVALID_ARG, "sizes must be positive (rows=%lld H=%d dv=%d)", (long long)rows, H, dv);
+    for (ret_dtype_t t : {o_dt, gate_dt, y_dt})
+        if (t != RET_F32 && t != RET_BF16) return fail(RET_ERR_INVALID_ARG, "bad dtype %d", (int)t);
+    if (!(eps >= 0.f) || !isfinite(eps)) return fail(RET_ERR_INVALID_ARG, "eps=%g must be finite and >= 0", eps);
+    if (!aligned16(o) || !aligned16(y) || (gate && !aligned16(gate)) || (gn_weight && !aligned16(gn_weight)) ||
+        (gn_bias && !aligned16(gn_bias)))
+        return fail(RET_ERR_INVALID_ARG, "o/gate/y/gn_weight/gn_bias must be 16-byte aligned");
+    int gpw = 0;
+    const epi_kernel_t fn = epilogue_kernel_get(dv, &gpw);
+    if (!fn) return fail(RET_ERR_UNSUPPORTED, "epilogue: d_v=%d not in {16,32,64,128,256,512}", dv);
+    const long long groups = (long long)rows * H;
+    if (groups == 0) return RET_OK;
+    if (groups > 0x7fffffffLL)
+        return fail(RET_ERR_UNSUPPORTED, "epilogue: %lld rows x %d heads exceed 2^31 groups", (long long)rows, H);
+    const long long wgs = (groups + gpw - 1) / gpw;
+    EpiArgs A;
+    A.o = o;
+    A.gate = gate;
+    A.weight = gn_weight;
+    A.bias = gn_bias;
+    A.y = y;
+    A.groups = groups;
+    A.H = H;
+    A.dv = dv;
+    A.o_bf16 = o_dt == RET_BF16;
+    A.gate_bf16 = gate_dt == RET_BF16;
+    A.y_bf16 = y_dt == RET_BF16;
+    A.eps = eps;
+    hipStream_t s = (hipStream_t)stream;
+    LaunchTimer tm("ret_msr_epilogue", s, op);
+    hipLaunchKernelGGL(fn, dim3((unsigned)wgs), dim3(256), 0, s, A);
+    tm.done();
+    return launch_status("ret_msr_epilogue");
+}
 
 // The epilogue a chunkwise call may fuse into its output stores.
 struct EpiRequest {
@@ -277,7 +357,7 @@ ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o,
                            int dv, ret_dtype_t in_dt, ret_dtype_t out_dt, const float* gamma, const double* theta,
                            int64_t pos0, int chunk, const float* state_in, float* state_out, void* workspace,
                            size_t workspace_bytes, void* stream, const EpiRequest* epi, bool* fused,
-                           bool rev = false, const double* out_theta = nullptr) {
+                           const Opts& op, bool rev = false, const double* out_theta = nullptr) {
     if (fused) *fused = false;
     ret_status_t st = check_common(q, k, v, o, B, N, H, dk, dv, in_dt, out_dt, gamma, theta);
     if (st != RET_OK) return st;
@@ -287,7 +367,7 @@ ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o,
     if (workspace_bytes > 0 && !workspace) return fail(RET_ERR_WORKSPACE, "workspace_bytes > 0 with a null workspace");
     if (workspace && !aligned16(workspace)) return fail(RET_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
     ChunkKernels ck;
-    if (!pick_chunk(in_dt, dk, dv, chunk, &ck))
+    if (!pick_chunk(in_dt, dk, dv, chunk, &ck, op))
         return fail(RET_ERR_UNSUPPORTED, "chunkwise form: unsupported d_k=%d d_v=%d chunk=%d for %s input", dk, dv,
                     chunk, in_dt == RET_F32 ? "F32" : "BF16");
     if (rev && !ck.fused) return fail(RET_ERR_UNSUPPORTED, "reversed chunkwise run: not available for this shape");
@@ -295,7 +375,7 @@ ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o,
     if ((long long)chunk * H * (dk > dv ? dk : dv) * 4 >= (1LL << 31))
         return fail(RET_ERR_UNSUPPORTED, "chunkwise form: chunk*H*max(d_k,d_v) too large (%d*%d*%d)", chunk, H,
                     dk > dv ? dk : dv);
-    const ChunkPlan plan = plan_chunk(ck, B, N, H, dk, dv, chunk, theta != nullptr, workspace_bytes);
+    const ChunkPlan plan = plan_chunk(ck, B, N, H, dk, dv, chunk, theta != nullptr, workspace_bytes, op);
     const int nseg = plan.nseg, seg_len = plan.seg_len;
 
     FwdArgs A;
@@ -306,11 +386,12 @@ ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o,
     A.ws = ck.fused || !workspace ? (float*)workspace : (float*)((char*)workspace + sizeof(ChainHeader));
     A.nseg = nseg;
     A.seg_len = seg_len;
+    A.chain_spin = chain_spin_arg(op);
     hipStream_t s = (hipStream_t)stream;
     const int ntiles = dv / ck.dvt;
     if (ck.fused) {
         // Segments short enough to stay on chip take the on-chip variant.
-        const bool onchip = plan_onchip(ck, plan);
+        const bool onchip = plan_onchip(ck, plan, op);
         // Staging copies rows instead of rotating them when there is no rotation, or when q and k are rotated
         // once up front (several d_v tiles stage the same rows).
         fwd_kernel_t fn = onchip ? ck.seg : ck.fused;
@@ -332,7 +413,7 @@ ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o,
             fn = fn_pre;
             A.qr = (char*)workspace + plan.chain_bytes;
             A.kr = (char*)A.qr + plan.rot_bytes / 2;
-            LaunchTimer tr("ret_rotate_qk", s);
+            LaunchTimer tr("ret_rotate_qk", s, op);
             hipLaunchKernelGGL(rotate_qk_get(), dim3(rotate_qk_blocks(B, N, H, dk)), dim3(256), 0, s, A);
             tr.done();
             if ((st = launch_status("ret_rotate_qk")) != RET_OK) return st;
@@ -348,28 +429,28 @@ ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o,
             A.eps = epi->eps;
             if (fused) *fused = true;
         }
-        LaunchTimer tm(name, s);
+        LaunchTimer tm(name, s, op);
         hipLaunchKernelGGL(fn, dim3(grid), dim3(threads), 0, s, A);
         tm.done();
         return launch_status(name);
     }
     if (nseg > 1) {
         {
-            LaunchTimer tm("ret_chunk_local", s);
+            LaunchTimer tm("ret_chunk_local", s, op);
             hipLaunchKernelGGL(ck.local, dim3(nseg - 1, ntiles, B * H), dim3(kThreads), 0, s, A);
             tm.done();
             if ((st = launch_status("ret_chunk_local")) != RET_OK) return st;
         }
         {
             const long long per4 = (long long)dk * dv / 4;
-            LaunchTimer tm("ret_segment_scan", s);
+            LaunchTimer tm("ret_segment_scan", s, op);
             hipLaunchKernelGGL(segment_scan_get(), dim3((unsigned)((per4 + kThreads - 1) / kThreads), B * H),
                                dim3(kThreads), 0, s, A);
             tm.done();
             if ((st = launch_status("ret_segment_scan")) != RET_OK) return st;
         }
     }
-    LaunchTimer tm("ret_chunk_full", s);
+    LaunchTimer tm("ret_chunk_full", s, op);
     hipLaunchKernelGGL(ck.full, dim3(nseg, ntiles, B * H), dim3(kThreads), 0, s, A);
     tm.done();
     return launch_status("ret_chunk_full");
@@ -386,25 +467,26 @@ struct BwdLayout {
     size_t qp, kp, kr, qr, vr, dor, g1, g2, g3, chain, chain_bytes, total;
     size_t vbn[2], dobn[2], vbr[2], dobr[2], g1b[2], g3b[2];  // per block (nb = 2)
 };
-bool bwd_layout(int B, int N, int H, int dk, int dv, int chunk, ret_dtype_t in_dt, bool rotate, BwdLayout* L) {
+bool bwd_layout(int B, int N, int H, int dk, int dv, int chunk, ret_dtype_t in_dt, bool rotate, BwdLayout* L,
+                const Opts& op = kDefaultOpts) {
     ChunkKernels ca, cb;
     memset(L, 0, sizeof(*L));
     L->nb = 1;
     L->wb = dv;
-    if (!pick_chunk(in_dt, dv, dk, chunk, &ca)) {
+    if (!pick_chunk(in_dt, dv, dk, chunk, &ca, op)) {
         // d_v too wide to be the contraction width of a retention: two halves, each a retention of its own
-        if (dv % 2 || (dv / 2) % 16 || !pick_chunk(in_dt, dv / 2, dk, chunk, &ca)) return false;
+        if (dv % 2 || (dv / 2) % 16 || !pick_chunk(in_dt, dv / 2, dk, chunk, &ca, op)) return false;
         L->nb = 2;
         L->wb = dv / 2;
     }
-    if (!pick_chunk(in_dt, dk, dv, chunk, &cb)) return false;
+    if (!pick_chunk(in_dt, dk, dv, chunk, &cb, op)) return false;
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     const size_t nk = (size_t)B * N * H * dk, nv = (size_t)B * N * H * dv, es = in_dt == RET_BF16 ? 2 : 4;
     const size_t nw = (size_t)B * N * H * L->wb;
-    const ChunkPlan pa = plan_chunk(ca, B, N, H, L->wb, dk, chunk, false, SIZE_MAX);
-    const ChunkPlan pb = plan_chunk(cb, B, N, H, dk, dv, chunk, false, SIZE_MAX);
-    L->direct = in_dt == RET_BF16 && L->nb == 1 && plan_onchip(ca, pa) && ca.seg_rev && plan_onchip(cb, pb) &&
-                cb.seg_rev && env_int("RET_BWD_DIRECT", 1) != 0;
+    const ChunkPlan pa = plan_chunk(ca, B, N, H, L->wb, dk, chunk, false, SIZE_MAX, op);
+    const ChunkPlan pb = plan_chunk(cb, B, N, H, dk, dv, chunk, false, SIZE_MAX, op);
+    L->direct = in_dt == RET_BF16 && L->nb == 1 && plan_onchip(ca, pa, op) && ca.seg_rev && plan_onchip(cb, pb, op) &&
+                cb.seg_rev && op.bwd_direct != 0;
     L->chain = 0;
     L->chain_bytes = pa.chain_bytes > pb.chain_bytes ? pa.chain_bytes : pb.chain_bytes;
     size_t off = up(L->chain_bytes > 256 ? L->chain_bytes : 256);
@@ -456,10 +538,10 @@ bool bwd_layout(int B, int N, int H, int dk, int dv, int chunk, ret_dtype_t in_d
 // layout differs from the previous call's, its counters and flags (not the header, which keeps a sticky error)
 // are zeroed by a small kernel (graph-safe, unlike a memset node).
 ret_status_t chain_meta_zero(ret_dtype_t in_dt, int B, int N, int H, int dk, int dv, int chunk, void* chain,
-                             size_t chain_bytes, hipStream_t s) {
+                             size_t chain_bytes, hipStream_t s, const Opts& op) {
     ChunkKernels ck;
-    if (!pick_chunk(in_dt, dk, dv, chunk, &ck) || !ck.fused) return RET_OK;  // the split kernels keep no flags
-    const ChunkPlan p = plan_chunk(ck, B, N, H, dk, dv, chunk, false, chain_bytes);
+    if (!pick_chunk(in_dt, dk, dv, chunk, &ck, op) || !ck.fused) return RET_OK;  // the split kernels keep no flags
+    const ChunkPlan p = plan_chunk(ck, B, N, H, dk, dv, chunk, false, chain_bytes, op);
     if (p.nseg <= 1) return RET_OK;
     const ChainLayout lay = chain_layout(B * H * (dv / ck.dvt), p.nseg, dk * ck.dvt);
     const long long n = (long long)(lay.agg_off - lay.ctr_off) / 4;
@@ -470,7 +552,7 @@ ret_status_t chain_meta_zero(ret_dtype_t in_dt, int B, int N, int H, int dk, int
 
 // One launch of permute_rotate_kernel over the given jobs (at most kMaxPermJobs), one grid row per job.
 ret_status_t permute(const PermJob* jobs, int njobs, int B, int N, int H, const double* theta, int64_t pos0,
-                     hipStream_t s) {
+                     hipStream_t s, const Opts& op) {
     PermArgs P;
     memset(&P, 0, sizeof(P));
     P.B = B;
@@ -489,7 +571,7 @@ ret_status_t permute(const PermJob* jobs, int njobs, int B, int N, int H, const 
     const unsigned long long threads = (unsigned long long)B * ((N + kPermTokens - 1) / kPermTokens) * segs;
     if ((long long)B * N >= (1LL << 31) || threads > 0xFFFFFF00ull)
         return fail(RET_ERR_UNSUPPORTED, "gradients: B*N*H*max(d_k,d_v) too large for one reordering launch");
-    LaunchTimer tm("ret_permute_rotate", s);
+    LaunchTimer tm("ret_permute_rotate", s, op);
     hipLaunchKernelGGL(permute_rotate_get(), dim3((unsigned)((threads + 255) / 256), njobs), dim3(256), 0, s, P);
     tm.done();
     return launch_status("ret_permute_rotate");
@@ -499,12 +581,21 @@ ret_status_t permute(const PermJob* jobs, int njobs, int B, int N, int H, const 
 
 extern "C" {
 
+ret_status_t ret_chunkwise_fwd_ex(const void* q, const void* k, const void* v, void* o, int B, int N, int H, int dk,
+                                  int dv, ret_dtype_t in_dt, ret_dtype_t out_dt, const float* gamma,
+                                  const double* theta, int64_t pos0, int chunk, const float* state_in,
+                                  float* state_out, void* workspace, size_t workspace_bytes, void* stream,
+                                  const ret_options_t* opts) {
+    return chunkwise_run(q, k, v, o, B, N, H, dk, dv, in_dt, out_dt, gamma, theta, pos0, chunk, state_in, state_out,
+                         workspace, workspace_bytes, stream, nullptr, nullptr, resolve(opts));
+}
+
 ret_status_t ret_chunkwise_fwd(const void* q, const void* k, const void* v, void* o, int B, int N, int H, int dk,
                                int dv, ret_dtype_t in_dt, ret_dtype_t out_dt, const float* gamma,
                                const double* theta, int64_t pos0, int chunk, const float* state_in,
                                float* state_out, void* workspace, size_t workspace_bytes, void* stream) {
-    return chunkwise_run(q, k, v, o, B, N, H, dk, dv, in_dt, out_dt, gamma, theta, pos0, chunk, state_in, state_out,
-                         workspace, workspace_bytes, stream, nullptr, nullptr);
+    return ret_chunkwise_fwd_ex(q, k, v, o, B, N, H, dk, dv, in_dt, out_dt, gamma, theta, pos0, chunk, state_in,
+                                state_out, workspace, workspace_bytes, stream, nullptr);
 }
 
 ret_status_t ret_chunkwise_msr_fwd(const void* q, const void* k, const void* v, const void* gate, void* y, int B,
@@ -513,6 +604,18 @@ ret_status_t ret_chunkwise_msr_fwd(const void* q, const void* k, const void* v, 
                                    int chunk, const float* state_in, float* state_out, const float* gn_weight,
                                    const float* gn_bias, float eps, void* workspace, size_t workspace_bytes,
                                    void* stream) {
+    return ret_chunkwise_msr_fwd_ex(q, k, v, gate, y, B, N, H, dk, dv, in_dt, out_dt, gate_dt, gamma, theta, pos0,
+                                    chunk, state_in, state_out, gn_weight, gn_bias, eps, workspace, workspace_bytes,
+                                    stream, nullptr);
+}
+
+ret_status_t ret_chunkwise_msr_fwd_ex(const void* q, const void* k, const void* v, const void* gate, void* y, int B,
+                                      int N, int H, int dk, int dv, ret_dtype_t in_dt, ret_dtype_t out_dt,
+                                      ret_dtype_t gate_dt, const float* gamma, const double* theta, int64_t pos0,
+                                      int chunk, const float* state_in, float* state_out, const float* gn_weight,
+                                      const float* gn_bias, float eps, void* workspace, size_t workspace_bytes,
+                                      void* stream, const ret_options_t* opts) {
+    const Opts op = resolve(opts);
     // The epilogue's own checks first, so that nothing is launched for a call that would fail half way.
     if (gate_dt != RET_F32 && gate_dt != RET_BF16) return fail(RET_ERR_INVALID_ARG, "bad gate dtype %d", (int)gate_dt);
     if (!(eps >= 0.f) || !isfinite(eps)) return fail(RET_ERR_INVALID_ARG, "eps=%g must be finite and >= 0", eps);
@@ -528,11 +631,11 @@ ret_status_t ret_chunkwise_msr_fwd(const void* q, const void* k, const void* v, 
     const EpiRequest epi{gate, gate_dt, gn_weight, gn_bias, eps};
     bool fused = false;
     ret_status_t st = chunkwise_run(q, k, v, y, B, N, H, dk, dv, in_dt, out_dt, gamma, theta, pos0, chunk, state_in,
-                                    state_out, workspace, workspace_bytes, stream, &epi, &fused);
+                                    state_out, workspace, workspace_bytes, stream, &epi, &fused, op);
     if (st != RET_OK || fused) return st;
     // not fused: the retention outputs are in y; the epilogue runs over them in place
-    return ret_msr_epilogue(y, gate, gn_weight, gn_bias, y, (int64_t)B * N, H, dv, out_dt, gate_dt, out_dt, eps,
-                            stream);
+    return epilogue_run(y, gate, gn_weight, gn_bias, y, (int64_t)B * N, H, dv, out_dt, gate_dt, out_dt, eps, stream,
+                        op);
 }
 
 }  // extern "C"
@@ -542,7 +645,7 @@ namespace {
 // One decode step; positions either one for the call (`pos`) or one per sequence (`pos_dev`, device [B]).
 ret_status_t step_run(const void* q, const void* k, const void* v, void* o, float* state, int B, int H, int dk,
                       int dv, ret_dtype_t in_dt, ret_dtype_t out_dt, const float* gamma, const double* theta,
-                      int64_t pos, const int64_t* pos_dev, void* stream) {
+                      int64_t pos, const int64_t* pos_dev, void* stream, const Opts& op) {
     ret_status_t st = check_common(q, k, v, o, B, 1, H, dk, dv, in_dt, out_dt, gamma, theta);
     if (st != RET_OK) return st;
     if (!state) return fail(RET_ERR_INVALID_ARG, "null state");
@@ -575,12 +678,11 @@ ret_status_t step_run(const void* q, const void* k, const void* v, void* o, floa
             A.rs[i] = (float)sin(ang);
         }
     int cw = 0, wr = 0, ppw = 1;
-    step_kernel_t fn = step_kernel_get(in_dt == RET_BF16, dk, dv, B * H, env_int("RET_STEP_CW", 0),
-                                       env_int("RET_STEP_WR", 0), env_int("RET_STEP_PAIRS", 0), A.pos != nullptr,
-                                       &cw, &wr, &ppw);
+    step_kernel_t fn = step_kernel_get(in_dt == RET_BF16, dk, dv, B * H, op.step_cw, op.step_wr, op.step_pairs,
+                                       A.pos != nullptr, &cw, &wr, &ppw);
     if (!fn) return fail(RET_ERR_UNSUPPORTED, "decode step: d_k=%d not in {16,32,64,128,256}", dk);
     hipStream_t s = (hipStream_t)stream;
-    LaunchTimer tm("ret_recurrent_step", s);
+    LaunchTimer tm("ret_recurrent_step", s, op);
     hipLaunchKernelGGL(fn, dim3((dv + cw - 1) / cw, (B * H + ppw - 1) / ppw), dim3(64 * (dk / wr) * ppw), 0, s, A);
     tm.done();
     return launch_status("ret_recurrent_step");
@@ -590,73 +692,69 @@ ret_status_t step_run(const void* q, const void* k, const void* v, void* o, floa
 
 extern "C" {
 
+ret_status_t ret_recurrent_step_ex(const void* q, const void* k, const void* v, void* o, float* state, int B, int H,
+                                   int dk, int dv, ret_dtype_t in_dt, ret_dtype_t out_dt, const float* gamma,
+                                   const double* theta, int64_t pos, void* stream, const ret_options_t* opts) {
+    return step_run(q, k, v, o, state, B, H, dk, dv, in_dt, out_dt, gamma, theta, pos, nullptr, stream,
+                    resolve(opts));
+}
+
 ret_status_t ret_recurrent_step(const void* q, const void* k, const void* v, void* o, float* state, int B, int H,
                                 int dk, int dv, ret_dtype_t in_dt, ret_dtype_t out_dt, const float* gamma,
                                 const double* theta, int64_t pos, void* stream) {
-    return step_run(q, k, v, o, state, B, H, dk, dv, in_dt, out_dt, gamma, theta, pos, nullptr, stream);
+    return ret_recurrent_step_ex(q, k, v, o, state, B, H, dk, dv, in_dt, out_dt, gamma, theta, pos, stream, nullptr);
+}
+
+ret_status_t ret_recurrent_step_positions_ex(const void* q, const void* k, const void* v, void* o, float* state,
+                                             int B, int H, int dk, int dv, ret_dtype_t in_dt, ret_dtype_t out_dt,
+                                             const float* gamma, const double* theta, const int64_t* pos,
+                                             void* stream, const ret_options_t* opts) {
+    if (!pos) return fail(RET_ERR_INVALID_ARG, "null pos");
+    if ((uintptr_t)pos % 8) return fail(RET_ERR_INVALID_ARG, "pos must be 8-byte aligned");
+    return step_run(q, k, v, o, state, B, H, dk, dv, in_dt, out_dt, gamma, theta, 0, pos, stream, resolve(opts));
 }
 
 ret_status_t ret_recurrent_step_positions(const void* q, const void* k, const void* v, void* o, float* state, int B,
                                           int H, int dk, int dv, ret_dtype_t in_dt, ret_dtype_t out_dt,
                                           const float* gamma, const double* theta, const int64_t* pos,
                                           void* stream) {
-    if (!pos) return fail(RET_ERR_INVALID_ARG, "null pos");
-    if ((uintptr_t)pos % 8) return fail(RET_ERR_INVALID_ARG, "pos must be 8-byte aligned");
-    return step_run(q, k, v, o, state, B, H, dk, dv, in_dt, out_dt, gamma, theta, 0, pos, stream);
+    return ret_recurrent_step_positions_ex(q, k, v, o, state, B, H, dk, dv, in_dt, out_dt, gamma, theta, pos, stream,
+                                           nullptr);
 }
 
 ret_status_t ret_msr_epilogue(const void* o, const void* gate, const float* gn_weight, const float* gn_bias,
                               void* y, int64_t rows, int H, int dv, ret_dtype_t o_dt, ret_dtype_t gate_dt,
                               ret_dtype_t y_dt, float eps, void* stream) {
-    if (!o || !y) return fail(RET_ERR_INVALID_ARG, "null o/y pointer");
-    if (rows < 0 || H <= 0 || dv <= 0)
-        return fail(RET_ERR_INVALID_ARG, "sizes must be positive (rows=%lld H=%d dv=%d)", (long long)rows, H, dv);
-    for (ret_dtype_t t : {o_dt, gate_dt, y_dt})
-        if (t != RET_F32 && t != RET_BF16) return fail(RET_ERR_INVALID_ARG, "bad dtype %d", (int)t);
-    if (!(eps >= 0.f) || !isfinite(eps)) return fail(RET_ERR_INVALID_ARG, "eps=%g must be finite and >= 0", eps);
-    if (!aligned16(o) || !aligned16(y) || (gate && !aligned16(gate)) || (gn_weight && !aligned16(gn_weight)) ||
-        (gn_bias && !aligned16(gn_bias)))
-        return fail(RET_ERR_INVALID_ARG, "o/gate/y/gn_weight/gn_bias must be 16-byte aligned");
-    int gpw = 0;
-    const epi_kernel_t fn = epilogue_kernel_get(dv, &gpw);
-    if (!fn) return fail(RET_ERR_UNSUPPORTED, "epilogue: d_v=%d not in {16,32,64,128,256,512}", dv);
-    const long long groups = (long long)rows * H;
-    if (groups == 0) return RET_OK;
-    if (groups > 0x7fffffffLL)
-        return fail(RET_ERR_UNSUPPORTED, "epilogue: %lld rows x %d heads exceed 2^31 groups", (long long)rows, H);
-    const long long wgs = (groups + gpw - 1) / gpw;
-    EpiArgs A;
-    A.o = o;
-    A.gate = gate;
-    A.weight = gn_weight;
-    A.bias = gn_bias;
-    A.y = y;
-    A.groups = groups;
-    A.H = H;
-    A.dv = dv;
-    A.o_bf16 = o_dt == RET_BF16;
-    A.gate_bf16 = gate_dt == RET_BF16;
-    A.y_bf16 = y_dt == RET_BF16;
-    A.eps = eps;
-    hipStream_t s = (hipStream_t)stream;
-    LaunchTimer tm("ret_msr_epilogue", s);
-    hipLaunchKernelGGL(fn, dim3((unsigned)wgs), dim3(256), 0, s, A);
-    tm.done();
-    return launch_status("ret_msr_epilogue");
-}
-
-size_t ret_chunkwise_bwd_workspace_bytes(int B, int N, int H, int dk, int dv, int chunk, ret_dtype_t in_dt) {
-    BwdLayout L;
-    if (B <= 0 || N <= 0 || H <= 0 || dk <= 0 || dv <= 0 || chunk <= 0) return 0;
-    if (in_dt != RET_F32 && in_dt != RET_BF16) return 0;
-    if (!bwd_layout(B, N, H, dk, dv, chunk, in_dt, true, &L)) return 0;
-    return L.total;
+    return epilogue_run(o, gate, gn_weight, gn_bias, y, rows, H, dv, o_dt, gate_dt, y_dt, eps, stream, kDefaultOpts);
 }
 
 ret_status_t ret_chunkwise_bwd(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk_out,
                                void* dv_out, int B, int N, int H, int dk, int dv, ret_dtype_t in_dt,
                                ret_dtype_t out_dt, const float* gamma, const double* theta, int64_t pos0, int chunk,
                                void* workspace, size_t workspace_bytes, void* stream) {
+    return ret_chunkwise_bwd_ex(q, k, v, dout, dq, dk_out, dv_out, B, N, H, dk, dv, in_dt, out_dt, gamma, theta, pos0,
+                                chunk, workspace, workspace_bytes, stream, nullptr);
+}
+
+size_t ret_chunkwise_bwd_workspace_bytes_ex(int B, int N, int H, int dk, int dv, int chunk, ret_dtype_t in_dt,
+                                            const ret_options_t* opts) {
+    BwdLayout L;
+    if (B <= 0 || N <= 0 || H <= 0 || dk <= 0 || dv <= 0 || chunk <= 0) return 0;
+    if (in_dt != RET_F32 && in_dt != RET_BF16) return 0;
+    if (!bwd_layout(B, N, H, dk, dv, chunk, in_dt, true, &L, resolve(opts))) return 0;
+    return L.total;
+}
+
+size_t ret_chunkwise_bwd_workspace_bytes(int B, int N, int H, int dk, int dv, int chunk, ret_dtype_t in_dt) {
+    return ret_chunkwise_bwd_workspace_bytes_ex(B, N, H, dk, dv, chunk, in_dt, nullptr);
+}
+
+ret_status_t ret_chunkwise_bwd_ex(const void* q, const void* k, const void* v, const void* dout, void* dq,
+                                  void* dk_out, void* dv_out, int B, int N, int H, int dk, int dv, ret_dtype_t in_dt,
+                                  ret_dtype_t out_dt, const float* gamma, const double* theta, int64_t pos0,
+                                  int chunk, void* workspace, size_t workspace_bytes, void* stream,
+                                  const ret_options_t* opts) {
+    const Opts op = resolve(opts);
     ret_status_t st = check_common(q, k, v, dq, B, N, H, dk, dv, in_dt, out_dt, gamma, theta);
     if (st != RET_OK) return st;
     if (!dout || !dk_out || !dv_out) return fail(RET_ERR_INVALID_ARG, "null dout/dk/dv pointer");
@@ -667,7 +765,7 @@ ret_status_t ret_chunkwise_bwd(const void* q, const void* k, const void* v, cons
     if (dq == dk_out || dq == dv_out || dk_out == dv_out) return fail(RET_ERR_INVALID_ARG, "dq, dk, dv must differ");
     if (chunk <= 0) return fail(RET_ERR_INVALID_ARG, "chunk must be positive (got %d)", chunk);
     BwdLayout L;
-    if (!bwd_layout(B, N, H, dk, dv, chunk, in_dt, theta != nullptr, &L))
+    if (!bwd_layout(B, N, H, dk, dv, chunk, in_dt, theta != nullptr, &L, op))
         return fail(RET_ERR_UNSUPPORTED,
                     "gradients: d_k=%d d_v=%d chunk=%d for %s input (both (d_k, d_v) and (d_v, d_k) need kernels)", dk,
                     dv, chunk, in_dt == RET_F32 ? "F32" : "BF16");
@@ -689,7 +787,7 @@ ret_status_t ret_chunkwise_bwd(const void* q, const void* k, const void* v, cons
             A.kr = ws + L.kp;
             Qp = A.qr;
             Kp = A.kr;
-            LaunchTimer tr("ret_rotate_qk", s);
+            LaunchTimer tr("ret_rotate_qk", s, op);
             hipLaunchKernelGGL(rotate_qk_get(), dim3(rotate_qk_blocks(B, N, H, dk)), dim3(256), 0, s, A);
             tr.done();
             if ((st = launch_status("ret_rotate_qk")) != RET_OK) return st;
@@ -697,14 +795,14 @@ ret_status_t ret_chunkwise_bwd(const void* q, const void* k, const void* v, cons
         // dq and dk straight from the retentions, their output rows turned back by the transpose rotation
         void* chain = ws + L.chain;
         if ((st = chunkwise_run(dout, v, Kp, dq, B, N, H, dv, dk, RET_BF16, out_dt, gamma, nullptr, pos0, chunk,
-                                nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, false, theta)) !=
+                                nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, op, false, theta)) !=
             RET_OK)
             return st;
         if ((st = chunkwise_run(Kp, Qp, dout, dv_out, B, N, H, dk, dv, RET_BF16, out_dt, gamma, nullptr, 0, chunk,
-                                nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, true)) != RET_OK)
+                                nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, op, true)) != RET_OK)
             return st;
         return chunkwise_run(v, dout, Qp, dk_out, B, N, H, dv, dk, RET_BF16, out_dt, gamma, nullptr, pos0, chunk,
-                             nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, true, theta);
+                             nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, op, true, theta);
     }
     const int ib = in_dt == RET_BF16;
     if (L.nb == 2) {
@@ -717,35 +815,35 @@ ret_status_t ret_chunkwise_bwd(const void* q, const void* k, const void* v, cons
             {q, {Qr, nullptr}, dk, 1, 0, {1, 0}, ib, ib},
             {dout, {dOr, nullptr}, dv, 0, 0, {1, 0}, ib, ib},
         };
-        if ((st = permute(pre, 3, B, N, H, theta, pos0, s)) != RET_OK) return st;
+        if ((st = permute(pre, 3, B, N, H, theta, pos0, s, op)) != RET_OK) return st;
         const PermJob halves[4] = {
             {v, {ws + L.vbn[0], ws + L.vbr[0]}, wb, 0, 0, {0, 1}, ib, ib, nullptr, dv, 0},
             {v, {ws + L.vbn[1], ws + L.vbr[1]}, wb, 0, 0, {0, 1}, ib, ib, nullptr, dv, wb},
             {dout, {ws + L.dobn[0], ws + L.dobr[0]}, wb, 0, 0, {0, 1}, ib, ib, nullptr, dv, 0},
             {dout, {ws + L.dobn[1], ws + L.dobr[1]}, wb, 0, 0, {0, 1}, ib, ib, nullptr, dv, wb},
         };
-        if ((st = permute(halves, 4, B, N, H, nullptr, 0, s)) != RET_OK) return st;
+        if ((st = permute(halves, 4, B, N, H, nullptr, 0, s, op)) != RET_OK) return st;
         for (int i = 0; i < 2; ++i)
             if ((st = chunkwise_run(ws + L.dobn[i], ws + L.vbn[i], Kp, ws + L.g1b[i], B, N, H, wb, dk, in_dt, RET_F32,
                                     gamma, nullptr, 0, chunk, nullptr, nullptr, chain, L.chain_bytes, stream, nullptr,
-                                    nullptr)) != RET_OK)
+                                    nullptr, op)) != RET_OK)
                 return st;
-        if ((st = chain_meta_zero(in_dt, B, N, H, dk, dv, chunk, chain, L.chain_bytes, s)) != RET_OK) return st;
+        if ((st = chain_meta_zero(in_dt, B, N, H, dk, dv, chunk, chain, L.chain_bytes, s, op)) != RET_OK) return st;
         if ((st = chunkwise_run(Kr, Qr, dOr, ws + L.g2, B, N, H, dk, dv, in_dt, RET_F32, gamma, nullptr, 0, chunk,
-                                nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr)) != RET_OK)
+                                nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, op)) != RET_OK)
             return st;
-        if ((st = chain_meta_zero(in_dt, B, N, H, wb, dk, chunk, chain, L.chain_bytes, s)) != RET_OK) return st;
+        if ((st = chain_meta_zero(in_dt, B, N, H, wb, dk, chunk, chain, L.chain_bytes, s, op)) != RET_OK) return st;
         for (int i = 0; i < 2; ++i)
             if ((st = chunkwise_run(ws + L.vbr[i], ws + L.dobr[i], Qr, ws + L.g3b[i], B, N, H, wb, dk, in_dt, RET_F32,
                                     gamma, nullptr, 0, chunk, nullptr, nullptr, chain, L.chain_bytes, stream, nullptr,
-                                    nullptr)) != RET_OK)
+                                    nullptr, op)) != RET_OK)
                 return st;
         const PermJob post[3] = {
             {ws + L.g1b[0], {dq, nullptr}, dk, -1, 0, {0, 0}, 0, ob, ws + L.g1b[1]},
             {ws + L.g3b[0], {dk_out, nullptr}, dk, -1, 1, {0, 0}, 0, ob, ws + L.g3b[1]},
             {ws + L.g2, {dv_out, nullptr}, dv, 0, 1, {0, 0}, 0, ob},
         };
-        return permute(post, 3, B, N, H, theta, pos0, s);
+        return permute(post, 3, B, N, H, theta, pos0, s, op);
     }
     void *Kp = ws + L.kp, *Kr = ws + L.kr, *Qr = ws + L.qr, *Vr = ws + L.vr, *dOr = ws + L.dor;
     void *G1 = ws + L.g1, *G2 = ws + L.g2, *G3 = ws + L.g3, *chain = ws + L.chain;
@@ -756,20 +854,20 @@ ret_status_t ret_chunkwise_bwd(const void* q, const void* k, const void* v, cons
         {v, {Vr, nullptr}, dv, 0, 0, {1, 0}, ib, ib},
         {dout, {dOr, nullptr}, dv, 0, 0, {1, 0}, ib, ib},
     };
-    if ((st = permute(pre, 4, B, N, H, theta, pos0, s)) != RET_OK) return st;
+    if ((st = permute(pre, 4, B, N, H, theta, pos0, s, op)) != RET_OK) return st;
     // dq' = retention(dO, V, K'); dv^rev = retention(K'^rev, Q'^rev, dO^rev); dk'^rev = retention(V^rev, dO^rev, Q'^rev)
     if ((st = chunkwise_run(dout, v, Kp, G1, B, N, H, dv, dk, in_dt, RET_F32, gamma, nullptr, 0, chunk, nullptr,
-                            nullptr, chain, L.chain_bytes, stream, nullptr, nullptr)) != RET_OK)
+                            nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, op)) != RET_OK)
         return st;
-    if (dk != dv && (st = chain_meta_zero(in_dt, B, N, H, dk, dv, chunk, chain, L.chain_bytes, s)) != RET_OK)
+    if (dk != dv && (st = chain_meta_zero(in_dt, B, N, H, dk, dv, chunk, chain, L.chain_bytes, s, op)) != RET_OK)
         return st;
     if ((st = chunkwise_run(Kr, Qr, dOr, G2, B, N, H, dk, dv, in_dt, RET_F32, gamma, nullptr, 0, chunk, nullptr,
-                            nullptr, chain, L.chain_bytes, stream, nullptr, nullptr)) != RET_OK)
+                            nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, op)) != RET_OK)
         return st;
-    if (dk != dv && (st = chain_meta_zero(in_dt, B, N, H, dv, dk, chunk, chain, L.chain_bytes, s)) != RET_OK)
+    if (dk != dv && (st = chain_meta_zero(in_dt, B, N, H, dv, dk, chunk, chain, L.chain_bytes, s, op)) != RET_OK)
         return st;
     if ((st = chunkwise_run(Vr, dOr, Qr, G3, B, N, H, dv, dk, in_dt, RET_F32, gamma, nullptr, 0, chunk, nullptr,
-                            nullptr, chain, L.chain_bytes, stream, nullptr, nullptr)) != RET_OK)
+                            nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, op)) != RET_OK)
         return st;
     // back to the caller's order, dq and dk turned back by the transpose rotation
     const PermJob post[3] = {
@@ -777,31 +875,52 @@ ret_status_t ret_chunkwise_bwd(const void* q, const void* k, const void* v, cons
         {G3, {dk_out, nullptr}, dk, -1, 1, {0, 0}, 0, ob},
         {G2, {dv_out, nullptr}, dv, 0, 1, {0, 0}, 0, ob},
     };
-    return permute(post, 3, B, N, H, theta, pos0, s);
+    return permute(post, 3, B, N, H, theta, pos0, s, op);
 }
 
-int ret_timing_enable(int on) {
-    std::lock_guard<std::mutex> lk(g_timing_mu);
-    int prev = g_timing_on;
-    g_timing_on = on != 0;
-    return prev;
+ret_timer_t* ret_timer_create(void) { return new (std::nothrow) ret_timer(); }
+
+void ret_timer_reset(ret_timer_t* t) {
+    if (!t) return;
+    std::lock_guard<std::mutex> lk(t->mu);
+    for (auto& r : t->recs) {
+        (void)hipEventDestroy(r.start);
+        (void)hipEventDestroy(r.stop);
+    }
+    t->recs.clear();
 }
 
-int ret_timing_query(const char* kernel, double* total_ms, int64_t* launches) {
-    std::lock_guard<std::mutex> lk(g_timing_mu);
+void ret_timer_destroy(ret_timer_t* t) {
+    if (!t) return;
+    ret_timer_reset(t);
+    delete t;
+}
+
+int ret_timer_query(ret_timer_t* t, const char* kernel, double* total_ms, int64_t* launches) {
     double tot = 0.0;
     int64_t n = 0;
-    for (auto& r : g_timing) {
-        if (kernel && *kernel && strcmp(kernel, r.name) != 0) continue;
-        if (hipEventSynchronize(r.stop) != hipSuccess) return RET_ERR_HIP;
-        float ms = 0.f;
-        if (hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess) return RET_ERR_HIP;
-        tot += ms;
-        ++n;
+    if (t) {
+        std::lock_guard<std::mutex> lk(t->mu);
+        for (auto& r : t->recs) {
+            if (kernel && *kernel && strcmp(kernel, r.name) != 0) continue;
+            if (hipEventSynchronize(r.stop) != hipSuccess) return RET_ERR_HIP;
+            float ms = 0.f;
+            if (hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess) return RET_ERR_HIP;
+            tot += ms;
+            ++n;
+        }
     }
     if (total_ms) *total_ms = tot;
     if (launches) *launches = n;
     return RET_OK;
+}
+
+void ret_options_default(ret_options_t* o) {
+    if (!o) return;
+    memset(o, 0, sizeof(*o));
+    o->prerotate = -1;
+    o->onchip = 1;
+    o->bwd_direct = 1;
 }
 
 ret_status_t ret_chunkwise_check(const void* workspace, void* stream) {
@@ -812,15 +931,6 @@ ret_status_t ret_chunkwise_check(const void* workspace, void* stream) {
         return fail(RET_ERR_HIP, "reading the workspace header failed");
     if (h.error) return fail(RET_ERR_HIP, "a segment-chain wait gave up: outputs of that call are invalid");
     return RET_OK;
-}
-
-void ret_timing_reset(void) {
-    std::lock_guard<std::mutex> lk(g_timing_mu);
-    for (auto& r : g_timing) {
-        (void)hipEventDestroy(r.start);
-        (void)hipEventDestroy(r.stop);
-    }
-    g_timing.clear();
 }
 
 }  // extern "C"

@@ -176,22 +176,46 @@ struct SliceRot {
 // that enters the group, which the last segment of the previous group publishes (it computes its own R_in
 // the same way). Every R_in is thus a sum in a fixed order, independent of timing, over at most 8 slots.
 // Published states are written and read at device scope (sc1) and a slot's flag is raised only after the
-// slot's stores completed; a wait that sees no progress for ~0.17 s gives up and sets the sticky error word
-// instead of hanging. The unit's last workgroup past the look-back returns its counters and flags to zero.
+// slot's stores completed (the ordering argument is below chain_wait); a wait that sees no progress for the
+// call's limit (default ~0.17 s) gives up, sets the sticky error word and takes NaN for the entering state, so
+// the outputs that depend on it are NaN instead of silently wrong. The unit's last workgroup past the look-back
+// returns its counters and flags to zero.
 // ---------------------------------------------------------------------------------------------------
 constexpr int kOutAux = 0;                        // output stores: default policy (nt and sc1 measured no faster)
 constexpr int kChainGroup = 8;                    // segments per look-back group
 constexpr int kChainAux = 16;                     // buffer cache policy: sc1 (device-scope coherent)
-constexpr unsigned long long kChainSpin = 1ull << 24;  // give-up time in s_memrealtime ticks (100 MHz)
 
-// Waits until flags[lo .. lo+n) are all nonzero (n <= 64; lane i watches flag lo + i). False if it gave up.
-__device__ __forceinline__ bool chain_wait(const int* flags, int lo, int n, int* error) {
+// Waits until flags[lo .. lo+n) are all nonzero (n <= 64; lane i watches flag lo + i). False if it gave up: after
+// `spin` ticks of the 100 MHz s_memrealtime clock in which no further flag rose (each flag that rises restarts
+// the limit), or at once when spin < 0 (the host's way to exercise this path without a real stall).
+//
+// Ordering. A publisher stores its slot with device-scope (sc1) buffer stores, waits for them to complete
+// (s_waitcnt vmcnt(0): on gfx9 a store is counted until the device-coherent level has acknowledged it), and only
+// then stores the flag, itself a device-scope store. A waiter reads the flag with a device-scope load, and issues
+// its slot loads only after the flag's value has come back (the ballot and the branch depend on it). Those slot
+// loads are device-scope too: they are not served from the waiter's L1 or its XCD's L2, which may hold stale lines
+// of the reused workspace, but from the device-coherent level, where the slot's stores had completed before the
+// flag was written. So a waiter that sees the flag sees the slot. The same holds for the prefix slot and its flag
+// value 2. (Release/acquire atomics would give the same guarantee through a write-back and an invalidation of
+// the whole L2 per publication; these scoped accesses touch only the lines involved.)
+__device__ __forceinline__ bool chain_wait(const int* flags, int lo, int n, int* error, long long spin) {
     const int lane = threadIdx.x & 63;
-    const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+    if (spin < 0) {
+        __hip_atomic_store(error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return false;
+    }
+    unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+    int seen = 0;
     for (;;) {
         const int f = lane < n ? __hip_atomic_load(flags + lo + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 1;
-        if (__builtin_amdgcn_ballot_w64(f == 0) == 0) return true;
-        if (__builtin_amdgcn_s_memrealtime() - t0 > kChainSpin) {
+        const unsigned long long missing = __builtin_amdgcn_ballot_w64(f == 0);
+        if (missing == 0) return true;
+        const int up = 64 - __builtin_popcountll(missing);  // flags up (and idle lanes)
+        const unsigned long long now = __builtin_amdgcn_s_memrealtime();
+        if (up > seen) {  // progress: the limit counts from here
+            seen = up;
+            t0 = now;
+        } else if (now - t0 > (unsigned long long)spin) {
             __hip_atomic_store(error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             return false;
         }
@@ -250,8 +274,10 @@ struct Chain {
     float* inc;    // [nseg][slot]: prefixes leaving a group (published by its last segment)
     int* error;    // sticky error word of the header
     int slot;      // floats per state slot
+    long long spin;  // wait limit (chain_wait)
 };
-__device__ __forceinline__ Chain chain_of(void* ws, int units, int nseg, int unit, int slot_floats) {
+__device__ __forceinline__ Chain chain_of(void* ws, int units, int nseg, int unit, int slot_floats,
+                                          long long spin = 0) {
     const ChainLayout lay = chain_layout(units, nseg, slot_floats);
     char* base = reinterpret_cast<char*>(ws);
     Chain ch;
@@ -261,6 +287,7 @@ __device__ __forceinline__ Chain chain_of(void* ws, int units, int nseg, int uni
     ch.inc = reinterpret_cast<float*>(base + lay.inc_off) + (size_t)unit * nseg * slot_floats;
     ch.error = &reinterpret_cast<ChainHeader*>(ws)->error;
     ch.slot = slot_floats;
+    ch.spin = spin;
     return ch;
 }
 
@@ -296,6 +323,7 @@ __device__ __forceinline__ void chain_publish(const Chain& ch, int seg, const f3
 
 // R_in of segment seg: the sum over the group's earlier segments j of gamma^((seg-1-j)T) A_j, plus
 // gamma^((seg-g0)T) times the prefix entering the group (published by the previous group's last segment).
+// If the wait gives up, R_in is NaN (and so is the prefix a group's last segment publishes from it).
 // One poll covers every flag; slots are read in batches and added in a fixed order, so results do not depend
 // on timing. A group's last segment (not the sequence's) then publishes gamma^T R_in + A_seg, A_seg = Rown.
 // With COUNT, the workgroup then counts itself past the look-back and the unit's last one resets the unit's
@@ -312,8 +340,14 @@ __device__ __forceinline__ void chain_enter(const Chain& ch, int seg, int nseg, 
     for (int x = 0; x < NKB; ++x) Rin[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     if (seg > 0) {
         const int lo = g0 > 0 ? g0 - 1 : g0;
-        // (wave-uniform: the wait's result is a ballot; on give-up the sum stays partial)
-        const bool ok = __builtin_amdgcn_readfirstlane((int)chain_wait(ch.flags, lo, seg - lo, ch.error)) != 0;
+        // (wave-uniform: the wait's result is a ballot)
+        const bool ok =
+            __builtin_amdgcn_readfirstlane((int)chain_wait(ch.flags, lo, seg - lo, ch.error, ch.spin)) != 0;
+        if (!ok) {
+            const float nan = __builtin_nanf("");
+#pragma unroll
+            for (int x = 0; x < NKB; ++x) Rin[x] = f32x4_t{nan, nan, nan, nan};
+        }
         constexpr int LB = NKB >= 16 ? 1 : NKB >= 8 ? 2 : 4;
         float dec = 1.f;
         for (int j0 = seg - 1; ok && j0 >= g0; j0 -= LB) {
@@ -458,7 +492,7 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT, NDW>::OCC)) void ch
     int seg = __builtin_amdgcn_readfirstlane((int)(blockIdx.x / (unsigned)units));
     Chain ch{};
     if (chained) {
-        ch = chain_of(a.ws, units, a.nseg, unit, DK * DVT);
+        ch = chain_of(a.ws, units, a.nseg, unit, DK * DVT, a.chain_spin);
         seg = chain_ticket(ch, s_word);
     }
     // Scalar arguments re-read as wave-uniform values: they are live across the divergent ticket branch.
@@ -594,8 +628,16 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT, NDW>::OCC)) void ch
             if (c + 1 < nchunks) lchunk(c + 1, std::integral_constant<int, 1>{});
         }
         __syncthreads();  // the local tiles are dead before the full pass reuses the LDS
-        // publish the aggregate for the later segments of the group (nothing else in flight)
-        if (!boundary) chain_publish<NR, NT>(ch, seg, R);
+        // Publish the aggregate for the later segments of the group (nothing else in flight). The first segment
+        // starts its full pass from state_in again: it reloads it into R behind the slot stores and before its
+        // flag rises, since state_out may be the same buffer, and the last segment writes it only after every
+        // earlier segment's flag (segment 0 is never a group's last segment, so it always publishes here).
+        if (!boundary) {
+            if (seg == 0 && a.state_in)
+                chain_publish<NR, NT, 0>(ch, seg, R, [&] { load_state_in(R); });
+            else
+                chain_publish<NR, NT>(ch, seg, R);
+        }
     }
 
     // ---- full pass: staging ----
@@ -629,16 +671,13 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT, NDW>::OCC)) void ch
     if constexpr (NBUF == 2)
         if (nst > 1) issue(1, std::integral_constant<int, 1>{});
 
-    // ---- entering state: state_in for the first segment, else R_in from the segment chain ----
+    // ---- entering state: state_in for the first segment (already back in R), else R_in from the chain ----
     if (chained) {
         f32x4_t Rin[NR];
         chain_enter<NR, NT, true>(ch, seg, anseg, gpow(lg, (float)aseg_len), R, Rin, s_word);
+        if (seg > 0 || !a.state_in) {  // (segment 0's R_in is zero)
 #pragma unroll
-        for (int x = 0; x < NR; ++x) R[x] = Rin[x];
-        if (seg == 0) {
-#pragma unroll
-            for (int x = 0; x < NR; ++x) R[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            if (a.state_in) load_state_in(R);
+            for (int x = 0; x < NR; ++x) R[x] = Rin[x];
         }
     }
 

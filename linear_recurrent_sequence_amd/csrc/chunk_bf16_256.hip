@@ -2,21 +2,15 @@
 // run as 64-token sub-chunks: the instances differ only in the segment plan). Where d_v is a multiple of 128 the d_v
 // tile is 128 columns: 512 threads whose waves own 16 columns each (the default: two waves per SIMD), or 256
 // threads whose waves own 32 columns each (twice the operand reuse per LDS read, one wave per SIMD).
-// RET_DK256_THREADS picks 512, 256x2, or 256 (the 256-thread kernel with 16-column waves and d_v tiles of 64).
-// Other d_v: 256 threads with d_v tiles of 64.
-#include <stdlib.h>
-#include <string.h>
-
+// `variant` picks 0: 512 x 16 (default), 1: 256 x 32, 2: the 256-thread kernel with 16-column waves and d_v
+// tiles of 64. Other d_v: 256 threads with d_v tiles of 64.
 #include "chunk_bf16.h"
 
 namespace ret {
 
-bool chunk_kernels_bf16_256(int dk, int dv, int C, ChunkKernels* out) {
+bool chunk_kernels_bf16_256(int dk, int dv, int C, int variant, ChunkKernels* out) {
     if (dv % 64) return false;
-    const char* env = getenv("RET_DK256_THREADS");
-    int mode = 1;  // 0: 256 threads x 16 columns, 1: 512 x 16, 2: 256 x 32
-    if (env && !strcmp(env, "256")) mode = 0;
-    else if (env && !strcmp(env, "256x2")) mode = 2;
+    int mode = variant == 1 ? 2 : variant == 2 ? 0 : 1;  // 0: 256 threads x 16 columns, 1: 512 x 16, 2: 256 x 32
     if (dv % 128) mode = 0;
 #define RET_CASE(DKv, Cv)                                                                             \
     if (dk == DKv && C == Cv) {                                                                       \

@@ -63,7 +63,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_seg_bf16(FwdArgs a) {
     const int ntiles = __builtin_amdgcn_readfirstlane(a.dv / 64);
     const int units = __builtin_amdgcn_readfirstlane(a.B * a.H * ntiles);
     const int unit = unit_of_block(ntiles, units);
-    const Chain ch = chain_of(a.ws, units, a.nseg, unit, DK * 64);
+    const Chain ch = chain_of(a.ws, units, a.nseg, unit, DK * 64, a.chain_spin);
     // Scalar arguments as wave-uniform values.
     const int aN = __builtin_amdgcn_readfirstlane(a.N), aH = __builtin_amdgcn_readfirstlane(a.H);
     const int adk = __builtin_amdgcn_readfirstlane(a.dk), adv = __builtin_amdgcn_readfirstlane(a.dv);

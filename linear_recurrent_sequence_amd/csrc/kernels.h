@@ -22,6 +22,7 @@ struct FwdArgs {
     int B, N, H, dk, dv;
     int nseg;                // segments per sequence
     int seg_len;             // tokens per segment (multiple of the chunk), last segment may be shorter
+    long long chain_spin;    // segment-chain wait limit without progress (100 MHz ticks); < 0: give up at once
     int out_bf16;
     int rotate;
     long long pos0;
@@ -982,7 +983,7 @@ inline unsigned rotate_qk_blocks(int B, int N, int H, int dk) {
 bool chunk_kernels_f32(int dk, int dv, int C, ChunkKernels* out);
 bool chunk_kernels_bf16_small(int dk, int dv, int C, ChunkKernels* out);   // d_k in {32, 64}
 bool chunk_kernels_bf16_128(int dk, int dv, int C, ChunkKernels* out);     // d_k = 128
-bool chunk_kernels_bf16_256(int dk, int dv, int C, ChunkKernels* out);     // d_k = 256
+bool chunk_kernels_bf16_256(int dk, int dv, int C, int variant, ChunkKernels* out);  // d_k = 256
 bool parallel_kernel_get(bool bf16_in, int dk, int dv, ParKernel* out);
 // Decode kernel for a (d_k, column tile cw, rows per wave wr) tile, 0 = default, null if none; with pairs_mode 0
 // it groups (b, h) pairs into workgroups of up to 8 waves where B*H leaves a workgroup per CU; 1 / 2 force one

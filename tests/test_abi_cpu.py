@@ -35,7 +35,8 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ret_abi_version() == 5
+    declared = int(re.search(r"#define RET_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert lib.ret_abi_version() == declared
     assert lib.ret_status_string(0) == b"ok"
     assert lib.ret_status_string(-2) == b"unsupported shape or dtype"
 
@@ -175,3 +176,82 @@ def test_gradients_workspace_and_rejections(lib):
     assert call(dkk=48) == -2           # no kernel for d_k = 48
     assert call(wsb=need - 256) == -3   # workspace too small
     assert call(ws=None) == -3
+
+
+def test_library_matches_its_sources(lib):
+    """The loaded library was built from the sources in the tree (a stale build is rebuilt or refused)."""
+    from linear_recurrent_sequence_amd import build
+    lib.ret_source_digest.restype = ctypes.c_char_p
+    assert lib.ret_source_digest().decode() == build.source_digest()
+
+
+def test_options_and_timer_objects(lib):
+    """ret_options_default fills the documented defaults; a timer is a caller-owned object that starts empty
+    (no GPU call is made)."""
+    from linear_recurrent_sequence_amd import retention as R
+    o = R.Options()
+    lib.ret_options_default(ctypes.byref(o))
+    assert (o.segments, o.target_wgs, o.prerotate, o.onchip, o.variant, o.bwd_direct, o.chain_spin) == \
+        (0, 0, -1, 1, 0, 1, 0)
+    assert o.timer is None
+    t = R.Timer()
+    assert t.query("") == (0.0, 0)
+    t.reset()
+    t.close()
+    with pytest.raises(ValueError):
+        R._options({"no_such_option": 1})
+
+
+def test_options_change_the_plan_on_the_host(lib):
+    """A forced segment count changes the chunkwise workspace the plan wants (host-side planning only)."""
+    from linear_recurrent_sequence_amd import retention as R
+    import torch
+    n_default = R.ret_chunkwise_workspace_bytes(1, 4096, 2, 64, 64, 64, torch.bfloat16)
+    n_one = R.ret_chunkwise_workspace_bytes(1, 4096, 2, 64, 64, 64, torch.bfloat16, options={"segments": 1})
+    n_many = R.ret_chunkwise_workspace_bytes(1, 4096, 2, 64, 64, 64, torch.bfloat16, options={"segments": 32})
+    assert n_one == 0 and n_many > n_default > 0
+
+
+# The binding checks shapes and dtypes before it forms any device pointer, so mismatches are caught on CPU
+# tensors here (the device check would only come after).
+def _cpu_qkv(B=1, N=8, H=2, dk=16, dv=16, dt=None):
+    import torch
+    dt = dt or torch.float32
+    return (torch.zeros(B, N, H, dk, dtype=dt), torch.zeros(B, N, H, dk, dtype=dt), torch.zeros(B, N, H, dv, dtype=dt))
+
+
+@pytest.mark.parametrize("bad", ["k_shape", "v_heads", "o_shape", "mixed_dtype", "state_shape", "o_dtype"])
+def test_binding_rejects_mismatched_tensors(lib, bad):
+    import torch
+    from linear_recurrent_sequence_amd import retention as R
+    q, k, v = _cpu_qkv()
+    o = torch.zeros(1, 8, 2, 16)
+    state = None
+    if bad == "k_shape":
+        k = torch.zeros(1, 8, 2, 32)
+    elif bad == "v_heads":
+        v = torch.zeros(1, 8, 3, 16)
+    elif bad == "o_shape":
+        o = torch.zeros(1, 4, 2, 16)
+    elif bad == "mixed_dtype":
+        k = k.to(torch.bfloat16)
+    elif bad == "state_shape":
+        state = torch.zeros(1, 2, 16, 8)
+    elif bad == "o_dtype":
+        o = torch.zeros(1, 8, 2, 16, dtype=torch.float64)
+    with pytest.raises(ValueError):
+        R.ret_chunkwise_fwd(q, k, v, o, [0.9, 0.9], 16, state_out=state)
+
+
+def test_binding_rejects_mismatched_step_and_gradients(lib):
+    import torch
+    from linear_recurrent_sequence_amd import retention as R
+    q, k, v = (torch.zeros(2, 3, 16) for _ in range(3))
+    with pytest.raises(ValueError):  # o of a step is [B, H, d_v]
+        R.ret_recurrent_step(q, k, v, torch.zeros(2, 3, 8), torch.zeros(2, 3, 16, 16), [0.9] * 3, pos=0)
+    with pytest.raises(ValueError):  # missing state
+        R.ret_recurrent_step(q, k, v, torch.zeros(2, 3, 16), None, [0.9] * 3, pos=0)
+    q, k, v = _cpu_qkv()
+    with pytest.raises(ValueError):  # dv of the wrong shape
+        R.ret_chunkwise_bwd(q, k, v, torch.zeros_like(v), torch.zeros_like(q), torch.zeros_like(k),
+                            torch.zeros(1, 8, 2, 8), [0.9, 0.9], 16)

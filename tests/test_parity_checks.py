@@ -1,0 +1,186 @@
+"""GPU checks of properties that hold whatever the rounding ("RetNet" reading note, implementation checks:
+causal masking must not leak future tokens; and the chunkwise form's result does not depend on how the
+sequence is split): for every kernel family, outputs before a perturbed token are bitwise unchanged; the same
+inputs split into 1, the planner's and forced numbers of segments agree with each other and with the oracle;
+a state handed in and out through one buffer; and the segment chain's give-up path, forced from the host.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from linear_recurrent_sequence_amd import workloads as W
+from tests.conftest import print_case
+from tests.helpers import empty_out, rel_err, to_dev, to_host, tol
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def R():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from linear_recurrent_sequence_amd import retention
+    retention.load(build_if_missing=True)
+    return retention
+
+
+def _run(R, form, qd, kd, vd, dt, gamma, C, theta, options=None, state_in=None, state_out=None):
+    import torch
+    B, N, H, dk = qd.shape
+    dv = vd.shape[3]
+    o = empty_out((B, N, H, dv), dt)
+    if form == "parallel":
+        R.ret_parallel_fwd(qd, kd, vd, o, gamma, theta=theta)
+        ws = None
+    else:
+        ws = R.chunkwise_workspace(qd, vd, C, options)
+        R.ret_chunkwise_fwd(qd, kd, vd, o, gamma, C, theta=theta, workspace=ws, options=options,
+                            state_in=state_in, state_out=state_out)
+    torch.cuda.synchronize()
+    return o, ws
+
+
+# kernel families: (name, dtype, d_k, d_v, chunk, form, options)
+FAMILIES = [
+    ("onchip-dk64", "bf16", 64, 64, 64, "chunkwise", {"segments": 4}),
+    ("streaming-dk64", "bf16", 64, 128, 64, "chunkwise", {"segments": 3, "onchip": 0}),
+    ("streaming-dk128", "bf16", 128, 128, 128, "chunkwise", {"segments": 3}),
+    ("streaming-dk256", "bf16", 256, 256, 128, "chunkwise", {"segments": 2}),
+    ("prerotated-dk256", "bf16", 256, 512, 128, "chunkwise", {"segments": 2, "prerotate": 1}),
+    ("one-segment-dk128", "bf16", 128, 64, 64, "chunkwise", {"segments": 1}),
+    ("split-f32", "f32", 32, 32, 32, "chunkwise", {"segments": 3}),
+    ("parallel-bf16", "bf16", 64, 64, 0, "parallel", None),
+    ("parallel-f32", "f32", 32, 32, 0, "parallel", None),
+]
+
+
+@pytest.mark.parametrize("fam", FAMILIES, ids=lambda f: f[0])
+def test_no_leakage_from_later_tokens(R, fam):
+    """k and v of token t (mid-chunk, mid-segment) replaced by other values: every output row before t is
+    bitwise the same, and rows from t on differ."""
+    import torch
+    name, dt, dk, dv, C, form, opts = fam
+    B, N, H = 1, 700, 2
+    print_case("leakage", name)
+    rng = np.random.default_rng(5)
+    scale = 1.0 if dt == "f32" else 8.0
+    q = W.normal(rng, (B, N, H, dk), scale, dt)
+    k = W.normal(rng, (B, N, H, dk), scale, dt)
+    v = W.normal(rng, (B, N, H, dv), scale, dt)
+    gamma, theta = W.gamma_schedule(H), W.theta_schedule(dk)
+    for t in (37, 333, 650):
+        k2, v2 = k.copy(), v.copy()
+        k2[:, t] = W.normal(rng, (B, H, dk), scale, dt)
+        v2[:, t] = W.normal(rng, (B, H, dv), scale, dt)
+        qd = to_dev(q, dt)
+        o1, _ = _run(R, form, qd, to_dev(k, dt), to_dev(v, dt), dt, gamma, C, theta, opts)
+        o2, _ = _run(R, form, qd, to_dev(k2, dt), to_dev(v2, dt), dt, gamma, C, theta, opts)
+        assert torch.equal(o1[:, :t], o2[:, :t]), (name, t)
+        assert not torch.equal(o1[:, t:], o2[:, t:]), (name, t)
+
+
+@pytest.mark.parametrize("shape", [(2, 1500, 2, 64, 64, 64), (1, 1300, 2, 128, 128, 128), (1, 900, 2, 256, 512, 128),
+                                   (1, 600, 2, 32, 32, 32)], ids=lambda s: "dk%d-dv%d" % (s[3], s[4]))
+def test_segment_invariance(R, shape):
+    """One sequence split into 1 segment, the planner's, and forced counts (a group boundary included where the
+    length allows): every split matches the oracle, and the splits match each other to rounding."""
+    import torch
+    B, N, H, dk, dv, C = shape
+    dt = "f32" if dk == 32 else "bf16"
+    print_case("segment_invariance", shape)
+    rng = np.random.default_rng(11 + dk)
+    scale = 1.0 if dt == "f32" else 8.0
+    q = W.normal(rng, (B, N, H, dk), scale, dt)
+    k = W.normal(rng, (B, N, H, dk), scale, dt)
+    v = W.normal(rng, (B, N, H, dv), scale, dt)
+    s0 = rng.standard_normal((B, H, dk, dv)).astype(np.float32)
+    gamma, theta = W.gamma_schedule(H), W.theta_schedule(dk)
+    o_ref, s_ref = oracle.chunkwise(q, k, v, gamma, C, theta=theta, state_in=s0)
+    qd, kd, vd, sin = to_dev(q, dt), to_dev(k, dt), to_dev(v, dt), torch.from_numpy(s0).cuda()
+    nchunks = (N + C - 1) // C
+    outs = {}
+    for segs in sorted({1, 0, 2, 3, min(9, nchunks), nchunks}):
+        opts = {"segments": segs} if segs else None
+        sout = torch.empty((B, H, dk, dv), dtype=torch.float32, device="cuda")
+        o, ws = _run(R, "chunkwise", qd, kd, vd, dt, gamma, C, theta, opts, state_in=sin, state_out=sout)
+        R.ret_chunkwise_check(ws)
+        oh, sh = to_host(o), to_host(sout)
+        eo, es = rel_err(oh, o_ref), rel_err(sh, s_ref)
+        print("  segments=%s err o=%.3g state=%.3g" % (segs or "planner", eo, es))
+        assert eo <= tol(dt) and es <= tol(dt), (segs, eo, es)
+        outs[segs] = (oh, sh)
+    base = outs[1]
+    for segs, (oh, sh) in outs.items():
+        # two roundings of the same value apart at most: twice the bar against each other
+        assert rel_err(oh, base[0]) <= 2 * tol(dt) and rel_err(sh, base[1]) <= 2 * tol(dt), segs
+
+
+@pytest.mark.parametrize("case", [("dk128", 128, 128, 128, {"segments": 4}),
+                                  ("dk64-streaming", 64, 64, 64, {"segments": 4, "onchip": 0}),
+                                  ("dk64-onchip", 64, 64, 64, {"segments": 4}),
+                                  ("dk256", 256, 256, 128, {"segments": 3}),
+                                  ("f32-split", 32, 32, 32, {"segments": 3})], ids=lambda c: c[0])
+def test_state_out_may_be_state_in(R, case):
+    """state_out the same buffer as state_in, with several segments: the initial state is read before the final
+    state is written."""
+    import torch
+    name, dk, dv, C, opts = case
+    dt = "f32" if dk == 32 else "bf16"
+    B, N, H = 1, 1100, 2
+    print_case("state_alias", name)
+    rng = np.random.default_rng(3 + dk)
+    scale = 1.0 if dt == "f32" else 8.0
+    q = W.normal(rng, (B, N, H, dk), scale, dt)
+    k = W.normal(rng, (B, N, H, dk), scale, dt)
+    v = W.normal(rng, (B, N, H, dv), scale, dt)
+    s0 = rng.standard_normal((B, H, dk, dv)).astype(np.float32)
+    gamma, theta = W.gamma_schedule(H), W.theta_schedule(dk)
+    o_ref, s_ref = oracle.chunkwise(q, k, v, gamma, C, theta=theta, pos0=3, state_in=s0)
+    qd, kd, vd = to_dev(q, dt), to_dev(k, dt), to_dev(v, dt)
+    for _ in range(2):  # twice: the second call resumes nothing, it starts again from s0
+        state = torch.from_numpy(s0).cuda()
+        o = empty_out((B, N, H, dv), dt)
+        ws = R.chunkwise_workspace(qd, vd, C, opts)
+        R.ret_chunkwise_fwd(qd, kd, vd, o, gamma, C, theta=theta, pos0=3, state_in=state, state_out=state,
+                            workspace=ws, options=opts)
+        torch.cuda.synchronize()
+        R.ret_chunkwise_check(ws)
+        eo, es = rel_err(to_host(o), o_ref), rel_err(to_host(state), s_ref)
+        print("  err o=%.3g state=%.3g" % (eo, es))
+        assert eo <= tol(dt) and es <= tol(dt), (eo, es)
+
+
+@pytest.mark.parametrize("case", [("onchip-dk64", 64, 64, 64, {"segments": 4}),
+                                  ("streaming-dk128", 128, 128, 128, {"segments": 4})], ids=lambda c: c[0])
+def test_chain_give_up_is_visible(R, case):
+    """Every segment-chain wait made to give up at once (chain_spin < 0, set from the host; no kernel stalls):
+    the first segment's outputs are right, every later segment's outputs and the final state are NaN, and
+    ret_chunkwise_check reports it. The workspace then still serves a normal call, which is right."""
+    import torch
+    name, dk, dv, C, opts = case
+    B, N, H, segs = 1, 1024, 2, opts["segments"]
+    print_case("chain_give_up", name)
+    rng = np.random.default_rng(13)
+    q = W.normal(rng, (B, N, H, dk), 8.0, "bf16")
+    k = W.normal(rng, (B, N, H, dk), 8.0, "bf16")
+    v = W.normal(rng, (B, N, H, dv), 8.0, "bf16")
+    gamma, theta = W.gamma_schedule(H), W.theta_schedule(dk)
+    o_ref, s_ref = oracle.chunkwise(q, k, v, gamma, C, theta=theta)
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    ws = R.chunkwise_workspace(qd, vd, C, opts)
+    o = empty_out((B, N, H, dv), "bf16")
+    sout = torch.empty((B, H, dk, dv), dtype=torch.float32, device="cuda")
+    R.ret_chunkwise_fwd(qd, kd, vd, o, gamma, C, theta=theta, state_out=sout, workspace=ws,
+                        options=dict(opts, chain_spin=-1))
+    torch.cuda.synchronize()
+    with pytest.raises(R.RetentionError):
+        R.ret_chunkwise_check(ws)
+    oh, seg_len = to_host(o), N // segs
+    assert rel_err(oh[:, :seg_len], o_ref[:, :seg_len]) <= tol("bf16")
+    assert np.isnan(oh[:, seg_len:]).all()
+    assert np.isnan(to_host(sout)).all()
+    # the counters and flags were left at zero: a normal call on the same workspace is right
+    o2 = empty_out((B, N, H, dv), "bf16")
+    R.ret_chunkwise_fwd(qd, kd, vd, o2, gamma, C, theta=theta, state_out=sout, workspace=ws, options=opts)
+    torch.cuda.synchronize()
+    assert rel_err(to_host(o2), o_ref) <= tol("bf16") and rel_err(to_host(sout), s_ref) <= tol("bf16")

@@ -23,11 +23,12 @@ def R():
     return retention
 
 
-def _gpu_grad(R, q, k, v, do, gamma, chunk, theta, pos0, out_dt, workspace=None, in_dt="bf16"):
+def _gpu_grad(R, q, k, v, do, gamma, chunk, theta, pos0, out_dt, workspace=None, in_dt="bf16", options=None):
     import torch
     qd, kd, vd, dod = (to_dev(x, in_dt) for x in (q, k, v, do))
     dq, dk, dv = empty_out(q.shape, out_dt), empty_out(k.shape, out_dt), empty_out(v.shape, out_dt)
-    R.ret_chunkwise_bwd(qd, kd, vd, dod, dq, dk, dv, gamma, chunk, theta=theta, pos0=pos0, workspace=workspace)
+    R.ret_chunkwise_bwd(qd, kd, vd, dod, dq, dk, dv, gamma, chunk, theta=theta, pos0=pos0, workspace=workspace,
+                        options=options, check=workspace is None)
     torch.cuda.synchronize()
     return to_host(dq), to_host(dk), to_host(dv)
 
@@ -72,15 +73,14 @@ def test_gradients_small(R, case):
 
 
 @pytest.mark.parametrize("direct", ["1", "0"])
-def test_gradients_both_paths(R, direct, monkeypatch):
-    """The reversed-traversal path and the reordered-copies path (RET_BWD_DIRECT=0) on one shape."""
-    monkeypatch.setenv("RET_BWD_DIRECT", direct)
+def test_gradients_both_paths(R, direct):
+    """The reversed-traversal path and the reordered-copies path (bwd_direct 0) on one shape."""
     w = W.Workload("grad", B=3, N=900, H=2, dk=64, dv=64, dtype="bf16", scale=8.0, seed=43, chunk=64, rotate=True)
     print_case("gradients-path", direct, w)
     q, k, v, rng = W.make_qkv(w)
     do = W.make_dout(w, rng)
     ref = oracle.grad(q, k, v, do, w.gamma, theta=w.theta, pos0=2)
-    got = _gpu_grad(R, q, k, v, do, w.gamma, w.chunk, w.theta, 2, "bf16")
+    got = _gpu_grad(R, q, k, v, do, w.gamma, w.chunk, w.theta, 2, "bf16", options={"bwd_direct": int(direct)})
     _check(got, ref, tol("bf16"))
 
 

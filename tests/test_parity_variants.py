@@ -137,10 +137,10 @@ def _steps_per_position(q, k, v, gamma, theta, s0, pos):
 @pytest.mark.parametrize("pairs", ["0", "2"])
 @pytest.mark.parametrize("dt,dk,dv", [("f32", 16, 16), ("f32", 64, 36), ("bf16", 64, 64), ("bf16", 128, 128),
                                       ("bf16", 256, 200)])
-def test_step_per_sequence_positions(R, dt, dk, dv, pairs, monkeypatch):
+def test_step_per_sequence_positions(R, dt, dk, dv, pairs):
     import torch
     print_case("step_positions", dt, dk, dv, pairs)
-    monkeypatch.setenv("RET_STEP_PAIRS", pairs)
+    opts = {"step_pairs": int(pairs)}
     rng = np.random.default_rng(21)
     B, H = 6, 3
     pos = np.array([0, 5, 100, 65536, 3, 1 << 30], np.int64)
@@ -154,7 +154,7 @@ def test_step_per_sequence_positions(R, dt, dk, dv, pairs, monkeypatch):
     state = torch.from_numpy(s0).cuda()
     o = empty_out((B, H, dv), dt)
     R.ret_recurrent_step_positions(to_dev(q, dt), to_dev(k, dt), to_dev(v, dt), o, state, gamma,
-                                   torch.from_numpy(pos).cuda(), theta=theta)
+                                   torch.from_numpy(pos).cuda(), theta=theta, options=opts)
     torch.cuda.synchronize()
     eo, es = rel_err(to_host(o), o_ref), rel_err(to_host(state), s_ref)
     print("  err o=%.3g state=%.3g" % (eo, es))
