@@ -83,7 +83,8 @@ ret_status_t ret_parallel_fwd(const void* q, const void* k, const void* v, void*
  *    segment is built from the end states of the segments before it (a scan of the chunk state over
  *    segments; BF16 input: counters, flags and two d_k x 64 fp32 slots per segment and d_v tile of 64);
  *  - BF16 input with rotation and d_v >= 256: bf16 copies of q and k rotated once (2 * B*N*H*d_k*2 bytes),
- *    so the d_v tiles of a head do not each rotate the same rows.
+ *    so the d_v tiles of a head do not each rotate the same rows. They start past the chain's first 64 KB
+ *    (header, counters, flags), which are reserved even when the plan has a single segment.
  * 0 means the call runs one segment per (b, h) and needs none. A smaller workspace is allowed: the call then
  * first drops the rotated copies, then uses fewer segments; the results are the same up to rounding order.
  * The workspace must be zero-filled before its first use. Every call leaves it in a state the next call
@@ -219,7 +220,8 @@ ret_status_t ret_chunkwise_bwd(const void* q, const void* k, const void* v, cons
  * returns the total milliseconds and launch count recorded for kernels whose name equals `kernel` ("" or NULL =
  * all). Kernel names: "ret_chunk_seg", "ret_chunk_fused" and "ret_rotate_qk" (bf16 input), "ret_chunk_full",
  * "ret_chunk_local", "ret_segment_scan" (fp32 input), "ret_parallel", "ret_recurrent_step", "ret_msr_epilogue",
- * "ret_permute_rotate" (gradients), "ret_norm_rows" (score normalization). A timer must not be attached to
+ * "ret_permute_rotate" (gradients), "ret_norm_zseg", "ret_norm_rows", "ret_norm_scale", "ret_norm_step" (score
+ * normalizations). A timer must not be attached to
  * calls that are being captured into a graph. One timer may be shared by calls on several threads.
  */
 typedef struct ret_timer ret_timer_t;
@@ -289,6 +291,51 @@ ret_status_t ret_recurrent_step_positions_ex(const void* q, const void* k, const
                                              int B, int H, int dk, int dv, ret_dtype_t in_dt, ret_dtype_t out_dt,
                                              const float* gamma, const double* theta, const int64_t* pos,
                                              void* stream, const ret_options_t* opts);
+
+/*
+ * Retention score normalizations ("Hybrid Architectures: RetNet and the Three Computation Paradigms", section
+ * 8.5; RetNet paper summary, "Retention Score Normalization"), selected by `norm` (any combination, 0 = none):
+ *   RET_NORM_SCALE   scores Q K^T divided by sqrt(d_k)
+ *   RET_NORM_DECAY   each row of the decay matrix divided by the square root of its sum, sum_{i<=p} gamma^i
+ *   RET_NORM_SCORES  each row of the (scaled) scores divided by max(|row sum|, 1)
+ * The pages state them for the parallel form. Each is a positive factor per output row, so the normalized
+ * output of the row at absolute position p is the plain one times c_p / den_p, with c_p the product of the
+ * first two factors and den_p = max(|c_p q'_p . z_p|, 1) under RET_NORM_SCORES, where z_p = gamma z_{p-1} + k'_p
+ * is the decayed sum of the rotated keys (q'_p . z_p is the row sum of the scores). Rows refer to the whole
+ * sequence from its first token at position 0: a call that resumes at pos0 passes the key sum z [B, H, d_k]
+ * (fp32) of the tokens before it, as it passes the state. GroupNorm cancels every factor (section 8.4).
+ */
+#define RET_NORM_SCALE 1
+#define RET_NORM_DECAY 2
+#define RET_NORM_SCORES 4
+
+/*
+ * Chunkwise form (as ret_chunkwise_fwd, options as the _ex calls) with the score normalizations. z_in: the key
+ * sum before token 0 ([B, H, d_k] fp32 device, or NULL = zeros); z_out: the key sum after the last token (or
+ * NULL; may equal z_in). pos0 >= 0. The workspace is required: ret_chunkwise_normalized_workspace_bytes (0 for
+ * an unsupported shape) bytes, zero-filled before first use like the chunkwise workspace. Supported: as
+ * ret_chunkwise_fwd. RET_ERR_INVALID_ARG also for norm outside 0..7 and misaligned z buffers,
+ * RET_ERR_WORKSPACE for a missing or short workspace. Kernels: the chunkwise kernels, then "ret_norm_zseg",
+ * "ret_segment_scan", "ret_norm_rows" and "ret_norm_scale" (the output scaled in place).
+ */
+size_t ret_chunkwise_normalized_workspace_bytes(int B, int N, int H, int dk, int dv, int chunk, ret_dtype_t in_dt,
+                                                const ret_options_t* opts);
+ret_status_t ret_chunkwise_normalized_fwd(const void* q, const void* k, const void* v, void* o, int B, int N, int H,
+                                          int dk, int dv, ret_dtype_t in_dt, ret_dtype_t out_dt, const float* gamma,
+                                          const double* theta, int64_t pos0, int chunk, int norm,
+                                          const float* state_in, float* state_out, const float* z_in, float* z_out,
+                                          void* workspace, size_t workspace_bytes, void* stream,
+                                          const ret_options_t* opts);
+
+/*
+ * One decode step (as ret_recurrent_step) with the score normalizations: the state S and the key sum z
+ * ([B, H, d_k] fp32 device, required) are both updated in place, S <- gamma S + k'^T v, z <- gamma z + k', and
+ * o = c_p (q' S) / den_p at position p = pos >= 0. Kernels: "ret_recurrent_step", then "ret_norm_step".
+ */
+ret_status_t ret_recurrent_step_normalized(const void* q, const void* k, const void* v, void* o, float* state,
+                                           float* z, int B, int H, int dk, int dv, ret_dtype_t in_dt,
+                                           ret_dtype_t out_dt, const float* gamma, const double* theta, int64_t pos,
+                                           int norm, void* stream, const ret_options_t* opts);
 
 #ifdef __cplusplus
 }

@@ -216,7 +216,10 @@ ChunkPlan plan_chunk(const ChunkKernels& ck, int B, int N, int H, int dk, int dv
     const int pre = op.prerotate;
     if (ck.fused_pre && rotate && (pre < 0 ? dv / ck.dvt >= 4 : pre != 0))
         p.rot_bytes = 2 * (((size_t)B * N * H * dk * 2 + 255) / 256 * 256);
-    if (p.chain_bytes + p.rot_bytes > avail) p.rot_bytes = 0;
+    // The rotated copies follow the chain's header, counters and flags (the first kChainMeta bytes) even when
+    // the plan has no chain, so that those stay zero for any later call that shares the workspace.
+    auto chain_part = [&](size_t chain) { return p.rot_bytes > 0 && chain < kChainMeta ? kChainMeta : chain; };
+    if (chain_part(p.chain_bytes) + p.rot_bytes > avail) p.rot_bytes = 0;
     while (p.nseg > 1 && segment_ws_bytes(ck, B, H, dk, dv, p.nseg) > avail) {
         const int nchunks = (N + chunk - 1) / chunk;
         int spc = p.seg_len / chunk * 2;
@@ -229,6 +232,7 @@ ChunkPlan plan_chunk(const ChunkKernels& ck, int B, int N, int H, int dk, int dv
         p.seg_len = N;
         p.chain_bytes = 0;
     }
+    p.chain_bytes = chain_part(p.chain_bytes);
     return p;
 }
 
@@ -876,6 +880,179 @@ ret_status_t ret_chunkwise_bwd_ex(const void* q, const void* k, const void* v, c
         {G2, {dv_out, nullptr}, dv, 0, 1, {0, 0}, 0, ob},
     };
     return permute(post, 3, B, N, H, theta, pos0, s, op);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Workspace of the normalized chunkwise call: the chunkwise plan's workspace, then the normalization's segment
+// sums W [B*H][nseg][d_k] and row factors f [B*N*H] (fp32).
+struct NormLayout {
+    size_t chunk_bytes, w_off, f_off, total;
+    int nseg;
+};
+bool norm_layout(int B, int N, int H, int dk, int dv, int chunk, ret_dtype_t in_dt, const Opts& op, NormLayout* L) {
+    ChunkKernels ck;
+    NormKernels nk;
+    if (B <= 0 || N <= 0 || H <= 0 || dk <= 0 || dv <= 0 || chunk <= 0) return false;
+    if (!pick_chunk(in_dt, dk, dv, chunk, &ck, op) || !norm_kernels_get(in_dt == RET_BF16, dk, &nk)) return false;
+    const ChunkPlan p = plan_chunk(ck, B, N, H, dk, dv, chunk, true, SIZE_MAX, op);
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    L->nseg = (N + kNormSegTokens - 1) / kNormSegTokens;
+    L->chunk_bytes = up(p.chain_bytes + p.rot_bytes);
+    L->w_off = L->chunk_bytes;
+    L->f_off = L->w_off + up((size_t)B * H * L->nseg * dk * 4);
+    L->total = L->f_off + up((size_t)B * N * H * 4);
+    return true;
+}
+
+void fill_norm(NormArgs& A, const void* q, const void* k, void* o, int B, int N, int H, int dk, int dv,
+               ret_dtype_t in_dt, ret_dtype_t out_dt, const float* gamma, const double* theta, int64_t pos, int norm,
+               const float* z_in, float* z_out) {
+    memset(&A, 0, sizeof(A));
+    A.q = q;
+    A.k = k;
+    A.o = o;
+    A.z_in = z_in;
+    A.z_out = z_out;
+    A.B = B;
+    A.N = N;
+    A.H = H;
+    A.dk = dk;
+    A.dv = dv;
+    A.in_bf16 = in_dt == RET_BF16;
+    A.out_bf16 = out_dt == RET_BF16;
+    A.norm = norm;
+    A.rotate = theta != nullptr;
+    A.pos0 = pos;
+    for (int h = 0; h < H; ++h) {
+        A.gamma[h] = gamma[h];
+        A.lng[h] = log((double)gamma[h]);
+    }
+    if (theta)
+        for (int i = 0; i < dk / 2; ++i) A.theta[i] = theta[i];
+}
+
+ret_status_t check_norm(int norm, const float* z_in, const float* z_out) {
+    if (norm < 0 || norm > 7) return fail(RET_ERR_INVALID_ARG, "norm flags %d outside 0..7", norm);
+    if ((z_in && !aligned16(z_in)) || (z_out && !aligned16(z_out)))
+        return fail(RET_ERR_INVALID_ARG, "z buffers must be 16-byte aligned");
+    return RET_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ret_chunkwise_normalized_workspace_bytes(int B, int N, int H, int dk, int dv, int chunk, ret_dtype_t in_dt,
+                                                const ret_options_t* opts) {
+    NormLayout L;
+    if (!norm_layout(B, N, H, dk, dv, chunk, in_dt, resolve(opts), &L)) return 0;
+    return L.total;
+}
+
+ret_status_t ret_chunkwise_normalized_fwd(const void* q, const void* k, const void* v, void* o, int B, int N, int H,
+                                          int dk, int dv, ret_dtype_t in_dt, ret_dtype_t out_dt, const float* gamma,
+                                          const double* theta, int64_t pos0, int chunk, int norm,
+                                          const float* state_in, float* state_out, const float* z_in, float* z_out,
+                                          void* workspace, size_t workspace_bytes, void* stream,
+                                          const ret_options_t* opts) {
+    const Opts op = resolve(opts);
+    ret_status_t st = check_common(q, k, v, o, B, N, H, dk, dv, in_dt, out_dt, gamma, theta);
+    if (st != RET_OK) return st;
+    if ((st = check_norm(norm, z_in, z_out)) != RET_OK) return st;
+    if (pos0 < 0) return fail(RET_ERR_INVALID_ARG, "normalized forms need pos0 >= 0 (got %lld)", (long long)pos0);
+    if (chunk <= 0) return fail(RET_ERR_INVALID_ARG, "chunk must be positive (got %d)", chunk);
+    NormLayout L;
+    if (!norm_layout(B, N, H, dk, dv, chunk, in_dt, op, &L))
+        return fail(RET_ERR_UNSUPPORTED, "normalized chunkwise form: unsupported d_k=%d d_v=%d chunk=%d", dk, dv,
+                    chunk);
+    if (!workspace || workspace_bytes < L.total)
+        return fail(RET_ERR_WORKSPACE, "the normalized chunkwise form needs a workspace of %zu bytes (got %zu)",
+                    L.total, workspace_bytes);
+    if (!aligned16(workspace)) return fail(RET_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    NormKernels nk;
+    norm_kernels_get(in_dt == RET_BF16, dk, &nk);
+    // the plain chunkwise output and state
+    st = chunkwise_run(q, k, v, o, B, N, H, dk, dv, in_dt, out_dt, gamma, theta, pos0, chunk, state_in, state_out,
+                       workspace, L.chunk_bytes, stream, nullptr, nullptr, op);
+    if (st != RET_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    NormArgs A;
+    fill_norm(A, q, k, o, B, N, H, dk, dv, in_dt, out_dt, gamma, theta, pos0, norm, z_in, z_out);
+    A.W = (float*)((char*)workspace + L.w_off);
+    A.f = (float*)((char*)workspace + L.f_off);
+    A.nseg = L.nseg;
+    A.seg_len = kNormSegTokens;
+    if (L.nseg > 1) {
+        LaunchTimer tm("ret_norm_zseg", s, op);
+        hipLaunchKernelGGL(nk.zseg, dim3(L.nseg - 1, B * H), dim3(64), 0, s, A);
+        tm.done();
+        if ((st = launch_status("ret_norm_zseg")) != RET_OK) return st;
+    }
+    {
+        // the sums entering the segments: W[0] = z_in, W[g] = gamma^T W[g-1] + W[g] (the segment scan, d_v = 1)
+        FwdArgs F;
+        memset(&F, 0, sizeof(F));
+        F.B = B;
+        F.N = N;
+        F.H = H;
+        F.dk = dk;
+        F.dv = 1;
+        F.nseg = L.nseg;
+        F.seg_len = kNormSegTokens;
+        F.state_in = z_in;
+        F.ws = A.W;
+        for (int h = 0; h < H; ++h) F.log2g[h] = (float)log2((double)gamma[h]);
+        LaunchTimer tm("ret_segment_scan", s, op);
+        hipLaunchKernelGGL(segment_scan_get(), dim3((unsigned)((dk / 4 + kThreads - 1) / kThreads), B * H),
+                           dim3(kThreads), 0, s, F);
+        tm.done();
+        if ((st = launch_status("ret_segment_scan")) != RET_OK) return st;
+    }
+    {
+        LaunchTimer tm("ret_norm_rows", s, op);
+        hipLaunchKernelGGL(nk.rows, dim3(L.nseg, B * H), dim3(64), 0, s, A);
+        tm.done();
+        if ((st = launch_status("ret_norm_rows")) != RET_OK) return st;
+    }
+    const long long groups = (long long)B * N * H * dv / 8;
+    LaunchTimer tm("ret_norm_scale", s, op);
+    hipLaunchKernelGGL(nk.scale, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, s, A);
+    tm.done();
+    return launch_status("ret_norm_scale");
+}
+
+ret_status_t ret_recurrent_step_normalized(const void* q, const void* k, const void* v, void* o, float* state,
+                                           float* z, int B, int H, int dk, int dv, ret_dtype_t in_dt,
+                                           ret_dtype_t out_dt, const float* gamma, const double* theta, int64_t pos,
+                                           int norm, void* stream, const ret_options_t* opts) {
+    const Opts op = resolve(opts);
+    ret_status_t st = check_common(q, k, v, o, B, 1, H, dk, dv, in_dt, out_dt, gamma, theta);
+    if (st != RET_OK) return st;
+    if (!z) return fail(RET_ERR_INVALID_ARG, "null z (the normalized step carries the key sum)");
+    if ((st = check_norm(norm, z, z)) != RET_OK) return st;
+    if (pos < 0) return fail(RET_ERR_INVALID_ARG, "normalized forms need pos >= 0 (got %lld)", (long long)pos);
+    NormKernels nk;
+    if (!norm_kernels_get(in_dt == RET_BF16, dk, &nk))
+        return fail(RET_ERR_UNSUPPORTED, "normalized decode step: d_k=%d", dk);
+    if ((st = step_run(q, k, v, o, state, B, H, dk, dv, in_dt, out_dt, gamma, theta, pos, nullptr, stream, op)) !=
+        RET_OK)
+        return st;
+    NormArgs A;
+    fill_norm(A, q, k, o, B, 1, H, dk, dv, in_dt, out_dt, gamma, theta, pos, norm, z, z);
+    if (theta)
+        for (int i = 0; i < dk / 2; ++i) {
+            const double ang = (double)pos * theta[i];
+            A.rc[i] = (float)cos(ang);
+            A.rs[i] = (float)sin(ang);
+        }
+    hipStream_t s = (hipStream_t)stream;
+    LaunchTimer tm("ret_norm_step", s, op);
+    hipLaunchKernelGGL(nk.step, dim3(B * H), dim3(64), 0, s, A);
+    tm.done();
+    return launch_status("ret_norm_step");
 }
 
 ret_timer_t* ret_timer_create(void) { return new (std::nothrow) ret_timer(); }

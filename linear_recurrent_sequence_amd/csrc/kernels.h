@@ -1036,4 +1036,35 @@ zero_kernel_t zero_words_get();
 // Kernel for d_v in {16, 32, 64, 128, 256, 512} (null otherwise) and its groups per 256-thread workgroup.
 epi_kernel_t epilogue_kernel_get(int dv, int* groups_per_wg);
 
+// Retention score normalizations carried through the decayed key sum z_p = gamma z_{p-1} + k'_p: each output
+// row p is the plain row times c_p / den_p, c_p = (1/sqrt(d_k)) (1/sqrt(sum_{i<=p} gamma^i)) for the selected
+// factors, den_p = max(|c_p q'_p . z_p|, 1) when the scores are normalized.
+struct NormArgs {
+    const void* q;       // [B, N, H, dk] (a decode step: [B, H, dk])
+    const void* k;
+    void* o;             // [B, N, H, dv] (a step: [B, H, dv]), scaled in place
+    const float* z_in;   // [B, H, dk] or null (zero)
+    float* z_out;        // [B, H, dk] or null
+    float* W;            // [B*H][nseg][dk]: local end sums of the segments, then the sums entering them
+    float* f;            // [B*N*H] row factors
+    int B, N, H, dk, dv;
+    int nseg, seg_len;   // the normalization's own segments of the sequence
+    int in_bf16, out_bf16, norm, rotate;
+    long long pos0;      // absolute position of token 0 (a step: its position)
+    float gamma[kMaxHeads];
+    double lng[kMaxHeads];           // ln(gamma) in fp64, for the decay row sums
+    double theta[kMaxPairs];         // chunkwise: rotation frequencies
+    float rc[kMaxPairs], rs[kMaxPairs];  // a step: cos and sin of pos * theta_i from the host
+};
+constexpr int kNormSegTokens = 256;  // tokens per segment of the chunkwise normalization pass
+typedef void (*norm_kernel_t)(NormArgs);
+// The normalization kernels for the input dtype and d_k (d_k even, <= 256; null otherwise): the local end sums
+// of the segments (one 64-thread workgroup per (segment, b*H + h) for segments 0 .. nseg-2), the row factors (one
+// per (segment, b*H + h)), the row scaling (256-thread workgroups over B*N*H*d_v / 8 groups of 8 values), and
+// the decode step's factor and key sum update (one 64-thread workgroup per (b, h)).
+struct NormKernels {
+    norm_kernel_t zseg, rows, scale, step;
+};
+bool norm_kernels_get(bool bf16_in, int dk, NormKernels* out);
+
 }  // namespace ret

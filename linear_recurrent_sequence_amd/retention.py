@@ -18,6 +18,7 @@ import torch
 from . import build as _build
 
 RET_F32, RET_BF16 = 0, 1
+RET_NORM_SCALE, RET_NORM_DECAY, RET_NORM_SCORES = 1, 2, 4
 _STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "workspace", -4: "hip error"}
 
 _lib = None
@@ -161,6 +162,14 @@ def load(build_if_missing: bool = True):
     lib.ret_recurrent_step_ex.restype = i32
     lib.ret_recurrent_step_positions_ex.argtypes = lib.ret_recurrent_step_positions.argtypes + [op]
     lib.ret_recurrent_step_positions_ex.restype = i32
+    lib.ret_chunkwise_normalized_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32, op]
+    lib.ret_chunkwise_normalized_workspace_bytes.restype = sz
+    lib.ret_chunkwise_normalized_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, fp, dp, i64, i32,
+                                                 i32, vp, vp, vp, vp, vp, sz, vp, op]
+    lib.ret_chunkwise_normalized_fwd.restype = i32
+    lib.ret_recurrent_step_normalized.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, fp, dp, i64,
+                                                  i32, vp, op]
+    lib.ret_recurrent_step_normalized.restype = i32
     lib.ret_options_default.argtypes = [op]
     lib.ret_options_default.restype = None
     lib.ret_timer_create.restype = vp
@@ -452,3 +461,69 @@ def ret_chunkwise_bwd(q, k, v, dout, dq, dk, dv, gamma, chunk, theta=None, pos0=
     if check:
         ret_chunkwise_check(workspace, stream)
     return dq, dk, dv
+
+
+def norm_flags(scale=False, decay=False, scores=False) -> int:
+    """RET_NORM_* flags: scores / sqrt(d_k), decay rows divided by the root of their sums, scores rows divided by
+    max(|row sum|, 1)."""
+    return (RET_NORM_SCALE if scale else 0) | (RET_NORM_DECAY if decay else 0) | (RET_NORM_SCORES if scores else 0)
+
+
+def chunkwise_normalized_workspace(q, v, chunk, options=None):
+    """A zero-filled workspace of ret_chunkwise_normalized_workspace_bytes for these shapes."""
+    B, N, H, dk = q.shape
+    nbytes = load().ret_chunkwise_normalized_workspace_bytes(B, N, H, dk, v.shape[3], int(chunk), _dt(q),
+                                                             _options(options))
+    if nbytes == 0:
+        raise ValueError("normalized chunkwise form: unsupported shape")
+    return torch.zeros((nbytes,), dtype=torch.uint8, device=q.device)
+
+
+def ret_chunkwise_normalized_fwd(q, k, v, o, gamma, chunk, norm, theta=None, pos0=0, state_in=None, state_out=None,
+                                 z_in=None, z_out=None, workspace=None, stream=None, options=None):
+    """o <- chunkwise retention with the score normalizations `norm` (RET_NORM_* flags); the state and the key
+    sum z [B,H,dk] are carried in and out."""
+    lib = load()
+    _qkv(q, k, v)
+    B, N, H, dk = q.shape
+    dv = v.shape[3]
+    _shape(o, "o", (B, N, H, dv), _IO)
+    for name, t in (("state_in", state_in), ("state_out", state_out)):
+        _shape(t, name, (B, H, dk, dv), (torch.float32,))
+    for name, t in (("z_in", z_in), ("z_out", z_out)):
+        _shape(t, name, (B, H, dk), (torch.float32,))
+    _same_device(q, k, v, o, state_in, state_out, z_in, z_out, workspace)
+    g, gp = _gamma(gamma, H)
+    th, tp = _theta(theta, dk)
+    if workspace is None:
+        workspace = chunkwise_normalized_workspace(q, v, chunk, options)
+    wsb = workspace.numel() * workspace.element_size()
+    st = lib.ret_chunkwise_normalized_fwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"), B, N, H, dk, dv,
+                                          _dt(q), _dt(o), gp, tp, int(pos0), int(chunk), int(norm),
+                                          _dev(state_in, "state_in"), _dev(state_out, "state_out"),
+                                          _dev(z_in, "z_in"), _dev(z_out, "z_out"), _dev(workspace, "workspace"), wsb,
+                                          _stream(stream), _options(options))
+    _check("ret_chunkwise_normalized_fwd", st)
+    return o
+
+
+def ret_recurrent_step_normalized(q, k, v, o, state, z, gamma, pos, norm, theta=None, stream=None, options=None):
+    """One decode step with the score normalizations: state and z [B,H,dk] updated in place, o <- normalized
+    q' state."""
+    lib = load()
+    _qkv(q, k, v, step=True)
+    B, H, dk = q.shape
+    dv = v.shape[2]
+    _shape(o, "o", (B, H, dv), _IO)
+    if state is None or z is None:
+        raise ValueError("state [B,H,dk,dv] and z [B,H,dk] (float32) are required")
+    _shape(state, "state", (B, H, dk, dv), (torch.float32,))
+    _shape(z, "z", (B, H, dk), (torch.float32,))
+    _same_device(q, k, v, o, state, z)
+    g, gp = _gamma(gamma, H)
+    th, tp = _theta(theta, dk)
+    st = lib.ret_recurrent_step_normalized(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"),
+                                           _dev(state, "state"), _dev(z, "z"), B, H, dk, dv, _dt(q), _dt(o), gp, tp,
+                                           int(pos), int(norm), _stream(stream), _options(options))
+    _check("ret_recurrent_step_normalized", st)
+    return o

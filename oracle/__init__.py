@@ -54,8 +54,9 @@ def _load():
     lib.orc_parallel_normalized.argtypes = [P, P, P, P, I, I, I, I, I, P, P, LL, I, I]
     lib.orc_msr_epilogue.argtypes = [P, P, P, P, P, LL, I, I, ctypes.c_double]
     lib.orc_grad.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P, P, LL, I]
+    lib.orc_normalized.argtypes = [P, P, P, P, I, I, I, I, I, P, P, LL, I, I, P, P, P, P, I]
     for f in (lib.orc_parallel, lib.orc_parallel_rows, lib.orc_recurrent, lib.orc_chunkwise,
-              lib.orc_parallel_normalized, lib.orc_msr_epilogue, lib.orc_grad):
+              lib.orc_parallel_normalized, lib.orc_msr_epilogue, lib.orc_grad, lib.orc_normalized):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -200,3 +201,35 @@ def chunkwise(q, k, v, gamma, chunk, theta=None, pos0=0, state_in=None, threads=
                                int(pos0), int(chunk), _ptr(s_in), _ptr(s_out), threads or default_threads())
     _check(rc, "chunkwise")
     return o, s_out
+
+
+def _norm_flags(scale, decay, scores):
+    return (1 if scale else 0) | (2 if decay else 0) | (4 if scores else 0)
+
+
+def normalized(q, k, v, gamma, chunk=0, theta=None, pos0=0, scale=False, decay=False, scores=False,
+               state_in=None, z_in=None, threads=None):
+    """Recurrent (chunk 0) or chunkwise (chunk > 0) form with the score normalizations, carrying the state S
+    [B,H,dk,dv] and the decayed key sum z [B,H,dk] (see the C file for the reading); returns (O, S, z)."""
+    q, k, v, g, th, (B, N, H, dk, dv) = _common(q, k, v, gamma, theta)
+    o = np.zeros((B, N, H, dv), np.float64)
+    s_in = None if state_in is None else _f64(state_in)
+    zi = None if z_in is None else _f64(z_in)
+    if s_in is not None and s_in.shape != (B, H, dk, dv):
+        raise ValueError("state_in must be [B,H,dk,dv]")
+    if zi is not None and zi.shape != (B, H, dk):
+        raise ValueError("z_in must be [B,H,dk]")
+    s_out = np.zeros((B, H, dk, dv), np.float64)
+    z_out = np.zeros((B, H, dk), np.float64)
+    rc = _load().orc_normalized(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, N, H, dk, dv, _ptr(g), _ptr(th), int(pos0),
+                                int(chunk), _norm_flags(scale, decay, scores), _ptr(s_in), _ptr(s_out), _ptr(zi),
+                                _ptr(z_out), threads or default_threads())
+    _check(rc, "normalized")
+    return o, s_out, z_out
+
+
+def normalized_step(q, k, v, gamma, state, z, pos, theta=None, scale=False, decay=False, scores=False):
+    """One normalized decode step at absolute position ``pos``: q, k [B,H,dk], v [B,H,dv]; returns (o, S, z)."""
+    o, s, zz = normalized(_f64(q)[:, None], _f64(k)[:, None], _f64(v)[:, None], gamma, 0, theta=theta, pos0=pos,
+                          scale=scale, decay=decay, scores=scores, state_in=state, z_in=z)
+    return o[:, 0], s, zz

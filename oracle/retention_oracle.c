@@ -12,7 +12,8 @@
  *   - the chunkwise form  O_[i] = (Q_[i] K_[i]^T (.) D) V_[i] + (Q_[i] R_{i-1}) (.) xi,
  *                         R_i = gamma^L R_{i-1} + K_[i]^T (V_[i] (.) zeta);
  *   - the parallel form with the retention score normalizations (blog section 8.5; paper summary,
- *     "Retention Score Normalization"): QK^T / sqrt(d_k), D~ and R~;
+ *     "Retention Score Normalization"): QK^T / sqrt(d_k), D~ and R~; and the recurrent and chunkwise forms
+ *     with the same normalizations, carried through the decayed key sum z (reading below);
  *   - the multi-scale retention epilogue (blog sections 8.4 and 9.1; paper summary, "Gating mechanism"):
  *     y = swish(g) (.) GroupNorm_h(o), with g = X W_G given;
  *   - the gradients of the recurrent form from a zero state (the pages train with the chunkwise form, paper
@@ -102,14 +103,15 @@ static double* out_row(double* o, int N, int H, int dv, int b, int n, int h) {
 /* ------------------------------------------------------------------------------------------------ */
 
 typedef struct {
-    const double *q, *k, *v, *gamma, *theta, *s_in;
-    double *o, *s_out;
+    const double *q, *k, *v, *gamma, *theta, *s_in, *z_in;
+    double *o, *s_out, *z_out;
     const long long* rows;
     int nrows;
     int B, N, H, dk, dv, chunk;
     long long pos0;
-    int form; /* 0 parallel, 1 recurrent, 2 chunkwise, 3 parallel rows, 4 normalized parallel */
-    int norm; /* normalized parallel form: ORC_NORM_* flags */
+    int form; /* 0 parallel, 1 recurrent, 2 chunkwise, 3 parallel rows, 4 normalized parallel,
+                 6 normalized recurrent, 7 normalized chunkwise */
+    int norm; /* normalized forms: ORC_NORM_* flags */
     const double* dout; /* gradients (form 5): dO [B][N][H][dv] in, dq, dk, dv out */
     double *dq, *dk_, *dv_;
     int nthreads, tid;
@@ -122,6 +124,8 @@ static int form_chunkwise(job* J, int b, int h);
 static int form_parallel_rows(job* J, int b, int h);
 static int form_parallel_norm(job* J, int b, int h);
 static int form_grad(job* J, int b, int h);
+static int form_recurrent_norm(job* J, int b, int h);
+static int form_chunkwise_norm(job* J, int b, int h);
 
 static void* worker(void* arg) {
     job* J = (job*)arg;
@@ -134,6 +138,8 @@ static void* worker(void* arg) {
             case 2: rc = form_chunkwise(J, b, h); break;
             case 4: rc = form_parallel_norm(J, b, h); break;
             case 5: rc = form_grad(J, b, h); break;
+            case 6: rc = form_recurrent_norm(J, b, h); break;
+            case 7: rc = form_chunkwise_norm(J, b, h); break;
             default: rc = form_parallel_rows(J, b, h); break;
         }
         if (rc) J->status = rc;
@@ -449,6 +455,120 @@ static int form_chunkwise(job* J, int b, int h) {
 }
 
 /* ------------------------------------------------------------------------------------------------ */
+/* Score normalizations through a carried state. The pages define them on the parallel form only (blog */
+/* section 8.5; paper summary, "Retention Score Normalization"). Reading: each refers to the whole      */
+/* sequence from its first token, so row n of a call that starts at absolute position pos0 is row       */
+/* p = pos0 + n of the sequence, and                                                                  */
+/*   c_p  = (scale ? 1/sqrt(d_k) : 1) * (decay ? 1/sqrt(sum_{i<=p} D[p][i]) : 1),                     */
+/*          sum_{i<=p} D[p][i] = sum_{m=0}^{p} gamma^(p-m)                                            */
+/*   r_p  = sum_{m<=p} c_p gamma^(p-m) (q'_p . k'_m) = c_p (q'_p . z_p),   z_p = gamma z_{p-1} + k'_p  */
+/*   o~_p = c_p o_p / (scores ? max(|r_p|, 1) : 1),   o_p the plain retention output.                 */
+/* z (d_k values per (b, h)) is the decayed sum of the rotated keys; z_in is z before the call's first */
+/* token (NULL: zero, a fresh sequence).                                                              */
+/* ------------------------------------------------------------------------------------------------ */
+
+/* Row p's sum of the decay matrix, sum_{m=0}^{p} gamma^(p-m), written out term by term. */
+static double decay_row_sum(double g, long long p) {
+    double s = 0.0;
+    for (long long m = 0; m <= p; ++m) s += pow(g, (double)(p - m));
+    return s;
+}
+
+/* The factor c_p / den_p that turns the plain output of row p into the normalized one, given q'_p . z_p. */
+static double norm_row_factor(int norm, int dk, double g, long long p, double qz) {
+    double c = 1.0;
+    if (norm & ORC_NORM_SCALE) c /= sqrt((double)dk);
+    if (norm & ORC_NORM_DECAY) c /= sqrt(decay_row_sum(g, p));
+    double den = 1.0;
+    if (norm & ORC_NORM_SCORES) {
+        const double r = c * qz;
+        den = fabs(r) > 1.0 ? fabs(r) : 1.0;
+    }
+    return c / den;
+}
+
+/* Recurrent form with the normalizations: S <- gamma S + k'^T v, z <- gamma z + k', o = c (q' S) / den. */
+static int form_recurrent_norm(job* J, int b, int h) {
+    const int N = J->N, H = J->H, dk = J->dk, dv = J->dv;
+    const double g = J->gamma[h];
+    double* S = (double*)calloc((size_t)dk * dv, sizeof(double));
+    double* z = (double*)calloc((size_t)dk, sizeof(double));
+    double* qr = (double*)malloc(sizeof(double) * dk);
+    double* kr = (double*)malloc(sizeof(double) * dk);
+    if (!S || !z || !qr || !kr) {
+        free(S); free(z); free(qr); free(kr);
+        return -3;
+    }
+    const size_t soff = ((size_t)b * H + h) * (size_t)dk * dv, zoff = ((size_t)b * H + h) * (size_t)dk;
+    if (J->s_in) memcpy(S, J->s_in + soff, sizeof(double) * (size_t)dk * dv);
+    if (J->z_in) memcpy(z, J->z_in + zoff, sizeof(double) * (size_t)dk);
+    for (int n = 0; n < N; ++n) {
+        const long long p = J->pos0 + n;
+        gather_rotated(J->q, qr, N, H, dk, b, n, h, J->theta, p);
+        gather_rotated(J->k, kr, N, H, dk, b, n, h, J->theta, p);
+        const double* vn = J->v + (((size_t)b * N + n) * H + h) * (size_t)dv;
+        for (int i = 0; i < dk; ++i) {
+            for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] = g * S[(size_t)i * dv + j] + kr[i] * vn[j];
+            z[i] = g * z[i] + kr[i];
+        }
+        double* on = out_row(J->o, N, H, dv, b, n, h);
+        for (int j = 0; j < dv; ++j) on[j] = 0.0;
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j) on[j] += qr[i] * S[(size_t)i * dv + j];
+        const double f = norm_row_factor(J->norm, dk, g, p, dot(qr, z, dk));
+        for (int j = 0; j < dv; ++j) on[j] *= f;
+    }
+    if (J->s_out) memcpy(J->s_out + soff, S, sizeof(double) * (size_t)dk * dv);
+    if (J->z_out) memcpy(J->z_out + zoff, z, sizeof(double) * (size_t)dk);
+    free(S); free(z); free(qr); free(kr);
+    return 0;
+}
+
+/* Chunkwise form with the normalizations: the plain chunkwise outputs and state (form_chunkwise), and the row
+ * sums q'_j . z_j of each chunk [t0, t0 + L) computed the chunkwise way, as the outputs are:
+ *   q'_j . z_j = sum_{l<=j} gamma^(j-l) (q'_j . k'_l) + gamma^(j+1) (q'_j . z),   z <- gamma^L z + sum_l zeta_l k'_l
+ * with z the decayed key sum entering the chunk; each output row is then scaled by its factor. */
+static int form_chunkwise_norm(job* J, int b, int h) {
+    int rc = form_chunkwise(J, b, h);
+    if (rc) return rc;
+    const int N = J->N, H = J->H, dk = J->dk, dv = J->dv, C = J->chunk;
+    const double g = J->gamma[h];
+    head_seq hs;
+    double* z = (double*)calloc((size_t)dk, sizeof(double));
+    double* rs = (double*)malloc(sizeof(double) * (size_t)C + 8);
+    rc = load_head(&hs, J->q, J->k, J->v, N, H, dk, dv, b, h, J->theta, J->pos0);
+    if (rc || !z || !rs) {
+        free_head(&hs); free(z); free(rs);
+        return -3;
+    }
+    const size_t zoff = ((size_t)b * H + h) * (size_t)dk;
+    if (J->z_in) memcpy(z, J->z_in + zoff, sizeof(double) * (size_t)dk);
+    for (int t0 = 0; t0 < N; t0 += C) {
+        const int L = (N - t0 < C) ? (N - t0) : C;
+        const double* Qc = hs.Qr + (size_t)t0 * dk;
+        const double* Kc = hs.Kr + (size_t)t0 * dk;
+        for (int j = 0; j < L; ++j) {
+            double inner = 0.0;
+            for (int l = 0; l <= j; ++l) inner += pow(g, (double)(j - l)) * dot(Qc + (size_t)j * dk, Kc + (size_t)l * dk, dk);
+            rs[j] = inner + pow(g, (double)(j + 1)) * dot(Qc + (size_t)j * dk, z, dk);
+        }
+        for (int i = 0; i < dk; ++i) {
+            double u = 0.0;
+            for (int l = 0; l < L; ++l) u += pow(g, (double)(L - 1 - l)) * Kc[(size_t)l * dk + i];
+            z[i] = pow(g, (double)L) * z[i] + u;
+        }
+        for (int j = 0; j < L; ++j) {
+            const double f = norm_row_factor(J->norm, dk, g, J->pos0 + t0 + j, rs[j]);
+            double* oj = out_row(J->o, N, H, dv, b, t0 + j, h);
+            for (int c = 0; c < dv; ++c) oj[c] *= f;
+        }
+    }
+    if (J->z_out) memcpy(J->z_out + zoff, z, sizeof(double) * (size_t)dk);
+    free_head(&hs); free(z); free(rs);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------------------ */
 /* Exported entry points. Return 0 on success, -1 bad arguments, -2 thread error, -3 out of memory. */
 /* ------------------------------------------------------------------------------------------------ */
 
@@ -574,6 +694,38 @@ int orc_chunkwise(const double* q, const double* k, const double* v, double* o, 
     job J = {0};
     J.q = q; J.k = k; J.v = v; J.o = o; J.gamma = gamma; J.theta = theta; J.s_in = s_in; J.s_out = s_out;
     J.B = B; J.N = N; J.H = H; J.dk = dk; J.dv = dv; J.pos0 = pos0; J.chunk = chunk; J.form = 2;
+    J.nthreads = nthreads;
+    return run(J);
+}
+
+/* The recurrent (chunk <= 0) or chunkwise (chunk > 0) form with the score normalizations selected by norm
+ * (ORC_NORM_* flags), carrying the state S and the decayed key sum z ([B][H][dk]); z_in NULL means zero. */
+int orc_normalized(const double* q, const double* k, const double* v, double* o, int B, int N, int H, int dk,
+                   int dv, const double* gamma, const double* theta, long long pos0, int chunk, int norm,
+                   const double* s_in, double* s_out, const double* z_in, double* z_out, int nthreads) {
+    if (check_args(B, N, H, dk, dv, gamma, theta) || !q || !k || !v || !o || norm < 0 || norm > 7 || pos0 < 0)
+        return -1;
+    job J;
+    memset(&J, 0, sizeof(J));
+    J.q = q;
+    J.k = k;
+    J.v = v;
+    J.o = o;
+    J.gamma = gamma;
+    J.theta = theta;
+    J.s_in = s_in;
+    J.s_out = s_out;
+    J.z_in = z_in;
+    J.z_out = z_out;
+    J.B = B;
+    J.N = N;
+    J.H = H;
+    J.dk = dk;
+    J.dv = dv;
+    J.pos0 = pos0;
+    J.chunk = chunk;
+    J.norm = norm;
+    J.form = chunk > 0 ? 7 : 6;
     J.nthreads = nthreads;
     return run(J);
 }

@@ -52,9 +52,17 @@ MUTANTS = {
                        "for (int i = 0; i < dk; ++i) acc += qn[i] * S[(size_t)i * dv + j];"),
     "grad_dq_reads_state_transposed": ("for (int j = 0; j < dv; ++j) acc += S[(size_t)i * dv + j] * don[j];",
                                        "for (int j = 0; j < dv; ++j) acc += S[(size_t)j * dk + i] * don[j];"),
+    # normalized forms carried through a state
+    "norm_key_sum_no_decay": ("z[i] = g * z[i] + kr[i];", "z[i] = z[i] + kr[i];"),
+    "norm_decay_row_local_index": ("norm_row_factor(J->norm, dk, g, J->pos0 + t0 + j, rs[j])",
+                                   "norm_row_factor(J->norm, dk, g, t0 + j, rs[j])"),
+    "norm_rowsum_cross_exponent": ("pow(g, (double)(j + 1)) * dot(", "pow(g, (double)(j)) * dot("),
+    "norm_key_sum_chunk_zeta": ("pow(g, (double)(L - 1 - l)) * Kc[", "pow(g, (double)(L - l)) * Kc["),
+    "norm_scores_before_scaling": ("const double r = c * qz;", "const double r = qz;"),
 }
 
-PIN_TESTS = ["test_oracle_pins.py", "test_oracle_forms.py", "test_oracle_epilogue.py", "test_oracle_grad.py"]
+PIN_TESTS = ["test_oracle_pins.py", "test_oracle_forms.py", "test_oracle_epilogue.py", "test_oracle_grad.py",
+             "test_oracle_normalized.py"]
 
 
 def _run_pins_against(src_text, tmp_path):

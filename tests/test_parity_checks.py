@@ -184,3 +184,30 @@ def test_chain_give_up_is_visible(R, case):
     R.ret_chunkwise_fwd(qd, kd, vd, o2, gamma, C, theta=theta, state_out=sout, workspace=ws, options=opts)
     torch.cuda.synchronize()
     assert rel_err(to_host(o2), o_ref) <= tol("bf16") and rel_err(to_host(sout), s_ref) <= tol("bf16")
+
+
+def test_workspace_of_an_unchained_call_stays_usable(R):
+    """A call planned with one segment but rotated copies of q and k in the workspace (d_v = 512: 4 tiles), then
+    chained calls on the same workspace: the copies never overwrite the chain's header, counters and flags, so
+    ret_chunkwise_check stays clean and every call matches the oracle."""
+    import torch
+    B, N, H, dk, dv, C = 1, 700, 2, 256, 512, 128
+    print_case("workspace_unchained_then_chained", (B, N, H, dk, dv, C))
+    rng = np.random.default_rng(17)
+    q = W.normal(rng, (B, N, H, dk), 16.0, "bf16")
+    k = W.normal(rng, (B, N, H, dk), 16.0, "bf16")
+    v = W.normal(rng, (B, N, H, dv), 16.0, "bf16")
+    gamma, theta = W.gamma_schedule(H), W.theta_schedule(dk)
+    o_ref, _ = oracle.chunkwise(q, k, v, gamma, C, theta=theta)
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    plans = [{"segments": 1, "prerotate": 1}, {"segments": 3}, {"segments": 1, "prerotate": 1}, {"segments": 2}]
+    need = max(R.ret_chunkwise_workspace_bytes(B, N, H, dk, dv, C, options=p) for p in plans)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for p in plans:
+        o = empty_out((B, N, H, dv), "bf16")
+        R.ret_chunkwise_fwd(qd, kd, vd, o, gamma, C, theta=theta, workspace=ws, options=p)
+        torch.cuda.synchronize()
+        R.ret_chunkwise_check(ws)
+        e = rel_err(to_host(o), o_ref)
+        print("  plan %s: err %.3g" % (p, e))
+        assert e <= tol("bf16"), (p, e)
