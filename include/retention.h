@@ -337,6 +337,25 @@ ret_status_t ret_recurrent_step_normalized(const void* q, const void* k, const v
                                            ret_dtype_t out_dt, const float* gamma, const double* theta, int64_t pos,
                                            int norm, void* stream, const ret_options_t* opts);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): ret_chunkwise_fwd (arguments as there, defaults for the options) with the workspace
+ * taken from a device array the library owns, RET_NOALLOC_SCRATCH_BYTES on every GPU it runs on, held until the
+ * process ends. The call allocates nothing; the first call on a device looks up the array's address and zeroes
+ * its first 64 KB with a fill kernel on `stream`. The call uses the library's segment plan for the shape, with
+ * the rotated copies of q and k only where they fit beside the chain (otherwise staging rotates: the same result
+ * up to rounding). RET_ERR_WORKSPACE (before anything is enqueued) when the plan's segment chain needs more than
+ * the array, or more counters and flags than its zeroed region holds. Every call on a GPU shares that GPU's
+ * array and leaves its counters and flags zero: calls that overlap in time on one GPU (different streams or
+ * threads) race and must not be made. The array is not visible to ret_chunkwise_check; a segment-chain wait
+ * that gives up shows as NaN outputs.
+ */
+#define RET_NOALLOC_SCRATCH_BYTES (128u << 20)
+ret_status_t ret_chunkwise_fwd_noalloc(const void* q, const void* k, const void* v, void* o, int B, int N, int H,
+                                       int dk, int dv, ret_dtype_t in_dt, ret_dtype_t out_dt, const float* gamma,
+                                       const double* theta, int64_t pos0, int chunk, const float* state_in,
+                                       float* state_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

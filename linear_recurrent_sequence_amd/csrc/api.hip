@@ -886,8 +886,8 @@ ret_status_t ret_chunkwise_bwd_ex(const void* q, const void* k, const void* v, c
 
 namespace {
 
-// Workspace of the normalized chunkwise call: the chunkwise plan's workspace, then the normalization's segment
-// sums W [B*H][nseg][d_k] and row factors f [B*N*H] (fp32).
+// Workspace of the normalized chunkwise call: the chunkwise plan's workspace (at least the chain's metadata
+// region), then the normalization's segment sums W [B*H][nseg][d_k] and row factors f [B*N*H] (fp32).
 struct NormLayout {
     size_t chunk_bytes, w_off, f_off, total;
     int nseg;
@@ -900,7 +900,10 @@ bool norm_layout(int B, int N, int H, int dk, int dv, int chunk, ret_dtype_t in_
     const ChunkPlan p = plan_chunk(ck, B, N, H, dk, dv, chunk, true, SIZE_MAX, op);
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     L->nseg = (N + kNormSegTokens - 1) / kNormSegTokens;
+    // the chain's header, counters and flags (first kChainMeta bytes) stay reserved even without a chain, so the
+    // normalization's slots never cover what ret_chunkwise_check and later chained calls read
     L->chunk_bytes = up(p.chain_bytes + p.rot_bytes);
+    if (L->chunk_bytes < kChainMeta) L->chunk_bytes = kChainMeta;
     L->w_off = L->chunk_bytes;
     L->f_off = L->w_off + up((size_t)B * H * L->nseg * dk * 4);
     L->total = L->f_off + up((size_t)B * N * H * 4);
@@ -1053,6 +1056,78 @@ ret_status_t ret_recurrent_step_normalized(const void* q, const void* k, const v
     hipLaunchKernelGGL(nk.step, dim3(B * H), dim3(64), 0, s, A);
     tm.done();
     return launch_status("ret_norm_step");
+}
+
+}  // extern "C"
+
+// ---- the no-allocation chunkwise call: its workspace is a library-owned device array ----
+// `scratch` is the array as the device code sees it. In host code its name is a host-side stand-in, not a
+// device address: host code uses only the per-device address hipGetSymbolAddress returns (g_scratch[device]).
+static __device__ __align__(256) unsigned char scratch[RET_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+
+// The scratch array's address on the current device, looked up once per device (with that device current);
+// the first call on a device also zeroes the chain's header, counters and flags there with a fill kernel on
+// `s` (not a memset node, which a graph capture would record).
+ret_status_t scratch_of_device(hipStream_t s, void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return fail(RET_ERR_HIP, "no current device (or device index >= %d)", kMaxDevices);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(RET_ERR_HIP, "scratch address on device %d: %s", dev, hipGetErrorString(e));
+        const long long n = (long long)(kChainMeta / 4);
+        hipLaunchKernelGGL(zero_words_get(), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (int*)p, n);
+        ret_status_t st = launch_status("scratch set-up");
+        if (st != RET_OK) return st;
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return RET_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ret_status_t ret_chunkwise_fwd_noalloc(const void* q, const void* k, const void* v, void* o, int B, int N, int H,
+                                       int dk, int dv, ret_dtype_t in_dt, ret_dtype_t out_dt, const float* gamma,
+                                       const double* theta, int64_t pos0, int chunk, const float* state_in,
+                                       float* state_out, void* stream) {
+    ret_status_t st = check_common(q, k, v, o, B, N, H, dk, dv, in_dt, out_dt, gamma, theta);
+    if (st != RET_OK) return st;
+    if (chunk <= 0) return fail(RET_ERR_INVALID_ARG, "chunk must be positive (got %d)", chunk);
+    ChunkKernels ck;
+    if (!pick_chunk(in_dt, dk, dv, chunk, &ck))
+        return fail(RET_ERR_UNSUPPORTED, "chunkwise form: unsupported d_k=%d d_v=%d chunk=%d for %s input", dk, dv,
+                    chunk, in_dt == RET_F32 ? "F32" : "BF16");
+    // The library's own segment plan; its chain must fit in the scratch (the rotated copies of q and k are
+    // dropped when they do not: staging then rotates, which changes only the rounding).
+    const ChunkPlan full = plan_chunk(ck, B, N, H, dk, dv, chunk, theta != nullptr, SIZE_MAX);
+    if (full.chain_bytes > (size_t)RET_NOALLOC_SCRATCH_BYTES)
+        return fail(RET_ERR_WORKSPACE,
+                    "no-allocation chunkwise call: the segment chain of this shape needs %zu bytes, more than the "
+                    "%u-byte scratch array; use ret_chunkwise_fwd with a workspace",
+                    full.chain_bytes, (unsigned)RET_NOALLOC_SCRATCH_BYTES);
+    // the chain must also keep its counters and flags inside the region the set-up zeroed
+    if (full.nseg > 1 && ck.fused && chain_layout(B * H * (dv / ck.dvt), full.nseg, dk * ck.dvt).agg_off > kChainMeta)
+        return fail(RET_ERR_WORKSPACE, "no-allocation chunkwise call: %d units x %d segments exceed the chain's "
+                    "counter and flag region", B * H * (dv / ck.dvt), full.nseg);
+    void* ws = nullptr;
+    if ((st = scratch_of_device((hipStream_t)stream, &ws)) != RET_OK) return st;
+    const size_t avail = full.chain_bytes + full.rot_bytes <= (size_t)RET_NOALLOC_SCRATCH_BYTES
+                             ? full.chain_bytes + full.rot_bytes
+                             : full.chain_bytes;
+    return chunkwise_run(q, k, v, o, B, N, H, dk, dv, in_dt, out_dt, gamma, theta, pos0, chunk, state_in, state_out,
+                         ws, avail, stream, nullptr, nullptr, kDefaultOpts);
 }
 
 ret_timer_t* ret_timer_create(void) { return new (std::nothrow) ret_timer(); }

@@ -170,6 +170,8 @@ def load(build_if_missing: bool = True):
     lib.ret_recurrent_step_normalized.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, fp, dp, i64,
                                                   i32, vp, op]
     lib.ret_recurrent_step_normalized.restype = i32
+    lib.ret_chunkwise_fwd_noalloc.argtypes = lib.ret_chunkwise_fwd.argtypes[:17] + [vp]
+    lib.ret_chunkwise_fwd_noalloc.restype = i32
     lib.ret_options_default.argtypes = [op]
     lib.ret_options_default.restype = None
     lib.ret_timer_create.restype = vp
@@ -526,4 +528,25 @@ def ret_recurrent_step_normalized(q, k, v, o, state, z, gamma, pos, norm, theta=
                                            _dev(state, "state"), _dev(z, "z"), B, H, dk, dv, _dt(q), _dt(o), gp, tp,
                                            int(pos), int(norm), _stream(stream), _options(options))
     _check("ret_recurrent_step_normalized", st)
+    return o
+
+
+def ret_chunkwise_fwd_noalloc(q, k, v, o, gamma, chunk, theta=None, pos0=0, state_in=None, state_out=None,
+                              stream=None):
+    """ret_chunkwise_fwd with the library's own device scratch array as the workspace: allocates nothing (for
+    callers that cannot). Calls that overlap in time on one GPU must not be made."""
+    lib = load()
+    _qkv(q, k, v)
+    B, N, H, dk = q.shape
+    dv = v.shape[3]
+    _shape(o, "o", (B, N, H, dv), _IO)
+    for name, s in (("state_in", state_in), ("state_out", state_out)):
+        _shape(s, name, (B, H, dk, dv), (torch.float32,))
+    _same_device(q, k, v, o, state_in, state_out)
+    g, gp = _gamma(gamma, H)
+    th, tp = _theta(theta, dk)
+    st = lib.ret_chunkwise_fwd_noalloc(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"), B, N, H, dk, dv,
+                                       _dt(q), _dt(o), gp, tp, int(pos0), int(chunk), _dev(state_in, "state_in"),
+                                       _dev(state_out, "state_out"), _stream(stream))
+    _check("ret_chunkwise_fwd_noalloc", st)
     return o
