@@ -238,8 +238,9 @@ void ret_timer_reset(ret_timer_t* t);
  *   target_wgs   > 0: workgroups the segment planner aims for; 0: the kernel's default
  *   prerotate    -1: planner; 0: q and k rotated while staging; 1: rotated once up front into the workspace
  *   onchip       -1 or 1: the on-chip segment kernel where segments fit (d_k <= 64, <= 256 tokens); 0: never
- *   variant      0: default kernel of the shape; d_k = 256 with d_v a multiple of 128: 1 = 256 threads whose
- *                waves own 32 columns, 2 = 256 threads with d_v tiles of 64
+ *   variant      0: default kernel of the shape; d_v a multiple of 128: 3 = the wide-head kernel (32-token steps,
+ *                q and k rotated once up front; the default for d_k = 256); d_k = 256: 1 = 256 threads whose
+ *                waves own 32 columns, 2 = 256 threads with d_v tiles of 64, 4 = 512 threads x 16 columns
  *   step_cw, step_wr, step_pairs   decode tile: columns per workgroup (16, 32, 64), rows per wave (16, 32, 64),
  *                pairs (0 planner, 1 one (b, h) per workgroup, 2 grouped); 0 = default
  *   bwd_direct   -1 or 1: gradients by the reversed traversal where available; 0: through reordered copies

@@ -25,6 +25,8 @@ COMMON = [
     "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall", "-Wno-unused-function", "-Wno-unused-result",
 ]
+# per-source additions: the wide-head kernel keeps its MFMA accumulators in architectural registers
+EXTRA = {"chunk_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 NOISE = "'-packed-fp32-ops' is not a recognized feature"
 
 
@@ -57,7 +59,7 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     for src in sources():
         obj = os.path.join(OBJ_DIR, os.path.basename(src)[:-4] + ".o")
         objs.append(obj)
-        cmds.append(["hipcc"] + COMMON + inc + ["-c", src, "-o", obj])
+        cmds.append(["hipcc"] + COMMON + EXTRA.get(os.path.basename(src), []) + inc + ["-c", src, "-o", obj])
     jobs = jobs or min(len(cmds), max(1, min(16, os.cpu_count() or 1)))
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         results = list(ex.map(_run, cmds))

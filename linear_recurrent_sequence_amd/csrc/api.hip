@@ -160,7 +160,7 @@ void fill_fwd(FwdArgs& A, const void* q, const void* k, const void* v, void* o, 
 bool pick_chunk(ret_dtype_t in_dt, int dk, int dv, int C, ChunkKernels* out, const Opts& op = kDefaultOpts) {
     if (in_dt == RET_F32) return chunk_kernels_f32(dk, dv, C, out);
     if (dk == 32 || dk == 64) return chunk_kernels_bf16_small(dk, dv, C, out);
-    if (dk == 128) return chunk_kernels_bf16_128(dk, dv, C, out);
+    if (dk == 128) return chunk_kernels_bf16_128(dk, dv, C, op.variant, out);
     if (dk == 256) return chunk_kernels_bf16_256(dk, dv, C, op.variant, out);
     return false;
 }
@@ -214,7 +214,7 @@ ChunkPlan plan_chunk(const ChunkKernels& ck, int B, int N, int H, int dk, int dv
     p.rot_bytes = 0;
     // prerotate 0 / 1 turns the up-front rotation off / on wherever a kernel supports it.
     const int pre = op.prerotate;
-    if (ck.fused_pre && rotate && (pre < 0 ? dv / ck.dvt >= 4 : pre != 0))
+    if (ck.fused_pre && rotate && (pre < 0 ? (ck.pre_always || dv / ck.dvt >= 4) : pre != 0))
         p.rot_bytes = 2 * (((size_t)B * N * H * dk * 2 + 255) / 256 * 256);
     // The rotated copies follow the chain's header, counters and flags (the first kChainMeta bytes) even when
     // the plan has no chain, so that those stay zero for any later call that shares the workspace.
@@ -423,7 +423,9 @@ ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o,
             if ((st = launch_status("ret_rotate_qk")) != RET_OK) return st;
         }
         const unsigned grid = (unsigned)((long long)nseg * B * H * ntiles);
-        const int threads = onchip || !ck.threads ? kThreads : ck.threads;
+        const int threads = onchip || !ck.threads          ? kThreads
+                            : fn == ck.fused_pre && ck.threads_pre ? ck.threads_pre
+                                                                 : ck.threads;
         if (epi && onchip && out_dt == RET_BF16 && dv == 64) {
             A.epi = 1;
             A.gate = epi->gate;

@@ -1,16 +1,33 @@
 // bf16-input chunkwise kernels, d_k in {256}, chunk in {32, 64, 128, 256, 512} (chunks longer than 64 tokens
 // run as 64-token sub-chunks: the instances differ only in the segment plan). Where d_v is a multiple of 128 the d_v
-// tile is 128 columns: 512 threads whose waves own 16 columns each (the default: two waves per SIMD), or 256
-// threads whose waves own 32 columns each (twice the operand reuse per LDS read, one wave per SIMD).
-// `variant` picks 0: 512 x 16 (default), 1: 256 x 32, 2: the 256-thread kernel with 16-column waves and d_v
-// tiles of 64. Other d_v: 256 threads with d_v tiles of 64.
+// tile is 128 columns. `variant` picks 0 (default) or 3: the wide-head kernel (256 threads whose waves own 32
+// columns, 32-token steps, operands rotated once up front), 1: the chained kernel with 256 threads x 32 columns,
+// 2: the 256-thread kernel with 16-column waves and d_v tiles of 64, anything else: the chained kernel with 512
+// threads x 16 columns (two waves per SIMD). Other d_v: 256 threads with d_v tiles of 64.
 #include "chunk_bf16.h"
 
 namespace ret {
 
+// The wide-head kernel (256 threads, waves of 32 columns, 32-token steps) on operands staged as given, with the
+// 512-thread kernel rotating while staging where no workspace holds rotated copies.
+template <int C>
+ChunkKernels chunk_entry_wide256() {
+    ChunkKernels k = chunk_entry_bf16<256, C, 512>();
+    k.fused_pre = chunk_wide_get(256);
+    k.threads_pre = kWideThreads;
+    k.pre_always = 1;
+    return k;
+}
+
 bool chunk_kernels_bf16_256(int dk, int dv, int C, int variant, ChunkKernels* out) {
     if (dv % 64) return false;
-    int mode = variant == 1 ? 2 : variant == 2 ? 0 : 1;  // 0: 256 threads x 16 columns, 1: 512 x 16, 2: 256 x 32
+    if ((variant == 0 || variant == 3) && dv % 128 == 0 && dk == 256 &&
+        (C == 32 || C == 64 || C == 128 || C == 256 || C == 512)) {
+        *out = C == 32 ? chunk_entry_wide256<32>() : C == 64 ? chunk_entry_wide256<64>() : chunk_entry_wide256<128>();
+        return true;
+    }
+    // 0: 256 threads x 16 columns, 1: 512 x 16 (variant 4), 2: 256 x 32
+    int mode = variant == 1 ? 2 : variant == 2 ? 0 : 1;
     if (dv % 128) mode = 0;
 #define RET_CASE(DKv, Cv)                                                                             \
     if (dk == DKv && C == Cv) {                                                                       \

@@ -958,6 +958,9 @@ struct ChunkKernels {
     int seg_tokens;
     int threads;      // workgroup size of the fused kernels (0: kThreads)
     int target_wgs;   // workgroups the segment planner aims for (0: the default)
+    int threads_pre;  // workgroup size of fused_pre where it differs from `threads` (0: the same)
+    int pre_always;   // fused_pre stages operands as given only: with rotation, q and k are rotated up front
+                      // whenever the workspace holds the copies
 };
 struct ParKernel {
     fwd_kernel_t fn;
@@ -982,8 +985,12 @@ inline unsigned rotate_qk_blocks(int B, int N, int H, int dk) {
 }
 bool chunk_kernels_f32(int dk, int dv, int C, ChunkKernels* out);
 bool chunk_kernels_bf16_small(int dk, int dv, int C, ChunkKernels* out);   // d_k in {32, 64}
-bool chunk_kernels_bf16_128(int dk, int dv, int C, ChunkKernels* out);     // d_k = 128
+bool chunk_kernels_bf16_128(int dk, int dv, int C, int variant, ChunkKernels* out);  // d_k = 128
 bool chunk_kernels_bf16_256(int dk, int dv, int C, int variant, ChunkKernels* out);  // d_k = 256
+// The wide-head kernel (chunk_wide_bf16.h) for d_k in {128, 256} (null otherwise): kWideThreads threads, d_v tiles
+// of 128, operands staged as given.
+constexpr int kWideThreads = 256;
+fwd_kernel_t chunk_wide_get(int dk);
 bool parallel_kernel_get(bool bf16_in, int dk, int dv, ParKernel* out);
 // Decode kernel for a (d_k, column tile cw, rows per wave wr) tile, 0 = default, null if none; with pairs_mode 0
 // it groups (b, h) pairs into workgroups of up to 8 waves where B*H leaves a workgroup per CU; 1 / 2 force one

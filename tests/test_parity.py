@@ -117,12 +117,12 @@ def test_chunkwise_small(R, case):
     assert eo <= tol(dt) and es <= tol(dt), (eo, es)
 
 
-@pytest.mark.parametrize("threads", ["256x2", "512", "256"])
+@pytest.mark.parametrize("threads", ["wide", "256x2", "512", "256"])
 def test_chunkwise_dk256_workgroup_sizes(R, threads):
-    """d_k 256 with d_v tiles of 128 (512 threads whose waves own 16 columns: the default; or 256 threads of 32
-    columns), and the 256-thread kernels with d_v tiles of 64. All match the oracle, with two segments and 3 d_v
-    tiles of 128."""
-    opts = {"variant": {"512": 0, "256x2": 1, "256": 2}[threads], "segments": 2}
+    """d_k 256 with d_v tiles of 128 (the wide-head kernel: the default; the chained kernel with 512 threads whose
+    waves own 16 columns, or 256 threads of 32 columns), and the 256-thread kernels with d_v tiles of 64. All match
+    the oracle, with two segments and 3 d_v tiles of 128."""
+    opts = {"variant": {"wide": 0, "512": 4, "256x2": 1, "256": 2}[threads], "segments": 2}
     B, N, H, dk, dv, C = 1, 300, 2, 256, 384, 64
     print_case("dk256 threads=%s" % threads, (B, N, H, dk, dv, C))
     rng = np.random.default_rng(71)
@@ -136,6 +136,44 @@ def test_chunkwise_dk256_workgroup_sizes(R, threads):
     eo, es = rel_err(o, o_ref), rel_err(s, s_ref)
     print("  err o=%.3g state=%.3g" % (eo, es))
     assert eo <= tol("bf16") and es <= tol("bf16"), (eo, es)
+
+
+WIDE = [  # (d_k, B, N, H, d_v, chunk, rotation, state_in, segments)
+    (256, 1, 333, 2, 256, 64, True, True, 3),
+    (256, 2, 37, 1, 128, 64, True, False, None),
+    (256, 1, 1, 2, 128, 32, True, True, None),
+    (256, 1, 200, 2, 128, 32, False, True, 2),
+    (256, 1, 300, 1, 384, 128, True, False, 2),
+    (256, 1, 129, 3, 128, 512, True, True, 1),
+    (128, 1, 333, 2, 256, 64, True, True, 3),
+    (128, 2, 100, 2, 128, 32, False, False, None),
+    (128, 1, 65, 1, 128, 128, True, True, 1),
+]
+
+
+@pytest.mark.parametrize("case", WIDE, ids=lambda c: "dk%d-B%d-N%d-H%d-dv%d-C%d-rot%d-s%d-seg%s" % c)
+def test_chunkwise_wide_kernel(R, case):
+    """The wide-head kernel (32-token steps, q and k rotated once up front): d_k 128 and 256, chunks of 32 to
+    512 tokens, ragged tails shorter than one step, with and without rotation and an incoming state, one or several
+    chained segments. Matches the oracle's output and final state."""
+    dk, B, N, H, dv, C, rot, with_state, segs = case
+    print_case("wide", case)
+    opts = {"variant": 3}
+    if segs is not None:
+        opts["segments"] = segs
+    rng = np.random.default_rng(400 + N + dk)
+    q = W.normal(rng, (B, N, H, dk), 16.0, "bf16")
+    k = W.normal(rng, (B, N, H, dk), 16.0, "bf16")
+    v = W.normal(rng, (B, N, H, dv), 16.0, "bf16")
+    s0 = rng.standard_normal((B, H, dk, dv)).astype(np.float32) if with_state else None
+    gamma = W.gamma_schedule(H)
+    theta = W.theta_schedule(dk) if rot else None
+    o_ref, s_ref = oracle.chunkwise(q, k, v, gamma, C, theta=theta, pos0=5, state_in=s0)
+    o, s = _gpu_chunkwise(R, q, k, v, "bf16", gamma, C, theta=theta, pos0=5, s_in=s0, options=opts)
+    for h in range(H):
+        eo, es = rel_err(o[:, :, h], o_ref[:, :, h]), rel_err(s[:, h], s_ref[:, h])
+        print("  head %d err o=%.3g state=%.3g" % (h, eo, es))
+        assert eo <= tol("bf16") and es <= tol("bf16"), (h, eo, es)
 
 
 @pytest.mark.parametrize("onchip", ["1", "0"])
