@@ -19,8 +19,12 @@ The same JSON line carries, each with its own roofline:
   * the fp64 CPU oracle timed on this host on a bounded sample of the 7b-class workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-decode] [--no-epilogue]
-                       [--no-backward] [--no-cpu-baseline] [--no-extra] [--copy-calibration]
-                       [--decode-steps S]
+                       [--no-backward] [--no-cpu-baseline] [--no-extra] [--no-cold] [--decode-mode MODE]
+                       [--decode-steps S] [--copy-calibration]
+       python bench.py --record-traffic KEY KERNEL FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR
+The second form (no GPU) records HBM traffic per launch of the kernels whose name contains KERNEL from two
+`rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs, scaled by the same counters of `--copy-calibration` runs,
+under KEY ("timer name@workload") in profiles/traffic.json.
 """
 from __future__ import annotations
 
@@ -39,8 +43,8 @@ METRIC = "retention fwd tokens/sec (chunkwise) + decode steps/sec; % MFMA / HBM 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # Chunkwise workloads by name -> key (and seed) in workloads.WORKLOADS
 CHUNK_WORKLOADS = {"retention-layer-d512": 2, "7b-class-layer": 4, "long-sequence": 5}
-CHUNK_KERNELS = ("ret_rotate_qk", "ret_chunk_seg", "ret_chunk_fused", "ret_chunk_local", "ret_segment_scan",
-                 "ret_chunk_full")
+CHUNK_KERNELS = ("ret_rotate_qk", "ret_chunk_seg", "ret_chunk_fused", "ret_chunk_wide", "ret_chunk_dma",
+                 "ret_chunk_local", "ret_segment_scan", "ret_chunk_full")
 
 
 def source_digest() -> str:
@@ -168,12 +172,12 @@ def bench_chunkwise(R, W, torch, wid, steps, warmup, cold_reps=20):
     R.ret_chunkwise_check(ws)  # no call of the timed regions abandoned a segment-chain wait
     cold.sort()
     nbytes, f_causal, f_pages = chunk_algorithmic(w)
+    ms_cold = cold[len(cold) // 2] if cold else None
     tokens = w.B * w.N
     dom = max(kernels, key=lambda n: kernels[n]["avg_us"] * kernels[n]["launches_per_call"])
     # When a call is one kernel its duration is also the replayed graph's per-call time; otherwise its share
     # from the per-launch events.
     dom_us = kernels[dom]["avg_us"]
-    ms_cold = cold[len(cold) // 2]
     res = {
         "workload": "%s: B=%d N=%d H=%d d_k=%d d_v=%d chunk=%d, bf16 in/out, fp32 state, xPos rotation"
                     % (w.name, w.B, w.N, w.H, w.dk, w.dv, w.chunk),
@@ -181,7 +185,7 @@ def bench_chunkwise(R, W, torch, wid, steps, warmup, cold_reps=20):
         "tokens_per_s": tokens / (ms_graph * 1e-3),
         "ms_per_call_eager": ms_eager,
         "ms_per_call_mall_cold_median": ms_cold,
-        "tokens_per_s_mall_cold": tokens / (ms_cold * 1e-3),
+        "tokens_per_s_mall_cold": tokens / (ms_cold * 1e-3) if cold else None,
         "kernels": kernels,
         "dominant_kernel": dom,
         "dominant_kernel_avg_us": dom_us,
@@ -297,10 +301,11 @@ def bench_backward(R, W, torch, wid, steps):
     }
 
 
-def bench_decode(R, W, torch, steps_graph=1024, reps=3, cold_states=32):
+def bench_decode(R, W, torch, steps_graph=1024, reps=3, cold_states=32, mode="both"):
     """Batched decode: 1024 steps of the workload's q, k, v (drawn step by step) from its prefilled state,
     replayed from a HIP graph. Warm: one state. MALL-cold: step t updates state t % cold_states, a working set
-    of cold_states x 16 MiB, so no state is still cached when its turn comes again."""
+    of cold_states x 16 MiB, so no state is still cached when its turn comes again. mode "warm" / "cold" runs
+    one of the two (None for the other)."""
     import numpy as np
     w = W.WORKLOADS[3]
     rng = np.random.default_rng(w.seed)
@@ -329,19 +334,19 @@ def bench_decode(R, W, torch, steps_graph=1024, reps=3, cold_states=32):
             R.ret_recurrent_step(sqd[t], skd[t], svd[t], outs[t], st, w.gamma, pos=w.prefill + t, theta=theta,
                                  options=options)
 
-    us_warm = 1e3 * graph_ms(torch, run_steps, 1, reps) / steps_graph
-    us_cold = 1e3 * graph_ms(torch, lambda: run_steps(True), 1, reps) / steps_graph
-    # kernel durations from per-launch events (eager launches), both ways
-    timer = R.Timer()
-    run_steps(False, {"timer": timer})
-    torch.cuda.synchronize()
-    tot, n = timer.query("ret_recurrent_step")
-    timer.reset()
-    run_steps(True, {"timer": timer})
-    torch.cuda.synchronize()
-    tot_c, n_c = timer.query("ret_recurrent_step")
-    timer.close()
-    return w, us_warm, us_cold, 1e3 * tot / n, 1e3 * tot_c / n_c
+    def measure(cold):
+        us = 1e3 * graph_ms(torch, lambda: run_steps(cold), 1, reps) / steps_graph
+        # kernel duration from per-launch events (eager launches)
+        timer = R.Timer()
+        run_steps(cold, {"timer": timer})
+        torch.cuda.synchronize()
+        tot, n = timer.query("ret_recurrent_step")
+        timer.close()
+        return us, 1e3 * tot / n
+
+    us_warm, k_warm = measure(False) if mode != "cold" else (None, None)
+    us_cold, k_cold = measure(True) if mode != "warm" else (None, None)
+    return w, us_warm, us_cold, k_warm, k_cold
 
 
 def _cpu_model() -> str:
@@ -388,9 +393,12 @@ def cpu_baseline(W, wid, seconds=8.0, single_seconds=3.0, sample_tokens=1024):
             "cpu_model": _cpu_model(), "host_cpus": len(os.sched_getaffinity(0))}
 
 
+COPY_BYTES = 256 << 20
+
+
 def copy_calibration(torch):
     """A plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
-    n = 256 << 20
+    n = COPY_BYTES
     src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty_like(src)
     for _ in range(3):
@@ -399,7 +407,58 @@ def copy_calibration(torch):
     print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
 
 
+def _counter_rows(directory, counter, kernel_substr):
+    """Per-dispatch values of `counter` for kernels whose name contains kernel_substr, from the
+    *_counter_collection.csv files rocprofv3 wrote under directory."""
+    import csv
+    vals = {}
+    for root, _, files in os.walk(directory):
+        for fn in files:
+            if not fn.endswith("counter_collection.csv"):
+                continue
+            with open(os.path.join(root, fn), newline="") as f:
+                for row in csv.DictReader(f):
+                    if row["Counter_Name"] == counter and kernel_substr in row["Kernel_Name"]:
+                        key = (fn, row["Dispatch_Id"])
+                        vals[key] = vals.get(key, 0.0) + float(row["Counter_Value"])
+    return list(vals.values())
+
+
+def record_traffic(key, kernel_substr, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
+    workload = key.split("@", 1)[1] if "@" in key else ""
+    cf = _counter_rows(copy_fetch_dir, "FETCH_SIZE", "copyBuffer")
+    cw = _counter_rows(copy_write_dir, "WRITE_SIZE", "copyBuffer")
+    fe = _counter_rows(fetch_dir, "FETCH_SIZE", kernel_substr)
+    wr = _counter_rows(write_dir, "WRITE_SIZE", kernel_substr)
+    if not (cf and cw and fe and wr):
+        sys.exit("record-traffic: no counter rows (copy %d/%d, kernel %d/%d)" % (len(cf), len(cw), len(fe), len(wr)))
+    avg = lambda xs: sum(xs) / len(xs)
+    rec = {"workload": workload, "kernel_match": kernel_substr,
+           "fetch_kib_per_launch": avg(fe), "write_kib_per_launch": avg(wr), "dispatches": [len(fe), len(wr)],
+           # counter KiB per byte of a plain copy of COPY_BYTES (both directions)
+           "copy_factor_fetch": avg(cf) * 1024.0 / COPY_BYTES, "copy_factor_write": avg(cw) * 1024.0 / COPY_BYTES,
+           "source_digest": source_digest()}
+    try:
+        with open(TRAFFIC_FILE) as f:
+            recs = json.load(f)
+    except (OSError, ValueError):
+        recs = {}
+    recs[key] = rec
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(recs, f, indent=1, sort_keys=True)
+        f.write("\n")
+    mb = lambda kib, fac: kib * 1024.0 / fac / 1e6
+    print("%s: fetch %.2f MB, write %.2f MB per launch (%d / %d dispatches)"
+          % (key, mb(rec["fetch_kib_per_launch"], rec["copy_factor_fetch"]),
+             mb(rec["write_kib_per_launch"], rec["copy_factor_write"]), len(fe), len(wr)))
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--record-traffic":
+        if len(sys.argv) != 8:
+            sys.exit("usage: bench.py --record-traffic KEY KERNEL FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR")
+        record_traffic(*sys.argv[2:8])
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
@@ -411,6 +470,8 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="only the `value` workload's chunkwise call")
+    ap.add_argument("--no-cold", action="store_true", help="skip the MALL-cold chunkwise calls (warm-only traces)")
+    ap.add_argument("--decode-mode", default="both", choices=("both", "warm", "cold"))
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=1024, help="decode steps per graph (1024 in the workload)")
     args = ap.parse_args()
@@ -436,7 +497,8 @@ def main():
 
     wid = CHUNK_WORKLOADS[args.workload]
     progress("chunkwise %s" % args.workload)
-    w, main_res = bench_chunkwise(R, W, torch, wid, args.steps, args.warmup)
+    cold_reps = 0 if args.no_cold else 20
+    w, main_res = bench_chunkwise(R, W, torch, wid, args.steps, args.warmup, cold_reps)
     bound = "mfma" if w.dk >= 256 else "hbm"  # the d_k 256 layer sits at the ridge; the others are HBM-bound
     tokens = w.B * w.N
     result = {
@@ -462,33 +524,36 @@ def main():
             if key == wid:
                 continue
             progress("chunkwise %s" % name)
-            wx, res = bench_chunkwise(R, W, torch, key, args.steps, args.warmup)
+            wx, res = bench_chunkwise(R, W, torch, key, args.steps, args.warmup, cold_reps)
             res["roofline"] = roofline_of(res, "mfma" if wx.dk >= 256 else "hbm")
             result[name] = res
     if not args.no_decode:
         progress("decode")
-        dw, us_warm, us_cold, k_warm, k_cold = bench_decode(R, W, torch, steps_graph=args.decode_steps)
+        dw, us_warm, us_cold, k_warm, k_cold = bench_decode(R, W, torch, steps_graph=args.decode_steps,
+                                                            mode=args.decode_mode)
         db, dflops = decode_algorithmic(dw.B, dw.H, dw.dk, dw.dv)
-        ach_c, ach_w = db / (us_cold * 1e-6) / 1e9, db / (us_warm * 1e-6) / 1e9
+
+        def decode_roofline(us, key, state):
+            ach = db / (us * 1e-6) / 1e9
+            # one kernel per step: the graph's per-step time (events on the replay stream)
+            return {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                    "traffic": load_traffic("ret_recurrent_step", key), "kernel": "ret_recurrent_step",
+                    "kernel_avg_us": us, "alg_bytes_per_launch": db, "state": state}
+
+        cold_state = "MALL-cold: the steps cycle through 32 distinct 16 MiB states (512 MiB)"
+        warm_state = "warm: one 16 MiB state, held by the Infinity Cache between steps"
+        us_main = us_cold if us_cold is not None else us_warm
         result["decode"] = {
             "workload": "%s: B=%d H=%d d_k=%d d_v=%d, fp32 state, bf16 q/k/v/o, %d steps from a %d-token prefill, "
                         "HIP graph" % (dw.name, dw.B, dw.H, dw.dk, dw.dv, args.decode_steps, dw.prefill),
-            "steps_per_s": 1e6 / us_cold, "tokens_per_s": dw.B * 1e6 / us_cold, "us_per_step": us_cold,
-            # one kernel per step: the graph's per-step time (events on the replay stream)
-            "roofline": {"bound": "hbm", "achieved": ach_c, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": ach_c / HBM_PEAK_GBS,
-                         "traffic": load_traffic("ret_recurrent_step", dw.name + " mall-cold"),
-                         "kernel": "ret_recurrent_step", "kernel_avg_us": us_cold, "alg_bytes_per_launch": db,
-                         "state": "MALL-cold: the steps cycle through 32 distinct 16 MiB states (512 MiB)"},
-            "warm": {"us_per_step": us_warm, "steps_per_s": 1e6 / us_warm,
-                     "roofline": {"bound": "hbm", "achieved": ach_w, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                  "frac": ach_w / HBM_PEAK_GBS,
-                                  "traffic": load_traffic("ret_recurrent_step", dw.name),
-                                  "kernel": "ret_recurrent_step", "kernel_avg_us": us_warm,
-                                  "alg_bytes_per_launch": db,
-                                  "state": "warm: one 16 MiB state, held by the Infinity Cache between steps"}},
+            "steps_per_s": 1e6 / us_main, "tokens_per_s": dw.B * 1e6 / us_main, "us_per_step": us_main,
+            "roofline": decode_roofline(us_cold, dw.name + " mall-cold", cold_state) if us_cold is not None
+            else decode_roofline(us_warm, dw.name, warm_state),
             "kernel_avg_us_eager": {"warm": k_warm, "mall_cold": k_cold},
         }
+        if us_cold is not None and us_warm is not None:
+            result["decode"]["warm"] = {"us_per_step": us_warm, "steps_per_s": 1e6 / us_warm,
+                                        "roofline": decode_roofline(us_warm, dw.name, warm_state)}
     if not args.no_epilogue:
         progress("epilogue")
         result["epilogue"] = bench_epilogue(R, W, torch, CHUNK_WORKLOADS["retention-layer-d512"], args.steps)

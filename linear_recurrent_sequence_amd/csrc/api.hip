@@ -357,6 +357,21 @@ struct EpiRequest {
 
 // ret_chunkwise_fwd's work. With `epi`, the kernel applies the epilogue to the outputs before storing them where
 // it holds whole head rows (the on-chip kernel with bf16 output and d_v = 64), and *fused says whether it did.
+// The kernel set and plan of a chunkwise call. A set whose kernels stage operands as given only (pre_only)
+// gives way to its fallback variant when q and k need rotating and the workspace holds no rotated copies.
+bool resolve_chunk(ret_dtype_t in_dt, int B, int N, int H, int dk, int dv, int chunk, bool rotate, size_t avail,
+                   const Opts& op, ChunkKernels* ck, ChunkPlan* plan) {
+    if (!pick_chunk(in_dt, dk, dv, chunk, ck, op)) return false;
+    *plan = plan_chunk(*ck, B, N, H, dk, dv, chunk, rotate, avail, op);
+    if (ck->pre_only && rotate && plan->rot_bytes == 0) {
+        Opts o2 = op;
+        o2.variant = ck->fallback_variant;
+        if (!pick_chunk(in_dt, dk, dv, chunk, ck, o2) || ck->pre_only) return false;
+        *plan = plan_chunk(*ck, B, N, H, dk, dv, chunk, rotate, avail, o2);
+    }
+    return true;
+}
+
 ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o, int B, int N, int H, int dk,
                            int dv, ret_dtype_t in_dt, ret_dtype_t out_dt, const float* gamma, const double* theta,
                            int64_t pos0, int chunk, const float* state_in, float* state_out, void* workspace,
@@ -370,16 +385,16 @@ ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o,
         return fail(RET_ERR_INVALID_ARG, "state buffers must be 16-byte aligned");
     if (workspace_bytes > 0 && !workspace) return fail(RET_ERR_WORKSPACE, "workspace_bytes > 0 with a null workspace");
     if (workspace && !aligned16(workspace)) return fail(RET_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-    ChunkKernels ck;
-    if (!pick_chunk(in_dt, dk, dv, chunk, &ck, op))
-        return fail(RET_ERR_UNSUPPORTED, "chunkwise form: unsupported d_k=%d d_v=%d chunk=%d for %s input", dk, dv,
-                    chunk, in_dt == RET_F32 ? "F32" : "BF16");
-    if (rev && !ck.fused) return fail(RET_ERR_UNSUPPORTED, "reversed chunkwise run: not available for this shape");
     // The kernels address one chunk of one head with 32-bit byte offsets.
     if ((long long)chunk * H * (dk > dv ? dk : dv) * 4 >= (1LL << 31))
         return fail(RET_ERR_UNSUPPORTED, "chunkwise form: chunk*H*max(d_k,d_v) too large (%d*%d*%d)", chunk, H,
                     dk > dv ? dk : dv);
-    const ChunkPlan plan = plan_chunk(ck, B, N, H, dk, dv, chunk, theta != nullptr, workspace_bytes, op);
+    ChunkKernels ck;
+    ChunkPlan plan;
+    if (!resolve_chunk(in_dt, B, N, H, dk, dv, chunk, theta != nullptr, workspace_bytes, op, &ck, &plan))
+        return fail(RET_ERR_UNSUPPORTED, "chunkwise form: unsupported d_k=%d d_v=%d chunk=%d for %s input", dk, dv,
+                    chunk, in_dt == RET_F32 ? "F32" : "BF16");
+    if (rev && !ck.fused) return fail(RET_ERR_UNSUPPORTED, "reversed chunkwise run: not available for this shape");
     const int nseg = plan.nseg, seg_len = plan.seg_len;
 
     FwdArgs A;
@@ -408,7 +423,6 @@ ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o,
             A.orot = 1;
             for (int i = 0; i < dv / 2; ++i) A.theta[i] = out_theta[i];
         }
-        const char* name = onchip ? "ret_chunk_seg" : "ret_chunk_fused";
         if (!theta) {
             fn = fn_pre;
             A.qr = const_cast<void*>(q);
@@ -423,9 +437,11 @@ ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o,
             if ((st = launch_status("ret_rotate_qk")) != RET_OK) return st;
         }
         const unsigned grid = (unsigned)((long long)nseg * B * H * ntiles);
-        const int threads = onchip || !ck.threads          ? kThreads
-                            : fn == ck.fused_pre && ck.threads_pre ? ck.threads_pre
-                                                                 : ck.threads;
+        if (ck.pre_only && fn != fn_pre)
+            return fail(RET_ERR_UNSUPPORTED, "chunkwise form: kernel set without in-staging rotation");
+        const bool pre = !onchip && fn == ck.fused_pre;
+        const int threads = onchip || !ck.threads ? kThreads : pre && ck.threads_pre ? ck.threads_pre : ck.threads;
+        const char* name = onchip ? "ret_chunk_seg" : pre && ck.pre_name ? ck.pre_name : "ret_chunk_fused";
         if (epi && onchip && out_dt == RET_BF16 && dv == 64) {
             A.epi = 1;
             A.gate = epi->gate;
@@ -1108,26 +1124,30 @@ ret_status_t ret_chunkwise_fwd_noalloc(const void* q, const void* k, const void*
     if (st != RET_OK) return st;
     if (chunk <= 0) return fail(RET_ERR_INVALID_ARG, "chunk must be positive (got %d)", chunk);
     ChunkKernels ck;
-    if (!pick_chunk(in_dt, dk, dv, chunk, &ck))
+    ChunkPlan full;
+    if (!resolve_chunk(in_dt, B, N, H, dk, dv, chunk, theta != nullptr, SIZE_MAX, kDefaultOpts, &ck, &full))
         return fail(RET_ERR_UNSUPPORTED, "chunkwise form: unsupported d_k=%d d_v=%d chunk=%d for %s input", dk, dv,
                     chunk, in_dt == RET_F32 ? "F32" : "BF16");
     // The library's own segment plan; its chain must fit in the scratch (the rotated copies of q and k are
     // dropped when they do not: staging then rotates, which changes only the rounding).
-    const ChunkPlan full = plan_chunk(ck, B, N, H, dk, dv, chunk, theta != nullptr, SIZE_MAX);
     if (full.chain_bytes > (size_t)RET_NOALLOC_SCRATCH_BYTES)
         return fail(RET_ERR_WORKSPACE,
                     "no-allocation chunkwise call: the segment chain of this shape needs %zu bytes, more than the "
                     "%u-byte scratch array; use ret_chunkwise_fwd with a workspace",
                     full.chain_bytes, (unsigned)RET_NOALLOC_SCRATCH_BYTES);
-    // the chain must also keep its counters and flags inside the region the set-up zeroed
-    if (full.nseg > 1 && ck.fused && chain_layout(B * H * (dv / ck.dvt), full.nseg, dk * ck.dvt).agg_off > kChainMeta)
-        return fail(RET_ERR_WORKSPACE, "no-allocation chunkwise call: %d units x %d segments exceed the chain's "
-                    "counter and flag region", B * H * (dv / ck.dvt), full.nseg);
-    void* ws = nullptr;
-    if ((st = scratch_of_device((hipStream_t)stream, &ws)) != RET_OK) return st;
     const size_t avail = full.chain_bytes + full.rot_bytes <= (size_t)RET_NOALLOC_SCRATCH_BYTES
                              ? full.chain_bytes + full.rot_bytes
                              : full.chain_bytes;
+    // the plan the call takes in that room: its chain must keep its counters and flags inside the region the
+    // set-up zeroed
+    ChunkPlan used;
+    if (!resolve_chunk(in_dt, B, N, H, dk, dv, chunk, theta != nullptr, avail, kDefaultOpts, &ck, &used))
+        return fail(RET_ERR_UNSUPPORTED, "chunkwise form: unsupported d_k=%d d_v=%d chunk=%d", dk, dv, chunk);
+    if (used.nseg > 1 && ck.fused && chain_layout(B * H * (dv / ck.dvt), used.nseg, dk * ck.dvt).agg_off > kChainMeta)
+        return fail(RET_ERR_WORKSPACE, "no-allocation chunkwise call: %d units x %d segments exceed the chain's "
+                    "counter and flag region", B * H * (dv / ck.dvt), used.nseg);
+    void* ws = nullptr;
+    if ((st = scratch_of_device((hipStream_t)stream, &ws)) != RET_OK) return st;
     return chunkwise_run(q, k, v, o, B, N, H, dk, dv, in_dt, out_dt, gamma, theta, pos0, chunk, state_in, state_out,
                          ws, avail, stream, nullptr, nullptr, kDefaultOpts);
 }

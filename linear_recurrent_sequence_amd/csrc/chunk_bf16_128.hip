@@ -13,6 +13,7 @@ ChunkKernels chunk_entry_wide128() {
     k.threads_pre = kWideThreads;
     k.pre_always = 1;
     k.target_wgs = 512;
+    k.pre_name = "ret_chunk_wide";
     return k;
 }
 

@@ -1,9 +1,13 @@
 // bf16-input chunkwise kernels, d_k in {256}, chunk in {32, 64, 128, 256, 512} (chunks longer than 64 tokens
-// run as 64-token sub-chunks: the instances differ only in the segment plan). Where d_v is a multiple of 128 the d_v
-// tile is 128 columns. `variant` picks 0 (default) or 3: the wide-head kernel (256 threads whose waves own 32
-// columns, 32-token steps, operands rotated once up front), 1: the chained kernel with 256 threads x 32 columns,
-// 2: the 256-thread kernel with 16-column waves and d_v tiles of 64, anything else: the chained kernel with 512
-// threads x 16 columns (two waves per SIMD). Other d_v: 256 threads with d_v tiles of 64.
+// run as 64-token sub-chunks: the instances differ only in the segment plan). `variant` picks
+//   0 (default): the wide-head kernel where d_v is a multiple of 128 (variant 3), else the 256-thread kernel
+//      with d_v tiles of 64;
+//   3: the wide-head kernel (four waves of 32 columns, 32-token steps, operands staged through registers, q and
+//      k rotated once up front);
+//   5: the LDS-loading wide-head kernel (d_v a multiple of 256: eight waves of 32 columns, operands loaded
+//      straight into the LDS; with rotation and no room for rotated copies in the workspace, variant 4);
+//   1: the chained kernel with 256 threads x 32 columns; 2: the 256-thread kernel with 16-column waves and d_v
+//   tiles of 64; 4 (or any other): the chained kernel with 512 threads x 16 columns (two waves per SIMD).
 #include "chunk_bf16.h"
 
 namespace ret {
@@ -16,13 +20,33 @@ ChunkKernels chunk_entry_wide256() {
     k.fused_pre = chunk_wide_get(256);
     k.threads_pre = kWideThreads;
     k.pre_always = 1;
+    k.pre_name = "ret_chunk_wide";
+    return k;
+}
+
+// The LDS-loading wide-head kernel alone (it only stages operands as given).
+template <int C>
+ChunkKernels chunk_entry_dma256() {
+    ChunkKernels k = chunk_entry_bf16<256, C, 512>();
+    k.fused = k.fused_pre = chunk_dma_get(256);
+    k.dvt = kDmaDvt;
+    k.threads = k.threads_pre = kDmaThreads;
+    k.pre_always = 1;
+    k.pre_only = 1;
+    k.fallback_variant = 4;
+    k.target_wgs = 256;  // one workgroup per CU
+    k.pre_name = "ret_chunk_dma";
     return k;
 }
 
 bool chunk_kernels_bf16_256(int dk, int dv, int C, int variant, ChunkKernels* out) {
     if (dv % 64) return false;
-    if ((variant == 0 || variant == 3) && dv % 128 == 0 && dk == 256 &&
-        (C == 32 || C == 64 || C == 128 || C == 256 || C == 512)) {
+    const bool chunk_ok = C == 32 || C == 64 || C == 128 || C == 256 || C == 512;
+    if (variant == 5 && dv % kDmaDvt == 0 && dk == 256 && chunk_ok) {
+        *out = C == 32 ? chunk_entry_dma256<32>() : C == 64 ? chunk_entry_dma256<64>() : chunk_entry_dma256<128>();
+        return true;
+    }
+    if ((variant == 0 || variant == 3) && dv % 128 == 0 && dk == 256 && chunk_ok) {
         *out = C == 32 ? chunk_entry_wide256<32>() : C == 64 ? chunk_entry_wide256<64>() : chunk_entry_wide256<128>();
         return true;
     }

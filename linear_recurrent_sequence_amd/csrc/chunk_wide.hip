@@ -1,15 +1,24 @@
-// Instances of the wide-head chunkwise kernel. This source is compiled with the MFMA accumulators held in
-// architectural registers (build.py): the kernel's state is read back as MFMA operands every step, and
+// Instances of the wide-head chunkwise kernels. This source is compiled with the MFMA accumulators held in
+// architectural registers (build.py): the kernels' state is read back as MFMA operands every step, and
 // accumulators in the accumulation registers would cost a move for each of those reads.
+#include "chunk_dma_bf16.h"
 #include "chunk_wide_bf16.h"
 
 namespace ret {
 
 static_assert(WideB<256>::NT == kWideThreads && WideB<128>::NT == kWideThreads, "workgroup size");
+static_assert(DmaB<256>::NT == kDmaThreads && DmaB<128>::NT == kDmaThreads, "workgroup size");
+static_assert(DmaB<256>::DVT == kDmaDvt && DmaB<128>::DVT == kDmaDvt, "d_v tile");
 
 fwd_kernel_t chunk_wide_get(int dk) {
     if (dk == 256) return chunk_wide_bf16<256>;
     if (dk == 128) return chunk_wide_bf16<128>;
+    return nullptr;
+}
+
+fwd_kernel_t chunk_dma_get(int dk) {
+    if (dk == 256) return chunk_dma_bf16<256>;
+    if (dk == 128) return chunk_dma_bf16<128>;
     return nullptr;
 }
 

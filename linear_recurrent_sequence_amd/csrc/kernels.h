@@ -961,6 +961,10 @@ struct ChunkKernels {
     int threads_pre;  // workgroup size of fused_pre where it differs from `threads` (0: the same)
     int pre_always;   // fused_pre stages operands as given only: with rotation, q and k are rotated up front
                       // whenever the workspace holds the copies
+    int pre_only;     // `fused` is fused_pre too: with rotation and no room for rotated copies, the set gives way
+                      // to the kernel set of `fallback_variant`
+    int fallback_variant;
+    const char* pre_name;  // timer name of fused_pre launches (null: the set's default)
 };
 struct ParKernel {
     fwd_kernel_t fn;
@@ -991,6 +995,10 @@ bool chunk_kernels_bf16_256(int dk, int dv, int C, int variant, ChunkKernels* ou
 // of 128, operands staged as given.
 constexpr int kWideThreads = 256;
 fwd_kernel_t chunk_wide_get(int dk);
+// The LDS-loading wide-head kernel (chunk_dma_bf16.h) for d_k in {128, 256} (null otherwise): kDmaThreads
+// threads, d_v tiles of kDmaDvt, operands staged as given.
+constexpr int kDmaThreads = 512, kDmaDvt = 256;
+fwd_kernel_t chunk_dma_get(int dk);
 bool parallel_kernel_get(bool bf16_in, int dk, int dv, ParKernel* out);
 // Decode kernel for a (d_k, column tile cw, rows per wave wr) tile, 0 = default, null if none; with pairs_mode 0
 // it groups (b, h) pairs into workgroups of up to 8 waves where B*H leaves a workgroup per CU; 1 / 2 force one

@@ -119,9 +119,9 @@ def test_chunkwise_small(R, case):
 
 @pytest.mark.parametrize("threads", ["wide", "256x2", "512", "256"])
 def test_chunkwise_dk256_workgroup_sizes(R, threads):
-    """d_k 256 with d_v tiles of 128 (the wide-head kernel: the default; the chained kernel with 512 threads whose
-    waves own 16 columns, or 256 threads of 32 columns), and the 256-thread kernels with d_v tiles of 64. All match
-    the oracle, with two segments and 3 d_v tiles of 128."""
+    """d_k 256 with d_v tiles of 128 (the wide-head kernel: the default where d_v is not a multiple of 256; the
+    chained kernel with 512 threads whose waves own 16 columns, or 256 threads of 32 columns), and the 256-thread
+    kernels with d_v tiles of 64. All match the oracle, with two segments and 3 d_v tiles of 128."""
     opts = {"variant": {"wide": 0, "512": 4, "256x2": 1, "256": 2}[threads], "segments": 2}
     B, N, H, dk, dv, C = 1, 300, 2, 256, 384, 64
     print_case("dk256 threads=%s" % threads, (B, N, H, dk, dv, C))
@@ -174,6 +174,64 @@ def test_chunkwise_wide_kernel(R, case):
         eo, es = rel_err(o[:, :, h], o_ref[:, :, h]), rel_err(s[:, h], s_ref[:, h])
         print("  head %d err o=%.3g state=%.3g" % (h, eo, es))
         assert eo <= tol("bf16") and es <= tol("bf16"), (h, eo, es)
+
+
+DMA = [  # (B, N, H, d_v, chunk, rotation, state_in, segments, options)
+    (1, 333, 2, 256, 64, True, True, 3, {}),
+    (2, 37, 1, 256, 64, True, False, None, {}),
+    (1, 1, 2, 512, 32, True, True, None, {}),
+    (1, 200, 2, 256, 32, False, True, 2, {}),
+    (1, 300, 1, 512, 128, True, False, 2, {}),
+    (1, 129, 3, 256, 512, True, True, 1, {}),
+    (1, 1000, 2, 256, 128, True, True, 9, {}),
+    (1, 333, 2, 256, 64, True, True, 3, {"prerotate": 0}),  # no rotated copies: the 512-thread kernel instead
+]
+
+
+@pytest.mark.parametrize("case", DMA, ids=lambda c: "B%d-N%d-H%d-dv%d-C%d-rot%d-s%d-seg%s-%s" % (
+    c[:8] + ("".join("%s%s" % kv for kv in c[8].items()) or "default",)))
+def test_chunkwise_dma_kernel(R, case):
+    """The LDS-loading wide-head kernel (d_k 256, d_v tiles of 256, variant 5): ragged tails shorter than
+    one step, with and without rotation and an incoming state, one to nine chained segments, chunks of 32 to 512
+    tokens; and the same call without room for rotated copies, which takes the 512-thread kernel. Matches the
+    oracle's output and final state per head."""
+    B, N, H, dv, C, rot, with_state, segs, extra = case
+    dk = 256
+    print_case("dma", case)
+    opts = dict(extra, variant=5)
+    if segs is not None:
+        opts["segments"] = segs
+    rng = np.random.default_rng(700 + N + dv)
+    q = W.normal(rng, (B, N, H, dk), 16.0, "bf16")
+    k = W.normal(rng, (B, N, H, dk), 16.0, "bf16")
+    v = W.normal(rng, (B, N, H, dv), 16.0, "bf16")
+    s0 = rng.standard_normal((B, H, dk, dv)).astype(np.float32) if with_state else None
+    gamma = W.gamma_schedule(H)
+    theta = W.theta_schedule(dk) if rot else None
+    o_ref, s_ref = oracle.chunkwise(q, k, v, gamma, C, theta=theta, pos0=3, state_in=s0)
+    o, s = _gpu_chunkwise(R, q, k, v, "bf16", gamma, C, theta=theta, pos0=3, s_in=s0, options=opts)
+    for h in range(H):
+        eo, es = rel_err(o[:, :, h], o_ref[:, :, h]), rel_err(s[:, h], s_ref[:, h])
+        print("  head %d err o=%.3g state=%.3g" % (h, eo, es))
+        assert eo <= tol("bf16") and es <= tol("bf16"), (h, eo, es)
+
+
+def test_chunkwise_dma_kernel_is_launched(R):
+    """d_k 256 with d_v 512 and variant 5: the plan launches the LDS-loading kernel (timer name ret_chunk_dma),
+    after the up-front rotation."""
+    import torch
+    B, N, H, dk, dv, C = 1, 256, 2, 256, 512, 128
+    rng = np.random.default_rng(5)
+    q = to_dev(W.normal(rng, (B, N, H, dk), 8.0, "bf16"), "bf16")
+    k = to_dev(W.normal(rng, (B, N, H, dk), 8.0, "bf16"), "bf16")
+    v = to_dev(W.normal(rng, (B, N, H, dv), 8.0, "bf16"), "bf16")
+    o = empty_out((B, N, H, dv), "bf16")
+    timer = R.Timer()
+    R.ret_chunkwise_fwd(q, k, v, o, W.gamma_schedule(H), C, theta=W.theta_schedule(dk),
+                        workspace=R.chunkwise_workspace(q, v, C, {"variant": 5}), options={"timer": timer, "variant": 5})
+    torch.cuda.synchronize()
+    assert timer.query("ret_chunk_dma")[1] == 1 and timer.query("ret_rotate_qk")[1] == 1
+    timer.close()
 
 
 @pytest.mark.parametrize("onchip", ["1", "0"])
