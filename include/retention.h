@@ -218,8 +218,8 @@ ret_status_t ret_chunkwise_bwd(const void* q, const void* k, const void* v, cons
  * call holds one, every kernel it launches is bracketed by a pair of HIP events on the launch stream and
  * recorded in it (the library keeps no timing state of its own). ret_timer_query synchronises those events and
  * returns the total milliseconds and launch count recorded for kernels whose name equals `kernel` ("" or NULL =
- * all). Kernel names: "ret_chunk_seg", "ret_chunk_fused", "ret_chunk_wide", "ret_chunk_dma" and "ret_rotate_qk"
- * (bf16 input), "ret_chunk_full", "ret_chunk_local", "ret_segment_scan" (fp32 input), "ret_parallel",
+ * all). Kernel names: "ret_chunk_seg", "ret_chunk_fused", "ret_chunk_wide", "ret_chunk_dma_local",
+ * "ret_chunk_dma_scan", "ret_chunk_dma" and "ret_rotate_qk" (bf16 input), "ret_chunk_full", "ret_chunk_local", "ret_segment_scan" (fp32 input), "ret_parallel",
  * "ret_recurrent_step", "ret_msr_epilogue", "ret_permute_rotate" (gradients), "ret_norm_zseg", "ret_norm_rows",
  * "ret_norm_scale", "ret_norm_step" (score normalizations). A timer must not be attached to calls that are being captured into a
  * graph. One timer may be shared by calls on several threads.
@@ -239,10 +239,11 @@ void ret_timer_reset(ret_timer_t* t);
  *   prerotate    -1: planner; 0: q and k rotated while staging; 1: rotated once up front into the workspace
  *   onchip       -1 or 1: the on-chip segment kernel where segments fit (d_k <= 64, <= 256 tokens); 0: never
  *   variant      0: default kernel of the shape; d_v a multiple of 128: 3 = the wide-head kernel (32-token steps,
- *                q and k rotated once up front; the default for d_k = 256); d_k = 256: 5 = the LDS-loading
- *                wide-head kernel (d_v a multiple of 256; gives way to 4 when q and k need rotating and the
- *                workspace has no room for rotated copies), 1 = 256 threads whose waves own 32 columns,
- *                2 = 256 threads with d_v tiles of 64, 4 = 512 threads x 16 columns
+ *                q and k rotated once up front; the default for d_k = 256 where d_v is not a multiple of 256);
+ *                d_k = 256: 5 = the LDS-loading wide-head kernels (d_v a multiple of 256, the default there:
+ *                local passes, a scan, the full pass; gives way to 4 when q and k need rotating and the workspace
+ *                has no room for rotated copies), 1 = 256 threads whose waves own 32 columns, 2 = 256 threads
+ *                with d_v tiles of 64, 4 = 512 threads x 16 columns
  *   step_cw, step_wr, step_pairs   decode tile: columns per workgroup (16, 32, 64), rows per wave (16, 32, 64),
  *                pairs (0 planner, 1 one (b, h) per workgroup, 2 grouped); 0 = default
  *   bwd_direct   -1 or 1: gradients by the reversed traversal where available; 0: through reordered copies

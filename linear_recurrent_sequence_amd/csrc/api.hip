@@ -194,6 +194,8 @@ void plan_segments(int B, int N, int H, int dv, int C, int dvt, int target_wgs, 
 // (sequence, segment) for the split kernels.
 size_t segment_ws_bytes(const ChunkKernels& ck, int B, int H, int dk, int dv, int nseg) {
     if (nseg <= 1) return 0;
+    // the split launches: a state slot per (unit, segment) after the chain's (untouched) first kChainMeta bytes
+    if (ck.split_local) return kChainMeta + (size_t)B * H * (dv / ck.dvt) * nseg * dk * ck.dvt * sizeof(float);
     if (ck.fused) return chain_layout(B * H * (dv / ck.dvt), nseg, dk * ck.dvt).bytes;
     return sizeof(ChainHeader) + (size_t)B * H * nseg * dk * dv * sizeof(float);
 }
@@ -439,6 +441,27 @@ ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o,
         const unsigned grid = (unsigned)((long long)nseg * B * H * ntiles);
         if (ck.pre_only && fn != fn_pre)
             return fail(RET_ERR_UNSUPPORTED, "chunkwise form: kernel set without in-staging rotation");
+        if (ck.split_local) {
+            // local passes, the scan of their states, then the full pass of every segment (no chain)
+            if (epi || onchip) return fail(RET_ERR_UNSUPPORTED, "chunkwise form: split launches with this plan");
+            A.ws = workspace ? (float*)((char*)workspace + kChainMeta) : nullptr;
+            const unsigned units = (unsigned)((long long)B * H * ntiles);
+            if (nseg > 1) {
+                LaunchTimer tl("ret_chunk_dma_local", s, op);
+                hipLaunchKernelGGL(ck.split_local, dim3(units * (unsigned)(nseg - 1)), dim3(ck.threads_pre), 0, s, A);
+                tl.done();
+                if ((st = launch_status("ret_chunk_dma_local")) != RET_OK) return st;
+                LaunchTimer tc("ret_chunk_dma_scan", s, op);
+                hipLaunchKernelGGL(ck.split_scan, dim3((unsigned)((long long)dk * ck.dvt / 1024), units), dim3(256), 0,
+                                   s, A);
+                tc.done();
+                if ((st = launch_status("ret_chunk_dma_scan")) != RET_OK) return st;
+            }
+            LaunchTimer tm(ck.pre_name, s, op);
+            hipLaunchKernelGGL(fn, dim3(grid), dim3(ck.threads_pre), 0, s, A);
+            tm.done();
+            return launch_status(ck.pre_name);
+        }
         const bool pre = !onchip && fn == ck.fused_pre;
         const int threads = onchip || !ck.threads ? kThreads : pre && ck.threads_pre ? ck.threads_pre : ck.threads;
         const char* name = onchip ? "ret_chunk_seg" : pre && ck.pre_name ? ck.pre_name : "ret_chunk_fused";
@@ -562,7 +585,8 @@ bool bwd_layout(int B, int N, int H, int dk, int dv, int chunk, ret_dtype_t in_d
 ret_status_t chain_meta_zero(ret_dtype_t in_dt, int B, int N, int H, int dk, int dv, int chunk, void* chain,
                              size_t chain_bytes, hipStream_t s, const Opts& op) {
     ChunkKernels ck;
-    if (!pick_chunk(in_dt, dk, dv, chunk, &ck, op) || !ck.fused) return RET_OK;  // the split kernels keep no flags
+    // the split kernels keep no flags
+    if (!pick_chunk(in_dt, dk, dv, chunk, &ck, op) || !ck.fused || ck.split_local) return RET_OK;
     const ChunkPlan p = plan_chunk(ck, B, N, H, dk, dv, chunk, false, chain_bytes, op);
     if (p.nseg <= 1) return RET_OK;
     const ChainLayout lay = chain_layout(B * H * (dv / ck.dvt), p.nseg, dk * ck.dvt);
@@ -1143,7 +1167,8 @@ ret_status_t ret_chunkwise_fwd_noalloc(const void* q, const void* k, const void*
     ChunkPlan used;
     if (!resolve_chunk(in_dt, B, N, H, dk, dv, chunk, theta != nullptr, avail, kDefaultOpts, &ck, &used))
         return fail(RET_ERR_UNSUPPORTED, "chunkwise form: unsupported d_k=%d d_v=%d chunk=%d", dk, dv, chunk);
-    if (used.nseg > 1 && ck.fused && chain_layout(B * H * (dv / ck.dvt), used.nseg, dk * ck.dvt).agg_off > kChainMeta)
+    if (used.nseg > 1 && ck.fused && !ck.split_local &&
+        chain_layout(B * H * (dv / ck.dvt), used.nseg, dk * ck.dvt).agg_off > kChainMeta)
         return fail(RET_ERR_WORKSPACE, "no-allocation chunkwise call: %d units x %d segments exceed the chain's "
                     "counter and flag region", B * H * (dv / ck.dvt), used.nseg);
     void* ws = nullptr;

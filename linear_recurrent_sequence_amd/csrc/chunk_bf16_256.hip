@@ -1,11 +1,12 @@
 // bf16-input chunkwise kernels, d_k in {256}, chunk in {32, 64, 128, 256, 512} (chunks longer than 64 tokens
 // run as 64-token sub-chunks: the instances differ only in the segment plan). `variant` picks
-//   0 (default): the wide-head kernel where d_v is a multiple of 128 (variant 3), else the 256-thread kernel
-//      with d_v tiles of 64;
+//   0 (default): variant 5 where d_v is a multiple of 256, else variant 3 where d_v is a multiple of 128, else
+//      the 256-thread kernel with d_v tiles of 64;
 //   3: the wide-head kernel (four waves of 32 columns, 32-token steps, operands staged through registers, q and
 //      k rotated once up front);
-//   5: the LDS-loading wide-head kernel (d_v a multiple of 256: eight waves of 32 columns, operands loaded
-//      straight into the LDS; with rotation and no room for rotated copies in the workspace, variant 4);
+//   5: the LDS-loading wide-head kernels (d_v a multiple of 256: local passes, a scan of their states and the
+//      full pass, eight waves of 32 columns, operands loaded straight into the LDS; with rotation and no room for
+//      rotated copies in the workspace, variant 4);
 //   1: the chained kernel with 256 threads x 32 columns; 2: the 256-thread kernel with 16-column waves and d_v
 //   tiles of 64; 4 (or any other): the chained kernel with 512 threads x 16 columns (two waves per SIMD).
 #include "chunk_bf16.h"
@@ -24,11 +25,15 @@ ChunkKernels chunk_entry_wide256() {
     return k;
 }
 
-// The LDS-loading wide-head kernel alone (it only stages operands as given).
+// The LDS-loading wide-head kernels alone (they only stage operands as given): local pass, scan, full pass.
 template <int C>
 ChunkKernels chunk_entry_dma256() {
     ChunkKernels k = chunk_entry_bf16<256, C, 512>();
-    k.fused = k.fused_pre = chunk_dma_get(256);
+    DmaKernels d;
+    chunk_dma_get(256, &d);
+    k.fused = k.fused_pre = d.full;
+    k.split_local = d.local;
+    k.split_scan = d.scan;
     k.dvt = kDmaDvt;
     k.threads = k.threads_pre = kDmaThreads;
     k.pre_always = 1;
@@ -42,7 +47,7 @@ ChunkKernels chunk_entry_dma256() {
 bool chunk_kernels_bf16_256(int dk, int dv, int C, int variant, ChunkKernels* out) {
     if (dv % 64) return false;
     const bool chunk_ok = C == 32 || C == 64 || C == 128 || C == 256 || C == 512;
-    if (variant == 5 && dv % kDmaDvt == 0 && dk == 256 && chunk_ok) {
+    if ((variant == 0 || variant == 5) && dv % kDmaDvt == 0 && dk == 256 && chunk_ok) {
         *out = C == 32 ? chunk_entry_dma256<32>() : C == 64 ? chunk_entry_dma256<64>() : chunk_entry_dma256<128>();
         return true;
     }

@@ -1,16 +1,21 @@
-// bf16 chunkwise kernel for wide heads (d_k in {128, 256}) with d_v tiles of 256, on operands staged as given
-// (q and k rotated once up front, or no rotation). Same computation, state bookkeeping and segment chain as the
-// four-wave wide kernel (chunk_wide_bf16.h); what differs is how operands reach the LDS and how many waves share
-// them:
-//  * eight waves, two per SIMD, each owning a d_k x 32 block of the state; one workgroup per compute unit, so
-//    every SIMD has a second wave to issue while one waits on the LDS;
-//  * q', k' and v rows go from memory straight into the LDS (buffer loads with the LDS bit: no staging
-//    registers, no copy instructions), three steps deep: the loads of step c + 2 are issued when step c starts
-//    and waited for with explicit counts, so a step's operands have two steps' time to arrive;
-//  * the decay weights of the state update, zeta'_l = gamma^-(T + l + 1), are applied to the V^T fragments in
-//    registers (16 values per lane and step) instead of to a scaled copy of V in the LDS;
-//  * one d_v tile of 256 stages the q' and k' rows and computes the causal scores once for 256 columns.
-// Chunks of 64 or more tokens run as 32-token sub-chunks.
+// bf16 chunkwise kernels for wide heads (d_k in {128, 256}) with d_v tiles of 256, on operands staged as given
+// (q and k rotated once up front, or no rotation), in three launches instead of one chained launch:
+//  1. chunk_dma_local_bf16: every segment but the last runs the state recurrence from zero over its tokens,
+//     R_s = sum_t gamma^(L-1-t) k'_t^T v_t (the chunkwise carry without outputs), and stores it in slot s + 1 of
+//     its unit (one d_v tile of one (b, h)) in the workspace;
+//  2. unit_scan_kernel: per unit and element, slot s becomes the state entering segment s from zero,
+//     W_s = gamma^T W_(s-1) + R_(s-1), W_0 = 0 (T tokens per segment);
+//  3. chunk_dma_full_bf16: every segment runs the chunkwise form from W_s + gamma^(sT) state_in, writing the
+//     outputs (and the last segment the final state).
+// No workgroup waits for another, so no segment chain is needed, and each kernel holds only what its pass needs.
+// The full pass: eight waves, two per SIMD, each owning a d_k x 32 block of the state; 32-token steps; q', k' and v
+// rows go from memory straight into the LDS (buffer loads with the LDS bit), three steps deep, waited for with
+// explicit counts; the decay weights of the state update, zeta'_l = gamma^-(T + l + 1), are applied to the V^T
+// fragments in registers; the state is carried unscaled between rescales (R = gamma^T R^). One d_v tile of 256
+// stages the q' and k' rows and computes the causal scores once for 256 columns. The local pass stages k' and v
+// through registers (loads straight into the LDS issue too slowly when a step holds only the state update).
+// Chunks of 64 or more tokens run as 32-token sub-chunks (the chunkwise form gives the same result for any chunk
+// size, up to rounding).
 #pragma once
 
 #include "chunk_bf16.h"
@@ -106,52 +111,252 @@ __device__ __forceinline__ bf16x8_t scale_frag(bf16x8_t f, const float* z) {
     return __builtin_bit_cast(bf16x8_t, pack8(x));
 }
 
+
+// The unit and segment of a workgroup of a grid of units x segments workgroups, segment-major. Workgroups go to
+// the 8 XCDs in turn (launch index mod 8); when a segment's units divide evenly, the d_v tiles of one (b, h)
+// get launch indices of one residue, so they run on one XCD and its L2 serves the q' and k' rows they all load.
+__device__ __forceinline__ void unit_seg_of_block(int ntiles, int units, int* unit, int* seg) {
+    const int bid = blockIdx.x, s = bid / units, r = bid % units;
+    int u = r;
+    if (ntiles > 1 && units % (8 * ntiles) == 0) {
+        const int xcd = r % 8, q8 = r / 8;
+        u = ((q8 / ntiles) * 8 + xcd) * ntiles + q8 % ntiles;
+    }
+    *unit = __builtin_amdgcn_readfirstlane(u);
+    *seg = __builtin_amdgcn_readfirstlane(s);
+}
+
+// The values every pass of one workgroup shares.
 template <int DK>
-__global__ __launch_bounds__(512, 1) void chunk_dma_bf16(FwdArgs a) {
+struct DmaCtx {
+    typedef DmaB<DK> F;
+    int tid, lane, w, g4, n16;
+    int unit, seg, aN, aH, adv, anseg, aseg_len, pair, dv0, seg_n, nchunks, rsk, rsv;
+    float lg;
+    long long seg_t0, head0;
+    __device__ __forceinline__ DmaCtx(const FwdArgs& a) {
+        tid = threadIdx.x;
+        lane = tid & 63;
+        w = wave_id();
+        g4 = 4 * (lane >> 4);
+        n16 = lane & 15;
+        const int ntiles = __builtin_amdgcn_readfirstlane(a.dv / F::DVT);
+        const int units = __builtin_amdgcn_readfirstlane(a.B * a.H * ntiles);
+        unit_seg_of_block(ntiles, units, &unit, &seg);
+        aN = __builtin_amdgcn_readfirstlane(a.N);
+        aH = __builtin_amdgcn_readfirstlane(a.H);
+        const int adk = __builtin_amdgcn_readfirstlane(a.dk);
+        adv = __builtin_amdgcn_readfirstlane(a.dv);
+        anseg = __builtin_amdgcn_readfirstlane(a.nseg);
+        aseg_len = __builtin_amdgcn_readfirstlane(a.seg_len);
+        pair = unit / ntiles;
+        const int b = pair / aH, h = pair % aH;
+        dv0 = (unit % ntiles) * F::DVT;
+        lg = a.log2g[h];
+        seg_t0 = (long long)seg * aseg_len;
+        seg_n = (int)(min((long long)aN, seg_t0 + aseg_len) - seg_t0);
+        nchunks = (seg_n + F::C - 1) / F::C;
+        rsk = aH * adk;
+        rsv = aH * adv;
+        head0 = ((long long)b * aN + seg_t0) * aH + h;
+    }
+    // slot s of this unit (state slots of DK x DVT floats in the thread order of slot_store)
+    __device__ __forceinline__ float* slot(const FwdArgs& a, int s) const {
+        return a.ws + ((size_t)unit * anseg + s) * (size_t)(DK * F::DVT);
+    }
+    // R[x * 2 + j][e]: state row x * 16 + g4 + e, column dv0 + (2w + j) * 16 + n16 of the (b, h) state
+    __device__ __forceinline__ long long state_index(int x, int j, int e) const {
+        return ((long long)pair * DK + x * 16 + g4 + e) * adv + dv0 + (w * 2 + j) * 16 + n16;
+    }
+};
+
+// V^T fragments of wave w's two 16-column blocks of a Swz<256> V tile, scaled by zeta'_r = gamma^-(T + r + 1) for
+// the 8 token rows r of the lane's values (4g + i and 16 + 4g + i; zero from row L on).
+template <int DVT>
+__device__ __forceinline__ void vz_frags(const uint16_t* sV, int L, float T, float lg, int g4, int w, int lv_t,
+                                         bf16x8_t* fvz) {
+    float z[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int r = e < 4 ? g4 + e : 16 + g4 + e - 4;
+        z[e] = r < L ? gpow(lg, -(T + (float)(r + 1))) : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) fvz[j] = scale_frag(frag_trps<DVT>(sV, 0, (w * 2 + j) * 16, lv_t), z);
+}
+
+// ---- 1. the local pass of every segment but the last ----
+template <int DK>
+__global__ __launch_bounds__(512, 1) void chunk_dma_local_bf16(FwdArgs a) {
+    typedef DmaB<DK> F;
+    constexpr int NT = F::NT, C = F::C, NKB = F::NKB;
+    constexpr int NR = NKB * 2;
+    typedef typename F::ZQ ZK;
+    typedef typename F::ZV ZV;
+    typedef RowTile<C, DK, NT> TK;
+    typedef RowTile<C, F::DVT, NT> TV;
+    constexpr int BUFL = F::SQ + F::SV;  // one step: sK, sV
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * BUFL];
+    const DmaCtx<DK> x0(a);
+    const int tid = x0.tid, lane = x0.lane, w = x0.w, nchunks = x0.nchunks, seg_n = x0.seg_n;
+    const int rsk = x0.rsk, rsv = x0.rsv;
+    const float lg = x0.lg;
+    const uint16_t* kh = (const uint16_t*)a.kr + x0.head0 * __builtin_amdgcn_readfirstlane(a.dk);
+    const uint16_t* vh = (const uint16_t*)a.v + x0.head0 * x0.adv + x0.dv0;
+    const int lk_t = ZK::lane_trp(lane), lv_t = ZV::lane_trp(lane);
+    const int krow = tid / TK::SPR, kseg = tid % TK::SPR, vrow = tid / TV::SPR, vseg = tid % TV::SPR;
+    const int koff = (krow * rsk + kseg * 8) * 2, voff = (vrow * rsv + vseg * 8) * 2;
+
+    f32x4_t R[NR];
+#pragma unroll
+    for (int x = 0; x < NR; ++x) R[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float T = 0.f;  // tokens since the last rescale: R = gamma^T R^
+    auto rescale = [&]() __attribute__((always_inline)) {
+        const float f = gpow(lg, T);
+#pragma unroll
+        for (int x = 0; x < NR; ++x) R[x] *= f;
+        T = 0.f;
+    };
+    // k' and v rows of step c into register set par (two steps ahead); rows past the segment read as zero
+    u32x4_t lk[2][TK::NP], lv[2][TV::NP];
+    auto lissue = [&](int c, auto parc) __attribute__((always_inline)) {
+        constexpr int par = decltype(parc)::value;
+        const int L = min(C, seg_n - c * C);
+        const long long tc = (long long)c * C;
+        const rsrc_t rk = bytes_rsrc(kh + tc * rsk, L > 0 ? ((L - 1) * rsk + DK) * 2 : 0);
+        const rsrc_t rv = bytes_rsrc(vh + tc * rsv, L > 0 ? ((L - 1) * rsv + F::DVT) * 2 : 0);
+#pragma unroll
+        for (int p = 0; p < TK::NP; ++p) lk[par][p] = buf_load16(rk, koff, p * TK::RP * rsk * 2);
+#pragma unroll
+        for (int p = 0; p < TV::NP; ++p) lv[par][p] = buf_load16(rv, voff, p * TV::RP * rsv * 2);
+    };
+    auto lstep = [&](int c, auto parc) __attribute__((always_inline)) {
+        constexpr int par = decltype(parc)::value;
+        // a step of C tokens (segments before the last hold whole steps only): rescale first if gamma^-(T + C)
+        // could leave the range
+        if (-(T + (float)C) * lg > F::RESCALE_LOG2) rescale();
+        // buffer c & 1 was last read by step c - 2, which every wave finished before step c - 1's barrier
+        uint16_t* sK = smem + (c & 1) * BUFL;
+        uint16_t* sV = sK + F::SQ;
+#pragma unroll
+        for (int p = 0; p < TK::NP; ++p) lds_store16(sK + ZK::off(krow + p * TK::RP, kseg * 8), lk[par][p]);
+#pragma unroll
+        for (int p = 0; p < TV::NP; ++p) lds_store16(sV + ZV::off(vrow + p * TV::RP, vseg * 8), lv[par][p]);
+        lissue(c + 2, parc);  // (past the end too: the loads read zeros, and every path counts alike)
+        __syncthreads();
+        bf16x8_t fvz[2];
+        vz_frags<F::DVT>(sV, C, T, lg, x0.g4, w, lv_t, fvz);
+        // R^ <- R^ + K'^T (V (.) zeta'), a ring of 4 K'^T fragments in flight
+        constexpr int PD = 4;
+        bf16x8_t kr[PD];
+#pragma unroll
+        for (int x = 0; x < PD; ++x) kr[x] = frag_trps<DK>(sK, 0, x * 16, lk_t);
+#pragma unroll
+        for (int x = 0; x < NKB; ++x) {
+            const bf16x8_t ka = kr[x % PD];
+            if (x + PD < NKB) kr[x % PD] = frag_trps<DK>(sK, 0, (x + PD) * 16, lk_t);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) mfma(R[x * 2 + j], ka, fvz[j]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        T += (float)C;
+    };
+    // Pairs of steps with no branch inside, so both register sets are in the same state on every path around
+    // the loop, and the compiler's wait before a step's LDS stores covers that step's loads only.
+    const std::integral_constant<int, 0> set0;
+    const std::integral_constant<int, 1> set1;
+    lissue(0, set0);
+    lissue(1, set1);
+    int c = 0;
+    for (; c + 1 < nchunks; c += 2) {
+        lstep(c, set0);
+        lstep(c + 1, set1);
+    }
+    if (c < nchunks) lstep(c, set0);
+    rescale();
+    slot_store<NR, NT>(x0.slot(a, x0.seg + 1), R, tid);
+}
+
+// ---- 2. the states entering the segments: W_s = gamma^T W_(s-1) + W_s over s = 1 .. nseg-1, W_0 = 0 ----
+// One thread per 4 consecutive floats of a slot, grid (slot floats / 1024, units); the loads of a group of
+// segments are issued together, so the dependent chain costs one memory round trip per group.
+template <int DK>
+__global__ __launch_bounds__(256) void unit_scan_kernel(FwdArgs a) {
+    typedef DmaB<DK> F;
+    constexpr int G = 8;
+    constexpr long long PER = (long long)DK * F::DVT;
+    const int unit = blockIdx.y;
+    const long long e = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (e >= PER) return;
+    const int ntiles = a.dv / F::DVT, nseg = a.nseg;
+    const float decay = __builtin_amdgcn_exp2f((float)a.seg_len * a.log2g[(unit / ntiles) % a.H]);
+    float* W = a.ws + (long long)unit * nseg * PER + e;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    *reinterpret_cast<float4*>(W) = acc;
+    for (int g0 = 1; g0 < nseg; g0 += G) {
+        float4 u[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j)  // past the last segment re-read the last one (unused)
+            u[j] = *reinterpret_cast<const float4*>(W + (long long)min(g0 + j, nseg - 1) * PER);
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+            if (g0 + j < nseg) {
+                acc.x = decay * acc.x + u[j].x;
+                acc.y = decay * acc.y + u[j].y;
+                acc.z = decay * acc.z + u[j].z;
+                acc.w = decay * acc.w + u[j].w;
+                *reinterpret_cast<float4*>(W + (long long)(g0 + j) * PER) = acc;
+            }
+    }
+}
+
+// ---- 3. the full pass of every segment ----
+template <int DK>
+__global__ __launch_bounds__(512, 1) void chunk_dma_full_bf16(FwdArgs a) {
     typedef DmaB<DK> F;
     constexpr int NT = F::NT, NW = F::NW, C = F::C, NKB = F::NKB, KS = F::KS, NBUF = F::NBUF;
     constexpr int NR = NKB * 2;  // R[x * 2 + j]: d_k block x, d_v block 2w + j of the tile
     typedef typename F::ZQ ZQ;
     typedef typename F::ZV ZV;
     __shared__ __attribute__((aligned(16))) uint16_t smem[F::LDS_BYTES / 2];
-    __shared__ int s_word;  // broadcast word (ticket, counts)
     uint16_t* const sP = smem + NBUF * F::BUF;
-
-    const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g4 = 4 * (lane >> 4), n16 = lane & 15;
-    const int ntiles = __builtin_amdgcn_readfirstlane(a.dv / F::DVT);
-    const int units = __builtin_amdgcn_readfirstlane(a.B * a.H * ntiles);
-    const bool chained = a.nseg > 1;
-    const int unit = unit_of_block(ntiles, units);
-    int seg = __builtin_amdgcn_readfirstlane((int)(blockIdx.x / (unsigned)units));
-    Chain ch{};
-    if (chained) {
-        ch = chain_of(a.ws, units, a.nseg, unit, DK * F::DVT, a.chain_spin);
-        seg = chain_ticket(ch, s_word);
-    }
-    const int aN = __builtin_amdgcn_readfirstlane(a.N);
-    const int aH = __builtin_amdgcn_readfirstlane(a.H), adk = __builtin_amdgcn_readfirstlane(a.dk);
-    const int adv = __builtin_amdgcn_readfirstlane(a.dv), anseg = __builtin_amdgcn_readfirstlane(a.nseg);
-    const int aseg_len = __builtin_amdgcn_readfirstlane(a.seg_len);
-    const int pair = unit / ntiles;
-    const int b = pair / aH, h = pair % aH;
-    const int dv0 = (unit % ntiles) * F::DVT;
-    const float lg = a.log2g[h];
-    const long long seg_t0 = (long long)seg * aseg_len;
-    const int seg_n = (int)(min((long long)aN, seg_t0 + aseg_len) - seg_t0);
-    const int nchunks = (seg_n + C - 1) / C;
-    const int rsk = aH * adk, rsv = aH * adv;
-    const long long head0 = ((long long)b * aN + seg_t0) * aH + h;
-    const uint16_t* qh = (const uint16_t*)a.qr + head0 * adk;
-    const uint16_t* kh = (const uint16_t*)a.kr + head0 * adk;
-    const uint16_t* vh = (const uint16_t*)a.v + head0 * adv + dv0;
+    const DmaCtx<DK> x0(a);
+    const int tid = x0.tid, lane = x0.lane, w = x0.w, g4 = x0.g4, n16 = x0.n16;
+    const int seg = x0.seg, nchunks = x0.nchunks, seg_n = x0.seg_n, rsk = x0.rsk, rsv = x0.rsv;
+    const float lg = x0.lg;
+    const int adk = __builtin_amdgcn_readfirstlane(a.dk);
+    const uint16_t* qh = (const uint16_t*)a.qr + x0.head0 * adk;
+    const uint16_t* kh = (const uint16_t*)a.kr + x0.head0 * adk;
+    const uint16_t* vh = (const uint16_t*)a.v + x0.head0 * x0.adv + x0.dv0;
     const int osz = a.out_bf16 ? 2 : 4;
-    char* oh = (char*)a.o + (head0 * adv + dv0) * osz;
+    char* oh = (char*)a.o + (x0.head0 * x0.adv + x0.dv0) * osz;
     const int lq_p = ZQ::lane_p(lane), lq_t = ZQ::lane_trp(lane), lv_t = ZV::lane_trp(lane);
+
+    // The state entering the segment: W_s (the scan of the local passes) plus gamma^(sT) state_in.
+    f32x4_t R[NR];
+    if (seg > 0) {
+        slot_load<NR, NT>(x0.slot(a, seg), R, tid);
+    } else {
+#pragma unroll
+        for (int x = 0; x < NR; ++x) R[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    if (a.state_in) {
+        const float f = gpow(lg, (float)x0.seg_t0);
+#pragma unroll
+        for (int x = 0; x < NKB; ++x)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) R[x * 2 + j][e] += f * a.state_in[x0.state_index(x, j, e)];
+    }
 
     // Every slot starts at zero: rows past a segment's end are loaded as zeros, and no stale or uninitialised
     // value can reach a product even if a load past the end left its slots alone.
     for (int i = tid; i < F::LDS_BYTES / 16; i += NT) lds_store16(smem + 8 * i, u32x4_t{0u, 0u, 0u, 0u});
     __syncthreads();
+    // Nothing else in flight from here on but the loads below (the state's loads are consumed above): the
+    // explicit counts of wait_step then hold.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 
     // this lane's source offsets for the tile slots it fills (instruction i of wave w: slots 64 (w + NW i) + lane)
     int voq[F::NIW_Q], vov[F::NIW_V];
@@ -160,147 +365,74 @@ __global__ __launch_bounds__(512, 1) void chunk_dma_bf16(FwdArgs a) {
 #pragma unroll
     for (int i = 0; i < F::NIW_V; ++i) vov[i] = slot_src<F::DVT>(64 * (w + NW * i) + lane, rsv);
     // Loads of step c into LDS buffer c % NBUF; rows past the segment's end read as zero (the resources cover
-    // the live rows only). Issued for every step number, past the end too, so the counts below hold.
-    auto issue = [&](int c, int buf, auto withq) __attribute__((always_inline)) {
-        uint16_t* sQ = smem + buf * F::BUF;
-        uint16_t* sK = sQ + F::SQ;
-        uint16_t* sV = sK + F::SQ;
+    // the live rows only). Issued for every step number, past the end too, so the counts below hold. A step's
+    // loads go out in three parts (k', q', v rows), so that they can be spread over the products of the step
+    // before: issued all at once, the eight waves' loads queue behind each other in the address unit.
+    struct Dma {
+        i32x4_t rk, rq, rv;
+        uint16_t *sQ, *sK, *sV;
+    };
+    auto dma_of = [&](int c, int buf) __attribute__((always_inline)) {
+        Dma d;
+        d.sQ = smem + buf * F::BUF;
+        d.sK = d.sQ + F::SQ;
+        d.sV = d.sK + F::SQ;
         const int L = min(C, seg_n - c * C);
         const long long tc = (long long)c * C;
-        const i32x4_t rk = rsrc_words(kh + tc * rsk, L > 0 ? ((L - 1) * rsk + DK) * 2 : 0);
-        const i32x4_t rv = rsrc_words(vh + tc * rsv, L > 0 ? ((L - 1) * rsv + F::DVT) * 2 : 0);
-#pragma unroll
-        for (int i = 0; i < F::NIW_Q; ++i)
-            if (w + NW * i < F::NIQ) lds_load16(rk, sK + 512 * (w + NW * i), voq[i]);
-        if constexpr (decltype(withq)::value) {
-            const i32x4_t rq = rsrc_words(qh + tc * rsk, L > 0 ? ((L - 1) * rsk + DK) * 2 : 0);
+        d.rk = rsrc_words(kh + tc * rsk, L > 0 ? ((L - 1) * rsk + DK) * 2 : 0);
+        d.rq = rsrc_words(qh + tc * rsk, L > 0 ? ((L - 1) * rsk + DK) * 2 : 0);
+        d.rv = rsrc_words(vh + tc * rsv, L > 0 ? ((L - 1) * rsv + F::DVT) * 2 : 0);
+        return d;
+    };
+    auto issue_part = [&](const Dma& d, int part) __attribute__((always_inline)) {
+        if (part == 0) {
 #pragma unroll
             for (int i = 0; i < F::NIW_Q; ++i)
-                if (w + NW * i < F::NIQ) lds_load16(rq, sQ + 512 * (w + NW * i), voq[i]);
-        }
+                if (w + NW * i < F::NIQ) lds_load16(d.rk, d.sK + 512 * (w + NW * i), voq[i]);
+        } else if (part == 1) {
 #pragma unroll
-        for (int i = 0; i < F::NIW_V; ++i)
-            if (w + NW * i < F::NIV) lds_load16(rv, sV + 512 * (w + NW * i), vov[i]);
+            for (int i = 0; i < F::NIW_Q; ++i)
+                if (w + NW * i < F::NIQ) lds_load16(d.rq, d.sQ + 512 * (w + NW * i), voq[i]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < F::NIW_V; ++i)
+                if (w + NW * i < F::NIV) lds_load16(d.rv, d.sV + 512 * (w + NW * i), vov[i]);
+        }
     };
-    // Waits until this wave's loads of the current step have landed, while the next step's (issued after them)
-    // may still be in flight. Vector memory loads complete in order, so with at most `n` younger loads
+    auto issue = [&](int c, int buf) __attribute__((always_inline)) {
+        const Dma d = dma_of(c, buf);
+        issue_part(d, 0);
+        issue_part(d, 1);
+        issue_part(d, 2);
+    };
+    // Waits until this wave's loads of the current step have landed, while the next steps' (issued after them)
+    // may still be in flight. Vector memory loads complete in order, so with at most the younger steps' loads
     // outstanding none of the current step's is; each wave counts its own loads per step (the first waves hold
     // one instruction more of a tile whose instruction count is not a multiple of the waves).
-    auto wait_step = [&](auto withq) __attribute__((always_inline)) {
-        constexpr bool Q = decltype(withq)::value;
-        constexpr int NMIN = Q ? F::NL_MIN : F::NLK_MIN;
+    auto wait_step = [&]() __attribute__((always_inline)) {
         const int nq = (F::NIQ - w + NW - 1) / NW, nv = (F::NIV - w + NW - 1) / NW;
-        const int n = (Q ? 2 * nq : nq) + nv;
-        if (n == NMIN) {
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm(NMIN * (NBUF - 2)));
-        } else if (n == NMIN + 1) {
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm((NMIN + 1) * (NBUF - 2)));
-        } else if (n == NMIN + 2) {
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm((NMIN + 2) * (NBUF - 2)));
+        const int n = 2 * nq + nv;
+        if (n == F::NL_MIN) {
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(F::NL_MIN * (NBUF - 2)));
+        } else if (n == F::NL_MIN + 1) {
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm((F::NL_MIN + 1) * (NBUF - 2)));
+        } else if (n == F::NL_MIN + 2) {
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm((F::NL_MIN + 2) * (NBUF - 2)));
         } else {
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm((NMIN + 3) * (NBUF - 2)));
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm((F::NL_MIN + 3) * (NBUF - 2)));
         }
     };
     static_assert(F::NL_MAX - F::NL_MIN <= 3, "per-wave load counts");
+#pragma unroll
+    for (int c = 0; c < NBUF - 1; ++c) issue(c, c);
 
-    auto load_state_in = [&](f32x4_t* R) __attribute__((always_inline)) {
-#pragma unroll
-        for (int x = 0; x < NKB; ++x)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    R[x * 2 + j][e] = a.state_in[((long long)pair * DK + x * 16 + g4 + e) * adv + dv0 +
-                                                 (w * 2 + j) * 16 + n16];
-    };
-    f32x4_t R[NR];
-#pragma unroll
-    for (int x = 0; x < NR; ++x) R[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    if (seg == 0 && a.state_in) load_state_in(R);
-    const bool last = seg == anseg - 1;
-    const bool boundary = seg % kChainGroup == kChainGroup - 1;
-
-    // Tokens of the state since its last rescale (R = gamma^T R^; wave-uniform).
-    float T = 0.f;
+    float T = 0.f;  // tokens of the state since its last rescale (R = gamma^T R^; wave-uniform)
     auto rescale = [&]() __attribute__((always_inline)) {
         const float f = gpow(lg, T);
 #pragma unroll
         for (int x = 0; x < NR; ++x) R[x] *= f;
         T = 0.f;
     };
-    auto need_rescale = [&](int L) __attribute__((always_inline)) { return -(T + (float)L) * lg > F::RESCALE_LOG2; };
-    // zeta' of the 8 tokens of this lane's V^T fragment values (rows 4g + i and 16 + 4g + i), up to gamma^-T
-    float zb[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) zb[e] = gpow(lg, -(float)((e < 4 ? g4 + e : 16 + g4 + e - 4) + 1));
-    // V^T fragments of this wave's two 16-column blocks, scaled by zeta' (zero past the step's last row)
-    auto vz_frags = [&](const uint16_t* sV, int L, bf16x8_t* fvz) __attribute__((always_inline)) {
-        const float fT = gpow(lg, -T);
-        float z[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) z[e] = (e < 4 ? g4 + e : 16 + g4 + e - 4) < L ? zb[e] * fT : 0.f;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) fvz[j] = scale_frag(frag_trps<F::DVT>(sV, 0, (w * 2 + j) * 16, lv_t), z);
-    };
-    // R^ <- R^ + K'^T (V (.) zeta') from LDS buffer buf (local pass), a ring of 4 K'^T fragments in flight.
-    auto state_update = [&](const uint16_t* sK, const bf16x8_t* fvz) __attribute__((always_inline)) {
-        constexpr int PD = 4;
-        bf16x8_t kr[PD];
-#pragma unroll
-        for (int x = 0; x < PD; ++x) kr[x] = frag_trps<DK>(sK, 0, x * 16, lq_t);
-#pragma unroll
-        for (int x = 0; x < NKB; ++x) {
-            const bf16x8_t ka = kr[x % PD];
-            if (x + PD < NKB) kr[x % PD] = frag_trps<DK>(sK, 0, (x + PD) * 16, lq_t);
-#pragma unroll
-            for (int j = 0; j < 2; ++j) mfma(R[x * 2 + j], ka, fvz[j]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    };
-
-    // ---- local pass over the segment (chained runs, all segments but the last): the state only ----
-    if (chained && !last) {
-        const std::integral_constant<bool, false> noq;
-#pragma unroll
-        for (int c = 0; c < NBUF - 1; ++c) issue(c, c, noq);
-        int buf = 0;
-        for (int c = 0; c < nchunks; ++c) {
-            if (need_rescale(C)) rescale();  // (segments before the last hold whole steps only)
-            wait_step(noq);
-            lds_barrier();  // step c's rows are in; every wave is past step c - 1
-            issue(c + NBUF - 1, buf == 0 ? NBUF - 1 : buf - 1, noq);  // into the buffer step c - 1 used
-            const uint16_t* sK = smem + buf * F::BUF + F::SQ;
-            bf16x8_t fvz[2];
-            vz_frags(sK + F::SQ, C, fvz);
-            state_update(sK, fvz);
-            T += (float)C;
-            buf = buf == NBUF - 1 ? 0 : buf + 1;
-        }
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the loads past the end have landed too
-        lds_barrier();
-        rescale();  // the true end state
-        // publish the aggregate; the first segment reloads state_in before its flag rises (state_out may be the
-        // same buffer, and the last segment writes it only after every earlier flag)
-        if (!boundary) {
-            if (seg == 0 && a.state_in)
-                chain_publish<NR, NT, 0>(ch, seg, R, [&] { load_state_in(R); });
-            else
-                chain_publish<NR, NT>(ch, seg, R);
-        }
-    }
-
-    // ---- full pass ----
-    const std::integral_constant<bool, true> withq;
-#pragma unroll
-    for (int c = 0; c < NBUF - 1; ++c) issue(c, c, withq);
-    if (chained) {
-        f32x4_t Rin[NR];
-        chain_enter<NR, NT, true>(ch, seg, anseg, gpow(lg, (float)aseg_len), R, Rin, s_word);
-        if (seg > 0 || !a.state_in) {
-#pragma unroll
-            for (int x = 0; x < NR; ++x) R[x] = Rin[x];
-        }
-    }
     // decay factors: the mask gamma^(j - l) of this wave's score tile (wave 0: queries 0-15 x keys 0-15, wave
     // 1: queries 16-31 x keys 0-15, wave 2: queries 16-31 x keys 16-31; the other waves have none),
     // xi_j = gamma^(j+1)
@@ -343,17 +475,18 @@ __global__ __launch_bounds__(512, 1) void chunk_dma_bf16(FwdArgs a) {
     // output stores.
     int buf = 0;
     for (int c = 0; c < nchunks; ++c) {
-        if (need_rescale(C)) rescale();
-        wait_step(withq);
+        if (-(T + (float)C) * lg > F::RESCALE_LOG2) rescale();
+        wait_step();
         lds_barrier();
-        issue(c + NBUF - 1, buf == 0 ? NBUF - 1 : buf - 1, withq);
+        // step c + NBUF - 1's loads into the buffer step c - 1 used, in three parts during the products below
+        const Dma nd = dma_of(c + NBUF - 1, buf == 0 ? NBUF - 1 : buf - 1);
         const uint16_t* sQ = smem + buf * F::BUF;
         const uint16_t* sK = sQ + F::SQ;
         const uint16_t* sV = sK + F::SQ;
         const int L = min(C, seg_n - c * C);
         const float gT = gpow(lg, T);  // scale of the state entering the step
         bf16x8_t fvz[2];
-        vz_frags(sV, L, fvz);
+        vz_frags<F::DVT>(sV, L, T, lg, g4, w, lv_t, fvz);
         // One pass over d_k in steps of 32: the cross term O^T = R^T Q'^T (the state entering the step,
         // unscaled), this wave's score tile, and the state update of the two d_k blocks the cross term has just
         // read. Hand-pipelined: step s + 1's fragments are read during step s's products, and a scheduling fence
@@ -374,6 +507,7 @@ __global__ __launch_bounds__(512, 1) void chunk_dma_bf16(FwdArgs a) {
         for (int s = 0; s < KS; ++s) {
             const int slot = s & 1;
             if (s + 1 < KS) fetch(s + 1, slot ^ 1);
+            if (s * 3 % KS < 3 && s * 3 / KS < 3) issue_part(nd, s * 3 / KS);
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const bf16x8_t ra = acc_pair(R[(2 * s) * 2 + j], R[(2 * s + 1) * 2 + j]);
@@ -405,16 +539,14 @@ __global__ __launch_bounds__(512, 1) void chunk_dma_bf16(FwdArgs a) {
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the loads past the end have landed before the waves end
 
-    if (last && a.state_out) {
+    if (seg == x0.anseg - 1 && a.state_out) {
         rescale();
-        float* out = a.state_out + (long long)pair * DK * adv;
 #pragma unroll
         for (int x = 0; x < NKB; ++x)
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    out[(long long)(x * 16 + g4 + e) * adv + dv0 + (w * 2 + j) * 16 + n16] = R[x * 2 + j][e];
+                for (int e = 0; e < 4; ++e) a.state_out[x0.state_index(x, j, e)] = R[x * 2 + j][e];
     }
 }
 

@@ -16,10 +16,16 @@ fwd_kernel_t chunk_wide_get(int dk) {
     return nullptr;
 }
 
-fwd_kernel_t chunk_dma_get(int dk) {
-    if (dk == 256) return chunk_dma_bf16<256>;
-    if (dk == 128) return chunk_dma_bf16<128>;
-    return nullptr;
+bool chunk_dma_get(int dk, DmaKernels* out) {
+    if (dk == 256) {
+        *out = {chunk_dma_local_bf16<256>, unit_scan_kernel<256>, chunk_dma_full_bf16<256>};
+        return true;
+    }
+    if (dk == 128) {
+        *out = {chunk_dma_local_bf16<128>, unit_scan_kernel<128>, chunk_dma_full_bf16<128>};
+        return true;
+    }
+    return false;
 }
 
 }  // namespace ret

@@ -965,6 +965,10 @@ struct ChunkKernels {
                       // to the kernel set of `fallback_variant`
     int fallback_variant;
     const char* pre_name;  // timer name of fused_pre launches (null: the set's default)
+    // Three launches instead of one chained one (split_local, split_scan, then fused_pre over every segment),
+    // with the segment states in the workspace after its first kChainMeta bytes: split_local, split_scan null
+    // otherwise.
+    fwd_kernel_t split_local, split_scan;
 };
 struct ParKernel {
     fwd_kernel_t fn;
@@ -995,10 +999,14 @@ bool chunk_kernels_bf16_256(int dk, int dv, int C, int variant, ChunkKernels* ou
 // of 128, operands staged as given.
 constexpr int kWideThreads = 256;
 fwd_kernel_t chunk_wide_get(int dk);
-// The LDS-loading wide-head kernel (chunk_dma_bf16.h) for d_k in {128, 256} (null otherwise): kDmaThreads
-// threads, d_v tiles of kDmaDvt, operands staged as given.
+// The LDS-loading wide-head kernels (chunk_dma_bf16.h) for d_k in {128, 256} (false otherwise): the local pass
+// (grid units x (segments - 1)) and the full pass (units x segments) of kDmaThreads threads, d_v tiles of kDmaDvt,
+// operands staged as given; and the scan between them (grid (d_k * kDmaDvt / 1024, units), 256 threads).
 constexpr int kDmaThreads = 512, kDmaDvt = 256;
-fwd_kernel_t chunk_dma_get(int dk);
+struct DmaKernels {
+    fwd_kernel_t local, scan, full;
+};
+bool chunk_dma_get(int dk, DmaKernels* out);
 bool parallel_kernel_get(bool bf16_in, int dk, int dv, ParKernel* out);
 // Decode kernel for a (d_k, column tile cw, rows per wave wr) tile, 0 = default, null if none; with pairs_mode 0
 // it groups (b, h) pairs into workgroups of up to 8 waves where B*H leaves a workgroup per CU; 1 / 2 force one

@@ -117,13 +117,14 @@ def test_chunkwise_small(R, case):
     assert eo <= tol(dt) and es <= tol(dt), (eo, es)
 
 
-@pytest.mark.parametrize("threads", ["wide", "256x2", "512", "256"])
+@pytest.mark.parametrize("threads", ["wide", "256x2", "512", "256", "dma"])
 def test_chunkwise_dk256_workgroup_sizes(R, threads):
     """d_k 256 with d_v tiles of 128 (the wide-head kernel: the default where d_v is not a multiple of 256; the
-    chained kernel with 512 threads whose waves own 16 columns, or 256 threads of 32 columns), and the 256-thread
-    kernels with d_v tiles of 64. All match the oracle, with two segments and 3 d_v tiles of 128."""
-    opts = {"variant": {"wide": 0, "512": 4, "256x2": 1, "256": 2}[threads], "segments": 2}
-    B, N, H, dk, dv, C = 1, 300, 2, 256, 384, 64
+    chained kernel with 512 threads whose waves own 16 columns, or 256 threads of 32 columns), the 256-thread
+    kernels with d_v tiles of 64, and the LDS-loading kernels with d_v tiles of 256 (d_v 512). All match the
+    oracle, with two segments."""
+    opts = {"variant": {"wide": 0, "512": 4, "256x2": 1, "256": 2, "dma": 5}[threads], "segments": 2}
+    B, N, H, dk, dv, C = 1, 300, 2, 256, 384 if threads != "dma" else 512, 64
     print_case("dk256 threads=%s" % threads, (B, N, H, dk, dv, C))
     rng = np.random.default_rng(71)
     q = W.normal(rng, (B, N, H, dk), 16.0, "bf16")
