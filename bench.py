@@ -212,10 +212,17 @@ def roofline_of(res, bound):
     else:
         ach = res["alg_bytes_per_call"] / (dom_us * 1e-6) / 1e9
         peak, unit = HBM_PEAK_GBS, "GB/s"
+    # The dominant kernel is credited with the call's algorithmic work (it writes every output); where the call
+    # has other launches (rotation, local passes, a scan), the whole call's fraction is given beside it.
+    ms = res["ms_per_call"]
+    whole = (res["alg_flops_causal_per_call"] / (ms * 1e-3) / 1e12 if bound == "mfma"
+             else res["alg_bytes_per_call"] / (ms * 1e-3) / 1e9)
     return {"bound": bound, "achieved": ach, "peak": peak, "unit": unit, "frac": ach / peak,
             "traffic": res["traffic_bytes_dominant_kernel"], "kernel": res["dominant_kernel"],
             "kernel_avg_us": dom_us, "alg_bytes_per_launch": res["alg_bytes_per_call"],
-            "alg_flops_causal_per_launch": res["alg_flops_causal_per_call"]}
+            "alg_flops_causal_per_launch": res["alg_flops_causal_per_call"],
+            "whole_call": {"achieved": whole, "frac": whole / peak, "ms_per_call": ms,
+                           "launches": {k: v["launches_per_call"] for k, v in res["kernels"].items()}}}
 
 
 def bench_epilogue(R, W, torch, wid, steps):
