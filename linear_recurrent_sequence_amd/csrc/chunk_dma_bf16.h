@@ -217,8 +217,9 @@ __global__ __launch_bounds__(512, 1) void chunk_dma_local_bf16(FwdArgs a) {
         for (int x = 0; x < NR; ++x) R[x] *= f;
         T = 0.f;
     };
-    // k' and v rows of step c into register set par (two steps ahead); rows past the segment read as zero
-    u32x4_t lk[2][TK::NP], lv[2][TV::NP];
+    // k' and v rows of step c into register set par (LSETS - 1 steps ahead); rows past the segment read as zero
+    constexpr int LSETS = 3;
+    u32x4_t lk[LSETS][TK::NP], lv[LSETS][TV::NP];
     auto lissue = [&](int c, auto parc) __attribute__((always_inline)) {
         constexpr int par = decltype(parc)::value;
         const int L = min(C, seg_n - c * C);
@@ -242,7 +243,7 @@ __global__ __launch_bounds__(512, 1) void chunk_dma_local_bf16(FwdArgs a) {
         for (int p = 0; p < TK::NP; ++p) lds_store16(sK + ZK::off(krow + p * TK::RP, kseg * 8), lk[par][p]);
 #pragma unroll
         for (int p = 0; p < TV::NP; ++p) lds_store16(sV + ZV::off(vrow + p * TV::RP, vseg * 8), lv[par][p]);
-        lissue(c + 2, parc);  // (past the end too: the loads read zeros, and every path counts alike)
+        lissue(c + LSETS, parc);  // (past the end too: the loads read zeros, and every path counts alike)
         __syncthreads();
         bf16x8_t fvz[2];
         vz_frags<F::DVT>(sV, C, T, lg, x0.g4, w, lv_t, fvz);
@@ -261,18 +262,23 @@ __global__ __launch_bounds__(512, 1) void chunk_dma_local_bf16(FwdArgs a) {
         }
         T += (float)C;
     };
-    // Pairs of steps with no branch inside, so both register sets are in the same state on every path around
-    // the loop, and the compiler's wait before a step's LDS stores covers that step's loads only.
+    // Groups of LSETS steps with no branch inside, so every register set is in the same state on every path
+    // around the loop, and the compiler's wait before a step's LDS stores covers that step's loads only; the
+    // last steps after it.
     const std::integral_constant<int, 0> set0;
     const std::integral_constant<int, 1> set1;
+    const std::integral_constant<int, 2> set2;
     lissue(0, set0);
     lissue(1, set1);
+    lissue(2, set2);
     int c = 0;
-    for (; c + 1 < nchunks; c += 2) {
+    for (; c + 2 < nchunks; c += 3) {
         lstep(c, set0);
         lstep(c + 1, set1);
+        lstep(c + 2, set2);
     }
     if (c < nchunks) lstep(c, set0);
+    if (c + 1 < nchunks) lstep(c + 1, set1);
     rescale();
     slot_store<NR, NT>(x0.slot(a, x0.seg + 1), R, tid);
 }
