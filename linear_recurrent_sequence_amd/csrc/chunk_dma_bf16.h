@@ -3,10 +3,11 @@
 //  1. chunk_dma_local_bf16: every segment but the last runs the state recurrence from zero over its tokens,
 //     R_s = sum_t gamma^(L-1-t) k'_t^T v_t (the chunkwise carry without outputs), and stores it in slot s + 1 of
 //     its unit (one d_v tile of one (b, h)) in the workspace;
-//  2. unit_scan_kernel: per unit and element, slot s becomes the state entering segment s from zero,
-//     W_s = gamma^T W_(s-1) + R_(s-1), W_0 = 0 (T tokens per segment);
-//  3. chunk_dma_full_bf16: every segment runs the chunkwise form from W_s + gamma^(sT) state_in, writing the
-//     outputs (and the last segment the final state).
+//  2. unit_scan_kernel: per unit and element, slot s becomes the state entering segment s,
+//     W_s = gamma^T W_(s-1) + R_(s-1), W_0 = state_in (or 0; T tokens per segment);
+//  3. chunk_dma_full_bf16: every segment runs the chunkwise form from W_s (from state_in when the call has one
+//     segment), writing the outputs (and the last segment the final state). Only the scan reads state_in when
+//     there are several segments, so state_out, written by the last segment, may be the same buffer.
 // No workgroup waits for another, so no segment chain is needed, and each kernel holds only what its pass needs.
 // The full pass: eight waves, two per SIMD, each owning a d_k x 32 block of the state; 32-token steps; q', k' and v
 // rows go from memory straight into the LDS (buffer loads with the LDS bit), three steps deep, waited for with
@@ -283,9 +284,12 @@ __global__ __launch_bounds__(512, 1) void chunk_dma_local_bf16(FwdArgs a) {
     slot_store<NR, NT>(x0.slot(a, x0.seg + 1), R, tid);
 }
 
-// ---- 2. the states entering the segments: W_s = gamma^T W_(s-1) + W_s over s = 1 .. nseg-1, W_0 = 0 ----
-// One thread per 4 consecutive floats of a slot, grid (slot floats / 1024, units); the loads of a group of
-// segments are issued together, so the dependent chain costs one memory round trip per group.
+// ---- 2. the states entering the segments: W_s = gamma^T W_(s-1) + W_s over s = 1 .. nseg-1 ----
+// W_0 = state_in (or 0), gathered into the slots' thread order: the 4 floats at slot offset e are R[xr][0..3] of
+// thread t of the full pass (xr = e / (4 NT), t = e / 4 mod NT), state rows x*16 + g4 + 0..3 of column
+// dv0 + (2w + j)*16 + n16 (x = xr / 2, j = xr mod 2; w, g4, n16 of t). One thread per 4 consecutive floats of a
+// slot, grid (slot floats / 1024, units); the loads of a group of segments are issued together, so the
+// dependent chain costs one memory round trip per group.
 template <int DK>
 __global__ __launch_bounds__(256) void unit_scan_kernel(FwdArgs a) {
     typedef DmaB<DK> F;
@@ -295,9 +299,16 @@ __global__ __launch_bounds__(256) void unit_scan_kernel(FwdArgs a) {
     const long long e = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
     if (e >= PER) return;
     const int ntiles = a.dv / F::DVT, nseg = a.nseg;
-    const float decay = __builtin_amdgcn_exp2f((float)a.seg_len * a.log2g[(unit / ntiles) % a.H]);
+    const int pair = unit / ntiles, dv0 = (unit % ntiles) * F::DVT;
+    const float decay = __builtin_amdgcn_exp2f((float)a.seg_len * a.log2g[pair % a.H]);
     float* W = a.ws + (long long)unit * nseg * PER + e;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (a.state_in) {
+        const int xr = (int)(e / (4 * F::NT)), t = (int)(e / 4 % F::NT);
+        const int x = xr / 2, j = xr % 2, w = t / 64, lane = t % 64, g4 = 4 * (lane >> 4), n16 = lane & 15;
+        const float* si = a.state_in + ((long long)pair * DK + x * 16 + g4) * a.dv + dv0 + (w * 2 + j) * 16 + n16;
+        acc = make_float4(si[0], si[a.dv], si[2 * a.dv], si[3 * a.dv]);
+    }
     *reinterpret_cast<float4*>(W) = acc;
     for (int g0 = 1; g0 < nseg; g0 += G) {
         float4 u[G];
@@ -338,22 +349,19 @@ __global__ __launch_bounds__(512, 1) void chunk_dma_full_bf16(FwdArgs a) {
     char* oh = (char*)a.o + (x0.head0 * x0.adv + x0.dv0) * osz;
     const int lq_p = ZQ::lane_p(lane), lq_t = ZQ::lane_trp(lane), lv_t = ZV::lane_trp(lane);
 
-    // The state entering the segment: W_s (the scan of the local passes) plus gamma^(sT) state_in.
+    // The state entering the segment: W_s (the scan of the local passes, state_in included), or state_in itself
+    // when the call has one segment.
     f32x4_t R[NR];
-    if (seg > 0) {
+    if (x0.anseg > 1) {
         slot_load<NR, NT>(x0.slot(a, seg), R, tid);
     } else {
-#pragma unroll
-        for (int x = 0; x < NR; ++x) R[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-    if (a.state_in) {
-        const float f = gpow(lg, (float)x0.seg_t0);
 #pragma unroll
         for (int x = 0; x < NKB; ++x)
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) R[x * 2 + j][e] += f * a.state_in[x0.state_index(x, j, e)];
+                for (int e = 0; e < 4; ++e)
+                    R[x * 2 + j][e] = a.state_in ? a.state_in[x0.state_index(x, j, e)] : 0.f;
     }
 
     // Every slot starts at zero: rows past a segment's end are loaded as zeros, and no stale or uninitialised

@@ -119,6 +119,8 @@ def test_segment_invariance(R, shape):
                                   ("dk64-streaming", 64, 64, 64, {"segments": 4, "onchip": 0}),
                                   ("dk64-onchip", 64, 64, 64, {"segments": 4}),
                                   ("dk256", 256, 256, 128, {"segments": 3}),
+                                  ("dk256-dv512-8seg", 256, 512, 128, {"segments": 8}),
+                                  ("dk256-wide", 256, 256, 128, {"segments": 3, "variant": 3}),
                                   ("f32-split", 32, 32, 32, {"segments": 3})], ids=lambda c: c[0])
 def test_state_out_may_be_state_in(R, case):
     """state_out the same buffer as state_in, with several segments: the initial state is read before the final
