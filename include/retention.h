@@ -246,7 +246,8 @@ void ret_timer_reset(ret_timer_t* t);
  *                with d_v tiles of 64, 4 = 512 threads x 16 columns
  *   step_cw, step_wr, step_pairs   decode tile: columns per workgroup (16, 32, 64), rows per wave (16, 32, 64),
  *                pairs (0 planner, 1 one (b, h) per workgroup, 2 grouped); 0 = default
- *   bwd_direct   -1 or 1: gradients by the reversed traversal where available; 0: through reordered copies
+ *   bwd_direct   -1 or 1: gradients by the reversed traversal, with d_v blocks of dO and V read in place, where
+ *                the kernels have them; 0: through reordered copies
  *   chain_spin   segment-chain wait limit in device clock ticks (100 MHz) without progress before a wait gives
  *                up; 0 = default (2^24 ticks, ~0.17 s); negative: every wait gives up at once (for testing the
  *                give-up path: the affected outputs become NaN and ret_chunkwise_check reports it)

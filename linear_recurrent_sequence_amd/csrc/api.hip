@@ -378,7 +378,8 @@ ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o,
                            int dv, ret_dtype_t in_dt, ret_dtype_t out_dt, const float* gamma, const double* theta,
                            int64_t pos0, int chunk, const float* state_in, float* state_out, void* workspace,
                            size_t workspace_bytes, void* stream, const EpiRequest* epi, bool* fused,
-                           const Opts& op, bool rev = false, const double* out_theta = nullptr) {
+                           const Opts& op, bool rev = false, const double* out_theta = nullptr, int qk_din = 0,
+                           int qk_col0 = 0) {
     if (fused) *fused = false;
     ret_status_t st = check_common(q, k, v, o, B, N, H, dk, dv, in_dt, out_dt, gamma, theta);
     if (st != RET_OK) return st;
@@ -387,8 +388,12 @@ ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o,
         return fail(RET_ERR_INVALID_ARG, "state buffers must be 16-byte aligned");
     if (workspace_bytes > 0 && !workspace) return fail(RET_ERR_WORKSPACE, "workspace_bytes > 0 with a null workspace");
     if (workspace && !aligned16(workspace)) return fail(RET_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    // q and k as columns qk_col0 .. qk_col0 + d_k - 1 of heads qk_din wide (16-byte aligned rows)
+    if (qk_din && (qk_din % 8 || qk_col0 % 8 || qk_col0 < 0 || qk_col0 + dk > qk_din))
+        return fail(RET_ERR_INVALID_ARG, "q/k column block %d..%d of heads %d wide", qk_col0, qk_col0 + dk, qk_din);
     // The kernels address one chunk of one head with 32-bit byte offsets.
-    if ((long long)chunk * H * (dk > dv ? dk : dv) * 4 >= (1LL << 31))
+    const int dmax = qk_din > dk ? qk_din : dk;
+    if ((long long)chunk * H * (dmax > dv ? dmax : dv) * 4 >= (1LL << 31))
         return fail(RET_ERR_UNSUPPORTED, "chunkwise form: chunk*H*max(d_k,d_v) too large (%d*%d*%d)", chunk, H,
                     dk > dv ? dk : dv);
     ChunkKernels ck;
@@ -417,10 +422,17 @@ ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o,
         // once up front (several d_v tiles stage the same rows).
         fwd_kernel_t fn = onchip ? ck.seg : ck.fused;
         const fwd_kernel_t fn_pre = onchip ? (rev ? ck.seg_rev : ck.seg_pre) : ck.fused_pre;
-        // the reversed run and the rotation of the outputs exist for the on-chip kernel without input rotation,
-        // state or epilogue only
-        if ((rev || out_theta) && (!onchip || (rev && !ck.seg_rev) || theta || state_in || state_out || epi))
-            return fail(RET_ERR_UNSUPPORTED, "reversed or output-rotated chunkwise run: not available for this shape");
+        // The reversed run and the rotation of the outputs exist for the on-chip kernel, the reversed run and q, k
+        // taken from wider heads for the three-launch kernels (whole steps only when reversed); both without
+        // input rotation, state or epilogue.
+        if (rev || out_theta || qk_din) {
+            const bool plain = !theta && !state_in && !state_out && !epi;
+            const bool seg_ok = onchip && !qk_din && (!rev || ck.seg_rev);
+            const bool split_ok = ck.split_local && !onchip && !out_theta && (!rev || N % kDmaStep == 0);
+            if (!plain || !(seg_ok || split_ok))
+                return fail(RET_ERR_UNSUPPORTED, "reversed, output-rotated or column-block chunkwise run: not "
+                                                 "available for this shape");
+        }
         if (out_theta) {
             A.orot = 1;
             for (int i = 0; i < dv / 2; ++i) A.theta[i] = out_theta[i];
@@ -445,10 +457,15 @@ ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o,
             // local passes, the scan of their states, then the full pass of every segment (no chain)
             if (epi || onchip) return fail(RET_ERR_UNSUPPORTED, "chunkwise form: split launches with this plan");
             A.ws = workspace ? (float*)((char*)workspace + kChainMeta) : nullptr;
+            A.qk_din = qk_din;
+            A.qk_col0 = qk_col0;
             const unsigned units = (unsigned)((long long)B * H * ntiles);
+            if (rev && (!ck.split_local_rev || !ck.split_full_rev))
+                return fail(RET_ERR_UNSUPPORTED, "reversed chunkwise run: not available for this shape");
             if (nseg > 1) {
                 LaunchTimer tl("ret_chunk_dma_local", s, op);
-                hipLaunchKernelGGL(ck.split_local, dim3(units * (unsigned)(nseg - 1)), dim3(ck.threads_pre), 0, s, A);
+                hipLaunchKernelGGL(rev ? ck.split_local_rev : ck.split_local, dim3(units * (unsigned)(nseg - 1)),
+                                   dim3(ck.threads_pre), 0, s, A);
                 tl.done();
                 if ((st = launch_status("ret_chunk_dma_local")) != RET_OK) return st;
                 LaunchTimer tc("ret_chunk_dma_scan", s, op);
@@ -458,7 +475,7 @@ ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o,
                 if ((st = launch_status("ret_chunk_dma_scan")) != RET_OK) return st;
             }
             LaunchTimer tm(ck.pre_name, s, op);
-            hipLaunchKernelGGL(fn, dim3(grid), dim3(ck.threads_pre), 0, s, A);
+            hipLaunchKernelGGL(rev ? ck.split_full_rev : fn, dim3(grid), dim3(ck.threads_pre), 0, s, A);
             tm.done();
             return launch_status(ck.pre_name);
         }
@@ -501,12 +518,16 @@ ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o,
     return launch_status("ret_chunk_full");
 }
 
-// Workspace of the gradients. At offset 0 the segment chain the three retentions share (one call after
-// another; at least 256 bytes, so ret_chunkwise_check reads its header). Then, when both reversed retentions run
-// on the on-chip kernel's reversed traversal (direct, bf16 only): Q' and K' (bf16, only with rotation). Otherwise the reordered inputs K', K' reversed, Q' reversed, V reversed, dO reversed (in
-// the input dtype) and the three fp32 outputs.
+// Workspace of the gradients. At offset 0 the segment chain (or the segment states) the retentions share (one
+// call after another; at least 256 bytes, so ret_chunkwise_check reads its header). Then:
+// - when both reversed retentions run on the on-chip kernel's reversed traversal (direct, bf16 only): Q' and K'
+//   (bf16, only with rotation);
+// - when every retention runs on the three-launch kernels, which take reversed rows and d_v blocks in place (dma,
+//   bf16, N a multiple of their step): Q' and K' (only with rotation) and the fp32 dq' and dk' of each d_v block;
+// - otherwise the reordered inputs (K', K' reversed, Q' reversed, and V and dO reversed, or their blocks forward
+//   and reversed) in the input dtype, and the fp32 outputs.
 struct BwdLayout {
-    bool direct;
+    bool direct, dma;
     int nb, wb;  // d_v blocks of width wb for the retentions that contract over d_v (nb = 2 when d_v is wider
                  // than their kernels' d_k; dq' and dk' are then sums of two retentions)
     size_t qp, kp, kr, qr, vr, dor, g1, g2, g3, chain, chain_bytes, total;
@@ -532,15 +553,23 @@ bool bwd_layout(int B, int N, int H, int dk, int dv, int chunk, ret_dtype_t in_d
     const ChunkPlan pb = plan_chunk(cb, B, N, H, dk, dv, chunk, false, SIZE_MAX, op);
     L->direct = in_dt == RET_BF16 && L->nb == 1 && plan_onchip(ca, pa, op) && ca.seg_rev && plan_onchip(cb, pb, op) &&
                 cb.seg_rev && op.bwd_direct != 0;
+    L->dma = !L->direct && in_dt == RET_BF16 && N % kDmaStep == 0 && ca.split_local && !plan_onchip(ca, pa, op) &&
+             cb.split_local && !plan_onchip(cb, pb, op) && op.bwd_direct != 0;
     L->chain = 0;
     L->chain_bytes = pa.chain_bytes > pb.chain_bytes ? pa.chain_bytes : pb.chain_bytes;
     size_t off = up(L->chain_bytes > 256 ? L->chain_bytes : 256);
-    if (L->direct) {
+    if (L->direct || L->dma) {
         if (rotate) {
             L->qp = off;
             L->kp = L->qp + up(nk * 2);
             off = L->kp + up(nk * 2);
         }
+        if (L->dma)
+            for (int i = 0; i < L->nb; ++i) {
+                L->g1b[i] = off;
+                L->g3b[i] = L->g1b[i] + up(nk * 4);
+                off = L->g3b[i] + up(nk * 4);
+            }
         L->total = off;
         return true;
     }
@@ -821,6 +850,47 @@ ret_status_t ret_chunkwise_bwd_ex(const void* q, const void* k, const void* v, c
     hipStream_t s = (hipStream_t)stream;
     char* ws = (char*)workspace;
     const int ob = out_dt == RET_BF16;
+    if (L.dma) {
+        // Q', K' (rotated once), then, with the d_v blocks b of dO and V read in place:
+        //   dq' = sum over b of retention(dO_b, V_b, K')
+        //   dv  = retention(K', Q', dO) over the reversed sequence, rows read and written in reverse order
+        //   dk' = sum over b of retention(V_b, dO_b, Q') over the reversed sequence
+        // dv is written as the output; dq and dk are the block sums turned back by the transpose rotation.
+        const void *Qp = q, *Kp = k;
+        if (theta) {
+            FwdArgs A;
+            fill_fwd(A, q, k, v, nullptr, B, N, H, dk, dv, out_dt, gamma, theta, pos0);
+            A.qr = ws + L.qp;
+            A.kr = ws + L.kp;
+            Qp = A.qr;
+            Kp = A.kr;
+            LaunchTimer tr("ret_rotate_qk", s, op);
+            hipLaunchKernelGGL(rotate_qk_get(), dim3(rotate_qk_blocks(B, N, H, dk)), dim3(256), 0, s, A);
+            tr.done();
+            if ((st = launch_status("ret_rotate_qk")) != RET_OK) return st;
+        }
+        void* chain = ws + L.chain;
+        const int wb = L.wb, din = L.nb > 1 ? dv : 0;
+        for (int i = 0; i < L.nb; ++i)
+            if ((st = chunkwise_run(dout, v, Kp, ws + L.g1b[i], B, N, H, wb, dk, RET_BF16, RET_F32, gamma, nullptr, 0,
+                                    chunk, nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, op, false,
+                                    nullptr, din, i * wb)) != RET_OK)
+                return st;
+        if ((st = chunkwise_run(Kp, Qp, dout, dv_out, B, N, H, dk, dv, RET_BF16, out_dt, gamma, nullptr, 0, chunk,
+                                nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, op, true)) != RET_OK)
+            return st;
+        for (int i = 0; i < L.nb; ++i)
+            if ((st = chunkwise_run(v, dout, Qp, ws + L.g3b[i], B, N, H, wb, dk, RET_BF16, RET_F32, gamma, nullptr, 0,
+                                    chunk, nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, op, true,
+                                    nullptr, din, i * wb)) != RET_OK)
+                return st;
+        const bool two = L.nb > 1;
+        const PermJob post[2] = {
+            {ws + L.g1b[0], {dq, nullptr}, dk, -1, 0, {0, 0}, 0, ob, two ? ws + L.g1b[1] : nullptr},
+            {ws + L.g3b[0], {dk_out, nullptr}, dk, -1, 0, {0, 0}, 0, ob, two ? ws + L.g3b[1] : nullptr},
+        };
+        return permute(post, 2, B, N, H, theta, pos0, s, op);
+    }
     if (L.direct) {
         // Q', K' (rotated once; q and k themselves without rotation), then dq' = retention(dO, V, K') and, over
         // the reversed sequence on the reversed traversal, dv = retention(K', Q', dO) and dk' = retention(V, dO,

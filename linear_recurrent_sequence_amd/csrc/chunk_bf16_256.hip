@@ -34,6 +34,8 @@ ChunkKernels chunk_entry_dma256() {
     k.fused = k.fused_pre = d.full;
     k.split_local = d.local;
     k.split_scan = d.scan;
+    k.split_local_rev = d.local_rev;
+    k.split_full_rev = d.full_rev;
     k.dvt = kDmaDvt;
     k.threads = k.threads_pre = kDmaThreads;
     k.pre_always = 1;

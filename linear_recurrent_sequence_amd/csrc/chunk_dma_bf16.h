@@ -16,7 +16,9 @@
 // stages the q' and k' rows and computes the causal scores once for 256 columns. The local pass stages k' and v
 // through registers (loads straight into the LDS issue too slowly when a step holds only the state update).
 // Chunks of 64 or more tokens run as 32-token sub-chunks (the chunkwise form gives the same result for any chunk
-// size, up to rounding).
+// size, up to rounding). The gradients run two of their retentions over the reversed sequence and take d_v blocks
+// of wider heads as q and k: the kernels read and write those rows and columns in place (REV instances, and
+// FwdArgs::qk_din).
 #pragma once
 
 #include "chunk_bf16.h"
@@ -91,15 +93,16 @@ __device__ __forceinline__ void lds_load16(const i32x4_t& r, uint16_t* lds, int 
         : "memory");
 }
 
-// Byte offset, from a tile's first row, of the global 16-byte segment that LDS slot p of a Swz<W> tile holds
-// (row stride `rs` elements); pad slots get an offset past any record count, so they load zeros.
+// Byte offset, from a tile's first row in memory, of the global 16-byte segment that LDS slot p of a Swz<W> tile
+// holds (row stride `rs` elements; tile row r from memory row r, or from row rows - 1 - r when the tile's `rows`
+// rows are taken in reverse); pad slots get an offset past any record count, so they load zeros.
 template <int W>
-__device__ __forceinline__ int slot_src(int p, int rs) {
+__device__ __forceinline__ int slot_src(int p, int rs, bool flip, int rows) {
     constexpr int SPR = Swz<W>::LD / 8;  // slots per row
     const int r = p / SPR, q = p % SPR;
     if (q >= W / 8) return 0x7ff00000;
     const int s = q ^ ((r >> 3) & 1);   // Swz swaps the two 8-column halves of each 16 in rows 8..15 (mod 16)
-    return (r * rs + 8 * s) * 2;
+    return ((flip ? rows - 1 - r : r) * rs + 8 * s) * 2;
 }
 
 // An 8-value bf16 fragment scaled by per-value factors (rounded back to bf16).
@@ -127,14 +130,14 @@ __device__ __forceinline__ void unit_seg_of_block(int ntiles, int units, int* un
     *seg = __builtin_amdgcn_readfirstlane(s);
 }
 
-// The values every pass of one workgroup shares.
-template <int DK>
+// The values every pass of one workgroup shares (REV: the run goes over the reversed sequence).
+template <int DK, bool REV>
 struct DmaCtx {
     typedef DmaB<DK> F;
     int tid, lane, w, g4, n16;
-    int unit, seg, aN, aH, adv, anseg, aseg_len, pair, dv0, seg_n, nchunks, rsk, rsv;
+    int unit, seg, aN, aH, adk, adv, din, anseg, aseg_len, pair, dv0, seg_n, nchunks, rsk, rsv;
     float lg;
-    long long seg_t0, head0;
+    long long seg_t0, hrow;  // hrow: token 0 of this (b, h), in head rows
     __device__ __forceinline__ DmaCtx(const FwdArgs& a) {
         tid = threadIdx.x;
         lane = tid & 63;
@@ -146,7 +149,7 @@ struct DmaCtx {
         unit_seg_of_block(ntiles, units, &unit, &seg);
         aN = __builtin_amdgcn_readfirstlane(a.N);
         aH = __builtin_amdgcn_readfirstlane(a.H);
-        const int adk = __builtin_amdgcn_readfirstlane(a.dk);
+        adk = __builtin_amdgcn_readfirstlane(a.dk);
         adv = __builtin_amdgcn_readfirstlane(a.dv);
         anseg = __builtin_amdgcn_readfirstlane(a.nseg);
         aseg_len = __builtin_amdgcn_readfirstlane(a.seg_len);
@@ -157,9 +160,20 @@ struct DmaCtx {
         seg_t0 = (long long)seg * aseg_len;
         seg_n = (int)(min((long long)aN, seg_t0 + aseg_len) - seg_t0);
         nchunks = (seg_n + F::C - 1) / F::C;
-        rsk = aH * adk;
+        din = a.qk_din ? __builtin_amdgcn_readfirstlane(a.qk_din) : adk;
+        rsk = aH * din;
         rsv = aH * adv;
-        head0 = ((long long)b * aN + seg_t0) * aH + h;
+        hrow = (long long)b * aN * aH + h;
+    }
+    // q' or k' (the pre-rotated copies), v and o of this unit's head at its token 0 (from there token t is row t)
+    __device__ __forceinline__ const uint16_t* qk_head(const void* p, const FwdArgs& a) const {
+        return (const uint16_t*)p + hrow * din + __builtin_amdgcn_readfirstlane(a.qk_col0);
+    }
+    __device__ __forceinline__ long long v_head() const { return hrow * adv + dv0; }
+    // The first row in memory of step c's C rows: token seg_t0 + c C of the run, or, over the reversed sequence,
+    // row N - seg_t0 - (c + 1) C, whose C rows are then the step's tokens in reverse order.
+    __device__ __forceinline__ long long crow(int c) const {
+        return REV ? (long long)aN - seg_t0 - (long long)(c + 1) * F::C : seg_t0 + (long long)c * F::C;
     }
     // slot s of this unit (state slots of DK x DVT floats in the thread order of slot_store)
     __device__ __forceinline__ float* slot(const FwdArgs& a, int s) const {
@@ -187,7 +201,7 @@ __device__ __forceinline__ void vz_frags(const uint16_t* sV, int L, float T, flo
 }
 
 // ---- 1. the local pass of every segment but the last ----
-template <int DK>
+template <int DK, bool REV>
 __global__ __launch_bounds__(512, 1) void chunk_dma_local_bf16(FwdArgs a) {
     typedef DmaB<DK> F;
     constexpr int NT = F::NT, C = F::C, NKB = F::NKB;
@@ -198,15 +212,17 @@ __global__ __launch_bounds__(512, 1) void chunk_dma_local_bf16(FwdArgs a) {
     typedef RowTile<C, F::DVT, NT> TV;
     constexpr int BUFL = F::SQ + F::SV;  // one step: sK, sV
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * BUFL];
-    const DmaCtx<DK> x0(a);
+    const DmaCtx<DK, REV> x0(a);
     const int tid = x0.tid, lane = x0.lane, w = x0.w, nchunks = x0.nchunks, seg_n = x0.seg_n;
     const int rsk = x0.rsk, rsv = x0.rsv;
     const float lg = x0.lg;
-    const uint16_t* kh = (const uint16_t*)a.kr + x0.head0 * __builtin_amdgcn_readfirstlane(a.dk);
-    const uint16_t* vh = (const uint16_t*)a.v + x0.head0 * x0.adv + x0.dv0;
+    const uint16_t* kh = x0.qk_head(a.kr, a);
+    const uint16_t* vh = (const uint16_t*)a.v + x0.v_head();
     const int lk_t = ZK::lane_trp(lane), lv_t = ZV::lane_trp(lane);
     const int krow = tid / TK::SPR, kseg = tid % TK::SPR, vrow = tid / TV::SPR, vseg = tid % TV::SPR;
     const int koff = (krow * rsk + kseg * 8) * 2, voff = (vrow * rsv + vseg * 8) * 2;
+    // the LDS row of the step's memory row r (the rows of a reversed run in reverse order; whole steps only)
+    auto lrow = [&](int r) __attribute__((always_inline)) { return REV ? C - 1 - r : r; };
 
     f32x4_t R[NR];
 #pragma unroll
@@ -224,7 +240,7 @@ __global__ __launch_bounds__(512, 1) void chunk_dma_local_bf16(FwdArgs a) {
     auto lissue = [&](int c, auto parc) __attribute__((always_inline)) {
         constexpr int par = decltype(parc)::value;
         const int L = min(C, seg_n - c * C);
-        const long long tc = (long long)c * C;
+        const long long tc = x0.crow(c);
         const rsrc_t rk = bytes_rsrc(kh + tc * rsk, L > 0 ? ((L - 1) * rsk + DK) * 2 : 0);
         const rsrc_t rv = bytes_rsrc(vh + tc * rsv, L > 0 ? ((L - 1) * rsv + F::DVT) * 2 : 0);
 #pragma unroll
@@ -241,9 +257,9 @@ __global__ __launch_bounds__(512, 1) void chunk_dma_local_bf16(FwdArgs a) {
         uint16_t* sK = smem + (c & 1) * BUFL;
         uint16_t* sV = sK + F::SQ;
 #pragma unroll
-        for (int p = 0; p < TK::NP; ++p) lds_store16(sK + ZK::off(krow + p * TK::RP, kseg * 8), lk[par][p]);
+        for (int p = 0; p < TK::NP; ++p) lds_store16(sK + ZK::off(lrow(krow + p * TK::RP), kseg * 8), lk[par][p]);
 #pragma unroll
-        for (int p = 0; p < TV::NP; ++p) lds_store16(sV + ZV::off(vrow + p * TV::RP, vseg * 8), lv[par][p]);
+        for (int p = 0; p < TV::NP; ++p) lds_store16(sV + ZV::off(lrow(vrow + p * TV::RP), vseg * 8), lv[par][p]);
         lissue(c + LSETS, parc);  // (past the end too: the loads read zeros, and every path counts alike)
         __syncthreads();
         bf16x8_t fvz[2];
@@ -328,7 +344,7 @@ __global__ __launch_bounds__(256) void unit_scan_kernel(FwdArgs a) {
 }
 
 // ---- 3. the full pass of every segment ----
-template <int DK>
+template <int DK, bool REV>
 __global__ __launch_bounds__(512, 1) void chunk_dma_full_bf16(FwdArgs a) {
     typedef DmaB<DK> F;
     constexpr int NT = F::NT, NW = F::NW, C = F::C, NKB = F::NKB, KS = F::KS, NBUF = F::NBUF;
@@ -337,16 +353,15 @@ __global__ __launch_bounds__(512, 1) void chunk_dma_full_bf16(FwdArgs a) {
     typedef typename F::ZV ZV;
     __shared__ __attribute__((aligned(16))) uint16_t smem[F::LDS_BYTES / 2];
     uint16_t* const sP = smem + NBUF * F::BUF;
-    const DmaCtx<DK> x0(a);
+    const DmaCtx<DK, REV> x0(a);
     const int tid = x0.tid, lane = x0.lane, w = x0.w, g4 = x0.g4, n16 = x0.n16;
     const int seg = x0.seg, nchunks = x0.nchunks, seg_n = x0.seg_n, rsk = x0.rsk, rsv = x0.rsv;
     const float lg = x0.lg;
-    const int adk = __builtin_amdgcn_readfirstlane(a.dk);
-    const uint16_t* qh = (const uint16_t*)a.qr + x0.head0 * adk;
-    const uint16_t* kh = (const uint16_t*)a.kr + x0.head0 * adk;
-    const uint16_t* vh = (const uint16_t*)a.v + x0.head0 * x0.adv + x0.dv0;
+    const uint16_t* qh = x0.qk_head(a.qr, a);
+    const uint16_t* kh = x0.qk_head(a.kr, a);
+    const uint16_t* vh = (const uint16_t*)a.v + x0.v_head();
     const int osz = a.out_bf16 ? 2 : 4;
-    char* oh = (char*)a.o + (x0.head0 * x0.adv + x0.dv0) * osz;
+    char* oh = (char*)a.o + x0.v_head() * osz;
     const int lq_p = ZQ::lane_p(lane), lq_t = ZQ::lane_trp(lane), lv_t = ZV::lane_trp(lane);
 
     // The state entering the segment: W_s (the scan of the local passes, state_in included), or state_in itself
@@ -375,11 +390,11 @@ __global__ __launch_bounds__(512, 1) void chunk_dma_full_bf16(FwdArgs a) {
     // this lane's source offsets for the tile slots it fills (instruction i of wave w: slots 64 (w + NW i) + lane)
     int voq[F::NIW_Q], vov[F::NIW_V];
 #pragma unroll
-    for (int i = 0; i < F::NIW_Q; ++i) voq[i] = slot_src<DK>(64 * (w + NW * i) + lane, rsk);
+    for (int i = 0; i < F::NIW_Q; ++i) voq[i] = slot_src<DK>(64 * (w + NW * i) + lane, rsk, REV, C);
 #pragma unroll
-    for (int i = 0; i < F::NIW_V; ++i) vov[i] = slot_src<F::DVT>(64 * (w + NW * i) + lane, rsv);
+    for (int i = 0; i < F::NIW_V; ++i) vov[i] = slot_src<F::DVT>(64 * (w + NW * i) + lane, rsv, REV, C);
     // Loads of step c into LDS buffer c % NBUF; rows past the segment's end read as zero (the resources cover
-    // the live rows only). Issued for every step number, past the end too, so the counts below hold. A step's
+    // the live rows only; a reversed run has whole steps only). Issued for every step number, past the end too, so the counts below hold. A step's
     // loads go out in three parts (k', q', v rows), so that they can be spread over the products of the step
     // before: issued all at once, the eight waves' loads queue behind each other in the address unit.
     struct Dma {
@@ -392,7 +407,7 @@ __global__ __launch_bounds__(512, 1) void chunk_dma_full_bf16(FwdArgs a) {
         d.sK = d.sQ + F::SQ;
         d.sV = d.sK + F::SQ;
         const int L = min(C, seg_n - c * C);
-        const long long tc = (long long)c * C;
+        const long long tc = x0.crow(c);
         d.rk = rsrc_words(kh + tc * rsk, L > 0 ? ((L - 1) * rsk + DK) * 2 : 0);
         d.rq = rsrc_words(qh + tc * rsk, L > 0 ? ((L - 1) * rsk + DK) * 2 : 0);
         d.rv = rsrc_words(vh + tc * rsv, L > 0 ? ((L - 1) * rsv + F::DVT) * 2 : 0);
@@ -461,10 +476,12 @@ __global__ __launch_bounds__(512, 1) void chunk_dma_full_bf16(FwdArgs a) {
     float Xi[2];
 #pragma unroll
     for (int x = 0; x < 2; ++x) Xi[x] = gpow(lg, (float)(x * 16 + n16 + 1));
-    const int o_voff = (n16 * rsv + w * 2 * 16 + g4) * osz;
+    // output row x * 16 + n16 of a step: at row x * 16 + n16 of its rows in memory, or reversed at
+    // (1 - x) * 16 + 15 - n16
+    const int o_voff = ((REV ? 15 - n16 : n16) * rsv + w * 2 * 16 + g4) * osz;
     auto store_out = [&](int c, const f32x4_t* O) __attribute__((always_inline)) {
         const int L = min(C, seg_n - c * C);
-        const rsrc_t ro = bytes_rsrc(oh + (long long)c * C * rsv * osz, ((L - 1) * rsv + F::DVT) * osz);
+        const rsrc_t ro = bytes_rsrc(oh + x0.crow(c) * rsv * osz, ((L - 1) * rsv + F::DVT) * osz);
         if (a.out_bf16) {
 #pragma unroll
             for (int x = 0; x < 2; ++x)
@@ -474,14 +491,14 @@ __global__ __launch_bounds__(512, 1) void chunk_dma_full_bf16(FwdArgs a) {
                         __builtin_bit_cast(uint32_t __attribute__((ext_vector_type(2))),
                                            make_uint2(pack2_bf16(O[x * 2 + j][0], O[x * 2 + j][1]),
                                                       pack2_bf16(O[x * 2 + j][2], O[x * 2 + j][3]))),
-                        ro, o_voff, (x * 16 * rsv + j * 16) * 2, kOutAux);
+                        ro, o_voff, ((REV ? 1 - x : x) * 16 * rsv + j * 16) * 2, kOutAux);
         } else {
 #pragma unroll
             for (int x = 0; x < 2; ++x)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
                     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, O[x * 2 + j]), ro, o_voff,
-                                                           (x * 16 * rsv + j * 16) * 4, kOutAux);
+                                                           ((REV ? 1 - x : x) * 16 * rsv + j * 16) * 4, kOutAux);
         }
     };
     // Step c: wait for its rows, barrier (every wave is past step c - 1, so the buffer it used and sP are free),

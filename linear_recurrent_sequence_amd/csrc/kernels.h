@@ -36,6 +36,9 @@ struct FwdArgs {
     // Output rows turned back by the transpose rotation at their positions (theta, pos0), for kernels that stage
     // q and k as given (the gradients' dq' and dk' retentions).
     int orot;
+    // Three-launch bf16 kernels only. qk_din (0: d_k): q and k are columns qk_col0 .. qk_col0 + d_k - 1 of heads
+    // qk_din wide, so that a run can take one block of wider heads in place.
+    int qk_din, qk_col0;
     float log2g[kMaxHeads];
     double theta[kMaxPairs];
 };
@@ -967,8 +970,9 @@ struct ChunkKernels {
     const char* pre_name;  // timer name of fused_pre launches (null: the set's default)
     // Three launches instead of one chained one (split_local, split_scan, then fused_pre over every segment),
     // with the segment states in the workspace after its first kChainMeta bytes: split_local, split_scan null
-    // otherwise.
-    fwd_kernel_t split_local, split_scan;
+    // otherwise. split_local_rev and split_full_rev run over the reversed sequence (token n of the run is row N-1-n
+    // of q, k, v and o; N a multiple of kDmaStep).
+    fwd_kernel_t split_local, split_scan, split_local_rev, split_full_rev;
 };
 struct ParKernel {
     fwd_kernel_t fn;
@@ -1001,10 +1005,11 @@ constexpr int kWideThreads = 256;
 fwd_kernel_t chunk_wide_get(int dk);
 // The LDS-loading wide-head kernels (chunk_dma_bf16.h) for d_k in {128, 256} (false otherwise): the local pass
 // (grid units x (segments - 1)) and the full pass (units x segments) of kDmaThreads threads, d_v tiles of kDmaDvt,
-// operands staged as given; and the scan between them (grid (d_k * kDmaDvt / 1024, units), 256 threads).
-constexpr int kDmaThreads = 512, kDmaDvt = 256;
+// operands staged as given; and the scan between them (grid (d_k * kDmaDvt / 1024, units), 256 threads). The
+// local and full passes also over the reversed sequence (local_rev, full_rev).
+constexpr int kDmaThreads = 512, kDmaDvt = 256, kDmaStep = 32;  // kDmaStep: tokens per step
 struct DmaKernels {
-    fwd_kernel_t local, scan, full;
+    fwd_kernel_t local, scan, full, local_rev, full_rev;
 };
 bool chunk_dma_get(int dk, DmaKernels* out);
 bool parallel_kernel_get(bool bf16_in, int dk, int dv, ParKernel* out);

@@ -151,10 +151,14 @@ def test_gradients_workspace_and_rejections(lib):
     n2 = 1 * 4096 * 4 * 128
     assert wsq(1, 4096, 4, 128, 128, 64) >= 5 * n2 * 2 + 3 * n2 * 4
     assert wsq(1, 100, 2, 32, 64, 64) == 0      # d_k = 32: no bf16 kernel
-    # d_v = 512 is wider than any retention's d_k: dq' and dk' are sums over two halves of 256 (copies of each
-    # half of V and dO, natural and reversed, and two fp32 outputs per half)
+    # d_v = 512 is wider than any retention's d_k: dq' and dk' are sums over two halves of 256. With N a multiple
+    # of 32 every retention runs on the three-launch kernels, which read the halves and reversed rows in place:
+    # the segment states, Q', K' (bf16) and two fp32 outputs per half
     n4k, n4v = 8192 * 16 * 256, 8192 * 16 * 512
-    assert wsq(1, 8192, 16, 256, 512, 128) >= 3 * n4k * 2 + n4v * 2 + 8 * n4k * 2 + 4 * n4k * 4 + n4v * 4
+    assert 2 * n4k * 2 + 4 * n4k * 4 <= wsq(1, 8192, 16, 256, 512, 128) < 2 * n4k * 2 + 4 * n4k * 4 + n4v * 4
+    # otherwise copies of each half of V and dO, natural and reversed, and two fp32 outputs per half
+    n5k, n5v = 8190 * 16 * 256, 8190 * 16 * 512
+    assert wsq(1, 8190, 16, 256, 512, 128) >= 3 * n5k * 2 + n5v * 2 + 8 * n5k * 2 + 4 * n5k * 4 + n5v * 4
     assert wsq(1, 100, 2, 64, 1024, 64) == 0     # halves of 512 are still too wide
     assert wsq(1, 0, 2, 64, 64, 64) == 0
     g = np.asarray([0.9, 0.99], np.float32).ctypes.data_as(ctypes.POINTER(ctypes.c_float))

@@ -72,6 +72,51 @@ def test_gradients_small(R, case):
     _check(got, ref, tol("bf16"))
 
 
+GRAD_DMA = [
+    # B, N, H, dk, dv, chunk, rotate, pos0, out dtype. d_k 256 and N a multiple of 32: every retention runs on the
+    # three-launch kernels, the reversed ones reading and writing rows in reverse order and the d_v blocks of dO
+    # and V read in place
+    (1, 640, 2, 256, 512, 128, True, 5, "bf16"),   # 5 segments, two d_v blocks
+    (2, 512, 2, 256, 256, 64, True, 0, "f32"),     # one block
+    (1, 1024, 1, 256, 512, 32, False, 0, "f32"),   # no rotation, chunk 32
+    (1, 32, 2, 256, 512, 128, True, 9, "f32"),     # one step
+]
+
+
+@pytest.mark.parametrize("case", GRAD_DMA, ids=lambda c: "B%d-N%d-H%d-dk%d-dv%d-C%d" % c[:6] + "-" + c[8])
+def test_gradients_in_place(R, case):
+    """Gradients with no reordered copies: the only reordering launch left is the one that sums the d_v blocks'
+    dq' and dk' and turns them back by the transpose rotation."""
+    B, N, H, dk, dv, chunk, rot, pos0, out_dt = case
+    w = W.Workload("grad", B=B, N=N, H=H, dk=dk, dv=dv, dtype="bf16", scale=float(np.sqrt(dk)), seed=61 + N,
+                   chunk=chunk, rotate=rot)
+    print_case("gradients-in-place", w)
+    q, k, v, rng = W.make_qkv(w)
+    do = W.make_dout(w, rng)
+    ref = oracle.grad(q, k, v, do, w.gamma, theta=w.theta, pos0=pos0)
+    timer = R.Timer()
+    got = _gpu_grad(R, q, k, v, do, w.gamma, chunk, w.theta, pos0, out_dt, options={"timer": timer})
+    nb = dv // 256
+    assert timer.query("ret_permute_rotate")[1] == 1
+    assert timer.query("ret_chunk_dma")[1] == 2 * nb + 1
+    assert timer.query("ret_rotate_qk")[1] == (1 if rot else 0)
+    timer.close()
+    _check(got, ref, tol("bf16"))
+
+
+@pytest.mark.parametrize("direct", ["1", "0"])
+def test_gradients_in_place_or_copied(R, direct):
+    """d_k 256, d_v 512 in place (bwd_direct 1) and through reordered copies (0)."""
+    w = W.Workload("grad", B=1, N=768, H=2, dk=256, dv=512, dtype="bf16", scale=16.0, seed=47, chunk=128,
+                   rotate=True)
+    print_case("gradients-path-dk256", direct, w)
+    q, k, v, rng = W.make_qkv(w)
+    do = W.make_dout(w, rng)
+    ref = oracle.grad(q, k, v, do, w.gamma, theta=w.theta, pos0=1)
+    got = _gpu_grad(R, q, k, v, do, w.gamma, w.chunk, w.theta, 1, "f32", options={"bwd_direct": int(direct)})
+    _check(got, ref, tol("bf16"))
+
+
 @pytest.mark.parametrize("direct", ["1", "0"])
 def test_gradients_both_paths(R, direct):
     """The reversed-traversal path and the reordered-copies path (bwd_direct 0) on one shape."""
@@ -149,7 +194,7 @@ def test_gradients_long_sequence_full(R):
 
 def test_gradients_7b_class_layer_full(R):
     """The 7b-class-layer workload (B=1, N=8192, H=16, d_k=256, d_v=512, chunk 128) at full size: the paper's
-    head shape, dq' and dk' as sums over the two halves of d_v."""
+    head shape, dq' and dk' as sums over the two halves of d_v, read in place."""
     w = W.WORKLOADS[4]
     print_case("gradients-workload4", w)
     q, k, v, rng = W.make_qkv(w)
