@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define RET_ABI_VERSION 6
+#define RET_ABI_VERSION 7
 
 typedef enum { RET_F32 = 0, RET_BF16 = 1 } ret_dtype_t;
 
@@ -248,6 +248,10 @@ void ret_timer_reset(ret_timer_t* t);
  *                pairs (0 planner, 1 one (b, h) per workgroup, 2 grouped); 0 = default
  *   bwd_direct   -1 or 1: gradients by the reversed traversal, with d_v blocks of dO and V read in place, where
  *                the kernels have them; 0: through reordered copies
+ *   step_cache   0: the decode step streams the state (non-temporal loads and stores, one (b, h) per
+ *                workgroup): right when each step's state has left the caches by the next step, as with a state
+ *                per layer of a model; 1: the state's accesses may stay cached (grouped workgroups), faster when
+ *                the same state is stepped again while it still fits the 256 MB Infinity Cache
  *   chain_spin   segment-chain wait limit in device clock ticks (100 MHz) without progress before a wait gives
  *                up; 0 = default (2^24 ticks, ~0.17 s); negative: every wait gives up at once (for testing the
  *                give-up path: the affected outputs become NaN and ret_chunkwise_check reports it)
@@ -261,6 +265,7 @@ typedef struct {
     int variant;
     int step_cw, step_wr, step_pairs;
     int bwd_direct;
+    int step_cache;
     long long chain_spin;
     ret_timer_t* timer;
 } ret_options_t;

@@ -54,7 +54,7 @@ namespace {
 // The plan options with the library's defaults filled in (ret_options_t documents each field).
 struct Opts {
     int segments = 0, target_wgs = 0, prerotate = -1, onchip = 1, variant = 0;
-    int step_cw = 0, step_wr = 0, step_pairs = 0, bwd_direct = 1;
+    int step_cw = 0, step_wr = 0, step_pairs = 0, bwd_direct = 1, step_cache = 0;
     long long chain_spin = 0;
     ret_timer_t* timer = nullptr;
 };
@@ -70,6 +70,7 @@ Opts resolve(const ret_options_t* o) {
     r.step_wr = o->step_wr;
     r.step_pairs = o->step_pairs;
     r.bwd_direct = o->bwd_direct != 0;
+    r.step_cache = o->step_cache != 0;
     r.chain_spin = o->chain_spin;
     r.timer = o->timer;
     return r;
@@ -754,7 +755,7 @@ ret_status_t step_run(const void* q, const void* k, const void* v, void* o, floa
         }
     int cw = 0, wr = 0, ppw = 1;
     step_kernel_t fn = step_kernel_get(in_dt == RET_BF16, dk, dv, B * H, op.step_cw, op.step_wr, op.step_pairs,
-                                       A.pos != nullptr, &cw, &wr, &ppw);
+                                       A.pos != nullptr, !op.step_cache, &cw, &wr, &ppw);
     if (!fn) return fail(RET_ERR_UNSUPPORTED, "decode step: d_k=%d not in {16,32,64,128,256}", dk);
     hipStream_t s = (hipStream_t)stream;
     LaunchTimer tm("ret_recurrent_step", s, op);

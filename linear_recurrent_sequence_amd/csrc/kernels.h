@@ -814,14 +814,19 @@ __device__ __forceinline__ void load_n(const typename E::st* p, float* f) {
 // (b, h) pairs per grouped decode workgroup: as many as fill 8 waves of d_k / wr waves each.
 __host__ __device__ constexpr int step_group_pairs(int dk, int wr) { return dk / wr >= 8 ? 1 : 8 / (dk / wr); }
 
+// Cache-policy operand of a buffer access with the non-temporal hint (gfx950).
+constexpr int kCachePolicyNT = 2;
+
 // One decode step for PPW (b, h) pairs and CW state columns: NW waves of WR rows per pair. Lane (rg, cg) of a wave
 // owns columns 4cg..4cg+3 of rows rg*RPT .. +RPT-1 (each row segment one 16-byte access, a row's CW columns
 // contiguous across the cg lanes). Every address is formed first and every load (q, k, v, the rotation factors,
 // then the state rows) issued before any is waited for; each row is updated and written back as soon as it
 // arrives, so loads and stores overlap. o sums q_r S_r over the rows (shuffles within a wave, LDS across waves).
 // Several pairs share a workgroup of up to 8 waves: fewer, larger workgroups reach the state sooner than many
-// small ones. Pairs past B*H (a partial last workgroup) load the last pair and store nothing.
-template <class E, int DK, int CW, int WR, int PPW, bool POS>
+// small ones. Pairs past B*H (a partial last workgroup) load the last pair and store nothing. NT: the state's
+// loads and stores carry the non-temporal hint, for a state that is read and written once per step and not
+// again before it has left the caches (one state of many, as one per layer of a model).
+template <class E, int DK, int CW, int WR, int PPW, bool POS, bool NT>
 __global__ __launch_bounds__(64 * (DK / WR) * PPW) void recurrent_step_kernel(StepArgs a) {
     typedef typename E::st st;
     constexpr int NW = DK / WR;                 // waves per pair
@@ -867,10 +872,12 @@ __global__ __launch_bounds__(64 * (DK / WR) * PPW) void recurrent_step_kernel(St
             rs[p] = a.rs[r0 / 2 + p];
         }
     }
+    constexpr int cpol = NT ? kCachePolicyNT : 0;
     float4 x[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-        const f32x4_t t = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(srs, svoff, i * dv * 4, 0));
+        const f32x4_t t =
+            __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(srs, svoff, i * dv * 4, cpol));
         x[i] = make_float4(t[0], t[1], t[2], t[3]);
     }
     // Every row has arrived before the first state store goes out. The compiler's own waits would otherwise let
@@ -902,7 +909,7 @@ __global__ __launch_bounds__(64 * (DK / WR) * PPW) void recurrent_step_kernel(St
         x[i].z = g * x[i].z + kv[i] * vv[2];
         x[i].w = g * x[i].w + kv[i] * vv[3];
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, f32x4_t{x[i].x, x[i].y, x[i].z, x[i].w}), srs,
-                                               svoff, i * dv * 4, 0);
+                                               svoff, i * dv * 4, cpol);
         acc.x += qv[i] * x[i].x;
         acc.y += qv[i] * x[i].y;
         acc.z += qv[i] * x[i].z;
@@ -1016,9 +1023,10 @@ bool parallel_kernel_get(bool bf16_in, int dk, int dv, ParKernel* out);
 // Decode kernel for a (d_k, column tile cw, rows per wave wr) tile, 0 = default, null if none; with pairs_mode 0
 // it groups (b, h) pairs into workgroups of up to 8 waves where B*H leaves a workgroup per CU; 1 / 2 force one
 // / grouped. The launch is ceil(d_v / cw) x ceil(B*H / ppw) workgroups of 64 * (d_k / wr) * ppw threads.
-// positions: the per-sequence-position kernel (default tile only: cw and wr are ignored).
+// positions: the per-sequence-position kernel (default tile only: cw and wr are ignored). stream: the state's
+// accesses carry the non-temporal hint, and pairs_mode 0 keeps one pair per workgroup.
 step_kernel_t step_kernel_get(bool bf16_in, int dk, int dv, int npairs, int cw, int wr, int pairs_mode,
-                              bool positions, int* cw_used, int* wr_used, int* ppw_used);
+                              bool positions, bool stream, int* cw_used, int* wr_used, int* ppw_used);
 
 // Multi-scale retention epilogue y = swish(gate) (.) GroupNorm_h(o) over groups of d_v values.
 struct EpiArgs {

@@ -107,53 +107,54 @@ bool parallel_kernel_get(bool bf16_in, int dk, int dv, ParKernel* out) {
 // fill 8 waves (step_group_pairs).
 namespace {
 template <class E, int DK, int CW, int WR, bool POS = false>
-step_kernel_t step_pick(bool grouped) {
+step_kernel_t step_pick(bool grouped, bool nt) {
     if constexpr (WR <= DK && WR * CW >= 512 && DK / WR <= 16) {
         constexpr int G = step_group_pairs(DK, WR);
-        if (grouped && G > 1) return recurrent_step_kernel<E, DK, CW, WR, G, POS>;
-        return recurrent_step_kernel<E, DK, CW, WR, 1, POS>;
+        if (grouped && G > 1)
+            return nt ? recurrent_step_kernel<E, DK, CW, WR, G, POS, true> : recurrent_step_kernel<E, DK, CW, WR, G, POS, false>;
+        return nt ? recurrent_step_kernel<E, DK, CW, WR, 1, POS, true> : recurrent_step_kernel<E, DK, CW, WR, 1, POS, false>;
     }
     return nullptr;
 }
 // Per-sequence positions: the default tile of each d_k (64 columns; 32 rows per wave, d_k rows below 32).
 template <class E>
-step_kernel_t step_pick_positions(int dk, bool grouped) {
+step_kernel_t step_pick_positions(int dk, bool grouped, bool nt) {
     switch (dk) {
-        case 16: return step_pick<E, 16, 64, 16, true>(grouped);
-        case 32: return step_pick<E, 32, 64, 32, true>(grouped);
-        case 64: return step_pick<E, 64, 64, 32, true>(grouped);
-        case 128: return step_pick<E, 128, 64, 32, true>(grouped);
-        case 256: return step_pick<E, 256, 64, 32, true>(grouped);
+        case 16: return step_pick<E, 16, 64, 16, true>(grouped, nt);
+        case 32: return step_pick<E, 32, 64, 32, true>(grouped, nt);
+        case 64: return step_pick<E, 64, 64, 32, true>(grouped, nt);
+        case 128: return step_pick<E, 128, 64, 32, true>(grouped, nt);
+        case 256: return step_pick<E, 256, 64, 32, true>(grouped, nt);
         default: return nullptr;
     }
 }
 template <class E, int DK, int CW>
-step_kernel_t step_pick_wr(int wr, bool grouped) {
-    if (wr == 16) return step_pick<E, DK, CW, 16>(grouped);
-    if (wr == 32) return step_pick<E, DK, CW, 32>(grouped);
-    return step_pick<E, DK, CW, 64>(grouped);
+step_kernel_t step_pick_wr(int wr, bool grouped, bool nt) {
+    if (wr == 16) return step_pick<E, DK, CW, 16>(grouped, nt);
+    if (wr == 32) return step_pick<E, DK, CW, 32>(grouped, nt);
+    return step_pick<E, DK, CW, 64>(grouped, nt);
 }
 template <class E, int DK>
-step_kernel_t step_pick_cw(int cw, int wr, bool grouped) {
-    if (cw == 16) return step_pick_wr<E, DK, 16>(wr, grouped);
-    if (cw == 32) return step_pick_wr<E, DK, 32>(wr, grouped);
-    return step_pick_wr<E, DK, 64>(wr, grouped);
+step_kernel_t step_pick_cw(int cw, int wr, bool grouped, bool nt) {
+    if (cw == 16) return step_pick_wr<E, DK, 16>(wr, grouped, nt);
+    if (cw == 32) return step_pick_wr<E, DK, 32>(wr, grouped, nt);
+    return step_pick_wr<E, DK, 64>(wr, grouped, nt);
 }
 template <class E>
-step_kernel_t step_pick_dk(int dk, int cw, int wr, bool grouped) {
+step_kernel_t step_pick_dk(int dk, int cw, int wr, bool grouped, bool nt) {
     switch (dk) {
-        case 16: return step_pick_cw<E, 16>(cw, wr, grouped);
-        case 32: return step_pick_cw<E, 32>(cw, wr, grouped);
-        case 64: return step_pick_cw<E, 64>(cw, wr, grouped);
-        case 128: return step_pick_cw<E, 128>(cw, wr, grouped);
-        case 256: return step_pick_cw<E, 256>(cw, wr, grouped);
+        case 16: return step_pick_cw<E, 16>(cw, wr, grouped, nt);
+        case 32: return step_pick_cw<E, 32>(cw, wr, grouped, nt);
+        case 64: return step_pick_cw<E, 64>(cw, wr, grouped, nt);
+        case 128: return step_pick_cw<E, 128>(cw, wr, grouped, nt);
+        case 256: return step_pick_cw<E, 256>(cw, wr, grouped, nt);
         default: return nullptr;
     }
 }
 }  // namespace
 
 step_kernel_t step_kernel_get(bool bf16_in, int dk, int dv, int npairs, int cw, int wr, int pairs_mode,
-                              bool positions, int* cw_used, int* wr_used, int* ppw_used) {
+                              bool positions, bool stream, int* cw_used, int* wr_used, int* ppw_used) {
     if (cw == 0 || positions) cw = 64;  // defaults: 64 columns x 32 rows per wave (two waves per 64-row tile)
     if (wr == 0 || positions) wr = 32;
     if (cw != 16 && cw != 32 && cw != 64) return nullptr;
@@ -163,13 +164,16 @@ step_kernel_t step_kernel_get(bool bf16_in, int dk, int dv, int npairs, int cw, 
     while (wr * cw < 512 && wr < 64 && wr < dk) wr *= 2;
     *cw_used = cw;
     *wr_used = wr;
-    // Grouped workgroups where they still give every CU one: mode 0 decides, 1 forces one pair, 2 grouping.
+    // Grouped workgroups where they still give every CU one: mode 0 decides, 1 forces one pair, 2 grouping. A
+    // streamed state goes one pair per workgroup by default: its requests reach memory sooner from many small
+    // workgroups.
     const int g = step_group_pairs(dk, wr);
     const long long wgs = (long long)(npairs + g - 1) / g * ((dv + cw - 1) / cw);
-    const bool grouped = g > 1 && (pairs_mode == 2 || (pairs_mode == 0 && wgs >= 256));
+    const bool grouped = g > 1 && (pairs_mode == 2 || (pairs_mode == 0 && !stream && wgs >= 256));
     *ppw_used = grouped ? g : 1;
-    if (positions) return bf16_in ? step_pick_positions<BF16>(dk, grouped) : step_pick_positions<F32>(dk, grouped);
-    return bf16_in ? step_pick_dk<BF16>(dk, cw, wr, grouped) : step_pick_dk<F32>(dk, cw, wr, grouped);
+    if (positions)
+        return bf16_in ? step_pick_positions<BF16>(dk, grouped, stream) : step_pick_positions<F32>(dk, grouped, stream);
+    return bf16_in ? step_pick_dk<BF16>(dk, cw, wr, grouped, stream) : step_pick_dk<F32>(dk, cw, wr, grouped, stream);
 }
 
 fwd_kernel_t segment_scan_get() { return segment_scan_kernel; }

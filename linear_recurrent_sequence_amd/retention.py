@@ -39,6 +39,7 @@ class Options(ctypes.Structure):
     _fields_ = [("segments", ctypes.c_int), ("target_wgs", ctypes.c_int), ("prerotate", ctypes.c_int),
                 ("onchip", ctypes.c_int), ("variant", ctypes.c_int), ("step_cw", ctypes.c_int),
                 ("step_wr", ctypes.c_int), ("step_pairs", ctypes.c_int), ("bwd_direct", ctypes.c_int),
+                ("step_cache", ctypes.c_int),
                 ("chain_spin", ctypes.c_longlong), ("timer", ctypes.c_void_p)]
 
 

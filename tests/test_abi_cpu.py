@@ -195,8 +195,8 @@ def test_options_and_timer_objects(lib):
     from linear_recurrent_sequence_amd import retention as R
     o = R.Options()
     lib.ret_options_default(ctypes.byref(o))
-    assert (o.segments, o.target_wgs, o.prerotate, o.onchip, o.variant, o.bwd_direct, o.chain_spin) == \
-        (0, 0, -1, 1, 0, 1, 0)
+    assert (o.segments, o.target_wgs, o.prerotate, o.onchip, o.variant, o.bwd_direct, o.step_cache, o.chain_spin) == \
+        (0, 0, -1, 1, 0, 1, 0, 0)
     assert o.timer is None
     t = R.Timer()
     assert t.query("") == (0.0, 0)

@@ -357,16 +357,18 @@ def test_parallel_small(R, dt, dk, dv):
 
 
 # decode tiles: state columns and rows per wave (the library widens tiles too small for a shape); pairs "2"
-# forces workgroups of several (b, h) pairs, here with a partial last workgroup (6 pairs)
+# forces workgroups of several (b, h) pairs, here with a partial last workgroup (6 pairs); cache "1" the state's
+# accesses without the non-temporal hint
+@pytest.mark.parametrize("cache", ["0", "1"])
 @pytest.mark.parametrize("pairs", ["0", "2"])
 @pytest.mark.parametrize("cw,wr", [("16", "64"), ("32", "64"), ("64", "64"), ("32", "32"), ("32", "16"),
                                    ("64", "16")])
 @pytest.mark.parametrize("dt,dk,dv", [("f32", 16, 16), ("f32", 64, 36), ("bf16", 64, 64), ("bf16", 128, 128),
                                       ("bf16", 256, 200)])
-def test_recurrent_steps_small(R, dt, dk, dv, cw, wr, pairs):
+def test_recurrent_steps_small(R, dt, dk, dv, cw, wr, pairs, cache):
     import torch
-    print_case("recurrent_small", dt, dk, dv, cw, wr, pairs)
-    opts = {"step_cw": int(cw), "step_wr": int(wr), "step_pairs": int(pairs)}
+    print_case("recurrent_small", dt, dk, dv, cw, wr, pairs, cache)
+    opts = {"step_cw": int(cw), "step_wr": int(wr), "step_pairs": int(pairs), "step_cache": int(cache)}
     rng = np.random.default_rng(9)
     B, H, n = 3, 2, 20
     scale = 1.0 if dt == "f32" else 8.0

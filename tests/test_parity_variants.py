@@ -134,13 +134,14 @@ def _steps_per_position(q, k, v, gamma, theta, s0, pos):
     return o, s
 
 
+@pytest.mark.parametrize("cache", ["0", "1"])
 @pytest.mark.parametrize("pairs", ["0", "2"])
 @pytest.mark.parametrize("dt,dk,dv", [("f32", 16, 16), ("f32", 64, 36), ("bf16", 64, 64), ("bf16", 128, 128),
                                       ("bf16", 256, 200)])
-def test_step_per_sequence_positions(R, dt, dk, dv, pairs):
+def test_step_per_sequence_positions(R, dt, dk, dv, pairs, cache):
     import torch
-    print_case("step_positions", dt, dk, dv, pairs)
-    opts = {"step_pairs": int(pairs)}
+    print_case("step_positions", dt, dk, dv, pairs, cache)
+    opts = {"step_pairs": int(pairs), "step_cache": int(cache)}
     rng = np.random.default_rng(21)
     B, H = 6, 3
     pos = np.array([0, 5, 100, 65536, 3, 1 << 30], np.int64)
