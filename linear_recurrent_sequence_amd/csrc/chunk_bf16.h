@@ -26,6 +26,10 @@ __device__ __forceinline__ rsrc_t bytes_rsrc(const void* base, int nbytes) {
 __device__ __forceinline__ u32x4_t buf_load16(rsrc_t r, int voff, int soff) {
     return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
+// The same with the non-temporal hint, for rows a kernel reads once.
+__device__ __forceinline__ u32x4_t buf_load16_nt(rsrc_t r, int voff, int soff) {
+    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kCachePolicyNT));
+}
 __device__ __forceinline__ void buf_store16(rsrc_t r, int voff, int soff, u32x4_t x) {
     __builtin_amdgcn_raw_buffer_store_b128(x, r, voff, soff, 0);
 }

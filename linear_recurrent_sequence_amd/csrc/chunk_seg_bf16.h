@@ -8,7 +8,8 @@
 // which is added once R_in is known. Until then each chunk's local outputs stay in fp32 registers and its Q'
 // (rotated q) stays in its own LDS tile; the local end state is the segment's aggregate, published for the
 // later segments as soon as the last chunk is done. The chain's latency thus overlaps the segment's streaming
-// and main products instead of preceding them, and q, k and v are read from HBM once.
+// and main products instead of preceding them, and q, k and v are read from HBM once (with the non-temporal
+// hint: no row is read again).
 //
 // REV runs the same recurrence over the reversed sequence (token n of the run is row N-1-n of q, k, v and o):
 // the gradients' retentions that sum over later tokens. Only with q and k as given (PRE, no rotation), and
@@ -128,19 +129,19 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_seg_bf16(FwdArgs a) {
 #pragma unroll
             for (int p = 0; p < TQ::NP; ++p) {
                 const int off = row_off(L, qrow + p * TQ::RP, rsk, qseg * 8, 2);
-                bk[par][p] = buf_load16(rk, off, 0);
-                bq[par][p] = buf_load16(rq, off, 0);
+                bk[par][p] = buf_load16_nt(rk, off, 0);
+                bq[par][p] = buf_load16_nt(rq, off, 0);
             }
 #pragma unroll
-            for (int p = 0; p < TV::NP; ++p) bv[par][p] = buf_load16(rv, row_off(L, vrow + p * TV::RP, rsv, vseg * 8, 2), 0);
+            for (int p = 0; p < TV::NP; ++p) bv[par][p] = buf_load16_nt(rv, row_off(L, vrow + p * TV::RP, rsv, vseg * 8, 2), 0);
         } else {
 #pragma unroll
             for (int p = 0; p < TQ::NP; ++p) {
-                bk[par][p] = buf_load16(rk, qoff, p * TQ::RP * rsk * 2);
-                bq[par][p] = buf_load16(rq, qoff, p * TQ::RP * rsk * 2);
+                bk[par][p] = buf_load16_nt(rk, qoff, p * TQ::RP * rsk * 2);
+                bq[par][p] = buf_load16_nt(rq, qoff, p * TQ::RP * rsk * 2);
             }
 #pragma unroll
-            for (int p = 0; p < TV::NP; ++p) bv[par][p] = buf_load16(rv, voff, p * TV::RP * rsv * 2);
+            for (int p = 0; p < TV::NP; ++p) bv[par][p] = buf_load16_nt(rv, voff, p * TV::RP * rsv * 2);
         }
     };
     static_for<0, (NBUF < F::MAXC ? NBUF : F::MAXC)>([&](auto cc) __attribute__((always_inline)) { issue(cc); });
@@ -338,8 +339,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_seg_bf16(FwdArgs a) {
 #pragma unroll
             for (int p = 0; p < C / 32; ++p) {
                 const int off = ((row + 32 * p) * rsv + sg * 8) * gsz;
-                gu[p][0] = buf_load16(rg, off, 0);
-                gu[p][1] = a.gate_bf16 ? u32x4_t{0u, 0u, 0u, 0u} : buf_load16(rg, off + 16, 0);
+                gu[p][0] = buf_load16_nt(rg, off, 0);
+                gu[p][1] = a.gate_bf16 ? u32x4_t{0u, 0u, 0u, 0u} : buf_load16_nt(rg, off + 16, 0);
             }
         }
     };

@@ -26,11 +26,12 @@ struct EpiTile {
     static_assert(LPG >= 1 && LPG <= 64 && 64 % LPG == 0, "epilogue tile");
 };
 
-// 8 consecutive values at element offset i of an fp32 or bf16 array (16-byte vectors).
+// 8 consecutive values at element offset i of an fp32 or bf16 array (16-byte vectors). The epilogue reads and
+// writes every value once: its accesses carry the non-temporal hint.
 __device__ __forceinline__ void load8(const void* p, long long i, bool bf16, float* f) {
     if (bf16) {
-        const uint4 u = *reinterpret_cast<const uint4*>((const uint16_t*)p + i);
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+        const u32x4_t u = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>((const uint16_t*)p + i));
+        const uint32_t w[4] = {u[0], u[1], u[2], u[3]};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             f[2 * e] = __uint_as_float(w[e] << 16);
@@ -39,11 +40,11 @@ __device__ __forceinline__ void load8(const void* p, long long i, bool bf16, flo
     } else {
 #pragma unroll
         for (int e = 0; e < 8; e += 4) {
-            const float4 x = *reinterpret_cast<const float4*>((const float*)p + i + e);
-            f[e] = x.x;
-            f[e + 1] = x.y;
-            f[e + 2] = x.z;
-            f[e + 3] = x.w;
+            const f32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>((const float*)p + i + e));
+            f[e] = x[0];
+            f[e + 1] = x[1];
+            f[e + 2] = x[2];
+            f[e + 3] = x[3];
         }
     }
 }
@@ -95,14 +96,14 @@ __global__ __launch_bounds__(256) void msr_epilogue_kernel(EpiArgs a) {
         }
         if (gi[r] >= a.groups) continue;
         if (a.y_bf16) {
-            *reinterpret_cast<uint4*>((uint16_t*)a.y + i0[r]) =
-                make_uint4(pack2_bf16(x[r][0], x[r][1]), pack2_bf16(x[r][2], x[r][3]), pack2_bf16(x[r][4], x[r][5]),
-                           pack2_bf16(x[r][6], x[r][7]));
+            __builtin_nontemporal_store(u32x4_t{pack2_bf16(x[r][0], x[r][1]), pack2_bf16(x[r][2], x[r][3]),
+                                                pack2_bf16(x[r][4], x[r][5]), pack2_bf16(x[r][6], x[r][7])},
+                                        reinterpret_cast<u32x4_t*>((uint16_t*)a.y + i0[r]));
         } else {
 #pragma unroll
             for (int e = 0; e < 8; e += 4)
-                *reinterpret_cast<float4*>((float*)a.y + i0[r] + e) =
-                    make_float4(x[r][e], x[r][e + 1], x[r][e + 2], x[r][e + 3]);
+                __builtin_nontemporal_store(f32x4_t{x[r][e], x[r][e + 1], x[r][e + 2], x[r][e + 3]},
+                                            reinterpret_cast<f32x4_t*>((float*)a.y + i0[r] + e));
         }
     }
 }

@@ -7,6 +7,12 @@
 #include "retention_device.h"
 
 namespace ret {
+// Cache-policy operand of a buffer access with the non-temporal hint (gfx950): for data read or written once,
+// which need not stay in the caches.
+constexpr int kCachePolicyNT = 2;
+}  // namespace ret
+
+namespace ret {
 
 // Arguments shared by the chunk and parallel kernels (passed by value in the kernel-argument segment).
 struct FwdArgs {
@@ -813,9 +819,6 @@ __device__ __forceinline__ void load_n(const typename E::st* p, float* f) {
 
 // (b, h) pairs per grouped decode workgroup: as many as fill 8 waves of d_k / wr waves each.
 __host__ __device__ constexpr int step_group_pairs(int dk, int wr) { return dk / wr >= 8 ? 1 : 8 / (dk / wr); }
-
-// Cache-policy operand of a buffer access with the non-temporal hint (gfx950).
-constexpr int kCachePolicyNT = 2;
 
 // One decode step for PPW (b, h) pairs and CW state columns: NW waves of WR rows per pair. Lane (rg, cg) of a wave
 // owns columns 4cg..4cg+3 of rows rg*RPT .. +RPT-1 (each row segment one 16-byte access, a row's CW columns
