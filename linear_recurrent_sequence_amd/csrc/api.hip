@@ -422,15 +422,18 @@ ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o,
         // Staging copies rows instead of rotating them when there is no rotation, or when q and k are rotated
         // once up front (several d_v tiles stage the same rows).
         fwd_kernel_t fn = onchip ? ck.seg : ck.fused;
-        const fwd_kernel_t fn_pre = onchip ? (rev ? ck.seg_rev : ck.seg_pre) : ck.fused_pre;
+        const fwd_kernel_t fn_pre = onchip ? (rev ? ck.seg_rev : ck.seg_pre)
+                                           : (rev && !ck.split_local ? ck.fused_rev : ck.fused_pre);
         // The reversed run and the rotation of the outputs exist for the on-chip kernel, the reversed run and q, k
-        // taken from wider heads for the three-launch kernels (whole steps only when reversed); both without
-        // input rotation, state or epilogue.
+        // taken from wider heads for the three-launch kernels, and the reversed run for the single-pass kernels
+        // that have one (whole steps only when reversed); all without input rotation, state or epilogue.
         if (rev || out_theta || qk_din) {
             const bool plain = !theta && !state_in && !state_out && !epi;
             const bool seg_ok = onchip && !qk_din && (!rev || ck.seg_rev);
             const bool split_ok = ck.split_local && !onchip && !out_theta && (!rev || N % kDmaStep == 0);
-            if (!plain || !(seg_ok || split_ok))
+            const bool fused_ok = !ck.split_local && !onchip && rev && ck.fused_rev && !out_theta && !qk_din &&
+                                  N % ck.rev_step == 0;
+            if (!plain || !(seg_ok || split_ok || fused_ok))
                 return fail(RET_ERR_UNSUPPORTED, "reversed, output-rotated or column-block chunkwise run: not "
                                                  "available for this shape");
         }
@@ -480,7 +483,7 @@ ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o,
             tm.done();
             return launch_status(ck.pre_name);
         }
-        const bool pre = !onchip && fn == ck.fused_pre;
+        const bool pre = !onchip && (fn == ck.fused_pre || (rev && fn == ck.fused_rev));
         const int threads = onchip || !ck.threads ? kThreads : pre && ck.threads_pre ? ck.threads_pre : ck.threads;
         const char* name = onchip ? "ret_chunk_seg" : pre && ck.pre_name ? ck.pre_name : "ret_chunk_fused";
         if (epi && onchip && out_dt == RET_BF16 && dv == 64) {
@@ -528,7 +531,8 @@ ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o,
 // - otherwise the reordered inputs (K', K' reversed, Q' reversed, and V and dO reversed, or their blocks forward
 //   and reversed) in the input dtype, and the fp32 outputs.
 struct BwdLayout {
-    bool direct, dma;
+    bool direct, inplace;
+    int variant;  // kernel variant of the retentions (the wide-head kernels' for the in-place path on them)
     int nb, wb;  // d_v blocks of width wb for the retentions that contract over d_v (nb = 2 when d_v is wider
                  // than their kernels' d_k; dq' and dk' are then sums of two retentions)
     size_t qp, kp, kr, qr, vr, dor, g1, g2, g3, chain, chain_bytes, total;
@@ -554,18 +558,35 @@ bool bwd_layout(int B, int N, int H, int dk, int dv, int chunk, ret_dtype_t in_d
     const ChunkPlan pb = plan_chunk(cb, B, N, H, dk, dv, chunk, false, SIZE_MAX, op);
     L->direct = in_dt == RET_BF16 && L->nb == 1 && plan_onchip(ca, pa, op) && ca.seg_rev && plan_onchip(cb, pb, op) &&
                 cb.seg_rev && op.bwd_direct != 0;
-    L->dma = !L->direct && in_dt == RET_BF16 && N % kDmaStep == 0 && ca.split_local && !plan_onchip(ca, pa, op) &&
-             cb.split_local && !plan_onchip(cb, pb, op) && op.bwd_direct != 0;
+    L->variant = op.variant;
+    L->inplace = !L->direct && in_dt == RET_BF16 && N % kDmaStep == 0 && ca.split_local &&
+                 !plan_onchip(ca, pa, op) && cb.split_local && !plan_onchip(cb, pb, op) && op.bwd_direct != 0;
     L->chain = 0;
     L->chain_bytes = pa.chain_bytes > pb.chain_bytes ? pa.chain_bytes : pb.chain_bytes;
+    if (!L->direct && !L->inplace && in_dt == RET_BF16 && L->nb == 1 && op.bwd_direct != 0 && op.variant == 0) {
+        // the wide-head kernels run over the reversed sequence in place
+        Opts o3 = op;
+        o3.variant = 3;
+        ChunkKernels wa, wb;
+        if (pick_chunk(in_dt, L->wb, dk, chunk, &wa, o3) && wa.fused_rev && N % wa.rev_step == 0 &&
+            pick_chunk(in_dt, dk, dv, chunk, &wb, o3) && wb.fused_rev && N % wb.rev_step == 0) {
+            const ChunkPlan qa = plan_chunk(wa, B, N, H, L->wb, dk, chunk, false, SIZE_MAX, o3);
+            const ChunkPlan qb = plan_chunk(wb, B, N, H, dk, dv, chunk, false, SIZE_MAX, o3);
+            if (!plan_onchip(wa, qa, o3) && !plan_onchip(wb, qb, o3)) {
+                L->inplace = true;
+                L->variant = 3;
+                L->chain_bytes = qa.chain_bytes > qb.chain_bytes ? qa.chain_bytes : qb.chain_bytes;
+            }
+        }
+    }
     size_t off = up(L->chain_bytes > 256 ? L->chain_bytes : 256);
-    if (L->direct || L->dma) {
+    if (L->direct || L->inplace) {
         if (rotate) {
             L->qp = off;
             L->kp = L->qp + up(nk * 2);
             off = L->kp + up(nk * 2);
         }
-        if (L->dma)
+        if (L->inplace)
             for (int i = 0; i < L->nb; ++i) {
                 L->g1b[i] = off;
                 L->g3b[i] = L->g1b[i] + up(nk * 4);
@@ -851,12 +872,16 @@ ret_status_t ret_chunkwise_bwd_ex(const void* q, const void* k, const void* v, c
     hipStream_t s = (hipStream_t)stream;
     char* ws = (char*)workspace;
     const int ob = out_dt == RET_BF16;
-    if (L.dma) {
+    if (L.inplace) {
         // Q', K' (rotated once), then, with the d_v blocks b of dO and V read in place:
         //   dq' = sum over b of retention(dO_b, V_b, K')
         //   dv  = retention(K', Q', dO) over the reversed sequence, rows read and written in reverse order
         //   dk' = sum over b of retention(V_b, dO_b, Q') over the reversed sequence
-        // dv is written as the output; dq and dk are the block sums turned back by the transpose rotation.
+        // dv is written as the output; dq and dk are the block sums turned back by the transpose rotation. The
+        // retentions run on the three-launch kernels, or (one block) on the wide-head kernels (variant 3), whose
+        // segment chain is cleared between calls of different shapes.
+        Opts ov = op;
+        ov.variant = L.variant;
         const void *Qp = q, *Kp = k;
         if (theta) {
             FwdArgs A;
@@ -874,15 +899,20 @@ ret_status_t ret_chunkwise_bwd_ex(const void* q, const void* k, const void* v, c
         const int wb = L.wb, din = L.nb > 1 ? dv : 0;
         for (int i = 0; i < L.nb; ++i)
             if ((st = chunkwise_run(dout, v, Kp, ws + L.g1b[i], B, N, H, wb, dk, RET_BF16, RET_F32, gamma, nullptr, 0,
-                                    chunk, nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, op, false,
+                                    chunk, nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, ov, false,
                                     nullptr, din, i * wb)) != RET_OK)
                 return st;
+        const bool reshaped = wb != dk || dk != dv;  // the (d_k, d_v) of the runs differ
+        if (reshaped && (st = chain_meta_zero(in_dt, B, N, H, dk, dv, chunk, chain, L.chain_bytes, s, ov)) != RET_OK)
+            return st;
         if ((st = chunkwise_run(Kp, Qp, dout, dv_out, B, N, H, dk, dv, RET_BF16, out_dt, gamma, nullptr, 0, chunk,
-                                nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, op, true)) != RET_OK)
+                                nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, ov, true)) != RET_OK)
+            return st;
+        if (reshaped && (st = chain_meta_zero(in_dt, B, N, H, wb, dk, chunk, chain, L.chain_bytes, s, ov)) != RET_OK)
             return st;
         for (int i = 0; i < L.nb; ++i)
             if ((st = chunkwise_run(v, dout, Qp, ws + L.g3b[i], B, N, H, wb, dk, RET_BF16, RET_F32, gamma, nullptr, 0,
-                                    chunk, nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, op, true,
+                                    chunk, nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, ov, true,
                                     nullptr, din, i * wb)) != RET_OK)
                 return st;
         const bool two = L.nb > 1;

@@ -19,22 +19,25 @@ namespace {
 // job (blockIdx.y: the job's fields are scalar loads). Its loads are issued together; the rotation factors of
 // the first token are evaluated exactly and carried to the next by angle addition with the one-token step.
 // Consecutive threads take consecutive segments of a row, and a job with two outputs writes both from one read.
+// Every value is read and written once per launch: the accesses carry the non-temporal hint.
 __device__ __forceinline__ void perm_load(const void* p, bool bf16, long long i, float* x) {
     if (bf16) {
-        unpack8_bf16(*reinterpret_cast<const uint4*>((const uint16_t*)p + i), x);
+        const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>((const uint16_t*)p + i));
+        unpack8_bf16(make_uint4(t[0], t[1], t[2], t[3]), x);
     } else {
-        const float4 u = *reinterpret_cast<const float4*>((const float*)p + i);
-        const float4 w = *reinterpret_cast<const float4*>((const float*)p + i + 4);
-        x[0] = u.x, x[1] = u.y, x[2] = u.z, x[3] = u.w, x[4] = w.x, x[5] = w.y, x[6] = w.z, x[7] = w.w;
+        const f32x4_t u = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>((const float*)p + i));
+        const f32x4_t w = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>((const float*)p + i + 4));
+        x[0] = u[0], x[1] = u[1], x[2] = u[2], x[3] = u[3], x[4] = w[0], x[5] = w[1], x[6] = w[2], x[7] = w[3];
     }
 }
 
 __device__ __forceinline__ void perm_store(const PermJob& J, void* out, long long i, const float* x) {
     if (J.out_bf16) {
-        *reinterpret_cast<uint4*>((uint16_t*)out + i) = pack8_bf16(x);
+        const uint4 t = pack8_bf16(x);
+        __builtin_nontemporal_store(u32x4_t{t.x, t.y, t.z, t.w}, reinterpret_cast<u32x4_t*>((uint16_t*)out + i));
     } else {
-        *reinterpret_cast<float4*>((float*)out + i) = make_float4(x[0], x[1], x[2], x[3]);
-        *reinterpret_cast<float4*>((float*)out + i + 4) = make_float4(x[4], x[5], x[6], x[7]);
+        __builtin_nontemporal_store(f32x4_t{x[0], x[1], x[2], x[3]}, reinterpret_cast<f32x4_t*>((float*)out + i));
+        __builtin_nontemporal_store(f32x4_t{x[4], x[5], x[6], x[7]}, reinterpret_cast<f32x4_t*>((float*)out + i + 4));
     }
 }
 

@@ -19,6 +19,8 @@ template <int C>
 ChunkKernels chunk_entry_wide256() {
     ChunkKernels k = chunk_entry_bf16<256, C, 512>();
     k.fused_pre = chunk_wide_get(256);
+    k.fused_rev = chunk_wide_get(256, true);
+    k.rev_step = kWideStep;
     k.threads_pre = kWideThreads;
     k.pre_always = 1;
     k.pre_name = "ret_chunk_wide";

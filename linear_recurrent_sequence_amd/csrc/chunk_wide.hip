@@ -7,13 +7,14 @@
 namespace ret {
 
 static_assert(WideB<256>::NT == kWideThreads && WideB<128>::NT == kWideThreads, "workgroup size");
+static_assert(WideB<256>::C == kWideStep && WideB<128>::C == kWideStep, "step");
 static_assert(DmaB<256>::NT == kDmaThreads && DmaB<128>::NT == kDmaThreads, "workgroup size");
 static_assert(DmaB<256>::DVT == kDmaDvt && DmaB<128>::DVT == kDmaDvt, "d_v tile");
 static_assert(DmaB<256>::C == kDmaStep && DmaB<128>::C == kDmaStep, "step");
 
-fwd_kernel_t chunk_wide_get(int dk) {
-    if (dk == 256) return chunk_wide_bf16<256>;
-    if (dk == 128) return chunk_wide_bf16<128>;
+fwd_kernel_t chunk_wide_get(int dk, bool rev) {
+    if (dk == 256) return rev ? chunk_wide_bf16<256, true> : chunk_wide_bf16<256, false>;
+    if (dk == 128) return rev ? chunk_wide_bf16<128, true> : chunk_wide_bf16<128, false>;
     return nullptr;
 }
 

@@ -11,7 +11,8 @@
 //    pass over 128 registers per step otherwise); the cross term takes gamma^T with xi. R^ is rescaled (R^ <-
 //    gamma^T R^, T = 0) before gamma^-T could exceed 2^64, and before it is published or stored.
 // Chunks of 64 or more tokens run as 32-token sub-chunks (the chunkwise form gives the same result for any chunk
-// size, up to rounding).
+// size, up to rounding). REV runs the recurrence over the reversed sequence in place (token n of the run is row
+// N-1-n of q, k, v and o; whole steps only, N a multiple of 32): the gradients' retentions over later tokens.
 #pragma once
 
 #include "chunk_bf16.h"
@@ -39,7 +40,7 @@ struct WideB {
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
-template <int DK>
+template <int DK, bool REV>
 __global__ __launch_bounds__(256, (DK <= 128 ? 2 : 1)) void chunk_wide_bf16(FwdArgs a) {
     typedef WideB<DK> F;
     constexpr int NT = F::NT, C = F::C, NKB = F::NKB, KS = F::KS;
@@ -75,12 +76,19 @@ __global__ __launch_bounds__(256, (DK <= 128 ? 2 : 1)) void chunk_wide_bf16(FwdA
     const int seg_n = (int)(min((long long)aN, seg_t0 + aseg_len) - seg_t0);
     const int nchunks = (seg_n + C - 1) / C;
     const int rsk = aH * adk, rsv = aH * adv;
-    const long long head0 = ((long long)b * aN + seg_t0) * aH + h;
-    const uint16_t* qh = (const uint16_t*)a.qr + head0 * adk;
-    const uint16_t* kh = (const uint16_t*)a.kr + head0 * adk;
-    const uint16_t* vh = (const uint16_t*)a.v + head0 * adv + dv0;
+    // token 0 of this (b, h), in head rows; the first row in memory of step c: token seg_t0 + c C of the run, or,
+    // over the reversed sequence, row N - seg_t0 - (c + 1) C, whose C rows are the step's tokens in reverse order
+    const long long hrow = (long long)b * aN * aH + h;
+    auto crow = [&](int c) __attribute__((always_inline)) {
+        return REV ? (long long)aN - seg_t0 - (long long)(c + 1) * C : seg_t0 + (long long)c * C;
+    };
+    const uint16_t* qh = (const uint16_t*)a.qr + hrow * adk;
+    const uint16_t* kh = (const uint16_t*)a.kr + hrow * adk;
+    const uint16_t* vh = (const uint16_t*)a.v + hrow * adv + dv0;
     const int osz = a.out_bf16 ? 2 : 4;
-    char* oh = (char*)a.o + (head0 * adv + dv0) * osz;
+    char* oh = (char*)a.o + (hrow * adv + dv0) * osz;
+    // the step's row (and LDS row) of memory row r of its rows
+    auto lrow = [&](int r) __attribute__((always_inline)) { return REV ? C - 1 - r : r; };
 
     // staging: thread t moves 16-byte row segments: q'/k' rows qrow + 8p (segment qseg), v rows vrow + 16p
     const int qrow = tid / TQ::SPR, qseg = tid % TQ::SPR;
@@ -112,7 +120,7 @@ __global__ __launch_bounds__(256, (DK <= 128 ? 2 : 1)) void chunk_wide_bf16(FwdA
     auto issue = [&](int c, auto parc, auto withq) __attribute__((always_inline)) {
         constexpr int par = decltype(parc)::value;
         const int L = min(C, seg_n - c * C);
-        const long long tc = (long long)c * C;
+        const long long tc = crow(c);
         const rsrc_t rk = bytes_rsrc(kh + tc * rsk, L > 0 ? ((L - 1) * rsk + DK) * 2 : 0);
         const rsrc_t rv = bytes_rsrc(vh + tc * rsv, L > 0 ? ((L - 1) * rsv + F::DVT) * 2 : 0);
 #pragma unroll
@@ -144,12 +152,13 @@ __global__ __launch_bounds__(256, (DK <= 128 ? 2 : 1)) void chunk_wide_bf16(FwdA
         const int L = min(C, seg_n - c * C);
 #pragma unroll
         for (int p = 0; p < TQ::NP; ++p) {
-            lds_store16(sK + ZQ::off(qrow + p * TQ::RP, qseg * 8), bk[par][p]);
-            if constexpr (decltype(withq)::value) lds_store16(sQ + ZQ::off(qrow + p * TQ::RP, qseg * 8), bq[par][p]);
+            lds_store16(sK + ZQ::off(lrow(qrow + p * TQ::RP), qseg * 8), bk[par][p]);
+            if constexpr (decltype(withq)::value)
+                lds_store16(sQ + ZQ::off(lrow(qrow + p * TQ::RP), qseg * 8), bq[par][p]);
         }
 #pragma unroll
         for (int p = 0; p < TV::NP; ++p) {
-            const int r = vrow + p * TV::RP;
+            const int r = lrow(vrow + p * TV::RP);
             lds_store16(sV + ZV::off(r, vseg * 8), bv[par][p]);
             const float z = r < L ? gpow(lg, -(T + (float)(r + 1))) : 0.f;
             float vf[8];
@@ -244,10 +253,12 @@ __global__ __launch_bounds__(256, (DK <= 128 ? 2 : 1)) void chunk_wide_bf16(FwdA
 #pragma unroll
     for (int x = 0; x < 2; ++x) Xi[x] = gpow(lg, (float)(x * 16 + n16 + 1));
     for (int i = tid; i < C * F::LDP; i += NT) sP[i] = 0;  // keys above the diagonal stay zero
-    const int o_voff = (n16 * rsv + w * 2 * 16 + g4) * osz;
+    // output row x * 16 + n16 of a step: at row x * 16 + n16 of its rows in memory, or reversed at
+    // (1 - x) * 16 + 15 - n16
+    const int o_voff = ((REV ? 15 - n16 : n16) * rsv + w * 2 * 16 + g4) * osz;
     auto store_out = [&](int c, const f32x4_t* O) __attribute__((always_inline)) {
         const int L = min(C, seg_n - c * C);
-        const rsrc_t ro = bytes_rsrc(oh + (long long)c * C * rsv * osz, ((L - 1) * rsv + F::DVT) * osz);
+        const rsrc_t ro = bytes_rsrc(oh + crow(c) * rsv * osz, ((L - 1) * rsv + F::DVT) * osz);
         if (a.out_bf16) {
 #pragma unroll
             for (int x = 0; x < 2; ++x)
@@ -257,14 +268,14 @@ __global__ __launch_bounds__(256, (DK <= 128 ? 2 : 1)) void chunk_wide_bf16(FwdA
                         __builtin_bit_cast(uint32_t __attribute__((ext_vector_type(2))),
                                            make_uint2(pack2_bf16(O[x * 2 + j][0], O[x * 2 + j][1]),
                                                       pack2_bf16(O[x * 2 + j][2], O[x * 2 + j][3]))),
-                        ro, o_voff, (x * 16 * rsv + j * 16) * 2, kOutAux);
+                        ro, o_voff, ((REV ? 1 - x : x) * 16 * rsv + j * 16) * 2, kOutAux);
         } else {
 #pragma unroll
             for (int x = 0; x < 2; ++x)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
                     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, O[x * 2 + j]), ro, o_voff,
-                                                           (x * 16 * rsv + j * 16) * 4, kOutAux);
+                                                           ((REV ? 1 - x : x) * 16 * rsv + j * 16) * 4, kOutAux);
         }
     };
     // Step c: commit its registers to buffer c & 1 (last read by step c - 2, which every wave finished before

@@ -983,6 +983,10 @@ struct ChunkKernels {
     // otherwise. split_local_rev and split_full_rev run over the reversed sequence (token n of the run is row N-1-n
     // of q, k, v and o; N a multiple of kDmaStep).
     fwd_kernel_t split_local, split_scan, split_local_rev, split_full_rev;
+    // fused_pre over the reversed sequence (token n of the run is row N-1-n of q, k, v and o; N a multiple of
+    // rev_step), or null
+    fwd_kernel_t fused_rev;
+    int rev_step;
 };
 struct ParKernel {
     fwd_kernel_t fn;
@@ -1010,9 +1014,10 @@ bool chunk_kernels_bf16_small(int dk, int dv, int C, ChunkKernels* out);   // d_
 bool chunk_kernels_bf16_128(int dk, int dv, int C, int variant, ChunkKernels* out);  // d_k = 128
 bool chunk_kernels_bf16_256(int dk, int dv, int C, int variant, ChunkKernels* out);  // d_k = 256
 // The wide-head kernel (chunk_wide_bf16.h) for d_k in {128, 256} (null otherwise): kWideThreads threads, d_v tiles
-// of 128, operands staged as given.
-constexpr int kWideThreads = 256;
-fwd_kernel_t chunk_wide_get(int dk);
+// of 128, operands staged as given, steps of kWideStep tokens; rev: over the reversed sequence (N a multiple of
+// kWideStep).
+constexpr int kWideThreads = 256, kWideStep = 32;
+fwd_kernel_t chunk_wide_get(int dk, bool rev = false);
 // The LDS-loading wide-head kernels (chunk_dma_bf16.h) for d_k in {128, 256} (false otherwise): the local pass
 // (grid units x (segments - 1)) and the full pass (units x segments) of kDmaThreads threads, d_v tiles of kDmaDvt,
 // operands staged as given; and the scan between them (grid (d_k * kDmaDvt / 1024, units), 256 threads). The

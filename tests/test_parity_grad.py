@@ -72,33 +72,37 @@ def test_gradients_small(R, case):
     _check(got, ref, tol("bf16"))
 
 
-GRAD_DMA = [
-    # B, N, H, dk, dv, chunk, rotate, pos0, out dtype. d_k 256 and N a multiple of 32: every retention runs on the
-    # three-launch kernels, the reversed ones reading and writing rows in reverse order and the d_v blocks of dO
-    # and V read in place
-    (1, 640, 2, 256, 512, 128, True, 5, "bf16"),   # 5 segments, two d_v blocks
-    (2, 512, 2, 256, 256, 64, True, 0, "f32"),     # one block
-    (1, 1024, 1, 256, 512, 32, False, 0, "f32"),   # no rotation, chunk 32
-    (1, 32, 2, 256, 512, 128, True, 9, "f32"),     # one step
+GRAD_IN_PLACE = [
+    # B, N, H, dk, dv, chunk, rotate, pos0, out dtype, kernel. N a multiple of 32: every retention runs over the
+    # reversed sequence in place on the kernel named, with no reordered copies. d_k 256 with d_v a multiple of 256:
+    # the three-launch kernels, which also read the d_v blocks of dO and V in place; otherwise the wide-head
+    # kernels (one block)
+    (1, 640, 2, 256, 512, 128, True, 5, "bf16", "ret_chunk_dma"),   # 5 segments, two d_v blocks
+    (2, 512, 2, 256, 256, 64, True, 0, "f32", "ret_chunk_dma"),     # one block
+    (1, 1024, 1, 256, 512, 32, False, 0, "f32", "ret_chunk_dma"),   # no rotation, chunk 32
+    (1, 32, 2, 256, 512, 128, True, 9, "f32", "ret_chunk_dma"),     # one step
+    (1, 640, 2, 128, 128, 128, True, 5, "bf16", "ret_chunk_wide"),  # the long-sequence head
+    (1, 512, 2, 128, 256, 64, True, 0, "f32", "ret_chunk_wide"),    # d_k < d_v
+    (2, 384, 1, 256, 128, 32, False, 0, "f32", "ret_chunk_wide"),   # d_k > d_v, chunk 32
 ]
 
 
-@pytest.mark.parametrize("case", GRAD_DMA, ids=lambda c: "B%d-N%d-H%d-dk%d-dv%d-C%d" % c[:6] + "-" + c[8])
+@pytest.mark.parametrize("case", GRAD_IN_PLACE, ids=lambda c: "B%d-N%d-H%d-dk%d-dv%d-C%d" % c[:6] + "-" + c[8])
 def test_gradients_in_place(R, case):
     """Gradients with no reordered copies: the only reordering launch left is the one that sums the d_v blocks'
     dq' and dk' and turns them back by the transpose rotation."""
-    B, N, H, dk, dv, chunk, rot, pos0, out_dt = case
+    B, N, H, dk, dv, chunk, rot, pos0, out_dt, kernel = case
     w = W.Workload("grad", B=B, N=N, H=H, dk=dk, dv=dv, dtype="bf16", scale=float(np.sqrt(dk)), seed=61 + N,
                    chunk=chunk, rotate=rot)
-    print_case("gradients-in-place", w)
+    print_case("gradients-in-place", kernel, w)
     q, k, v, rng = W.make_qkv(w)
     do = W.make_dout(w, rng)
     ref = oracle.grad(q, k, v, do, w.gamma, theta=w.theta, pos0=pos0)
     timer = R.Timer()
     got = _gpu_grad(R, q, k, v, do, w.gamma, chunk, w.theta, pos0, out_dt, options={"timer": timer})
-    nb = dv // 256
+    nb = max(1, dv // 256) if kernel == "ret_chunk_dma" else 1
     assert timer.query("ret_permute_rotate")[1] == 1
-    assert timer.query("ret_chunk_dma")[1] == 2 * nb + 1
+    assert timer.query(kernel)[1] == 2 * nb + 1
     assert timer.query("ret_rotate_qk")[1] == (1 if rot else 0)
     timer.close()
     _check(got, ref, tol("bf16"))
@@ -181,8 +185,8 @@ def test_gradients_workload2_full(R):
 
 
 def test_gradients_long_sequence_full(R):
-    """The long-sequence workload (B=1, N=65536, H=8, d=128, chunk 128) at full size: the streaming kernels on
-    reordered copies, 64 segments per head."""
+    """The long-sequence workload (B=1, N=65536, H=8, d=128, chunk 128) at full size: the wide-head kernels over
+    the reversed sequence in place, many segments per head."""
     w = W.WORKLOADS[5]
     print_case("gradients-workload5", w)
     q, k, v, rng = W.make_qkv(w)
