@@ -586,12 +586,10 @@ bool bwd_layout(int B, int N, int H, int dk, int dv, int chunk, ret_dtype_t in_d
             L->kp = L->qp + up(nk * 2);
             off = L->kp + up(nk * 2);
         }
-        if (L->inplace)
-            for (int i = 0; i < L->nb; ++i) {
-                L->g1b[i] = off;
-                L->g3b[i] = L->g1b[i] + up(nk * 4);
-                off = L->g3b[i] + up(nk * 4);
-            }
+        if (L->inplace) {  // dq' of each block, then dk' of each block (one after another: one launch may write both)
+            for (int i = 0; i < L->nb; ++i, off += up(nk * 4)) L->g1b[i] = off;
+            for (int i = 0; i < L->nb; ++i, off += up(nk * 4)) L->g3b[i] = off;
+        }
         L->total = off;
         return true;
     }
@@ -908,13 +906,40 @@ ret_status_t ret_chunkwise_bwd_ex(const void* q, const void* k, const void* v, c
         if ((st = chunkwise_run(Kp, Qp, dout, dv_out, B, N, H, dk, dv, RET_BF16, out_dt, gamma, nullptr, 0, chunk,
                                 nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, ov, true)) != RET_OK)
             return st;
-        if (reshaped && (st = chain_meta_zero(in_dt, B, N, H, wb, dk, chunk, chain, L.chain_bytes, s, ov)) != RET_OK)
-            return st;
-        for (int i = 0; i < L.nb; ++i)
-            if ((st = chunkwise_run(v, dout, Qp, ws + L.g3b[i], B, N, H, wb, dk, RET_BF16, RET_F32, gamma, nullptr, 0,
-                                    chunk, nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, ov, true,
-                                    nullptr, din, i * wb)) != RET_OK)
+        // dk' runs over the same reversed segments as dv, and the state it carries is the transpose of dv's
+        // (sum of dO_t^T Q'_t against sum of Q'_t^T dO_t, block by block): on the three-launch kernels with square
+        // states it enters each segment with the transposed states the dv run left in the workspace, all blocks
+        // in one launch and no local passes or scan of its own.
+        ChunkKernels ck_dv, ck_dk;
+        ChunkPlan plan_dv;
+        if (L.variant != 3 && wb == kDmaDvt && dk == kDmaDvt &&
+            resolve_chunk(RET_BF16, B, N, H, dk, dv, chunk, false, L.chain_bytes, ov, &ck_dv, &plan_dv) &&
+            ck_dv.split_local && plan_dv.nseg > 1 && pick_chunk(RET_BF16, wb, dk, chunk, &ck_dk, ov) &&
+            ck_dk.split_full_rev && ck_dk.dvt == dk) {
+            FwdArgs A;
+            fill_fwd(A, v, dout, Qp, ws + L.g3b[0], B, N, H, wb, dk, RET_F32, gamma, nullptr, 0);
+            A.qr = const_cast<void*>(v);
+            A.kr = const_cast<void*>(dout);
+            A.nseg = plan_dv.nseg;
+            A.seg_len = plan_dv.seg_len;
+            A.qk_din = din;
+            A.qk_blocks = L.nb;
+            A.o_block = L.nb > 1 ? (long long)(L.g3b[1] - L.g3b[0]) / 4 : 0;
+            A.ws_t = (const float*)((char*)chain + kChainMeta);
+            const unsigned grid = (unsigned)((long long)B * H * L.nb * plan_dv.nseg);
+            LaunchTimer tm(ck_dk.pre_name, s, ov);
+            hipLaunchKernelGGL(ck_dk.split_full_rev, dim3(grid), dim3(kDmaThreads), 0, s, A);
+            tm.done();
+            if ((st = launch_status(ck_dk.pre_name)) != RET_OK) return st;
+        } else {
+            if (reshaped && (st = chain_meta_zero(in_dt, B, N, H, wb, dk, chunk, chain, L.chain_bytes, s, ov)) != RET_OK)
                 return st;
+            for (int i = 0; i < L.nb; ++i)
+                if ((st = chunkwise_run(v, dout, Qp, ws + L.g3b[i], B, N, H, wb, dk, RET_BF16, RET_F32, gamma, nullptr,
+                                        0, chunk, nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, ov,
+                                        true, nullptr, din, i * wb)) != RET_OK)
+                    return st;
+        }
         const bool two = L.nb > 1;
         const PermJob post[2] = {
             {ws + L.g1b[0], {dq, nullptr}, dk, -1, 0, {0, 0}, 0, ob, two ? ws + L.g1b[1] : nullptr},

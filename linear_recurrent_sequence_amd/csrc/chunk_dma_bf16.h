@@ -135,7 +135,7 @@ template <int DK, bool REV>
 struct DmaCtx {
     typedef DmaB<DK> F;
     int tid, lane, w, g4, n16;
-    int unit, seg, aN, aH, adk, adv, din, anseg, aseg_len, pair, dv0, seg_n, nchunks, rsk, rsv;
+    int unit, seg, aN, aH, adk, adv, din, anseg, aseg_len, pair, blk, dv0, seg_n, nchunks, rsk, rsv;
     float lg;
     long long seg_t0, hrow;  // hrow: token 0 of this (b, h), in head rows
     __device__ __forceinline__ DmaCtx(const FwdArgs& a) {
@@ -145,15 +145,17 @@ struct DmaCtx {
         g4 = 4 * (lane >> 4);
         n16 = lane & 15;
         const int ntiles = __builtin_amdgcn_readfirstlane(a.dv / F::DVT);
-        const int units = __builtin_amdgcn_readfirstlane(a.B * a.H * ntiles);
-        unit_seg_of_block(ntiles, units, &unit, &seg);
+        const int nblk = __builtin_amdgcn_readfirstlane(a.qk_blocks > 1 ? a.qk_blocks : 1);
+        const int units = __builtin_amdgcn_readfirstlane(a.B * a.H * ntiles * nblk);
+        unit_seg_of_block(ntiles * nblk, units, &unit, &seg);
         aN = __builtin_amdgcn_readfirstlane(a.N);
         aH = __builtin_amdgcn_readfirstlane(a.H);
         adk = __builtin_amdgcn_readfirstlane(a.dk);
         adv = __builtin_amdgcn_readfirstlane(a.dv);
         anseg = __builtin_amdgcn_readfirstlane(a.nseg);
         aseg_len = __builtin_amdgcn_readfirstlane(a.seg_len);
-        pair = unit / ntiles;
+        pair = unit / (ntiles * nblk);
+        blk = unit / ntiles % nblk;
         const int b = pair / aH, h = pair % aH;
         dv0 = (unit % ntiles) * F::DVT;
         lg = a.log2g[h];
@@ -167,9 +169,10 @@ struct DmaCtx {
     }
     // q' or k' (the pre-rotated copies), v and o of this unit's head at its token 0 (from there token t is row t)
     __device__ __forceinline__ const uint16_t* qk_head(const void* p, const FwdArgs& a) const {
-        return (const uint16_t*)p + hrow * din + __builtin_amdgcn_readfirstlane(a.qk_col0);
+        return (const uint16_t*)p + hrow * din + __builtin_amdgcn_readfirstlane(a.qk_col0) + blk * adk;
     }
     __device__ __forceinline__ long long v_head() const { return hrow * adv + dv0; }
+    __device__ __forceinline__ long long o_head(const FwdArgs& a) const { return blk * a.o_block + v_head(); }
     // The first row in memory of step c's C rows: token seg_t0 + c C of the run, or, over the reversed sequence,
     // row N - seg_t0 - (c + 1) C, whose C rows are then the step's tokens in reverse order.
     __device__ __forceinline__ long long crow(int c) const {
@@ -184,6 +187,29 @@ struct DmaCtx {
         return ((long long)pair * DK + x * 16 + g4 + e) * adv + dv0 + (w * 2 + j) * 16 + n16;
     }
 };
+
+// R[x * 2 + j][e] = W[(2w + j) 16 + n16][x 16 + g4 + e]: the transpose of a square DK x DK state W that another
+// run's slot holds in the thread order of the full pass (slot_store: element (r, c) is component r mod 4 of
+// register (r / 16) 2 + (c / 16) mod 2 of thread ((c / 16) / 2) 64 + ((r mod 16) / 4) 16 + c mod 16). For each
+// register the four values come from four consecutive threads' vectors, so the 4 loads of a register, issued back
+// to back, cover one 1 KB stretch of the slot.
+template <int DK>
+__device__ __forceinline__ void slot_load_t(const float* src, f32x4_t* R, int w, int g4, int n16) {
+    typedef DmaB<DK> F;
+    static_assert(DK == F::DVT, "a square state");
+    const rsrc_t r = bytes_rsrc(uniform_ptr(src), DK * F::DVT * 4);
+    const int lo = ((n16 >> 2) * 16 + g4) * 16 + (n16 & 3) * 4;  // bytes: this lane's thread and component
+#pragma unroll
+    for (int x = 0; x < F::NKB; ++x)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int xr = (2 * w + j) * 2 + (x & 1);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                R[x * 2 + j][e] = __builtin_bit_cast(
+                    float, __builtin_amdgcn_raw_buffer_load_b32(r, lo, (xr * F::NT + (x >> 1) * 64 + e) * 16, 0));
+        }
+}
 
 // V^T fragments of wave w's two 16-column blocks of a Swz<256> V tile, scaled by zeta'_r = gamma^-(T + r + 1) for
 // the 8 token rows r of the lane's values (4g + i and 16 + 4g + i; zero from row L on).
@@ -361,13 +387,16 @@ __global__ __launch_bounds__(512, 1) void chunk_dma_full_bf16(FwdArgs a) {
     const uint16_t* kh = x0.qk_head(a.kr, a);
     const uint16_t* vh = (const uint16_t*)a.v + x0.v_head();
     const int osz = a.out_bf16 ? 2 : 4;
-    char* oh = (char*)a.o + x0.v_head() * osz;
+    char* oh = (char*)a.o + x0.o_head(a) * osz;
     const int lq_p = ZQ::lane_p(lane), lq_t = ZQ::lane_trp(lane), lv_t = ZV::lane_trp(lane);
 
     // The state entering the segment: W_s (the scan of the local passes, state_in included), or state_in itself
-    // when the call has one segment.
+    // when the call has one segment; or the transpose of another run's W_s.
     f32x4_t R[NR];
-    if (x0.anseg > 1) {
+    if (DK == F::DVT && a.ws_t) {  // (square states only)
+        if constexpr (DK == F::DVT)
+            slot_load_t<DK>(a.ws_t + ((size_t)x0.unit * x0.anseg + seg) * (DK * F::DVT), R, w, g4, n16);
+    } else if (x0.anseg > 1) {
         slot_load<NR, NT>(x0.slot(a, seg), R, tid);
     } else {
 #pragma unroll

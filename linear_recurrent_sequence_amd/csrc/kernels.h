@@ -43,8 +43,13 @@ struct FwdArgs {
     // q and k as given (the gradients' dq' and dk' retentions).
     int orot;
     // Three-launch bf16 kernels only. qk_din (0: d_k): q and k are columns qk_col0 .. qk_col0 + d_k - 1 of heads
-    // qk_din wide, so that a run can take one block of wider heads in place.
-    int qk_din, qk_col0;
+    // qk_din wide, so that a run can take one block of wider heads in place. The full pass alone also takes:
+    // qk_blocks > 1: the units run over that many such blocks (block i at columns qk_col0 + i d_k, its outputs
+    // o_block elements after block i - 1's); ws_t: each segment enters with the transpose of the state in the
+    // slot of its unit and segment there (another run's states, d_k = d_v tile).
+    int qk_din, qk_col0, qk_blocks;
+    long long o_block;
+    const float* ws_t;
     float log2g[kMaxHeads];
     double theta[kMaxPairs];
 };

@@ -73,17 +73,18 @@ def test_gradients_small(R, case):
 
 
 GRAD_IN_PLACE = [
-    # B, N, H, dk, dv, chunk, rotate, pos0, out dtype, kernel. N a multiple of 32: every retention runs over the
-    # reversed sequence in place on the kernel named, with no reordered copies. d_k 256 with d_v a multiple of 256:
-    # the three-launch kernels, which also read the d_v blocks of dO and V in place; otherwise the wide-head
-    # kernels (one block)
-    (1, 640, 2, 256, 512, 128, True, 5, "bf16", "ret_chunk_dma"),   # 5 segments, two d_v blocks
-    (2, 512, 2, 256, 256, 64, True, 0, "f32", "ret_chunk_dma"),     # one block
-    (1, 1024, 1, 256, 512, 32, False, 0, "f32", "ret_chunk_dma"),   # no rotation, chunk 32
-    (1, 32, 2, 256, 512, 128, True, 9, "f32", "ret_chunk_dma"),     # one step
-    (1, 640, 2, 128, 128, 128, True, 5, "bf16", "ret_chunk_wide"),  # the long-sequence head
-    (1, 512, 2, 128, 256, 64, True, 0, "f32", "ret_chunk_wide"),    # d_k < d_v
-    (2, 384, 1, 256, 128, 32, False, 0, "f32", "ret_chunk_wide"),   # d_k > d_v, chunk 32
+    # B, N, H, dk, dv, chunk, rotate, pos0, out dtype, kernel, several segments. N a multiple of 32: every
+    # retention runs over the reversed sequence in place on the kernel named, with no reordered copies. d_k 256 with
+    # d_v a multiple of 256: the three-launch kernels, which also read the d_v blocks of dO and V in place, and with
+    # several segments dk' of every block in one launch from the transposed states of the dv retention; otherwise
+    # the wide-head kernels (one block)
+    (1, 640, 2, 256, 512, 128, True, 5, "bf16", "ret_chunk_dma", True),   # 5 segments, two d_v blocks
+    (2, 512, 2, 256, 256, 64, True, 0, "f32", "ret_chunk_dma", True),     # one block
+    (1, 1024, 1, 256, 512, 32, False, 0, "f32", "ret_chunk_dma", True),   # no rotation, chunk 32
+    (1, 32, 2, 256, 512, 128, True, 9, "f32", "ret_chunk_dma", False),    # one step
+    (1, 640, 2, 128, 128, 128, True, 5, "bf16", "ret_chunk_wide", True),  # the long-sequence head
+    (1, 512, 2, 128, 256, 64, True, 0, "f32", "ret_chunk_wide", True),    # d_k < d_v
+    (2, 384, 1, 256, 128, 32, False, 0, "f32", "ret_chunk_wide", True),   # d_k > d_v, chunk 32
 ]
 
 
@@ -91,7 +92,7 @@ GRAD_IN_PLACE = [
 def test_gradients_in_place(R, case):
     """Gradients with no reordered copies: the only reordering launch left is the one that sums the d_v blocks'
     dq' and dk' and turns them back by the transpose rotation."""
-    B, N, H, dk, dv, chunk, rot, pos0, out_dt, kernel = case
+    B, N, H, dk, dv, chunk, rot, pos0, out_dt, kernel, multi = case
     w = W.Workload("grad", B=B, N=N, H=H, dk=dk, dv=dv, dtype="bf16", scale=float(np.sqrt(dk)), seed=61 + N,
                    chunk=chunk, rotate=rot)
     print_case("gradients-in-place", kernel, w)
@@ -100,10 +101,15 @@ def test_gradients_in_place(R, case):
     ref = oracle.grad(q, k, v, do, w.gamma, theta=w.theta, pos0=pos0)
     timer = R.Timer()
     got = _gpu_grad(R, q, k, v, do, w.gamma, chunk, w.theta, pos0, out_dt, options={"timer": timer})
-    nb = max(1, dv // 256) if kernel == "ret_chunk_dma" else 1
     assert timer.query("ret_permute_rotate")[1] == 1
-    assert timer.query(kernel)[1] == 2 * nb + 1
     assert timer.query("ret_rotate_qk")[1] == (1 if rot else 0)
+    if kernel == "ret_chunk_dma":
+        nb = dv // 256
+        # dq' per block, dv, then dk' per block, or (several segments) all blocks' dk' in one launch
+        assert timer.query(kernel)[1] == (nb + 2 if multi else 2 * nb + 1)
+        assert timer.query("ret_chunk_dma_local")[1] == (nb + 1 if multi else 0)
+    else:
+        assert timer.query(kernel)[1] == 3
     timer.close()
     _check(got, ref, tol("bf16"))
 
