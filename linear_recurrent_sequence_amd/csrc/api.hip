@@ -895,42 +895,72 @@ ret_status_t ret_chunkwise_bwd_ex(const void* q, const void* k, const void* v, c
         }
         void* chain = ws + L.chain;
         const int wb = L.wb, din = L.nb > 1 ? dv : 0;
-        for (int i = 0; i < L.nb; ++i)
-            if ((st = chunkwise_run(dout, v, Kp, ws + L.g1b[i], B, N, H, wb, dk, RET_BF16, RET_F32, gamma, nullptr, 0,
-                                    chunk, nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, ov, false,
-                                    nullptr, din, i * wb)) != RET_OK)
-                return st;
+        // On the three-launch kernels with square states (d_k = d_v / blocks = 256) and several segments, dq' and
+        // dk' carry the transposes of (d_k, d_v)-shaped states, block by block: dq' that of sum K'_t^T V_t (the
+        // forward's), dk' that of sum Q'_t^T dO_t over the reversed sequence (the dv retention's). So one local
+        // pass and scan over (K', V) give dq' its segment states, the dv retention's give dk' theirs, and dq' and
+        // dk' each run as one full-pass launch over all blocks that enters each segment with the transposed state
+        // (no local passes or scans of their own).
+        ChunkKernels ck_sq, ck_bl;
+        ChunkPlan plan_sq;
+        const bool share = L.variant != 3 && wb == kDmaDvt && dk == kDmaDvt &&
+                           resolve_chunk(RET_BF16, B, N, H, dk, dv, chunk, false, L.chain_bytes, ov, &ck_sq, &plan_sq) &&
+                           ck_sq.split_local && plan_sq.nseg > 1 && pick_chunk(RET_BF16, wb, dk, chunk, &ck_bl, ov) &&
+                           ck_bl.split_full_rev && ck_bl.dvt == dk;
+        float* const slots = (float*)((char*)chain + kChainMeta);  // segment states of the (d_k, d_v) runs
+        // every block's dq' (rev = false) or dk' (rev = true) in one full-pass launch from the transposed states
+        auto blocks_from_t = [&](const void* qq, const void* kk, const void* vv, void* out, bool rev) {
+            FwdArgs A;
+            fill_fwd(A, qq, kk, vv, out, B, N, H, wb, dk, RET_F32, gamma, nullptr, 0);
+            A.qr = const_cast<void*>(qq);
+            A.kr = const_cast<void*>(kk);
+            A.nseg = plan_sq.nseg;
+            A.seg_len = plan_sq.seg_len;
+            A.qk_din = din;
+            A.qk_blocks = L.nb;
+            A.o_block = L.nb > 1 ? (long long)(rev ? L.g3b[1] - L.g3b[0] : L.g1b[1] - L.g1b[0]) / 4 : 0;
+            A.ws_t = slots;
+            const unsigned grid = (unsigned)((long long)B * H * L.nb * plan_sq.nseg);
+            LaunchTimer tm(ck_bl.pre_name, s, ov);
+            hipLaunchKernelGGL(rev ? ck_bl.split_full_rev : ck_bl.fused_pre, dim3(grid), dim3(kDmaThreads), 0, s, A);
+            tm.done();
+            return launch_status(ck_bl.pre_name);
+        };
+        if (share) {
+            // the forward's segment states: local passes and scan over (K', V) alone
+            FwdArgs A;
+            fill_fwd(A, nullptr, Kp, v, nullptr, B, N, H, dk, dv, RET_F32, gamma, nullptr, 0);
+            A.kr = const_cast<void*>(Kp);
+            A.ws = slots;
+            A.nseg = plan_sq.nseg;
+            A.seg_len = plan_sq.seg_len;
+            const unsigned units = (unsigned)((long long)B * H * (dv / ck_sq.dvt));
+            LaunchTimer tl("ret_chunk_dma_local", s, ov);
+            hipLaunchKernelGGL(ck_sq.split_local, dim3(units * (unsigned)(plan_sq.nseg - 1)), dim3(kDmaThreads), 0, s,
+                               A);
+            tl.done();
+            if ((st = launch_status("ret_chunk_dma_local")) != RET_OK) return st;
+            LaunchTimer tc("ret_chunk_dma_scan", s, ov);
+            hipLaunchKernelGGL(ck_sq.split_scan, dim3((unsigned)((long long)dk * ck_sq.dvt / 1024), units), dim3(256), 0,
+                               s, A);
+            tc.done();
+            if ((st = launch_status("ret_chunk_dma_scan")) != RET_OK) return st;
+            if ((st = blocks_from_t(dout, v, Kp, ws + L.g1b[0], false)) != RET_OK) return st;
+        } else {
+            for (int i = 0; i < L.nb; ++i)
+                if ((st = chunkwise_run(dout, v, Kp, ws + L.g1b[i], B, N, H, wb, dk, RET_BF16, RET_F32, gamma, nullptr,
+                                        0, chunk, nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, ov,
+                                        false, nullptr, din, i * wb)) != RET_OK)
+                    return st;
+        }
         const bool reshaped = wb != dk || dk != dv;  // the (d_k, d_v) of the runs differ
         if (reshaped && (st = chain_meta_zero(in_dt, B, N, H, dk, dv, chunk, chain, L.chain_bytes, s, ov)) != RET_OK)
             return st;
         if ((st = chunkwise_run(Kp, Qp, dout, dv_out, B, N, H, dk, dv, RET_BF16, out_dt, gamma, nullptr, 0, chunk,
                                 nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, ov, true)) != RET_OK)
             return st;
-        // dk' runs over the same reversed segments as dv, and the state it carries is the transpose of dv's
-        // (sum of dO_t^T Q'_t against sum of Q'_t^T dO_t, block by block): on the three-launch kernels with square
-        // states it enters each segment with the transposed states the dv run left in the workspace, all blocks
-        // in one launch and no local passes or scan of its own.
-        ChunkKernels ck_dv, ck_dk;
-        ChunkPlan plan_dv;
-        if (L.variant != 3 && wb == kDmaDvt && dk == kDmaDvt &&
-            resolve_chunk(RET_BF16, B, N, H, dk, dv, chunk, false, L.chain_bytes, ov, &ck_dv, &plan_dv) &&
-            ck_dv.split_local && plan_dv.nseg > 1 && pick_chunk(RET_BF16, wb, dk, chunk, &ck_dk, ov) &&
-            ck_dk.split_full_rev && ck_dk.dvt == dk) {
-            FwdArgs A;
-            fill_fwd(A, v, dout, Qp, ws + L.g3b[0], B, N, H, wb, dk, RET_F32, gamma, nullptr, 0);
-            A.qr = const_cast<void*>(v);
-            A.kr = const_cast<void*>(dout);
-            A.nseg = plan_dv.nseg;
-            A.seg_len = plan_dv.seg_len;
-            A.qk_din = din;
-            A.qk_blocks = L.nb;
-            A.o_block = L.nb > 1 ? (long long)(L.g3b[1] - L.g3b[0]) / 4 : 0;
-            A.ws_t = (const float*)((char*)chain + kChainMeta);
-            const unsigned grid = (unsigned)((long long)B * H * L.nb * plan_dv.nseg);
-            LaunchTimer tm(ck_dk.pre_name, s, ov);
-            hipLaunchKernelGGL(ck_dk.split_full_rev, dim3(grid), dim3(kDmaThreads), 0, s, A);
-            tm.done();
-            if ((st = launch_status(ck_dk.pre_name)) != RET_OK) return st;
+        if (share) {
+            if ((st = blocks_from_t(v, dout, Qp, ws + L.g3b[0], true)) != RET_OK) return st;
         } else {
             if (reshaped && (st = chain_meta_zero(in_dt, B, N, H, wb, dk, chunk, chain, L.chain_bytes, s, ov)) != RET_OK)
                 return st;

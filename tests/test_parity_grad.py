@@ -76,8 +76,8 @@ GRAD_IN_PLACE = [
     # B, N, H, dk, dv, chunk, rotate, pos0, out dtype, kernel, several segments. N a multiple of 32: every
     # retention runs over the reversed sequence in place on the kernel named, with no reordered copies. d_k 256 with
     # d_v a multiple of 256: the three-launch kernels, which also read the d_v blocks of dO and V in place, and with
-    # several segments dk' of every block in one launch from the transposed states of the dv retention; otherwise
-    # the wide-head kernels (one block)
+    # several segments dq' and dk' of every block each in one launch from transposed states (of a local pass and
+    # scan over K' and V, and of the dv retention); otherwise the wide-head kernels (one block)
     (1, 640, 2, 256, 512, 128, True, 5, "bf16", "ret_chunk_dma", True),   # 5 segments, two d_v blocks
     (2, 512, 2, 256, 256, 64, True, 0, "f32", "ret_chunk_dma", True),     # one block
     (1, 1024, 1, 256, 512, 32, False, 0, "f32", "ret_chunk_dma", True),   # no rotation, chunk 32
@@ -105,9 +105,11 @@ def test_gradients_in_place(R, case):
     assert timer.query("ret_rotate_qk")[1] == (1 if rot else 0)
     if kernel == "ret_chunk_dma":
         nb = dv // 256
-        # dq' per block, dv, then dk' per block, or (several segments) all blocks' dk' in one launch
-        assert timer.query(kernel)[1] == (nb + 2 if multi else 2 * nb + 1)
-        assert timer.query("ret_chunk_dma_local")[1] == (nb + 1 if multi else 0)
+        # dq' per block, dv, then dk' per block; or (several segments) the states of (K', V), dq' of all blocks,
+        # dv, dk' of all blocks
+        assert timer.query(kernel)[1] == (3 if multi else 2 * nb + 1)
+        assert timer.query("ret_chunk_dma_local")[1] == (2 if multi else 0)
+        assert timer.query("ret_chunk_dma_scan")[1] == (2 if multi else 0)
     else:
         assert timer.query(kernel)[1] == 3
     timer.close()
