@@ -117,11 +117,13 @@ def test_gradients_in_place(R, case):
 
 
 @pytest.mark.parametrize("direct", ["1", "0"])
-def test_gradients_in_place_or_copied(R, direct):
-    """d_k 256, d_v 512 in place (bwd_direct 1) and through reordered copies (0)."""
-    w = W.Workload("grad", B=1, N=768, H=2, dk=256, dv=512, dtype="bf16", scale=16.0, seed=47, chunk=128,
-                   rotate=True)
-    print_case("gradients-path-dk256", direct, w)
+@pytest.mark.parametrize("dk,dv", [(256, 512), (128, 128)])
+def test_gradients_in_place_or_copied(R, direct, dk, dv):
+    """d_k 256, d_v 512 (the three-launch kernels) and d_k = d_v = 128 (the wide-head kernels) in place
+    (bwd_direct 1) and through reordered copies (0)."""
+    w = W.Workload("grad", B=1, N=768, H=2, dk=dk, dv=dv, dtype="bf16", scale=float(np.sqrt(dk)), seed=47,
+                   chunk=128, rotate=True)
+    print_case("gradients-path", direct, w)
     q, k, v, rng = W.make_qkv(w)
     do = W.make_dout(w, rng)
     ref = oracle.grad(q, k, v, do, w.gamma, theta=w.theta, pos0=1)
