@@ -243,7 +243,9 @@ void ret_timer_reset(ret_timer_t* t);
  *                d_k = 256: 5 = the LDS-loading wide-head kernels (d_v a multiple of 256, the default there:
  *                local passes, a scan, the full pass; gives way to 4 when q and k need rotating and the workspace
  *                has no room for rotated copies), 1 = 256 threads whose waves own 32 columns, 2 = 256 threads
- *                with d_v tiles of 64, 4 = 512 threads x 16 columns
+ *                with d_v tiles of 64, 4 = 512 threads x 16 columns; d_k = 128: 4 = 512 threads x 16 columns
+ *                (d_v tiles of 128, the default where d_v is a multiple of 128), 1 = 256 threads whose waves
+ *                own 32 columns, 2 = 256 threads with d_v tiles of 64
  *   step_cw, step_wr, step_pairs   decode tile: columns per workgroup (16, 32, 64), rows per wave (16, 32, 64),
  *                pairs (0 planner, 1 one (b, h) per workgroup, 2 grouped); 0 = default
  *   bwd_direct   -1 or 1: gradients by the reversed traversal, with d_v blocks of dO and V read in place, where

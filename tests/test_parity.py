@@ -139,6 +139,26 @@ def test_chunkwise_dk256_workgroup_sizes(R, threads):
     assert eo <= tol("bf16") and es <= tol("bf16"), (eo, es)
 
 
+@pytest.mark.parametrize("variant", ["0", "1", "2", "4"])
+def test_chunkwise_dk128_tiles(R, variant):
+    """d_k 128: d_v tiles of 128 (512 threads x 16 columns: the default; 256 threads x 32 columns) and of 64, with
+    rotation while staging, state in and out and three segments, all matching the oracle."""
+    opts = {"variant": int(variant), "segments": 3}
+    B, N, H, dk, dv, C = 2, 333, 2, 128, 256, 128
+    print_case("dk128 variant=%s" % variant, (B, N, H, dk, dv, C))
+    rng = np.random.default_rng(73)
+    q = W.normal(rng, (B, N, H, dk), 11.0, "bf16")
+    k = W.normal(rng, (B, N, H, dk), 11.0, "bf16")
+    v = W.normal(rng, (B, N, H, dv), 11.0, "bf16")
+    s0 = rng.standard_normal((B, H, dk, dv)).astype(np.float32)
+    gamma, theta = W.gamma_schedule(H), W.theta_schedule(dk)
+    o_ref, s_ref = oracle.chunkwise(q, k, v, gamma, C, theta=theta, pos0=4, state_in=s0)
+    o, s = _gpu_chunkwise(R, q, k, v, "bf16", gamma, C, theta=theta, pos0=4, s_in=s0, options=opts)
+    eo, es = rel_err(o, o_ref), rel_err(s, s_ref)
+    print("  err o=%.3g state=%.3g" % (eo, es))
+    assert eo <= tol("bf16") and es <= tol("bf16"), (eo, es)
+
+
 WIDE = [  # (d_k, B, N, H, d_v, chunk, rotation, state_in, segments)
     (256, 1, 333, 2, 256, 64, True, True, 3),
     (256, 2, 37, 1, 128, 64, True, False, None),
