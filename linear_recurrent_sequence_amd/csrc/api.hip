@@ -563,7 +563,8 @@ bool bwd_layout(int B, int N, int H, int dk, int dv, int chunk, ret_dtype_t in_d
                  !plan_onchip(ca, pa, op) && cb.split_local && !plan_onchip(cb, pb, op) && op.bwd_direct != 0;
     L->chain = 0;
     L->chain_bytes = pa.chain_bytes > pb.chain_bytes ? pa.chain_bytes : pb.chain_bytes;
-    if (!L->direct && !L->inplace && in_dt == RET_BF16 && L->nb == 1 && op.bwd_direct != 0 && op.variant == 0) {
+    if (!L->direct && !L->inplace && in_dt == RET_BF16 && L->nb == 1 && op.bwd_direct != 0 &&
+        (op.variant == 0 || op.variant == 3)) {
         // the wide-head kernels run over the reversed sequence in place
         Opts o3 = op;
         o3.variant = 3;
