@@ -526,8 +526,9 @@ ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o,
 // call after another; at least 256 bytes, so ret_chunkwise_check reads its header). Then:
 // - when both reversed retentions run on the on-chip kernel's reversed traversal (direct, bf16 only): Q' and K'
 //   (bf16, only with rotation);
-// - when every retention runs on the three-launch kernels, which take reversed rows and d_v blocks in place (dma,
-//   bf16, N a multiple of their step): Q' and K' (only with rotation) and the fp32 dq' and dk' of each d_v block;
+// - when every retention runs in place over reversed rows and d_v blocks (inplace: the three-launch kernels, or
+//   with one block the wide-head kernels; bf16, N a multiple of their 32-token step): Q' and K' (only with
+//   rotation), then the fp32 dq' of each d_v block and the fp32 dk' of each block, each set contiguous;
 // - otherwise the reordered inputs (K', K' reversed, Q' reversed, and V and dO reversed, or their blocks forward
 //   and reversed) in the input dtype, and the fp32 outputs.
 struct BwdLayout {

@@ -16,9 +16,9 @@
 // stages the q' and k' rows and computes the causal scores once for 256 columns. The local pass stages k' and v
 // through registers (loads straight into the LDS issue too slowly when a step holds only the state update).
 // Chunks of 64 or more tokens run as 32-token sub-chunks (the chunkwise form gives the same result for any chunk
-// size, up to rounding). The gradients run two of their retentions over the reversed sequence and take d_v blocks
-// of wider heads as q and k: the kernels read and write those rows and columns in place (REV instances, and
-// FwdArgs::qk_din).
+// size, up to rounding). For the gradients the kernels also run over the reversed sequence (REV instances), take
+// q and k as a block of columns of wider heads (FwdArgs::qk_din, qk_col0), and the full pass runs several such
+// blocks in one grid (qk_blocks) and can enter each segment with the transpose of another run's state (ws_t).
 #pragma once
 
 #include "chunk_bf16.h"
@@ -167,7 +167,8 @@ struct DmaCtx {
         rsv = aH * adv;
         hrow = (long long)b * aN * aH + h;
     }
-    // q' or k' (the pre-rotated copies), v and o of this unit's head at its token 0 (from there token t is row t)
+    // q' or k' (the pre-rotated copies: this unit's block of columns), v and o of this unit's head at its token 0
+    // (from there token t is row t)
     __device__ __forceinline__ const uint16_t* qk_head(const void* p, const FwdArgs& a) const {
         return (const uint16_t*)p + hrow * din + __builtin_amdgcn_readfirstlane(a.qk_col0) + blk * adk;
     }
