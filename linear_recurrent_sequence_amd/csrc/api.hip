@@ -533,7 +533,7 @@ ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o,
 //   and reversed) in the input dtype, and the fp32 outputs.
 struct BwdLayout {
     bool direct, inplace;
-    int variant;  // kernel variant of the retentions (the wide-head kernels' for the in-place path on them)
+    int variant;  // kernel variant of the retentions (the wide-head kernels' where the in-place path takes them)
     int nb, wb;  // d_v blocks of width wb for the retentions that contract over d_v (nb = 2 when d_v is wider
                  // than their kernels' d_k; dq' and dk' are then sums of two retentions)
     size_t qp, kp, kr, qr, vr, dor, g1, g2, g3, chain, chain_bytes, total;
@@ -564,22 +564,23 @@ bool bwd_layout(int B, int N, int H, int dk, int dv, int chunk, ret_dtype_t in_d
                  !plan_onchip(ca, pa, op) && cb.split_local && !plan_onchip(cb, pb, op) && op.bwd_direct != 0;
     L->chain = 0;
     L->chain_bytes = pa.chain_bytes > pb.chain_bytes ? pa.chain_bytes : pb.chain_bytes;
-    if (!L->direct && !L->inplace && in_dt == RET_BF16 && L->nb == 1 && op.bwd_direct != 0 &&
-        (op.variant == 0 || op.variant == 3)) {
-        // the wide-head kernels run over the reversed sequence in place
-        Opts o3 = op;
-        o3.variant = 3;
+    // Otherwise, with one block of d_v, the single-pass kernels that have reversed instances: the shape's own set,
+    // else (default variant) the wide-head kernels'.
+    const int tries[2] = {op.variant, op.variant == 0 ? 3 : -1};
+    for (int t = 0; t < 2 && !L->direct && !L->inplace && in_dt == RET_BF16 && L->nb == 1 && op.bwd_direct != 0; ++t) {
+        if (tries[t] < 0) break;
+        Opts ot = op;
+        ot.variant = tries[t];
         ChunkKernels wa, wb;
-        if (pick_chunk(in_dt, L->wb, dk, chunk, &wa, o3) && wa.fused_rev && N % wa.rev_step == 0 &&
-            pick_chunk(in_dt, dk, dv, chunk, &wb, o3) && wb.fused_rev && N % wb.rev_step == 0) {
-            const ChunkPlan qa = plan_chunk(wa, B, N, H, L->wb, dk, chunk, false, SIZE_MAX, o3);
-            const ChunkPlan qb = plan_chunk(wb, B, N, H, dk, dv, chunk, false, SIZE_MAX, o3);
-            if (!plan_onchip(wa, qa, o3) && !plan_onchip(wb, qb, o3)) {
-                L->inplace = true;
-                L->variant = 3;
-                L->chain_bytes = qa.chain_bytes > qb.chain_bytes ? qa.chain_bytes : qb.chain_bytes;
-            }
-        }
+        if (!pick_chunk(in_dt, L->wb, dk, chunk, &wa, ot) || !wa.fused_rev || N % wa.rev_step ||
+            !pick_chunk(in_dt, dk, dv, chunk, &wb, ot) || !wb.fused_rev || N % wb.rev_step)
+            continue;
+        const ChunkPlan qa = plan_chunk(wa, B, N, H, L->wb, dk, chunk, false, SIZE_MAX, ot);
+        const ChunkPlan qb = plan_chunk(wb, B, N, H, dk, dv, chunk, false, SIZE_MAX, ot);
+        if (plan_onchip(wa, qa, ot) || plan_onchip(wb, qb, ot)) continue;
+        L->inplace = true;
+        L->variant = tries[t];
+        L->chain_bytes = qa.chain_bytes > qb.chain_bytes ? qa.chain_bytes : qb.chain_bytes;
     }
     size_t off = up(L->chain_bytes > 256 ? L->chain_bytes : 256);
     if (L->direct || L->inplace) {
@@ -878,8 +879,8 @@ ret_status_t ret_chunkwise_bwd_ex(const void* q, const void* k, const void* v, c
         //   dv  = retention(K', Q', dO) over the reversed sequence, rows read and written in reverse order
         //   dk' = sum over b of retention(V_b, dO_b, Q') over the reversed sequence
         // dv is written as the output; dq and dk are the block sums turned back by the transpose rotation. The
-        // retentions run on the three-launch kernels, or (one block) on the wide-head kernels (variant 3), whose
-        // segment chain is cleared between calls of different shapes.
+        // retentions run on the three-launch kernels, or (one block) on single-pass kernels with reversed
+        // instances, whose segment chain is cleared between calls of different shapes.
         Opts ov = op;
         ov.variant = L.variant;
         const void *Qp = q, *Kp = k;

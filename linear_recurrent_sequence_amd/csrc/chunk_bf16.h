@@ -471,8 +471,11 @@ struct FullB {
     static_assert(KS % 32 == 0, "tiling");
 };
 
-template <int DK, int C, int DVT, bool PRE, int NT, int NDW>
+// REV (with PRE only): the run goes over the reversed sequence in place (token n of the run is row N-1-n of q, k, v
+// and o; whole chunks only, N a multiple of C): the gradients' retentions over later tokens.
+template <int DK, int C, int DVT, bool PRE, int NT, int NDW, bool REV = false>
 __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT, NDW>::OCC)) void chunk_fused_bf16(FwdArgs a) {
+    static_assert(!REV || PRE, "reversed runs take q and k as given");
     typedef FullB<DK, C, DVT, PRE, NT, NDW> F;
     constexpr int NR = F::NKB * NDW;  // state tiles of a wave: R[x * NDW + j] = rows 16x.., d_v block w * NDW + j
     typedef typename F::TQ TQ;
@@ -512,13 +515,20 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT, NDW>::OCC)) void ch
     const int seg_n = (int)(min((long long)aN, seg_t0 + aseg_len) - seg_t0);  // tokens in this segment
     const int nchunks = (seg_n + C - 1) / C;
     const int rsk = aH * adk, rsv = aH * adv;  // elements between consecutive tokens
-    const long long head0 = ((long long)b * aN + seg_t0) * aH + h;
+    // token 0 of this (b, h), in head rows; the first row in memory of chunk c: token seg_t0 + c C of the run, or,
+    // over the reversed sequence, row N - seg_t0 - (c + 1) C, whose C rows are the chunk's tokens in reverse order
+    const long long hrow = (long long)b * aN * aH + h;
+    auto crow = [&](int c) __attribute__((always_inline)) {
+        return REV ? (long long)aN - seg_t0 - (long long)(c + 1) * C : seg_t0 + (long long)c * C;
+    };
+    // the chunk's row (and LDS row) of memory row r of its rows
+    auto lrow = [&](int r) __attribute__((always_inline)) { return REV ? C - 1 - r : r; };
     // q and k, or their rotated copies (PRE: staging copies rows instead of rotating them)
-    const uint16_t* qh = (const uint16_t*)(PRE ? a.qr : a.q) + head0 * adk;
-    const uint16_t* kh = (const uint16_t*)(PRE ? a.kr : a.k) + head0 * adk;
-    const uint16_t* vh = (const uint16_t*)a.v + head0 * adv + dv0;
+    const uint16_t* qh = (const uint16_t*)(PRE ? a.qr : a.q) + hrow * adk;
+    const uint16_t* kh = (const uint16_t*)(PRE ? a.kr : a.k) + hrow * adk;
+    const uint16_t* vh = (const uint16_t*)a.v + hrow * adv + dv0;
     const int osz = a.out_bf16 ? 2 : 4;
-    char* oh = (char*)a.o + (head0 * adv + dv0) * osz;
+    char* oh = (char*)a.o + (hrow * adv + dv0) * osz;
     const int vrow = tid / TV::SPR, vseg = tid % TV::SPR;
     const int voff = (vrow * rsv + vseg * 8) * 2;
     typedef Swz<F::KS> ZQ;
@@ -557,7 +567,7 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT, NDW>::OCC)) void ch
         u32x4_t lk[2][TK::NP], lv[2][TV::NP];
         auto lissue = [&](int c, auto parc) __attribute__((always_inline)) {
             constexpr int par = decltype(parc)::value;
-            const long long tc = (long long)c * C;
+            const long long tc = crow(c);
             const rsrc_t rk = bytes_rsrc(kh + tc * rsk, ((C - 1) * rsk + DK) * 2);
             const rsrc_t rv = bytes_rsrc(vh + tc * rsv, ((C - 1) * rsv + DVT) * 2);
 #pragma unroll
@@ -569,9 +579,9 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT, NDW>::OCC)) void ch
         if (nchunks > 1) lissue(1, std::integral_constant<int, 1>{});
         float zl[TK::NP], zlv[TV::NP];
 #pragma unroll
-        for (int p = 0; p < TK::NP; ++p) zl[p] = gpow(lg, (float)(C - 1 - (krow + p * TK::RP)));
+        for (int p = 0; p < TK::NP; ++p) zl[p] = gpow(lg, (float)(C - 1 - lrow(krow + p * TK::RP)));
 #pragma unroll
-        for (int p = 0; p < TV::NP; ++p) zlv[p] = gpow(lg, (float)(C - 1 - (vrow + p * TV::RP)));
+        for (int p = 0; p < TV::NP; ++p) zlv[p] = gpow(lg, (float)(C - 1 - lrow(vrow + p * TV::RP)));
         const float gC = gpow(lg, (float)C);
         SliceRot<C, TK::RP, TK::NP> lrot;  // identity factors without rotation (theta all zero)
         if constexpr (!PRE) lrot.init_steps(a.theta, kseg * 4);
@@ -582,7 +592,7 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT, NDW>::OCC)) void ch
             if constexpr (PRE) {  // K' as staged; zeta on V
 #pragma unroll
                 for (int p = 0; p < TK::NP; ++p)
-                    if (TK::live(krow, p)) lds_store16(lK + ZK::off(krow + p * TK::RP, kseg * 8), lk[par][p]);
+                    if (TK::live(krow, p)) lds_store16(lK + ZK::off(lrow(krow + p * TK::RP), kseg * 8), lk[par][p]);
 #pragma unroll
                 for (int p = 0; p < TV::NP; ++p)
                     if (TV::live(vrow, p)) {
@@ -590,7 +600,7 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT, NDW>::OCC)) void ch
                         unpack8(lv[par][p], vf);
 #pragma unroll
                         for (int e = 0; e < 8; ++e) vf[e] *= zlv[p];
-                        lds_store16(lV + ZV::off(vrow + p * TV::RP, vseg * 8), pack8(vf));
+                        lds_store16(lV + ZV::off(lrow(vrow + p * TV::RP), vseg * 8), pack8(vf));
                     }
             } else {
                 if ((c & 7) == 0) lrot.cur.eval(a.pos0 + seg_t0 + (long long)c * C + krow, a.theta, kseg * 4);
@@ -656,7 +666,7 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT, NDW>::OCC)) void ch
         constexpr int par = decltype(parc)::value;
         const int c = i / F::NSL, sl = i % F::NSL;
         const int L = min(C, seg_n - c * C);
-        const long long tc = (long long)c * C;
+        const long long tc = crow(c);
         const rsrc_t rq = bytes_rsrc(qh + tc * rsk + sl * F::KS, ((L - 1) * rsk + F::KS) * 2);
         const rsrc_t rk = bytes_rsrc(kh + tc * rsk + sl * F::KS, ((L - 1) * rsk + F::KS) * 2);
 #pragma unroll
@@ -711,10 +721,10 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT, NDW>::OCC)) void ch
         }
     }
 #pragma unroll
-    for (int p = 0; p < TQ::NP; ++p) zfull[p] = gpow(lg, (float)(C - 1 - (qrow + p * TQ::RP)));
+    for (int p = 0; p < TQ::NP; ++p) zfull[p] = gpow(lg, (float)(C - 1 - lrow(qrow + p * TQ::RP)));
     float zvfull[TV::NP];  // zeta of the staged V rows of a full chunk (pre-rotated operands)
 #pragma unroll
-    for (int p = 0; p < TV::NP; ++p) zvfull[p] = gpow(lg, (float)(C - 1 - (vrow + p * TV::RP)));
+    for (int p = 0; p < TV::NP; ++p) zvfull[p] = gpow(lg, (float)(C - 1 - lrow(vrow + p * TV::RP)));
     const float gC = gpow(lg, (float)C);
     // Without rotation theta is all zero and every factor is exactly (1, 0).
     SliceRot<C, TQ::RP, TQ::NP> rot[F::NSL];
@@ -735,14 +745,14 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT, NDW>::OCC)) void ch
 #pragma unroll
             for (int p = 0; p < TQ::NP; ++p)
                 if (TQ::live(qrow, p)) {
-                    lds_store16(sQ + ZQ::off(qrow + p * TQ::RP, qseg * 8), bq[par][p]);
-                    lds_store16(sK + ZQ::off(qrow + p * TQ::RP, qseg * 8), bk[par][p]);
+                    lds_store16(sQ + ZQ::off(lrow(qrow + p * TQ::RP), qseg * 8), bq[par][p]);
+                    lds_store16(sK + ZQ::off(lrow(qrow + p * TQ::RP), qseg * 8), bk[par][p]);
                 }
             if constexpr (sl == 0) {
                 uint16_t* sVz = sV + F::SV;
 #pragma unroll
                 for (int p = 0; p < TV::NP; ++p) {
-                    const int r = vrow + p * TV::RP;
+                    const int r = lrow(vrow + p * TV::RP);
                     if (TV::live(vrow, p)) {
                         lds_store16(sV + ZV::off(r, vseg * 8), bv[par][p]);
                         const float z = L == C ? zvfull[p] : (r < L ? gpow(lg, (float)(L - 1 - r)) : 0.f);
@@ -786,12 +796,12 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT, NDW>::OCC)) void ch
     };
 
     // Output stores straight from the O^T accumulators: lane (g, n16) of tile (x, j) holds 4 consecutive d_v of
-    // query x*16 + n16 in d_v block w * NDW + j. Rows past the sequence fall outside the buffer range and are
-    // dropped.
-    const int o_voff = (n16 * rsv + w * NDW * 16 + g4) * osz;
+    // query x*16 + n16 in d_v block w * NDW + j (REV: memory row (NB-1-x)*16 + 15 - n16 of the chunk's rows). Rows
+    // past the sequence fall outside the buffer range and are dropped.
+    const int o_voff = ((REV ? 15 - n16 : n16) * rsv + w * NDW * 16 + g4) * osz;
     auto store_out = [&](int c, const f32x4_t* O) __attribute__((always_inline)) {
         const int L = min(C, seg_n - c * C);
-        const rsrc_t ro = bytes_rsrc(oh + (long long)c * C * rsv * osz, ((L - 1) * rsv + DVT) * osz);
+        const rsrc_t ro = bytes_rsrc(oh + crow(c) * rsv * osz, ((L - 1) * rsv + DVT) * osz);
         if (a.out_bf16) {
 #pragma unroll
             for (int x = 0; x < F::NB; ++x)
@@ -801,14 +811,15 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT, NDW>::OCC)) void ch
                         __builtin_bit_cast(uint32_t __attribute__((ext_vector_type(2))),
                                            make_uint2(pack2_bf16(O[x * NDW + j][0], O[x * NDW + j][1]),
                                                       pack2_bf16(O[x * NDW + j][2], O[x * NDW + j][3]))),
-                        ro, o_voff, (x * 16 * rsv + j * 16) * 2, kOutAux);
+                        ro, o_voff, ((REV ? F::NB - 1 - x : x) * 16 * rsv + j * 16) * 2, kOutAux);
         } else {
 #pragma unroll
             for (int x = 0; x < F::NB; ++x)
 #pragma unroll
                 for (int j = 0; j < NDW; ++j)
                     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, O[x * NDW + j]), ro, o_voff,
-                                                           (x * 16 * rsv + j * 16) * 4, kOutAux);
+                                                           ((REV ? F::NB - 1 - x : x) * 16 * rsv + j * 16) * 4,
+                                                           kOutAux);
         }
     };
 
@@ -981,12 +992,17 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT, NDW>::OCC)) void ch
 // products are d_k-deep, so a wider tile shares the scores and the q/k staging among twice the columns. The
 // wider tile is either 8 waves of 16 columns (two waves per SIMD hide each other's latencies) or 4 waves of
 // NDW = 2 blocks of 16 columns (each Q', K' or P fragment read from LDS feeds two MFMAs).
-template <int DK, int C, int NT = (DK >= 256 ? 512 : 256), int NDW = 1>
+// WITH_REV: the set also has the PRE kernel over the reversed sequence (fused_rev).
+template <int DK, int C, int NT = (DK >= 256 ? 512 : 256), int NDW = 1, bool WITH_REV = false>
 ChunkKernels chunk_entry_bf16() {
     constexpr int CI = C > 64 ? 64 : C, DVT = 16 * (NT / 64) * NDW;
     ChunkKernels k{};
     k.fused = chunk_fused_bf16<DK, CI, DVT, false, NT, NDW>;
     k.fused_pre = chunk_fused_bf16<DK, CI, DVT, true, NT, NDW>;
+    if constexpr (WITH_REV) {
+        k.fused_rev = chunk_fused_bf16<DK, CI, DVT, true, NT, NDW, true>;
+        k.rev_step = CI;
+    }
     k.dvt = DVT;
     k.threads = NT;
     // d_v tiles of 128 run one workgroup per CU: one workgroup per CU in total measured fastest (fewer, longer

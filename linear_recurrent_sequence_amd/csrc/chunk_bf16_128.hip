@@ -35,7 +35,7 @@ bool chunk_kernels_bf16_128(int dk, int dv, int C, int variant, ChunkKernels* ou
     const int c = C > 128 ? 128 : C;
 #define RET_CASE(Cv)                                                                                          \
     if (c == Cv) {                                                                                            \
-        *out = mode == 4   ? chunk_entry_bf16<128, Cv, 512>()                                                 \
+        *out = mode == 4   ? chunk_entry_bf16<128, Cv, 512, 1, true>()                                        \
                : mode == 1 ? chunk_entry_bf16<128, Cv, 256, 2>()                                              \
                            : chunk_entry_bf16<128, Cv>();                                                     \
         return true;                                                                                          \

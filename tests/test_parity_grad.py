@@ -77,14 +77,15 @@ GRAD_IN_PLACE = [
     # retention runs over the reversed sequence in place on the kernel named, with no reordered copies. d_k 256 with
     # d_v a multiple of 256: the three-launch kernels, which also read the d_v blocks of dO and V in place, and with
     # several segments dq' and dk' of every block each in one launch from transposed states (of a local pass and
-    # scan over K' and V, and of the dv retention); otherwise the wide-head kernels (one block)
+    # scan over K' and V, and of the dv retention); otherwise (one block) the single-pass kernels' reversed
+    # instances: the streaming kernel with d_v tiles of 128 for d_k = 128, the wide-head kernel for d_k = 256
     (1, 640, 2, 256, 512, 128, True, 5, "bf16", "ret_chunk_dma", True),   # 5 segments, two d_v blocks
     (2, 512, 2, 256, 256, 64, True, 0, "f32", "ret_chunk_dma", True),     # one block
     (1, 1024, 1, 256, 512, 32, False, 0, "f32", "ret_chunk_dma", True),   # no rotation, chunk 32
     (1, 32, 2, 256, 512, 128, True, 9, "f32", "ret_chunk_dma", False),    # one step
-    (1, 640, 2, 128, 128, 128, True, 5, "bf16", "ret_chunk_wide", True),  # the long-sequence head
-    (1, 512, 2, 128, 256, 64, True, 0, "f32", "ret_chunk_wide", True),    # d_k < d_v
-    (2, 384, 1, 256, 128, 32, False, 0, "f32", "ret_chunk_wide", True),   # d_k > d_v, chunk 32
+    (1, 640, 2, 128, 128, 128, True, 5, "bf16", "ret_chunk_fused", True),  # the long-sequence head
+    (1, 512, 2, 128, 256, 64, True, 0, "f32", "ret_chunk_fused", True),    # d_k < d_v (d_k 256 runs: wide)
+    (2, 384, 1, 256, 128, 32, False, 0, "f32", "ret_chunk_fused", True),   # d_k > d_v, chunk 32
 ]
 
 
@@ -111,23 +112,25 @@ def test_gradients_in_place(R, case):
         assert timer.query("ret_chunk_dma_local")[1] == (2 if multi else 0)
         assert timer.query("ret_chunk_dma_scan")[1] == (2 if multi else 0)
     else:
-        assert timer.query(kernel)[1] == 3
+        assert timer.query(kernel)[1] >= 1
+        assert timer.query("ret_chunk_fused")[1] + timer.query("ret_chunk_wide")[1] == 3
     timer.close()
     _check(got, ref, tol("bf16"))
 
 
 @pytest.mark.parametrize("direct", ["1", "0"])
-@pytest.mark.parametrize("dk,dv", [(256, 512), (128, 128)])
-def test_gradients_in_place_or_copied(R, direct, dk, dv):
-    """d_k 256, d_v 512 (the three-launch kernels) and d_k = d_v = 128 (the wide-head kernels) in place
-    (bwd_direct 1) and through reordered copies (0)."""
+@pytest.mark.parametrize("dk,dv,variant", [(256, 512, 0), (128, 128, 0), (128, 128, 3)])
+def test_gradients_in_place_or_copied(R, direct, dk, dv, variant):
+    """d_k 256, d_v 512 (the three-launch kernels) and d_k = d_v = 128 (the streaming kernel, or the wide-head
+    kernel with variant 3) in place (bwd_direct 1) and through reordered copies (0)."""
     w = W.Workload("grad", B=1, N=768, H=2, dk=dk, dv=dv, dtype="bf16", scale=float(np.sqrt(dk)), seed=47,
                    chunk=128, rotate=True)
     print_case("gradients-path", direct, w)
     q, k, v, rng = W.make_qkv(w)
     do = W.make_dout(w, rng)
     ref = oracle.grad(q, k, v, do, w.gamma, theta=w.theta, pos0=1)
-    got = _gpu_grad(R, q, k, v, do, w.gamma, w.chunk, w.theta, 1, "f32", options={"bwd_direct": int(direct)})
+    got = _gpu_grad(R, q, k, v, do, w.gamma, w.chunk, w.theta, 1, "f32",
+                    options={"bwd_direct": int(direct), "variant": variant})
     _check(got, ref, tol("bf16"))
 
 
@@ -195,7 +198,7 @@ def test_gradients_workload2_full(R):
 
 
 def test_gradients_long_sequence_full(R):
-    """The long-sequence workload (B=1, N=65536, H=8, d=128, chunk 128) at full size: the wide-head kernels over
+    """The long-sequence workload (B=1, N=65536, H=8, d=128, chunk 128) at full size: the streaming kernels over
     the reversed sequence in place, many segments per head."""
     w = W.WORKLOADS[5]
     print_case("gradients-workload5", w)
