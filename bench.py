@@ -267,7 +267,8 @@ def bench_epilogue(R, W, torch, wid, steps):
 
 def bench_backward(R, W, torch, wid, steps):
     """Gradients dq, dk, dv of the chunkwise workload (bf16 q, k, v, dO in; bf16 gradients out), replayed from a
-    HIP graph, with the per-kernel split from the launch events of eager calls."""
+    HIP graph (the fastest of three replays), with the per-kernel split from the launch events of eager calls; on
+    their own, and after the forward call whose workspace they reuse."""
     import numpy as np
     w = W.WORKLOADS[wid]
     q, k, v, rng = W.make_qkv(w)
@@ -279,7 +280,7 @@ def bench_backward(R, W, torch, wid, steps):
     ws = R.chunkwise_bwd_workspace(qd, vd, w.chunk)
     call = lambda options=None: R.ret_chunkwise_bwd(qd, kd, vd, dod, dq, dk, dv, w.gamma, w.chunk, theta=w.theta,
                                                     workspace=ws, options=options)
-    ms = graph_ms(torch, call, steps)
+    ms = graph_ms(torch, call, steps, 3)
     torch.cuda.synchronize()
     timer = R.Timer()
     for _ in range(3):
@@ -288,6 +289,24 @@ def bench_backward(R, W, torch, wid, steps):
     kernels = kernel_times(timer, ("ret_rotate_qk", "ret_permute_rotate") + CHUNK_KERNELS[1:], 3)
     timer.close()
     R.ret_chunkwise_check(ws)
+    # after the forward call of a training step: its workspace (rotated q, k and segment states, where its kernels
+    # leave them) passed to the gradients, which then reuse them (ret_chunkwise_bwd_saved_ex); the forward runs
+    # once, outside the timed replays
+    o = torch.empty_like(vd)
+    fws = R.chunkwise_workspace(qd, vd, w.chunk)
+    R.ret_chunkwise_fwd(qd, kd, vd, o, w.gamma, w.chunk, theta=w.theta, workspace=fws)
+    call_saved = lambda options=None: R.ret_chunkwise_bwd(qd, kd, vd, dod, dq, dk, dv, w.gamma, w.chunk,
+                                                          theta=w.theta, workspace=ws, fwd_workspace=fws,
+                                                          options=options)
+    ms_saved = graph_ms(torch, call_saved, steps, 3)
+    torch.cuda.synchronize()
+    timer = R.Timer()
+    for _ in range(3):
+        call_saved({"timer": timer})
+    torch.cuda.synchronize()
+    kernels_saved = kernel_times(timer, ("ret_rotate_qk", "ret_permute_rotate") + CHUNK_KERNELS[1:], 3)
+    timer.close()
+    del o, fws
     toks = w.B * w.N * w.H
     nbytes = toks * (2 * w.dk + 2 * w.dv) * 2 + toks * (2 * w.dk + w.dv) * 2  # q, k, v, dO in; dq, dk, dv out
     C = w.chunk
@@ -298,12 +317,14 @@ def bench_backward(R, W, torch, wid, steps):
         "workload": "%s: B=%d N=%d H=%d d_k=%d d_v=%d chunk=%d, bf16 q/k/v/dO in, bf16 dq/dk/dv out, xPos rotation"
                     % (w.name, w.B, w.N, w.H, w.dk, w.dv, w.chunk),
         "us_per_call": 1e3 * ms,
+        "us_per_call_after_forward": 1e3 * ms_saved,
         "tokens_per_s": w.B * w.N / (ms * 1e-3),
         "hbm_frac_whole_call": ach / HBM_PEAK_GBS,
         "alg_bytes_per_call": nbytes,
         "tflops_causal": flops / (ms * 1e-3) / 1e12,
         "mfma_frac_causal": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
         "kernels": kernels,
+        "kernels_after_forward": kernels_saved,
         "workspace_bytes": ws.numel(),
     }
 
@@ -579,6 +600,7 @@ def main():
                 fwd = result["chunkwise"] if key == wid else result.get(name)
                 if fwd:
                     bres["x_forward"] = bres["us_per_call"] / (1e3 * fwd["ms_per_call"])
+                    bres["x_forward_after_forward"] = bres["us_per_call_after_forward"] / (1e3 * fwd["ms_per_call"])
                 result["backward"][name] = bres
     if not args.no_cpu_baseline:
         progress("cpu baseline")

@@ -296,6 +296,23 @@ ret_status_t ret_chunkwise_bwd_ex(const void* q, const void* k, const void* v, c
                                   ret_dtype_t out_dt, const float* gamma, const double* theta, int64_t pos0,
                                   int chunk, void* workspace, size_t workspace_bytes, void* stream,
                                   const ret_options_t* opts);
+/*
+ * ret_chunkwise_bwd after the forward, for a training step: fwd_workspace (fwd_workspace_bytes) is the workspace of
+ * a ret_chunkwise_fwd call on the same q, k, v, gamma, theta, pos0 and chunk with no state_in (and the same
+ * options), passed unchanged since that call. Where that call ran the LDS-loading d_k = 256 kernels (d_v a
+ * multiple of 256, several segments, N a multiple of 32) it left there the rotated copies of q and k and the
+ * state entering each segment, which the gradients need too: they are read instead of recomputed (the dq'
+ * retentions enter their segments with those states, transposed). Otherwise, or with fwd_workspace NULL, the
+ * call is ret_chunkwise_bwd_ex. Same results as ret_chunkwise_bwd_ex (bit for bit where the forward's plan is
+ * the gradients' own); a forward workspace from another call gives wrong gradients, which the library cannot
+ * detect. fwd_workspace is only read.
+ */
+ret_status_t ret_chunkwise_bwd_saved_ex(const void* q, const void* k, const void* v, const void* dout, void* dq,
+                                        void* dk_out, void* dv_out, int B, int N, int H, int dk, int dv,
+                                        ret_dtype_t in_dt, ret_dtype_t out_dt, const float* gamma, const double* theta,
+                                        int64_t pos0, int chunk, const void* fwd_workspace, size_t fwd_workspace_bytes,
+                                        void* workspace, size_t workspace_bytes, void* stream,
+                                        const ret_options_t* opts);
 ret_status_t ret_recurrent_step_ex(const void* q, const void* k, const void* v, void* o, float* state, int B, int H,
                                    int dk, int dv, ret_dtype_t in_dt, ret_dtype_t out_dt, const float* gamma,
                                    const double* theta, int64_t pos, void* stream, const ret_options_t* opts);

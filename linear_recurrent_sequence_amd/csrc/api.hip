@@ -852,7 +852,18 @@ ret_status_t ret_chunkwise_bwd_ex(const void* q, const void* k, const void* v, c
                                   ret_dtype_t out_dt, const float* gamma, const double* theta, int64_t pos0,
                                   int chunk, void* workspace, size_t workspace_bytes, void* stream,
                                   const ret_options_t* opts) {
+    return ret_chunkwise_bwd_saved_ex(q, k, v, dout, dq, dk_out, dv_out, B, N, H, dk, dv, in_dt, out_dt, gamma, theta,
+                                      pos0, chunk, nullptr, 0, workspace, workspace_bytes, stream, opts);
+}
+
+ret_status_t ret_chunkwise_bwd_saved_ex(const void* q, const void* k, const void* v, const void* dout, void* dq,
+                                        void* dk_out, void* dv_out, int B, int N, int H, int dk, int dv,
+                                        ret_dtype_t in_dt, ret_dtype_t out_dt, const float* gamma, const double* theta,
+                                        int64_t pos0, int chunk, const void* fwd_workspace, size_t fwd_workspace_bytes,
+                                        void* workspace, size_t workspace_bytes, void* stream,
+                                        const ret_options_t* opts) {
     const Opts op = resolve(opts);
+    if (fwd_workspace && !aligned16(fwd_workspace)) return fail(RET_ERR_INVALID_ARG, "fwd_workspace must be aligned");
     ret_status_t st = check_common(q, k, v, dq, B, N, H, dk, dv, in_dt, out_dt, gamma, theta);
     if (st != RET_OK) return st;
     if (!dout || !dk_out || !dv_out) return fail(RET_ERR_INVALID_ARG, "null dout/dk/dv pointer");
@@ -883,19 +894,6 @@ ret_status_t ret_chunkwise_bwd_ex(const void* q, const void* k, const void* v, c
         // instances, whose segment chain is cleared between calls of different shapes.
         Opts ov = op;
         ov.variant = L.variant;
-        const void *Qp = q, *Kp = k;
-        if (theta) {
-            FwdArgs A;
-            fill_fwd(A, q, k, v, nullptr, B, N, H, dk, dv, out_dt, gamma, theta, pos0);
-            A.qr = ws + L.qp;
-            A.kr = ws + L.kp;
-            Qp = A.qr;
-            Kp = A.kr;
-            LaunchTimer tr("ret_rotate_qk", s, op);
-            hipLaunchKernelGGL(rotate_qk_get(), dim3(rotate_qk_blocks(B, N, H, dk)), dim3(256), 0, s, A);
-            tr.done();
-            if ((st = launch_status("ret_rotate_qk")) != RET_OK) return st;
-        }
         void* chain = ws + L.chain;
         const int wb = L.wb, din = L.nb > 1 ? dv : 0;
         // On the three-launch kernels with square states (d_k = d_v / blocks = 256) and several segments, dq' and
@@ -910,9 +908,38 @@ ret_status_t ret_chunkwise_bwd_ex(const void* q, const void* k, const void* v, c
                            resolve_chunk(RET_BF16, B, N, H, dk, dv, chunk, false, L.chain_bytes, ov, &ck_sq, &plan_sq) &&
                            ck_sq.split_local && plan_sq.nseg > 1 && pick_chunk(RET_BF16, wb, dk, chunk, &ck_bl, ov) &&
                            ck_bl.split_full_rev && ck_bl.dvt == dk;
+        // The forward's workspace holds Q', K' and those same (K', V) states when its plan (with rotation, in its
+        // workspace) ran the three-launch kernels over the same segments: then they are read from there.
+        const char* fws = nullptr;
+        ChunkPlan plan_f;
+        if (share && fwd_workspace) {
+            ChunkKernels ck_f;
+            if (resolve_chunk(RET_BF16, B, N, H, dk, dv, chunk, theta != nullptr, fwd_workspace_bytes, op, &ck_f,
+                              &plan_f) &&
+                ck_f.split_local && plan_f.nseg == plan_sq.nseg && plan_f.seg_len == plan_sq.seg_len &&
+                (!theta || plan_f.rot_bytes > 0))
+                fws = (const char*)fwd_workspace;
+        }
+        const void *Qp = q, *Kp = k;
+        if (theta && fws) {
+            Qp = fws + plan_f.chain_bytes;
+            Kp = (const char*)Qp + plan_f.rot_bytes / 2;
+        } else if (theta) {
+            FwdArgs A;
+            fill_fwd(A, q, k, v, nullptr, B, N, H, dk, dv, out_dt, gamma, theta, pos0);
+            A.qr = ws + L.qp;
+            A.kr = ws + L.kp;
+            Qp = A.qr;
+            Kp = A.kr;
+            LaunchTimer tr("ret_rotate_qk", s, op);
+            hipLaunchKernelGGL(rotate_qk_get(), dim3(rotate_qk_blocks(B, N, H, dk)), dim3(256), 0, s, A);
+            tr.done();
+            if ((st = launch_status("ret_rotate_qk")) != RET_OK) return st;
+        }
         float* const slots = (float*)((char*)chain + kChainMeta);  // segment states of the (d_k, d_v) runs
         // every block's dq' (rev = false) or dk' (rev = true) in one full-pass launch from the transposed states
-        auto blocks_from_t = [&](const void* qq, const void* kk, const void* vv, void* out, bool rev) {
+        auto blocks_from_t = [&](const void* qq, const void* kk, const void* vv, void* out, bool rev,
+                                 const float* states) {
             FwdArgs A;
             fill_fwd(A, qq, kk, vv, out, B, N, H, wb, dk, RET_F32, gamma, nullptr, 0);
             A.qr = const_cast<void*>(qq);
@@ -922,14 +949,18 @@ ret_status_t ret_chunkwise_bwd_ex(const void* q, const void* k, const void* v, c
             A.qk_din = din;
             A.qk_blocks = L.nb;
             A.o_block = L.nb > 1 ? (long long)(rev ? L.g3b[1] - L.g3b[0] : L.g1b[1] - L.g1b[0]) / 4 : 0;
-            A.ws_t = slots;
+            A.ws_t = states;
             const unsigned grid = (unsigned)((long long)B * H * L.nb * plan_sq.nseg);
             LaunchTimer tm(ck_bl.pre_name, s, ov);
             hipLaunchKernelGGL(rev ? ck_bl.split_full_rev : ck_bl.fused_pre, dim3(grid), dim3(kDmaThreads), 0, s, A);
             tm.done();
             return launch_status(ck_bl.pre_name);
         };
-        if (share) {
+        if (share && fws) {
+            // the forward's segment states, as its scan left them
+            if ((st = blocks_from_t(dout, v, Kp, ws + L.g1b[0], false, (const float*)(fws + kChainMeta))) != RET_OK)
+                return st;
+        } else if (share) {
             // the forward's segment states: local passes and scan over (K', V) alone
             FwdArgs A;
             fill_fwd(A, nullptr, Kp, v, nullptr, B, N, H, dk, dv, RET_F32, gamma, nullptr, 0);
@@ -948,7 +979,7 @@ ret_status_t ret_chunkwise_bwd_ex(const void* q, const void* k, const void* v, c
                                s, A);
             tc.done();
             if ((st = launch_status("ret_chunk_dma_scan")) != RET_OK) return st;
-            if ((st = blocks_from_t(dout, v, Kp, ws + L.g1b[0], false)) != RET_OK) return st;
+            if ((st = blocks_from_t(dout, v, Kp, ws + L.g1b[0], false, slots)) != RET_OK) return st;
         } else {
             for (int i = 0; i < L.nb; ++i)
                 if ((st = chunkwise_run(dout, v, Kp, ws + L.g1b[i], B, N, H, wb, dk, RET_BF16, RET_F32, gamma, nullptr,
@@ -963,7 +994,7 @@ ret_status_t ret_chunkwise_bwd_ex(const void* q, const void* k, const void* v, c
                                 nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, ov, true)) != RET_OK)
             return st;
         if (share) {
-            if ((st = blocks_from_t(v, dout, Qp, ws + L.g3b[0], true)) != RET_OK) return st;
+            if ((st = blocks_from_t(v, dout, Qp, ws + L.g3b[0], true, slots)) != RET_OK) return st;
         } else {
             if (reshaped && (st = chain_meta_zero(in_dt, B, N, H, wb, dk, chunk, chain, L.chain_bytes, s, ov)) != RET_OK)
                 return st;

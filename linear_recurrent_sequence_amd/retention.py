@@ -159,6 +159,9 @@ def load(build_if_missing: bool = True):
     lib.ret_chunkwise_msr_fwd_ex.restype = i32
     lib.ret_chunkwise_bwd_ex.argtypes = lib.ret_chunkwise_bwd.argtypes + [op]
     lib.ret_chunkwise_bwd_ex.restype = i32
+    lib.ret_chunkwise_bwd_saved_ex.argtypes = lib.ret_chunkwise_bwd.argtypes[:18] + [vp, sz] + \
+        lib.ret_chunkwise_bwd.argtypes[18:] + [op]
+    lib.ret_chunkwise_bwd_saved_ex.restype = i32
     lib.ret_recurrent_step_ex.argtypes = lib.ret_recurrent_step.argtypes + [op]
     lib.ret_recurrent_step_ex.restype = i32
     lib.ret_recurrent_step_positions_ex.argtypes = lib.ret_recurrent_step_positions.argtypes + [op]
@@ -438,10 +441,12 @@ def chunkwise_bwd_workspace(q, v, chunk, options=None):
 
 
 def ret_chunkwise_bwd(q, k, v, dout, dq, dk, dv, gamma, chunk, theta=None, pos0=0, workspace=None, stream=None,
-                      options=None, check=False):
+                      options=None, check=False, fwd_workspace=None):
     """dq, dk, dv <- gradients of sum(dout (.) O), O = chunkwise retention of (q, k, v) from a zero state. Without a
     workspace one is allocated for the call; check=True then synchronises and raises if a segment-chain wait gave
-    up (the affected gradients are NaN either way)."""
+    up (the affected gradients are NaN either way). fwd_workspace: the workspace of the ret_chunkwise_fwd call that
+    made O (same inputs and options, no state_in), whose rotated q, k and segment states are then reused where its
+    kernels left them (ret_chunkwise_bwd_saved_ex)."""
     lib = load()
     _qkv(q, k, v)
     B, N, H, d_k = q.shape
@@ -450,16 +455,18 @@ def ret_chunkwise_bwd(q, k, v, dout, dq, dk, dv, gamma, chunk, theta=None, pos0=
     _shape(dq, "dq", (B, N, H, d_k), _IO)
     _shape(dk, "dk", (B, N, H, d_k), (dq.dtype,))
     _shape(dv, "dv", (B, N, H, d_v), (dq.dtype,))
-    _same_device(q, k, v, dout, dq, dk, dv, workspace)
+    _same_device(q, k, v, dout, dq, dk, dv, workspace, fwd_workspace)
     g, gp = _gamma(gamma, H)
     th, tp = _theta(theta, d_k)
     if workspace is None:
         workspace = chunkwise_bwd_workspace(q, v, chunk, options)
     wsb = workspace.numel() * workspace.element_size()
-    st = lib.ret_chunkwise_bwd_ex(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(dout, "dout"), _dev(dq, "dq"),
-                                  _dev(dk, "dk"), _dev(dv, "dv"), B, N, H, d_k, d_v, _dt(q), _dt(dq), gp, tp,
-                                  int(pos0), int(chunk), _dev(workspace, "workspace"), wsb, _stream(stream),
-                                  _options(options))
+    fwp = _dev(fwd_workspace, "fwd_workspace") if fwd_workspace is not None else None
+    fwb = fwd_workspace.numel() * fwd_workspace.element_size() if fwd_workspace is not None else 0
+    st = lib.ret_chunkwise_bwd_saved_ex(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(dout, "dout"), _dev(dq, "dq"),
+                                        _dev(dk, "dk"), _dev(dv, "dv"), B, N, H, d_k, d_v, _dt(q), _dt(dq), gp, tp,
+                                        int(pos0), int(chunk), fwp, fwb, _dev(workspace, "workspace"), wsb,
+                                        _stream(stream), _options(options))
     _check("ret_chunkwise_bwd", st)
     if check:
         ret_chunkwise_check(workspace, stream)

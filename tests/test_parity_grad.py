@@ -211,7 +211,9 @@ def test_gradients_long_sequence_full(R):
 
 def test_gradients_7b_class_layer_full(R):
     """The 7b-class-layer workload (B=1, N=8192, H=16, d_k=256, d_v=512, chunk 128) at full size: the paper's
-    head shape, dq' and dk' as sums over the two halves of d_v, read in place."""
+    head shape, dq' and dk' as sums over the two halves of d_v, read in place; and the same gradients, bit for bit,
+    from the forward call's saved rotated q, k and segment states."""
+    import torch
     w = W.WORKLOADS[4]
     print_case("gradients-workload4", w)
     q, k, v, rng = W.make_qkv(w)
@@ -219,3 +221,50 @@ def test_gradients_7b_class_layer_full(R):
     ref = oracle.grad(q, k, v, do, w.gamma, theta=w.theta)
     got = _gpu_grad(R, q, k, v, do, w.gamma, w.chunk, w.theta, 0, "bf16")
     _check(got, ref, tol("bf16"))
+    qd, kd, vd, dod = (to_dev(x, "bf16") for x in (q, k, v, do))
+    fws = R.chunkwise_workspace(qd, vd, w.chunk)
+    R.ret_chunkwise_fwd(qd, kd, vd, empty_out(v.shape, "bf16"), w.gamma, w.chunk, theta=w.theta, workspace=fws)
+    dq, dk_, dv_ = empty_out(q.shape, "bf16"), empty_out(k.shape, "bf16"), empty_out(v.shape, "bf16")
+    R.ret_chunkwise_bwd(qd, kd, vd, dod, dq, dk_, dv_, w.gamma, w.chunk, theta=w.theta, fwd_workspace=fws, check=True)
+    torch.cuda.synchronize()
+    for a, b in zip(got, (to_host(dq), to_host(dk_), to_host(dv_))):
+        assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("case", [
+    # B, N, H, dk, dv, chunk, rotate, pos0, forward options: the forward's rotated q, k and segment states reused
+    (1, 640, 2, 256, 512, 128, True, 5, None),
+    (2, 512, 2, 256, 256, 64, False, 0, None),
+    # nothing to reuse: a forward with another segment plan, or another kernel family
+    (1, 640, 2, 256, 512, 128, True, 5, {"segments": 2}),
+    (1, 300, 2, 64, 64, 64, True, 3, None),
+], ids=["dk256-dv512", "dk256-dv256-norot", "other-plan", "dk64"])
+def test_gradients_after_forward(R, case):
+    """ret_chunkwise_bwd_saved_ex with the forward call's workspace gives the same gradients, bit for bit, as the
+    gradients computed on their own, and skips the rotation and the (K', V) states where it reuses them."""
+    import torch
+    B, N, H, dk, dv, chunk, rot, pos0, fopts = case
+    w = W.Workload("grad", B=B, N=N, H=H, dk=dk, dv=dv, dtype="bf16", scale=float(np.sqrt(dk)), seed=71 + N,
+                   chunk=chunk, rotate=rot)
+    print_case("gradients-after-forward", fopts, w)
+    q, k, v, rng = W.make_qkv(w)
+    do = W.make_dout(w, rng)
+    qd, kd, vd, dod = (to_dev(x, "bf16") for x in (q, k, v, do))
+    o = empty_out(v.shape, "bf16")
+    fws = R.chunkwise_workspace(qd, vd, chunk, fopts)
+    R.ret_chunkwise_fwd(qd, kd, vd, o, w.gamma, chunk, theta=w.theta, pos0=pos0, workspace=fws, options=fopts)
+    grads = []
+    for saved in (False, True):
+        dq, dk_, dv_ = empty_out(q.shape, "f32"), empty_out(k.shape, "f32"), empty_out(v.shape, "f32")
+        timer = R.Timer()
+        R.ret_chunkwise_bwd(qd, kd, vd, dod, dq, dk_, dv_, w.gamma, chunk, theta=w.theta, pos0=pos0,
+                            options={"timer": timer}, fwd_workspace=fws if saved else None, check=True)
+        torch.cuda.synchronize()
+        grads.append((to_host(dq), to_host(dk_), to_host(dv_)))
+        if saved and fopts is None and dk == 256:
+            assert timer.query("ret_rotate_qk")[1] == 0
+            assert timer.query("ret_chunk_dma_local")[1] == 1 and timer.query("ret_chunk_dma_scan")[1] == 1
+        timer.close()
+    for a, b in zip(*grads):
+        assert np.array_equal(a, b)
+    _check(grads[1], oracle.grad(q, k, v, do, w.gamma, theta=w.theta, pos0=pos0), tol("bf16"))
