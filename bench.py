@@ -44,7 +44,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # Chunkwise workloads by name -> key (and seed) in workloads.WORKLOADS
 CHUNK_WORKLOADS = {"retention-layer-d512": 2, "7b-class-layer": 4, "long-sequence": 5}
 CHUNK_KERNELS = ("ret_rotate_qk", "ret_chunk_seg", "ret_chunk_fused", "ret_chunk_wide", "ret_chunk_dma",
-                 "ret_chunk_dma_local", "ret_chunk_dma_scan", "ret_chunk_local", "ret_segment_scan", "ret_chunk_full")
+                 "ret_chunk_dma_local", "ret_chunk_dma_scan", "ret_chunk_fused_local", "ret_chunk_fused_scan",
+                 "ret_chunk_local", "ret_segment_scan", "ret_chunk_full")
 
 
 def source_digest() -> str:

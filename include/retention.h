@@ -218,10 +218,11 @@ ret_status_t ret_chunkwise_bwd(const void* q, const void* k, const void* v, cons
  * call holds one, every kernel it launches is bracketed by a pair of HIP events on the launch stream and
  * recorded in it (the library keeps no timing state of its own). ret_timer_query synchronises those events and
  * returns the total milliseconds and launch count recorded for kernels whose name equals `kernel` ("" or NULL =
- * all). Kernel names: "ret_chunk_seg", "ret_chunk_fused", "ret_chunk_wide", "ret_chunk_dma_local",
- * "ret_chunk_dma_scan", "ret_chunk_dma" and "ret_rotate_qk" (bf16 input), "ret_chunk_full", "ret_chunk_local", "ret_segment_scan" (fp32 input), "ret_parallel",
- * "ret_recurrent_step", "ret_msr_epilogue", "ret_permute_rotate" (gradients), "ret_norm_zseg", "ret_norm_rows",
- * "ret_norm_scale", "ret_norm_step" (score normalizations). A timer must not be attached to calls that are being captured into a
+ * all). Kernel names: "ret_chunk_seg", "ret_chunk_fused", "ret_chunk_fused_local", "ret_chunk_fused_scan",
+ * "ret_chunk_wide", "ret_chunk_dma_local", "ret_chunk_dma_scan", "ret_chunk_dma" and "ret_rotate_qk" (bf16 input),
+ * "ret_chunk_full", "ret_chunk_local", "ret_segment_scan" (fp32 input), "ret_parallel", "ret_recurrent_step",
+ * "ret_msr_epilogue", "ret_permute_rotate" (gradients), "ret_norm_zseg", "ret_norm_rows", "ret_norm_scale",
+ * "ret_norm_step" (score normalizations). A timer must not be attached to calls that are being captured into a
  * graph. One timer may be shared by calls on several threads.
  */
 typedef struct ret_timer ret_timer_t;

@@ -196,7 +196,8 @@ void plan_segments(int B, int N, int H, int dv, int C, int dvt, int target_wgs, 
 size_t segment_ws_bytes(const ChunkKernels& ck, int B, int H, int dk, int dv, int nseg) {
     if (nseg <= 1) return 0;
     // the split launches: a state slot per (unit, segment) after the chain's (untouched) first kChainMeta bytes
-    if (ck.split_local) return kChainMeta + (size_t)B * H * (dv / ck.dvt) * nseg * dk * ck.dvt * sizeof(float);
+    if (ck.split_local || ck.fused_split)
+        return kChainMeta + (size_t)B * H * (dv / ck.dvt) * nseg * dk * ck.dvt * sizeof(float);
     if (ck.fused) return chain_layout(B * H * (dv / ck.dvt), nseg, dk * ck.dvt).bytes;
     return sizeof(ChainHeader) + (size_t)B * H * nseg * dk * dv * sizeof(float);
 }
@@ -486,6 +487,26 @@ ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o,
         const bool pre = !onchip && (fn == ck.fused_pre || (rev && fn == ck.fused_rev));
         const int threads = onchip || !ck.threads ? kThreads : pre && ck.threads_pre ? ck.threads_pre : ck.threads;
         const char* name = onchip ? "ret_chunk_seg" : pre && ck.pre_name ? ck.pre_name : "ret_chunk_fused";
+        if (ck.fused_split && !onchip && nseg > 1 && !epi) {
+            // local passes, the scan of their states, then the full pass of every segment (no chain)
+            A.ws = workspace ? (float*)((char*)workspace + kChainMeta) : nullptr;
+            const unsigned units = (unsigned)((long long)B * H * ntiles);
+            A.split = 1;
+            LaunchTimer tl("ret_chunk_fused_local", s, op);
+            hipLaunchKernelGGL(fn, dim3(units * (unsigned)(nseg - 1)), dim3(threads), 0, s, A);
+            tl.done();
+            if ((st = launch_status("ret_chunk_fused_local")) != RET_OK) return st;
+            LaunchTimer tc("ret_chunk_fused_scan", s, op);
+            hipLaunchKernelGGL(slot_scan_get(), dim3((unsigned)((long long)dk * ck.dvt / 512), units), dim3(256), 0, s,
+                               A);
+            tc.done();
+            if ((st = launch_status("ret_chunk_fused_scan")) != RET_OK) return st;
+            A.split = 2;
+            LaunchTimer tm(name, s, op);
+            hipLaunchKernelGGL(fn, dim3(grid), dim3(threads), 0, s, A);
+            tm.done();
+            return launch_status(name);
+        }
         if (epi && onchip && out_dt == RET_BF16 && dv == 64) {
             A.epi = 1;
             A.gate = epi->gate;
@@ -638,7 +659,7 @@ ret_status_t chain_meta_zero(ret_dtype_t in_dt, int B, int N, int H, int dk, int
                              size_t chain_bytes, hipStream_t s, const Opts& op) {
     ChunkKernels ck;
     // the split kernels keep no flags
-    if (!pick_chunk(in_dt, dk, dv, chunk, &ck, op) || !ck.fused || ck.split_local) return RET_OK;
+    if (!pick_chunk(in_dt, dk, dv, chunk, &ck, op) || !ck.fused || ck.split_local || ck.fused_split) return RET_OK;
     const ChunkPlan p = plan_chunk(ck, B, N, H, dk, dv, chunk, false, chain_bytes, op);
     if (p.nseg <= 1) return RET_OK;
     const ChainLayout lay = chain_layout(B * H * (dv / ck.dvt), p.nseg, dk * ck.dvt);
@@ -1357,7 +1378,7 @@ ret_status_t ret_chunkwise_fwd_noalloc(const void* q, const void* k, const void*
     ChunkPlan used;
     if (!resolve_chunk(in_dt, B, N, H, dk, dv, chunk, theta != nullptr, avail, kDefaultOpts, &ck, &used))
         return fail(RET_ERR_UNSUPPORTED, "chunkwise form: unsupported d_k=%d d_v=%d chunk=%d", dk, dv, chunk);
-    if (used.nseg > 1 && ck.fused && !ck.split_local &&
+    if (used.nseg > 1 && ck.fused && !ck.split_local && !ck.fused_split &&
         chain_layout(B * H * (dv / ck.dvt), used.nseg, dk * ck.dvt).agg_off > kChainMeta)
         return fail(RET_ERR_WORKSPACE, "no-allocation chunkwise call: %d units x %d segments exceed the chain's "
                     "counter and flag region", B * H * (dv / ck.dvt), used.nseg);

@@ -269,6 +269,20 @@ __device__ __forceinline__ int unit_of_block(int ntiles, int units) {
     return __builtin_amdgcn_readfirstlane(unit_i);
 }
 
+// The unit and segment of a workgroup of a grid of units x segments workgroups, segment-major. Workgroups go to
+// the 8 XCDs in turn (launch index mod 8); when a segment's units divide evenly, the d_v tiles of one (b, h)
+// get launch indices of one residue, so they run on one XCD and its L2 serves the q' and k' rows they all load.
+__device__ __forceinline__ void unit_seg_of_block(int ntiles, int units, int* unit, int* seg) {
+    const int bid = blockIdx.x, s = bid / units, r = bid % units;
+    int u = r;
+    if (ntiles > 1 && units % (8 * ntiles) == 0) {
+        const int xcd = r % 8, q8 = r / 8;
+        u = ((q8 / ntiles) * 8 + xcd) * ntiles + q8 % ntiles;
+    }
+    *unit = __builtin_amdgcn_readfirstlane(u);
+    *seg = __builtin_amdgcn_readfirstlane(s);
+}
+
 // Chain storage of one unit (chained runs).
 struct Chain {
     int* ctr;      // [2]: next segment ticket, workgroups past the look-back
@@ -493,10 +507,19 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT, NDW>::OCC)) void ch
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g4 = 4 * (lane >> 4), n16 = lane & 15;
     const int ntiles = __builtin_amdgcn_readfirstlane(a.dv / DVT);
     const int units = __builtin_amdgcn_readfirstlane(a.B * a.H * ntiles);
-    const bool chained = a.nseg > 1;
+    // split 1: the local pass alone of every segment but the last, its state stored to the segment's slot;
+    // split 2: the full pass alone of every segment, from the state in its slot (a scan of the local passes' states
+    // in between); split 0: one launch, the segments chained.
+    const int split = __builtin_amdgcn_readfirstlane(a.split);
+    const bool chained = a.nseg > 1 && split == 0;
     // The unit comes from the launch index; with several segments the segment is the unit's next ticket.
-    const int unit = unit_of_block(ntiles, units);
-    int seg = __builtin_amdgcn_readfirstlane((int)(blockIdx.x / (unsigned)units));
+    int unit, seg;
+    if (split) {  // segment-major grids of units x segments
+        unit_seg_of_block(ntiles, units, &unit, &seg);
+    } else {
+        unit = unit_of_block(ntiles, units);
+        seg = __builtin_amdgcn_readfirstlane((int)(blockIdx.x / (unsigned)units));
+    }
     Chain ch{};
     if (chained) {
         ch = chain_of(a.ws, units, a.nseg, unit, DK * DVT, a.chain_spin);
@@ -548,16 +571,31 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT, NDW>::OCC)) void ch
                                                    (w * NDW + j) * 16 + n16];
     };
 
+    // slot s of this unit (split launches): DK x DVT floats in the thread order of slot_store
+    auto split_slot = [&](int s) __attribute__((always_inline)) {
+        return a.ws + ((size_t)unit * anseg + s) * (size_t)(DK * DVT);
+    };
     f32x4_t R[NR];
 #pragma unroll
     for (int x = 0; x < NR; ++x) R[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    if (seg == 0 && a.state_in) load_state_in(R);
+    if (split == 2) {
+        slot_load<NR, NT>(split_slot(seg), R, tid);
+    } else if (seg == 0 && a.state_in) {
+        load_state_in(R);
+        if (split == 1) {  // the scan starts from state_in, in slot 0; the local pass itself from zero
+            slot_store<NR, NT>(split_slot(0), R, tid);
+#pragma unroll
+            for (int x = 0; x < NR; ++x) R[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+    } else if (split == 1 && seg == 0) {
+        slot_store<NR, NT>(split_slot(0), R, tid);  // zero
+    }
 
     const bool last = seg == anseg - 1;
     const bool boundary = seg % kChainGroup == kChainGroup - 1;  // a group's last segment publishes a prefix
 
-    // ---- local pass over the segment (chained runs, all segments but the last) ----
-    if (chained && !last) {
+    // ---- local pass over the segment (chained or split runs, all segments but the last) ----
+    if ((chained || split == 1) && !last) {
         uint16_t* lK = smem;
         uint16_t* lV = smem + C * ZK::LD;
         const int lk_t = ZK::lane_trp(lane);
@@ -642,6 +680,10 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT, NDW>::OCC)) void ch
             if (c + 1 < nchunks) lchunk(c + 1, std::integral_constant<int, 1>{});
         }
         __syncthreads();  // the local tiles are dead before the full pass reuses the LDS
+        if (split == 1) {  // the segment's state, for the scan
+            slot_store<NR, NT>(split_slot(seg + 1), R, tid);
+            return;
+        }
         // Publish the aggregate for the later segments of the group (nothing else in flight). The first segment
         // starts its full pass from state_in again: it reloads it into R behind the slot stores and before its
         // flag rises, since state_out may be the same buffer, and the last segment writes it only after every

@@ -20,6 +20,12 @@ ChunkKernels chunk_entry_wide128() {
     return k;
 }
 
+// The set in three launches for chained segments (local passes, scan, full passes): no workgroup waits on a chain.
+ChunkKernels split_launches(ChunkKernels k) {
+    k.fused_split = 1;
+    return k;
+}
+
 bool chunk_kernels_bf16_128(int dk, int dv, int C, int variant, ChunkKernels* out) {
     if (dv % 64 || dk != 128) return false;
     const bool chunk_ok = C == 32 || C == 64 || C == 128 || C == 256 || C == 512;
@@ -35,7 +41,7 @@ bool chunk_kernels_bf16_128(int dk, int dv, int C, int variant, ChunkKernels* ou
     const int c = C > 128 ? 128 : C;
 #define RET_CASE(Cv)                                                                                          \
     if (c == Cv) {                                                                                            \
-        *out = mode == 4   ? chunk_entry_bf16<128, Cv, 512, 1, true>()                                        \
+        *out = mode == 4   ? split_launches(chunk_entry_bf16<128, Cv, 512, 1, true>())                        \
                : mode == 1 ? chunk_entry_bf16<128, Cv, 256, 2>()                                              \
                            : chunk_entry_bf16<128, Cv>();                                                     \
         return true;                                                                                          \

@@ -116,20 +116,6 @@ __device__ __forceinline__ bf16x8_t scale_frag(bf16x8_t f, const float* z) {
 }
 
 
-// The unit and segment of a workgroup of a grid of units x segments workgroups, segment-major. Workgroups go to
-// the 8 XCDs in turn (launch index mod 8); when a segment's units divide evenly, the d_v tiles of one (b, h)
-// get launch indices of one residue, so they run on one XCD and its L2 serves the q' and k' rows they all load.
-__device__ __forceinline__ void unit_seg_of_block(int ntiles, int units, int* unit, int* seg) {
-    const int bid = blockIdx.x, s = bid / units, r = bid % units;
-    int u = r;
-    if (ntiles > 1 && units % (8 * ntiles) == 0) {
-        const int xcd = r % 8, q8 = r / 8;
-        u = ((q8 / ntiles) * 8 + xcd) * ntiles + q8 % ntiles;
-    }
-    *unit = __builtin_amdgcn_readfirstlane(u);
-    *seg = __builtin_amdgcn_readfirstlane(s);
-}
-
 // The values every pass of one workgroup shares (REV: the run goes over the reversed sequence).
 template <int DK, bool REV>
 struct DmaCtx {

@@ -50,6 +50,8 @@ struct FwdArgs {
     int qk_din, qk_col0, qk_blocks;
     long long o_block;
     const float* ws_t;
+    // chunk_fused_bf16 in three launches: 1 = the local passes, 2 = the full passes (0: one chained launch)
+    int split;
     float log2g[kMaxHeads];
     double theta[kMaxPairs];
 };
@@ -992,6 +994,9 @@ struct ChunkKernels {
     // rev_step), or null
     fwd_kernel_t fused_rev;
     int rev_step;
+    // the single-pass kernels run chained segments as three launches instead (FwdArgs::split: the local passes,
+    // slot_scan_kernel, the full passes), with the segment states in the workspace after its first kChainMeta bytes
+    int fused_split;
 };
 struct ParKernel {
     fwd_kernel_t fn;
@@ -1006,6 +1011,9 @@ ChunkKernels chunk_entry() {
 
 // Getters, one per kernel-group source. Return false when the shape has no instance.
 fwd_kernel_t segment_scan_get();
+// W_s = gamma^T W_(s-1) + slot s over a unit's slots (slot 0 holds W_0), in place; grid (slot floats / 512, units)
+// of 256 threads.
+fwd_kernel_t slot_scan_get();
 // q' and k' (bf16): q and k rotated by their absolute positions, into a.qr / a.kr; rotate_qk_blocks() 256-thread
 // workgroups.
 fwd_kernel_t rotate_qk_get();

@@ -38,6 +38,35 @@ __global__ __launch_bounds__(kThreads) void segment_scan_kernel(FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------------
+// slot_scan: the states entering the segments of a split run. Slot 0 of each unit holds W_0 (state_in, or zero),
+// slot s >= 1 the local end state of segment s - 1, each in one layout (the same in every slot); W_s =
+// gamma^seg_len W_(s-1) + slot s replaces slot s. Elementwise: one thread per 2 consecutive floats of a slot of
+// gridDim.x * 512 floats (many small workgroups: the chain over the segments is latency-bound); grid.y = the
+// units, d_v tiles of each (b, h) consecutive. The loads of a group of 16 segments are issued together.
+// ---------------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void slot_scan_kernel(FwdArgs a) {
+    constexpr int G = 16;
+    const long long per = (long long)gridDim.x * 512;
+    const int unit = blockIdx.y, ntiles = gridDim.y / (a.B * a.H);
+    const float decay = __builtin_amdgcn_exp2f((float)a.seg_len * a.log2g[unit / ntiles % a.H]);
+    float* W = a.ws + (long long)unit * a.nseg * per + ((long long)blockIdx.x * 256 + threadIdx.x) * 2;
+    float2 acc = *reinterpret_cast<const float2*>(W);
+    for (int g0 = 1; g0 < a.nseg; g0 += G) {
+        float2 u[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j)  // branch-free: past the last segment re-read the last one (unused)
+            u[j] = *reinterpret_cast<const float2*>(W + (long long)min(g0 + j, a.nseg - 1) * per);
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+            if (g0 + j < a.nseg) {
+                acc.x = decay * acc.x + u[j].x;
+                acc.y = decay * acc.y + u[j].y;
+                *reinterpret_cast<float2*>(W + (long long)(g0 + j) * per) = acc;
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------------------------------
 // rotate_qk: q' = rotated q, k' = rotated k (bf16 in, bf16 out), the rotation the chunk kernels otherwise
 // apply while staging. Written once when a call stages the same rows for several d_v tiles. Thread: one
 // 16-byte segment (8 dims, 4 pairs) of one (b, h) row over kRotTokens consecutive tokens; the factors of the
@@ -177,5 +206,6 @@ step_kernel_t step_kernel_get(bool bf16_in, int dk, int dv, int npairs, int cw, 
 }
 
 fwd_kernel_t segment_scan_get() { return segment_scan_kernel; }
+fwd_kernel_t slot_scan_get() { return slot_scan_kernel; }
 
 }  // namespace ret

@@ -77,10 +77,9 @@ def test_chunkwise_rejects_invalid_arguments(lib, kw, status):
 def test_workspace_query(lib):
     # one (b, h) with a long sequence is split into segments; many short sequences are not
     n_long = lib.ret_chunkwise_workspace_bytes(1, 65536, 8, 128, 128, 128, 1)
-    # 8 units (8 heads x 1 d_v tile of 128) x 32 segments of 2048 tokens: a 256-byte header, two int
-    # counters per unit and one int flag per (unit, segment) in the first 64 KB, then two 128x128 fp32 state
-    # slots (aggregate, inclusive prefix) per (unit, segment)
-    assert n_long == 64 * 1024 + 2 * 8 * 32 * 128 * 128 * 4
+    # 8 units (8 heads x 1 d_v tile of 128) x 32 segments of 2048 tokens in three launches (local passes, scan,
+    # full passes): the first 64 KB (header, untouched), then one 128x128 fp32 state slot per (unit, segment)
+    assert n_long == 64 * 1024 + 8 * 32 * 128 * 128 * 4
     # fp32 input runs the split kernels: the header, then one d_k x d_v state per (b, h, segment)
     n_f32 = lib.ret_chunkwise_workspace_bytes(1, 4096, 2, 64, 64, 64, 0)
     assert n_f32 > 256 and (n_f32 - 256) % (2 * 64 * 64 * 4) == 0

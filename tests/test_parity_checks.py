@@ -153,9 +153,11 @@ def test_state_out_may_be_state_in(R, case):
 
 
 @pytest.mark.parametrize("case", [("onchip-dk64", 64, 64, 64, {"segments": 4}),
-                                  ("streaming-dk128", 128, 128, 128, {"segments": 4})], ids=lambda c: c[0])
+                                  ("streaming-dk128", 128, 128, 128, {"segments": 4, "variant": 2})],
+                         ids=lambda c: c[0])
 def test_chain_give_up_is_visible(R, case):
-    """Every segment-chain wait made to give up at once (chain_spin < 0, set from the host; no kernel stalls):
+    """Every segment-chain wait made to give up at once (chain_spin < 0, set from the host; no kernel stalls), in
+    the chained on-chip kernel and the chained streaming kernel (d_v tiles of 64; tiles of 128 run unchained):
     the first segment's outputs are right, every later segment's outputs and the final state are NaN, and
     ret_chunkwise_check reports it. The workspace then still serves a normal call, which is right."""
     import torch
