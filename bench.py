@@ -440,8 +440,13 @@ def copy_calibration(torch):
 
 def _counter_rows(directory, counter, kernel_substr):
     """Per-dispatch values of `counter` for kernels whose name contains kernel_substr, from the
-    *_counter_collection.csv files rocprofv3 wrote under directory."""
+    *_counter_collection.csv files rocprofv3 wrote under directory. "NAME@grid=N" also requires a grid of N
+    threads (one kernel launched in several roles, as the split launches of the streaming kernel)."""
     import csv
+    grid = None
+    if "@grid=" in kernel_substr:
+        kernel_substr, g = kernel_substr.split("@grid=", 1)
+        grid = int(g)
     vals = {}
     for root, _, files in os.walk(directory):
         for fn in files:
@@ -449,6 +454,8 @@ def _counter_rows(directory, counter, kernel_substr):
                 continue
             with open(os.path.join(root, fn), newline="") as f:
                 for row in csv.DictReader(f):
+                    if grid is not None and int(row["Grid_Size"]) != grid:
+                        continue
                     if row["Counter_Name"] == counter and kernel_substr in row["Kernel_Name"]:
                         key = (fn, row["Dispatch_Id"])
                         vals[key] = vals.get(key, 0.0) + float(row["Counter_Value"])
