@@ -38,7 +38,8 @@ struct DmaB {
     static constexpr int SQ = C * ZQ::LD, SV = C * ZV::LD;  // elements of one q' (k') and one v tile
     static constexpr int BUF = 2 * SQ + SV;                 // one step: sQ, sK, sV
     static constexpr int LDP = C + 8;                       // P rows (query) of 32 keys
-    static constexpr int LDS_BYTES = (NBUF * BUF + C * LDP) * 2;
+    static constexpr int SPB = C * LDP;                     // one P buffer (two: a step's P is read in the next)
+    static constexpr int LDS_BYTES = (NBUF * BUF + 2 * SPB) * 2;
     // LDS loads: a tile is C rows of LD / 8 16-byte slots (pads included); one wave instruction fills 64
     // consecutive slots, and instruction i of a tile belongs to wave i % NW.
     static constexpr int NIQ = SQ / 8 / 64, NIV = SV / 8 / 64;
@@ -517,14 +518,27 @@ __global__ __launch_bounds__(512, 1) void chunk_dma_full_bf16(FwdArgs a) {
                                                            ((REV ? 1 - x : x) * 16 * rsv + j * 16) * 4, kOutAux);
         }
     };
-    // Step c: wait for its rows, barrier (every wave is past step c - 1, so the buffer it used and sP are free),
-    // the loads of step c + NBUF - 1 into that buffer, products, P of the score tiles to LDS, barrier, P.V and the
-    // output stores.
+    // The P.V product of a step and its output stores run at the start of the next step, after its barrier, which
+    // also makes the step's P visible: one barrier per step, and the stores go out ahead of the next loads.
+    f32x4_t Op[4];    // the cross term of the previous step, scaled, awaiting its P.V product
+    bf16x8_t fvp[2];  // V^T fragments of the previous step (A of P.V)
+    auto finish = [&](int c) __attribute__((always_inline)) {
+        const uint16_t* sPc = sP + (c & 1) * F::SPB;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int x = 0; x < 2; ++x) mfma(Op[x * 2 + j], fvp[j], frag_p(sPc + x * 16 * F::LDP, F::LDP, 0, lane));
+        store_out(c, Op);
+    };
+    // Step c: wait for its rows, barrier (every wave is past step c - 1: the buffer it used is free, and so is the
+    // P buffer of step c - 2), P.V and the output stores of step c - 1, the loads of step c + NBUF - 1 into the
+    // free buffer, products, P of the score tiles to LDS.
     int buf = 0;
     for (int c = 0; c < nchunks; ++c) {
         if (-(T + (float)C) * lg > F::RESCALE_LOG2) rescale();
         wait_step();
         lds_barrier();
+        if (c > 0) finish(c - 1);
         // step c + NBUF - 1's loads into the buffer step c - 1 used, in three parts during the products below
         const Dma nd = dma_of(c + NBUF - 1, buf == 0 ? NBUF - 1 : buf - 1);
         const uint16_t* sQ = smem + buf * F::BUF;
@@ -570,19 +584,18 @@ __global__ __launch_bounds__(512, 1) void chunk_dma_full_bf16(FwdArgs a) {
             __builtin_amdgcn_sched_barrier(0);
         }
         T += (float)L;
-        if (scorer) store4(sP + (sjb * 16 + n16) * F::LDP + slb * 16 + g4, S * DmS);
-        lds_barrier();
-        // O^T = gamma^T xi (.) O^T + V^T P^T
+        if (scorer) store4(sP + (c & 1) * F::SPB + (sjb * 16 + n16) * F::LDP + slb * 16 + g4, S * DmS);
+        // O^T = gamma^T xi (.) O^T + V^T P^T: the first term now, the second at the next step's start (the V rows
+        // are read now: the buffer takes new loads in the next step)
 #pragma unroll
-        for (int x = 0; x < 4; ++x) O[x] *= gT * Xi[x / 2];
+        for (int x = 0; x < 4; ++x) Op[x] = O[x] * (gT * Xi[x / 2]);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const bf16x8_t fv = frag_trps<F::DVT>(sV, 0, (w * 2 + j) * 16, lv_t);
-#pragma unroll
-            for (int x = 0; x < 2; ++x) mfma(O[x * 2 + j], fv, frag_p(sP + x * 16 * F::LDP, F::LDP, 0, lane));
-        }
-        store_out(c, O);
+        for (int j = 0; j < 2; ++j) fvp[j] = frag_trps<F::DVT>(sV, 0, (w * 2 + j) * 16, lv_t);
         buf = buf == NBUF - 1 ? 0 : buf + 1;
+    }
+    if (nchunks > 0) {
+        lds_barrier();
+        finish(nchunks - 1);
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the loads past the end have landed before the waves end
 
