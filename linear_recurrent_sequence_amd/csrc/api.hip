@@ -426,14 +426,15 @@ ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o,
         const fwd_kernel_t fn_pre = onchip ? (rev ? ck.seg_rev : ck.seg_pre)
                                            : (rev && !ck.split_local ? ck.fused_rev : ck.fused_pre);
         // The reversed run and the rotation of the outputs exist for the on-chip kernel, the reversed run and q, k
-        // taken from wider heads for the three-launch kernels, and the reversed run for the single-pass kernels
-        // that have one (whole steps only when reversed); all without input rotation, state or epilogue.
+        // taken from wider heads for the three-launch kernels, and the reversed run and (chunk_fused_bf16) the
+        // rotation of the outputs for the single-pass kernels that have them (whole steps only when reversed); all
+        // without input rotation, state or epilogue.
         if (rev || out_theta || qk_din) {
             const bool plain = !theta && !state_in && !state_out && !epi;
             const bool seg_ok = onchip && !qk_din && (!rev || ck.seg_rev);
             const bool split_ok = ck.split_local && !onchip && !out_theta && (!rev || N % kDmaStep == 0);
-            const bool fused_ok = !ck.split_local && !onchip && rev && ck.fused_rev && !out_theta && !qk_din &&
-                                  N % ck.rev_step == 0;
+            const bool fused_ok = !ck.split_local && !onchip && !qk_din &&
+                                  (!rev || (ck.fused_rev && N % ck.rev_step == 0)) && (!out_theta || ck.fused_orot);
             if (!plain || !(seg_ok || split_ok || fused_ok))
                 return fail(RET_ERR_UNSUPPORTED, "reversed, output-rotated or column-block chunkwise run: not "
                                                  "available for this shape");
@@ -554,6 +555,7 @@ ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o,
 //   and reversed) in the input dtype, and the fp32 outputs.
 struct BwdLayout {
     bool direct, inplace;
+    bool own_out;  // in place with one block, on single-pass kernels that write dq and dk themselves
     int variant;  // kernel variant of the retentions (the wide-head kernels' where the in-place path takes them)
     int nb, wb;  // d_v blocks of width wb for the retentions that contract over d_v (nb = 2 when d_v is wider
                  // than their kernels' d_k; dq' and dk' are then sums of two retentions)
@@ -603,6 +605,15 @@ bool bwd_layout(int B, int N, int H, int dk, int dv, int chunk, ret_dtype_t in_d
         L->variant = tries[t];
         L->chain_bytes = qa.chain_bytes > qb.chain_bytes ? qa.chain_bytes : qb.chain_bytes;
     }
+    // With one block of d_v, retentions on the single-pass kernels write dq and dk themselves, turned back by the
+    // transpose rotation in their kernels: no fp32 outputs in the workspace and no final reordering launch.
+    if (L->inplace && L->nb == 1) {
+        Opts ot = op;
+        ot.variant = L->variant;
+        ChunkKernels ko;
+        L->own_out = pick_chunk(in_dt, L->wb, dk, chunk, &ko, ot) && !ko.split_local && ko.fused_rev &&
+                     N % ko.rev_step == 0 && (!rotate || ko.fused_orot);
+    }
     size_t off = up(L->chain_bytes > 256 ? L->chain_bytes : 256);
     if (L->direct || L->inplace) {
         if (rotate) {
@@ -610,7 +621,7 @@ bool bwd_layout(int B, int N, int H, int dk, int dv, int chunk, ret_dtype_t in_d
             L->kp = L->qp + up(nk * 2);
             off = L->kp + up(nk * 2);
         }
-        if (L->inplace) {  // dq' of each block, then dk' of each block (one after another: one launch may write both)
+        if (L->inplace && !L->own_out) {  // dq' of each block, then dk' of each block (one launch may write both)
             for (int i = 0; i < L->nb; ++i, off += up(nk * 4)) L->g1b[i] = off;
             for (int i = 0; i < L->nb; ++i, off += up(nk * 4)) L->g3b[i] = off;
         }
@@ -1001,6 +1012,11 @@ ret_status_t ret_chunkwise_bwd_saved_ex(const void* q, const void* k, const void
             tc.done();
             if ((st = launch_status("ret_chunk_dma_scan")) != RET_OK) return st;
             if ((st = blocks_from_t(dout, v, Kp, ws + L.g1b[0], false, slots)) != RET_OK) return st;
+        } else if (L.own_out) {
+            if ((st = chunkwise_run(dout, v, Kp, dq, B, N, H, wb, dk, RET_BF16, out_dt, gamma, nullptr, pos0, chunk,
+                                    nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, ov, false,
+                                    theta)) != RET_OK)
+                return st;
         } else {
             for (int i = 0; i < L.nb; ++i)
                 if ((st = chunkwise_run(dout, v, Kp, ws + L.g1b[i], B, N, H, wb, dk, RET_BF16, RET_F32, gamma, nullptr,
@@ -1016,6 +1032,12 @@ ret_status_t ret_chunkwise_bwd_saved_ex(const void* q, const void* k, const void
             return st;
         if (share) {
             if ((st = blocks_from_t(v, dout, Qp, ws + L.g3b[0], true, slots)) != RET_OK) return st;
+        } else if (L.own_out) {
+            if (reshaped && (st = chain_meta_zero(in_dt, B, N, H, wb, dk, chunk, chain, L.chain_bytes, s, ov)) != RET_OK)
+                return st;
+            // dq and dk leave their kernels finished: nothing to reorder
+            return chunkwise_run(v, dout, Qp, dk_out, B, N, H, wb, dk, RET_BF16, out_dt, gamma, nullptr, pos0, chunk,
+                                 nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, ov, true, theta);
         } else {
             if (reshaped && (st = chain_meta_zero(in_dt, B, N, H, wb, dk, chunk, chain, L.chain_bytes, s, ov)) != RET_OK)
                 return st;

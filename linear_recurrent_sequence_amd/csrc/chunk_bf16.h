@@ -841,7 +841,55 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT, NDW>::OCC)) void ch
     // query x*16 + n16 in d_v block w * NDW + j (REV: memory row (NB-1-x)*16 + 15 - n16 of the chunk's rows). Rows
     // past the sequence fall outside the buffer range and are dropped.
     const int o_voff = ((REV ? 15 - n16 : n16) * rsv + w * NDW * 16 + g4) * osz;
-    auto store_out = [&](int c, const f32x4_t* O) __attribute__((always_inline)) {
+    // a.orot (PRE only, for the gradients): every output row turned back by the transpose of the rotation at its
+    // position. The lane's values of tile (x, j) are columns dv0 + (w NDW + j) 16 + g4 .. + 3 (two pairs) of run
+    // row seg_t0 + c C + 16 x + n16, at position pos0 + that row (REV: pos0 + N - 1 - that row). The factors of a
+    // chunk's first tile are evaluated exactly every 8 chunks and otherwise carried from the chunk before by angle
+    // addition; those of the later tiles follow by steps of 16 rows.
+    float oc[NDW][2], os[NDW][2], o16c[NDW][2], o16s[NDW][2], oCc[NDW][2], oCs[NDW][2];
+    if constexpr (PRE) {
+        if (a.orot) {
+#pragma unroll
+            for (int j = 0; j < NDW; ++j)
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const double th = a.theta[(dv0 + (w * NDW + j) * 16 + g4) / 2 + e];
+                    rot_cs(REV ? -16 : 16, th, &o16c[j][e], &o16s[j][e]);
+                    rot_cs(REV ? -C : C, th, &oCc[j][e], &oCs[j][e]);
+                }
+        }
+    }
+    auto out_rotate = [&](int c, f32x4_t* O) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < NDW; ++j)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                if ((c & 7) == 0) {
+                    const long long r = seg_t0 + (long long)c * C + n16;
+                    rot_cs(a.pos0 + (REV ? (long long)aN - 1 - r : r), a.theta[(dv0 + (w * NDW + j) * 16 + g4) / 2 + e],
+                           &oc[j][e], &os[j][e]);
+                } else {
+                    const float nc = oc[j][e] * oCc[j][e] - os[j][e] * oCs[j][e];
+                    os[j][e] = os[j][e] * oCc[j][e] + oc[j][e] * oCs[j][e];
+                    oc[j][e] = nc;
+                }
+                float cx = oc[j][e], sx = os[j][e];
+#pragma unroll
+                for (int x = 0; x < F::NB; ++x) {
+                    const float x0 = O[x * NDW + j][2 * e], x1 = O[x * NDW + j][2 * e + 1];
+                    O[x * NDW + j][2 * e] = x0 * cx + x1 * sx;
+                    O[x * NDW + j][2 * e + 1] = x1 * cx - x0 * sx;
+                    if (x + 1 < F::NB) {
+                        const float nc = cx * o16c[j][e] - sx * o16s[j][e];
+                        sx = sx * o16c[j][e] + cx * o16s[j][e];
+                        cx = nc;
+                    }
+                }
+            }
+    };
+    auto store_out = [&](int c, f32x4_t* O) __attribute__((always_inline)) {
+        if constexpr (PRE)
+            if (a.orot) out_rotate(c, O);
         const int L = min(C, seg_n - c * C);
         const rsrc_t ro = bytes_rsrc(oh + crow(c) * rsv * osz, ((L - 1) * rsv + DVT) * osz);
         if (a.out_bf16) {
@@ -1047,6 +1095,7 @@ ChunkKernels chunk_entry_bf16() {
     }
     k.dvt = DVT;
     k.threads = NT;
+    k.fused_orot = 1;
     // d_v tiles of 128 run one workgroup per CU: one workgroup per CU in total measured fastest (fewer, longer
     // segments); 256-thread ones with 16-column waves two per CU, with two rounds of them.
     k.target_wgs = NT * NDW >= 512 ? 256 : 1024;

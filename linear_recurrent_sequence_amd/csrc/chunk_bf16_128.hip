@@ -12,6 +12,7 @@ ChunkKernels chunk_entry_wide128() {
     ChunkKernels k = chunk_entry_bf16<128, C, 512>();  // (d_v tiles of 128 for both kernels of the set)
     k.fused_pre = chunk_wide_get(128);
     k.fused_rev = chunk_wide_get(128, true);
+    k.fused_orot = 0;
     k.rev_step = kWideStep;
     k.threads_pre = kWideThreads;
     k.pre_always = 1;

@@ -20,6 +20,7 @@ ChunkKernels chunk_entry_wide256() {
     ChunkKernels k = chunk_entry_bf16<256, C, 512>();
     k.fused_pre = chunk_wide_get(256);
     k.fused_rev = chunk_wide_get(256, true);
+    k.fused_orot = 0;
     k.rev_step = kWideStep;
     k.threads_pre = kWideThreads;
     k.pre_always = 1;
@@ -34,6 +35,7 @@ ChunkKernels chunk_entry_dma256() {
     DmaKernels d;
     chunk_dma_get(256, &d);
     k.fused = k.fused_pre = d.full;
+    k.fused_orot = 0;
     k.split_local = d.local;
     k.split_scan = d.scan;
     k.split_local_rev = d.local_rev;

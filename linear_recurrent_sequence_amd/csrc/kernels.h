@@ -997,6 +997,8 @@ struct ChunkKernels {
     // the single-pass kernels run chained segments as three launches instead (FwdArgs::split: the local passes,
     // slot_scan_kernel, the full passes), with the segment states in the workspace after its first kChainMeta bytes
     int fused_split;
+    // fused_pre and fused_rev can turn their output rows back by the transpose rotation (FwdArgs::orot)
+    int fused_orot;
 };
 struct ParKernel {
     fwd_kernel_t fn;

@@ -73,27 +73,29 @@ def test_gradients_small(R, case):
 
 
 GRAD_IN_PLACE = [
-    # B, N, H, dk, dv, chunk, rotate, pos0, out dtype, kernel, several segments. N a multiple of 32: every
-    # retention runs over the reversed sequence in place on the kernel named, with no reordered copies. d_k 256 with
-    # d_v a multiple of 256: the three-launch kernels, which also read the d_v blocks of dO and V in place, and with
-    # several segments dq' and dk' of every block each in one launch from transposed states (of a local pass and
-    # scan over K' and V, and of the dv retention); otherwise (one block) the single-pass kernels' reversed
-    # instances: the streaming kernel with d_v tiles of 128 for d_k = 128, the wide-head kernel for d_k = 256
-    (1, 640, 2, 256, 512, 128, True, 5, "bf16", "ret_chunk_dma", True),   # 5 segments, two d_v blocks
-    (2, 512, 2, 256, 256, 64, True, 0, "f32", "ret_chunk_dma", True),     # one block
-    (1, 1024, 1, 256, 512, 32, False, 0, "f32", "ret_chunk_dma", True),   # no rotation, chunk 32
-    (1, 32, 2, 256, 512, 128, True, 9, "f32", "ret_chunk_dma", False),    # one step
-    (1, 640, 2, 128, 128, 128, True, 5, "bf16", "ret_chunk_fused", True),  # the long-sequence head
-    (1, 512, 2, 128, 256, 64, True, 0, "f32", "ret_chunk_fused", True),    # d_k < d_v (d_k 256 runs: wide)
-    (2, 384, 1, 256, 128, 32, False, 0, "f32", "ret_chunk_fused", True),   # d_k > d_v, chunk 32
+    # B, N, H, dk, dv, chunk, rotate, pos0, out dtype, kernel, several segments, final reordering launches. N a
+    # multiple of 32: every retention runs over the reversed sequence in place on the kernel named, with no
+    # reordered copies. d_k 256 with d_v a multiple of 256: the three-launch kernels, which also read the d_v blocks
+    # of dO and V in place, and with several segments dq' and dk' of every block each in one launch from transposed
+    # states (of a local pass and scan over K' and V, and of the dv retention); otherwise (one block) the
+    # single-pass kernels' reversed instances: the streaming kernel with d_v tiles of 128 for d_k = 128, the
+    # wide-head kernel for d_k = 256. Where the dq' and dk' retentions run on the streaming kernel, it writes dq and
+    # dk itself, turned back by the transpose rotation: no final reordering launch.
+    (1, 640, 2, 256, 512, 128, True, 5, "bf16", "ret_chunk_dma", True, 1),   # 5 segments, two d_v blocks
+    (2, 512, 2, 256, 256, 64, True, 0, "f32", "ret_chunk_dma", True, 1),     # one block
+    (1, 1024, 1, 256, 512, 32, False, 0, "f32", "ret_chunk_dma", True, 1),   # no rotation, chunk 32
+    (1, 32, 2, 256, 512, 128, True, 9, "f32", "ret_chunk_dma", False, 1),    # one step
+    (1, 640, 2, 128, 128, 128, True, 5, "bf16", "ret_chunk_fused", True, 0),  # the long-sequence head
+    (1, 512, 2, 128, 256, 64, True, 0, "f32", "ret_chunk_fused", True, 1),    # d_k < d_v (d_k 256 runs: wide)
+    (2, 384, 1, 256, 128, 32, False, 0, "f32", "ret_chunk_fused", True, 0),   # d_k > d_v, chunk 32
 ]
 
 
 @pytest.mark.parametrize("case", GRAD_IN_PLACE, ids=lambda c: "B%d-N%d-H%d-dk%d-dv%d-C%d" % c[:6] + "-" + c[8])
 def test_gradients_in_place(R, case):
     """Gradients with no reordered copies: the only reordering launch left is the one that sums the d_v blocks'
-    dq' and dk' and turns them back by the transpose rotation."""
-    B, N, H, dk, dv, chunk, rot, pos0, out_dt, kernel, multi = case
+    dq' and dk' and turns them back by the transpose rotation, and none where the retentions' kernel does that."""
+    B, N, H, dk, dv, chunk, rot, pos0, out_dt, kernel, multi, nperm = case
     w = W.Workload("grad", B=B, N=N, H=H, dk=dk, dv=dv, dtype="bf16", scale=float(np.sqrt(dk)), seed=61 + N,
                    chunk=chunk, rotate=rot)
     print_case("gradients-in-place", kernel, w)
@@ -102,7 +104,7 @@ def test_gradients_in_place(R, case):
     ref = oracle.grad(q, k, v, do, w.gamma, theta=w.theta, pos0=pos0)
     timer = R.Timer()
     got = _gpu_grad(R, q, k, v, do, w.gamma, chunk, w.theta, pos0, out_dt, options={"timer": timer})
-    assert timer.query("ret_permute_rotate")[1] == 1
+    assert timer.query("ret_permute_rotate")[1] == nperm
     assert timer.query("ret_rotate_qk")[1] == (1 if rot else 0)
     if kernel == "ret_chunk_dma":
         nb = dv // 256
@@ -114,6 +116,26 @@ def test_gradients_in_place(R, case):
     else:
         assert timer.query(kernel)[1] >= 1
         assert timer.query("ret_chunk_fused")[1] + timer.query("ret_chunk_wide")[1] == 3
+    timer.close()
+    _check(got, ref, tol("bf16"))
+
+
+@pytest.mark.parametrize("out_dt", ["bf16", "f32"])
+def test_gradients_rotated_by_their_kernel(R, out_dt):
+    """d_k = d_v = 128 in two segments of 2048 tokens (32 chunks of 64 each, the rotation factors carried from chunk
+    to chunk and evaluated exactly every 8) at positions past 70000: the streaming kernel turns dq and dk back by
+    the transpose rotation itself, with no reordering launch."""
+    w = W.Workload("grad", B=1, N=4096, H=2, dk=128, dv=128, dtype="bf16", scale=float(np.sqrt(128)), seed=73,
+                   chunk=128, rotate=True)
+    print_case("gradients-own-outputs", out_dt, w)
+    q, k, v, rng = W.make_qkv(w)
+    do = W.make_dout(w, rng)
+    ref = oracle.grad(q, k, v, do, w.gamma, theta=w.theta, pos0=70001)
+    timer = R.Timer()
+    got = _gpu_grad(R, q, k, v, do, w.gamma, w.chunk, w.theta, 70001, out_dt,
+                    options={"timer": timer, "segments": 2})
+    assert timer.query("ret_permute_rotate")[1] == 0
+    assert timer.query("ret_chunk_fused")[1] == 3
     timer.close()
     _check(got, ref, tol("bf16"))
 
