@@ -549,8 +549,9 @@ ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o,
 // - when both reversed retentions run on the on-chip kernel's reversed traversal (direct, bf16 only): Q' and K'
 //   (bf16, only with rotation);
 // - when every retention runs in place over reversed rows and d_v blocks (inplace: the three-launch kernels, or
-//   with one block the wide-head kernels; bf16, N a multiple of their 32-token step): Q' and K' (only with
-//   rotation), then the fp32 dq' of each d_v block and the fp32 dk' of each block, each set contiguous;
+//   with one block the single-pass kernels' reversed instances; bf16, N a multiple of their step): Q' and K' (only
+//   with rotation), then (room for fp32, held in the gradients' precision) the dq' of each d_v block and the dk'
+//   of each block, each set contiguous; none where the streaming kernel writes dq and dk itself (own_out);
 // - otherwise the reordered inputs (K', K' reversed, Q' reversed, and V and dO reversed, or their blocks forward
 //   and reversed) in the input dtype, and the fp32 outputs.
 struct BwdLayout {
@@ -969,18 +970,22 @@ ret_status_t ret_chunkwise_bwd_saved_ex(const void* q, const void* k, const void
             if ((st = launch_status("ret_rotate_qk")) != RET_OK) return st;
         }
         float* const slots = (float*)((char*)chain + kChainMeta);  // segment states of the (d_k, d_v) runs
+        // The blocks' dq' and dk' (summed and turned back by the last launch) are kept in the gradients' own
+        // precision: bf16 for bf16 gradients, which halves what they write and the last launch reads.
+        const ret_dtype_t pdt = ob ? RET_BF16 : RET_F32;
+        const int psz = ob ? 2 : 4;
         // every block's dq' (rev = false) or dk' (rev = true) in one full-pass launch from the transposed states
         auto blocks_from_t = [&](const void* qq, const void* kk, const void* vv, void* out, bool rev,
                                  const float* states) {
             FwdArgs A;
-            fill_fwd(A, qq, kk, vv, out, B, N, H, wb, dk, RET_F32, gamma, nullptr, 0);
+            fill_fwd(A, qq, kk, vv, out, B, N, H, wb, dk, pdt, gamma, nullptr, 0);
             A.qr = const_cast<void*>(qq);
             A.kr = const_cast<void*>(kk);
             A.nseg = plan_sq.nseg;
             A.seg_len = plan_sq.seg_len;
             A.qk_din = din;
             A.qk_blocks = L.nb;
-            A.o_block = L.nb > 1 ? (long long)(rev ? L.g3b[1] - L.g3b[0] : L.g1b[1] - L.g1b[0]) / 4 : 0;
+            A.o_block = L.nb > 1 ? (long long)(rev ? L.g3b[1] - L.g3b[0] : L.g1b[1] - L.g1b[0]) / psz : 0;
             A.ws_t = states;
             const unsigned grid = (unsigned)((long long)B * H * L.nb * plan_sq.nseg);
             LaunchTimer tm(ck_bl.pre_name, s, ov);
@@ -1019,7 +1024,7 @@ ret_status_t ret_chunkwise_bwd_saved_ex(const void* q, const void* k, const void
                 return st;
         } else {
             for (int i = 0; i < L.nb; ++i)
-                if ((st = chunkwise_run(dout, v, Kp, ws + L.g1b[i], B, N, H, wb, dk, RET_BF16, RET_F32, gamma, nullptr,
+                if ((st = chunkwise_run(dout, v, Kp, ws + L.g1b[i], B, N, H, wb, dk, RET_BF16, pdt, gamma, nullptr,
                                         0, chunk, nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, ov,
                                         false, nullptr, din, i * wb)) != RET_OK)
                     return st;
@@ -1042,15 +1047,15 @@ ret_status_t ret_chunkwise_bwd_saved_ex(const void* q, const void* k, const void
             if (reshaped && (st = chain_meta_zero(in_dt, B, N, H, wb, dk, chunk, chain, L.chain_bytes, s, ov)) != RET_OK)
                 return st;
             for (int i = 0; i < L.nb; ++i)
-                if ((st = chunkwise_run(v, dout, Qp, ws + L.g3b[i], B, N, H, wb, dk, RET_BF16, RET_F32, gamma, nullptr,
+                if ((st = chunkwise_run(v, dout, Qp, ws + L.g3b[i], B, N, H, wb, dk, RET_BF16, pdt, gamma, nullptr,
                                         0, chunk, nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, ov,
                                         true, nullptr, din, i * wb)) != RET_OK)
                     return st;
         }
         const bool two = L.nb > 1;
         const PermJob post[2] = {
-            {ws + L.g1b[0], {dq, nullptr}, dk, -1, 0, {0, 0}, 0, ob, two ? ws + L.g1b[1] : nullptr},
-            {ws + L.g3b[0], {dk_out, nullptr}, dk, -1, 0, {0, 0}, 0, ob, two ? ws + L.g3b[1] : nullptr},
+            {ws + L.g1b[0], {dq, nullptr}, dk, -1, 0, {0, 0}, ob, ob, two ? ws + L.g1b[1] : nullptr},
+            {ws + L.g3b[0], {dk_out, nullptr}, dk, -1, 0, {0, 0}, ob, ob, two ? ws + L.g3b[1] : nullptr},
         };
         return permute(post, 2, B, N, H, theta, pos0, s, op);
     }
