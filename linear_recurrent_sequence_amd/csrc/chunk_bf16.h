@@ -601,11 +601,14 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT, NDW>::OCC)) void ch
         const int lk_t = ZK::lane_trp(lane);
         const int krow = tid / TK::SPR, kseg = tid % TK::SPR;
         const int koff = (krow * rsk + kseg * 8) * 2;
-        // Two register buffers: the loads of chunk c+2 go out as soon as chunk c is staged.
+        // The chunks are taken last first: step s adds chunk n-1-s (n chunks) scaled by gamma^(sC), its decay to
+        // the segment's end, so the state is never rescaled and the sum is the same (measured 62 -> 56-57 us per
+        // call for the local passes of long-sequence). Two register buffers: the loads of step s+2 go out as soon
+        // as step s is staged.
         u32x4_t lk[2][TK::NP], lv[2][TV::NP];
-        auto lissue = [&](int c, auto parc) __attribute__((always_inline)) {
+        auto lissue = [&](int st, auto parc) __attribute__((always_inline)) {
             constexpr int par = decltype(parc)::value;
-            const long long tc = crow(c);
+            const long long tc = crow(nchunks - 1 - st);
             const rsrc_t rk = bytes_rsrc(kh + tc * rsk, ((C - 1) * rsk + DK) * 2);
             const rsrc_t rv = bytes_rsrc(vh + tc * rsv, ((C - 1) * rsv + DVT) * 2);
 #pragma unroll
@@ -620,13 +623,19 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT, NDW>::OCC)) void ch
         for (int p = 0; p < TK::NP; ++p) zl[p] = gpow(lg, (float)(C - 1 - lrow(krow + p * TK::RP)));
 #pragma unroll
         for (int p = 0; p < TV::NP; ++p) zlv[p] = gpow(lg, (float)(C - 1 - lrow(vrow + p * TV::RP)));
-        const float gC = gpow(lg, (float)C);
-        SliceRot<C, TK::RP, TK::NP> lrot;  // identity factors without rotation (theta all zero)
-        if constexpr (!PRE) lrot.init_steps(a.theta, kseg * 4);
-        // One chunk of the local pass (segments before the last hold whole chunks only).
-        auto lchunk = [&](int c, auto parc) __attribute__((always_inline)) {
+        // rotation factors of the thread's rows: the step between passes, and from the last pass of a chunk back to
+        // the first of the chunk before it (identity factors without rotation: theta all zero)
+        Rot4 lrcur, lrpass, lrback;
+        if constexpr (!PRE) {
+            lrpass.eval(TK::RP, a.theta, kseg * 4);
+            lrback.eval(-(C + (TK::NP - 1) * TK::RP), a.theta, kseg * 4);
+        }
+        // Step st of the local pass: chunk c = n-1-st (segments before the last hold whole chunks only).
+        auto lchunk = [&](int st, auto parc) __attribute__((always_inline)) {
             constexpr int par = decltype(parc)::value;
-            if (c > 0) __syncthreads();
+            const int c = nchunks - 1 - st;
+            const float gs = gpow(lg, (float)(st * C));  // decay of the chunk's end to the segment's end
+            if (st > 0) __syncthreads();
             if constexpr (PRE) {  // K' as staged; zeta on V
 #pragma unroll
                 for (int p = 0; p < TK::NP; ++p)
@@ -636,32 +645,32 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT, NDW>::OCC)) void ch
                     if (TV::live(vrow, p)) {
                         float vf[8];
                         unpack8(lv[par][p], vf);
+                        const float z = zlv[p] * gs;
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) vf[e] *= zlv[p];
+                        for (int e = 0; e < 8; ++e) vf[e] *= z;
                         lds_store16(lV + ZV::off(lrow(vrow + p * TV::RP), vseg * 8), pack8(vf));
                     }
             } else {
-                if ((c & 7) == 0) lrot.cur.eval(a.pos0 + seg_t0 + (long long)c * C + krow, a.theta, kseg * 4);
+                if ((st & 7) == 0) lrcur.eval(a.pos0 + seg_t0 + (long long)c * C + krow, a.theta, kseg * 4);
 #pragma unroll
                 for (int p = 0; p < TK::NP; ++p)
                     if (TK::live(krow, p)) {
                         float kf[8];
                         unpack8(lk[par][p], kf);
-                        lrot.cur.apply(kf);
-                        if (p + 1 < TK::NP) lrot.cur.turn(lrot.pass);
+                        lrcur.apply(kf);
+                        if (p + 1 < TK::NP) lrcur.turn(lrpass);
+                        const float z = zl[p] * gs;
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) kf[e] *= zl[p];
+                        for (int e = 0; e < 8; ++e) kf[e] *= z;
                         lds_store16(lK + ZK::off(krow + p * TK::RP, kseg * 8), pack8(kf));
                     }
-                lrot.next_chunk();
+                lrcur.turn(lrback);
 #pragma unroll
                 for (int p = 0; p < TV::NP; ++p)
                     if (TV::live(vrow, p)) lds_store16(lV + ZV::off(vrow + p * TV::RP, vseg * 8), lv[par][p]);
             }
-            if (c + 2 < nchunks) lissue(c + 2, parc);
+            if (st + 2 < nchunks) lissue(st + 2, parc);
             __syncthreads();
-#pragma unroll
-            for (int x = 0; x < NR; ++x) R[x] *= gC;
 #pragma unroll
             for (int f = 0; f < C / 32; ++f) {
                 bf16x8_t fb[NDW];
@@ -675,9 +684,15 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT, NDW>::OCC)) void ch
                 }
             }
         };
-        for (int c = 0; c < nchunks; c += 2) {
-            lchunk(c, std::integral_constant<int, 0>{});
-            if (c + 1 < nchunks) lchunk(c + 1, std::integral_constant<int, 1>{});
+        // (chained runs: the first segment's local pass starts from state_in, decayed here to the segment's end)
+        if (chained && seg == 0 && a.state_in) {
+            const float gL = gpow(lg, (float)(nchunks * C));
+#pragma unroll
+            for (int x = 0; x < NR; ++x) R[x] *= gL;
+        }
+        for (int st = 0; st < nchunks; st += 2) {
+            lchunk(st, std::integral_constant<int, 0>{});
+            if (st + 1 < nchunks) lchunk(st + 1, std::integral_constant<int, 1>{});
         }
         __syncthreads();  // the local tiles are dead before the full pass reuses the LDS
         if (split == 1) {  // the segment's state, for the scan
