@@ -381,7 +381,7 @@ ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o,
                            int64_t pos0, int chunk, const float* state_in, float* state_out, void* workspace,
                            size_t workspace_bytes, void* stream, const EpiRequest* epi, bool* fused,
                            const Opts& op, bool rev = false, const double* out_theta = nullptr, int qk_din = 0,
-                           int qk_col0 = 0) {
+                           int qk_col0 = 0, bool v_rot = false) {
     if (fused) *fused = false;
     ret_status_t st = check_common(q, k, v, o, B, N, H, dk, dv, in_dt, out_dt, gamma, theta);
     if (st != RET_OK) return st;
@@ -422,25 +422,30 @@ ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o,
         const bool onchip = plan_onchip(ck, plan, op);
         // Staging copies rows instead of rotating them when there is no rotation, or when q and k are rotated
         // once up front (several d_v tiles stage the same rows).
-        fwd_kernel_t fn = onchip ? ck.seg : ck.fused;
+        // (reversed runs with rotation: the reversed instance that rotates q and k while staging)
+        const bool rot_rev = rev && theta && ck.fused_rot_rev && !onchip && plan.rot_bytes == 0 && !qk_din &&
+                             !out_theta && !v_rot && N % ck.rev_step == 0;
+        fwd_kernel_t fn = onchip ? ck.seg : rot_rev ? ck.fused_rot_rev : ck.fused;
         const fwd_kernel_t fn_pre = onchip ? (rev ? ck.seg_rev : ck.seg_pre)
                                            : (rev && !ck.split_local ? ck.fused_rev : ck.fused_pre);
         // The reversed run and the rotation of the outputs exist for the on-chip kernel, the reversed run and q, k
         // taken from wider heads for the three-launch kernels, and the reversed run and (chunk_fused_bf16) the
         // rotation of the outputs for the single-pass kernels that have them (whole steps only when reversed); all
         // without input rotation, state or epilogue.
-        if (rev || out_theta || qk_din) {
-            const bool plain = !theta && !state_in && !state_out && !epi;
-            const bool seg_ok = onchip && !qk_din && (!rev || ck.seg_rev);
+        if (rev || out_theta || qk_din || v_rot) {
+            const bool plain = (!theta || rot_rev) && !state_in && !state_out && !epi;
+            const bool seg_ok = onchip && !qk_din && (!rev || ck.seg_rev) && !v_rot;
             const bool split_ok = ck.split_local && !onchip && !out_theta && (!rev || N % kDmaStep == 0);
             const bool fused_ok = !ck.split_local && !onchip && !qk_din &&
-                                  (!rev || (ck.fused_rev && N % ck.rev_step == 0)) && (!out_theta || ck.fused_orot);
+                                  (!rev || (ck.fused_rev && N % ck.rev_step == 0)) &&
+                                  (!(out_theta || v_rot) || ck.fused_orot) && (!v_rot || out_theta);
             if (!plain || !(seg_ok || split_ok || fused_ok))
                 return fail(RET_ERR_UNSUPPORTED, "reversed, output-rotated or column-block chunkwise run: not "
                                                  "available for this shape");
         }
         if (out_theta) {
             A.orot = 1;
+            A.vrot = v_rot;  // (v has the outputs' width: one rotation for both)
             for (int i = 0; i < dv / 2; ++i) A.theta[i] = out_theta[i];
         }
         if (!theta) {
@@ -556,7 +561,8 @@ ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o,
 //   and reversed) in the input dtype, and the fp32 outputs.
 struct BwdLayout {
     bool direct, inplace;
-    bool own_out;  // in place with one block, on single-pass kernels that write dq and dk themselves
+    bool own_out;    // in place with one block, on single-pass kernels that write dq and dk themselves
+    bool stage_rot;  // own_out, and the kernels rotate while staging: no rotated copies of q and k
     int variant;  // kernel variant of the retentions (the wide-head kernels' where the in-place path takes them)
     int nb, wb;  // d_v blocks of width wb for the retentions that contract over d_v (nb = 2 when d_v is wider
                  // than their kernels' d_k; dq' and dk' are then sums of two retentions)
@@ -614,10 +620,16 @@ bool bwd_layout(int B, int N, int H, int dk, int dv, int chunk, ret_dtype_t in_d
         ChunkKernels ko;
         L->own_out = pick_chunk(in_dt, L->wb, dk, chunk, &ko, ot) && !ko.split_local && ko.fused_rev &&
                      N % ko.rev_step == 0 && (!rotate || ko.fused_orot);
+        // With rotation, the dq' and dk' runs can turn their v (K, Q) while staging, and the dv run can rotate its
+        // q and k (K, Q) while staging on its reversed rotating instance: then Q', K' are never written.
+        ChunkKernels kv;
+        L->stage_rot = L->own_out && rotate && pick_chunk(in_dt, dk, dv, chunk, &kv, ot) && !kv.split_local &&
+                       kv.fused_rot_rev && N % kv.rev_step == 0 &&
+                       !plan_onchip(kv, plan_chunk(kv, B, N, H, dk, dv, chunk, false, SIZE_MAX, ot), ot);
     }
     size_t off = up(L->chain_bytes > 256 ? L->chain_bytes : 256);
     if (L->direct || L->inplace) {
-        if (rotate) {
+        if (rotate && !L->stage_rot) {
             L->qp = off;
             L->kp = L->qp + up(nk * 2);
             off = L->kp + up(nk * 2);
@@ -953,11 +965,12 @@ ret_status_t ret_chunkwise_bwd_saved_ex(const void* q, const void* k, const void
                 (!theta || plan_f.rot_bytes > 0))
                 fws = (const char*)fwd_workspace;
         }
+        // Q', K': the forward's copies, or rotated here, or (stage_rot) q and k as given, rotated while staging
         const void *Qp = q, *Kp = k;
-        if (theta && fws) {
+        if (theta && fws && !L.stage_rot) {
             Qp = fws + plan_f.chain_bytes;
             Kp = (const char*)Qp + plan_f.rot_bytes / 2;
-        } else if (theta) {
+        } else if (theta && !L.stage_rot) {
             FwdArgs A;
             fill_fwd(A, q, k, v, nullptr, B, N, H, dk, dv, out_dt, gamma, theta, pos0);
             A.qr = ws + L.qp;
@@ -1020,7 +1033,7 @@ ret_status_t ret_chunkwise_bwd_saved_ex(const void* q, const void* k, const void
         } else if (L.own_out) {
             if ((st = chunkwise_run(dout, v, Kp, dq, B, N, H, wb, dk, RET_BF16, out_dt, gamma, nullptr, pos0, chunk,
                                     nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, ov, false,
-                                    theta)) != RET_OK)
+                                    theta, 0, 0, L.stage_rot)) != RET_OK)
                 return st;
         } else {
             for (int i = 0; i < L.nb; ++i)
@@ -1032,8 +1045,9 @@ ret_status_t ret_chunkwise_bwd_saved_ex(const void* q, const void* k, const void
         const bool reshaped = wb != dk || dk != dv;  // the (d_k, d_v) of the runs differ
         if (reshaped && (st = chain_meta_zero(in_dt, B, N, H, dk, dv, chunk, chain, L.chain_bytes, s, ov)) != RET_OK)
             return st;
-        if ((st = chunkwise_run(Kp, Qp, dout, dv_out, B, N, H, dk, dv, RET_BF16, out_dt, gamma, nullptr, 0, chunk,
-                                nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, ov, true)) != RET_OK)
+        if ((st = chunkwise_run(Kp, Qp, dout, dv_out, B, N, H, dk, dv, RET_BF16, out_dt, gamma,
+                                L.stage_rot ? theta : nullptr, L.stage_rot ? pos0 : 0, chunk, nullptr, nullptr, chain,
+                                L.chain_bytes, stream, nullptr, nullptr, ov, true)) != RET_OK)
             return st;
         if (share) {
             if ((st = blocks_from_t(v, dout, Qp, ws + L.g3b[0], true, slots)) != RET_OK) return st;
@@ -1042,7 +1056,8 @@ ret_status_t ret_chunkwise_bwd_saved_ex(const void* q, const void* k, const void
                 return st;
             // dq and dk leave their kernels finished: nothing to reorder
             return chunkwise_run(v, dout, Qp, dk_out, B, N, H, wb, dk, RET_BF16, out_dt, gamma, nullptr, pos0, chunk,
-                                 nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, ov, true, theta);
+                                 nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, ov, true, theta, 0,
+                                 0, L.stage_rot);
         } else {
             if (reshaped && (st = chain_meta_zero(in_dt, B, N, H, wb, dk, chunk, chain, L.chain_bytes, s, ov)) != RET_OK)
                 return st;

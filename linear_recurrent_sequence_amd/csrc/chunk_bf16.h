@@ -152,15 +152,16 @@ __device__ __forceinline__ void lds_store16(uint16_t* p, u32x4_t x) { *reinterpr
 
 // Per-thread rotation state of the Q/K segments of one d_k slice: the factors of the thread's row in the
 // current pass (cur), the step between passes (RP tokens) and the step from the last pass of a chunk to the
-// first of the next (C - (NP - 1) RP tokens; the same step unless the tile is partial).
-template <int C, int RP, int NP>
+// first of the next (C - (NP - 1) RP tokens; the same step unless the tile is partial). BACKW: the chunks of a
+// reversed run, each C rows before the one before it in memory (a step of -C - (NP - 1) RP).
+template <int C, int RP, int NP, bool BACKW = false>
 struct SliceRot {
     Rot4 cur, pass;
-    Rot4 wrap;  // used only for partial tiles
-    static constexpr bool SAME = C == NP * RP;
+    Rot4 wrap;  // used only for partial tiles and reversed runs
+    static constexpr bool SAME = !BACKW && C == NP * RP;
     __device__ __forceinline__ void init_steps(const double* theta, int pair0) {
         pass.eval(RP, theta, pair0);
-        if constexpr (!SAME) wrap.eval(C - (NP - 1) * RP, theta, pair0);
+        if constexpr (!SAME) wrap.eval(BACKW ? -(C + (NP - 1) * RP) : C - (NP - 1) * RP, theta, pair0);
     }
     __device__ __forceinline__ void next_chunk() {
         if constexpr (SAME) cur.turn(pass);
@@ -485,11 +486,12 @@ struct FullB {
     static_assert(KS % 32 == 0, "tiling");
 };
 
-// REV (with PRE only): the run goes over the reversed sequence in place (token n of the run is row N-1-n of q, k, v
-// and o; whole chunks only, N a multiple of C): the gradients' retentions over later tokens.
-template <int DK, int C, int DVT, bool PRE, int NT, int NDW, bool REV = false>
+// REV: the run goes over the reversed sequence in place (token n of the run is row N-1-n of q, k, v and o; whole
+// chunks only, N a multiple of C): the gradients' retentions over later tokens. Rows are rotated (q, k without
+// PRE; v with a.vrot) by the rotation at their own positions in memory. GR (with PRE): the gradients' rotations
+// of v rows (a.vrot) and of the outputs (a.orot) are compiled in.
+template <int DK, int C, int DVT, bool PRE, int NT, int NDW, bool REV = false, bool GR = false>
 __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT, NDW>::OCC)) void chunk_fused_bf16(FwdArgs a) {
-    static_assert(!REV || PRE, "reversed runs take q and k as given");
     typedef FullB<DK, C, DVT, PRE, NT, NDW> F;
     constexpr int NR = F::NKB * NDW;  // state tiles of a wave: R[x * NDW + j] = rows 16x.., d_v block w * NDW + j
     typedef typename F::TQ TQ;
@@ -623,12 +625,19 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT, NDW>::OCC)) void ch
         for (int p = 0; p < TK::NP; ++p) zl[p] = gpow(lg, (float)(C - 1 - lrow(krow + p * TK::RP)));
 #pragma unroll
         for (int p = 0; p < TV::NP; ++p) zlv[p] = gpow(lg, (float)(C - 1 - lrow(vrow + p * TV::RP)));
-        // rotation factors of the thread's rows: the step between passes, and from the last pass of a chunk back to
-        // the first of the chunk before it (identity factors without rotation: theta all zero)
+        // rotation factors of the thread's k rows (without PRE), or v rows (PRE with a.vrot): the step between
+        // passes, and from the last pass of a chunk to the first of the chunk taken next, the one before it in the
+        // run (C rows earlier in memory, or later over the reversed sequence; identity factors without rotation:
+        // theta all zero)
+        constexpr int LRP = PRE ? TV::RP : TK::RP, LNP = PRE ? TV::NP : TK::NP;
+        const int lpair0 = PRE ? (dv0 + vseg * 8) / 2 : kseg * 4;
+        const int lrow0 = PRE ? vrow : krow;
+        constexpr bool VR = PRE && GR;  // (v rotation compiled in)
+        const bool lrot_on = !PRE || (VR && a.vrot);
         Rot4 lrcur, lrpass, lrback;
-        if constexpr (!PRE) {
-            lrpass.eval(TK::RP, a.theta, kseg * 4);
-            lrback.eval(-(C + (TK::NP - 1) * TK::RP), a.theta, kseg * 4);
+        if (lrot_on) {
+            lrpass.eval(LRP, a.theta, lpair0);
+            lrback.eval(REV ? C - (LNP - 1) * LRP : -(C + (LNP - 1) * LRP), a.theta, lpair0);
         }
         // Step st of the local pass: chunk c = n-1-st (segments before the last hold whole chunks only).
         auto lchunk = [&](int st, auto parc) __attribute__((always_inline)) {
@@ -636,7 +645,8 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT, NDW>::OCC)) void ch
             const int c = nchunks - 1 - st;
             const float gs = gpow(lg, (float)(st * C));  // decay of the chunk's end to the segment's end
             if (st > 0) __syncthreads();
-            if constexpr (PRE) {  // K' as staged; zeta on V
+            if (lrot_on && (st & 7) == 0) lrcur.eval(a.pos0 + crow(c) + lrow0, a.theta, lpair0);
+            if constexpr (PRE) {  // K' as staged; zeta on V (turned by the rotation first with a.vrot)
 #pragma unroll
                 for (int p = 0; p < TK::NP; ++p)
                     if (TK::live(krow, p)) lds_store16(lK + ZK::off(lrow(krow + p * TK::RP), kseg * 8), lk[par][p]);
@@ -645,13 +655,17 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT, NDW>::OCC)) void ch
                     if (TV::live(vrow, p)) {
                         float vf[8];
                         unpack8(lv[par][p], vf);
+                        if (VR && a.vrot) {
+                            lrcur.apply(vf);
+                            if (p + 1 < TV::NP) lrcur.turn(lrpass);
+                        }
                         const float z = zlv[p] * gs;
 #pragma unroll
                         for (int e = 0; e < 8; ++e) vf[e] *= z;
                         lds_store16(lV + ZV::off(lrow(vrow + p * TV::RP), vseg * 8), pack8(vf));
                     }
+                if (VR && a.vrot) lrcur.turn(lrback);
             } else {
-                if ((st & 7) == 0) lrcur.eval(a.pos0 + seg_t0 + (long long)c * C + krow, a.theta, kseg * 4);
 #pragma unroll
                 for (int p = 0; p < TK::NP; ++p)
                     if (TK::live(krow, p)) {
@@ -662,12 +676,12 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT, NDW>::OCC)) void ch
                         const float z = zl[p] * gs;
 #pragma unroll
                         for (int e = 0; e < 8; ++e) kf[e] *= z;
-                        lds_store16(lK + ZK::off(krow + p * TK::RP, kseg * 8), pack8(kf));
+                        lds_store16(lK + ZK::off(lrow(krow + p * TK::RP), kseg * 8), pack8(kf));
                     }
                 lrcur.turn(lrback);
 #pragma unroll
                 for (int p = 0; p < TV::NP; ++p)
-                    if (TV::live(vrow, p)) lds_store16(lV + ZV::off(vrow + p * TV::RP, vseg * 8), lv[par][p]);
+                    if (TV::live(vrow, p)) lds_store16(lV + ZV::off(lrow(vrow + p * TV::RP), vseg * 8), lv[par][p]);
             }
             if (st + 2 < nchunks) lissue(st + 2, parc);
             __syncthreads();
@@ -784,11 +798,17 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT, NDW>::OCC)) void ch
     for (int p = 0; p < TV::NP; ++p) zvfull[p] = gpow(lg, (float)(C - 1 - lrow(vrow + p * TV::RP)));
     const float gC = gpow(lg, (float)C);
     // Without rotation theta is all zero and every factor is exactly (1, 0).
-    SliceRot<C, TQ::RP, TQ::NP> rot[F::NSL];
+    SliceRot<C, TQ::RP, TQ::NP, REV> rot[F::NSL];
     if constexpr (!PRE) {
 #pragma unroll
         for (int sl = 0; sl < F::NSL; ++sl) rot[sl].init_steps(a.theta, (sl * F::KS + qseg * 8) / 2);
     }
+    // PRE with a.vrot: the factors of the thread's v rows, as those of q and k without PRE
+    SliceRot<C, TV::RP, TV::NP, REV> vrot;
+    const int vpair0 = (dv0 + vseg * 8) / 2;
+    constexpr bool VRF = PRE && GR;  // (v rotation compiled in)
+    if constexpr (VRF)
+        if (a.vrot) vrot.init_steps(a.theta, vpair0);
 
     auto commit = [&](int i, auto parc, auto slc) __attribute__((always_inline)) {
         constexpr int par = decltype(parc)::value, sl = decltype(slc)::value;
@@ -807,27 +827,35 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT, NDW>::OCC)) void ch
                 }
             if constexpr (sl == 0) {
                 uint16_t* sVz = sV + F::SV;
+                if (VRF && a.vrot && (c & 7) == 0) vrot.cur.eval(a.pos0 + crow(c) + vrow, a.theta, vpair0);
 #pragma unroll
                 for (int p = 0; p < TV::NP; ++p) {
                     const int r = lrow(vrow + p * TV::RP);
                     if (TV::live(vrow, p)) {
-                        lds_store16(sV + ZV::off(r, vseg * 8), bv[par][p]);
                         const float z = L == C ? zvfull[p] : (r < L ? gpow(lg, (float)(L - 1 - r)) : 0.f);
                         float vf[8];
                         unpack8(bv[par][p], vf);
+                        if (VRF && a.vrot) {
+                            vrot.cur.apply(vf);
+                            if (p + 1 < TV::NP) vrot.cur.turn(vrot.pass);
+                            lds_store16(sV + ZV::off(r, vseg * 8), pack8(vf));
+                        } else {
+                            lds_store16(sV + ZV::off(r, vseg * 8), bv[par][p]);
+                        }
 #pragma unroll
                         for (int e = 0; e < 8; ++e) vf[e] *= z;
                         lds_store16(sVz + ZV::off(r, vseg * 8), pack8(vf));
                     }
                 }
+                if (VRF && a.vrot) vrot.next_chunk();
             }
         } else {
             uint16_t* sKz = sK + F::SQ;
             if ((c & 7) == 0)  // exact factors every 8 chunks; angle addition in between
-                rot[sl].cur.eval(a.pos0 + seg_t0 + (long long)c * C + qrow, a.theta, (sl * F::KS + qseg * 8) / 2);
+                rot[sl].cur.eval(a.pos0 + crow(c) + qrow, a.theta, (sl * F::KS + qseg * 8) / 2);
 #pragma unroll
             for (int p = 0; p < TQ::NP; ++p) {
-                const int r = qrow + p * TQ::RP;
+                const int r = lrow(qrow + p * TQ::RP);
                 if (TQ::live(qrow, p)) {
                     float qf[8], kf[8];
                     unpack8(bq[par][p], qf);
@@ -847,7 +875,7 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT, NDW>::OCC)) void ch
             if constexpr (sl == 0) {
 #pragma unroll
                 for (int p = 0; p < TV::NP; ++p)
-                    if (TV::live(vrow, p)) lds_store16(sV + ZV::off(vrow + p * TV::RP, vseg * 8), bv[par][p]);
+                    if (TV::live(vrow, p)) lds_store16(sV + ZV::off(lrow(vrow + p * TV::RP), vseg * 8), bv[par][p]);
             }
         }
     };
@@ -862,7 +890,7 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT, NDW>::OCC)) void ch
     // chunk's first tile are evaluated exactly every 8 chunks and otherwise carried from the chunk before by angle
     // addition; those of the later tiles follow by steps of 16 rows.
     float oc[NDW][2], os[NDW][2], o16c[NDW][2], o16s[NDW][2], oCc[NDW][2], oCs[NDW][2];
-    if constexpr (PRE) {
+    if constexpr (PRE && GR) {
         if (a.orot) {
 #pragma unroll
             for (int j = 0; j < NDW; ++j)
@@ -903,7 +931,7 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT, NDW>::OCC)) void ch
             }
     };
     auto store_out = [&](int c, f32x4_t* O) __attribute__((always_inline)) {
-        if constexpr (PRE)
+        if constexpr (PRE && GR)
             if (a.orot) out_rotate(c, O);
         const int L = min(C, seg_n - c * C);
         const rsrc_t ro = bytes_rsrc(oh + crow(c) * rsv * osz, ((L - 1) * rsv + DVT) * osz);
@@ -1103,14 +1131,16 @@ ChunkKernels chunk_entry_bf16() {
     constexpr int CI = C > 64 ? 64 : C, DVT = 16 * (NT / 64) * NDW;
     ChunkKernels k{};
     k.fused = chunk_fused_bf16<DK, CI, DVT, false, NT, NDW>;
-    k.fused_pre = chunk_fused_bf16<DK, CI, DVT, true, NT, NDW>;
+    // (the sets with reversed instances serve the gradients: their PRE instances rotate outputs and v rows)
+    k.fused_pre = chunk_fused_bf16<DK, CI, DVT, true, NT, NDW, false, WITH_REV>;
     if constexpr (WITH_REV) {
-        k.fused_rev = chunk_fused_bf16<DK, CI, DVT, true, NT, NDW, true>;
+        k.fused_rev = chunk_fused_bf16<DK, CI, DVT, true, NT, NDW, true, true>;
+        k.fused_rot_rev = chunk_fused_bf16<DK, CI, DVT, false, NT, NDW, true>;
         k.rev_step = CI;
     }
     k.dvt = DVT;
     k.threads = NT;
-    k.fused_orot = 1;
+    k.fused_orot = WITH_REV;
     // d_v tiles of 128 run one workgroup per CU: one workgroup per CU in total measured fastest (fewer, longer
     // segments); 256-thread ones with 16-column waves two per CU, with two rounds of them.
     k.target_wgs = NT * NDW >= 512 ? 256 : 1024;

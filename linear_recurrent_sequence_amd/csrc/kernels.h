@@ -40,8 +40,9 @@ struct FwdArgs {
     float eps;
     int epi, gate_bf16;
     // Output rows turned back by the transpose rotation at their positions (theta, pos0), for kernels that stage
-    // q and k as given (the gradients' dq' and dk' retentions).
-    int orot;
+    // q and k as given (the gradients' dq' and dk' retentions); vrot: v rows turned by the rotation at their
+    // positions while staged (those retentions' v is K' or Q').
+    int orot, vrot;
     // Three-launch bf16 kernels only. qk_din (0: d_k): q and k are columns qk_col0 .. qk_col0 + d_k - 1 of heads
     // qk_din wide, so that a run can take one block of wider heads in place. The full pass alone also takes:
     // qk_blocks > 1: the units run over that many such blocks (block i at columns qk_col0 + i d_k, its outputs
@@ -997,8 +998,11 @@ struct ChunkKernels {
     // the single-pass kernels run chained segments as three launches instead (FwdArgs::split: the local passes,
     // slot_scan_kernel, the full passes), with the segment states in the workspace after its first kChainMeta bytes
     int fused_split;
-    // fused_pre and fused_rev can turn their output rows back by the transpose rotation (FwdArgs::orot)
+    // fused_pre and fused_rev can turn their output rows back by the transpose rotation (FwdArgs::orot) and turn
+    // their v rows by the rotation while staging (FwdArgs::vrot)
     int fused_orot;
+    // `fused` over the reversed sequence, rotating q and k while staging (null: none)
+    fwd_kernel_t fused_rot_rev;
 };
 struct ParKernel {
     fwd_kernel_t fn;

@@ -146,10 +146,11 @@ def test_gradients_workspace_and_rejections(lib):
     n = 8 * 2048 * 8 * 64
     assert 2 * n * 2 <= wsq(8, 2048, 8, 64, 64, 64) < 2 * n * 2 + n * 4
     assert wsq(8, 2048, 8, 64, 64, 64) % 256 == 0
-    # d_k = 128, N a multiple of 32: the streaming kernel in place, writing dq and dk itself (the segment states,
-    # then Q', K'); otherwise five reordered bf16 copies (K' twice, Q', V, dO) and three fp32 outputs
+    # d_k = 128, N a multiple of 32: the streaming kernel in place, rotating while staging and writing dq and dk
+    # itself (the segment states alone: 4 units x 16 segments x 64 KB after the 64 KB of chain metadata);
+    # otherwise five reordered bf16 copies (K' twice, Q', V, dO) and three fp32 outputs
     n2 = 1 * 4096 * 4 * 128
-    assert 2 * n2 * 2 <= wsq(1, 4096, 4, 128, 128, 64) < 2 * n2 * 2 + n2 * 4
+    assert wsq(1, 4096, 4, 128, 128, 64) == 65536 + 4 * 16 * 128 * 128 * 4
     n2r = 1 * 4090 * 4 * 128
     assert wsq(1, 4090, 4, 128, 128, 64) >= 5 * n2r * 2 + 3 * n2r * 4
     assert wsq(1, 100, 2, 32, 64, 64) == 0      # d_k = 32: no bf16 kernel

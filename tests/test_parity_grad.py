@@ -80,7 +80,8 @@ GRAD_IN_PLACE = [
     # states (of a local pass and scan over K' and V, and of the dv retention); otherwise (one block) the
     # single-pass kernels' reversed instances: the streaming kernel with d_v tiles of 128 for d_k = 128, the
     # wide-head kernel for d_k = 256. Where the dq' and dk' retentions run on the streaming kernel, it writes dq and
-    # dk itself, turned back by the transpose rotation: no final reordering launch.
+    # dk itself, turned back by the transpose rotation: no final reordering launch; and where the dv retention runs
+    # on it too, every retention rotates its operands while staging: no up-front rotation either.
     (1, 640, 2, 256, 512, 128, True, 5, "bf16", "ret_chunk_dma", True, 1),   # 5 segments, two d_v blocks
     (2, 512, 2, 256, 256, 64, True, 0, "f32", "ret_chunk_dma", True, 1),     # one block
     (1, 1024, 1, 256, 512, 32, False, 0, "f32", "ret_chunk_dma", True, 1),   # no rotation, chunk 32
@@ -105,7 +106,7 @@ def test_gradients_in_place(R, case):
     timer = R.Timer()
     got = _gpu_grad(R, q, k, v, do, w.gamma, chunk, w.theta, pos0, out_dt, options={"timer": timer})
     assert timer.query("ret_permute_rotate")[1] == nperm
-    assert timer.query("ret_rotate_qk")[1] == (1 if rot else 0)
+    assert timer.query("ret_rotate_qk")[1] == (1 if rot and nperm else 0)
     if kernel == "ret_chunk_dma":
         nb = dv // 256
         # dq' per block, dv, then dk' per block; or (several segments) the states of (K', V), dq' of all blocks,
@@ -123,8 +124,9 @@ def test_gradients_in_place(R, case):
 @pytest.mark.parametrize("out_dt", ["bf16", "f32"])
 def test_gradients_rotated_by_their_kernel(R, out_dt):
     """d_k = d_v = 128 in two segments of 2048 tokens (32 chunks of 64 each, the rotation factors carried from chunk
-    to chunk and evaluated exactly every 8) at positions past 70000: the streaming kernel turns dq and dk back by
-    the transpose rotation itself, with no reordering launch."""
+    to chunk and evaluated exactly every 8) at positions past 70000: the streaming kernel rotates K and Q while
+    staging them (as v of the dq' and dk' retentions, as q and k of the dv retention over the reversed sequence)
+    and turns dq and dk back by the transpose rotation itself: no rotation or reordering launch."""
     w = W.Workload("grad", B=1, N=4096, H=2, dk=128, dv=128, dtype="bf16", scale=float(np.sqrt(128)), seed=73,
                    chunk=128, rotate=True)
     print_case("gradients-own-outputs", out_dt, w)
@@ -135,6 +137,7 @@ def test_gradients_rotated_by_their_kernel(R, out_dt):
     got = _gpu_grad(R, q, k, v, do, w.gamma, w.chunk, w.theta, 70001, out_dt,
                     options={"timer": timer, "segments": 2})
     assert timer.query("ret_permute_rotate")[1] == 0
+    assert timer.query("ret_rotate_qk")[1] == 0
     assert timer.query("ret_chunk_fused")[1] == 3
     timer.close()
     _check(got, ref, tol("bf16"))
