@@ -423,9 +423,9 @@ ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o,
         // Staging copies rows instead of rotating them when there is no rotation, or when q and k are rotated
         // once up front (several d_v tiles stage the same rows).
         // (reversed runs with rotation: the reversed instance that rotates q and k while staging)
-        const bool rot_rev = rev && theta && ck.fused_rot_rev && !onchip && plan.rot_bytes == 0 && !qk_din &&
-                             !out_theta && !v_rot && N % ck.rev_step == 0;
-        fwd_kernel_t fn = onchip ? ck.seg : rot_rev ? ck.fused_rot_rev : ck.fused;
+        const bool rot_rev = rev && theta && plan.rot_bytes == 0 && !qk_din && !out_theta && !v_rot &&
+                             (onchip ? ck.seg_rot_rev != nullptr : ck.fused_rot_rev && N % ck.rev_step == 0);
+        fwd_kernel_t fn = rot_rev ? (onchip ? ck.seg_rot_rev : ck.fused_rot_rev) : onchip ? ck.seg : ck.fused;
         const fwd_kernel_t fn_pre = onchip ? (rev ? ck.seg_rev : ck.seg_pre)
                                            : (rev && !ck.split_local ? ck.fused_rev : ck.fused_pre);
         // The reversed run and the rotation of the outputs exist for the on-chip kernel, the reversed run and q, k
@@ -434,7 +434,7 @@ ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o,
         // without input rotation, state or epilogue.
         if (rev || out_theta || qk_din || v_rot) {
             const bool plain = (!theta || rot_rev) && !state_in && !state_out && !epi;
-            const bool seg_ok = onchip && !qk_din && (!rev || ck.seg_rev) && !v_rot;
+            const bool seg_ok = onchip && !qk_din && (!rev || ck.seg_rev) && (!v_rot || out_theta);
             const bool split_ok = ck.split_local && !onchip && !out_theta && (!rev || N % kDmaStep == 0);
             const bool fused_ok = !ck.split_local && !onchip && !qk_din &&
                                   (!rev || (ck.fused_rev && N % ck.rev_step == 0)) &&
@@ -589,6 +589,8 @@ bool bwd_layout(int B, int N, int H, int dk, int dv, int chunk, ret_dtype_t in_d
     const ChunkPlan pb = plan_chunk(cb, B, N, H, dk, dv, chunk, false, SIZE_MAX, op);
     L->direct = in_dt == RET_BF16 && L->nb == 1 && plan_onchip(ca, pa, op) && ca.seg_rev && plan_onchip(cb, pb, op) &&
                 cb.seg_rev && op.bwd_direct != 0;
+    // (direct: the dq' and dk' runs turn their v rows while staging, the dv run rotates its q and k while staging)
+    if (L->direct) L->stage_rot = rotate && cb.seg_rot_rev;
     L->variant = op.variant;
     L->inplace = !L->direct && in_dt == RET_BF16 && N % kDmaStep == 0 && ca.split_local &&
                  !plan_onchip(ca, pa, op) && cb.split_local && !plan_onchip(cb, pb, op) && op.bwd_direct != 0;
@@ -1077,9 +1079,12 @@ ret_status_t ret_chunkwise_bwd_saved_ex(const void* q, const void* k, const void
     if (L.direct) {
         // Q', K' (rotated once; q and k themselves without rotation), then dq' = retention(dO, V, K') and, over
         // the reversed sequence on the reversed traversal, dv = retention(K', Q', dO) and dk' = retention(V, dO,
-        // Q'), written in token order; dq' and dk' leave their kernels turned back by the transpose rotation.
+        // Q'), written in token order; dq' and dk' leave their kernels turned back by the transpose rotation. With
+        // stage_rot no copies: the dq' and dk' runs turn their v rows (K, Q) while staging, and the dv run rotates
+        // its q and k (K, Q) while staging.
         const void *Qp = q, *Kp = k;
-        if (theta) {
+        const bool vr = theta && L.stage_rot;
+        if (theta && !L.stage_rot) {
             FwdArgs A;
             fill_fwd(A, q, k, v, nullptr, B, N, H, dk, dv, out_dt, gamma, theta, pos0);
             A.qr = ws + L.qp;
@@ -1094,14 +1099,16 @@ ret_status_t ret_chunkwise_bwd_saved_ex(const void* q, const void* k, const void
         // dq and dk straight from the retentions, their output rows turned back by the transpose rotation
         void* chain = ws + L.chain;
         if ((st = chunkwise_run(dout, v, Kp, dq, B, N, H, dv, dk, RET_BF16, out_dt, gamma, nullptr, pos0, chunk,
-                                nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, op, false, theta)) !=
-            RET_OK)
+                                nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, op, false, theta, 0, 0,
+                                vr)) != RET_OK)
             return st;
-        if ((st = chunkwise_run(Kp, Qp, dout, dv_out, B, N, H, dk, dv, RET_BF16, out_dt, gamma, nullptr, 0, chunk,
-                                nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, op, true)) != RET_OK)
+        if ((st = chunkwise_run(Kp, Qp, dout, dv_out, B, N, H, dk, dv, RET_BF16, out_dt, gamma, vr ? theta : nullptr,
+                                vr ? pos0 : 0, chunk, nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr,
+                                op, true)) != RET_OK)
             return st;
         return chunkwise_run(v, dout, Qp, dk_out, B, N, H, dv, dk, RET_BF16, out_dt, gamma, nullptr, pos0, chunk,
-                             nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, op, true, theta);
+                             nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, op, true, theta, 0, 0,
+                             vr);
     }
     const int ib = in_dt == RET_BF16;
     if (L.nb == 2) {

@@ -152,16 +152,19 @@ __device__ __forceinline__ void lds_store16(uint16_t* p, u32x4_t x) { *reinterpr
 
 // Per-thread rotation state of the Q/K segments of one d_k slice: the factors of the thread's row in the
 // current pass (cur), the step between passes (RP tokens) and the step from the last pass of a chunk to the
-// first of the next (C - (NP - 1) RP tokens; the same step unless the tile is partial). BACKW: the chunks of a
-// reversed run, each C rows before the one before it in memory (a step of -C - (NP - 1) RP).
-template <int C, int RP, int NP, bool BACKW = false>
+// first of the next (C - (NP - 1) RP tokens; the same step unless the tile is partial). MODE 1: the chunks of a
+// reversed run staged in memory order, each C rows before the one before it (a step of -C - (NP - 1) RP); MODE
+// 2: the rows of a reversed run taken in the run's order, every step negated.
+template <int C, int RP, int NP, int MODE = 0>
 struct SliceRot {
     Rot4 cur, pass;
-    Rot4 wrap;  // used only for partial tiles and reversed runs
-    static constexpr bool SAME = !BACKW && C == NP * RP;
+    Rot4 wrap;  // used only for partial tiles and reversed runs staged in memory order
+    static constexpr bool SAME = MODE != 1 && C == NP * RP;
     __device__ __forceinline__ void init_steps(const double* theta, int pair0) {
-        pass.eval(RP, theta, pair0);
-        if constexpr (!SAME) wrap.eval(BACKW ? -(C + (NP - 1) * RP) : C - (NP - 1) * RP, theta, pair0);
+        pass.eval(MODE == 2 ? -RP : RP, theta, pair0);
+        if constexpr (!SAME)
+            wrap.eval(MODE == 0 ? C - (NP - 1) * RP : MODE == 1 ? -(C + (NP - 1) * RP) : -(C - (NP - 1) * RP), theta,
+                      pair0);
     }
     __device__ __forceinline__ void next_chunk() {
         if constexpr (SAME) cur.turn(pass);
@@ -798,13 +801,13 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT, NDW>::OCC)) void ch
     for (int p = 0; p < TV::NP; ++p) zvfull[p] = gpow(lg, (float)(C - 1 - lrow(vrow + p * TV::RP)));
     const float gC = gpow(lg, (float)C);
     // Without rotation theta is all zero and every factor is exactly (1, 0).
-    SliceRot<C, TQ::RP, TQ::NP, REV> rot[F::NSL];
+    SliceRot<C, TQ::RP, TQ::NP, REV ? 1 : 0> rot[F::NSL];
     if constexpr (!PRE) {
 #pragma unroll
         for (int sl = 0; sl < F::NSL; ++sl) rot[sl].init_steps(a.theta, (sl * F::KS + qseg * 8) / 2);
     }
     // PRE with a.vrot: the factors of the thread's v rows, as those of q and k without PRE
-    SliceRot<C, TV::RP, TV::NP, REV> vrot;
+    SliceRot<C, TV::RP, TV::NP, REV ? 1 : 0> vrot;
     const int vpair0 = (dv0 + vseg * 8) / 2;
     constexpr bool VRF = PRE && GR;  // (v rotation compiled in)
     if constexpr (VRF)

@@ -13,8 +13,10 @@ ChunkKernels chunk_entry_small() {
     constexpr int CS = 32;
     ChunkKernels k = chunk_entry_bf16<DK, C>();
     k.seg = chunk_seg_bf16<DK, CS, false>;
-    k.seg_pre = chunk_seg_bf16<DK, CS, true>;
-    k.seg_rev = chunk_seg_bf16<DK, CS, true, true>;
+    // (the PRE instances serve the gradients: v rows rotated while staged, outputs turned back)
+    k.seg_pre = chunk_seg_bf16<DK, CS, true, false, true>;
+    k.seg_rev = chunk_seg_bf16<DK, CS, true, true, true>;
+    k.seg_rot_rev = chunk_seg_bf16<DK, CS, false, true>;
     k.seg_tokens = SegB<DK, CS, false>::RT;
     return k;
 }

@@ -12,9 +12,10 @@
 // hint: no row is read again).
 //
 // REV runs the same recurrence over the reversed sequence (token n of the run is row N-1-n of q, k, v and o):
-// the gradients' retentions that sum over later tokens. Only with q and k as given (PRE, no rotation), and
-// without state in, state out or the epilogue. Every row of a reversed chunk gets its own buffer offset, which
-// is negative, hence out of range and read as zero or dropped, for rows past the chunk.
+// the gradients' retentions that sum over later tokens, without state in, state out or the epilogue. Every row
+// of a reversed chunk gets its own buffer offset, which is negative, hence out of range and read as zero or
+// dropped, for rows past the chunk. Rows are rotated (q and k without PRE; v with a.vrot, PRE and GR) by the
+// rotation at their own positions in memory.
 #pragma once
 
 #include "chunk_bf16.h"
@@ -42,9 +43,8 @@ struct SegB {
     static_assert(VTILE >= TILE, "a V staging tile holds a chunk of bf16 output rows at pitch LD");
 };
 
-template <int DK, int C, bool PRE, bool REV = false>
+template <int DK, int C, bool PRE, bool REV = false, bool GR = false>
 __global__ __launch_bounds__(kThreads, 2) void chunk_seg_bf16(FwdArgs a) {
-    static_assert(!REV || PRE, "reversed runs take q and k as given");
     typedef SegB<DK, C, PRE> F;
     typedef typename F::TQ TQ;
     typedef typename F::TV TV;
@@ -183,9 +183,20 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_seg_bf16(FwdArgs a) {
     const float gC = gpow(lg, (float)C);
 
     // Rotation factors of the thread's rows (identity without rotation: theta all zero), shared by its q and k
-    // rows. Evaluated exactly every 8 chunks, by angle addition in between.
-    SliceRot<C, TQ::RP, TQ::NP> rot;
+    // rows. Evaluated exactly every 8 chunks, by angle addition in between. Run row r of chunk c is at position
+    // pos0 + seg_t0 + cC + r, or over the reversed sequence pos0 + N - 1 - (seg_t0 + cC + r).
+    SliceRot<C, TQ::RP, TQ::NP, REV ? 2 : 0> rot;
     if constexpr (!PRE) rot.init_steps(s_theta, qseg * 4);
+    auto run_pos = [&](int c, int r) __attribute__((always_inline)) {
+        const long long t = seg_t0 + (long long)c * C + r;
+        return a.pos0 + (REV ? (long long)aN - 1 - t : t);
+    };
+    // PRE with GR and a.vrot: the factors of the thread's v rows (columns dv0 + 8 vseg ..), the same way
+    constexpr bool VR = PRE && GR;
+    SliceRot<C, TV::RP, TV::NP, REV ? 2 : 0> vrt;
+    const int vpair0 = (dv0 + vseg * 8) / 2;
+    if constexpr (VR)
+        if (a.vrot) vrt.init_steps(a.theta, vpair0);
 
     // Output stores straight from the O^T accumulators: lane (g, n16) of tile x holds 4 consecutive d_v of
     // query x*16 + n16. Rows past the sequence fall outside the buffer range and are dropped.
@@ -222,7 +233,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_seg_bf16(FwdArgs a) {
             uint16_t* sK = sKst + (c & 1) * F::KTILE;
             uint16_t* sV = sVst + (c & 1) * F::VTILE;
             if constexpr (!PRE)
-                if (c % 8 == 0) rot.cur.eval(a.pos0 + seg_t0 + (long long)c * C + qrow, s_theta, qseg * 4);
+                if (c % 8 == 0) rot.cur.eval(run_pos(c, qrow), s_theta, qseg * 4);
 #pragma unroll
             for (int p = 0; p < TQ::NP; ++p)
                 if (TQ::live(qrow, p)) {
@@ -243,9 +254,21 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_seg_bf16(FwdArgs a) {
                     }
                 }
             if constexpr (!PRE) rot.next_chunk();
+            if (VR && a.vrot && c % 8 == 0) vrt.cur.eval(run_pos(c, vrow), a.theta, vpair0);
 #pragma unroll
             for (int p = 0; p < TV::NP; ++p)
-                if (TV::live(vrow, p)) lds_store16(sV + ZV::off(vrow + p * TV::RP, vseg * 8), bv[par][p]);
+                if (TV::live(vrow, p)) {
+                    if (VR && a.vrot) {
+                        float vf[8];
+                        unpack8(bv[par][p], vf);
+                        vrt.cur.apply(vf);
+                        if (p + 1 < TV::NP) vrt.cur.turn(vrt.pass);
+                        lds_store16(sV + ZV::off(vrow + p * TV::RP, vseg * 8), pack8(vf));
+                    } else {
+                        lds_store16(sV + ZV::off(vrow + p * TV::RP, vseg * 8), bv[par][p]);
+                    }
+                }
+            if (VR && a.vrot) vrt.next_chunk();
             if constexpr (c + NBUF < F::MAXC) issue(std::integral_constant<int, c + NBUF>{});
             __syncthreads();
 

@@ -1001,8 +1001,8 @@ struct ChunkKernels {
     // fused_pre and fused_rev can turn their output rows back by the transpose rotation (FwdArgs::orot) and turn
     // their v rows by the rotation while staging (FwdArgs::vrot)
     int fused_orot;
-    // `fused` over the reversed sequence, rotating q and k while staging (null: none)
-    fwd_kernel_t fused_rot_rev;
+    // `fused` over the reversed sequence, rotating q and k while staging (null: none), and `seg` likewise
+    fwd_kernel_t fused_rot_rev, seg_rot_rev;
 };
 struct ParKernel {
     fwd_kernel_t fn;
@@ -1011,8 +1011,12 @@ struct ParKernel {
 
 template <class E, int DK, int C, int DVT>
 ChunkKernels chunk_entry() {
-    return {chunk_full_kernel<E, DK, C, DVT>, chunk_local_kernel<E, DK, C, DVT>, nullptr, nullptr, DVT, nullptr, nullptr, 0,
-            kThreads, 0};
+    ChunkKernels k{};
+    k.full = chunk_full_kernel<E, DK, C, DVT>;
+    k.local = chunk_local_kernel<E, DK, C, DVT>;
+    k.dvt = DVT;
+    k.threads = kThreads;
+    return k;
 }
 
 // Getters, one per kernel-group source. Return false when the shape has no instance.

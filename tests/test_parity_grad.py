@@ -121,6 +121,26 @@ def test_gradients_in_place(R, case):
     _check(got, ref, tol("bf16"))
 
 
+@pytest.mark.parametrize("case", [(2, 700, 4, 64, 9), (1, 1024, 2, 64, 70001)], ids=["ragged", "far-positions"])
+def test_gradients_on_chip_rotate_while_staging(R, case):
+    """d = 64 in short segments (the on-chip kernel's reversed traversal): no rotation launch and no rotated
+    copies; the dq' and dk' runs turn their v rows (K, Q) while staging and their outputs back, the dv run rotates
+    its q and k (K, Q) while staging over the reversed sequence, a ragged last chunk included."""
+    B, N, H, d, pos0 = case
+    w = W.Workload("grad", B=B, N=N, H=H, dk=d, dv=d, dtype="bf16", scale=float(np.sqrt(d)), seed=79 + N, chunk=64,
+                   rotate=True)
+    print_case("gradients-on-chip-rotation", pos0, w)
+    q, k, v, rng = W.make_qkv(w)
+    do = W.make_dout(w, rng)
+    ref = oracle.grad(q, k, v, do, w.gamma, theta=w.theta, pos0=pos0)
+    timer = R.Timer()
+    got = _gpu_grad(R, q, k, v, do, w.gamma, w.chunk, w.theta, pos0, "f32", options={"timer": timer})
+    assert timer.query("ret_rotate_qk")[1] == 0
+    assert timer.query("ret_chunk_seg")[1] == 3
+    timer.close()
+    _check(got, ref, tol("bf16"))
+
+
 @pytest.mark.parametrize("out_dt", ["bf16", "f32"])
 def test_gradients_rotated_by_their_kernel(R, out_dt):
     """d_k = d_v = 128 in two segments of 2048 tokens (32 chunks of 64 each, the rotation factors carried from chunk
