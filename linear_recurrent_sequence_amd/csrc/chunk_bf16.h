@@ -446,9 +446,10 @@ __device__ __forceinline__ void chain_finish(const FwdArgs& a, int dvt, int slot
 }
 
 // ---------------------------------------------------------------------------------------------------
-// chunk_fused (bf16): one workgroup per (segment, d_v tile of 64, b*H + h). Wave w owns d_v block w of every
-// output and state tile. With several segments the workgroup first runs the local pass over its segment
-// (R <- gamma^L R + (K (.) zeta)^T V from zero, or from state_in for the first segment), publishes the end
+// chunk_fused (bf16): one workgroup per (segment, d_v tile, b*H + h). Wave w owns NDW d_v blocks of 16 columns of
+// every output and state tile. With several segments the workgroup first runs the local pass over its segment
+// (R = sum over its chunks of gamma^(decay to the segment's end) (K (.) zeta)^T V, from zero, or from state_in for
+// the first segment; split launches store it for the scan instead), publishes the end
 // state and joins the segment chain for its entering state. The full pass then runs from that state: per
 // chunk and d_k slice S^T = K Q^T (all lower-triangle tiles, kept in registers), the cross term
 // O^T += R^T Q^T with R^T taken from the state accumulators and the state update; then
