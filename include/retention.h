@@ -303,10 +303,12 @@ ret_status_t ret_chunkwise_bwd_ex(const void* q, const void* k, const void* v, c
  * options), passed unchanged since that call. Where that call ran the LDS-loading d_k = 256 kernels (d_v a
  * multiple of 256, several segments, N a multiple of 32) it left there the rotated copies of q and k and the
  * state entering each segment, which the gradients need too: they are read instead of recomputed (the dq'
- * retentions enter their segments with those states, transposed). Otherwise, or with fwd_workspace NULL, the
- * call is ret_chunkwise_bwd_ex. Same results as ret_chunkwise_bwd_ex (bit for bit where the forward's plan is
- * the gradients' own); a forward workspace from another call gives wrong gradients, which the library cannot
- * detect. fwd_workspace is only read.
+ * retentions enter their segments with those states, transposed); where it ran the streaming kernel's split
+ * launches (d_k = d_v = 128, several segments) it left the states, read the same way. Otherwise, or with
+ * fwd_workspace NULL, the call is ret_chunkwise_bwd_ex. Same results as ret_chunkwise_bwd_ex (bit for bit on the
+ * LDS-loading kernels, whose forward ran the same products; to rounding on the streaming kernel, whose forward
+ * formed the states in another order); a forward workspace from another call gives wrong gradients, which the
+ * library cannot detect. fwd_workspace is only read.
  */
 ret_status_t ret_chunkwise_bwd_saved_ex(const void* q, const void* k, const void* v, const void* dout, void* dq,
                                         void* dk_out, void* dv_out, int B, int N, int H, int dk, int dv,

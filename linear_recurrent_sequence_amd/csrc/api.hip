@@ -381,7 +381,7 @@ ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o,
                            int64_t pos0, int chunk, const float* state_in, float* state_out, void* workspace,
                            size_t workspace_bytes, void* stream, const EpiRequest* epi, bool* fused,
                            const Opts& op, bool rev = false, const double* out_theta = nullptr, int qk_din = 0,
-                           int qk_col0 = 0, bool v_rot = false) {
+                           int qk_col0 = 0, bool v_rot = false, const float* states_t = nullptr) {
     if (fused) *fused = false;
     ret_status_t st = check_common(q, k, v, o, B, N, H, dk, dv, in_dt, out_dt, gamma, theta);
     if (st != RET_OK) return st;
@@ -443,6 +443,8 @@ ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o,
                 return fail(RET_ERR_UNSUPPORTED, "reversed, output-rotated or column-block chunkwise run: not "
                                                  "available for this shape");
         }
+        if (states_t && ck.split_local)
+            return fail(RET_ERR_UNSUPPORTED, "chunkwise form: transposed entering states with this plan");
         if (out_theta) {
             A.orot = 1;
             A.vrot = v_rot;  // (v has the outputs' width: one rotation for both)
@@ -493,20 +495,27 @@ ret_status_t chunkwise_run(const void* q, const void* k, const void* v, void* o,
         const bool pre = !onchip && (fn == ck.fused_pre || (rev && fn == ck.fused_rev));
         const int threads = onchip || !ck.threads ? kThreads : pre && ck.threads_pre ? ck.threads_pre : ck.threads;
         const char* name = onchip ? "ret_chunk_seg" : pre && ck.pre_name ? ck.pre_name : "ret_chunk_fused";
+        if (states_t && !(ck.fused_split && ck.fused_orot && pre && nseg > 1 && dk == dv && dv == ck.dvt && !epi))
+            return fail(RET_ERR_UNSUPPORTED, "chunkwise form: transposed entering states with this plan");
         if (ck.fused_split && !onchip && nseg > 1 && !epi) {
-            // local passes, the scan of their states, then the full pass of every segment (no chain)
+            // local passes, the scan of their states, then the full pass of every segment (no chain); or, given
+            // the states of another run (states_t), the full passes alone, entering with their transposes
             A.ws = workspace ? (float*)((char*)workspace + kChainMeta) : nullptr;
             const unsigned units = (unsigned)((long long)B * H * ntiles);
-            A.split = 1;
-            LaunchTimer tl("ret_chunk_fused_local", s, op);
-            hipLaunchKernelGGL(fn, dim3(units * (unsigned)(nseg - 1)), dim3(threads), 0, s, A);
-            tl.done();
-            if ((st = launch_status("ret_chunk_fused_local")) != RET_OK) return st;
-            LaunchTimer tc("ret_chunk_fused_scan", s, op);
-            hipLaunchKernelGGL(slot_scan_get(), dim3((unsigned)((long long)dk * ck.dvt / 512), units), dim3(256), 0, s,
-                               A);
-            tc.done();
-            if ((st = launch_status("ret_chunk_fused_scan")) != RET_OK) return st;
+            if (states_t) {
+                A.ws_t = states_t;
+            } else {
+                A.split = 1;
+                LaunchTimer tl("ret_chunk_fused_local", s, op);
+                hipLaunchKernelGGL(fn, dim3(units * (unsigned)(nseg - 1)), dim3(threads), 0, s, A);
+                tl.done();
+                if ((st = launch_status("ret_chunk_fused_local")) != RET_OK) return st;
+                LaunchTimer tc("ret_chunk_fused_scan", s, op);
+                hipLaunchKernelGGL(slot_scan_get(), dim3((unsigned)((long long)dk * ck.dvt / 512), units), dim3(256),
+                                   0, s, A);
+                tc.done();
+                if ((st = launch_status("ret_chunk_fused_scan")) != RET_OK) return st;
+            }
             A.split = 2;
             LaunchTimer tm(name, s, op);
             hipLaunchKernelGGL(fn, dim3(grid), dim3(threads), 0, s, A);
@@ -955,6 +964,27 @@ ret_status_t ret_chunkwise_bwd_saved_ex(const void* q, const void* k, const void
                            resolve_chunk(RET_BF16, B, N, H, dk, dv, chunk, false, L.chain_bytes, ov, &ck_sq, &plan_sq) &&
                            ck_sq.split_local && plan_sq.nseg > 1 && pick_chunk(RET_BF16, wb, dk, chunk, &ck_bl, ov) &&
                            ck_bl.split_full_rev && ck_bl.dvt == dk;
+        // One block on the streaming kernel's split launches with square states (d_k = d_v = its tile): dk' enters
+        // its segments with the transposes of the dv retention's states, and (after the forward) dq' with those of
+        // the forward's, Σ K'^T V, so neither runs local passes or a scan of its own.
+        bool own_square = false;
+        const float* own_fws_states = nullptr;
+        if (L.own_out && dk == dv) {
+            ChunkKernels ka, kb;
+            ChunkPlan pla, plb;
+            own_square = resolve_chunk(RET_BF16, B, N, H, wb, dk, chunk, false, L.chain_bytes, ov, &ka, &pla) &&
+                         resolve_chunk(RET_BF16, B, N, H, dk, dv, chunk, false, L.chain_bytes, ov, &kb, &plb) &&
+                         ka.fused_split && kb.fused_split && ka.fused_orot && ka.dvt == dk && kb.dvt == dv &&
+                         !plan_onchip(ka, pla, ov) && !plan_onchip(kb, plb, ov) && pla.nseg > 1 &&
+                         pla.nseg == plb.nseg && pla.seg_len == plb.seg_len;
+            ChunkKernels kf;
+            ChunkPlan plf;
+            if (own_square && fwd_workspace &&
+                resolve_chunk(RET_BF16, B, N, H, dk, dv, chunk, theta != nullptr, fwd_workspace_bytes, op, &kf, &plf) &&
+                kf.fused_split && kf.dvt == dv && !plan_onchip(kf, plf, op) && plf.nseg == pla.nseg &&
+                plf.seg_len == pla.seg_len)
+                own_fws_states = (const float*)((const char*)fwd_workspace + kChainMeta);
+        }
         // The forward's workspace holds Q', K' and those same (K', V) states when its plan (with rotation, in its
         // workspace) ran the three-launch kernels over the same segments: then they are read from there.
         const char* fws = nullptr;
@@ -1035,7 +1065,7 @@ ret_status_t ret_chunkwise_bwd_saved_ex(const void* q, const void* k, const void
         } else if (L.own_out) {
             if ((st = chunkwise_run(dout, v, Kp, dq, B, N, H, wb, dk, RET_BF16, out_dt, gamma, nullptr, pos0, chunk,
                                     nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, ov, false,
-                                    theta, 0, 0, L.stage_rot)) != RET_OK)
+                                    theta, 0, 0, L.stage_rot, own_fws_states)) != RET_OK)
                 return st;
         } else {
             for (int i = 0; i < L.nb; ++i)
@@ -1056,10 +1086,11 @@ ret_status_t ret_chunkwise_bwd_saved_ex(const void* q, const void* k, const void
         } else if (L.own_out) {
             if (reshaped && (st = chain_meta_zero(in_dt, B, N, H, wb, dk, chunk, chain, L.chain_bytes, s, ov)) != RET_OK)
                 return st;
-            // dq and dk leave their kernels finished: nothing to reorder
+            // dq and dk leave their kernels finished: nothing to reorder. With square states in split launches,
+            // dk' enters its segments with the transposes of the dv retention's states, just left in the slots.
             return chunkwise_run(v, dout, Qp, dk_out, B, N, H, wb, dk, RET_BF16, out_dt, gamma, nullptr, pos0, chunk,
                                  nullptr, nullptr, chain, L.chain_bytes, stream, nullptr, nullptr, ov, true, theta, 0,
-                                 0, L.stage_rot);
+                                 0, L.stage_rot, own_square ? slots : nullptr);
         } else {
             if (reshaped && (st = chain_meta_zero(in_dt, B, N, H, wb, dk, chunk, chain, L.chain_bytes, s, ov)) != RET_OK)
                 return st;

@@ -258,6 +258,26 @@ __device__ __forceinline__ void slot_load(const float* slot, f32x4_t* v, int tid
                                   __builtin_amdgcn_raw_buffer_load_b128(r, tid * 16, x * NT * 16, kChainAux));
 }
 
+// The transpose of a square state slot (DK = DVT = 16 NW NDW) of another run into this thread's tiles:
+// R[x NDW + j][e] is the slot's element (c, r) with r = 16x + g4 + e and c = 16(w NDW + j) + n16, which slot_store
+// put in tile (c / 16) NDW + x % NDW of thread (x / NDW) 64 + (c % 16) / 4 * 16 + r % 16, component c % 4.
+template <int NKB, int NDW, int NT>
+__device__ __forceinline__ void slot_load_transposed(const float* slot, f32x4_t* R, int w, int g4, int n16) {
+    const rsrc_t r = bytes_rsrc(uniform_ptr(slot), NKB * NDW * NT * 16);
+#pragma unroll
+    for (int x = 0; x < NKB; ++x)
+#pragma unroll
+        for (int j = 0; j < NDW; ++j) {
+            const int c = 16 * (w * NDW + j) + n16;
+            const int xs = (c / 16) * NDW + x % NDW;
+            const int ts = (x / NDW) * 64 + (n16 / 4) * 16 + g4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                R[x * NDW + j][e] = __builtin_bit_cast(
+                    float, __builtin_amdgcn_raw_buffer_load_b32(r, ((xs * NT + ts + e) * 4 + n16 % 4) * 4, 0, 0));
+        }
+}
+
 // The unit (one d_v tile of one (b, h)) of this workgroup, from the launch index. Workgroups are dispatched to
 // the 8 XCDs in turn (launch index mod 8); when the grid divides evenly, the d_v tiles of one (b, h) get launch
 // indices of one residue, so they run on one XCD and its L2 serves the q and k rows they all stage.
@@ -585,7 +605,17 @@ __global__ __launch_bounds__(NT, (FullB<DK, C, DVT, PRE, NT, NDW>::OCC)) void ch
 #pragma unroll
     for (int x = 0; x < NR; ++x) R[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     if (split == 2) {
-        slot_load<NR, NT>(split_slot(seg), R, tid);
+        // (GR with a square state: a.ws_t, the transposes of another run's states, e.g. the gradients' dk' from the
+        // dv retention's)
+        if constexpr (PRE && GR && DK == DVT) {
+            if (a.ws_t)
+                slot_load_transposed<F::NKB, NDW, NT>(a.ws_t + ((size_t)unit * anseg + seg) * (size_t)(DK * DVT), R,
+                                                      w, g4, n16);
+            else
+                slot_load<NR, NT>(split_slot(seg), R, tid);
+        } else {
+            slot_load<NR, NT>(split_slot(seg), R, tid);
+        }
     } else if (seg == 0 && a.state_in) {
         load_state_in(R);
         if (split == 1) {  // the scan starts from state_in, in slot 0; the local pass itself from zero
