@@ -435,7 +435,15 @@ def copy_calibration(torch):
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+    # and its rate (bytes read + written per second) over 20 more copies, for context beside the HBM peak
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(20):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbps = 2 * n * 20 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 3, "copy_GBps": round(gbps, 1)}), flush=True)
 
 
 def _counter_rows(directory, counter, kernel_substr):
