@@ -121,6 +121,24 @@ def test_gradients_in_place(R, case):
     _check(got, ref, tol("bf16"))
 
 
+@pytest.mark.parametrize("N", [1000, 1056])
+def test_gradients_dk128_other_lengths(R, N):
+    """d_k = d_v = 128 where the streaming kernel's reversed instances do not apply (N not a multiple of its 64-token
+    step): 1056, a multiple of 32, runs in place on the wide-head kernels with the final reordering launch; 1000
+    through reordered copies. Both match the oracle."""
+    w = W.Workload("grad", B=1, N=N, H=2, dk=128, dv=128, dtype="bf16", scale=float(np.sqrt(128)), seed=83 + N,
+                   chunk=128, rotate=True)
+    print_case("gradients-dk128-length", N, w)
+    q, k, v, rng = W.make_qkv(w)
+    do = W.make_dout(w, rng)
+    ref = oracle.grad(q, k, v, do, w.gamma, theta=w.theta, pos0=11)
+    timer = R.Timer()
+    got = _gpu_grad(R, q, k, v, do, w.gamma, w.chunk, w.theta, 11, "bf16", options={"timer": timer})
+    assert timer.query("ret_permute_rotate")[1] == (1 if N % 32 == 0 else 2)
+    timer.close()
+    _check(got, ref, tol("bf16"))
+
+
 @pytest.mark.parametrize("case", [(2, 700, 4, 64, 9), (1, 1024, 2, 64, 70001)], ids=["ragged", "far-positions"])
 def test_gradients_on_chip_rotate_while_staging(R, case):
     """d = 64 in short segments (the on-chip kernel's reversed traversal): no rotation launch and no rotated
