@@ -121,6 +121,31 @@ def test_gradients_in_place(R, case):
     _check(got, ref, tol("bf16"))
 
 
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_gradients_streaming_seeded_shapes(R, seed):
+    """The streaming kernel's gradient path (rotation while staging, outputs turned back in the kernel, dk' from
+    the dv retention's states) on seeded shapes: N a multiple of 64 from 1024 to 6144, 1 or 2 heads, 2 to 5
+    segments (segments of 3 to 48 chunks, so the rotation factors are carried across groups of 8 and re-evaluated
+    mid-segment), a position offset up to 2^20, bf16 or fp32 gradients."""
+    rng0 = np.random.default_rng(1000 + seed)
+    N = int(rng0.integers(16, 97)) * 64
+    H = int(rng0.integers(1, 3))
+    nseg = int(rng0.integers(2, 6))
+    pos0 = int(rng0.integers(0, 1 << 20))
+    out_dt = ["bf16", "f32"][seed % 2]
+    w = W.Workload("grad", B=1, N=N, H=H, dk=128, dv=128, dtype="bf16", scale=float(np.sqrt(128)), seed=91 + seed,
+                   chunk=128, rotate=True)
+    print_case("gradients-streaming-seeded", (N, H, nseg, pos0, out_dt), w)
+    q, k, v, rng = W.make_qkv(w)
+    do = W.make_dout(w, rng)
+    ref = oracle.grad(q, k, v, do, w.gamma, theta=w.theta, pos0=pos0)
+    timer = R.Timer()
+    got = _gpu_grad(R, q, k, v, do, w.gamma, w.chunk, w.theta, pos0, out_dt, options={"timer": timer, "segments": nseg})
+    assert timer.query("ret_permute_rotate")[1] == 0 and timer.query("ret_rotate_qk")[1] == 0
+    timer.close()
+    _check(got, ref, tol("bf16"))
+
+
 @pytest.mark.parametrize("N", [1000, 1056])
 def test_gradients_dk128_other_lengths(R, N):
     """d_k = d_v = 128 where the streaming kernel's reversed instances do not apply (N not a multiple of its 64-token
