@@ -361,7 +361,8 @@ __global__ __launch_bounds__(256) void unit_scan_kernel(FwdArgs a) {
                 acc.y = decay * acc.y + u[j].y;
                 acc.z = decay * acc.z + u[j].z;
                 acc.w = decay * acc.w + u[j].w;
-                *reinterpret_cast<float4*>(W + (long long)(g0 + j) * PER) = acc;
+                // with no state_in, W_1 = R_0 is slot 1 as the local pass left it
+                if (g0 + j > 1 || a.state_in) *reinterpret_cast<float4*>(W + (long long)(g0 + j) * PER) = acc;
             }
     }
 }

@@ -70,7 +70,10 @@ __global__ __launch_bounds__(256) void slot_scan_kernel(FwdArgs a) {
 // rotate_qk: q' = rotated q, k' = rotated k (bf16 in, bf16 out), the rotation the chunk kernels otherwise
 // apply while staging. Written once when a call stages the same rows for several d_v tiles. Thread: one
 // 16-byte segment (8 dims, 4 pairs) of one (b, h) row over kRotTokens consecutive tokens; the factors of the
-// first token are evaluated exactly, later ones by angle addition with the one-token step.
+// first token are evaluated exactly, later ones by angle addition with the one-token step. All of a thread's
+// q and k rows are requested before the first is used (2 kRotTokens 16-byte loads in flight per thread instead
+// of two): the kernel streams, and what bounds it is the bytes in flight. The loads carry the non-temporal hint
+// (each row is read once here; the chunk kernels read q' and k', not q and k).
 // ---------------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void rotate_qk_kernel(FwdArgs a) {
     const int segs = a.H * a.dk / 8;  // segments of one token's row over all heads
@@ -81,21 +84,28 @@ __global__ __launch_bounds__(256) void rotate_qk_kernel(FwdArgs a) {
     const long long bt = gid / segs;
     const int b = (int)(bt / nblk), n0 = (int)(bt % nblk) * kRotTokens;
     const int h = r / (a.dk / 8), pair0 = (r % (a.dk / 8)) * 4;
+    const long long row = (long long)a.H * a.dk;  // elements between tokens
+    const long long base = (((long long)b * a.N + n0) * a.H + h) * a.dk + pair0 * 2;
+    const int nt = min(kRotTokens, a.N - n0);
+    // rows past the sequence's end (a partial last block) re-read its last row and are not stored
+    u32x4_t uq[kRotTokens], uk[kRotTokens];
+#pragma unroll
+    for (int i = 0; i < kRotTokens; ++i) {
+        const long long off = base + (long long)min(i, nt - 1) * row;
+        uq[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>((const uint16_t*)a.q + off));
+        uk[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>((const uint16_t*)a.k + off));
+    }
     float c[4], s[4], dc[4], ds[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         rot_cs(a.pos0 + n0, a.theta[pair0 + j], &c[j], &s[j]);
         rot_cs(1, a.theta[pair0 + j], &dc[j], &ds[j]);
     }
-    const long long row = (long long)a.H * a.dk;  // elements between tokens
-    const long long base = (((long long)b * a.N + n0) * a.H + h) * a.dk + pair0 * 2;
-    const int nt = min(kRotTokens, a.N - n0);
-    for (int i = 0; i < nt; ++i) {
-        const uint4 uq = *reinterpret_cast<const uint4*>((const uint16_t*)a.q + base + i * row);
-        const uint4 uk = *reinterpret_cast<const uint4*>((const uint16_t*)a.k + base + i * row);
+#pragma unroll
+    for (int i = 0; i < kRotTokens; ++i) {
         float fq[8], fk[8];
-        unpack8_bf16(uq, fq);
-        unpack8_bf16(uk, fk);
+        unpack8_bf16(make_uint4(uq[i][0], uq[i][1], uq[i][2], uq[i][3]), fq);
+        unpack8_bf16(make_uint4(uk[i][0], uk[i][1], uk[i][2], uk[i][3]), fk);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const float q0 = fq[2 * j], q1 = fq[2 * j + 1], k0 = fk[2 * j], k1 = fk[2 * j + 1];
@@ -107,8 +117,10 @@ __global__ __launch_bounds__(256) void rotate_qk_kernel(FwdArgs a) {
             s[j] = s[j] * dc[j] + c[j] * ds[j];
             c[j] = nc;
         }
-        *reinterpret_cast<uint4*>((uint16_t*)a.qr + base + i * row) = pack8_bf16(fq);
-        *reinterpret_cast<uint4*>((uint16_t*)a.kr + base + i * row) = pack8_bf16(fk);
+        if (i < nt) {
+            *reinterpret_cast<uint4*>((uint16_t*)a.qr + base + i * row) = pack8_bf16(fq);
+            *reinterpret_cast<uint4*>((uint16_t*)a.kr + base + i * row) = pack8_bf16(fk);
+        }
     }
 }
 
