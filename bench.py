@@ -11,6 +11,7 @@ of the same kernel is reported beside it.
 The same JSON line carries, each with its own roofline:
   * long-sequence (B=1, N=65536, H=8, d=128, chunk 128) and retention-layer-d512 (B=8, N=2048, H=8, d=64,
     chunk 64) chunkwise calls, warm and MALL-cold (each call after a 512 MiB scratch write);
+  * the long-sequence workload's 256 decode steps from its final state (steps/s; launch-latency-bound);
   * batched decode (B=128, H=8, d=64, fp32 state, 1024 single-token ret_recurrent_step calls replayed from a
     HIP graph), warm (one 16 MiB state, which the 256 MB Infinity Cache holds between steps) and MALL-cold
     (the graph's steps cycle through 32 distinct states, 512 MiB, so every state read comes from HBM);
@@ -380,6 +381,38 @@ def bench_decode(R, W, torch, steps_graph=1024, reps=3, cold_states=32, mode="bo
     return w, us_warm, us_cold, k_warm, k_cold
 
 
+def bench_decode_long(R, W, torch, reps=3):
+    """The long-sequence workload's 256 decode steps (B=1, H=8, d=128: a 512 KiB fp32 state, 1.06 MB per step)
+    from its chunkwise final state, replayed from a HIP graph; positions 65536 onward. Each step is one small
+    launch, so the figure is steps per second (launch latency bounds it, not HBM)."""
+    import numpy as np
+    w = W.WORKLOADS[5]
+    q, k, v, rng = W.make_qkv(w)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).cuda()
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    o = torch.empty((w.B, w.N, w.H, w.dv), dtype=torch.bfloat16, device="cuda")
+    state = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    R.ret_chunkwise_fwd(qd, kd, vd, o, w.gamma, w.chunk, theta=w.theta, state_out=state,
+                        workspace=R.chunkwise_workspace(qd, vd, w.chunk))
+    del qd, kd, vd, o
+    steps = [W.make_step(w, rng) for _ in range(w.steps)]
+    sqd = dev(np.stack([x[0] for x in steps]))
+    skd = dev(np.stack([x[1] for x in steps]))
+    svd = dev(np.stack([x[2] for x in steps]))
+    outs = torch.empty((w.steps, w.B, w.H, w.dv), dtype=torch.bfloat16, device="cuda")
+
+    def run_steps():
+        for t in range(w.steps):
+            R.ret_recurrent_step(sqd[t], skd[t], svd[t], outs[t], state, w.gamma, pos=w.N + t, theta=w.theta)
+
+    us = 1e3 * graph_ms(torch, run_steps, 1, reps) / w.steps
+    db, _ = decode_algorithmic(w.B, w.H, w.dk, w.dv)
+    return {"workload": "%s decode: B=%d H=%d d_k=%d d_v=%d, fp32 state from the %d-token chunkwise call, %d steps, "
+                        "HIP graph" % (w.name, w.B, w.H, w.dk, w.dv, w.N, w.steps),
+            "us_per_step": us, "steps_per_s": 1e6 / us, "alg_bytes_per_step": db,
+            "hbm_frac": db / (us * 1e-6) / 8e12, "bound": "launch latency (1.06 MB per step)"}
+
+
 def _cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -601,6 +634,9 @@ def main():
         if us_cold is not None and us_warm is not None:
             result["decode"]["warm"] = {"us_per_step": us_warm, "steps_per_s": 1e6 / us_warm,
                                         "roofline": decode_roofline(us_warm, dw.name, warm_state)}
+        if not args.no_extra:
+            progress("decode long-sequence")
+            result["long-sequence-decode"] = bench_decode_long(R, W, torch)
     if not args.no_epilogue:
         progress("epilogue")
         result["epilogue"] = bench_epilogue(R, W, torch, CHUNK_WORKLOADS["retention-layer-d512"], args.steps)
