@@ -100,3 +100,54 @@ def test_random_shapes_forward_and_gradients(R, seed):
         errs = [rel_err(to_host(g), r) for g, r in zip((dq, dkg, dvg), ref)]
         print("  err dq=%.3g dk=%.3g dv=%.3g" % tuple(errs))
         assert max(errs) <= tol("bf16"), errs
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_shapes_fp32(R, seed):
+    """fp32 inputs (d_k in {16, 32, 64}, chunks of 16 to 64): the chunkwise and parallel forms and the gradients
+    over seeded random shapes, positions and initial states, at the fp32 bar."""
+    import torch
+    rng = np.random.default_rng(9300 + seed)
+    for case in range(12):
+        dk = int(rng.choice([16, 32, 64]))
+        dv = int(rng.choice([16, 32, 48, 64, 80, 128]))
+        B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+        N = int(rng.integers(1, 400))
+        C = int(rng.choice([16, 32, 64]))
+        rot = bool(rng.random() < 0.7)
+        pos0 = int(rng.choice([0, 5, 4096, 2 ** 20 + 3]))
+        has_s = bool(rng.random() < 0.5)
+        opts = {"segments": int(rng.integers(1, 6))} if rng.random() < 0.5 else {}
+        print_case("sweep fp32", seed, case, (B, N, H, dk, dv, C, rot, pos0, has_s, opts))
+        q = rng.standard_normal((B, N, H, dk)).astype(np.float32)
+        k = rng.standard_normal((B, N, H, dk)).astype(np.float32)
+        v = rng.standard_normal((B, N, H, dv)).astype(np.float32)
+        s0 = rng.standard_normal((B, H, dk, dv)).astype(np.float32) if has_s else None
+        gamma, theta = W.gamma_schedule(H), (W.theta_schedule(dk) if rot else None)
+        qd, kd, vd = to_dev(q, "f32"), to_dev(k, "f32"), to_dev(v, "f32")
+        o = empty_out((B, N, H, dv), "f32")
+        sin = torch.from_numpy(s0).cuda() if has_s else None
+        sout = torch.empty((B, H, dk, dv), dtype=torch.float32, device="cuda")
+        ws = R.chunkwise_workspace(qd, vd, C, opts)
+        R.ret_chunkwise_fwd(qd, kd, vd, o, gamma, C, theta=theta, pos0=pos0, state_in=sin, state_out=sout,
+                            workspace=ws, options=opts)
+        op = empty_out((B, N, H, dv), "f32")
+        R.ret_parallel_fwd(qd, kd, vd, op, gamma, theta=theta, pos0=pos0)
+        torch.cuda.synchronize()
+        R.ret_chunkwise_check(ws)
+        o_ref, s_ref = oracle.chunkwise(q, k, v, gamma, C, theta=theta, pos0=pos0, state_in=s0)
+        p_ref = oracle.parallel(q, k, v, gamma, theta=theta, pos0=pos0)
+        errs = rel_err(to_host(o), o_ref), rel_err(to_host(sout), s_ref), rel_err(to_host(op), p_ref)
+        print("  err o=%.3g state=%.3g parallel=%.3g" % errs)
+        assert max(errs) <= tol("f32"), errs
+        if dv in (48, 80):  # the gradients' dq and dk retentions take d_v as their d_k: 16, 32, 64 or twice 64
+            continue
+        do = rng.standard_normal((B, N, H, dv)).astype(np.float32)
+        dq, dkg, dvg = empty_out(q.shape, "f32"), empty_out(k.shape, "f32"), empty_out(v.shape, "f32")
+        R.ret_chunkwise_bwd(qd, kd, vd, to_dev(do, "f32"), dq, dkg, dvg, gamma, C, theta=theta, pos0=pos0,
+                            options=opts, check=True)
+        torch.cuda.synchronize()
+        ref = oracle.grad(q, k, v, do, gamma, theta=theta, pos0=pos0)
+        gerrs = [rel_err(to_host(g), r) for g, r in zip((dq, dkg, dvg), ref)]
+        print("  err dq=%.3g dk=%.3g dv=%.3g" % tuple(gerrs))
+        assert max(gerrs) <= tol("f32"), gerrs
