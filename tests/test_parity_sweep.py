@@ -1,5 +1,6 @@
-"""GPU parity over seeded random shapes: the chunkwise forward and its gradients against the fp64 oracle, with
-shapes, chunk sizes, positions, initial states and plan options drawn per case. Every bf16 kernel family is
+"""GPU parity over seeded random shapes: the chunkwise forward, its gradients and the decode step against the fp64
+oracle, with shapes, chunk sizes, positions, initial states and plan options drawn per case. Every bf16 kernel
+family is
 reached this way: the on-chip d_k <= 64 kernel and the streaming one, the d_k = 128 and 256 kernels (chained,
 three launches, wide and LDS-loading variants, with and without rotated copies), segment counts from 1 to 9,
 ragged sequences, positions past 2^20, and the gradients on the reversed traversal or reordered copies, with
@@ -151,3 +152,35 @@ def test_random_shapes_fp32(R, seed):
         gerrs = [rel_err(to_host(g), r) for g, r in zip((dq, dkg, dvg), ref)]
         print("  err dq=%.3g dk=%.3g dv=%.3g" % tuple(gerrs))
         assert max(gerrs) <= tol("f32"), gerrs
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_shapes_decode(R, seed):
+    """Decode steps over seeded random shapes (bf16 d_k 32 to 256, fp32 d_k 16 to 64; batch and heads from 1 up to
+    40 and 8), positions and states: three consecutive steps, each output and state against the oracle's step."""
+    import torch
+    rng = np.random.default_rng(9500 + seed)
+    for case in range(10):
+        bf = bool(rng.random() < 0.6)
+        dk = int(rng.choice([32, 64, 128, 256] if bf else [16, 32, 64]))
+        dv = int(rng.choice([64, 128, 256] if bf else [16, 32, 64, 128]))
+        B, H = int(rng.integers(1, 41)), int(rng.integers(1, 9))
+        rot = bool(rng.random() < 0.8)
+        pos = int(rng.choice([0, 7, 70000, 2 ** 20 + 1]))
+        dt = "bf16" if bf else "f32"
+        print_case("sweep decode", seed, case, (dt, B, H, dk, dv, rot, pos))
+        gamma, theta = W.gamma_schedule(H), (W.theta_schedule(dk) if rot else None)
+        s_ref = rng.standard_normal((B, H, dk, dv)).astype(np.float32)
+        state = torch.from_numpy(s_ref.copy()).cuda()
+        for t in range(3):
+            scale = 8.0 if bf else 1.0
+            q = W.normal(rng, (B, H, dk), scale, dt)
+            k = W.normal(rng, (B, H, dk), scale, dt)
+            v = W.normal(rng, (B, H, dv), scale, dt)
+            o = empty_out((B, H, dv), dt)
+            R.ret_recurrent_step(to_dev(q, dt), to_dev(k, dt), to_dev(v, dt), o, state, gamma, pos + t, theta=theta)
+            torch.cuda.synchronize()
+            o_ref, s_ref = oracle.recurrent_step(q, k, v, gamma, s_ref, pos + t, theta=theta)
+            eo, es = rel_err(to_host(o), o_ref), rel_err(to_host(state), s_ref)
+            print("  step %d err o=%.3g state=%.3g" % (t, eo, es))
+            assert eo <= tol(dt) and es <= tol(dt), (t, eo, es)
