@@ -1,10 +1,9 @@
 """GPU parity over seeded random shapes: the chunkwise forward, its gradients and the decode step against the fp64
 oracle, with shapes, chunk sizes, positions, initial states and plan options drawn per case. Every bf16 kernel
-family is
-reached this way: the on-chip d_k <= 64 kernel and the streaming one, the d_k = 128 and 256 kernels (chained,
-three launches, wide and LDS-loading variants, with and without rotated copies), segment counts from 1 to 9,
-ragged sequences, positions past 2^20, and the gradients on the reversed traversal or reordered copies, with
-and without the forward call's workspace.
+family is reached this way: the on-chip d_k <= 64 kernel and the streaming one, the d_k = 128 and 256 kernels
+(chained, three launches, wide and LDS-loading variants, with and without rotated copies), segment counts from 1
+to 9, ragged sequences, positions past 2^20, and the gradients on the reversed traversal or reordered copies,
+with and without the forward call's workspace.
 
 Bar (max|gpu - oracle| / max|oracle|): 2e-2 for bf16 inputs. The gradients of bf16 heads with d_k = 32 have no
 kernels (their dq and dk retentions would need d_v = 32); such cases must report an unsupported shape.
